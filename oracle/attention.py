@@ -1,0 +1,50 @@
+"""Causal grouped-query softmax attention, two independent ways.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The pages call the attention layers standard multi-head attention and say the
+kernel fuses the QKV projection, RoPE, the causal softmax and the output
+projection (luce-megakernel announcement, page 1, layer-pattern paragraph and
+kernel-design bullets).  The model run here has 8 query heads sharing 2 key/value
+heads; query head i reads key/value head i // (n_q / n_kv), so MHA is the case
+n_kv = n_q.  Scores are scaled by 1/sqrt(head_dim), position t attends to
+positions 0..t (itself included), and softmax subtracts the row maximum.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .primitives import softmax
+
+
+def attend_one(q, Kc, Vc):
+    """One query position over a cache, head by head.
+
+    q [nq, hd]; Kc, Vc [nkv, L, hd] holding the L visible positions -> o [nq, hd]."""
+    nq, hd = q.shape
+    nkv = Kc.shape[0]
+    group = nq // nkv
+    o = np.empty_like(q)
+    for i in range(nq):
+        g = i // group
+        s = Kc[g] @ q[i] / np.sqrt(hd)
+        p = softmax(s)
+        o[i] = p @ Vc[g]
+    return o
+
+
+def causal_attention(Q, K, V):
+    """Whole sequence with the full masked score matrix.
+
+    Q [T, nq, hd]; K, V [T, nkv, hd] -> O [T, nq, hd]."""
+    T, nq, hd = Q.shape
+    nkv = K.shape[1]
+    group = nq // nkv
+    mask = np.tril(np.ones((T, T), dtype=bool))
+    O = np.empty_like(Q)
+    for i in range(nq):
+        g = i // group
+        s = (Q[:, i, :] @ K[:, g, :].T) / np.sqrt(hd)
+        s = np.where(mask, s, -np.inf)
+        O[:, i, :] = softmax(s, axis=-1) @ V[:, g, :]
+    return O

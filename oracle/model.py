@@ -1,0 +1,171 @@
+"""The whole hybrid decoder, token by token (``Oracle.step``) and whole-sequence (``Oracle.forward``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Layer pattern (luce-megakernel announcement, page 1, layer-pattern paragraph):
+18 DeltaNet layers and 6 full-attention layers out of 24, placed here as a
+repeating 3:1 pattern, layer l being attention when l % period == attn_slot.
+Each layer is pre-norm residual:
+
+    x += Mixer(RMSNorm(x; g1))         Mixer = gated DeltaNet or GQA attention
+    x += W_d (silu(W_g h) * (W_u h)),  h = RMSNorm(x; g2)
+
+followed after the last layer by ``logits = E . RMSNorm(x; g_f)`` with the input
+embedding E reused as the LM head, and greedy argmax (lowest index on ties).
+
+The two entry points share only the per-token primitives; ``step`` carries a
+recurrent DeltaNet state and a KV cache, ``forward`` uses the parallel DeltaNet
+form and the full causal score matrix, so they check each other.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .primitives import bf16_decode, rmsnorm, l2norm, silu, rope_angles, rope
+from .deltanet import gates, delta_step, delta_parallel
+from .attention import attend_one, causal_attention
+
+
+class Oracle:
+    def __init__(self, cfg, weight_bits: dict, dtype=np.float64):
+        self.cfg = cfg
+        self.dtype = dtype
+        self.W = {name: bf16_decode(bits, dtype) for name, bits in weight_bits.items()}
+        self.reset()
+
+    # ---------------------------------------------------------------- state
+    def reset(self):
+        c = self.cfg
+        self.pos = 0
+        self.S = {}
+        self.Kc = {}
+        self.Vc = {}
+        for l in range(c.n_layers):
+            if c.is_attention(l):
+                self.Kc[l] = np.zeros((c.n_kv_heads, c.max_ctx, c.head_dim), self.dtype)
+                self.Vc[l] = np.zeros((c.n_kv_heads, c.max_ctx, c.head_dim), self.dtype)
+            else:
+                self.S[l] = np.zeros((c.dn_heads, c.dn_dv, c.dn_dk), self.dtype)
+
+    def load_state(self, fwd: dict):
+        """Continue token by token from the end of a ``forward`` result."""
+        self.reset()
+        T = fwd["n_tokens"]
+        for l, S in fwd["S"].items():
+            self.S[l] = np.array(S, copy=True)
+        for l, (K, V) in fwd["KV"].items():
+            self.Kc[l][:, :T] = K
+            self.Vc[l][:, :T] = V
+        self.pos = T
+
+    # ------------------------------------------------------------ per layer
+    def _dn_project(self, l, h):
+        c = self.cfg
+        H, dk, dv = c.dn_heads, c.dn_dk, c.dn_dv
+        qkv = h @ self.W[f"l{l}.dn.wqkv"].T
+        q = qkv[..., : H * dk].reshape(*h.shape[:-1], H, dk)
+        k = qkv[..., H * dk: 2 * H * dk].reshape(*h.shape[:-1], H, dk)
+        v = qkv[..., 2 * H * dk:].reshape(*h.shape[:-1], H, dv)
+        a = h @ self.W[f"l{l}.dn.wa"].T
+        b = h @ self.W[f"l{l}.dn.wb"].T
+        alpha, beta = gates(a, b)
+        return l2norm(q, c.l2_eps), l2norm(k, c.l2_eps), v, alpha, beta
+
+    def _attn_project(self, l, h, positions):
+        c = self.cfg
+        q = (h @ self.W[f"l{l}.attn.wq"].T).reshape(*h.shape[:-1], c.n_q_heads, c.head_dim)
+        k = (h @ self.W[f"l{l}.attn.wk"].T).reshape(*h.shape[:-1], c.n_kv_heads, c.head_dim)
+        v = (h @ self.W[f"l{l}.attn.wv"].T).reshape(*h.shape[:-1], c.n_kv_heads, c.head_dim)
+        cos, sin = rope_angles(c.head_dim, c.rope_theta, positions, self.dtype)
+        cos = cos[..., None, :]
+        sin = sin[..., None, :]
+        return rope(q, cos, sin), rope(k, cos, sin), v
+
+    def _ffn(self, l, x):
+        c = self.cfg
+        h = rmsnorm(x, self.W[f"l{l}.norm2"], c.rms_eps)
+        gte = h @ self.W[f"l{l}.ffn.wg"].T
+        up = h @ self.W[f"l{l}.ffn.wu"].T
+        return x + (silu(gte) * up) @ self.W[f"l{l}.ffn.wd"].T
+
+    def _head(self, x):
+        xf = rmsnorm(x, self.W["final_norm"], self.cfg.rms_eps)
+        return xf @ self.W["embed"].T
+
+    # --------------------------------------------------- one token (O1 form)
+    def step(self, tok: int) -> np.ndarray:
+        """Run one token at the current position, update state and cache, return logits [vocab]."""
+        c = self.cfg
+        p = self.pos
+        if p >= c.max_ctx:
+            raise ValueError("context full")
+        x = self.W["embed"][int(tok)].copy()
+        for l in range(c.n_layers):
+            h = rmsnorm(x, self.W[f"l{l}.norm1"], c.rms_eps)
+            if c.is_attention(l):
+                q, k, v = self._attn_project(l, h, p)
+                self.Kc[l][:, p] = k
+                self.Vc[l][:, p] = v
+                o = attend_one(q, self.Kc[l][:, : p + 1], self.Vc[l][:, : p + 1])
+                x = x + o.reshape(-1) @ self.W[f"l{l}.attn.wo"].T
+            else:
+                q, k, v, alpha, beta = self._dn_project(l, h)
+                self.S[l], o = delta_step(self.S[l], q, k, v, alpha, beta)
+                x = x + o.reshape(-1) @ self.W[f"l{l}.dn.wo"].T
+            x = self._ffn(l, x)
+        self.pos = p + 1
+        return self._head(x)
+
+    # ------------------------------------------------ whole sequence (O2 form)
+    def forward(self, tokens, logits: str = "all") -> dict:
+        """Fresh state, whole sequence at once.  Returns logits ("all" [T, vocab] or "last" [vocab]),
+        the final DeltaNet state per layer, and the rotated K / V per attention layer [nkv, T, hd]."""
+        c = self.cfg
+        tokens = np.asarray(tokens)
+        T = tokens.shape[0]
+        positions = np.arange(T)
+        X = self.W["embed"][tokens].copy()
+        S_out, KV_out = {}, {}
+        for l in range(c.n_layers):
+            Hn = rmsnorm(X, self.W[f"l{l}.norm1"], c.rms_eps)
+            if c.is_attention(l):
+                Q, K, V = self._attn_project(l, Hn, positions)
+                O = causal_attention(Q, K, V)
+                KV_out[l] = (np.transpose(K, (1, 0, 2)).copy(), np.transpose(V, (1, 0, 2)).copy())
+                X = X + O.reshape(T, -1) @ self.W[f"l{l}.attn.wo"].T
+            else:
+                Q, K, V, alpha, beta = self._dn_project(l, Hn)
+                O = np.empty((T, c.dn_heads, c.dn_dv), self.dtype)
+                S_l = np.empty((c.dn_heads, c.dn_dv, c.dn_dk), self.dtype)
+                S0 = np.zeros((c.dn_dv, c.dn_dk), self.dtype)
+                for hh in range(c.dn_heads):
+                    O[:, hh], S_l[hh] = delta_parallel(S0, Q[:, hh], K[:, hh], V[:, hh],
+                                                       alpha[:, hh], beta[:, hh])
+                S_out[l] = S_l
+                X = X + O.reshape(T, -1) @ self.W[f"l{l}.dn.wo"].T
+            X = self._ffn(l, X)
+        out = {"n_tokens": T, "S": S_out, "KV": KV_out}
+        out["logits"] = self._head(X) if logits == "all" else self._head(X[-1])
+        return out
+
+    # ------------------------------------------------------------- helpers
+    @staticmethod
+    def argmax(logits) -> int:
+        """Greedy choice; numpy's argmax returns the lowest index among equal maxima."""
+        return int(np.argmax(logits))
+
+    def greedy(self, prompt, n_steps: int):
+        """Prompt through ``forward``, then ``n_steps`` token-by-token greedy steps.
+
+        Returns (tokens fed to each decode step [n_steps], logits of each decode step [n_steps, vocab],
+        last-prompt-position logits)."""
+        fwd = self.forward(prompt, logits="last")
+        self.load_state(fwd)
+        nxt = self.argmax(fwd["logits"])
+        fed, outs = [], []
+        for _ in range(n_steps):
+            fed.append(nxt)
+            lg = self.step(nxt)
+            outs.append(lg)
+            nxt = self.argmax(lg)
+        return np.array(fed, dtype=np.int32), np.stack(outs) if outs else None, fwd["logits"]

@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+closed form, a hand-worked example, brute force, an invariant, or its own
+independent second form.  The functions look up oracle routines through their
+modules at call time so that ``test_oracle_mutations.py`` can plant a mistake in
+the oracle and check that some pin catches it.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.primitives as prim
+import oracle.deltanet as dn
+import oracle.attention as att
+import oracle.model as om
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ------------------------------------------------------------------ primitives
+def pin_rmsnorm_closed_form():
+    # mean of squares of [1,-2,2,4] is 25/4, so the RMS is 5/2 (eps = 0)
+    x = np.array([1.0, -2.0, 2.0, 4.0])
+    g = np.array([1.0, 2.0, 3.0, 4.0])
+    _close(prim.rmsnorm(x, g, 0.0), [0.4, -1.6, 2.4, 6.4], 1e-15, "rmsnorm")
+    # a constant vector c normalises to sign(c) * g up to eps
+    _close(prim.rmsnorm(np.full(8, -3.0), np.arange(1.0, 9.0), 1e-6), -np.arange(1.0, 9.0), 1e-6, "rmsnorm const")
+
+
+def pin_l2norm_closed_form():
+    _close(prim.l2norm(np.array([3.0, 4.0]), 0.0), [0.6, 0.8], 1e-15, "l2norm")
+    _close(prim.l2norm(np.array([[0.0, 5.0], [-8.0, 6.0]]), 0.0), [[0.0, 1.0], [-0.8, 0.6]], 1e-15, "l2norm rows")
+
+
+def pin_gate_closed_forms():
+    # softplus(0) = ln 2 -> alpha = 1/2 ; sigmoid(0) = 1/2
+    a, b = dn.gates(np.array([0.0]), np.array([0.0]))
+    _close(a, [0.5], 1e-15, "alpha(0)")
+    _close(b, [0.5], 1e-15, "beta(0)")
+    # softplus(ln(e-1)) = ln(e) = 1 -> alpha = 1/e ; sigmoid(ln 3) = 3/4
+    a, b = dn.gates(np.array([math.log(math.e - 1.0)]), np.array([math.log(3.0)]))
+    _close(a, [1.0 / math.e], 1e-15, "alpha(ln(e-1))")
+    _close(b, [0.75], 1e-15, "beta(ln 3)")
+    # limits: alpha -> 1 and beta -> 0 as the logits go to -inf; alpha -> 0, beta -> 1 at +inf
+    a, b = dn.gates(np.array([-800.0, 800.0]), np.array([-800.0, 800.0]))
+    _close(a, [1.0, 0.0], 1e-300, "alpha limits")
+    _close(b, [0.0, 1.0], 1e-300, "beta limits")
+    _close(prim.silu(np.array([1.0, 0.0])), [1.0 / (1.0 + math.exp(-1.0)), 0.0], 1e-15, "silu")
+
+
+def pin_bf16_decode():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x4049], dtype=np.uint16)
+    _close(prim.bf16_decode(bits), [1.0, -2.0, 1.0078125, 0.0, 3.140625], 0.0, "bf16 decode")
+
+
+def pin_rope_pairing_and_sign():
+    # head_dim 4, theta 1e4: frequencies 1 and 0.01; element i pairs with i + 2
+    cos, sin = prim.rope_angles(4, 10000.0, 1)
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(0.01), math.sin(0.01)
+    want = [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2]
+    _close(prim.rope(x, cos, sin), want, 1e-14, "rope hd=4 pos=1")
+    # position 0 is the identity
+    cos0, sin0 = prim.rope_angles(8, 10000.0, 0)
+    y = np.arange(8.0)
+    _close(prim.rope(y, cos0, sin0), y, 0.0, "rope pos 0")
+
+
+def pin_rope_relativity():
+    rng = np.random.default_rng(7)
+    hd = 16
+    q, k = rng.standard_normal(hd), rng.standard_normal(hd)
+
+    def score(m, n):
+        cm, sm = prim.rope_angles(hd, 10000.0, m)
+        cn, sn = prim.rope_angles(hd, 10000.0, n)
+        return float(prim.rope(q, cm, sm) @ prim.rope(k, cn, sn))
+
+    for m, n, d in [(5, 2, 11), (40, 39, 100), (3, 3, 7)]:
+        assert abs(score(m, n) - score(m + d, n + d)) < 1e-11, "rope scores must depend on m - n only"
+    cm, sm = prim.rope_angles(hd, 10000.0, 123)
+    assert abs(np.linalg.norm(prim.rope(q, cm, sm)) - np.linalg.norm(q)) < 1e-12, "rope preserves norm"
+
+
+# -------------------------------------------------------------------- deltanet
+def pin_deltanet_hand_example():
+    with open(os.path.join(GOLDEN, "deltanet_two_step.json")) as f:
+        g = json.load(f)
+    S = np.array(g["S0"])
+    for i, st in enumerate(g["steps"]):
+        S, o = dn.delta_step(S, np.array(st["q"]), np.array(st["k"]), np.array(st["v"]),
+                             st["alpha"], st["beta"])
+        _close(S, st["S"], 1e-14, f"hand step {i} S")
+        _close(o, st["o"], 1e-14, f"hand step {i} o")
+
+
+def pin_deltanet_exact_recall():
+    """alpha = beta = 1, S0 = 0, orthonormal keys: the state stores each key->value pair exactly,
+    and querying with a stored key returns its value (so q carries no 1/sqrt(dk) scale)."""
+    rng = np.random.default_rng(11)
+    dk, dv, n = 8, 5, 6
+    Kq, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    K = Kq[:, :n].T.copy()
+    V = rng.standard_normal((n, dv))
+    S = np.zeros((dv, dk))
+    for t in range(n):
+        S, o = dn.delta_step(S, K[t], K[t], V[t], 1.0, 1.0)
+        _close(o, V[t], 1e-12, f"recall readout t={t}")
+    for j in range(n):
+        _close(S @ K[j], V[j], 1e-12, f"recall of pair {j}")
+
+
+def pin_deltanet_last_write():
+    """beta = 1, unit key, any alpha: right after a write, S_t k_t = v_t."""
+    rng = np.random.default_rng(12)
+    dk, dv = 6, 4
+    S = rng.standard_normal((dv, dk))
+    for t in range(5):
+        k = prim.l2norm(rng.standard_normal(dk), 0.0)
+        v = rng.standard_normal(dv)
+        alpha = float(rng.uniform(0.1, 1.0))
+        S, _ = dn.delta_step(S, k, k, v, alpha, 1.0)
+        _close(S @ k, v, 1e-12, f"last write t={t}")
+
+
+def pin_deltanet_gate_limits():
+    rng = np.random.default_rng(13)
+    dk, dv = 5, 3
+    S0 = rng.standard_normal((dv, dk))
+    k = prim.l2norm(rng.standard_normal(dk), 0.0)
+    q = rng.standard_normal(dk)
+    v = rng.standard_normal(dv)
+    S, _ = dn.delta_step(S0, q, k, v, 0.0, 0.7)
+    _close(S, 0.7 * np.outer(v, k), 1e-14, "alpha = 0 forgets everything")
+    S, _ = dn.delta_step(S0, q, k, v, 0.3, 0.0)
+    _close(S, 0.3 * S0, 1e-14, "beta = 0 only decays")
+    S, o = dn.delta_step(S0, q, k, v, 1.0, 0.0)
+    _close(S, S0, 0.0, "alpha = 1, beta = 0 keeps S")
+    _close(o, S0 @ q, 1e-14, "readout uses the updated S")
+    for alpha, beta in [(0.9, 0.4), (0.5, 1.0), (0.2, 0.05)]:
+        S, _ = dn.delta_step(S0, q, k, v, alpha, beta)
+        lhs = np.linalg.norm(S, 2)
+        rhs = alpha * np.linalg.norm(S0, 2) + beta * np.linalg.norm(v)
+        assert lhs <= rhs + 1e-12, "spectral-norm bound ||S_t|| <= alpha ||S_t-1|| + beta ||v||"
+
+
+def _random_sequence(rng, T, dk, dv):
+    Q = prim.l2norm(rng.standard_normal((T, dk)), 1e-6)
+    K = prim.l2norm(rng.standard_normal((T, dk)), 1e-6)
+    V = rng.standard_normal((T, dv))
+    alpha, beta = dn.gates(rng.standard_normal(T), rng.standard_normal(T))
+    S0 = rng.standard_normal((dv, dk))
+    return S0, Q, K, V, alpha, beta
+
+
+def pin_deltanet_forms_agree():
+    """recurrent == explicit product == parallel (one chunk) == chunked, fp64, T <= 16."""
+    rng = np.random.default_rng(14)
+    for T, dk, dv in [(1, 4, 3), (7, 6, 5), (16, 8, 8)]:
+        S0, Q, K, V, alpha, beta = _random_sequence(rng, T, dk, dv)
+        O_r, S_r = dn.delta_recurrent(S0, Q, K, V, alpha, beta)
+        O_e, S_e = dn.delta_explicit_product(S0, Q, K, V, alpha, beta)
+        O_p, S_p = dn.delta_parallel(S0, Q, K, V, alpha, beta)
+        _close(O_e, O_r, 1e-11, f"explicit vs recurrent O (T={T})")
+        _close(S_e, S_r, 1e-11, f"explicit vs recurrent S (T={T})")
+        _close(O_p, O_r, 1e-11, f"parallel vs recurrent O (T={T})")
+        _close(S_p, S_r, 1e-11, f"parallel vs recurrent S (T={T})")
+        for C in (1, 3, 4, 5):
+            O_c, S_c = dn.delta_chunked(S0, Q, K, V, alpha, beta, C)
+            _close(O_c, O_r, 1e-11, f"chunk {C} vs recurrent O (T={T})")
+            _close(S_c, S_r, 1e-11, f"chunk {C} vs recurrent S (T={T})")
+
+
+def pin_deltanet_long_decay_stable():
+    """alpha ~ 0.5 over 200 tokens: the parallel form stays finite (decays taken in log space)."""
+    rng = np.random.default_rng(15)
+    S0, Q, K, V, _, beta = _random_sequence(rng, 200, 4, 4)
+    alpha = np.full(200, 0.5)
+    O_r, S_r = dn.delta_recurrent(S0, Q, K, V, alpha, beta)
+    O_c, S_c = dn.delta_chunked(S0, Q, K, V, alpha, beta, 64)
+    assert np.all(np.isfinite(O_c)) and np.all(np.isfinite(S_c))
+    _close(O_c, O_r, 1e-10, "chunk 64 vs recurrent, strong decay")
+    _close(S_c, S_r, 1e-10, "chunk 64 vs recurrent S, strong decay")
+
+
+# ------------------------------------------------------------------- attention
+def pin_attention_closed_forms():
+    e = math.e
+    q = np.array([[2.0, 0.0, 0.0, 0.0]])                     # 1 head, hd = 4
+    Kc = np.array([[[1.0, 0.0, 0.0, 0.0], [0.0, 0.0, 0.0, 0.0]]])
+    Vc = np.array([[[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0]]])
+    # scores (2*1)/sqrt(4) = 1 and 0 -> weights e/(1+e), 1/(1+e)
+    _close(att.attend_one(q, Kc, Vc), [[e / (1 + e), 1 / (1 + e), 0.0, 0.0]], 1e-15, "two-key softmax")
+    rng = np.random.default_rng(16)
+    v0 = rng.standard_normal((1, 1, 8))
+    _close(att.attend_one(rng.standard_normal((3, 8)), rng.standard_normal((1, 1, 8)), v0),
+           np.repeat(v0[0], 3, axis=0), 1e-15, "one key -> its value")
+    k_same = np.repeat(rng.standard_normal((1, 1, 8)), 5, axis=1)
+    V5 = rng.standard_normal((1, 5, 8))
+    _close(att.attend_one(rng.standard_normal((2, 8)), k_same, V5),
+           np.repeat(V5[0].mean(axis=0, keepdims=True), 2, axis=0), 1e-14, "equal keys -> mean value")
+
+
+def pin_attention_gqa_grouping():
+    """query head i reads kv head i // (nq/nkv); brute-force scalar loops on a small case."""
+    rng = np.random.default_rng(17)
+    nq, nkv, L, hd = 4, 2, 3, 2
+    q = rng.standard_normal((nq, hd))
+    Kc = rng.standard_normal((nkv, L, hd))
+    Vc = rng.standard_normal((nkv, L, hd))
+    got = att.attend_one(q, Kc, Vc)
+    for i in range(nq):
+        g = i // (nq // nkv)
+        s = [sum(q[i, d] * Kc[g, j, d] for d in range(hd)) / math.sqrt(hd) for j in range(L)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = sum(w)
+        want = [sum(w[j] / z * Vc[g, j, d] for j in range(L)) for d in range(hd)]
+        _close(got[i], want, 1e-14, f"head {i}")
+
+
+def pin_attention_forms_agree():
+    """full masked matrix == one query at a time over a growing cache; future keys are invisible."""
+    rng = np.random.default_rng(18)
+    T, nq, nkv, hd = 9, 6, 3, 4
+    Q = rng.standard_normal((T, nq, hd))
+    K = rng.standard_normal((T, nkv, hd))
+    V = rng.standard_normal((T, nkv, hd))
+    O = att.causal_attention(Q, K, V)
+    Kc = np.transpose(K, (1, 0, 2))
+    Vc = np.transpose(V, (1, 0, 2))
+    for t in range(T):
+        _close(O[t], att.attend_one(Q[t], Kc[:, : t + 1], Vc[:, : t + 1]), 1e-14, f"row {t}")
+    K2, V2 = K.copy(), V.copy()
+    K2[5:] += 3.0
+    V2[5:] -= 1.0
+    _close(att.causal_attention(Q, K2, V2)[:5], O[:5], 0.0, "causal mask")
+
+
+# ----------------------------------------------------------------------- model
+def _tiny(**kw):
+    return synth.get_config("tiny", **kw)
+
+
+def pin_model_layer_pattern():
+    c = synth.get_config("hybrid_0p8b")
+    kinds = ["A" if c.is_attention(l) else "D" for l in range(c.n_layers)]
+    assert kinds.count("D") == 18 and kinds.count("A") == 6, "18 DeltaNet + 6 attention layers"
+    assert "".join(kinds[:8]) == "DDDADDDA"
+    t = _tiny()
+    assert ["A" if t.is_attention(l) else "D" for l in range(4)] == ["D", "D", "D", "A"]
+
+
+def pin_model_incremental_equals_recompute(cfg=None, seed=0, gain_noise=0.0, T=12):
+    """token-by-token (recurrent DeltaNet + KV cache) == whole sequence (parallel DeltaNet + full
+    masked attention): logits at every position, final DeltaNet states, rotated K and V."""
+    cfg = cfg or _tiny()
+    W = synth.make_weights(cfg, seed, gain_noise=gain_noise)
+    toks = synth.make_prompt(cfg.vocab, T, seed)
+    o = om.Oracle(cfg, W)
+    fwd = o.forward(toks, logits="all")
+    step_logits = np.stack([o.step(t) for t in toks])
+    _close(step_logits, fwd["logits"], 1e-10, "logits O1 vs O2")
+    for l, S in fwd["S"].items():
+        _close(o.S[l], S, 1e-10, f"state layer {l}")
+    for l, (K, V) in fwd["KV"].items():
+        _close(o.Kc[l][:, :T], K, 1e-12, f"K layer {l}")
+        _close(o.Vc[l][:, :T], V, 1e-12, f"V layer {l}")
+
+
+def pin_model_gain_noise():
+    pin_model_incremental_equals_recompute(seed=3, gain_noise=0.1, T=8)
+
+
+def pin_model_mha_special_case():
+    pin_model_incremental_equals_recompute(cfg=_tiny(n_kv_heads=4), seed=1, T=6)
+
+
+def pin_model_causal():
+    cfg = _tiny()
+    W = synth.make_weights(cfg, 2)
+    o = om.Oracle(cfg, W)
+    toks = synth.make_prompt(cfg.vocab, 10, 2)
+    a = o.forward(toks)["logits"]
+    toks2 = toks.copy()
+    toks2[6:] = (toks2[6:] + 17) % cfg.vocab
+    b = o.forward(toks2)["logits"]
+    _close(b[:6], a[:6], 0.0, "earlier logits ignore later tokens")
+    assert np.max(np.abs(b[6:] - a[6:])) > 1e-6
+
+
+def pin_model_continuation():
+    """forward(prompt) then step() == forward(prompt + continuation) at the continued positions."""
+    cfg = _tiny()
+    W = synth.make_weights(cfg, 4)
+    toks = synth.make_prompt(cfg.vocab, 11, 4)
+    o = om.Oracle(cfg, W)
+    full = o.forward(toks, logits="all")
+    part = o.forward(toks[:7], logits="last")
+    _close(part["logits"], full["logits"][6], 1e-10, "last-only logits")
+    o.load_state(part)
+    for t in range(7, 11):
+        _close(o.step(toks[t]), full["logits"][t], 1e-10, f"continued position {t}")
+
+
+def pin_argmax_lowest_index():
+    lg = np.array([0.1, 0.7, 0.3, 0.7, -1.0])
+    assert om.Oracle.argmax(lg) == 1
+
+
+def pin_fp32_vs_fp64_gap():
+    """The oracle's own rounding is far below the GPU tolerances (logits 1e-2, state 1e-3)."""
+    import oracle.metrics as mt
+    cfg = _tiny()
+    W = synth.make_weights(cfg, 0)
+    toks = synth.make_prompt(cfg.vocab, 16, 0)
+    o64 = om.Oracle(cfg, W, np.float64)
+    o32 = om.Oracle(cfg, W, np.float32)
+    l64 = np.stack([o64.step(t) for t in toks])
+    l32 = np.stack([o32.step(t) for t in toks])
+    assert mt.rel_l2(l32, l64) < 1e-5
+    for l in o64.S:
+        assert mt.rel_l2(o32.S[l], o64.S[l]) < 1e-5
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

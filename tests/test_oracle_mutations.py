@@ -1,0 +1,120 @@
+"""Plant a plausible mistake in the oracle (on the CPU) and check that some pin catches it.
+
+Each mutation is a wrong variant of one oracle routine: a dropped term, a wrong
+sign, a swapped operand or index.  A pin set that passes on a mutant would not
+be able to tell that mistake from the real method.
+"""
+import numpy as np
+import pytest
+
+import oracle.primitives as prim
+import oracle.deltanet as dn
+import oracle.attention as att
+import oracle.model as om
+from oracle_pins import ALL_PINS
+
+
+def _step_no_alpha(S, q, k, v, alpha, beta):
+    return _REAL_STEP(S, q, k, v, np.ones_like(np.asarray(alpha, dtype=float)), beta)
+
+
+def _step_transposed(S, q, k, v, alpha, beta):
+    St, _ = _REAL_STEP(np.swapaxes(S, -1, -2), q, k, v, alpha, beta)
+    St = np.swapaxes(St, -1, -2)
+    return St, (St @ q[..., :, None])[..., 0]
+
+
+def _step_read_before_update(S, q, k, v, alpha, beta):
+    S_new, _ = _REAL_STEP(S, q, k, v, alpha, beta)
+    return S_new, (S @ q[..., :, None])[..., 0]
+
+
+def _step_q_scaled(S, q, k, v, alpha, beta):
+    return _REAL_STEP(S, q / np.sqrt(q.shape[-1]), k, v, alpha, beta)
+
+
+def _gates_beta_swapped(a, b):
+    return np.exp(-prim.softplus(a)), prim.sigmoid(-b)
+
+
+def _gates_alpha_no_exp(a, b):
+    return 1.0 / (1.0 + prim.softplus(a)), prim.sigmoid(b)
+
+
+def _rope_interleaved(x, cos, sin):
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x1 * cos - x2 * sin
+    out[..., 1::2] = x2 * cos + x1 * sin
+    return out
+
+
+def _rope_sign(x, cos, sin):
+    return _REAL_ROPE(x, cos, -sin)
+
+
+def _rms_no_gain(x, g, eps):
+    return _REAL_RMS(x, np.ones_like(g), eps)
+
+
+def _rms_no_mean(x, g, eps):
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def _attend_no_scale(q, Kc, Vc):
+    return _REAL_ATTEND(q * np.sqrt(q.shape[-1]), Kc, Vc)
+
+
+def _attend_wrong_group(q, Kc, Vc):
+    # head i -> kv head i % nkv (interleaved) instead of contiguous groups
+    nq, hd = q.shape
+    nkv = Kc.shape[0]
+    o = np.empty_like(q)
+    for i in range(nq):
+        s = Kc[i % nkv] @ q[i] / np.sqrt(hd)
+        p = prim.softmax(s)
+        o[i] = p @ Vc[i % nkv]
+    return o
+
+
+def _parallel_no_s0_decay(S0, Q, K, V, alpha, beta):
+    O, S_T = _REAL_PAR(S0, Q, K, V, alpha, beta)
+    g = np.cumsum(np.log(alpha))
+    return O, S_T - np.exp(g[-1]) * S0 + S0
+
+
+_REAL_STEP = dn.delta_step
+_REAL_ROPE = prim.rope
+_REAL_RMS = prim.rmsnorm
+_REAL_ATTEND = att.attend_one
+_REAL_PAR = dn.delta_parallel
+
+# (label, [(module, attribute), ...], replacement)
+MUTANTS = [
+    ("deltanet: alpha dropped", [(dn, "delta_step"), (om, "delta_step")], _step_no_alpha),
+    ("deltanet: S transposed", [(dn, "delta_step"), (om, "delta_step")], _step_transposed),
+    ("deltanet: read before update", [(dn, "delta_step"), (om, "delta_step")], _step_read_before_update),
+    ("deltanet: q scaled by 1/sqrt(dk)", [(dn, "delta_step"), (om, "delta_step")], _step_q_scaled),
+    ("gates: beta sign flipped", [(dn, "gates"), (om, "gates")], _gates_beta_swapped),
+    ("gates: alpha without exp", [(dn, "gates"), (om, "gates")], _gates_alpha_no_exp),
+    ("rope: interleaved pairs", [(prim, "rope"), (om, "rope")], _rope_interleaved),
+    ("rope: sine sign", [(prim, "rope"), (om, "rope")], _rope_sign),
+    ("rmsnorm: gain dropped", [(prim, "rmsnorm"), (om, "rmsnorm")], _rms_no_gain),
+    ("rmsnorm: sum instead of mean", [(prim, "rmsnorm"), (om, "rmsnorm")], _rms_no_mean),
+    ("attention: no 1/sqrt(hd)", [(att, "attend_one"), (om, "attend_one")], _attend_no_scale),
+    ("attention: interleaved GQA groups", [(att, "attend_one"), (om, "attend_one")], _attend_wrong_group),
+    ("parallel form: S0 not decayed", [(dn, "delta_parallel"), (om, "delta_parallel")], _parallel_no_s0_decay),
+]
+
+
+@pytest.mark.parametrize("label,targets,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_some_pin_catches(label, targets, repl, monkeypatch):
+    for mod, attr in targets:
+        monkeypatch.setattr(mod, attr, repl)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, np.linalg.LinAlgError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake: {label}"
