@@ -1,0 +1,688 @@
+// Host runtime behind include/mk.h: configuration checks, workspace carving, the weight loader
+// (per-tensor name/type/shape checks, then repacking into the kernel's row order), sequence state
+// management and kernel launches.  No torch types: plain pointers, sizes and a HIP stream.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int fail_global(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+struct TensorSpec {
+  std::string name;
+  std::vector<int64_t> shape;
+};
+
+bool is_attention(const mk_config& c, int l) { return l % c.period == c.attn_slot; }
+
+std::vector<TensorSpec> manifest(const mk_config& c) {
+  std::vector<TensorSpec> m;
+  const int64_t D = c.hidden, H = c.dn_heads;
+  m.push_back({"embed", {c.vocab, D}});
+  for (int l = 0; l < c.n_layers; ++l) {
+    const std::string p = "l" + std::to_string(l) + ".";
+    m.push_back({p + "norm1", {D}});
+    if (is_attention(c, l)) {
+      m.push_back({p + "attn.wq", {(int64_t)c.n_q_heads * c.head_dim, D}});
+      m.push_back({p + "attn.wk", {(int64_t)c.n_kv_heads * c.head_dim, D}});
+      m.push_back({p + "attn.wv", {(int64_t)c.n_kv_heads * c.head_dim, D}});
+      m.push_back({p + "attn.wo", {D, (int64_t)c.n_q_heads * c.head_dim}});
+    } else {
+      m.push_back({p + "dn.wqkv", {2 * H * c.dn_dk + H * c.dn_dv, D}});
+      m.push_back({p + "dn.wa", {H, D}});
+      m.push_back({p + "dn.wb", {H, D}});
+      m.push_back({p + "dn.wo", {D, H * c.dn_dv}});
+    }
+    m.push_back({p + "norm2", {D}});
+    m.push_back({p + "ffn.wg", {c.ffn, D}});
+    m.push_back({p + "ffn.wu", {c.ffn, D}});
+    m.push_back({p + "ffn.wd", {D, c.ffn}});
+  }
+  m.push_back({"final_norm", {D}});
+  return m;
+}
+
+std::string check_config(const mk_config* c) {
+  if (!c) return "config is NULL";
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->ffn <= 0 || c->vocab <= 0) return "n_layers, hidden, ffn, vocab must be > 0";
+  if (c->period <= 0 || c->attn_slot < 0 || c->attn_slot >= c->period) return "need 0 <= attn_slot < period";
+  if (c->dn_heads <= 0 || c->dn_dk <= 0 || c->dn_dv <= 0) return "DeltaNet head sizes must be > 0";
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0) return "attention head sizes must be > 0";
+  if (c->n_q_heads % c->n_kv_heads != 0) return "n_q_heads must be a multiple of n_kv_heads";
+  if (c->hidden % 8 || c->ffn % 8 || (c->dn_heads * c->dn_dv) % 8 || (c->n_q_heads * c->head_dim) % 8)
+    return "hidden, ffn, dn_heads*dn_dv and n_q_heads*head_dim must be multiples of 8";
+  if (c->dn_dk % 2 || c->dn_dv % 2 || c->head_dim % 2) return "dn_dk, dn_dv and head_dim must be even";
+  if (c->dn_dk > 256 || c->dn_dv > 256 || c->head_dim > 256) return "dn_dk, dn_dv, head_dim must be <= 256";
+  if (c->tied_embeddings != 1) return "only tied embeddings are supported";
+  if (c->weight_dtype != MK_BF16) return "weight_dtype must be MK_BF16";
+  if (c->kv_dtype != MK_F32) return "kv_dtype must be MK_F32";
+  if (c->max_ctx <= 0 || c->max_ctx > (1 << 20)) return "max_ctx must be in [1, 2^20]";
+  if (c->max_verify_k < 0) return "max_verify_k must be >= 0";
+  if (!(c->rms_eps > 0.f) || !(c->l2_eps > 0.f) || !(c->rope_theta > 0.f)) return "eps and rope_theta must be > 0";
+  if (c->hidden > 16384 || c->ffn > 65536) return "hidden <= 16384 and ffn <= 65536";
+  return "";
+}
+
+// ----------------------------------------------------------------------- workspace layout
+struct LayerOff {
+  size_t w_in, w_out, w_gu, w_down, g1, g2, S, Kc, Vc, ll_in, ll_mid, ll_o, ll_x1, ll_h, ll_x2;
+  int64_t rows_in;
+};
+
+struct Layout {
+  size_t ctl, descs, rope_cos, rope_sin, g_final, embed, ll_am, scratch, total;
+  size_t state_begin, state_end;   // DeltaNet states + KV caches (cleared by mk_reset)
+  size_t ll_begin, ll_end;         // exchange records (cleared at create)
+  std::vector<LayerOff> layers;
+  int max_items;
+};
+
+constexpr int kMaxGrid = 1024;
+
+Layout make_layout(const mk_config& c) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  const int64_t D = c.hidden, H = c.dn_heads, half = c.head_dim / 2;
+  const int gs = c.n_q_heads / c.n_kv_heads;
+  L.max_items = ((c.max_ctx + MK_ATT_CHUNK - 1) / MK_ATT_CHUNK) * c.n_kv_heads;
+  L.ctl = take(sizeof(MkCtl));
+  L.descs = take(sizeof(MkLayerDev) * c.n_layers);
+  L.rope_cos = take((size_t)c.max_ctx * half * 4);
+  L.rope_sin = take((size_t)c.max_ctx * half * 4);
+  L.g_final = take(D * 4);
+  L.embed = take((size_t)c.vocab * D * 2);
+  L.layers.resize(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerOff& lo = L.layers[l];
+    if (is_attention(c, l)) {
+      lo.rows_in = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+      lo.w_out = 0;
+    } else {
+      lo.rows_in = 2 * H * c.dn_dk + H * c.dn_dv + 2 * H;
+    }
+    lo.w_in = take((size_t)lo.rows_in * D * 2);
+    const int64_t kout = is_attention(c, l) ? (int64_t)c.n_q_heads * c.head_dim : H * c.dn_dv;
+    lo.w_out = take((size_t)D * kout * 2);
+    lo.w_gu = take((size_t)2 * c.ffn * D * 2);
+    lo.w_down = take((size_t)D * c.ffn * 2);
+    lo.g1 = take(D * 4);
+    lo.g2 = take(D * 4);
+  }
+  L.state_begin = o;
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerOff& lo = L.layers[l];
+    if (is_attention(c, l)) {
+      lo.Kc = take((size_t)c.n_kv_heads * c.max_ctx * c.head_dim * 4);
+      lo.Vc = take((size_t)c.n_kv_heads * c.max_ctx * c.head_dim * 4);
+    } else {
+      lo.S = take((size_t)H * c.dn_dv * c.dn_dk * 4);
+    }
+  }
+  L.state_end = o;
+  L.ll_begin = o;
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerOff& lo = L.layers[l];
+    lo.ll_in = take((size_t)lo.rows_in * 8);
+    if (is_attention(c, l)) {
+      lo.ll_mid = take((size_t)L.max_items * gs * (c.head_dim + 2) * 8);
+      lo.ll_o = take((size_t)c.n_q_heads * c.head_dim * 8);
+    } else {
+      lo.ll_mid = take((size_t)H * c.dn_dv * 8);
+    }
+    lo.ll_x1 = take(D * 8);
+    lo.ll_h = take((size_t)c.ffn * 8);
+    lo.ll_x2 = take(D * 8);
+  }
+  L.ll_am = take((size_t)2 * kMaxGrid * 8);
+  L.ll_end = o;
+  L.scratch = take(4096);
+  L.total = o;
+  return L;
+}
+
+// LDS carve for the decode kernel (floats)
+void lds_layout(const mk_config& c, MkDecodeParams& p) {
+  const int D = c.hidden;
+  const int gs = c.n_q_heads / c.n_kv_heads;
+  const int nch_max = (c.max_ctx + MK_ATT_CHUNK - 1) / MK_ATT_CHUNK;
+  int vec = c.ffn;
+  vec = std::max(vec, c.dn_heads * c.dn_dv);
+  vec = std::max(vec, c.n_q_heads * c.head_dim);
+  vec = std::max(vec, 2 * c.dn_dk + 2 + c.dn_dv);
+  vec = std::max(vec, gs * c.head_dim + 2 * c.head_dim + gs * MK_ATT_CHUNK + 2 * gs);
+  vec = std::max(vec, 3 * std::max(2048, nch_max) + 3 * nch_max);
+  vec = std::max(vec, 2 * kMaxGrid);
+  auto segs = [](int K) { return (K + 511) / 512; };
+  int kmax = std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), c.n_q_heads * c.head_dim);
+  const int red = std::max(256 * segs(D), 128 * segs(kmax));
+  int o = 0;
+  auto take = [&](int n) {
+    const int at = o;
+    o += (n + 3) / 4 * 4;
+    return at;
+  };
+  p.lds_x = take(D);
+  p.lds_xn = take(D);
+  p.lds_vec = take(vec);
+  p.lds_red = take(red);
+  p.lds_out = take(256);
+  p.lds_scr = take(4 * MK_NWAVE);
+  // at least 96 KB so that only one workgroup fits per compute unit
+  p.lds_floats = std::max(o, 96 * 1024 / 4);
+}
+
+}  // namespace
+
+extern "C" int mk_decode_max_blocks_per_cu(int lds_bytes);
+
+struct mk_ctx {
+  mk_config cfg;
+  int device = 0;
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  Layout lay;
+  MkDecodeParams base{};
+  int n_cu = 0;
+  int grid = 0;
+  bool loaded = false;
+  int64_t pos_host = 0;
+  std::string err;
+};
+
+namespace {
+
+int fail(mk_ctx* ctx, int code, const std::string& msg) {
+  if (ctx) ctx->err = msg;
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHK(ctx, call)                                                                     \
+  do {                                                                                        \
+    hipError_t _e = (call);                                                                   \
+    if (_e != hipSuccess)                                                                     \
+      return fail((ctx), MK_E_HIP, std::string(#call) + ": " + hipGetErrorString(_e));        \
+  } while (0)
+
+int check_tensor_list(const mk_config& c, const mk_tensor* t, int32_t n, std::string& msg,
+                      std::vector<int>* order) {
+  const std::vector<TensorSpec> man = manifest(c);
+  std::map<std::string, int> idx;
+  for (size_t i = 0; i < man.size(); ++i) idx[man[i].name] = (int)i;
+  std::vector<int> seen(man.size(), -1);
+  if (n < 0 || (n > 0 && !t)) {
+    msg = "tensor list is NULL or n < 0";
+    return MK_E_INVALID;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (!t[i].name) {
+      msg = "tensor " + std::to_string(i) + " has no name";
+      return MK_E_NAME;
+    }
+    auto it = idx.find(t[i].name);
+    if (it == idx.end()) {
+      msg = std::string("unknown tensor '") + t[i].name + "'";
+      return MK_E_NAME;
+    }
+    if (seen[it->second] >= 0) {
+      msg = std::string("tensor '") + t[i].name + "' given twice";
+      return MK_E_NAME;
+    }
+    seen[it->second] = i;
+    if (t[i].dtype != MK_BF16) {
+      msg = std::string("tensor '") + t[i].name + "' has dtype " + std::to_string(t[i].dtype) + ", expected MK_BF16";
+      return MK_E_DTYPE;
+    }
+    const TensorSpec& sp = man[it->second];
+    bool same = (int)sp.shape.size() == t[i].ndim;
+    for (size_t d = 0; same && d < sp.shape.size(); ++d) same = (t[i].shape[d] == sp.shape[d]);
+    if (!same) {
+      std::string want = "[", got = "[";
+      for (size_t d = 0; d < sp.shape.size(); ++d) want += (d ? ", " : "") + std::to_string(sp.shape[d]);
+      for (int d = 0; d < t[i].ndim && d < 4; ++d) got += (d ? ", " : "") + std::to_string(t[i].shape[d]);
+      msg = std::string("tensor '") + t[i].name + "' has shape " + got + "], expected " + want + "]";
+      return MK_E_SHAPE;
+    }
+    if (!t[i].data) {
+      msg = std::string("tensor '") + t[i].name + "' has no data";
+      return MK_E_INVALID;
+    }
+  }
+  for (size_t i = 0; i < man.size(); ++i)
+    if (seen[i] < 0) {
+      msg = "missing tensor '" + man[i].name + "'";
+      return MK_E_NAME;
+    }
+  if (order) *order = seen;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mk_workspace_bytes(const mk_config* cfg) {
+  const std::string e = check_config(cfg);
+  if (!e.empty()) {
+    g_err = e;
+    return 0;
+  }
+  return make_layout(*cfg).total;
+}
+
+int mk_check_tensors(const mk_config* cfg, const mk_tensor* tensors, int32_t n) {
+  const std::string e = check_config(cfg);
+  if (!e.empty()) return fail_global(MK_E_INVALID, e);
+  std::string msg;
+  const int rc = check_tensor_list(*cfg, tensors, n, msg, nullptr);
+  if (rc != MK_OK) g_err = msg;
+  return rc;
+}
+
+const char* mk_last_error(const mk_ctx* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t workspace_bytes, void* hip_stream,
+              mk_ctx** out) {
+  if (!out) return fail_global(MK_E_INVALID, "out is NULL");
+  *out = nullptr;
+  const std::string e = check_config(cfg);
+  if (!e.empty()) return fail_global(MK_E_INVALID, e);
+  const Layout lay = make_layout(*cfg);
+  if (!d_workspace) return fail_global(MK_E_INVALID, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256) return fail_global(MK_E_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail_global(MK_E_INVALID, "workspace too small: need " + std::to_string(lay.total) + " bytes");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail_global(MK_E_NO_DEVICE, "no HIP device");
+  if (device < 0 || device >= ndev) return fail_global(MK_E_NO_DEVICE, "device index out of range");
+  if (hipSetDevice(device) != hipSuccess) return fail_global(MK_E_NO_DEVICE, "hipSetDevice failed");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return fail_global(MK_E_HIP, "hipGetDeviceProperties failed");
+  hipPointerAttribute_t pa;
+  if (hipPointerGetAttributes(&pa, d_workspace) != hipSuccess || pa.type != hipMemoryTypeDevice || pa.device != device)
+    return fail_global(MK_E_INVALID, "workspace is not device memory of the given device");
+
+  mk_ctx* ctx = new mk_ctx();
+  ctx->cfg = *cfg;
+  ctx->device = device;
+  ctx->stream = (hipStream_t)hip_stream;
+  ctx->ws = (char*)d_workspace;
+  ctx->ws_bytes = workspace_bytes;
+  ctx->lay = lay;
+  ctx->n_cu = prop.multiProcessorCount;
+  ctx->grid = std::min(ctx->n_cu, kMaxGrid);
+
+  MkDecodeParams& p = ctx->base;
+  p.n_layers = cfg->n_layers;
+  p.D = cfg->hidden;
+  p.ffn = cfg->ffn;
+  p.vocab = cfg->vocab;
+  p.H = cfg->dn_heads;
+  p.dk = cfg->dn_dk;
+  p.dv = cfg->dn_dv;
+  p.nq = cfg->n_q_heads;
+  p.nkv = cfg->n_kv_heads;
+  p.hd = cfg->head_dim;
+  p.max_ctx = cfg->max_ctx;
+  p.max_items = lay.max_items;
+  p.rms_eps = cfg->rms_eps;
+  p.l2_eps = cfg->l2_eps;
+  p.layers = (const MkLayerDev*)(ctx->ws + lay.descs);
+  p.embed = (const uint16_t*)(ctx->ws + lay.embed);
+  p.g_final = (const float*)(ctx->ws + lay.g_final);
+  p.rope_cos = (const float*)(ctx->ws + lay.rope_cos);
+  p.rope_sin = (const float*)(ctx->ws + lay.rope_sin);
+  p.ctl = (MkCtl*)(ctx->ws + lay.ctl);
+  p.ll_am = (mk_u64*)(ctx->ws + lay.ll_am);
+  lds_layout(*cfg, p);
+
+  const int lds_bytes = p.lds_floats * 4;
+  if (lds_bytes > (int)prop.sharedMemPerBlock || mk_decode_max_blocks_per_cu(lds_bytes) < 1) {
+    const std::string m = "decode kernel needs " + std::to_string(lds_bytes) + " B of LDS; device offers " +
+                          std::to_string(prop.sharedMemPerBlock);
+    delete ctx;
+    return fail_global(MK_E_OCCUPANCY, m);
+  }
+
+  // per-layer descriptors
+  std::vector<MkLayerDev> descs(cfg->n_layers);
+  int kvi = 0;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const LayerOff& lo = lay.layers[l];
+    MkLayerDev& d = descs[l];
+    std::memset(&d, 0, sizeof(d));
+    d.kind = is_attention(*cfg, l) ? MK_LAYER_ATT : MK_LAYER_DN;
+    d.kv_index = d.kind == MK_LAYER_ATT ? kvi++ : -1;
+    d.w_in = (const uint16_t*)(ctx->ws + lo.w_in);
+    d.w_out = (const uint16_t*)(ctx->ws + lo.w_out);
+    d.w_gu = (const uint16_t*)(ctx->ws + lo.w_gu);
+    d.w_down = (const uint16_t*)(ctx->ws + lo.w_down);
+    d.g1 = (const float*)(ctx->ws + lo.g1);
+    d.g2 = (const float*)(ctx->ws + lo.g2);
+    if (d.kind == MK_LAYER_ATT) {
+      d.Kc = (float*)(ctx->ws + lo.Kc);
+      d.Vc = (float*)(ctx->ws + lo.Vc);
+      d.ll_o = (mk_u64*)(ctx->ws + lo.ll_o);
+    } else {
+      d.S = (float*)(ctx->ws + lo.S);
+    }
+    d.ll_in = (mk_u64*)(ctx->ws + lo.ll_in);
+    d.ll_mid = (mk_u64*)(ctx->ws + lo.ll_mid);
+    d.ll_x1 = (mk_u64*)(ctx->ws + lo.ll_x1);
+    d.ll_h = (mk_u64*)(ctx->ws + lo.ll_h);
+    d.ll_x2 = (mk_u64*)(ctx->ws + lo.ll_x2);
+  }
+  // RoPE tables: angle = pos * theta^(-2i/hd), evaluated in double, stored as float
+  const int half = cfg->head_dim / 2;
+  std::vector<float> cs((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
+  for (int pos = 0; pos < cfg->max_ctx; ++pos)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+      const double a = pos * inv;
+      cs[(size_t)pos * half + i] = (float)std::cos(a);
+      sn[(size_t)pos * half + i] = (float)std::sin(a);
+    }
+  int rc = MK_OK;
+  auto hip_ok = [&](hipError_t er, const char* what) {
+    if (er != hipSuccess && rc == MK_OK) {
+      rc = MK_E_HIP;
+      g_err = std::string(what) + ": " + hipGetErrorString(er);
+    }
+  };
+  hip_ok(hipMemcpyAsync(ctx->ws + lay.descs, descs.data(), sizeof(MkLayerDev) * descs.size(), hipMemcpyHostToDevice,
+                        ctx->stream), "copy layer descriptors");
+  hip_ok(hipMemcpyAsync(ctx->ws + lay.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, ctx->stream),
+         "copy rope cos");
+  hip_ok(hipMemcpyAsync(ctx->ws + lay.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, ctx->stream),
+         "copy rope sin");
+  if (rc == MK_OK && mk_launch_zero(ctx->ws + lay.ctl, sizeof(MkCtl), ctx->stream)) rc = MK_E_HIP;
+  if (rc == MK_OK && mk_launch_zero(ctx->ws + lay.state_begin, lay.state_end - lay.state_begin, ctx->stream)) rc = MK_E_HIP;
+  if (rc == MK_OK && mk_launch_zero(ctx->ws + lay.ll_begin, lay.ll_end - lay.ll_begin, ctx->stream)) rc = MK_E_HIP;
+  if (rc == MK_OK && mk_launch_set_ctl(p.ctl, 0, 1, ctx->stream)) rc = MK_E_HIP;
+  if (rc == MK_OK) hip_ok(hipStreamSynchronize(ctx->stream), "synchronise after create");
+  if (rc != MK_OK) {
+    if (g_err.empty()) g_err = "kernel launch failed during create";
+    delete ctx;
+    return rc;
+  }
+  *out = ctx;
+  return MK_OK;
+}
+
+void mk_destroy(mk_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipStreamSynchronize(ctx->stream);
+  delete ctx;
+}
+
+int mk_set_grid(mk_ctx* ctx, int32_t n) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  if (n < 1 || n > ctx->n_cu || n > kMaxGrid)
+    return fail(ctx, MK_E_INVALID, "grid must be in [1, " + std::to_string(std::min(ctx->n_cu, kMaxGrid)) + "]");
+  ctx->grid = n;
+  return MK_OK;
+}
+
+int mk_get_grid(const mk_ctx* ctx, int32_t* n) {
+  if (!ctx || !n) return fail_global(MK_E_INVALID, "NULL argument");
+  *n = ctx->grid;
+  return MK_OK;
+}
+
+int mk_reset(mk_ctx* ctx) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  const Layout& lay = ctx->lay;
+  if (mk_launch_zero(ctx->ws + lay.state_begin, lay.state_end - lay.state_begin, ctx->stream))
+    return fail(ctx, MK_E_HIP, "zero state launch failed");
+  if (mk_launch_set_ctl(ctx->base.ctl, 0, 1, ctx->stream)) return fail(ctx, MK_E_HIP, "set position launch failed");
+  ctx->pos_host = 0;
+  return MK_OK;
+}
+
+int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  const mk_config& c = ctx->cfg;
+  std::string msg;
+  std::vector<int> order;
+  int rc = check_tensor_list(c, t, n, msg, &order);
+  if (rc != MK_OK) return fail(ctx, rc, msg);
+  HIPCHK(ctx, hipSetDevice(ctx->device));
+  const std::vector<TensorSpec> man = manifest(c);
+  // stage host tensors through one device buffer sized for the largest tensor
+  size_t max_bytes = 0;
+  for (size_t i = 0; i < man.size(); ++i) {
+    size_t b = 2;
+    for (int64_t d : man[i].shape) b *= (size_t)d;
+    max_bytes = std::max(max_bytes, b);
+  }
+  void* stage = nullptr;
+  int32_t* d_perm = nullptr;
+  HIPCHK(ctx, hipMalloc(&stage, max_bytes));
+  int64_t max_rows = std::max<int64_t>(2 * (int64_t)c.ffn, (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim);
+  if (hipMalloc(&d_perm, max_rows * 4) != hipSuccess) {
+    (void)hipFree(stage);
+    return fail(ctx, MK_E_HIP, "hipMalloc permutation buffer failed");
+  }
+  const Layout& lay = ctx->lay;
+  auto src_of = [&](const mk_tensor& tt, size_t bytes, const void** out) -> int {
+    if (tt.on_device) {
+      *out = tt.data;
+      return MK_OK;
+    }
+    if (hipMemcpyAsync(stage, tt.data, bytes, hipMemcpyHostToDevice, ctx->stream) != hipSuccess) return MK_E_HIP;
+    *out = stage;
+    return MK_OK;
+  };
+  auto tensor = [&](const std::string& name) -> const mk_tensor& {
+    for (size_t i = 0; i < man.size(); ++i)
+      if (man[i].name == name) return t[order[i]];
+    return t[0];  // unreachable: the list was checked
+  };
+  auto copy_plain = [&](const std::string& name, size_t dst_off) -> int {
+    const mk_tensor& tt = tensor(name);
+    size_t bytes = 2;
+    for (int d = 0; d < tt.ndim; ++d) bytes *= (size_t)tt.shape[d];
+    if (tt.on_device)
+      return hipMemcpyAsync(ctx->ws + dst_off, tt.data, bytes, hipMemcpyDeviceToDevice, ctx->stream) == hipSuccess
+                 ? MK_OK : MK_E_HIP;
+    return hipMemcpyAsync(ctx->ws + dst_off, tt.data, bytes, hipMemcpyHostToDevice, ctx->stream) == hipSuccess
+               ? MK_OK : MK_E_HIP;
+  };
+  auto copy_gain = [&](const std::string& name, size_t dst_off) -> int {
+    const mk_tensor& tt = tensor(name);
+    const void* src = nullptr;
+    const size_t bytes = (size_t)tt.shape[0] * 2;
+    if (src_of(tt, bytes, &src)) return MK_E_HIP;
+    return mk_launch_bf16_to_f32((const uint16_t*)src, (float*)(ctx->ws + dst_off), tt.shape[0], ctx->stream) ? MK_E_HIP
+                                                                                                            : MK_OK;
+  };
+  // rows of `name` go to dst rows perm[r] (dst is a matrix with the same row length)
+  auto copy_perm = [&](const std::string& name, size_t dst_off, const std::vector<int32_t>& perm) -> int {
+    const mk_tensor& tt = tensor(name);
+    const int64_t rows = tt.shape[0], cols = tt.shape[1];
+    const void* src = nullptr;
+    if (src_of(tt, (size_t)rows * cols * 2, &src)) return MK_E_HIP;
+    if (hipMemcpyAsync(d_perm, perm.data(), rows * 4, hipMemcpyHostToDevice, ctx->stream) != hipSuccess) return MK_E_HIP;
+    if (mk_launch_permute_rows((const uint16_t*)src, (uint16_t*)(ctx->ws + dst_off), d_perm, rows, cols, ctx->stream))
+      return MK_E_HIP;
+    // the staging buffers are reused by the next tensor
+    return hipStreamSynchronize(ctx->stream) == hipSuccess ? MK_OK : MK_E_HIP;
+  };
+
+  const int64_t D = c.hidden, H = c.dn_heads;
+  const int hd = c.head_dim, half = hd / 2;
+  rc = copy_plain("embed", lay.embed);
+  if (!rc) rc = copy_gain("final_norm", lay.g_final);
+  for (int l = 0; l < c.n_layers && !rc; ++l) {
+    const LayerOff& lo = lay.layers[l];
+    const std::string p = "l" + std::to_string(l) + ".";
+    rc = copy_gain(p + "norm1", lo.g1);
+    if (!rc) rc = copy_gain(p + "norm2", lo.g2);
+    if (rc) break;
+    if (is_attention(c, l)) {
+      // rows of every head in RoPE pair order: (0, hd/2, 1, hd/2 + 1, ...)
+      auto pair_perm = [&](int heads) {
+        std::vector<int32_t> pm((size_t)heads * hd);
+        for (int h = 0; h < heads; ++h)
+          for (int d = 0; d < hd; ++d) pm[(size_t)h * hd + d] = h * hd + 2 * (d % half) + d / half;
+        return pm;
+      };
+      rc = copy_perm(p + "attn.wq", lo.w_in, pair_perm(c.n_q_heads));
+      if (!rc) rc = copy_perm(p + "attn.wk", lo.w_in + (size_t)c.n_q_heads * hd * D * 2, pair_perm(c.n_kv_heads));
+      if (!rc)
+        rc = copy_perm(p + "attn.wv", lo.w_in + (size_t)(c.n_q_heads + c.n_kv_heads) * hd * D * 2,
+                       pair_perm(c.n_kv_heads));
+      if (!rc) rc = copy_plain(p + "attn.wo", lo.w_out);
+    } else {
+      const int64_t nqkv = 2 * H * c.dn_dk + H * c.dn_dv;
+      rc = copy_plain(p + "dn.wqkv", lo.w_in);
+      if (!rc) rc = copy_plain(p + "dn.wa", lo.w_in + (size_t)nqkv * D * 2);
+      if (!rc) rc = copy_plain(p + "dn.wb", lo.w_in + (size_t)(nqkv + H) * D * 2);
+      if (!rc) rc = copy_plain(p + "dn.wo", lo.w_out);
+    }
+    if (rc) break;
+    std::vector<int32_t> pg(c.ffn), pu(c.ffn);
+    for (int j = 0; j < c.ffn; ++j) {
+      pg[j] = 2 * j;
+      pu[j] = 2 * j + 1;
+    }
+    rc = copy_perm(p + "ffn.wg", lo.w_gu, pg);
+    if (!rc) rc = copy_perm(p + "ffn.wu", lo.w_gu, pu);
+    if (!rc) rc = copy_plain(p + "ffn.wd", lo.w_down);
+  }
+  const hipError_t se = hipStreamSynchronize(ctx->stream);
+  (void)hipFree(stage);
+  (void)hipFree(d_perm);
+  if (rc) return fail(ctx, rc, "copying weights failed");
+  if (se != hipSuccess) return fail(ctx, MK_E_HIP, std::string("weight copy: ") + hipGetErrorString(se));
+  ctx->loaded = true;
+  rc = mk_reset(ctx);
+  if (rc) return rc;
+  // warm-up launch (the output is discarded), then back to position 0
+  int32_t* scratch_tok = (int32_t*)(ctx->ws + lay.scratch);
+  HIPCHK(ctx, hipMemsetAsync(scratch_tok, 0, 64, ctx->stream));
+  rc = mk_decode_step(ctx, scratch_tok, scratch_tok + 1, nullptr);
+  if (rc) return rc;
+  rc = mk_sync(ctx);
+  if (rc) return rc;
+  return mk_reset(ctx);
+}
+
+int mk_decode_step(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_logits) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
+  if (!d_tok || !d_next) return fail(ctx, MK_E_INVALID, "d_tok and d_next are required");
+  if (ctx->pos_host + 1 > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "context is full");
+  MkDecodeParams p = ctx->base;
+  p.tok = d_tok;
+  p.next = d_next;
+  p.logits = d_logits;
+  if (mk_launch_decode(&p, ctx->grid, ctx->stream)) return fail(ctx, MK_E_HIP, "decode launch failed");
+  ctx->pos_host += 1;
+  return MK_OK;
+}
+
+int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next, float* d_logits) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
+  if (!d_tokens || !d_next || n <= 0) return fail(ctx, MK_E_INVALID, "need d_tokens, d_next and n > 0");
+  if (ctx->pos_host + n > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "prompt does not fit the context");
+  int32_t* scratch_tok = (int32_t*)(ctx->ws + ctx->lay.scratch) + 8;
+  for (int32_t i = 0; i < n; ++i) {
+    const bool last = (i == n - 1);
+    const int rc = mk_decode_step(ctx, d_tokens + i, last ? d_next : scratch_tok, last ? d_logits : nullptr);
+    if (rc) return rc;
+  }
+  return MK_OK;
+}
+
+int mk_verify_k(mk_ctx* ctx, const int32_t*, int32_t, int32_t*, int32_t*) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  return fail(ctx, MK_E_UNSUPPORTED, "speculative verify is not built");
+}
+
+int mk_sync(mk_ctx* ctx) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
+  MkCtl ctl;
+  HIPCHK(ctx, hipMemcpy(&ctl, ctx->base.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
+  if (ctl.err) {
+    // clear the flag so that the next launch starts clean; the sequence state is undefined now
+    if (mk_launch_set_ctl(ctx->base.ctl, -1, 1, ctx->stream) == 0) (void)hipStreamSynchronize(ctx->stream);
+    if (ctl.err == 2u)
+      return fail(ctx, MK_E_INVALID, "a decode launch saw a token id outside [0, vocab) or a full context; call mk_reset");
+    return fail(ctx, MK_E_DEVICE_TIMEOUT, "a grid-wide wait inside the decode kernel gave up; call mk_reset");
+  }
+  return MK_OK;
+}
+
+int mk_get_position(mk_ctx* ctx, int32_t* pos) {
+  if (!ctx || !pos) return fail_global(MK_E_INVALID, "NULL argument");
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
+  MkCtl ctl;
+  HIPCHK(ctx, hipMemcpy(&ctl, ctx->base.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
+  *pos = ctl.pos;
+  return MK_OK;
+}
+
+size_t mk_state_bytes(const mk_ctx* ctx, int32_t layer) {
+  if (!ctx || layer < 0 || layer >= ctx->cfg.n_layers) return 0;
+  const mk_config& c = ctx->cfg;
+  if (is_attention(c, layer)) return (size_t)2 * c.n_kv_heads * c.max_ctx * c.head_dim * 4;
+  return (size_t)c.dn_heads * c.dn_dv * c.dn_dk * 4;
+}
+
+int mk_read_state(mk_ctx* ctx, int32_t layer, void* dst) {
+  if (!ctx || !dst) return fail_global(MK_E_INVALID, "NULL argument");
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return fail(ctx, MK_E_INVALID, "layer out of range");
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
+  const LayerOff& lo = ctx->lay.layers[layer];
+  const size_t b = mk_state_bytes(ctx, layer);
+  if (is_attention(ctx->cfg, layer)) {
+    HIPCHK(ctx, hipMemcpy(dst, ctx->ws + lo.Kc, b / 2, hipMemcpyDeviceToHost));
+    HIPCHK(ctx, hipMemcpy((char*)dst + b / 2, ctx->ws + lo.Vc, b / 2, hipMemcpyDeviceToHost));
+  } else {
+    HIPCHK(ctx, hipMemcpy(dst, ctx->ws + lo.S, b, hipMemcpyDeviceToHost));
+  }
+  return MK_OK;
+}
+
+int mk_write_state(mk_ctx* ctx, int32_t layer, const void* src) {
+  if (!ctx || !src) return fail_global(MK_E_INVALID, "NULL argument");
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return fail(ctx, MK_E_INVALID, "layer out of range");
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
+  const LayerOff& lo = ctx->lay.layers[layer];
+  const size_t b = mk_state_bytes(ctx, layer);
+  if (is_attention(ctx->cfg, layer)) {
+    HIPCHK(ctx, hipMemcpy(ctx->ws + lo.Kc, src, b / 2, hipMemcpyHostToDevice));
+    HIPCHK(ctx, hipMemcpy(ctx->ws + lo.Vc, (const char*)src + b / 2, b / 2, hipMemcpyHostToDevice));
+  } else {
+    HIPCHK(ctx, hipMemcpy(ctx->ws + lo.S, src, b, hipMemcpyHostToDevice));
+  }
+  return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+/*
+ * mk.h -- C ABI of the batch-1 decode megakernel for a hybrid Gated-DeltaNet + full-attention
+ * decoder on AMD Instinct MI355X (gfx950).
+ *
+ * The model is the hybrid the luce-megakernel announcement runs as one kernel launch (page 1:
+ * 24 layers, 18 DeltaNet layers with a learned linear recurrence and 6 standard attention
+ * layers; BF16 weights with FP32 accumulation; the DeltaNet recurrence kept in FP32 registers;
+ * QKV, RoPE, causal softmax and output projection fused; a grid-wide sync in place of kernel
+ * boundaries).  Layer l is attention when l % period == attn_slot, DeltaNet otherwise; blocks
+ * are pre-norm residual with a SwiGLU FFN, and the input embedding doubles as the LM head.
+ *
+ * Conventions for every entry point:
+ *  - Every call returns an int status (MK_OK == 0, negative on error).  Nothing aborts and no
+ *    C++ exception crosses the ABI.  mk_last_error() describes the last failure.
+ *  - Pointers named d_* are device pointers (HIP device memory of the ctx's device); pointers
+ *    without the prefix are host pointers.  The library keeps no pointer past the call that
+ *    received it, except the workspace given to mk_create.
+ *  - Prefill, decode and verify are enqueued on the ctx's stream and return without waiting;
+ *    their outputs are written to caller-owned device buffers.  mk_sync waits for them.
+ *  - A ctx is bound to one device and one stream and is not thread-safe.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mk_ctx mk_ctx;
+
+enum mk_status {
+  MK_OK = 0,
+  MK_E_INVALID = -1,        /* bad argument or configuration field */
+  MK_E_SHAPE = -2,          /* tensor shape differs from the model's */
+  MK_E_DTYPE = -3,          /* tensor element type differs from the model's */
+  MK_E_NAME = -4,           /* unknown, duplicated or missing tensor name */
+  MK_E_ORDER = -5,          /* call made in the wrong state (e.g. decode before weights) */
+  MK_E_CTX_FULL = -6,       /* the step would pass max_ctx positions */
+  MK_E_NO_DEVICE = -7,      /* no usable HIP device */
+  MK_E_OCCUPANCY = -8,      /* the persistent grid cannot be co-resident on the device */
+  MK_E_HIP = -9,            /* a HIP runtime call failed */
+  MK_E_DEVICE_TIMEOUT = -10,/* a grid-wide wait inside a kernel gave up (bounded spin) */
+  MK_E_UNSUPPORTED = -11    /* valid request this build does not implement */
+};
+
+enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4 };
+
+/* Model shape.  All fields are required (there is no default constructor on purpose).
+ * Constraints checked by mk_workspace_bytes / mk_create: every size > 0; hidden, ffn, H*dk and
+ * H*dv multiples of 8; dk, dv, head_dim even and <= 256; n_q_heads a multiple of n_kv_heads;
+ * attn_slot < period; tied_embeddings == 1; weight_dtype == MK_BF16; kv_dtype == MK_F32. */
+typedef struct {
+  int32_t n_layers, hidden, ffn, vocab;
+  int32_t period, attn_slot;                       /* attention layers: l % period == attn_slot */
+  int32_t dn_heads, dn_dk, dn_dv;                  /* DeltaNet heads and key/value head sizes   */
+  int32_t n_q_heads, n_kv_heads, head_dim;         /* grouped-query attention                   */
+  int32_t tied_embeddings, weight_dtype, kv_dtype;
+  int32_t max_ctx;                                 /* positions the KV cache holds              */
+  int32_t max_verify_k;                            /* drafts per mk_verify_k call (0 = none)    */
+  float rms_eps, l2_eps, rope_theta;
+} mk_config;
+
+/* One weight tensor for mk_load_weights.  name follows the model's manifest:
+ *   embed [vocab, hidden]; per layer l: l{l}.norm1 [hidden], l{l}.norm2 [hidden],
+ *   DeltaNet:  l{l}.dn.wqkv [2*H*dk + H*dv, hidden] (q heads, k heads, v heads), l{l}.dn.wa [H, hidden],
+ *              l{l}.dn.wb [H, hidden], l{l}.dn.wo [hidden, H*dv];
+ *   attention: l{l}.attn.wq [nq*hd, hidden], l{l}.attn.wk [nkv*hd, hidden], l{l}.attn.wv [nkv*hd, hidden],
+ *              l{l}.attn.wo [hidden, nq*hd];
+ *   FFN:       l{l}.ffn.wg [ffn, hidden], l{l}.ffn.wu [ffn, hidden], l{l}.ffn.wd [hidden, ffn];
+ *   final_norm [hidden].
+ * Row-major [out][in], contiguous.  data is a host pointer when on_device == 0, else a device
+ * pointer on the ctx's device. */
+typedef struct {
+  const char* name;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[4];
+  const void* data;
+  int32_t on_device;
+} mk_tensor;
+
+/* Device bytes the caller must provide to mk_create for this configuration (weights, DeltaNet
+ * state, KV cache and the kernel's exchange buffers).  Returns 0 for an invalid configuration
+ * (mk_last_error(NULL) says why).  Needs no device. */
+size_t mk_workspace_bytes(const mk_config* cfg);
+
+/* Bind a context to `device`, the caller-owned workspace (>= mk_workspace_bytes, 256-byte
+ * aligned, must outlive the ctx) and a HIP stream (hipStream_t, NULL = the default stream).
+ * Validates cfg before touching the device.  Errors: MK_E_INVALID, MK_E_NO_DEVICE,
+ * MK_E_OCCUPANCY, MK_E_HIP.  On error *out is NULL and mk_last_error(NULL) holds the message. */
+int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t workspace_bytes,
+              void* hip_stream, mk_ctx** out);
+
+/* Copy all model tensors into the workspace in the kernel's layout.  Every manifest name must
+ * appear exactly once with dtype MK_BF16 and the manifest shape; the whole list is checked
+ * before anything is copied (MK_E_NAME / MK_E_DTYPE / MK_E_SHAPE name the offending tensor).
+ * Then resets the sequence state and runs one warm-up launch.  Synchronous. */
+int mk_load_weights(mk_ctx* ctx, const mk_tensor* tensors, int32_t n);
+
+/* Same checks as mk_load_weights, for a configuration alone; needs no device or context. */
+int mk_check_tensors(const mk_config* cfg, const mk_tensor* tensors, int32_t n);
+
+/* Process n prompt tokens d_tokens[0..n) starting at the current position; writes the greedy
+ * next token (argmax of the last position's logits, lowest index on ties) to d_next[0] and, if
+ * d_logits != NULL, that position's logits [vocab] as FP32.  Advances the position by n.
+ * Errors: MK_E_ORDER (no weights), MK_E_INVALID (n <= 0 or null pointers), MK_E_CTX_FULL. */
+int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next, float* d_logits);
+
+/* One decode step as ONE kernel launch: embeds d_tok[0] at the current position, runs every
+ * layer, writes the greedy next token to d_next[0] (may alias d_tok) and optional FP32 logits
+ * [vocab]; advances the position by one on the device.  Errors: MK_E_ORDER, MK_E_INVALID,
+ * MK_E_CTX_FULL (checked against the host's count of enqueued positions). */
+int mk_decode_step(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_logits);
+
+/* Speculative verify: score [pending, d1..dk] (d_tokens[0..k]) and accept the longest prefix of
+ * drafts that equals the greedy choices.  Not built yet: returns MK_E_UNSUPPORTED. */
+int mk_verify_k(mk_ctx* ctx, const int32_t* d_tokens, int32_t k, int32_t* d_out, int32_t* d_n_accepted);
+
+/* Position 0, zero DeltaNet states and KV cache (weights kept).  Enqueued on the stream. */
+int mk_reset(mk_ctx* ctx);
+
+/* Wait for the stream; returns MK_E_DEVICE_TIMEOUT if a kernel reported a failed grid wait. */
+int mk_sync(mk_ctx* ctx);
+
+/* Current position as the device holds it (synchronises). */
+int mk_get_position(mk_ctx* ctx, int32_t* pos);
+
+/* Copy one layer's recurrent state to/from host memory (synchronises).  DeltaNet layer: S as
+ * FP32 [dn_heads][dn_dv][dn_dk] (row i of head h maps keys to value dimension i).  Attention
+ * layer: K then V as FP32 [n_kv_heads][max_ctx][head_dim] each (keys already rotated).
+ * mk_state_bytes gives the byte count for `layer`, or 0 if it is out of range. */
+size_t mk_state_bytes(const mk_ctx* ctx, int32_t layer);
+int mk_read_state(mk_ctx* ctx, int32_t layer, void* dst);
+int mk_write_state(mk_ctx* ctx, int32_t layer, const void* src);
+
+/* Number of workgroups of the persistent grid (default: one per compute unit).  Results are
+ * bitwise identical for every grid size; smaller grids exist for that check and for tuning.
+ * Errors: MK_E_INVALID (n < 1 or more than the device's compute units). */
+int mk_set_grid(mk_ctx* ctx, int32_t n_workgroups);
+int mk_get_grid(const mk_ctx* ctx, int32_t* n_workgroups);
+
+/* Message for the last failed call on ctx; ctx == NULL gives the calling thread's message from
+ * a failed mk_workspace_bytes / mk_create / mk_check_tensors. */
+const char* mk_last_error(const mk_ctx* ctx);
+
+void mk_destroy(mk_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H */

@@ -1,0 +1,53 @@
+"""Shared helpers of the GPU tests: run the HIP library and the oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+
+
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device")
+    return torch
+
+
+def new_model(cfg, weights, grid=None):
+    from hybrid_deltanet_attention_amd import Model
+    m = Model(cfg, device=0)
+    m.mk_load_weights(weights)
+    if grid is not None:
+        m.mk_set_grid(grid)
+    return m
+
+
+def run_teacher_forced(m, prompt, fed, want_logits=True):
+    """mk_prefill(prompt) then one mk_decode_step per token in ``fed`` (the oracle's tokens).
+
+    Returns (prefill logits, prefill next token, [decode logits], [decode next tokens])."""
+    torch = torch_cuda()
+    vocab = m.cfg.vocab
+    d_prompt = torch.tensor(np.asarray(prompt, dtype=np.int32), device="cuda")
+    d_next = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_logits = torch.empty(vocab, dtype=torch.float32, device="cuda") if want_logits else None
+    m.mk_prefill(d_prompt, len(prompt), d_next, d_logits)
+    m.mk_sync()
+    pre_logits = d_logits.cpu().numpy().copy() if want_logits else None
+    pre_next = int(d_next.item())
+    d_fed = torch.tensor(np.asarray(fed, dtype=np.int32), device="cuda")
+    out_l, out_n = [], []
+    for t in range(len(fed)):
+        m.mk_decode_step(d_fed[t:t + 1], d_next, d_logits)
+        if want_logits:
+            out_l.append(d_logits.cpu().numpy().copy())
+        out_n.append(int(d_next.item()))
+    m.mk_sync()
+    return pre_logits, pre_next, out_l, out_n
+
+
+def oracle_reference(cfg, weights, prompt, n_steps):
+    from oracle import Oracle
+    o = Oracle(cfg, weights)
+    fed, logits, last = o.greedy(prompt, n_steps)
+    return o, fed, logits, last
