@@ -1,0 +1,192 @@
+"""Benchmark: batch-1 decode of the 0.8B-shaped hybrid (one kernel launch per token) and pp520 prefill.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (synthetic, seeded): the 0.8B-shaped hybrid -- 24 layers in a 3 DeltaNet : 1 attention
+pattern, hidden 1024, 16 DeltaNet heads of 128, 8 Q / 2 KV attention heads of 128, SwiGLU 3584,
+vocabulary 151936 tied -- with BF16 weights ~N(0, 0.02) from seed 0 and a 512-token uniform
+random prompt.  After the prompt, W untimed decode steps, then K timed decode steps, each one
+launch of the decode kernel with the token fed back on the device.  The pages time the same
+shapes (pp520, tg128) on a real checkpoint and real text (luce-megakernel announcement, page 1,
+results table); random ids and random weights stand in for them here.
+
+Prints ONE JSON line.  ``value`` is decode tokens/s on the one GPU.  ``roofline`` prices the
+decode kernel's algorithmic bytes per launch (weights + LM head + DeltaNet state read and write +
+KV cache) against the 8 TB/s HBM peak, using the kernel's average duration measured with events
+on the stream it is launched on.  ``cpu_baseline`` times the CPU oracle (fp64, token by token) on
+a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+PROMPT = 512
+PP = 520
+SEED = 0
+
+
+def algorithmic_bytes(cfg, L: int) -> dict:
+    """Bytes one decode launch must move at context length L (positions 0..L-1 visible)."""
+    D, H = cfg.hidden, cfg.dn_heads
+    w = 0
+    state = 0
+    kv = 0
+    for l in range(cfg.n_layers):
+        if cfg.is_attention(l):
+            rows_in = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+            kout = cfg.n_q_heads * cfg.head_dim
+            kv += 2 * cfg.n_kv_heads * cfg.head_dim * 4 * L  # K and V: L-1 positions read, 1 written
+        else:
+            rows_in = 2 * H * cfg.dn_dk + H * cfg.dn_dv + 2 * H
+            kout = H * cfg.dn_dv
+            state += 2 * H * cfg.dn_dv * cfg.dn_dk * 4       # read + write
+        w += 2 * (rows_in * D + D * kout + 3 * cfg.ffn * D) + 2 * 4 * D
+    head = 2 * cfg.vocab * D + 4 * D + 2 * D                 # tied LM head, final gain, embedding row
+    return {"weights": w, "lm_head": head, "state": state, "kv": kv, "total": w + head + state + kv}
+
+
+def cpu_baseline(cfg, W, n_prompt=32, n_steps=6) -> dict:
+    """The oracle as it stands (fp64 NumPy), token-by-token decode on a bounded sample."""
+    from oracle import Oracle
+    import synth
+    t0 = time.perf_counter()
+    o = Oracle(cfg, W)
+    t_load = time.perf_counter() - t0
+    prompt = synth.make_prompt(cfg.vocab, n_prompt, SEED)
+    fwd = o.forward(prompt, logits="last")
+    o.load_state(fwd)
+    tok = int(np.argmax(fwd["logits"]))
+    t1 = time.perf_counter()
+    for _ in range(n_steps):
+        tok = int(np.argmax(o.step(tok)))
+    dt = time.perf_counter() - t1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    return {"value": n_steps / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_steps} fp64 token-by-token decode steps after a {n_prompt}-token prompt "
+                      f"(whole-sequence form), 0.8B shape; weight decode to fp64 took {t_load:.1f} s "
+                      f"(not timed); host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", default="hybrid_0p8b")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the decode path is batch-1 on a single device and "
+              "this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from hybrid_deltanet_attention_amd import Model
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    cfg = synth.get_config(args.config)
+    assert PROMPT + args.warmup + args.steps <= cfg.max_ctx and PP + 1 <= cfg.max_ctx
+    print(f"[bench] generating {cfg.name} weights (seed {SEED})", file=sys.stderr, flush=True)
+    W = synth.make_weights(cfg, SEED)
+    m = Model(cfg, device=0)
+    m.mk_load_weights(W)
+    stream = m.stream
+    dev = torch.device("cuda:0")
+    prompt = torch.tensor(synth.make_prompt(cfg.vocab, PP, SEED), device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # ---- prefill pp520 (fresh context each time), median of 3 after one warm run
+    pp_times = []
+    for r in range(4):
+        m.mk_reset()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        m.mk_prefill(prompt, PP, tok)
+        e1.record(stream)
+        m.mk_sync()
+        if r:
+            pp_times.append(e0.elapsed_time(e1) / 1e3)
+    pp_s = float(np.median(pp_times))
+    print(f"[bench] prefill pp{PP}: {PP / pp_s:.0f} tok/s", file=sys.stderr, flush=True)
+
+    # ---- decode: 512-token prompt, W warm-up steps, K timed steps (token fed back on device)
+    m.mk_reset()
+    m.mk_prefill(prompt[:PROMPT], PROMPT, tok)
+    for _ in range(args.warmup):
+        m.mk_decode_step(tok, tok)
+    m.mk_sync()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        m.mk_decode_step(tok, tok)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    m.mk_sync()
+    per_launch = [s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends)]
+    region = starts[0].elapsed_time(ends[-1]) / 1e3
+    avg_launch = float(np.mean(per_launch))
+    L0 = PROMPT + args.warmup + 1
+    bytes_per = np.mean([algorithmic_bytes(cfg, L0 + i)["total"] for i in range(K)])
+    achieved = bytes_per / avg_launch / 1e9
+    tok_s = K / region
+    print(f"[bench] decode: {tok_s:.0f} tok/s, {avg_launch * 1e6:.1f} us/launch, "
+          f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s), wall {wall:.3f}s",
+          file=sys.stderr, flush=True)
+
+    out = {
+        "metric": "batch-1 decode tok/s + % HBM roofline (0.8B hybrid bf16); pp520 prefill tok/s",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(region / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} batch-1 decode after a {PROMPT}-token prompt, one launch per token",
+                   "layers": cfg.n_layers, "deltanet_layers": cfg.n_deltanet_layers,
+                   "attention_layers": cfg.n_attention_layers, "hidden": cfg.hidden, "ffn": cfg.ffn,
+                   "vocab": cfg.vocab, "weights": "bf16 N(0,0.02) seed 0", "prompt_tokens": PROMPT,
+                   "grid_workgroups": m.mk_get_grid()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(bytes_per), "avg_launch_us": round(avg_launch * 1e6, 2)},
+        "prefill": {"workload": f"pp{PP}", "value": round(PP / pp_s, 1), "unit": "tok/s",
+                    "ms": round(pp_s * 1e3, 3)},
+        "launches_per_token": 1,
+    }
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, W)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,7 +26,7 @@ STATUS = {
 EXPORTS = ["mk_workspace_bytes", "mk_create", "mk_load_weights", "mk_check_tensors", "mk_prefill",
            "mk_decode_step", "mk_verify_k", "mk_reset", "mk_sync", "mk_get_position",
            "mk_state_bytes", "mk_read_state", "mk_write_state", "mk_set_grid", "mk_get_grid",
-           "mk_last_error", "mk_destroy"]
+           "mk_set_trace", "mk_last_error", "mk_destroy"]
 
 
 class MkError(RuntimeError):
@@ -80,6 +80,7 @@ def load_library():
         "mk_write_state": (ctypes.c_int, [P, I32, P]),
         "mk_set_grid": (ctypes.c_int, [P, I32]),
         "mk_get_grid": (ctypes.c_int, [P, P]),
+        "mk_set_trace": (ctypes.c_int, [P, P, SZ]),
         "mk_last_error": (ctypes.c_char_p, [P]),
         "mk_destroy": (None, [P]),
     }
@@ -229,6 +230,10 @@ class Model:
         v = ctypes.c_int32()
         _check(self.lib.mk_get_grid(self.ctx, ctypes.byref(v)), self.ctx)
         return v.value
+
+    def mk_set_trace(self, d_trace=None):
+        nbytes = 0 if d_trace is None else d_trace.numel() * d_trace.element_size()
+        _check(self.lib.mk_set_trace(self.ctx, _ptr(d_trace), nbytes), self.ctx)
 
     def close(self):
         if getattr(self, "ctx", None):

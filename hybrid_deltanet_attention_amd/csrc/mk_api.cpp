@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/mk.h"
+#define MK_HOST_VIEW 1
 #include "mk_internal.h"
 
 namespace {
@@ -68,7 +69,7 @@ std::string check_config(const mk_config* c) {
   if (c->n_q_heads % c->n_kv_heads != 0) return "n_q_heads must be a multiple of n_kv_heads";
   if (c->hidden % 8 || c->ffn % 8 || (c->dn_heads * c->dn_dv) % 8 || (c->n_q_heads * c->head_dim) % 8)
     return "hidden, ffn, dn_heads*dn_dv and n_q_heads*head_dim must be multiples of 8";
-  if (c->dn_dk % 2 || c->dn_dv % 2 || c->head_dim % 2) return "dn_dk, dn_dv and head_dim must be even";
+  if (c->dn_dk % 2 || c->dn_dv % 2 || c->head_dim % 4) return "dn_dk and dn_dv must be even, head_dim a multiple of 4";
   if (c->dn_dk > 256 || c->dn_dv > 256 || c->head_dim > 256) return "dn_dk, dn_dv, head_dim must be <= 256";
   if (c->tied_embeddings != 1) return "only tied embeddings are supported";
   if (c->weight_dtype != MK_BF16) return "weight_dtype must be MK_BF16";
@@ -82,19 +83,17 @@ std::string check_config(const mk_config* c) {
 
 // ----------------------------------------------------------------------- workspace layout
 struct LayerOff {
-  size_t w_in, w_out, w_gu, w_down, g1, g2, S, Kc, Vc, ll_in, ll_mid, ll_o, ll_x1, ll_h, ll_x2;
-  int64_t rows_in;
+  size_t w_in, w_out, w_gu, w_down, g1, g2, S, Kc, Vc, ll_in, ll_part, ll_o, ll_x1, ll_h, ll_x2;
+  int64_t rows_in, k_out;
 };
 
 struct Layout {
   size_t ctl, descs, rope_cos, rope_sin, g_final, embed, ll_am, scratch, total;
-  size_t state_begin, state_end;   // DeltaNet states + KV caches (cleared by mk_reset)
-  size_t ll_begin, ll_end;         // exchange records (cleared at create)
+  size_t state_begin, state_end;  // DeltaNet states + KV caches
+  size_t xchg_begin, xchg_end;    // exchange records
   std::vector<LayerOff> layers;
   int max_items;
 };
-
-constexpr int kMaxGrid = 1024;
 
 Layout make_layout(const mk_config& c) {
   Layout L{};
@@ -116,15 +115,11 @@ Layout make_layout(const mk_config& c) {
   L.layers.resize(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
     LayerOff& lo = L.layers[l];
-    if (is_attention(c, l)) {
-      lo.rows_in = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
-      lo.w_out = 0;
-    } else {
-      lo.rows_in = 2 * H * c.dn_dk + H * c.dn_dv + 2 * H;
-    }
+    const bool att = is_attention(c, l);
+    lo.rows_in = att ? (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim : 2 * H * c.dn_dk + H * c.dn_dv + 2 * H;
+    lo.k_out = att ? (int64_t)c.n_q_heads * c.head_dim : H * c.dn_dv;
     lo.w_in = take((size_t)lo.rows_in * D * 2);
-    const int64_t kout = is_attention(c, l) ? (int64_t)c.n_q_heads * c.head_dim : H * c.dn_dv;
-    lo.w_out = take((size_t)D * kout * 2);
+    lo.w_out = take((size_t)D * lo.k_out * 2);
     lo.w_gu = take((size_t)2 * c.ffn * D * 2);
     lo.w_down = take((size_t)D * c.ffn * 2);
     lo.g1 = take(D * 4);
@@ -141,42 +136,36 @@ Layout make_layout(const mk_config& c) {
     }
   }
   L.state_end = o;
-  L.ll_begin = o;
+  L.xchg_begin = o;
   for (int l = 0; l < c.n_layers; ++l) {
     LayerOff& lo = L.layers[l];
     lo.ll_in = take((size_t)lo.rows_in * 8);
-    if (is_attention(c, l)) {
-      lo.ll_mid = take((size_t)L.max_items * gs * (c.head_dim + 2) * 8);
-      lo.ll_o = take((size_t)c.n_q_heads * c.head_dim * 8);
-    } else {
-      lo.ll_mid = take((size_t)H * c.dn_dv * 8);
-    }
+    if (is_attention(c, l)) lo.ll_part = take((size_t)L.max_items * gs * (c.head_dim + 2) * 8);
+    lo.ll_o = take((size_t)lo.k_out * 8);
     lo.ll_x1 = take(D * 8);
     lo.ll_h = take((size_t)c.ffn * 8);
     lo.ll_x2 = take(D * 8);
   }
-  L.ll_am = take((size_t)2 * kMaxGrid * 8);
-  L.ll_end = o;
+  L.ll_am = take((size_t)2 * MK_MAX_GRID * 8);
+  L.xchg_end = o;
   L.scratch = take(4096);
   L.total = o;
   return L;
 }
 
-// LDS carve for the decode kernel (floats)
-void lds_layout(const mk_config& c, MkDecodeParams& p) {
+// LDS carve for the decode kernel (floats) at grid size `grid`
+void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   const int D = c.hidden;
   const int gs = c.n_q_heads / c.n_kv_heads;
-  const int nch_max = (c.max_ctx + MK_ATT_CHUNK - 1) / MK_ATT_CHUNK;
-  int vec = c.ffn;
-  vec = std::max(vec, c.dn_heads * c.dn_dv);
-  vec = std::max(vec, c.n_q_heads * c.head_dim);
-  vec = std::max(vec, 2 * c.dn_dk + 2 + c.dn_dv);
-  vec = std::max(vec, gs * c.head_dim + 2 * c.head_dim + gs * MK_ATT_CHUNK + 2 * gs);
-  vec = std::max(vec, 3 * std::max(2048, nch_max) + 3 * nch_max);
-  vec = std::max(vec, 2 * kMaxGrid);
-  auto segs = [](int K) { return (K + 511) / 512; };
-  int kmax = std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), c.n_q_heads * c.head_dim);
-  const int red = std::max(256 * segs(D), 128 * segs(kmax));
+  const int hd = c.head_dim, C = MK_ATT_CHUNK, tpp = hd / 4;
+  const int nch_max = (c.max_ctx + C - 1) / C;
+  // gathered mixer output / FFN hidden, argmax records
+  const int vec = std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid));
+  // gathered DeltaNet inputs, attention scratch, combine staging; GEMV unit partials reuse it
+  int att = 2 * c.dn_dk + 2 + c.dn_dv;
+  att = std::max(att, gs * hd + 2 * hd + C * hd + gs * C * tpp + gs * C + 2 * gs);
+  att = std::max(att, 3 * std::max(2048, nch_max));
+  att = std::max(att, 4096);
   int o = 0;
   auto take = [&](int n) {
     const int at = o;
@@ -186,16 +175,16 @@ void lds_layout(const mk_config& c, MkDecodeParams& p) {
   p.lds_x = take(D);
   p.lds_xn = take(D);
   p.lds_vec = take(vec);
-  p.lds_red = take(red);
-  p.lds_out = take(256);
+  p.lds_att = take(att);
+  p.lds_red = p.lds_att;
   p.lds_scr = take(4 * MK_NWAVE);
+  o = (o + 255) / 256 * 256;  // 1 KB aligned stage
+  p.lds_stage = take(MK_NCW * MK_STAGE_FLOATS_PER_WAVE);
   // at least 96 KB so that only one workgroup fits per compute unit
   p.lds_floats = std::max(o, 96 * 1024 / 4);
 }
 
 }  // namespace
-
-extern "C" int mk_decode_max_blocks_per_cu(int lds_bytes);
 
 struct mk_ctx {
   mk_config cfg;
@@ -333,7 +322,7 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   ctx->ws_bytes = workspace_bytes;
   ctx->lay = lay;
   ctx->n_cu = prop.multiProcessorCount;
-  ctx->grid = std::min(ctx->n_cu, kMaxGrid);
+  ctx->grid = std::min(ctx->n_cu, MK_MAX_GRID);
 
   MkDecodeParams& p = ctx->base;
   p.n_layers = cfg->n_layers;
@@ -357,7 +346,7 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   p.rope_sin = (const float*)(ctx->ws + lay.rope_sin);
   p.ctl = (MkCtl*)(ctx->ws + lay.ctl);
   p.ll_am = (mk_u64*)(ctx->ws + lay.ll_am);
-  lds_layout(*cfg, p);
+  lds_layout(*cfg, ctx->grid, p);
 
   const int lds_bytes = p.lds_floats * 4;
   if (lds_bytes > (int)prop.sharedMemPerBlock || mk_decode_max_blocks_per_cu(lds_bytes) < 1) {
@@ -369,13 +358,12 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
 
   // per-layer descriptors
   std::vector<MkLayerDev> descs(cfg->n_layers);
-  int kvi = 0;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const LayerOff& lo = lay.layers[l];
     MkLayerDev& d = descs[l];
     std::memset(&d, 0, sizeof(d));
     d.kind = is_attention(*cfg, l) ? MK_LAYER_ATT : MK_LAYER_DN;
-    d.kv_index = d.kind == MK_LAYER_ATT ? kvi++ : -1;
+    d.rows_in = (int32_t)lo.rows_in;
     d.w_in = (const uint16_t*)(ctx->ws + lo.w_in);
     d.w_out = (const uint16_t*)(ctx->ws + lo.w_out);
     d.w_gu = (const uint16_t*)(ctx->ws + lo.w_gu);
@@ -385,12 +373,12 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
     if (d.kind == MK_LAYER_ATT) {
       d.Kc = (float*)(ctx->ws + lo.Kc);
       d.Vc = (float*)(ctx->ws + lo.Vc);
-      d.ll_o = (mk_u64*)(ctx->ws + lo.ll_o);
+      d.ll_part = (mk_u64*)(ctx->ws + lo.ll_part);
     } else {
       d.S = (float*)(ctx->ws + lo.S);
     }
     d.ll_in = (mk_u64*)(ctx->ws + lo.ll_in);
-    d.ll_mid = (mk_u64*)(ctx->ws + lo.ll_mid);
+    d.ll_o = (mk_u64*)(ctx->ws + lo.ll_o);
     d.ll_x1 = (mk_u64*)(ctx->ws + lo.ll_x1);
     d.ll_h = (mk_u64*)(ctx->ws + lo.ll_h);
     d.ll_x2 = (mk_u64*)(ctx->ws + lo.ll_x2);
@@ -420,8 +408,8 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
          "copy rope sin");
   if (rc == MK_OK && mk_launch_zero(ctx->ws + lay.ctl, sizeof(MkCtl), ctx->stream)) rc = MK_E_HIP;
   if (rc == MK_OK && mk_launch_zero(ctx->ws + lay.state_begin, lay.state_end - lay.state_begin, ctx->stream)) rc = MK_E_HIP;
-  if (rc == MK_OK && mk_launch_zero(ctx->ws + lay.ll_begin, lay.ll_end - lay.ll_begin, ctx->stream)) rc = MK_E_HIP;
-  if (rc == MK_OK && mk_launch_set_ctl(p.ctl, 0, 1, ctx->stream)) rc = MK_E_HIP;
+  if (rc == MK_OK && mk_launch_zero(ctx->ws + lay.xchg_begin, lay.xchg_end - lay.xchg_begin, ctx->stream)) rc = MK_E_HIP;
+  if (rc == MK_OK && mk_launch_set_ctl(p.ctl, 0, 1, 0, ctx->stream)) rc = MK_E_HIP;
   if (rc == MK_OK) hip_ok(hipStreamSynchronize(ctx->stream), "synchronise after create");
   if (rc != MK_OK) {
     if (g_err.empty()) g_err = "kernel launch failed during create";
@@ -440,8 +428,13 @@ void mk_destroy(mk_ctx* ctx) {
 
 int mk_set_grid(mk_ctx* ctx, int32_t n) {
   if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
-  if (n < 1 || n > ctx->n_cu || n > kMaxGrid)
-    return fail(ctx, MK_E_INVALID, "grid must be in [1, " + std::to_string(std::min(ctx->n_cu, kMaxGrid)) + "]");
+  if (n < 1 || n > ctx->n_cu || n > MK_MAX_GRID)
+    return fail(ctx, MK_E_INVALID, "grid must be in [1, " + std::to_string(std::min(ctx->n_cu, MK_MAX_GRID)) + "]");
+  MkDecodeParams q = ctx->base;
+  lds_layout(ctx->cfg, n, q);
+  if (mk_decode_max_blocks_per_cu(q.lds_floats * 4) < 1)
+    return fail(ctx, MK_E_OCCUPANCY, "decode kernel does not fit at this grid size");
+  ctx->base = q;
   ctx->grid = n;
   return MK_OK;
 }
@@ -457,7 +450,10 @@ int mk_reset(mk_ctx* ctx) {
   const Layout& lay = ctx->lay;
   if (mk_launch_zero(ctx->ws + lay.state_begin, lay.state_end - lay.state_begin, ctx->stream))
     return fail(ctx, MK_E_HIP, "zero state launch failed");
-  if (mk_launch_set_ctl(ctx->base.ctl, 0, 1, ctx->stream)) return fail(ctx, MK_E_HIP, "set position launch failed");
+  // exchange words too, so that a launch that gave up leaves nothing behind; the epoch moves on
+  if (mk_launch_zero(ctx->ws + lay.xchg_begin, lay.xchg_end - lay.xchg_begin, ctx->stream))
+    return fail(ctx, MK_E_HIP, "zero exchange launch failed");
+  if (mk_launch_set_ctl(ctx->base.ctl, 0, 1, 1, ctx->stream)) return fail(ctx, MK_E_HIP, "set position launch failed");
   ctx->pos_host = 0;
   return MK_OK;
 }
@@ -619,6 +615,14 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   return MK_OK;
 }
 
+int mk_set_trace(mk_ctx* ctx, void* d_trace, size_t bytes) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  if (d_trace && bytes < (size_t)ctx->grid * MK_TRACE_EVENTS * 8)
+    return fail(ctx, MK_E_INVALID, "trace buffer needs grid * " + std::to_string(MK_TRACE_EVENTS) + " * 8 bytes");
+  ctx->base.trace = (unsigned long long*)d_trace;
+  return MK_OK;
+}
+
 int mk_verify_k(mk_ctx* ctx, const int32_t*, int32_t, int32_t*, int32_t*) {
   if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
   return fail(ctx, MK_E_UNSUPPORTED, "speculative verify is not built");
@@ -631,9 +635,10 @@ int mk_sync(mk_ctx* ctx) {
   HIPCHK(ctx, hipMemcpy(&ctl, ctx->base.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
   if (ctl.err) {
     // clear the flag so that the next launch starts clean; the sequence state is undefined now
-    if (mk_launch_set_ctl(ctx->base.ctl, -1, 1, ctx->stream) == 0) (void)hipStreamSynchronize(ctx->stream);
+    if (mk_launch_set_ctl(ctx->base.ctl, -1, 1, 0, ctx->stream) == 0) (void)hipStreamSynchronize(ctx->stream);
     if (ctl.err == 2u)
       return fail(ctx, MK_E_INVALID, "a decode launch saw a token id outside [0, vocab) or a full context; call mk_reset");
+
     return fail(ctx, MK_E_DEVICE_TIMEOUT, "a grid-wide wait inside the decode kernel gave up; call mk_reset");
   }
   return MK_OK;

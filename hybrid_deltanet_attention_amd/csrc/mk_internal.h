@@ -5,19 +5,37 @@
 
 typedef unsigned long long mk_u64;
 
-// Threads per workgroup of the persistent decode grid (8 wave64s).
+// Device code sees pointers into device memory as global-address-space pointers, so the compiler
+// emits global (not flat) memory instructions for them; host code sees plain pointers.  The
+// layout is the same either way.  Host-only translation units define MK_HOST_VIEW.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(MK_HOST_VIEW)
+#define MK_G __attribute__((address_space(1)))
+#else
+#define MK_G
+#endif
+
+// Threads per workgroup of the persistent decode grid (8 wave64s): waves 0..6 compute and
+// prefetch, wave 7 only polls exchange records (so its waits never include prefetch traffic).
 #define MK_NT 512
 #define MK_NWAVE 8
+#define MK_NCW 7
+#define MK_NCT (MK_NCW * 64)
 // Positions per split-K attention work item.
 #define MK_ATT_CHUNK 16
-// Polls of an exchange record before a wait gives up and reports MK_E_DEVICE_TIMEOUT.
+// Timestamps per workgroup in the optional phase trace.
+#define MK_TRACE_EVENTS 512
+// Polls of an exchange word before a wait gives up and reports MK_E_DEVICE_TIMEOUT.
 #define MK_SPIN_LIMIT (1u << 22)
+// LDS prefetch stage per compute wave (floats): 8 x 1 KB large-stage slots + 4 x 1 KB small-stage slots.
+#define MK_STAGE_FLOATS_PER_WAVE 3072
+// Largest grid the exchange buffers are sized for.
+#define MK_MAX_GRID 1024
 
 // Device-resident control block (first 256 bytes of the workspace).
 struct MkCtl {
-  uint32_t step;   // launch epoch stamped into exchange records; starts at 1, never reset
+  uint32_t step;   // launch epoch stamped into exchange records; starts at 1, never reused
   int32_t pos;     // next position to write
-  uint32_t err;    // nonzero once any kernel wait gave up
+  uint32_t err;    // nonzero once a kernel gave up (1 = wait timeout, 2 = bad input)
   uint32_t pad[61];
 };
 
@@ -26,42 +44,45 @@ enum { MK_LAYER_DN = 0, MK_LAYER_ATT = 1 };
 // Per-layer device pointers (an array of these lives in the workspace).
 struct MkLayerDev {
   int32_t kind;
-  int32_t kv_index;         // attention layers: index among attention layers
-  const uint16_t* w_in;     // DeltaNet: [2*H*dk + H*dv + 2H][D] (q, k, v, a, b rows)
-                            // attention: [(nq + 2*nkv)*hd][D], rows of each head in RoPE pair order
-  const uint16_t* w_out;    // [D][H*dv] or [D][nq*hd]
-  const uint16_t* w_gu;     // [2*ffn][D], gate and up rows interleaved (g0, u0, g1, u1, ...)
-  const uint16_t* w_down;   // [D][ffn]
-  const float* g1;          // [D]
-  const float* g2;          // [D]
-  float* S;                 // DeltaNet: [H][dv][dk]
-  float* Kc;                // attention: [nkv][max_ctx][hd]
-  float* Vc;                // attention: [nkv][max_ctx][hd]
-  mk_u64* ll_in;            // DeltaNet: [2*H*dk + H*dv + 2H]; attention: q [nq*hd], k [nkv*hd], v [nkv*hd]
-  mk_u64* ll_mid;           // DeltaNet: o [H*dv]; attention: partials [max_items][gs][hd + 2]
-  mk_u64* ll_o;             // attention: combined o [nq*hd]
-  mk_u64* ll_x1;            // [D] residual after the mixer
-  mk_u64* ll_h;             // [ffn]
-  mk_u64* ll_x2;            // [D] residual after the FFN
+  int32_t rows_in;               // rows of w_in
+  MK_G const uint16_t* w_in;     // DeltaNet: [2*H*dk + H*dv + 2H][D] (q, k, v, a, b rows)
+                                 // attention: [(nq + 2*nkv)*hd][D], rows of each head in RoPE pair order
+  MK_G const uint16_t* w_out;    // [D][H*dv] or [D][nq*hd]
+  MK_G const uint16_t* w_gu;     // [2*ffn][D], gate and up rows interleaved (g0, u0, g1, u1, ...)
+  MK_G const uint16_t* w_down;   // [D][ffn]
+  MK_G const float* g1;          // [D]
+  MK_G const float* g2;          // [D]
+  MK_G float* S;                 // DeltaNet: [H][dv][dk]
+  MK_G float* Kc;                // attention: [nkv][max_ctx][hd]
+  MK_G float* Vc;                // attention: [nkv][max_ctx][hd]
+  MK_G mk_u64* ll_in;            // records. DeltaNet: [rows_in]; attention: q [nq*hd], k [nkv*hd], v [nkv*hd]
+  MK_G mk_u64* ll_part;          // attention partial records [max_items][gs][hd + 2]
+  MK_G mk_u64* ll_o;             // mixer outputs [H*dv] or [nq*hd]
+  MK_G mk_u64* ll_x1;            // residual after the mixer [D]
+  MK_G mk_u64* ll_h;             // FFN hidden [ffn]
+  MK_G mk_u64* ll_x2;            // residual after the FFN [D]
 };
 
 struct MkDecodeParams {
-  const MkLayerDev* layers;
+  MK_G const MkLayerDev* layers;
   int32_t n_layers, D, ffn, vocab;
   int32_t H, dk, dv, nq, nkv, hd;
   int32_t max_ctx, max_items;
   float rms_eps, l2_eps;
-  const uint16_t* embed;        // [vocab][D]
-  const float* g_final;         // [D]
-  const float* rope_cos;        // [max_ctx][hd/2]
-  const float* rope_sin;        // [max_ctx][hd/2]
-  MkCtl* ctl;
-  mk_u64* ll_am;                // [2 * max grid] argmax records
-  const int32_t* tok;           // device token to embed
-  int32_t* next;                // device output token
-  float* logits;                // optional [vocab]
-  // LDS carve (float offsets) and sizes
-  int32_t lds_x, lds_xn, lds_vec, lds_red, lds_out, lds_scr, lds_floats;
+  MK_G const uint16_t* embed;    // [vocab][D]
+  MK_G const float* g_final;     // [D]
+  MK_G const float* rope_cos;    // [max_ctx][hd/2]
+  MK_G const float* rope_sin;    // [max_ctx][hd/2]
+  MK_G MkCtl* ctl;
+  MK_G mk_u64* ll_am;            // [2 * MK_MAX_GRID] argmax records
+  MK_G const int32_t* tok;       // device token to embed
+  MK_G int32_t* next;            // device output token
+  MK_G float* logits;            // optional [vocab]
+  // optional per-workgroup phase timestamps: trace[w * MK_TRACE_EVENTS + 2e] = wall clock (100 MHz),
+  // [.. + 2e + 1] = core clock
+  MK_G unsigned long long* trace;
+  // LDS carve (float offsets) and size
+  int32_t lds_x, lds_xn, lds_vec, lds_att, lds_red, lds_scr, lds_stage, lds_floats;
 };
 
 #ifdef __cplusplus
@@ -73,8 +94,8 @@ int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_
                            int64_t cols, void* stream);
 int mk_launch_bf16_to_f32(const uint16_t* src, float* dst, int64_t n, void* stream);
 int mk_launch_zero(void* dst, int64_t bytes, void* stream);
-int mk_launch_set_ctl(MkCtl* ctl, int32_t pos, int reset_err, void* stream);
-int mk_decode_lds_bytes(const MkDecodeParams* p);
+int mk_launch_set_ctl(MkCtl* ctl, int32_t pos, int reset_err, int bump_step, void* stream);
+int mk_decode_max_blocks_per_cu(int lds_bytes);
 #ifdef __cplusplus
 }
 #endif

@@ -142,6 +142,11 @@ int mk_write_state(mk_ctx* ctx, int32_t layer, const void* src);
 int mk_set_grid(mk_ctx* ctx, int32_t n_workgroups);
 int mk_get_grid(const mk_ctx* ctx, int32_t* n_workgroups);
 
+/* Diagnostics: when d_trace != NULL, every later decode launch stores, per workgroup w, the device
+ * real-time clock (100 MHz) at each phase boundary into d_trace[w * 512 + e] (uint64).  bytes must
+ * cover grid * 512 * 8.  NULL turns the trace off.  Errors: MK_E_INVALID. */
+int mk_set_trace(mk_ctx* ctx, void* d_trace, size_t bytes);
+
 /* Message for the last failed call on ctx; ctx == NULL gives the calling thread's message from
  * a failed mk_workspace_bytes / mk_create / mk_check_tensors. */
 const char* mk_last_error(const mk_ctx* ctx);
