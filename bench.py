@@ -19,6 +19,8 @@ a bounded sample on this host.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +32,80 @@ HBM_PEAK_GBS = 8000.0
 PROMPT = 512
 PP = 520
 SEED = 0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL = "mk_decode_kernel"
+# measured HBM traffic of the decode kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE), valid only for the
+# kernel source it was measured on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_0p8b_traffic.json")
+KERNEL_SOURCES = ["hybrid_deltanet_attention_amd/csrc/mk_decode.hip", "hybrid_deltanet_attention_amd/csrc/mk_internal.h"]
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None when the kernel
+    source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(t["bytes_per_launch"])
+
+
+def _counter_rows(d):
+    import csv
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    return rows
+
+
+def _mean_counter(rows, kernel_sub, counter):
+    v = [float(r["Counter_Value"]) for r in rows if kernel_sub in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not v:
+        raise SystemExit(f"no {counter} rows for a kernel named like {kernel_sub}")
+    return float(np.mean(v)), len(v)
+
+
+def summarize_pmc(dirs: dict) -> dict:
+    """dirs: {"fetch": d, "write": d, "copy_fetch": d, "copy_write": d} (rocprofv3 -d output folders).
+    FETCH_SIZE and WRITE_SIZE read KiB per dispatch; each is scaled by bytes/KiB that the same counter
+    reports for a plain 1 GiB device-to-device copy."""
+    cf, _ = _mean_counter(_counter_rows(dirs["copy_fetch"]), "opy", "FETCH_SIZE")
+    cw, _ = _mean_counter(_counter_rows(dirs["copy_write"]), "opy", "WRITE_SIZE")
+    kf, nf = _mean_counter(_counter_rows(dirs["fetch"]), KERNEL, "FETCH_SIZE")
+    kw, nw = _mean_counter(_counter_rows(dirs["write"]), KERNEL, "WRITE_SIZE")
+    sf, sw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    return {"kernel": KERNEL, "source_sha256": kernel_source_hash(),
+            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": [nf, nw],
+            "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": COPY_BYTES,
+            "fetch_scale": sf, "write_scale": sw,
+            "bytes_per_launch": int(kf * 1024 * sf + kw * 1024 * sw)}
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, 4 times: the reference for the byte counters."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "reps": 4}), flush=True)
 
 
 def algorithmic_bytes(cfg, L: int) -> dict:
@@ -84,8 +160,17 @@ def main():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the pp520 prefill timing (profiling runs)")
     ap.add_argument("--config", default="hybrid_0p8b")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (reference for rocprofv3 byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc output folders into the traffic summary JSON")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        f, w, cf, cw = args.summarize_pmc
+        print(json.dumps(summarize_pmc({"fetch": f, "write": w, "copy_fetch": cf, "copy_write": cw}), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode path is batch-1 on a single device and "
               "this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
@@ -98,6 +183,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     cfg = synth.get_config(args.config)
     assert PROMPT + args.warmup + args.steps <= cfg.max_ctx and PP + 1 <= cfg.max_ctx
     print(f"[bench] generating {cfg.name} weights (seed {SEED})", file=sys.stderr, flush=True)
@@ -111,7 +199,7 @@ def main():
 
     # ---- prefill pp520 (fresh context each time), median of 3 after one warm run
     pp_times = []
-    for r in range(4):
+    for r in range(0 if args.no_prefill else 4):
         m.mk_reset()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -122,7 +210,7 @@ def main():
         m.mk_sync()
         if r:
             pp_times.append(e0.elapsed_time(e1) / 1e3)
-    pp_s = float(np.median(pp_times))
+    pp_s = float(np.median(pp_times)) if pp_times else float("nan")
     print(f"[bench] prefill pp{PP}: {PP / pp_s:.0f} tok/s", file=sys.stderr, flush=True)
 
     # ---- decode: 512-token prompt, W warm-up steps, K timed steps (token fed back on device)
@@ -173,10 +261,10 @@ def main():
                    "vocab": cfg.vocab, "weights": "bf16 N(0,0.02) seed 0", "prompt_tokens": PROMPT,
                    "grid_workgroups": m.mk_get_grid()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": int(bytes_per), "avg_launch_us": round(avg_launch * 1e6, 2)},
-        "prefill": {"workload": f"pp{PP}", "value": round(PP / pp_s, 1), "unit": "tok/s",
-                    "ms": round(pp_s * 1e3, 3)},
+        "prefill": None if not pp_times else {"workload": f"pp{PP}", "value": round(PP / pp_s, 1),
+                                              "unit": "tok/s", "ms": round(pp_s * 1e3, 3)},
         "launches_per_token": 1,
     }
     m.close()

@@ -178,6 +178,8 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   p.lds_att = take(att);
   p.lds_red = p.lds_att;
   p.lds_scr = take(4 * MK_NWAVE);
+  o = (o + 1) / 2 * 2;  // 8-byte aligned trace stamps
+  p.lds_trace = take(2 * MK_TRACE_EVENTS);
   o = (o + 255) / 256 * 256;  // 1 KB aligned stage
   p.lds_stage = take(MK_NCW * MK_STAGE_FLOATS_PER_WAVE);
   // at least 96 KB so that only one workgroup fits per compute unit

@@ -217,6 +217,29 @@ __device__ __forceinline__ bool ll_gather_vec(const Ctx& cx, const MK_G mk_u64* 
   return ll_gather(cx, n, [=](int f) { return src + f; }, dst);
 }
 
+struct Tracer {
+  LS unsigned long long* lbuf;  // timestamps are kept in LDS while the kernel runs ...
+  MK_G unsigned long long* buf; // ... and copied here at the end (null: tracing off)
+  int n;
+  // (wall clock, core clock) pairs, stamped by thread 0
+  __device__ __forceinline__ void mark() {
+    if (buf) {
+      if (threadIdx.x == 0 && 2 * n + 1 < MK_TRACE_EVENTS) {
+        lbuf[2 * n] = wall_clock64();
+        lbuf[2 * n + 1] = clock64();
+      }
+      ++n;
+    }
+  }
+  __device__ __forceinline__ void flush() {
+    if (buf) {
+      __syncthreads();
+      const int m = min(2 * n, MK_TRACE_EVENTS);
+      for (int i = tid(); i < m; i += MK_NT) buf[i] = lbuf[i];
+    }
+  }
+};
+
 // ------------------------------------------------------------------------ GEMV
 // out[r] = W[r] . x for the R rows of a workgroup's slice (row stride K).  Work unit = (row r,
 // 512-column segment s), u = r*S + s; compute wave w takes units w, w + 7, ...; lane l covers columns
@@ -275,9 +298,10 @@ __device__ __forceinline__ void gemv_issue(RegBatch& rb, const Gemv& g, int b0, 
 // row pair (block sizes are even).  Row/pair indices are relative to the slice.
 template <int NPF, bool PAIRS, typename Epi>
 __device__ __forceinline__ void gemv(const Gemv& g, const LS float* xin, const LS u32x4* stage, LS float* red,
-                                     Epi epi) {
+                                     Tracer& tr, Epi epi) {
   wait_vm();
   keep_issued();
+  tr.mark();
   for (int b0 = 0; b0 < g.R; b0 += g.rb) {
     const int nr = min(g.rb, g.R - b0);
     const int n = g.units(b0);
@@ -307,7 +331,9 @@ __device__ __forceinline__ void gemv(const Gemv& g, const LS float* xin, const L
 #pragma unroll
       for (int b = 0; b < PF_REG; ++b) cur.c[b] = nxt.c[b];
     }
+    tr.mark();
     __syncthreads();
+    tr.mark();
     if (PAIRS) {
       for (int t = tid(); t < nr / 2; t += MK_NT) {
         float v0 = 0.f, v1 = 0.f;
@@ -350,21 +376,6 @@ struct Lds {
   LS float* scr;   // reductions
   LS u32x4* stA;   // this wave's large prefetch stage (8 x 1 KB)
   LS u32x4* stB;   // this wave's small prefetch stage (4 x 1 KB)
-};
-
-struct Tracer {
-  MK_G unsigned long long* buf;
-  int n;
-  // (wall clock, core clock) pairs
-  __device__ __forceinline__ void mark() {
-    if (buf) {
-      if (threadIdx.x == 0 && 2 * n + 1 < MK_TRACE_EVENTS) {
-        buf[2 * n] = wall_clock64();
-        buf[2 * n + 1] = clock64();
-      }
-      ++n;
-    }
-  }
 };
 
 // ------------------------------------------------------------------------ DeltaNet
@@ -465,7 +476,7 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
 // ------------------------------------------------------------------------ attention
 // q/k/v rows in RoPE pair order: rotate q and k at position pos, append k and v to the cache
 __device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                        const Gemv& g, int P0, int pos) {
+                                        const Gemv& g, int P0, int pos, Tracer& tr) {
   const int hd = p.hd, half = hd / 2;
   const MK_G float* cs = p.rope_cos + (size_t)pos * half;
   const MK_G float* sn = p.rope_sin + (size_t)pos * half;
@@ -473,7 +484,7 @@ __device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDe
   MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   MK_G mk_u64* llv = llk + p.nkv * hd;
   const int nqp = p.nq * half, nkp = p.nkv * half;
-  gemv<PF_A, true>(g, s.xn, s.stA, s.red, [&](int pl, float x1, float x2) {
+  gemv<PF_A, true>(g, s.xn, s.stA, s.red, tr, [&](int pl, float x1, float x2) {
     const int P = P0 + pl;
     int sec, hh, m;
     if (P < nqp) {
@@ -718,7 +729,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     if (w == 0 && tid() == 0) set_err(cx, 2u);
     return;
   }
-  Tracer tr{p.trace ? p.trace + (size_t)w * MK_TRACE_EVENTS : nullptr, 0};
+  Tracer tr{(LS unsigned long long*)(lds + p.lds_trace), p.trace ? p.trace + (size_t)w * MK_TRACE_EVENTS : nullptr, 0};
   tr.mark();
   AttGeo ag;
   ag.init(p.hd);
@@ -744,6 +755,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
   for (int l = 0; l < p.n_layers; ++l) {
     const MkLayerDev L = p.layers[l];
     rmsnorm_lds(s.x, L.g1, s.xn, p.D, p.rms_eps, s.scr);
+    tr.mark();
     int K;  // mixer output width
     Gemv gout, ggu;
     ggu.init(L.w_gu + (size_t)2 * j0 * p.D, 2 * (j1 - j0), p.D);
@@ -751,7 +763,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
       K = p.H * p.dv;
       // in-projection rows -> records
       MK_G mk_u64* dst = L.ll_in + 2 * P0;
-      gemv<PF_A, false>(gin, s.xn, s.stA, s.red, [&](int r, float v, float) { ll_put(dst + r, cx.epoch, v); });
+      gemv<PF_A, false>(gin, s.xn, s.stA, s.red, tr, [&](int r, float v, float) { ll_put(dst + r, cx.epoch, v); });
       tr.mark();
       // state rows and the first out-projection rows go out before q/k/v/a/b are complete
       const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
@@ -762,7 +774,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
       if (!dn_state(p, L, cx, s, s0, s1, tr)) return;
     } else {
       K = p.nq * p.hd;
-      att_qkv(p, L, cx, s, gin, P0, pos);
+      att_qkv(p, L, cx, s, gin, P0, pos, tr);
       tr.mark();
       // K/V rows of the first work item and the first out-projection rows go out before q/k/v
       const int items = ((pos + MK_ATT_CHUNK) / MK_ATT_CHUNK) * p.nkv;
@@ -785,7 +797,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     // mixer output -> out-projection rows + residual -> records
     if (__syncthreads_or(!ll_gather_vec(cx, L.ll_o, K, s.vec))) return;
     tr.mark();
-    gemv<PF_B, false>(gout, s.vec, s.stB, s.red,
+    gemv<PF_B, false>(gout, s.vec, s.stB, s.red, tr,
                       [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     // down-projection rows go out before the residual is complete
     Gemv gdn;
@@ -796,7 +808,8 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     if (__syncthreads_or(!ll_gather_vec(cx, L.ll_x1, p.D, s.x))) return;
     tr.mark();
     rmsnorm_lds(s.x, L.g2, s.xn, p.D, p.rms_eps, s.scr);
-    gemv<PF_A, true>(ggu, s.xn, s.stA, s.red, [&](int j, float gv, float uv) {
+    tr.mark();
+    gemv<PF_A, true>(ggu, s.xn, s.stA, s.red, tr, [&](int j, float gv, float uv) {
       ll_put(L.ll_h + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
     });
     // next layer's input rows (or the LM head's) go out before the FFN hidden is complete
@@ -813,7 +826,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     tr.mark();
     if (__syncthreads_or(!ll_gather_vec(cx, L.ll_h, p.ffn, s.vec))) return;
     tr.mark();
-    gemv<PF_B, false>(gdn, s.vec, s.stB, s.red,
+    gemv<PF_B, false>(gdn, s.vec, s.stB, s.red, tr,
                       [&](int r, float v, float) { ll_put(L.ll_x2 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     tr.mark();
     if (__syncthreads_or(!ll_gather_vec(cx, L.ll_x2, p.D, s.x))) return;
@@ -825,7 +838,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
   float best = -INFINITY;
   int bidx = 0x7fffffff;
   const int v0 = 2 * P0;
-  gemv<PF_A, false>(gin, s.xn, s.stA, s.red, [&](int r, float v, float) {
+  gemv<PF_A, false>(gin, s.xn, s.stA, s.red, tr, [&](int r, float v, float) {
     const int idx = v0 + r;
     if (p.logits) p.logits[idx] = v;
     if (v > best || (v == best && idx < bidx)) {
@@ -862,7 +875,10 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     ll_put(p.ll_am + 2 * w + 1, cx.epoch, __int_as_float(bidx));
   }
   tr.mark();
-  if (w != 0) return;
+  if (w != 0) {
+    tr.flush();
+    return;
+  }
   // workgroup 0 reduces the per-workgroup winners and publishes the token
   __syncthreads();
   const MK_G mk_u64* am = p.ll_am;
@@ -884,6 +900,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     p.ctl->step = cx.epoch + 1u;
   }
   tr.mark();
+  tr.flush();
 }
 
 // ------------------------------------------------------------------------------------------

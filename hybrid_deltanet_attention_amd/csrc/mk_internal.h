@@ -82,7 +82,7 @@ struct MkDecodeParams {
   // [.. + 2e + 1] = core clock
   MK_G unsigned long long* trace;
   // LDS carve (float offsets) and size
-  int32_t lds_x, lds_xn, lds_vec, lds_att, lds_red, lds_scr, lds_stage, lds_floats;
+  int32_t lds_x, lds_xn, lds_vec, lds_att, lds_red, lds_scr, lds_trace, lds_stage, lds_floats;
 };
 
 #ifdef __cplusplus

@@ -50,7 +50,7 @@ enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4 };
 
 /* Model shape.  All fields are required (there is no default constructor on purpose).
  * Constraints checked by mk_workspace_bytes / mk_create: every size > 0; hidden, ffn, H*dk and
- * H*dv multiples of 8; dk, dv, head_dim even and <= 256; n_q_heads a multiple of n_kv_heads;
+ * H*dv multiples of 8; dk, dv even and head_dim a multiple of 4, all <= 256; n_q_heads a multiple of n_kv_heads;
  * attn_slot < period; tied_embeddings == 1; weight_dtype == MK_BF16; kv_dtype == MK_F32. */
 typedef struct {
   int32_t n_layers, hidden, ffn, vocab;
