@@ -69,7 +69,8 @@ std::string check_config(const mk_config* c) {
   if (c->n_q_heads % c->n_kv_heads != 0) return "n_q_heads must be a multiple of n_kv_heads";
   if (c->hidden % 8 || c->ffn % 8 || (c->dn_heads * c->dn_dv) % 8 || (c->n_q_heads * c->head_dim) % 8)
     return "hidden, ffn, dn_heads*dn_dv and n_q_heads*head_dim must be multiples of 8";
-  if (c->dn_dk % 2 || c->dn_dv % 2 || c->head_dim % 4) return "dn_dk and dn_dv must be even, head_dim a multiple of 4";
+  if (c->dn_dk % 4 || c->dn_dv % 2 || c->head_dim % 4) return "dn_dk and head_dim must be multiples of 4, dn_dv even";
+  if (c->n_q_heads / c->n_kv_heads > 32) return "at most 32 query heads per KV head";
   if (c->dn_dk > 256 || c->dn_dv > 256 || c->head_dim > 256) return "dn_dk, dn_dv, head_dim must be <= 256";
   if (c->tied_embeddings != 1) return "only tied embeddings are supported";
   if (c->weight_dtype != MK_BF16) return "weight_dtype must be MK_BF16";
@@ -83,7 +84,7 @@ std::string check_config(const mk_config* c) {
 
 // ----------------------------------------------------------------------- workspace layout
 struct LayerOff {
-  size_t w_in, w_out, w_gu, w_down, g1, g2, S, Kc, Vc, ll_in, ll_part, ll_o, ll_x1, ll_h, ll_x2;
+  size_t w_in, w_out, w_gu, w_down, g12, S, Kc, Vc, ll_in, ll_part, ll_o, ll_x1, ll_h, ll_x2;
   int64_t rows_in, k_out;
 };
 
@@ -110,7 +111,7 @@ Layout make_layout(const mk_config& c) {
   L.descs = take(sizeof(MkLayerDev) * c.n_layers);
   L.rope_cos = take((size_t)c.max_ctx * half * 4);
   L.rope_sin = take((size_t)c.max_ctx * half * 4);
-  L.g_final = take(D * 4);
+  L.g_final = take(D * 2);
   L.embed = take((size_t)c.vocab * D * 2);
   L.layers.resize(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
@@ -122,8 +123,7 @@ Layout make_layout(const mk_config& c) {
     lo.w_out = take((size_t)D * lo.k_out * 2);
     lo.w_gu = take((size_t)2 * c.ffn * D * 2);
     lo.w_down = take((size_t)D * c.ffn * 2);
-    lo.g1 = take(D * 4);
-    lo.g2 = take(D * 4);
+    lo.g12 = take(D * 4);  // BF16 [2][D]
   }
   L.state_begin = o;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -157,31 +157,33 @@ Layout make_layout(const mk_config& c) {
 void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   const int D = c.hidden;
   const int gs = c.n_q_heads / c.n_kv_heads;
-  const int hd = c.head_dim, C = MK_ATT_CHUNK, tpp = hd / 4;
-  const int nch_max = (c.max_ctx + C - 1) / C;
+  const int hd = c.head_dim, C = MK_ATT_CHUNK;
   // gathered mixer output / FFN hidden, argmax records
   const int vec = std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid));
-  // gathered DeltaNet inputs, attention scratch, combine staging; GEMV unit partials reuse it
+  // gathered DeltaNet inputs (one head), attention item inputs, combine staging, GEMV unit partials
   int att = 2 * c.dn_dk + 2 + c.dn_dv;
-  att = std::max(att, gs * hd + 2 * hd + C * hd + gs * C * tpp + gs * C + 2 * gs);
-  att = std::max(att, 3 * std::max(2048, nch_max));
-  att = std::max(att, 4096);
+  att = std::max(att, gs * hd + 2 * hd + gs * C + 2 * gs);
+  att = std::max(att, MK_RED_CAP);
   int o = 0;
   auto take = [&](int n) {
     const int at = o;
-    o += (n + 3) / 4 * 4;
+    o += (n + 3) / 4 * 4;  // 16-byte aligned regions
     return at;
   };
+  p.lds_desc = take(c.n_layers * (int)(sizeof(MkLayerDev) / 4));
+  p.lds_gain = take(2 * D);  // BF16 [2][2][D]
+  p.lds_rope = take(hd);
   p.lds_x = take(D);
   p.lds_xn = take(D);
   p.lds_vec = take(vec);
   p.lds_att = take(att);
-  p.lds_red = p.lds_att;
   p.lds_scr = take(4 * MK_NWAVE);
-  o = (o + 1) / 2 * 2;  // 8-byte aligned trace stamps
+  p.lds_flag = take(4);
+  o = (o + 1) / 2 * 2;
   p.lds_trace = take(2 * MK_TRACE_EVENTS);
-  o = (o + 255) / 256 * 256;  // 1 KB aligned stage
-  p.lds_stage = take(MK_NCW * MK_STAGE_FLOATS_PER_WAVE);
+  o = (o + 255) / 256 * 256;  // 1 KB aligned stages
+  p.lds_stA = take(MK_STAGE_A_SLOTS * 256);
+  p.lds_stB = take(MK_STAGE_B_SLOTS * 256);
   // at least 96 KB so that only one workgroup fits per compute unit
   p.lds_floats = std::max(o, 96 * 1024 / 4);
 }
@@ -343,7 +345,8 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   p.l2_eps = cfg->l2_eps;
   p.layers = (const MkLayerDev*)(ctx->ws + lay.descs);
   p.embed = (const uint16_t*)(ctx->ws + lay.embed);
-  p.g_final = (const float*)(ctx->ws + lay.g_final);
+  p.g_final = (const uint16_t*)(ctx->ws + lay.g_final);
+  p.gain0 = (const uint16_t*)(ctx->ws + lay.layers[0].g12);
   p.rope_cos = (const float*)(ctx->ws + lay.rope_cos);
   p.rope_sin = (const float*)(ctx->ws + lay.rope_sin);
   p.ctl = (MkCtl*)(ctx->ws + lay.ctl);
@@ -370,8 +373,7 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
     d.w_out = (const uint16_t*)(ctx->ws + lo.w_out);
     d.w_gu = (const uint16_t*)(ctx->ws + lo.w_gu);
     d.w_down = (const uint16_t*)(ctx->ws + lo.w_down);
-    d.g1 = (const float*)(ctx->ws + lo.g1);
-    d.g2 = (const float*)(ctx->ws + lo.g2);
+    d.g12 = (const uint16_t*)(ctx->ws + lo.g12);
     if (d.kind == MK_LAYER_ATT) {
       d.Kc = (float*)(ctx->ws + lo.Kc);
       d.Vc = (float*)(ctx->ws + lo.Vc);
@@ -509,14 +511,6 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
     return hipMemcpyAsync(ctx->ws + dst_off, tt.data, bytes, hipMemcpyHostToDevice, ctx->stream) == hipSuccess
                ? MK_OK : MK_E_HIP;
   };
-  auto copy_gain = [&](const std::string& name, size_t dst_off) -> int {
-    const mk_tensor& tt = tensor(name);
-    const void* src = nullptr;
-    const size_t bytes = (size_t)tt.shape[0] * 2;
-    if (src_of(tt, bytes, &src)) return MK_E_HIP;
-    return mk_launch_bf16_to_f32((const uint16_t*)src, (float*)(ctx->ws + dst_off), tt.shape[0], ctx->stream) ? MK_E_HIP
-                                                                                                            : MK_OK;
-  };
   // rows of `name` go to dst rows perm[r] (dst is a matrix with the same row length)
   auto copy_perm = [&](const std::string& name, size_t dst_off, const std::vector<int32_t>& perm) -> int {
     const mk_tensor& tt = tensor(name);
@@ -533,12 +527,12 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
   const int64_t D = c.hidden, H = c.dn_heads;
   const int hd = c.head_dim, half = hd / 2;
   rc = copy_plain("embed", lay.embed);
-  if (!rc) rc = copy_gain("final_norm", lay.g_final);
+  if (!rc) rc = copy_plain("final_norm", lay.g_final);
   for (int l = 0; l < c.n_layers && !rc; ++l) {
     const LayerOff& lo = lay.layers[l];
     const std::string p = "l" + std::to_string(l) + ".";
-    rc = copy_gain(p + "norm1", lo.g1);
-    if (!rc) rc = copy_gain(p + "norm2", lo.g2);
+    rc = copy_plain(p + "norm1", lo.g12);
+    if (!rc) rc = copy_plain(p + "norm2", lo.g12 + (size_t)D * 2);
     if (rc) break;
     if (is_attention(c, l)) {
       // rows of every head in RoPE pair order: (0, hd/2, 1, hd/2 + 1, ...)

@@ -4,19 +4,22 @@
 // recurrence in FP32 registers, QKV + RoPE + causal softmax + output projection fused).
 //
 // Grid: one 512-lane workgroup per compute unit (regular launch; one workgroup fits per CU and the
-// grid is no larger than the CU count, so all workgroups are resident together).
+// grid is no larger than the CU count, so all workgroups are resident together).  Inside a
+// workgroup, waves 0..3 stream (every global copy and store), waves 4..7 poll exchange records,
+// and all eight compute out of LDS.
 //
-// Exchanges between phases never use a barrier, a fence or a counter.  A phase publishes its
-// outputs as 8-byte records (FP32 value, launch epoch) with device-coherent stores; the next phase
-// polls exactly the records it needs until their epoch matches.  Each record is written once per
-// launch, so nothing is ever cleared.  Per DeltaNet layer there are five exchanges (in-projection,
-// mixer output, residual, FFN hidden, residual), per attention layer six (plus the split-K
-// attention partials).
+// Exchanges between phases use no barrier, fence or counter.  A phase publishes its outputs as
+// 8-byte records (FP32 value, launch epoch) with device-coherent stores; the next phase polls
+// exactly the records it needs until their epoch matches.  Each record is written once per launch,
+// so nothing is ever cleared.  Per DeltaNet layer there are five exchanges (in-projection, mixer
+// output, residual, FFN hidden, residual), per attention layer six (plus the split-K partials).
 //
-// Every phase's first batch of weights (and the DeltaNet state rows or the KV rows an attention
-// work item needs) is copied global -> LDS with asynchronous LDS-DMA loads before the workgroup
-// starts polling for the phase's inputs, so HBM streaming overlaps the exchange latency.  Every
-// wait is bounded: a wait that gives up sets ctl->err and every workgroup leaves the kernel.
+// Weights never depend on activations, so each phase's weights are copied global -> LDS with
+// asynchronous LDS-DMA before the workgroup waits for the phase's inputs; the copies run during
+// the exchange latency.  A streaming wave waits for exactly the copies it needs (vmcnt counts
+// loads, stores and LDS-DMA in issue order), and workgroup barriers order LDS only, so copies for
+// later phases stay in flight across them.  Every wait is bounded: a wait that gives up sets
+// ctl->err and every workgroup leaves the kernel.
 
 #include <hip/hip_runtime.h>
 #include "mk_internal.h"
@@ -32,33 +35,74 @@ typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int PF_A = 8;     // GEMV units per lane in the wave's large LDS stage (8 x 1 KB)
-constexpr int PF_B = 4;     // GEMV units per lane in the wave's small LDS stage (4 x 1 KB)
-constexpr int PF_REG = 8;   // GEMV units per lane per register batch beyond the stage
-constexpr int SR = 4;       // DeltaNet state rows per wave staged in LDS ahead of the update
-constexpr int RED_CAP = 4096;
-#ifndef MK_POLL_SLEEP
-#define MK_POLL_SLEEP 4  // s_sleep units (64 clocks each) between failed poll rounds
-#endif  // GEMV unit partials held in LDS per row block
+constexpr int NCW = MK_NCW;          // streaming waves 0..NCW-1
+constexpr int NCT = MK_NCT;          // streaming threads
+constexpr int NPT = MK_NT - MK_NCT;  // polling threads
+constexpr int SLOT = 64;             // u32x4 per 1 KB LDS slot
+constexpr int USLOTS = 4;            // slots per GEMV unit: 4 rows x 512 BF16 columns
+constexpr int A_UNITS = MK_STAGE_A_SLOTS / USLOTS;
+constexpr int PB = 8;                // poll loads in flight per lane
+constexpr int ATT_C = MK_ATT_CHUNK;
 
-// Compiler-only barrier: loads issued before it stay before it, so a prefetch is really in flight
-// during the poll that follows (without it the compiler may sink the loads to their first use).
+// Compiler-only barrier: memory operations issued before it stay before it.
 __device__ __forceinline__ void keep_issued() { asm volatile("" ::: "memory"); }
 
-// Thread / lane indices the compiler cannot treat as loop-invariant: per-lane index and address
-// arithmetic is recomputed where it is used instead of being hoisted out of the layer loop and kept
-// live (or spilled to scratch, whose reloads would wait behind in-flight prefetches).
+// Thread index the compiler cannot treat as loop-invariant: per-lane address arithmetic is
+// recomputed where it is used instead of being hoisted out of the layer loop and kept live.
 __device__ __forceinline__ int tid() {
   int t = (int)threadIdx.x;
   asm volatile("" : "+v"(t));
   return t;
 }
 __device__ __forceinline__ int lane() { return tid() & 63; }
-__device__ __forceinline__ int lane_here() { return tid() & 63; }
 __device__ __forceinline__ int wave() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+__device__ __forceinline__ bool streamer() { return wave() < NCW; }
+
+// Values that are the same in every lane, made scalar again after a call boundary (arguments of
+// out-of-line functions arrive in vector registers).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uni_ptr(T* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (T*)(((unsigned long long)hi << 32) | lo);
+}
 
 // contiguous balanced split of n items over parts: part i gets [split(n,parts,i), split(n,parts,i+1))
 __device__ __forceinline__ int split(int n, int parts, int i) { return (int)(((long long)n * i) / parts); }
+
+// Workgroup barrier ordering LDS only: it waits for this wave's LDS operations but not for its
+// global loads, stores or LDS-DMA copies.
+__device__ __forceinline__ void wg_bar() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  keep_issued();
+  __builtin_amdgcn_s_barrier();
+  keep_issued();
+}
+
+// vmcnt(N): at most N of this wave's vector memory operations still outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// at most n outstanding (rounded down to a supported count: waiting for more is always correct)
+__device__ __forceinline__ void wait_vm_n(int n) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  if (n >= 63) wait_vm<63>();
+  else if (n >= 48) wait_vm<48>();
+  else if (n >= 32) wait_vm<32>();
+  else if (n >= 24) wait_vm<24>();
+  else if (n >= 16) wait_vm<16>();
+  else if (n >= 12) wait_vm<12>();
+  else if (n >= 8) wait_vm<8>();
+  else if (n >= 6) wait_vm<6>();
+  else if (n >= 4) wait_vm<4>();
+  else if (n >= 3) wait_vm<3>();
+  else if (n >= 2) wait_vm<2>();
+  else if (n >= 1) wait_vm<1>();
+  else wait_vm<0>();
+}
 
 __device__ __forceinline__ void ll_put(MK_G mk_u64* p, u32 epoch, float v) {
   __hip_atomic_store(p, ((mk_u64)epoch << 32) | (mk_u64)__float_as_uint(v), __ATOMIC_RELAXED,
@@ -70,20 +114,15 @@ __device__ __forceinline__ mk_u64 ld_dev(const MK_G mk_u64* p) {
 
 __device__ __forceinline__ float bf_lo(u32 w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((u32)h << 16); }
 
 __device__ __forceinline__ u32x4 ldw(const MK_G uint16_t* p) { return __builtin_nontemporal_load((const MK_G u32x4*)p); }
 
-// Asynchronous global -> LDS copies (gfx950 LDS DMA): lane l's BYTES land at dst + l * BYTES, and the
-// copy is tracked by vmcnt like a load.  Prefetches use these so that the compiler can neither sink
-// nor drop them and no VGPRs are held across the waits that follow.
+// Asynchronous global -> LDS copy (gfx950 LDS DMA): lane l's 16 bytes land at dst + 16 l; tracked
+// by vmcnt like a load.  Lanes that are switched off copy nothing.
 __device__ __forceinline__ void dma16(const MK_G void* src, LS void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const MK_G void* src, LS void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
-}
-// wait until every vector memory operation of this wave (including LDS DMA) has completed
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // 8 BF16 weights . 8 FP32 activations (activations 16-byte aligned)
 __device__ __forceinline__ float dot8(u32x4 w, const LS float* x) {
@@ -102,51 +141,43 @@ __device__ __forceinline__ float dot8(u32x4 w, const LS float* x) {
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_add(float v) {
-  const int x = __float_as_int(v);
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF,
+                                                              false)));
 }
 
-// Full-wave sum with DPP row operations (quad swaps, row mirrors, row broadcasts); the total lands
-// in lane 63 and is broadcast to every lane.  Fixed order, so every call site is deterministic.
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum over each 16-lane row (quad swaps, half-row mirror, row mirror); every lane of the row ends
+// with the row's total.  Fixed order, so every call site is deterministic.
+__device__ __forceinline__ float row_sum16(float v) {
   v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
   v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
   v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
   v = dpp_add<0x140, 0xF>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = dpp_max<0xB1>(v);
+  v = dpp_max<0x4E>(v);
+  v = dpp_max<0x141>(v);
+  v = dpp_max<0x140>(v);
+  return v;
+}
+// Full-wave sum: row sums, then row broadcasts; the total lands in lane 63 and is broadcast.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
   v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
   v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Fixed-order workgroup sum; every thread receives the same value.
-__device__ __forceinline__ float block_sum(float v, LS float* scr) {
-  v = wave_sum(v);
-  if (lane() == 0) scr[wave()] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < MK_NWAVE; ++i) s += scr[i];
-  __syncthreads();
-  return s;
-}
-
-__device__ __forceinline__ void block_sum2(float& a, float& b, LS float* scr) {
-  a = wave_sum(a);
-  b = wave_sum(b);
-  if (lane() == 0) {
-    scr[wave()] = a;
-    scr[MK_NWAVE + wave()] = b;
-  }
-  __syncthreads();
-  float sa = 0.f, sb = 0.f;
-#pragma unroll
-  for (int i = 0; i < MK_NWAVE; ++i) {
-    sa += scr[i];
-    sb += scr[MK_NWAVE + i];
-  }
-  __syncthreads();
-  a = sa;
-  b = sb;
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max16(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 struct Ctx {
@@ -157,496 +188,674 @@ struct Ctx {
 __device__ __forceinline__ void set_err(const Ctx& cx, u32 code) {
   __hip_atomic_store(&cx.ctl->err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Poll n exchange words; word f lives at src(f), is complete when ready(word), and then
-// use(f, word) consumes it.  Only the poller wave (wave 7) loads: its vector-memory counter holds
-// nothing but these polls, so a completed poll is never held back by prefetch traffic issued by
-// the compute waves.  Each lane keeps up to PB loads in flight per round.  All threads call it
-// (the caller synchronises the workgroup afterwards); false if a wait gave up.
-template <typename SrcFn, typename ReadyFn, typename UseFn>
-__device__ __forceinline__ bool poll_words(const Ctx& cx, int n, SrcFn src, ReadyFn ready, UseFn use) {
-  constexpr int PB = 8;
-  bool ok = true;
-  if (wave() != MK_NWAVE - 1) return ok;
-  for (int base = 0; base < n && ok; base += 64 * PB) {
-    u32 pending = 0;
-#pragma unroll
-    for (int b = 0; b < PB; ++b)
-      if (base + b * 64 + lane() < n) pending |= 1u << b;
-    u32 spins = 0;
-    while (pending) {
-      mk_u64 v[PB];
-#pragma unroll
-      for (int b = 0; b < PB; ++b)
-        if ((pending >> b) & 1u) v[b] = ld_dev(src(base + b * 64 + lane()));
-#pragma unroll
-      for (int b = 0; b < PB; ++b)
-        if (((pending >> b) & 1u) && ready(v[b])) {
-          use(base + b * 64 + lane(), v[b]);
-          pending &= ~(1u << b);
-        }
-      if (pending) {
-        ++spins;
-        __builtin_amdgcn_s_sleep(MK_POLL_SLEEP);
-        if ((spins & 255u) == 0 &&
-            __hip_atomic_load(&cx.ctl->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-          ok = false;
-          break;
-        }
-        if (spins > MK_SPIN_LIMIT) {
-          set_err(cx, 1u);
-          ok = false;
-          break;
-        }
-      }
-    }
-  }
-  return ok;
+__device__ __forceinline__ bool err_seen(const Ctx& cx) {
+  return __hip_atomic_load(&cx.ctl->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
-// Records src(f) -> dst[f] (LDS).
-template <typename SrcFn>
-__device__ __forceinline__ bool ll_gather(const Ctx& cx, int n, SrcFn src, LS float* dst) {
-  const u32 e = cx.epoch;
-  return poll_words(cx, n, src, [=](mk_u64 v) { return (u32)(v >> 32) == e; },
-                    [=](int f, mk_u64 v) { dst[f] = __uint_as_float((u32)v); });
-}
+struct Lds {
+  LS MkLayerDev* desc;  // every layer's descriptor
+  LS uint16_t* gain;    // BF16 RMSNorm gains [2 (layer parity)][2][D]
+  LS float* rope;       // cos [hd/2], sin [hd/2] at this launch's position
+  LS float* x;          // residual [D]
+  LS float* xn;         // normalised residual [D]
+  LS float* vec;        // gathered mixer output / FFN hidden, argmax records
+  LS float* att;        // gathered DeltaNet / attention inputs, combine staging, GEMV unit partials
+  LS float* scr;        // small reductions
+  LS int* flag;         // set once a wait gave up
+  LS u32x4* stA;        // prefetch stage A
+  LS u32x4* stB;        // prefetch stage B
+};
 
-// Contiguous records src[0..n) -> dst[0..n).
-__device__ __forceinline__ bool ll_gather_vec(const Ctx& cx, const MK_G mk_u64* src, int n, LS float* dst) {
-  return ll_gather(cx, n, [=](int f) { return src + f; }, dst);
+// Workgroup barrier that also tells every thread whether any thread passed bad == true.  A wait
+// that gives up is final for the launch, so the flag is only ever raised.
+__device__ __forceinline__ bool wg_bar_or(const Lds& s, bool bad) {
+  if (bad) *s.flag = 1;
+  wg_bar();
+  return *s.flag != 0;
 }
 
 struct Tracer {
-  LS unsigned long long* lbuf;  // timestamps are kept in LDS while the kernel runs ...
-  MK_G unsigned long long* buf; // ... and copied here at the end (null: tracing off)
+  LS unsigned long long* lbuf;   // timestamps are kept in LDS while the kernel runs ...
+  MK_G unsigned long long* buf;  // ... and copied here at the end (null: tracing off)
   int n;
-  // (wall clock, core clock) pairs, stamped by thread 0
+  // wall-clock stamps: lane 0 of wave 0 (a streaming wave) at [n], lane 0 of the first polling
+  // wave at [MK_TRACE_EVENTS / 2 + n]
   __device__ __forceinline__ void mark() {
     if (buf) {
-      if (threadIdx.x == 0 && 2 * n + 1 < MK_TRACE_EVENTS) {
-        lbuf[2 * n] = wall_clock64();
-        lbuf[2 * n + 1] = clock64();
-      }
+      if ((threadIdx.x == 0 || threadIdx.x == NCT) && n < MK_TRACE_EVENTS / 2)
+        lbuf[(threadIdx.x == 0 ? 0 : MK_TRACE_EVENTS / 2) + n] = wall_clock64();
       ++n;
     }
   }
   __device__ __forceinline__ void flush() {
     if (buf) {
-      __syncthreads();
-      const int m = min(2 * n, MK_TRACE_EVENTS);
-      for (int i = tid(); i < m; i += MK_NT) buf[i] = lbuf[i];
+      wg_bar();
+      for (int i = tid(); i < MK_TRACE_EVENTS; i += MK_NT) buf[i] = lbuf[i];
     }
   }
 };
 
+// ------------------------------------------------------------------------ exchanges (polling waves)
+// Poll n records, record f at src(f); use(f, value) once its epoch matches.  Polling threads keep
+// PB loads in flight each.  Every thread calls it; streaming threads return at once.
+template <typename SrcFn, typename UseFn>
+__device__ __forceinline__ bool gather_map(const Ctx& cx, int n, SrcFn src, UseFn use) {
+  if (streamer()) return true;
+  const u32 e = cx.epoch;
+  const int pl = tid() - NCT;
+  for (int base = 0; base < n; base += NPT * PB) {
+    u32 pending = 0;
+#pragma unroll
+    for (int k = 0; k < PB; ++k)
+      if (base + k * NPT + pl < n) pending |= 1u << k;
+    u32 spins = 0;
+    while (pending) {
+      mk_u64 v[PB];
+#pragma unroll
+      for (int k = 0; k < PB; ++k)
+        if ((pending >> k) & 1u) v[k] = ld_dev(src(base + k * NPT + pl));
+#pragma unroll
+      for (int k = 0; k < PB; ++k)
+        if (((pending >> k) & 1u) && (u32)(v[k] >> 32) == e) {
+          use(base + k * NPT + pl, __uint_as_float((u32)v[k]));
+          pending &= ~(1u << k);
+        }
+      if (pending) {
+        ++spins;
+        if ((spins & 255u) == 0 && err_seen(cx)) return false;
+        if (spins > MK_SPIN_LIMIT) {
+          set_err(cx, 1u);
+          return false;
+        }
+      }
+    }
+  }
+  return true;
+}
+
+// Contiguous records src[0..n) -> dst[0..n), two records per 16-byte device-coherent load.  Each
+// 8-byte record is read whole (it sits in one aligned 8-byte word), so a pair is complete once
+// both halves carry the epoch.
+__device__ __forceinline__ bool gather_vec_impl(MK_G MkCtl* ctl, u32 epoch, const MK_G mk_u64* src, int n,
+                                            LS float* dst) {
+  Ctx cx;
+  cx.ctl = uni_ptr(ctl);
+  cx.epoch = (u32)uni((int)epoch);
+  src = uni_ptr(src);
+  n = uni(n);
+  const u32 e = cx.epoch;
+  const int pl = tid() - NCT;
+  const int np = (n + 1) >> 1;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, np * 16, 0x00020000);
+  for (int base = 0; base < np; base += NPT * PB) {
+    u32 pending = 0;
+#pragma unroll
+    for (int k = 0; k < PB; ++k)
+      if (base + k * NPT + pl < np) pending |= 1u << k;
+    u32 spins = 0;
+    while (pending) {
+      u32x4 v[PB];
+#pragma unroll
+      for (int k = 0; k < PB; ++k)
+        if ((pending >> k) & 1u)
+          v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + k * NPT + pl) * 16, 0, 16 /* sc1 */);
+#pragma unroll
+      for (int k = 0; k < PB; ++k) {
+        const int j = base + k * NPT + pl;
+        const bool two = 2 * j + 1 < n;
+        if (((pending >> k) & 1u) && v[k].y == e && (!two || v[k].w == e)) {
+          dst[2 * j] = __uint_as_float(v[k].x);
+          if (two) dst[2 * j + 1] = __uint_as_float(v[k].z);
+          pending &= ~(1u << k);
+        }
+      }
+      if (pending) {
+        ++spins;
+        if ((spins & 255u) == 0 && err_seen(cx)) return false;
+        if (spins > MK_SPIN_LIMIT) {
+          set_err(cx, 1u);
+          return false;
+        }
+      }
+    }
+  }
+  return true;
+}
+
+__device__ __forceinline__ bool gather_vec(const Ctx& cx, const MK_G mk_u64* src, int n, LS float* dst) {
+  if (streamer()) return true;
+  return gather_vec_impl(cx.ctl, cx.epoch, src, n, dst);
+}
+
 // ------------------------------------------------------------------------ GEMV
-// out[r] = W[r] . x for the R rows of a workgroup's slice (row stride K).  Work unit = (row r,
-// 512-column segment s), u = r*S + s; compute wave w takes units w, w + 7, ...; lane l covers columns
-// [s*512 + 8l, +8) with one 16-byte load.  A unit's partial is reduced over lanes in a fixed DPP
-// order and parked in LDS; a row's value is its segment partials added in segment order.  So a
-// row's result does not depend on how rows are split over workgroups.  Rows are processed in
-// blocks that fit RED_CAP unit partials.  The first `npf` units of a lane come from the wave's LDS
-// stage (filled earlier by gemv_stage); the rest stream through registers two batches deep.
+// out[r] = W[r] . x for the R rows of a workgroup's slice (row stride K).  A unit is 4 rows x 512
+// columns (4 KB of BF16): 16 lanes per row, each lane 8 columns of each of the unit's four 128-column
+// slots, so one wave instruction reads 4 rows x 256 contiguous bytes.  A unit's partial is reduced
+// over its 16 lanes in a fixed DPP order and parked in LDS; a row's value adds its 512-column
+// segment partials in segment order, so it does not depend on how rows are split over workgroups.
 struct Gemv {
   const MK_G uint16_t* W;
-  int R, K, S, rb;  // rb = rows per block
+  int R, K, S;  // rows, columns, 512-column segments
   __device__ __forceinline__ void init(const MK_G uint16_t* W_, int R_, int K_) {
     W = W_;
     R = R_;
     K = K_;
     S = (K + 511) >> 9;
-    rb = max(2, (RED_CAP / S) & ~1);
   }
-  // units of this lane in the block starting at row b0
-  __device__ __forceinline__ int units(int b0) const {
-    const int U = min(rb, R - b0) * S;
-    return (wave() < MK_NCW && U > wave()) ? (U - wave() + MK_NCW - 1) / MK_NCW : 0;
+  __device__ __forceinline__ int units() const { return ((R + 3) >> 2) * S; }
+  __device__ __forceinline__ int chunk_rows() const { return max(4, (MK_RED_CAP / S) & ~3); }
+  // this lane's 16 bytes of slot k of unit u; null outside the matrix
+  __device__ __forceinline__ const MK_G uint16_t* addr(int u, int k) const {
+    const int rb = u / S, s = u - rb * S;
+    const int row = rb * 4 + (lane() >> 4);
+    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
+    return (row < R && col < K) ? W + (size_t)row * K + col : nullptr;
   }
-  __device__ __forceinline__ const MK_G uint16_t* addr(int b0, int i) const {
-    const int u = wave() + MK_NCW * i;
-    const int r = u / S, s = u - r * S;
-    const int k = s * 512 + lane_here() * 8;
-    return k < K ? W + (size_t)(b0 + r) * K + k : nullptr;
-  }
+  // slot k of unit u holds columns of the matrix (uniform over the wave)
+  __device__ __forceinline__ bool live(int u, int k) const { return (u % S) * 512 + k * 128 < K; }
 };
 
-struct RegBatch {
-  u32x4 c[PF_REG];
-};
+// Units staged for g: the first min(units of its first row chunk, cap) units.
+__device__ __forceinline__ int staged_units(const Gemv& g, int cap) {
+  Gemv c0 = g;
+  c0.R = min(g.R, g.chunk_rows());
+  return min(c0.units(), cap);
+}
 
-// first npf units of this lane (block 0) -> the wave's LDS stage, 1 KB per unit slot
-template <int NPF>
-__device__ __forceinline__ void gemv_stage(const Gemv& g, LS u32x4* stage) {
-  const int n = g.units(0);  // 0 on the poller wave
+// First units of g -> stage slots [4u, 4u + 4): streaming wave c copies slot c of every unit.
+// Returns the number of copies this wave issued.
+__device__ __forceinline__ int gemv_stage_impl(const MK_G uint16_t* W, int R, int K, LS u32x4* stage, int cap) {
+  Gemv g;
+  g.init(uni_ptr(W), uni(R), uni(K));
+  const int n = staged_units(g, uni(cap));
+  const int c = wave();
+  int cnt = 0;
+  for (int u = 0; u < n; ++u) {
+    if (g.live(u, c)) {
+      const MK_G uint16_t* a = g.addr(u, c);
+      if (a) dma16(a, stage + (u * USLOTS + c) * SLOT);
+      ++cnt;  // lanes 0..15 (the unit's first row) are always live here, so the copy is issued
+    }
+  }
+  return cnt;
+}
+
+__device__ __forceinline__ int gemv_stage(const Gemv& g, LS u32x4* stage, int cap) {
+  if (!streamer()) return 0;
+  return gemv_stage_impl(g.W, g.R, g.K, stage, cap);
+}
+
+__device__ __forceinline__ float unit_dot(const Gemv& g, int u, const u32x4* w, const LS float* x) {
+  const int s = u % g.S;
+  float acc = 0.f;
 #pragma unroll
-  for (int b = 0; b < NPF; ++b) {
-    const MK_G uint16_t* a = (b < n) ? g.addr(0, b) : nullptr;
-    if (a) dma16(a, stage + b * 64);
+  for (int k = 0; k < USLOTS; ++k) {
+    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
+    if (col < g.K) acc += dot8(w[k], x + col);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void put_partial(const Gemv& g, int u, float v, LS float* red) {
+  if ((lane() & 15) == 0) {
+    const int rb = u / g.S, s = u - rb * g.S;
+    const int row = rb * 4 + (lane() >> 4);
+    if (row < g.R) red[row * g.S + s] = v;
   }
 }
 
-__device__ __forceinline__ void gemv_issue(RegBatch& rb, const Gemv& g, int b0, int i0, int n) {
+// a row's segment partials added in segment order; loads are issued eight at a time
+__device__ __forceinline__ float seg_sum(const LS float* p, int S) {
+  float v = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float t[8];
 #pragma unroll
-  for (int b = 0; b < PF_REG; ++b) {
-    const MK_G uint16_t* a = (i0 + b < n) ? g.addr(b0, i0 + b) : nullptr;
-    rb.c[b] = a ? ldw(a) : u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < 8; ++k) t[k] = s0 + k < S ? p[s0 + k] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < S) v += t[k];
+  }
+  return v;
+}
+
+template <int N>
+struct RegUnits {
+  u32x4 c[N * USLOTS];
+};
+
+template <int N>
+__device__ __forceinline__ void issue_units(RegUnits<N>& r, const Gemv& g, int u0, int stride, int uend) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int u = u0 + i * stride;
+#pragma unroll
+    for (int k = 0; k < USLOTS; ++k) {
+      const MK_G uint16_t* a = u < uend ? g.addr(u, k) : nullptr;
+      r.c[i * USLOTS + k] = a ? ldw(a) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
+// The staged units must be complete and visible (their streaming waves waited for their copies
+// before the barrier that precedes this call).  Units beyond the stage stream through registers,
+// on the streaming waves (ALL_STREAM: on every wave; only where no poll is pending).
 // PAIRS == false: epi(row, value) once per row; PAIRS == true: epi(pair, v_even, v_odd) once per
-// row pair (block sizes are even).  Row/pair indices are relative to the slice.
-template <int NPF, bool PAIRS, typename Epi>
-__device__ __forceinline__ void gemv(const Gemv& g, const LS float* xin, const LS u32x4* stage, LS float* red,
-                                     Tracer& tr, Epi epi) {
-  wait_vm();
-  keep_issued();
-  tr.mark();
-  for (int b0 = 0; b0 < g.R; b0 += g.rb) {
-    const int nr = min(g.rb, g.R - b0);
-    const int n = g.units(b0);
-    const int first = b0 == 0 ? NPF : 0;
-    RegBatch cur;
-    if (n > first) gemv_issue(cur, g, b0, first, n);
-    keep_issued();
-    auto consume = [&](int i, u32x4 wv) {
-      const int u = wave() + MK_NCW * i;
-      const int r = u / g.S, s = u - r * g.S;
-      const int k = s * 512 + lane() * 8;
-      const float d = wave_sum(k < g.K ? dot8(wv, xin + k) : 0.f);
-      if (lane() == 0) red[u] = d;
-    };
-    if (b0 == 0) {
+// row pair (slices hold whole pairs).  The epilogue runs on streaming threads (EPI_ALL: on all).
+// Unit partials of one row chunk -> red[row * S + segment].
+template <bool ALL_STREAM>
+__device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int K, int nst, const LS float* xin,
+                                           const LS u32x4* stage, LS float* red) {
+  Gemv g;
+  g.init(uni_ptr(W), uni(R), uni(K));
+  nst = uni(nst);
+  const int U = g.units();
+    // staged units, two per wave per round
+    for (int u0 = wave(); u0 < nst; u0 += 2 * MK_NWAVE) {
+      const int u1 = u0 + MK_NWAVE;
+      u32x4 w0[USLOTS], w1[USLOTS];
 #pragma unroll
-      for (int b = 0; b < NPF; ++b)
-        if (b < n) consume(b, stage[b * 64 + lane()]);
+      for (int k = 0; k < USLOTS; ++k) {
+        w0[k] = stage[(u0 * USLOTS + k) * SLOT + lane()];
+        w1[k] = u1 < nst ? stage[(u1 * USLOTS + k) * SLOT + lane()] : u32x4{0u, 0u, 0u, 0u};
+      }
+      float a0 = unit_dot(g, u0, w0, xin);
+      float a1 = u1 < nst ? unit_dot(g, u1, w1, xin) : 0.f;
+      a0 = row_sum16(a0);
+      a1 = row_sum16(a1);
+      put_partial(g, u0, a0, red);
+      if (u1 < nst) put_partial(g, u1, a1, red);
     }
-    for (int i0 = first; i0 < n; i0 += PF_REG) {
-      RegBatch nxt;
-      gemv_issue(nxt, g, b0, i0 + PF_REG, n);
-      keep_issued();
+    // the rest through registers, two units per batch, two batches in flight
+    if (ALL_STREAM || streamer()) {
+      const int nsw = ALL_STREAM ? MK_NWAVE : NCW;
+      const int first = nst + wave();
+      if (first < U) {
+        RegUnits<2> cur, nxt;
+        issue_units<2>(cur, g, first, nsw, U);
+        keep_issued();
+        for (int u = first; u < U; u += 2 * nsw) {
+          issue_units<2>(nxt, g, u + 2 * nsw, nsw, U);
+          keep_issued();
+          float a0 = unit_dot(g, u, cur.c, xin);
+          float a1 = u + nsw < U ? unit_dot(g, u + nsw, cur.c + USLOTS, xin) : 0.f;
+          a0 = row_sum16(a0);
+          a1 = row_sum16(a1);
+          put_partial(g, u, a0, red);
+          if (u + nsw < U) put_partial(g, u + nsw, a1, red);
 #pragma unroll
-      for (int b = 0; b < PF_REG; ++b)
-        if (i0 + b < n) consume(i0 + b, cur.c[b]);
-#pragma unroll
-      for (int b = 0; b < PF_REG; ++b) cur.c[b] = nxt.c[b];
-    }
-    tr.mark();
-    __syncthreads();
-    tr.mark();
-    if (PAIRS) {
-      for (int t = tid(); t < nr / 2; t += MK_NT) {
-        float v0 = 0.f, v1 = 0.f;
-        for (int s = 0; s < g.S; ++s) {
-          v0 += red[(2 * t) * g.S + s];
-          v1 += red[(2 * t + 1) * g.S + s];
+          for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = nxt.c[i];
         }
-        epi(b0 / 2 + t, v0, v1);
-      }
-    } else {
-      for (int t = tid(); t < nr; t += MK_NT) {
-        float v = 0.f;
-        for (int s = 0; s < g.S; ++s) v += red[t * g.S + s];
-        epi(b0 + t, v, 0.f);
       }
     }
-    __syncthreads();
+}
+
+template <bool PAIRS, bool EPI_ALL, bool ALL_STREAM, typename Epi>
+__device__ __forceinline__ void gemv(const Gemv& G, const LS float* xin, const LS u32x4* stage, int cap,
+                                     LS float* red, Tracer& tr, Epi epi) {
+  const int rc = G.chunk_rows();
+  for (int r0 = 0; r0 < G.R; r0 += rc) {
+    Gemv g;
+    g.init(G.W + (size_t)r0 * G.K, min(rc, G.R - r0), G.K);
+    const int nst = r0 == 0 ? min(g.units(), cap) : 0;
+    gemv_partials<ALL_STREAM>(g.W, g.R, g.K, nst, xin, stage, red);
+    tr.mark();
+    wg_bar();
+    tr.mark();
+    const int stride = EPI_ALL ? MK_NT : NCT;
+    if (EPI_ALL || streamer()) {
+      if (PAIRS) {
+        for (int t = tid(); t < g.R / 2; t += stride) epi(r0 / 2 + t, seg_sum(red + (2 * t) * g.S, g.S),
+                                                          seg_sum(red + (2 * t + 1) * g.S, g.S));
+      } else {
+        for (int t = tid(); t < g.R; t += stride) epi(r0 + t, seg_sum(red + t * g.S, g.S), 0.f);
+      }
+    }
+    if (r0 + rc < G.R) wg_bar();  // red is reused by the next chunk
   }
 }
 
-__device__ __forceinline__ void rmsnorm_lds(const LS float* x, const MK_G float* __restrict__ gain, LS float* xn, int D,
-                                            float eps, LS float* scr) {
+// x -> xn = x / sqrt(mean x^2 + eps) * g.  Every wave sums the squares itself (same order in every
+// wave), so only the barrier that publishes xn is needed.
+__device__ __forceinline__ void rmsnorm(const LS float* x, const LS uint16_t* g, LS float* xn, int D, float eps,
+                                        Tracer& tr) {
+  D = uni(D);
+  const int D4 = D >> 2;  // D is a multiple of 8
+  const LS float4* x4 = (const LS float4*)x;
+  // four float4 loads in flight per lane before any of them is used
   float s = 0.f;
-  for (int i = tid(); i < D; i += MK_NT) s += x[i] * x[i];
-  s = block_sum(s, scr);
+  for (int c0 = lane(); c0 < D4; c0 += 256) {
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = float4{0.f, 0.f, 0.f, 0.f};
+      if (c0 + 64 * k < D4) v[k] = x4[c0 + 64 * k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s = fmaf(v[k].x, v[k].x, s);
+      s = fmaf(v[k].y, v[k].y, s);
+      s = fmaf(v[k].z, v[k].z, s);
+      s = fmaf(v[k].w, v[k].w, s);
+    }
+  }
+  s = wave_sum(s);
   const float r = 1.0f / sqrtf(s / (float)D + eps);
-  for (int i = tid(); i < D; i += MK_NT) xn[i] = x[i] * r * gain[i];
-  __syncthreads();
+  tr.mark();
+  for (int c = tid(); c < D4; c += MK_NT) {
+    const float4 v = x4[c];
+    const uint2 gg = *(const LS uint2*)(g + 4 * c);
+    float4 o;
+    o.x = v.x * r * __uint_as_float(gg.x << 16);
+    o.y = v.y * r * __uint_as_float(gg.x & 0xffff0000u);
+    o.z = v.z * r * __uint_as_float(gg.y << 16);
+    o.w = v.w * r * __uint_as_float(gg.y & 0xffff0000u);
+    ((LS float4*)xn)[c] = o;
+  }
+  tr.mark();
+  wg_bar();
+}
+
+// BF16 gains [n] -> LDS (streaming waves, one 1 KB copy per slot); returns copies issued by this wave
+__device__ __forceinline__ int gain_stage(const MK_G uint16_t* src, int n, LS uint16_t* dst) {
+  if (!streamer()) return 0;
+  const int bytes = 2 * n, nslots = (bytes + 1023) >> 10;
+  int cnt = 0;
+  for (int j = wave(); j < nslots; j += NCW) {
+    const int off = j * 1024 + lane() * 16;
+    if (off < bytes) dma16((const MK_G char*)src + off, (LS char*)dst + j * 1024);
+    ++cnt;
+  }
+  return cnt;
+}
+
+__device__ __forceinline__ MkLayerDev layer_desc(const LS MkLayerDev* d, int l) {
+  MkLayerDev out;
+  const LS u32* src = (const LS u32*)(d + l);
+  u32* dst = (u32*)&out;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(MkLayerDev) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+  return out;
 }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 __device__ __forceinline__ float softplusf_(float z) { return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z))); }
 
-struct Lds {
-  LS float* x;     // residual [D]
-  LS float* xn;    // normalised residual [D]
-  LS float* vec;   // gathered mixer output / FFN hidden, argmax records
-  LS float* att;   // gathered DeltaNet inputs, attention scratch, combine staging
-  LS float* red;   // GEMV unit partials
-  LS float* scr;   // reductions
-  LS u32x4* stA;   // this wave's large prefetch stage (8 x 1 KB)
-  LS u32x4* stB;   // this wave's small prefetch stage (4 x 1 KB)
-};
-
 // ------------------------------------------------------------------------ DeltaNet
-// state rows [s0, s1) of this workgroup: compute wave w stages rows s0 + w + 7k (k < SR) in its large
-// LDS stage, element e = lane + 64t of row k at float offset (4k + t) * 64 + lane
-__device__ __forceinline__ void state_stage(const MkDecodeParams& p, const MkLayerDev& L, int s0, int s1,
-                                            LS u32x4* stage) {
-  LS float* st = (LS float*)stage;
-  if (wave() >= MK_NCW) return;
-#pragma unroll
-  for (int k = 0; k < SR; ++k) {
-    const int row = s0 + wave() + MK_NCW * k;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int e = lane() + 64 * t;
-      if (row < s1 && e < p.dk) dma4(L.S + (size_t)row * p.dk + e, st + (4 * k + t) * 64);
-    }
+// state rows [s0, s1) -> stage slots: dk/4 lanes per row, 64/(dk/4) rows per slot.  Returns copies
+// issued by this wave.
+__device__ __forceinline__ int state_stage(const MkDecodeParams& p, const MkLayerDev& L, int s0, int s1,
+                                           LS u32x4* stage, int max_slots) {
+  if (!streamer()) return 0;
+  const int lpr = p.dk >> 2, rps = 64 / lpr;
+  const int nslots = min((s1 - s0 + rps - 1) / rps, max_slots);
+  int cnt = 0;
+  for (int j = wave(); j < nslots; j += NCW) {
+    const int r = s0 + j * rps + lane() / lpr;
+    if (lane() < rps * lpr && r < s1) dma16(L.S + (size_t)r * p.dk + (lane() % lpr) * 4, stage + j * SLOT);
+    ++cnt;  // the slot's first row is always in range
   }
+  return cnt;
 }
 
-// gated delta rule on rows [s0, s1) of S; o = S q read after the update -> records
+// gated delta rule on rows [s0, s1) of S; o = S q read after the update -> records.  Rows of
+// staged slots come from LDS, the rest straight from HBM.  Streaming waves own the rows.
 __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                         int s0, int s1, Tracer& tr) {
+                                         int s0, int s1, int st_slots, int wait_after, Tracer& tr) {
   const int H = p.H, dk = p.dk, dv = p.dv;
-  if (s0 >= s1) return true;
-  const int h0 = s0 / dv, h1 = (s1 - 1) / dv;
+  const int lpr = dk >> 2, rps = 64 / lpr;
   LS float* q = s.att;
   LS float* k = s.att + dk;
   LS float* ab = s.att + 2 * dk;
   LS float* vr = s.att + 2 * dk + 2;
+  const LS float* st = (const LS float*)s.stB;
   const MK_G mk_u64* in = L.ll_in;
   const int off_k = H * dk, off_v = 2 * H * dk, off_a = 2 * H * dk + H * dv, off_b = off_a + H;
+  bool first = true;
+  const int h0 = s0 < s1 ? s0 / dv : 0, h1 = s0 < s1 ? (s1 - 1) / dv : -1;
   for (int h = h0; h <= h1; ++h) {
     const int i0 = max(s0, h * dv) - h * dv, i1 = min(s1, (h + 1) * dv) - h * dv;
     const int nv = i1 - i0;
     const int n = 2 * dk + 2 + nv;
-    const bool ok = ll_gather(cx, n, [=](int f) {
+    const bool ok = gather_map(cx, n, [=](int f) {
       if (f < dk) return in + h * dk + f;
       if (f < 2 * dk) return in + off_k + h * dk + (f - dk);
       if (f == 2 * dk) return in + off_a + h;
       if (f == 2 * dk + 1) return in + off_b + h;
       return in + off_v + h * dv + i0 + (f - 2 * dk - 2);
-    }, s.att);
-    if (__syncthreads_or(!ok)) return false;
-    wait_vm();
+    }, [=](int f, float v) { s.att[f] = v; });
     tr.mark();
-    float qq = 0.f, kk = 0.f;
-    for (int e = tid(); e < dk; e += MK_NT) {
-      qq += q[e] * q[e];
-      kk += k[e] * k[e];
-    }
-    block_sum2(qq, kk, s.scr);
-    const float sq = 1.0f / sqrtf(qq + p.l2_eps);
-    const float sk = 1.0f / sqrtf(kk + p.l2_eps);
-    const float alpha = expf(-softplusf_(ab[0]));
-    const float beta = sigmoidf_(ab[1]);
-    // rows of head h owned by this compute wave: local index li = row - s0 with li % 7 == wave
-    const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
-    const LS float* st = (const LS float*)s.stA;
-    const int first_li = wave() < MK_NCW ? lo + ((wave() - lo % MK_NCW) + MK_NCW) % MK_NCW : hi;
-    for (int li = first_li; li < hi; li += MK_NCW) {
-      const int row = s0 + li;
-      const int kslot = li / MK_NCW;
-      float sr[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int e = lane() + 64 * t;
-        float v = 0.f;
-        if (e < dk) v = kslot < SR ? st[(4 * kslot + t) * 64 + lane()] : L.S[(size_t)row * dk + e];
-        sr[t] = v;
+    if (first && streamer()) wait_vm_n(wait_after);  // the staged state rows
+    first = false;
+    tr.mark();
+    if (wg_bar_or(s, !ok)) return false;
+    tr.mark();
+    if (streamer()) {
+      float qq = 0.f, kk = 0.f;
+      for (int e = lane(); e < dk; e += 64) {
+        qq = fmaf(q[e], q[e], qq);
+        kk = fmaf(k[e], k[e], kk);
       }
-      float kd = 0.f;
+      qq = wave_sum(qq);
+      kk = wave_sum(kk);
+      const float sq = 1.0f / sqrtf(qq + p.l2_eps);
+      const float sk = 1.0f / sqrtf(kk + p.l2_eps);
+      const float alpha = expf(-softplusf_(ab[0]));
+      const float beta = sigmoidf_(ab[1]);
+      // rows of head h, local index li = row - s0, owned by streaming wave li % NCW
+      const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
+      for (int li = lo + ((wave() - lo % NCW) + NCW) % NCW; li < hi; li += NCW) {
+        const int row = s0 + li;
+        const int sl = li / rps;
+        const bool staged = sl < st_slots;
+        const LS float* srow = st + sl * 256 + (li % rps) * dk;
+        float sr[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int e = lane() + 64 * t;
-        if (e < dk) kd = fmaf(sr[t], k[e] * sk, kd);
-      }
-      kd = wave_sum(kd);
-      const float u = beta * (vr[row - h * dv - i0] - alpha * kd);
-      float od = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int e = lane() + 64 * t;
-        if (e < dk) {
-          const float nv2 = fmaf(u, k[e] * sk, alpha * sr[t]);
-          L.S[(size_t)row * dk + e] = nv2;
-          od = fmaf(nv2, q[e] * sq, od);
+        for (int t = 0; t < 4; ++t) {
+          const int e = lane() + 64 * t;
+          sr[t] = e < dk ? (staged ? srow[e] : L.S[(size_t)row * dk + e]) : 0.f;
         }
+        float kd = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int e = lane() + 64 * t;
+          if (e < dk) kd = fmaf(sr[t], k[e] * sk, kd);
+        }
+        kd = wave_sum(kd);
+        const float u = beta * (vr[row - h * dv - i0] - alpha * kd);
+        float od = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int e = lane() + 64 * t;
+          if (e < dk) {
+            const float nv2 = fmaf(u, k[e] * sk, alpha * sr[t]);
+            L.S[(size_t)row * dk + e] = nv2;
+            od = fmaf(nv2, q[e] * sq, od);
+          }
+        }
+        od = wave_sum(od);
+        if (lane() == 0) ll_put(L.ll_o + row, cx.epoch, od);
       }
-      od = wave_sum(od);
-      if (lane() == 0) ll_put(L.ll_o + row, cx.epoch, od);
     }
-    __syncthreads();
+    tr.mark();
+    wg_bar();  // s.att is reused by the next head
   }
+  if (first && streamer()) wait_vm_n(wait_after);
   return true;
 }
 
 // ------------------------------------------------------------------------ attention
+// K and V rows of work item `it` (16 positions of one KV head) -> stage slots [0, ks) (K) and
+// [ks, 2 ks) (V); hd/4 lanes per position.  Only positions already in the cache (< pos) are
+// copied; position pos comes from the exchange records.  Returns copies issued by this wave.
+__device__ __forceinline__ int kv_slots(int hd) {
+  const int pps = 64 / (hd >> 2);
+  return (ATT_C + pps - 1) / pps;
+}
+__device__ __forceinline__ int kv_stage(const MkDecodeParams& p, const MkLayerDev& L, int it, int pos,
+                                        LS u32x4* stage) {
+  if (!streamer()) return 0;
+  const int lpp = p.hd >> 2, pps = 64 / lpp, ks = kv_slots(p.hd);
+  const int c = it / p.nkv, g = it - c * p.nkv;
+  const int j0 = c * ATT_C, jend = min(pos, j0 + ATT_C);
+  int cnt = 0;
+  for (int q = wave(); q < 2 * ks; q += NCW) {
+    const int v = q >= ks ? 1 : 0;
+    const int sl = q - v * ks;
+    const int j = j0 + sl * pps + lane() / lpp;
+    if (lane() < pps * lpp && j < jend)
+      dma16((v ? L.Vc : L.Kc) + ((size_t)g * p.max_ctx + j) * p.hd + (lane() % lpp) * 4, stage + q * SLOT);
+    if (j0 + sl * pps < jend) ++cnt;
+  }
+  return cnt;
+}
+
 // q/k/v rows in RoPE pair order: rotate q and k at position pos, append k and v to the cache
 __device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                         const Gemv& g, int P0, int pos, Tracer& tr) {
   const int hd = p.hd, half = hd / 2;
-  const MK_G float* cs = p.rope_cos + (size_t)pos * half;
-  const MK_G float* sn = p.rope_sin + (size_t)pos * half;
   MK_G mk_u64* llq = L.ll_in;
   MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   MK_G mk_u64* llv = llk + p.nkv * hd;
   const int nqp = p.nq * half, nkp = p.nkv * half;
-  gemv<PF_A, true>(g, s.xn, s.stA, s.red, tr, [&](int pl, float x1, float x2) {
+  gemv<true, false, false>(g, s.xn, s.stA, A_UNITS, s.att, tr, [&](int pl, float x1, float x2) {
     const int P = P0 + pl;
-    int sec, hh, m;
-    if (P < nqp) {
-      sec = 0;
-      hh = P / half;
-      m = P - hh * half;
-    } else if (P < nqp + nkp) {
-      sec = 1;
-      hh = (P - nqp) / half;
-      m = (P - nqp) - hh * half;
+    if (P < nqp + nkp) {
+      const bool isq = P < nqp;
+      const int Q = isq ? P : P - nqp;
+      const int hh = Q / half, m = Q - hh * half;
+      const float c = s.rope[m], sv = s.rope[half + m];
+      const float y1 = x1 * c - x2 * sv;
+      const float y2 = x2 * c + x1 * sv;
+      if (isq) {
+        ll_put(llq + hh * hd + m, cx.epoch, y1);
+        ll_put(llq + hh * hd + m + half, cx.epoch, y2);
+      } else {
+        const size_t co = ((size_t)hh * p.max_ctx + pos) * hd + m;
+        ll_put(llk + hh * hd + m, cx.epoch, y1);
+        ll_put(llk + hh * hd + m + half, cx.epoch, y2);
+        L.Kc[co] = y1;
+        L.Kc[co + half] = y2;
+      }
     } else {
-      sec = 2;
-      hh = (P - nqp - nkp) / half;
-      m = (P - nqp - nkp) - hh * half;
-    }
-    float y1 = x1, y2 = x2;
-    if (sec < 2) {
-      const float c = cs[m], sv = sn[m];
-      y1 = x1 * c - x2 * sv;
-      y2 = x2 * c + x1 * sv;
-    }
-    const size_t co = ((size_t)hh * p.max_ctx + pos) * hd + m;
-    if (sec == 0) {
-      ll_put(llq + hh * hd + m, cx.epoch, y1);
-      ll_put(llq + hh * hd + m + half, cx.epoch, y2);
-    } else if (sec == 1) {
-      ll_put(llk + hh * hd + m, cx.epoch, y1);
-      ll_put(llk + hh * hd + m + half, cx.epoch, y2);
-      L.Kc[co] = y1;
-      L.Kc[co + half] = y2;
-    } else {
-      ll_put(llv + hh * hd + m, cx.epoch, y1);
-      ll_put(llv + hh * hd + m + half, cx.epoch, y2);
-      L.Vc[co] = y1;
-      L.Vc[co + half] = y2;
+      const int Q = P - nqp - nkp;
+      const int hh = Q / half, m = Q - hh * half;
+      const size_t co = ((size_t)hh * p.max_ctx + pos) * hd + m;
+      ll_put(llv + hh * hd + m, cx.epoch, x1);
+      ll_put(llv + hh * hd + m + half, cx.epoch, x2);
+      L.Vc[co] = x1;
+      L.Vc[co + half] = x2;
     }
   });
 }
 
-// K/V rows of one attention work item: a 4-float slice of one position per thread, two passes;
-// staged in the wave's large LDS stage, slot 2 * pass + {0: K, 1: V}
-constexpr int ATT_PASSES = 3;
-struct AttGeo {
-  int tpp, ppp;  // threads per position, positions per pass (compute threads only)
-  __device__ __forceinline__ void init(int hd) {
-    tpp = hd / 4;
-    ppp = MK_NCT / tpp;
-  }
-};
-
-__device__ __forceinline__ void kv_stage(const MkDecodeParams& p, const MkLayerDev& L, const AttGeo& ag, int it,
-                                         int pos, LS u32x4* stage) {
+// Split-K partial softmax attention.  Item = (chunk of 16 positions, KV head g); for each of the
+// gs query heads of group g it emits (max m, sum l, acc[hd]) over its positions.  Scores: one thread
+// per (head, position), a 16-lane DPP row per head for the max and the sum.
+__device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
+                                          int NW, int w, int pos, int wait_first, Tracer& tr) {
+  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv;
   const int Lpos = pos + 1;
-  const int c = it / p.nkv, g = it - c * p.nkv;
-  const int j0 = c * MK_ATT_CHUNK, j1 = min(Lpos, j0 + MK_ATT_CHUNK);
-  const int q4 = tid() % ag.tpp;
-#pragma unroll
-  for (int ps = 0; ps < ATT_PASSES; ++ps) {
-    const int jj = tid() / ag.tpp + ps * ag.ppp;
-    const int j = j0 + jj;
-    if (tid() < ag.tpp * ag.ppp && j < j1 && j < pos) {
-      const size_t off = ((size_t)g * p.max_ctx + j) * p.hd + 4 * q4;
-      dma16(L.Kc + off, stage + (2 * ps) * 64);
-      dma16(L.Vc + off, stage + (2 * ps + 1) * 64);
-    }
-  }
-}
-
-// split-K partial softmax attention: item = (kv head g, chunk of MK_ATT_CHUNK positions); emits
-// (max m, sum l, acc[hd]) per query head of group g
-__device__ __forceinline__ bool att_partial(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx,
-                                            const Lds& s, int NW, int w, int pos, const AttGeo& ag) {
-  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, C = MK_ATT_CHUNK;
-  const int Lpos = pos + 1;
-  const int nch = (Lpos + C - 1) / C;
-  const int items = nch * nkv;
+  const int items = ((Lpos + ATT_C - 1) / ATT_C) * nkv;
   const float scale = 1.0f / sqrtf((float)hd);
-  LS float* qv = s.att;                  // [gs][hd]
-  LS float* kpos = qv + gs * hd;         // [hd]
-  LS float* vpos = kpos + hd;            // [hd]
-  LS float* vst = vpos + hd;             // [C][hd]
-  LS float* sp = vst + C * hd;           // [gs][C][tpp]
-  LS float* sc = sp + gs * C * ag.tpp;   // [gs][C]
-  LS float* ml = sc + gs * C;            // [gs][2]
+  const int lpp = hd >> 2, pps = 64 / lpp, ks = kv_slots(hd);
+  LS float* qv = s.att;                // [gs][hd]
+  LS float* kpos = qv + gs * hd;       // [hd]
+  LS float* vpos = kpos + hd;          // [hd]
+  LS float* pb = vpos + hd;            // [gs][16] probabilities (unnormalised)
+  LS float* ml = pb + gs * ATT_C;      // [gs][2]
+  const LS float* stf = (const LS float*)s.stB;
   const MK_G mk_u64* llq = L.ll_in;
   const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   const MK_G mk_u64* llv = llk + nkv * hd;
+  (void)lpp;
   for (int it = w; it < items; it += NW) {
-    if (it != w) kv_stage(p, L, ag, it, pos, s.stA);
-    keep_issued();
     const int c = it / nkv, g = it - c * nkv;
-    const int j0 = c * C, j1 = min(Lpos, j0 + C);
-    const int nj = j1 - j0;
-    const bool has_pos = (j1 == Lpos);
+    const int j0 = c * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
+    const bool has_pos = j0 + nj == Lpos;
+    if (it != w) kv_stage(p, L, it, pos, s.stB);
     const int n = gs * hd + (has_pos ? 2 * hd : 0);
-    const bool ok = ll_gather(cx, n, [=](int f) {
+    const bool ok = gather_map(cx, n, [=](int f) {
       if (f < gs * hd) return llq + g * gs * hd + f;
       if (f < gs * hd + hd) return llk + g * hd + (f - gs * hd);
       return llv + g * hd + (f - gs * hd - hd);
-    }, s.att);
-    if (__syncthreads_or(!ok)) return false;
-    wait_vm();
-    // scores: partial dot products over 4 dims per thread, summed over the position's threads in LDS
-    const int q4 = tid() % ag.tpp;
-#pragma unroll
-    for (int ps = 0; ps < ATT_PASSES; ++ps) {
-      const int jj = tid() / ag.tpp + ps * ag.ppp;
-      if (tid() < ag.tpp * ag.ppp && jj < nj) {
+    }, [=](int f, float v) { s.att[f] = v; });
+    tr.mark();
+    if (streamer()) {
+      if (it == w) wait_vm_n(wait_first);
+      else wait_vm<0>();
+    }
+    tr.mark();
+    if (wg_bar_or(s, !ok)) return false;
+    tr.mark();
+    // scores, softmax numerators, row max and sum (whole rows of 16 lanes take part in the DPP)
+    const int t = tid();
+    if (t < gs * ATT_C) {
+      const int i = t >> 4, jj = t & 15;
+      const bool valid = jj < nj;
+      float sc = -INFINITY;
+      if (valid) {
         const int j = j0 + jj;
-        float4 kk, vv;
-        if (j != pos) {
-          const u32x4 kr = s.stA[(2 * ps) * 64 + lane()];
-          const u32x4 vr = s.stA[(2 * ps + 1) * 64 + lane()];
-          kk = float4{__uint_as_float(kr.x), __uint_as_float(kr.y), __uint_as_float(kr.z), __uint_as_float(kr.w)};
-          vv = float4{__uint_as_float(vr.x), __uint_as_float(vr.y), __uint_as_float(vr.z), __uint_as_float(vr.w)};
-        } else {
-          kk = *(const LS float4*)(kpos + 4 * q4);
-          vv = *(const LS float4*)(vpos + 4 * q4);
+        const LS float* kr = j == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
+        const LS float* qr = qv + i * hd;
+        const int n4 = hd >> 2;
+        const int start = jj % n4;  // staggered start: the 16 positions of a row read different banks
+        float a = 0.f;
+        for (int d0 = 0; d0 < n4; d0 += 8) {
+          float4 kk[8], qq[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            int dd = d0 + k + start;
+            dd = (dd >= n4 ? dd - n4 : dd) * 4;
+            kk[k] = float4{0.f, 0.f, 0.f, 0.f};
+            qq[k] = kk[k];
+            if (d0 + k < n4) {
+              kk[k] = *(const LS float4*)(kr + dd);
+              qq[k] = *(const LS float4*)(qr + dd);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            a = fmaf(kk[k].x, qq[k].x, a);
+            a = fmaf(kk[k].y, qq[k].y, a);
+            a = fmaf(kk[k].z, qq[k].z, a);
+            a = fmaf(kk[k].w, qq[k].w, a);
+          }
         }
-        *(LS float4*)(vst + jj * hd + 4 * q4) = vv;
-        for (int i = 0; i < gs; ++i) {
-          const float4 qq = *(const LS float4*)(qv + i * hd + 4 * q4);
-          float d = kk.x * qq.x;
-          d = fmaf(kk.y, qq.y, d);
-          d = fmaf(kk.z, qq.z, d);
-          d = fmaf(kk.w, qq.w, d);
-          sp[(i * C + jj) * ag.tpp + q4] = d;
-        }
+        sc = a * scale;
+      }
+      const float m = row_max16(sc);
+      const float e = valid ? expf(sc - m) : 0.f;
+      const float l = row_sum16(e);
+      pb[i * ATT_C + jj] = e;
+      if (jj == 0) {
+        ml[2 * i] = m;
+        ml[2 * i + 1] = l;
       }
     }
-    __syncthreads();
-    for (int t = tid(); t < gs * nj; t += MK_NT) {
-      const int i = t / nj, jj = t - i * nj;
-      float d = 0.f;
-      for (int u = 0; u < ag.tpp; ++u) d += sp[(i * C + jj) * ag.tpp + u];
-      sc[i * C + jj] = d * scale;
-    }
-    __syncthreads();
-    if (tid() < gs) {
-      const int i = tid();
-      float m = -INFINITY;
-      for (int jj = 0; jj < nj; ++jj) m = fmaxf(m, sc[i * C + jj]);
-      float l = 0.f;
-      for (int jj = 0; jj < nj; ++jj) {
-        const float e = expf(sc[i * C + jj] - m);
-        sc[i * C + jj] = e;
-        l += e;
+    tr.mark();
+    wg_bar();
+    tr.mark();
+    if (streamer()) {
+      MK_G mk_u64* part = L.ll_part + (size_t)it * gs * (hd + 2);
+      for (int o = tid(); o < gs * hd; o += NCT) {
+        const int i = o / hd, d = o - i * hd;
+        float pv[ATT_C], vv[ATT_C];
+#pragma unroll
+        for (int jj = 0; jj < ATT_C; ++jj) {
+          pv[jj] = pb[i * ATT_C + jj];  // zero beyond nj
+          vv[jj] = 0.f;
+          if (jj < nj) vv[jj] = (j0 + jj == pos) ? vpos[d] : stf[(ks + jj / pps) * 256 + (jj % pps) * hd + d];
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < ATT_C; ++jj) a = fmaf(pv[jj], vv[jj], a);
+        ll_put(part + i * (hd + 2) + 2 + d, cx.epoch, a);
       }
-      ml[2 * i] = m;
-      ml[2 * i + 1] = l;
+      if (tid() < 2 * gs) ll_put(part + (tid() >> 1) * (hd + 2) + (tid() & 1), cx.epoch, ml[tid()]);
     }
-    __syncthreads();
-    MK_G mk_u64* part = L.ll_part + (size_t)it * gs * (hd + 2);
-    for (int t = tid(); t < gs * hd; t += MK_NT) {
-      const int i = t / hd, d = t - i * hd;
-      float a = 0.f;
-      for (int jj = 0; jj < nj; ++jj) a = fmaf(sc[i * C + jj], vst[jj * hd + d], a);
-      ll_put(part + i * (hd + 2) + 2 + d, cx.epoch, a);
-    }
-    if (tid() < 2 * gs) ll_put(part + (tid() >> 1) * (hd + 2) + (tid() & 1), cx.epoch, ml[tid()]);
-    __syncthreads();
+    wg_bar();  // LDS and the KV slots are reused by the next item
   }
+  if (w >= items && streamer()) wait_vm_n(wait_first);
   return true;
 }
 
@@ -654,17 +863,16 @@ __device__ __forceinline__ bool att_partial(const MkDecodeParams& p, const MkLay
 __device__ __forceinline__ bool att_combine(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                             int o0, int o1, int pos) {
   const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv;
-  const int nch = (pos + MK_ATT_CHUNK) / MK_ATT_CHUNK;
+  const int nch = (pos + ATT_C) / ATT_C;
   const int nown = o1 - o0;
   if (nown <= 0) return true;
   LS float* stage = s.att;
-  const int cap = 2048;
-  const int vpp = max(1, cap / nch);
+  const int vpp = max(1, MK_RED_CAP / (3 * nch));
   const MK_G mk_u64* part = L.ll_part;
   for (int v0 = 0; v0 < nown; v0 += vpp) {
     const int vn = min(vpp, nown - v0);
     const int n = vn * nch * 3;
-    const bool ok = ll_gather(cx, n, [=](int f) {
+    const bool ok = gather_map(cx, n, [=](int f) {
       const int which = f % 3;
       const int vc = f / 3;
       const int v = vc / nch, c = vc - v * nch;
@@ -673,21 +881,27 @@ __device__ __forceinline__ bool att_combine(const MkDecodeParams& p, const MkLay
       const int g = i / gs, il = i - g * gs;
       const MK_G mk_u64* rec = part + ((size_t)(c * nkv + g) * gs + il) * (hd + 2);
       return rec + (which == 2 ? 2 + d : which);
-    }, stage);
-    if (__syncthreads_or(!ok)) return false;
-    for (int v = tid(); v < vn; v += MK_NT) {
-      const LS float* base = stage + (size_t)v * nch * 3;
-      float M = -INFINITY;
-      for (int c = 0; c < nch; ++c) M = fmaxf(M, base[3 * c]);
-      float num = 0.f, den = 0.f;
-      for (int c = 0; c < nch; ++c) {
-        const float e = expf(base[3 * c] - M);
-        den = fmaf(e, base[3 * c + 1], den);
-        num = fmaf(e, base[3 * c + 2], num);
+    }, [=](int f, float v) { stage[f] = v; });
+    if (wg_bar_or(s, !ok)) return false;
+    if (streamer()) {
+      // a wave per output: lanes over chunks, then wave reductions (fixed order)
+      for (int v = wave(); v < vn; v += NCW) {
+        const LS float* base = stage + (size_t)v * nch * 3;
+        float M = -INFINITY;
+        for (int c = lane(); c < nch; c += 64) M = fmaxf(M, base[3 * c]);
+        M = wave_max(M);
+        float num = 0.f, den = 0.f;
+        for (int c = lane(); c < nch; c += 64) {
+          const float e = expf(base[3 * c] - M);
+          den = fmaf(e, base[3 * c + 1], den);
+          num = fmaf(e, base[3 * c + 2], num);
+        }
+        num = wave_sum(num);
+        den = wave_sum(den);
+        if (lane() == 0) ll_put(L.ll_o + o0 + v0 + v, cx.epoch, num / den);
       }
-      ll_put(L.ll_o + o0 + v0 + v, cx.epoch, num / den);
     }
-    __syncthreads();
+    wg_bar();
   }
   return true;
 }
@@ -709,14 +923,18 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
   LS float* lds = (LS float*)lds_raw;
   const int NW = (int)gridDim.x, w = (int)blockIdx.x;
   Lds s;
+  s.desc = (LS MkLayerDev*)(lds + p.lds_desc);
+  s.gain = (LS uint16_t*)(lds + p.lds_gain);
+  s.rope = lds + p.lds_rope;
   s.x = lds + p.lds_x;
   s.xn = lds + p.lds_xn;
   s.vec = lds + p.lds_vec;
   s.att = lds + p.lds_att;
-  s.red = lds + p.lds_red;
   s.scr = lds + p.lds_scr;
-  s.stA = (LS u32x4*)(lds + p.lds_stage + min(wave(), MK_NCW - 1) * MK_STAGE_FLOATS_PER_WAVE);
-  s.stB = s.stA + PF_A * 64;
+  s.flag = (LS int*)(lds + p.lds_flag);
+  s.stA = (LS u32x4*)(lds + p.lds_stA);
+  s.stB = (LS u32x4*)(lds + p.lds_stB);
+  const int D = p.D;
 
   Ctx cx;
   cx.ctl = p.ctl;
@@ -729,13 +947,29 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     if (w == 0 && tid() == 0) set_err(cx, 2u);
     return;
   }
-  Tracer tr{(LS unsigned long long*)(lds + p.lds_trace), p.trace ? p.trace + (size_t)w * MK_TRACE_EVENTS : nullptr, 0};
+  Tracer tr{(LS unsigned long long*)(lds + p.lds_trace), p.trace ? p.trace + (size_t)w * MK_TRACE_EVENTS : nullptr,
+            0};
   tr.mark();
-  AttGeo ag;
-  ag.init(p.hd);
+
+  // launch-start loads (nothing else is in flight yet): descriptors, embedding row, RoPE row,
+  // layer 0's gains
+  {
+    const int nw = p.n_layers * (int)(sizeof(MkLayerDev) / 4);
+    const MK_G u32* dsrc = (const MK_G u32*)p.layers;
+    for (int i = tid(); i < nw; i += MK_NT) ((LS u32*)s.desc)[i] = dsrc[i];
+    for (int i = tid(); i < D; i += MK_NT) s.x[i] = bf16f(p.embed[(size_t)tok * D + i]);
+    const int half = p.hd / 2;
+    for (int i = tid(); i < half; i += MK_NT) {
+      s.rope[i] = p.rope_cos[(size_t)pos * half + i];
+      s.rope[half + i] = p.rope_sin[(size_t)pos * half + i];
+    }
+    for (int i = tid(); i < 2 * D; i += MK_NT) s.gain[i] = p.gain0[i];
+    if (tid() == 0) *s.flag = 0;
+  }
+  wg_bar();
 
   // this workgroup's rows of the residual-sized projections (out-projection, down projection)
-  const int d0 = split(p.D, NW, w), d1 = split(p.D, NW, w + 1);
+  const int d0 = split(D, NW, w), d1 = split(D, NW, w + 1);
   // FFN hidden range (gate/up row pairs)
   const int j0 = split(p.ffn, NW, w), j1 = split(p.ffn, NW, w + 1);
 
@@ -743,102 +977,129 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
   Gemv gin;
   int P0, P1;
   {
-    const MkLayerDev L0 = p.layers[0];
+    const MkLayerDev L0 = layer_desc(s.desc, 0);
     pair_range(L0.rows_in, NW, w, P0, P1);
-    gin.init(L0.w_in + (size_t)2 * P0 * p.D, min(2 * P1, L0.rows_in) - 2 * P0, p.D);
-    gemv_stage<PF_A>(gin, s.stA);
-    keep_issued();
+    gin.init(L0.w_in + (size_t)2 * P0 * D, min(2 * P1, L0.rows_in) - 2 * P0, D);
+    gemv_stage(gin, s.stA, A_UNITS);
+    if (streamer()) wait_vm<0>();
   }
-  for (int i = tid(); i < p.D; i += MK_NT) s.x[i] = __uint_as_float((u32)p.embed[(size_t)tok * p.D + i] << 16);
-  __syncthreads();
+  wg_bar();
 
   for (int l = 0; l < p.n_layers; ++l) {
-    const MkLayerDev L = p.layers[l];
-    rmsnorm_lds(s.x, L.g1, s.xn, p.D, p.rms_eps, s.scr);
+    const MkLayerDev L = layer_desc(s.desc, l);
+    const LS uint16_t* gl = s.gain + (size_t)(l & 1) * 2 * D;
+    // stage A holds this layer's input rows (waited for before the barrier that ended the last gather)
+    rmsnorm(s.x, gl, s.xn, D, p.rms_eps, tr);
     tr.mark();
     int K;  // mixer output width
     Gemv gout, ggu;
-    ggu.init(L.w_gu + (size_t)2 * j0 * p.D, 2 * (j1 - j0), p.D);
+    ggu.init(L.w_gu + (size_t)2 * j0 * D, 2 * (j1 - j0), D);
+    int cntA;
     if (L.kind == MK_LAYER_DN) {
       K = p.H * p.dv;
-      // in-projection rows -> records
       MK_G mk_u64* dst = L.ll_in + 2 * P0;
-      gemv<PF_A, false>(gin, s.xn, s.stA, s.red, tr, [&](int r, float v, float) { ll_put(dst + r, cx.epoch, v); });
+      gemv<false, false, false>(gin, s.xn, s.stA, A_UNITS, s.att, tr,
+                                [&](int r, float v, float) { ll_put(dst + r, cx.epoch, v); });
       tr.mark();
-      // state rows and the first out-projection rows go out before q/k/v/a/b are complete
+      // state rows and the out-projection units -> stage B; gate/up units -> stage A
       const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
+      const int rps = 64 / (p.dk >> 2);
+      const int sslots = min((s1 - s0 + rps - 1) / rps, MK_STAGE_B_SLOTS / 2);
+      const int boff = (sslots + 3) & ~3;
       gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
-      state_stage(p, L, s0, s1, s.stA);
-      gemv_stage<PF_B>(gout, s.stB);
-      keep_issued();
-      if (!dn_state(p, L, cx, s, s0, s1, tr)) return;
+      state_stage(p, L, s0, s1, s.stB, sslots);
+      gemv_stage(gout, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS);
+      if (!dn_state(p, L, cx, s, s0, s1, sslots, 0, tr)) return;
+      // gate/up units -> stage A once the critical state update is out
+      cntA = gemv_stage(ggu, s.stA, A_UNITS);
+      tr.mark();
+      // mixer output -> out-projection rows + residual -> records
+      {
+        const bool ok = gather_vec(cx, L.ll_o, K, s.vec);
+        if (wg_bar_or(s, !ok)) return;
+      }
+      tr.mark();
+      gemv<false, false, false>(gout, s.vec, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS, s.att, tr,
+                                [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     } else {
       K = p.nq * p.hd;
       att_qkv(p, L, cx, s, gin, P0, pos, tr);
       tr.mark();
-      // K/V rows of the first work item and the first out-projection rows go out before q/k/v
-      const int items = ((pos + MK_ATT_CHUNK) / MK_ATT_CHUNK) * p.nkv;
-      if (w < items) kv_stage(p, L, ag, w, pos, s.stA);
+      // K/V rows of the first work item and the out-projection units -> stage B; gate/up -> stage A
+      const int boff = (2 * kv_slots(p.hd) + 3) & ~3;
+      const int items = ((pos + ATT_C) / ATT_C) * p.nkv;
+      if (w < items) kv_stage(p, L, w, pos, s.stB);
       gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
-      gemv_stage<PF_B>(gout, s.stB);
-      keep_issued();
-      if (!att_partial(p, L, cx, s, NW, w, pos, ag)) return;
+      gemv_stage(gout, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS);
+      if (!att_items(p, L, cx, s, NW, w, pos, 0, tr)) return;
+      cntA = gemv_stage(ggu, s.stA, A_UNITS);
       tr.mark();
       const int o0 = split(K, NW, w), o1 = split(K, NW, w + 1);
-      gemv_stage<PF_A>(ggu, s.stA);
-      keep_issued();
       if (!att_combine(p, L, cx, s, o0, o1, pos)) return;
+      tr.mark();
+      {
+        const bool ok = gather_vec(cx, L.ll_o, K, s.vec);
+        if (wg_bar_or(s, !ok)) return;
+      }
+      tr.mark();
+      gemv<false, false, false>(gout, s.vec, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS, s.att, tr,
+                                [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     }
     tr.mark();
-    if (L.kind == MK_LAYER_DN) {
-      gemv_stage<PF_A>(ggu, s.stA);  // gate/up rows go out before the mixer output is complete
-      keep_issued();
-    }
-    // mixer output -> out-projection rows + residual -> records
-    if (__syncthreads_or(!ll_gather_vec(cx, L.ll_o, K, s.vec))) return;
-    tr.mark();
-    gemv<PF_B, false>(gout, s.vec, s.stB, s.red, tr,
-                      [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
-    // down-projection rows go out before the residual is complete
+    // down-projection units and the next layer's (or the final) gains -> stage B
     Gemv gdn;
     gdn.init(L.w_down + (size_t)d0 * p.ffn, d1 - d0, p.ffn);
-    gemv_stage<PF_B>(gdn, s.stB);
-    keep_issued();
+    int cntB = gemv_stage(gdn, s.stB, MK_STAGE_B_SLOTS / USLOTS);
+    LS uint16_t* gnext = s.gain + (size_t)((l + 1) & 1) * 2 * D;
+    if (l + 1 < p.n_layers) {
+      cntB += gain_stage(layer_desc(s.desc, l + 1).g12, 2 * D, gnext);
+    } else {
+      cntB += gain_stage(p.g_final, D, gnext);
+    }
+    {
+      const bool ok = gather_vec(cx, L.ll_x1, D, s.x);
+      if (streamer()) wait_vm_n(cntB);  // gate/up units (stage A)
+      if (wg_bar_or(s, !ok)) return;
+    }
     tr.mark();
-    if (__syncthreads_or(!ll_gather_vec(cx, L.ll_x1, p.D, s.x))) return;
-    tr.mark();
-    rmsnorm_lds(s.x, L.g2, s.xn, p.D, p.rms_eps, s.scr);
-    tr.mark();
-    gemv<PF_A, true>(ggu, s.xn, s.stA, s.red, tr, [&](int j, float gv, float uv) {
+    rmsnorm(s.x, gl + D, s.xn, D, p.rms_eps, tr);
+    gemv<true, false, false>(ggu, s.xn, s.stA, A_UNITS, s.att, tr, [&](int j, float gv, float uv) {
       ll_put(L.ll_h + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
     });
-    // next layer's input rows (or the LM head's) go out before the FFN hidden is complete
+    tr.mark();
+    // next layer's input rows (or the LM head's) -> stage A
     if (l + 1 < p.n_layers) {
-      const MkLayerDev Ln = p.layers[l + 1];
+      const MkLayerDev Ln = layer_desc(s.desc, l + 1);
       pair_range(Ln.rows_in, NW, w, P0, P1);
-      gin.init(Ln.w_in + (size_t)2 * P0 * p.D, min(2 * P1, Ln.rows_in) - 2 * P0, p.D);
+      gin.init(Ln.w_in + (size_t)2 * P0 * D, min(2 * P1, Ln.rows_in) - 2 * P0, D);
     } else {
       pair_range(p.vocab, NW, w, P0, P1);
-      gin.init(p.embed + (size_t)2 * P0 * p.D, min(2 * P1, p.vocab) - 2 * P0, p.D);
+      gin.init(p.embed + (size_t)2 * P0 * D, min(2 * P1, p.vocab) - 2 * P0, D);
     }
-    gemv_stage<PF_A>(gin, s.stA);
-    keep_issued();
+    cntA = gemv_stage(gin, s.stA, A_UNITS);
+    {
+      const bool ok = gather_vec(cx, L.ll_h, p.ffn, s.vec);
+      if (streamer()) wait_vm_n(cntA);  // down units and gains (stage B)
+      if (wg_bar_or(s, !ok)) return;
+    }
     tr.mark();
-    if (__syncthreads_or(!ll_gather_vec(cx, L.ll_h, p.ffn, s.vec))) return;
+    gemv<false, false, false>(gdn, s.vec, s.stB, MK_STAGE_B_SLOTS / USLOTS, s.att, tr,
+                              [&](int r, float v, float) { ll_put(L.ll_x2 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     tr.mark();
-    gemv<PF_B, false>(gdn, s.vec, s.stB, s.red, tr,
-                      [&](int r, float v, float) { ll_put(L.ll_x2 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
-    tr.mark();
-    if (__syncthreads_or(!ll_gather_vec(cx, L.ll_x2, p.D, s.x))) return;
+    {
+      const bool ok = gather_vec(cx, L.ll_x2, D, s.x);
+      if (streamer()) wait_vm<0>();  // next input rows (stage A)
+      if (wg_bar_or(s, !ok)) return;
+    }
     tr.mark();
   }
 
   // final norm + tied LM head + argmax (lowest index among equal maxima)
-  rmsnorm_lds(s.x, p.g_final, s.xn, p.D, p.rms_eps, s.scr);
+  rmsnorm(s.x, s.gain + (size_t)(p.n_layers & 1) * 2 * D, s.xn, D, p.rms_eps, tr);
   float best = -INFINITY;
   int bidx = 0x7fffffff;
   const int v0 = 2 * P0;
-  gemv<PF_A, false>(gin, s.xn, s.stA, s.red, tr, [&](int r, float v, float) {
+  gemv<false, true, true>(gin, s.xn, s.stA, A_UNITS, s.att, tr, [&](int r, float v, float) {
     const int idx = v0 + r;
     if (p.logits) p.logits[idx] = v;
     if (v > best || (v == best && idx < bidx)) {
@@ -847,7 +1108,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     }
   });
   tr.mark();
-  // workgroup argmax: fixed tree over lanes (DPP-free shuffles) then waves in order
+  // workgroup argmax: fixed tree over lanes then waves in order
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     const float ob = __shfl_xor(best, m, 64);
@@ -861,7 +1122,7 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     s.scr[wave()] = best;
     s.scr[MK_NWAVE + wave()] = __int_as_float(bidx);
   }
-  __syncthreads();
+  wg_bar();
   if (tid() == 0) {
     for (int i = 0; i < MK_NWAVE; ++i) {
       const float ob = s.scr[i];
@@ -880,10 +1141,10 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
     return;
   }
   // workgroup 0 reduces the per-workgroup winners and publishes the token
-  __syncthreads();
-  const MK_G mk_u64* am = p.ll_am;
-  const bool ok = ll_gather(cx, 2 * NW, [=](int f) { return am + f; }, s.vec);
-  if (__syncthreads_or(!ok)) return;
+  {
+    const bool ok = gather_vec(cx, p.ll_am, 2 * NW, s.vec);
+    if (wg_bar_or(s, !ok)) return;
+  }
   if (tid() == 0) {
     float b = -INFINITY;
     int bi = 0x7fffffff;
@@ -916,11 +1177,6 @@ __global__ void mk_permute_rows_kernel(const uint16_t* __restrict__ src, uint16_
   for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) d[c] = s[c];
 }
 
-__global__ void mk_bf16_to_f32_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = __uint_as_float((u32)src[i] << 16);
-}
-
 __global__ void mk_zero_kernel(uint32_t* __restrict__ dst, int64_t words) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = 0u;
@@ -945,13 +1201,6 @@ extern "C" int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const 
   if (rows <= 0) return 0;
   hipLaunchKernelGGL(mk_permute_rows_kernel, dim3((unsigned)rows), dim3(256), 0, (hipStream_t)stream, src, dst, d_perm,
                      rows, cols);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-extern "C" int mk_launch_bf16_to_f32(const uint16_t* src, float* dst, int64_t n, void* stream) {
-  if (n <= 0) return 0;
-  hipLaunchKernelGGL(mk_bf16_to_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, src,
-                     dst, n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

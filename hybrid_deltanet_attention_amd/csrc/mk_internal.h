@@ -14,20 +14,26 @@ typedef unsigned long long mk_u64;
 #define MK_G
 #endif
 
-// Threads per workgroup of the persistent decode grid (8 wave64s): waves 0..6 compute and
-// prefetch, wave 7 only polls exchange records (so its waits never include prefetch traffic).
+// Threads per workgroup of the persistent decode grid (8 wave64s).  Waves 0..MK_NCW-1 stream: they
+// issue every weight / state / KV copy and every store.  The other waves only poll exchange
+// records (their vector-memory counter never holds a prefetch, so a completed poll is never held
+// back behind one).  All 8 waves compute from LDS.
 #define MK_NT 512
 #define MK_NWAVE 8
-#define MK_NCW 7
+#define MK_NCW 4
 #define MK_NCT (MK_NCW * 64)
-// Positions per split-K attention work item.
+// Positions per split-K attention work item (one 16-lane DPP row per query head).
 #define MK_ATT_CHUNK 16
-// Timestamps per workgroup in the optional phase trace.
-#define MK_TRACE_EVENTS 512
+// 8-byte trace words per workgroup (pairs of wall clock, core clock).
+#define MK_TRACE_EVENTS 1024
 // Polls of an exchange word before a wait gives up and reports MK_E_DEVICE_TIMEOUT.
 #define MK_SPIN_LIMIT (1u << 22)
-// LDS prefetch stage per compute wave (floats): 8 x 1 KB large-stage slots + 4 x 1 KB small-stage slots.
-#define MK_STAGE_FLOATS_PER_WAVE 3072
+// LDS prefetch stages, in 1 KB slots: A holds the in-projection / gate-up / LM-head units, B the
+// state rows or KV rows plus the out-projection units, or the down-projection units.
+#define MK_STAGE_A_SLOTS 56
+#define MK_STAGE_B_SLOTS 32
+// GEMV unit partials held in LDS per row chunk.
+#define MK_RED_CAP 4096
 // Largest grid the exchange buffers are sized for.
 #define MK_MAX_GRID 1024
 
@@ -50,8 +56,7 @@ struct MkLayerDev {
   MK_G const uint16_t* w_out;    // [D][H*dv] or [D][nq*hd]
   MK_G const uint16_t* w_gu;     // [2*ffn][D], gate and up rows interleaved (g0, u0, g1, u1, ...)
   MK_G const uint16_t* w_down;   // [D][ffn]
-  MK_G const float* g1;          // [D]
-  MK_G const float* g2;          // [D]
+  MK_G const uint16_t* g12;      // BF16 RMSNorm gains [2][D]: pre-mixer, then pre-FFN
   MK_G float* S;                 // DeltaNet: [H][dv][dk]
   MK_G float* Kc;                // attention: [nkv][max_ctx][hd]
   MK_G float* Vc;                // attention: [nkv][max_ctx][hd]
@@ -70,7 +75,8 @@ struct MkDecodeParams {
   int32_t max_ctx, max_items;
   float rms_eps, l2_eps;
   MK_G const uint16_t* embed;    // [vocab][D]
-  MK_G const float* g_final;     // [D]
+  MK_G const uint16_t* g_final;  // BF16 final RMSNorm gain [D]
+  MK_G const uint16_t* gain0;    // layer 0's gains (its g12)
   MK_G const float* rope_cos;    // [max_ctx][hd/2]
   MK_G const float* rope_sin;    // [max_ctx][hd/2]
   MK_G MkCtl* ctl;
@@ -82,7 +88,8 @@ struct MkDecodeParams {
   // [.. + 2e + 1] = core clock
   MK_G unsigned long long* trace;
   // LDS carve (float offsets) and size
-  int32_t lds_x, lds_xn, lds_vec, lds_att, lds_red, lds_scr, lds_trace, lds_stage, lds_floats;
+  int32_t lds_desc, lds_gain, lds_rope, lds_x, lds_xn, lds_vec, lds_att, lds_scr, lds_flag, lds_trace;
+  int32_t lds_stA, lds_stB, lds_floats;
 };
 
 #ifdef __cplusplus
@@ -92,7 +99,6 @@ extern "C" {
 int mk_launch_decode(const MkDecodeParams* p, int n_wg, void* stream);
 int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_perm, int64_t rows,
                            int64_t cols, void* stream);
-int mk_launch_bf16_to_f32(const uint16_t* src, float* dst, int64_t n, void* stream);
 int mk_launch_zero(void* dst, int64_t bytes, void* stream);
 int mk_launch_set_ctl(MkCtl* ctl, int32_t pos, int reset_err, int bump_step, void* stream);
 int mk_decode_max_blocks_per_cu(int lds_bytes);
