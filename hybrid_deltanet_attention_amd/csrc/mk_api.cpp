@@ -94,7 +94,12 @@ struct Layout {
   size_t xchg_begin, xchg_end;    // exchange records
   std::vector<LayerOff> layers;
   int max_items;
+  // prefill scratch: a chunk of up to pf_T tokens
+  int pf_T, pf_lda, pf_ldy;
+  size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part;
 };
+
+constexpr int PF_LM_WG = 512;  // workgroups of the prefill LM head
 
 Layout make_layout(const mk_config& c) {
   Layout L{};
@@ -149,6 +154,26 @@ Layout make_layout(const mk_config& c) {
   L.ll_am = take((size_t)2 * MK_MAX_GRID * 8);
   L.xchg_end = o;
   L.scratch = take(4096);
+  // prefill scratch
+  {
+    const int64_t T = std::min(c.max_ctx, 1024);
+    const int64_t kmax = std::max(std::max(D, (int64_t)c.ffn), std::max(H * c.dn_dv, (int64_t)c.n_q_heads * c.head_dim));
+    const int64_t ndn = 2 * H * c.dn_dk + H * c.dn_dv + 2 * H;
+    const int64_t natt = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+    L.pf_T = (int)T;
+    L.pf_lda = (int)((kmax + 7) / 8 * 8);
+    L.pf_ldy = (int)std::max(ndn, natt);
+    L.pf_x = take((size_t)T * D * 4);
+    L.pf_ahi = take((size_t)T * L.pf_lda * 2);
+    L.pf_alo = take((size_t)T * L.pf_lda * 2);
+    L.pf_hhi = take((size_t)T * c.ffn * 2);
+    L.pf_hlo = take((size_t)T * c.ffn * 2);
+    L.pf_y = take((size_t)T * L.pf_ldy * 4);
+    L.pf_qk = take((size_t)T * H * 2 * c.dn_dk * 4);
+    L.pf_ab = take((size_t)T * H * 2 * 4);
+    L.pf_q = take((size_t)T * c.n_q_heads * c.head_dim * 4);
+    L.pf_part = take((size_t)PF_LM_WG * 2 * 4);
+  }
   L.total = o;
   return L;
 }
@@ -354,7 +379,7 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   lds_layout(*cfg, ctx->grid, p);
 
   const int lds_bytes = p.lds_floats * 4;
-  if (lds_bytes > (int)prop.sharedMemPerBlock || mk_decode_max_blocks_per_cu(lds_bytes) < 1) {
+  if (lds_bytes > (int)prop.sharedMemPerBlock || mk_decode_max_blocks_per_cu(&p, lds_bytes) < 1) {
     const std::string m = "decode kernel needs " + std::to_string(lds_bytes) + " B of LDS; device offers " +
                           std::to_string(prop.sharedMemPerBlock);
     delete ctx;
@@ -436,7 +461,7 @@ int mk_set_grid(mk_ctx* ctx, int32_t n) {
     return fail(ctx, MK_E_INVALID, "grid must be in [1, " + std::to_string(std::min(ctx->n_cu, MK_MAX_GRID)) + "]");
   MkDecodeParams q = ctx->base;
   lds_layout(ctx->cfg, n, q);
-  if (mk_decode_max_blocks_per_cu(q.lds_floats * 4) < 1)
+  if (mk_decode_max_blocks_per_cu(&q, q.lds_floats * 4) < 1)
     return fail(ctx, MK_E_OCCUPANCY, "decode kernel does not fit at this grid size");
   ctx->base = q;
   ctx->grid = n;
@@ -602,12 +627,74 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
   if (!d_tokens || !d_next || n <= 0) return fail(ctx, MK_E_INVALID, "need d_tokens, d_next and n > 0");
   if (ctx->pos_host + n > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "prompt does not fit the context");
-  int32_t* scratch_tok = (int32_t*)(ctx->ws + ctx->lay.scratch) + 8;
-  for (int32_t i = 0; i < n; ++i) {
-    const bool last = (i == n - 1);
-    const int rc = mk_decode_step(ctx, d_tokens + i, last ? d_next : scratch_tok, last ? d_logits : nullptr);
-    if (rc) return rc;
+  const mk_config& c = ctx->cfg;
+  const int gs = c.n_q_heads / c.n_kv_heads;
+  if (16 % gs != 0) {
+    // shapes the prefill attention tiling does not cover: token-by-token through the decode kernel
+    int32_t* scratch_tok = (int32_t*)(ctx->ws + ctx->lay.scratch) + 8;
+    for (int32_t i = 0; i < n; ++i) {
+      const bool last = (i == n - 1);
+      const int rc = mk_decode_step(ctx, d_tokens + i, last ? d_next : scratch_tok, last ? d_logits : nullptr);
+      if (rc) return rc;
+    }
+    return MK_OK;
   }
+  const Layout& L = ctx->lay;
+  char* ws = ctx->ws;
+  void* st = ctx->stream;
+  const int D = c.hidden, H = c.dn_heads, dk = c.dn_dk, dv = c.dn_dv, hd = c.head_dim;
+  const int nq = c.n_q_heads, nkv = c.n_kv_heads, F = c.ffn;
+  float* X = (float*)(ws + L.pf_x);
+  uint16_t* Ahi = (uint16_t*)(ws + L.pf_ahi);
+  uint16_t* Alo = (uint16_t*)(ws + L.pf_alo);
+  uint16_t* Hhi = (uint16_t*)(ws + L.pf_hhi);
+  uint16_t* Hlo = (uint16_t*)(ws + L.pf_hlo);
+  float* Y = (float*)(ws + L.pf_y);
+  float* QK = (float*)(ws + L.pf_qk);
+  float* AB = (float*)(ws + L.pf_ab);
+  float* Q = (float*)(ws + L.pf_q);
+  const int lda = L.pf_lda, ldy = L.pf_ldy;
+  MkCtl* ctl = (MkCtl*)(ws + L.ctl);
+  const float* rcos = (const float*)(ws + L.rope_cos);
+  const float* rsin = (const float*)(ws + L.rope_sin);
+  const uint16_t* embed = (const uint16_t*)(ws + L.embed);
+  int rc = 0;
+  int p0 = ctx->pos_host;
+  int T = 0;
+  for (int c0 = 0; c0 < n && !rc; c0 += T) {
+    T = std::min(L.pf_T, n - c0);
+    rc |= mk_pf_embed(d_tokens + c0, T, embed, D, c.vocab, X, ctl, st);
+    for (int l = 0; l < c.n_layers && !rc; ++l) {
+      const LayerOff& lo = L.layers[l];
+      const uint16_t* g12 = (const uint16_t*)(ws + lo.g12);
+      const uint16_t* w_in = (const uint16_t*)(ws + lo.w_in);
+      const uint16_t* w_out = (const uint16_t*)(ws + lo.w_out);
+      rc |= mk_pf_rms_split(X, T, D, g12, c.rms_eps, Ahi, Alo, lda, st);
+      rc |= mk_pf_gemm(0, Ahi, Alo, lda, T, D, w_in, (int)lo.rows_in, Y, ldy, nullptr, nullptr, 0, st);
+      if (is_attention(c, l)) {
+        float* Kc = (float*)(ws + lo.Kc);
+        float* Vc = (float*)(ws + lo.Vc);
+        rc |= mk_pf_att_rope(Y, ldy, T, p0, nq, nkv, hd, c.max_ctx, rcos, rsin, Q, Kc, Vc, st);
+        rc |= mk_pf_attention(Q, Kc, Vc, T, p0, nq, nkv, hd, c.max_ctx, Ahi, Alo, lda, st);
+      } else {
+        rc |= mk_pf_dn_prep(Y, ldy, T, H, dk, dv, c.l2_eps, QK, AB, st);
+        rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, Ahi, Alo, lda, st);
+      }
+      rc |= mk_pf_gemm(1, Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, nullptr, nullptr, 0, st);
+      rc |= mk_pf_rms_split(X, T, D, g12 + D, c.rms_eps, Ahi, Alo, lda, st);
+      rc |= mk_pf_gemm(2, Ahi, Alo, lda, T, D, (const uint16_t*)(ws + lo.w_gu), 2 * F, nullptr, 0, Hhi, Hlo, F, st);
+      rc |= mk_pf_gemm(1, Hhi, Hlo, F, T, F, (const uint16_t*)(ws + lo.w_down), D, X, D, nullptr, nullptr, 0, st);
+    }
+    p0 += T;
+  }
+  if (!rc) {
+    float* part = (float*)(ws + L.pf_part);
+    rc |= mk_pf_lmhead(X + (size_t)(T - 1) * D, D, (const uint16_t*)(ws + L.g_final), c.rms_eps, embed, c.vocab,
+                       d_logits, part, PF_LM_WG, st);
+    rc |= mk_pf_finish(part, PF_LM_WG, d_next, ctl, p0, st);
+  }
+  if (rc) return fail(ctx, MK_E_HIP, "prefill launch failed");
+  ctx->pos_host = p0;
   return MK_OK;
 }
 

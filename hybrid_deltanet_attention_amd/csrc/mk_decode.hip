@@ -913,12 +913,22 @@ __device__ __forceinline__ void pair_range(int R, int NW, int w, int& p0, int& p
   p1 = split(np, NW, w + 1);
 }
 
-}  // namespace
-
 // ------------------------------------------------------------------------------------------
-// the megakernel
+// the megakernel.  The body is compiled once per model shape it is specialised for (every size a
+// compile-time constant, so divisions and trip counts fold) and once generically (sizes read from
+// the parameters); the host picks the instance that matches the model.
 // ------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
+template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_>
+__device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
+  MkDecodeParams p = p0;
+  if (D_) p.D = D_;
+  if (FFN_) p.ffn = FFN_;
+  if (H_) p.H = H_;
+  if (DK_) p.dk = DK_;
+  if (DV_) p.dv = DV_;
+  if (NQ_) p.nq = NQ_;
+  if (NKV_) p.nkv = NKV_;
+  if (HD_) p.hd = HD_;
   extern __shared__ float lds_raw[];
   LS float* lds = (LS float*)lds_raw;
   const int NW = (int)gridDim.x, w = (int)blockIdx.x;
@@ -1164,6 +1174,35 @@ __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
   tr.flush();
 }
 
+}  // namespace
+
+// generic shape
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
+  decode_body<0, 0, 0, 0, 0, 0, 0, 0>(p);
+}
+// hidden 1024, FFN 3584, 16 DeltaNet heads of 128, 8 Q / 2 KV heads of 128 (the 0.8B-shaped hybrid)
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h1024(MkDecodeParams p) {
+  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128>(p);
+}
+// hidden 256, FFN 768, 4 DeltaNet heads of 64, 4 Q / 2 KV heads of 64 (the tiny hybrid)
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h256(MkDecodeParams p) {
+  decode_body<256, 768, 4, 64, 64, 4, 2, 64>(p);
+}
+
+namespace {
+template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_>
+bool shape_is(const MkDecodeParams& p) {
+  return p.D == D_ && p.ffn == FFN_ && p.H == H_ && p.dk == DK_ && p.dv == DV_ && p.nq == NQ_ && p.nkv == NKV_ &&
+         p.hd == HD_;
+}
+typedef void (*DecodeKernel)(MkDecodeParams);
+DecodeKernel pick_kernel(const MkDecodeParams& p) {
+  if (shape_is<1024, 3584, 16, 128, 128, 8, 2, 128>(p)) return mk_decode_kernel_h1024;
+  if (shape_is<256, 768, 4, 64, 64, 4, 2, 64>(p)) return mk_decode_kernel_h256;
+  return mk_decode_kernel;
+}
+}  // namespace
+
 // ------------------------------------------------------------------------------------------
 // load-time helper kernels
 // ------------------------------------------------------------------------------------------
@@ -1192,7 +1231,7 @@ __global__ void mk_set_ctl_kernel(MkCtl* ctl, int32_t pos, int reset_err, int bu
 }
 
 extern "C" int mk_launch_decode(const MkDecodeParams* p, int n_wg, void* stream) {
-  hipLaunchKernelGGL(mk_decode_kernel, dim3(n_wg), dim3(MK_NT), (size_t)p->lds_floats * 4, (hipStream_t)stream, *p);
+  hipLaunchKernelGGL(pick_kernel(*p), dim3(n_wg), dim3(MK_NT), (size_t)p->lds_floats * 4, (hipStream_t)stream, *p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -1215,8 +1254,8 @@ extern "C" int mk_launch_set_ctl(MkCtl* ctl, int32_t pos, int reset_err, int bum
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-extern "C" int mk_decode_max_blocks_per_cu(int lds_bytes) {
+extern "C" int mk_decode_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes) {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mk_decode_kernel, MK_NT, lds_bytes) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pick_kernel(*p), MK_NT, lds_bytes) != hipSuccess) return 0;
   return nb;
 }

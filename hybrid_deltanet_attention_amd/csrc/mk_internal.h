@@ -101,7 +101,23 @@ int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_
                            int64_t cols, void* stream);
 int mk_launch_zero(void* dst, int64_t bytes, void* stream);
 int mk_launch_set_ctl(MkCtl* ctl, int32_t pos, int reset_err, int bump_step, void* stream);
-int mk_decode_max_blocks_per_cu(int lds_bytes);
+int mk_decode_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
+// prefill kernels (mk_prefill.hip); all return 0 or -1 (launch error)
+int mk_pf_embed(const int32_t* tok, int T, const uint16_t* embed, int D, int vocab, float* X, MkCtl* ctl, void* stream);
+int mk_pf_rms_split(const float* X, int T, int D, const uint16_t* g, float eps, uint16_t* Ahi, uint16_t* Alo, int lda,
+                    void* stream);
+int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W, int N,
+               float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, void* stream);
+int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB, void* stream);
+int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk, int dv,
+                  uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream);
+int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, int max_ctx, const float* rcos,
+                   const float* rsin, float* Q, float* Kc, float* Vc, void* stream);
+int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,
+                    int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream);
+int mk_pf_lmhead(const float* x, int D, const uint16_t* g, float eps, const uint16_t* E, int vocab, float* logits,
+                 float* part, int nwg, void* stream);
+int mk_pf_finish(const float* part, int nwg, int32_t* next, MkCtl* ctl, int32_t pos, void* stream);
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,789 @@
+// Prefill of a prompt chunk (positions p0 .. p0 + T - 1) on gfx950, as a short sequence of kernels
+// per layer (luce-megakernel announcement, page 1: the same model as the decode path; its results
+// table quotes pp520 prefill).  Where decode is a matrix-vector product per weight byte, prefill
+// multiplies a T-row activation block by every weight matrix, so the projections and the FFN run on
+// the MFMA matrix cores:
+//
+//   * activations are FP32; before a GEMM they are split into a BF16 high part and a BF16 low part
+//     (x = hi + lo to about 2^-16 relative), and the GEMM accumulates hi.W + lo.W in FP32 against
+//     the exact BF16 weights, so prefill keeps FP32-grade accuracy;
+//   * v_mfma_f32_32x32x16_bf16: a 256-thread workgroup computes a 128 x 128 output tile, each wave a
+//     64 x 64 block of 2 x 2 MFMA tiles, operands loaded straight from global memory (the tiles that
+//     share weight rows are placed on the same XCD so they share its L2);
+//   * the DeltaNet recurrence runs row-parallel (every row of every head's state evolves on its own:
+//     16 lanes per row, the state in registers), sequential over the chunk's tokens;
+//   * causal attention is an online-softmax loop over the KV cache (previous context included).
+//
+// The DeltaNet state and the KV cache are left exactly as token-by-token decode would leave them.
+
+#include <hip/hip_runtime.h>
+#include "mk_internal.h"
+
+typedef unsigned int u32;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((u32)h << 16); }
+// round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  u32 u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ void split_store(float v, uint16_t* hi, uint16_t* lo, size_t i) {
+  const uint16_t h = f2bf(v);
+  hi[i] = h;
+  lo[i] = f2bf(v - bf16f(h));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over each 16-lane row; every lane of the row gets it
+__device__ __forceinline__ float row_sum16(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  v = dpp_add<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float softplusf_(float z) { return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z))); }
+
+// ------------------------------------------------------------------------ embedding, norms
+__global__ void pf_embed_kernel(const int32_t* __restrict__ tok, int T, const uint16_t* __restrict__ embed, int D,
+                                int vocab, float* __restrict__ X, MkCtl* ctl) {
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const int id = tok[t];
+  if (id < 0 || id >= vocab) {
+    if (threadIdx.x == 0) __hip_atomic_store(&ctl->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < D; i += blockDim.x) X[(size_t)t * D + i] = 0.f;
+    return;
+  }
+  for (int i = threadIdx.x; i < D; i += blockDim.x) X[(size_t)t * D + i] = bf16f(embed[(size_t)id * D + i]);
+}
+
+// rows of X -> rmsnorm(x) * g, split into BF16 hi/lo (one 256-thread workgroup per row)
+__global__ void __launch_bounds__(256) pf_rms_split_kernel(const float* __restrict__ X, int D,
+                                                           const uint16_t* __restrict__ g, float eps,
+                                                           uint16_t* __restrict__ Ahi, uint16_t* __restrict__ Alo,
+                                                           int lda) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const float* x = X + (size_t)t * D;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) s = fmaf(x[i], x[i], s);
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  s = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(s / (float)D + eps);
+  for (int i = threadIdx.x; i < D; i += 256) split_store(x[i] * r * bf16f(g[i]), Ahi, Alo, (size_t)t * lda + i);
+}
+
+// ------------------------------------------------------------------------ MFMA GEMM
+// C[M x N] (+)= (Ahi + Alo)[M x K] . W[N x K]^T.  K is a multiple of 8.
+// EPI 0: C = v;  EPI 1: C += v (residual);  EPI 2: columns (2c, 2c + 1) are (gate c, up c):
+// H[:, c] = silu(gate) * up, stored split into BF16 hi/lo.
+//
+// A workgroup (4 waves, 2 x 2) computes a BM x BN tile; each wave a (BM/2) x (BN/2) block of 32 x 32
+// MFMA tiles.  K advances in chunks of 32 through a ring of STAGES LDS buffers filled with LDS-DMA
+// (a wave copy is 16 rows x 64 bytes); a wave waits only for its own copies of the chunk it is about
+// to use, and the barriers order LDS only, so later chunks stay in flight.
+constexpr int BK = 32;
+constexpr int STAGES = 4;
+
+__device__ __forceinline__ void lds_bar() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// at most n outstanding, rounded down to a supported count (waiting for more is always correct)
+__device__ __forceinline__ void wait_vm_n(int n) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  if (n >= 32) wait_vm<32>();
+  else if (n >= 16) wait_vm<16>();
+  else if (n >= 12) wait_vm<12>();
+  else if (n >= 8) wait_vm<8>();
+  else if (n >= 6) wait_vm<6>();
+  else if (n >= 4) wait_vm<4>();
+  else if (n >= 3) wait_vm<3>();
+  else if (n >= 2) wait_vm<2>();
+  else if (n >= 1) wait_vm<1>();
+  else wait_vm<0>();
+}
+
+template <int BM, int BN, int EPI>
+__global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict__ Ahi, const uint16_t* __restrict__ Alo,
+                                                      int lda, int M, int K, const uint16_t* __restrict__ W, int N,
+                                                      float* __restrict__ C, int ldc, uint16_t* __restrict__ Hhi,
+                                                      uint16_t* __restrict__ Hlo, int ldh) {
+  constexpr int TI = BM / 64, TJ = BN / 64;            // 32 x 32 tiles per wave in each direction
+  constexpr int AC = BM / 16, BC = BN / 16;            // 1 KB copies per tile per chunk
+  constexpr int CPW = (2 * AC + BC) / 4;               // copies per wave per chunk
+  constexpr int SB = (2 * BM + BN) * BK * 2;           // bytes per stage
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int mb = (M + BM - 1) / BM, nb = (N + BN - 1) / BN;
+  const int tiles = mb * nb, per = (tiles + 7) / 8;
+  const int w = blockIdx.x;
+  // tiles of one column block (same weight rows) go to one XCD (workgroup w runs on XCD w % 8)
+  const int tile = (w % 8) * per + w / 8;
+  if (tile >= tiles) return;
+  const int m0 = (tile % mb) * BM, n0 = (tile / mb) * BN;
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int wr = wv >> 1, wc = wv & 1;
+  const int nchunk = (K + BK - 1) / BK;
+  // Copy q (0 .. 2AC + BC) of a chunk: tile part (A hi, A lo, B) and 16-row group; wave wv issues
+  // copies wv * CPW .. + CPW.  Rows past M / N read the last row instead (their results are never
+  // stored), so every copy has live lanes and each wave issues exactly CPW copies per chunk -- the
+  // waits below count on that.  Columns past K are left out; a chunk that has them was zeroed by the
+  // same wave first (its own 1 KB blocks only, so no other wave's copy can be overwritten).
+  auto issue = [&](int chunk) {
+    char* st = smem + (size_t)(chunk % STAGES) * SB;
+    const int k0 = chunk * BK;
+    const bool part_k = k0 + BK > K;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int q = wv * CPW + i;
+      const int part = q < AC ? 0 : (q < 2 * AC ? 1 : 2);
+      const int grp = part == 0 ? q : (part == 1 ? q - AC : q - 2 * AC);
+      const int r = grp * 16 + (l >> 2);
+      const int k = k0 + (l & 3) * 8;
+      const uint16_t* src;
+      if (part < 2) src = (part == 0 ? Ahi : Alo) + (size_t)min(m0 + r, M - 1) * lda + k;
+      else src = W + (size_t)min(n0 + r, N - 1) * K + k;
+      char* dst = st + (part == 0 ? 0 : (part == 1 ? BM * BK * 2 : 2 * BM * BK * 2)) + grp * 1024;
+      if (part_k) {
+        ((u32x4*)dst)[l] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+      }
+      if (k < K) __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  };
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < STAGES - 1; ++c)
+    if (c < nchunk) issue(c);
+  for (int c = 0; c < nchunk; ++c) {
+    // this wave's copies of chunk c are done once at most (later chunks issued) copies remain
+    const int later = min(STAGES - 2, nchunk - 1 - c);
+    if (later >= 2) wait_vm<2 * CPW>();
+    else if (later == 1) wait_vm<CPW>();
+    else wait_vm<0>();
+    lds_bar();
+    // chunk c + STAGES - 1 reuses the buffer of chunk c - 1, which every wave has finished
+    const int cn = c + STAGES - 1;
+    if (cn < nchunk) issue(cn);
+    const char* st = smem + (size_t)(c % STAGES) * SB;
+    const char* sah = st;
+    const char* sal = st + BM * BK * 2;
+    const char* sb = st + 2 * BM * BK * 2;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kb = (ks * 16 + 8 * (l >> 5)) * 2;  // byte offset of this lane's 8 k values in a row
+      bf16x8 fh[TI], fl[TI], fb[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int r = wr * (BM / 2) + i * 32 + (l & 31);
+        fh[i] = *(const bf16x8*)(sah + r * (BK * 2) + kb);
+        fl[i] = *(const bf16x8*)(sal + r * (BK * 2) + kb);
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int r = wc * (BN / 2) + j * 32 + (l & 31);
+        fb[j] = *(const bf16x8*)(sb + r * (BK * 2) + kb);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+  // result: accumulator r of lane l sits at row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wr * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int col = n0 + wc * (BN / 2) + j * 32 + (l & 31);
+        const float v = acc[i][j][r];
+        if (EPI == 2) {
+          // the odd neighbour lane holds the up value of the same hidden unit
+          const float u = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+          if ((l & 1) == 0 && row < M && col + 1 < N) {
+            const float h = v / (1.0f + expf(-v)) * u;
+            split_store(h, Hhi, Hlo, (size_t)row * ldh + (col >> 1));
+          }
+        } else if (row < M && col < N) {
+          float* cp = C + (size_t)row * ldc + col;
+          if (EPI == 1) *cp += v;
+          else *cp = v;
+        }
+      }
+}
+
+// ------------------------------------------------------------------------ DeltaNet
+// per (token, head): q, k L2-normalised -> QK[t][h][0..dk) = q, [dk..2dk) = k; AB[t][h] = (alpha, beta)
+__global__ void __launch_bounds__(64) pf_dn_prep_kernel(const float* __restrict__ Y, int ldy, int H, int dk, int dv,
+                                                        float l2eps, float* __restrict__ QK, float* __restrict__ AB) {
+  const int t = blockIdx.x / H, h = blockIdx.x % H;
+  const float* y = Y + (size_t)t * ldy;
+  const float* q = y + h * dk;
+  const float* k = y + H * dk + h * dk;
+  float qq = 0.f, kk = 0.f;
+  for (int e = threadIdx.x; e < dk; e += 64) {
+    qq = fmaf(q[e], q[e], qq);
+    kk = fmaf(k[e], k[e], kk);
+  }
+  qq = wave_sum(qq);
+  kk = wave_sum(kk);
+  const float sq = 1.0f / sqrtf(qq + l2eps), sk = 1.0f / sqrtf(kk + l2eps);
+  float* o = QK + ((size_t)t * H + h) * 2 * dk;
+  for (int e = threadIdx.x; e < dk; e += 64) {
+    o[e] = q[e] * sq;
+    o[dk + e] = k[e] * sk;
+  }
+  if (threadIdx.x == 0) {
+    const int off_a = 2 * H * dk + H * dv;
+    AB[((size_t)t * H + h) * 2] = expf(-softplusf_(y[off_a + h]));
+    AB[((size_t)t * H + h) * 2 + 1] = sigmoidf_(y[off_a + H + h]);
+  }
+}
+
+// Gated delta rule over T tokens, row-parallel.  A workgroup (4 waves, one per SIMD) owns 8 rows of
+// one head's state: 2 rows per wave, 32 lanes per row, NE = dk / 32 consecutive key elements per
+// lane, the row in registers; a row sum is a 16-lane DPP reduction plus one permlane16 swap.  Tokens
+// go through LDS in chunks of TC: while a chunk is processed the next chunk's q, k, gates and v are
+// already loading into registers.  o = S q is read after each update.
+constexpr int TC = 32;
+__device__ __forceinline__ float sum32(float v) {
+  v = row_sum16(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int NE>
+__global__ void __launch_bounds__(256) pf_dn_scan_kernel(float* __restrict__ S, const float* __restrict__ QK,
+                                                         const float* __restrict__ AB, const float* __restrict__ Y,
+                                                         int ldy, int T, int H, int dk, int dv,
+                                                         uint16_t* __restrict__ Ohi, uint16_t* __restrict__ Olo,
+                                                         int ldo) {
+  constexpr int DKM = 32 * NE;  // key width held per row
+  constexpr int RW = 8;         // rows per workgroup
+  __shared__ __attribute__((aligned(16))) float sqk[2][TC][2 * DKM];
+  __shared__ float sab[2][TC][2];
+  __shared__ float sv[2][TC][RW];
+  const int rbs = (dv + RW - 1) / RW;
+  const int h = blockIdx.x / rbs, r0 = (blockIdx.x % rbs) * RW;
+  const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+  const int rl = wv * 2 + (l >> 5), c = l & 31;  // local row, lane within the row
+  const int i = r0 + rl;
+  const bool valid = i < dv;
+  float* srow = S + ((size_t)h * dv + (valid ? i : 0)) * dk;
+  float s[NE];
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    const int e = NE * c + j;
+    s[j] = (valid && e < dk) ? srow[e] : 0.f;
+  }
+  const int off_v = 2 * H * dk + h * dv + r0;
+  constexpr int QK_PER = (TC * 2 * DKM + 255) / 256;
+  float rq[QK_PER], rab = 0.f, rvv = 0.f;
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int x = 0; x < QK_PER; ++x) {
+      const int f = tid + 256 * x;
+      const int tt = f / (2 * DKM), e = f % (2 * DKM);
+      const int t = t0 + tt;
+      const bool isk = e >= DKM;
+      const int ee = isk ? e - DKM : e;
+      rq[x] = (tt < TC && t < T && ee < dk) ? QK[((size_t)t * H + h) * 2 * dk + (isk ? dk : 0) + ee] : 0.f;
+    }
+    {
+      const int t = t0 + (tid >> 1);
+      rab = (tid < 2 * TC && t < T) ? AB[((size_t)t * H + h) * 2 + (tid & 1)] : 0.f;
+    }
+    {
+      const int tt = tid / RW, rr = tid % RW, t = t0 + tt;
+      rvv = (tt < TC && t < T && r0 + rr < dv) ? Y[(size_t)t * ldy + off_v + rr] : 0.f;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < QK_PER; ++x) {
+      const int f = tid + 256 * x;
+      const int tt = f / (2 * DKM), e = f % (2 * DKM);
+      if (tt < TC) sqk[buf][tt][e] = rq[x];
+    }
+    if (tid < 2 * TC) sab[buf][tid >> 1][tid & 1] = rab;
+    if (tid / RW < TC) sv[buf][tid / RW][tid % RW] = rvv;
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int t0 = 0, buf = 0; t0 < T; t0 += TC, buf ^= 1) {
+    if (t0 + TC < T) fetch(t0 + TC);
+    const int nt = min(TC, T - t0);
+    // the next step's operands are read from LDS while the current step computes
+    float q[NE], k[NE], a, b, v;
+    auto lds_step = [&](int tt, float* qo, float* ko, float& ao, float& bo, float& vo) {
+      const float* qp = &sqk[buf][tt][NE * c];
+      const float* kp = &sqk[buf][tt][DKM + NE * c];
+      if constexpr (NE % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < NE; j += 4) {
+          const float4 x = *(const float4*)(qp + j);
+          const float4 y = *(const float4*)(kp + j);
+          qo[j] = x.x; qo[j + 1] = x.y; qo[j + 2] = x.z; qo[j + 3] = x.w;
+          ko[j] = y.x; ko[j + 1] = y.y; ko[j + 2] = y.z; ko[j + 3] = y.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+          qo[j] = qp[j];
+          ko[j] = kp[j];
+        }
+      }
+      ao = sab[buf][tt][0];
+      bo = sab[buf][tt][1];
+      vo = sv[buf][tt][rl];
+    };
+    auto step = [&](int tt, const float* qv, const float* kv, float av, float bv, float vv) {
+      float kd = 0.f;
+#pragma unroll
+      for (int j = 0; j < NE; ++j) kd = fmaf(s[j], kv[j], kd);
+      kd = sum32(kd);
+      const float u = bv * (vv - av * kd);
+      float od = 0.f;
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        s[j] = fmaf(u, kv[j], av * s[j]);
+        od = fmaf(s[j], qv[j], od);
+      }
+      od = sum32(od);
+      if (c == 0 && valid) split_store(od, Ohi, Olo, (size_t)(t0 + tt) * ldo + h * dv + i);
+    };
+    // two steps per round with ping-pong operands: the reads for step t + 1 are in flight while
+    // step t computes, in straight-line code (TC is even, so every read stays inside the chunk; a
+    // step past the chunk's last token is skipped)
+    float q2[NE], k2[NE], a2, b2, v2;
+    lds_step(0, q, k, a, b, v);
+    for (int tt = 0; tt < nt; tt += 2) {
+      lds_step(tt + 1, q2, k2, a2, b2, v2);
+      step(tt, q, k, a, b, v);
+      if (tt + 2 < TC) lds_step(tt + 2, q, k, a, b, v);
+      if (tt + 1 < nt) step(tt + 1, q2, k2, a2, b2, v2);
+    }
+    __syncthreads();
+    if (t0 + TC < T) stash(buf ^ 1);
+    __syncthreads();
+  }
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const int e = NE * c + j;
+      if (e < dk) srow[e] = s[j];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ attention
+// q/k/v columns of Y are in RoPE pair order per head (2m, 2m + 1) = (dim m, dim m + hd/2).  Rotate q
+// and k at positions p0 + t, write k and v to the cache, q to Q[t][head][hd] in natural order.
+__global__ void pf_att_rope_kernel(const float* __restrict__ Y, int ldy, int p0, int nq, int nkv, int hd, int max_ctx,
+                                   const float* __restrict__ rcos, const float* __restrict__ rsin, float* __restrict__ Q,
+                                   float* __restrict__ Kc, float* __restrict__ Vc) {
+  const int t = blockIdx.x;
+  const int half = hd / 2, pos = p0 + t;
+  const float* y = Y + (size_t)t * ldy;
+  const int npairs = (nq + 2 * nkv) * half;
+  for (int P = threadIdx.x; P < npairs; P += blockDim.x) {
+    const float x1 = y[2 * P], x2 = y[2 * P + 1];
+    const int hh = P / half, m = P - hh * half;
+    if (hh < nq + nkv) {
+      const float c = rcos[(size_t)pos * half + m], sv = rsin[(size_t)pos * half + m];
+      const float y1 = x1 * c - x2 * sv, y2 = x2 * c + x1 * sv;
+      if (hh < nq) {
+        float* qo = Q + ((size_t)t * nq + hh) * hd;
+        qo[m] = y1;
+        qo[m + half] = y2;
+      } else {
+        float* ko = Kc + ((size_t)(hh - nq) * max_ctx + pos) * hd;
+        ko[m] = y1;
+        ko[m + half] = y2;
+      }
+    } else {
+      float* vo = Vc + ((size_t)(hh - nq - nkv) * max_ctx + pos) * hd;
+      vo[m] = x1;
+      vo[m + half] = x2;
+    }
+  }
+}
+
+// Causal attention for the chunk's queries over cache positions 0 .. p0 + t.  A workgroup (4 waves)
+// takes one KV head g and QB = 16 / gs consecutive queries of every query head of its group: 16
+// (head, query) rows.  Keys go through LDS in blocks of 32 positions (LDS-DMA, double-buffered, the
+// next block in flight while the current one is used).  Per block: scores with one thread per
+// (row, key pair), the block's max and sum per row over a 16-lane DPP row, then P.V with one thread
+// per (row, 8 dims); the running max / sum / output are rescaled per block (online softmax).
+constexpr int KB = 32;
+constexpr int HDM = 256;  // largest head size
+template <int DPL>  // head dims per lane in P.V (a power of two >= hd / 16)
+__global__ void __launch_bounds__(256) pf_attention_kernel(const float* __restrict__ Q, const float* __restrict__ Kc,
+                                                           const float* __restrict__ Vc, int T, int p0, int nq, int nkv,
+                                                           int hd, int max_ctx, uint16_t* __restrict__ Ohi,
+                                                           uint16_t* __restrict__ Olo, int ldo) {
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int lpp = hd >> 2, pps = 64 / lpp, nsl = (KB + pps - 1) / pps;  // lanes / keys per 1 KB slot
+  float* skv = sm;                                  // [2 buffers][2 (K, V)][nsl slots][256 floats]
+  float* sq = sm + 2 * 2 * nsl * 256;               // [16][hd]
+  float* sp = sq + 16 * HDM;                        // [16][KB]
+  float* sc = sp + 16 * KB;                         // [16] rescale of the running output
+  const int gs = nq / nkv, QB = 16 / gs;
+  const int nqb = (T + QB - 1) / QB;
+  const int g = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+  const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+  const int jend = p0 + min(T, (qb + 1) * QB);  // keys this workgroup needs: [0, jend)
+  const int nblk = (jend + KB - 1) / KB;
+  const float scale = 1.0f / sqrtf((float)hd);
+  auto issue = [&](int blk) {
+    float* base = skv + (size_t)(blk & 1) * 2 * nsl * 256;
+    for (int q = wv; q < 2 * nsl; q += 4) {
+      const int isv = q >= nsl, sl = q - isv * nsl;
+      const int kk = sl * pps + l / lpp, j = blk * KB + kk;
+      const float* src = (isv ? Vc : Kc) + ((size_t)g * max_ctx + min(j, jend - 1)) * hd + (l % lpp) * 4;
+      if (l < pps * lpp && kk < KB)
+        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + q * 256),
+                                         16, 0, 0);
+    }
+  };
+  const int ncopy = wv < 2 * nsl ? (2 * nsl - wv + 3) / 4 : 0;  // copies this wave issues per block
+  issue(0);
+  // queries of the 16 rows, pre-scaled
+  for (int x = tid; x < 16 * hd; x += 256) {
+    const int row = x / hd, e = x % hd;
+    const int hq = g * gs + row / QB, tq = qb * QB + row % QB;
+    sq[row * HDM + e] = tq < T ? Q[((size_t)tq * nq + hq) * hd + e] * scale : 0.f;
+  }
+  // P.V mapping: thread -> (row, 8 dims); score mapping: thread -> (row, keys 2c, 2c + 1)
+  const int prow = tid >> 4, pc = tid & 15;
+  const int tq_p = qb * QB + prow % QB;
+  const int jmax = p0 + min(tq_p, T - 1);
+  float acc[DPL];
+#pragma unroll
+  for (int x = 0; x < DPL; ++x) acc[x] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+  for (int blk = 0; blk < nblk; ++blk) {
+    if (blk + 1 < nblk) {
+      issue(blk + 1);
+      wait_vm_n(ncopy);  // this block's copies are done once only the next block's remain
+    } else {
+      wait_vm<0>();
+    }
+    lds_bar();
+    const float* kb = skv + (size_t)(blk & 1) * 2 * nsl * 256;
+    const float* vb = kb + nsl * 256;
+    const int j0 = blk * KB;
+    // scores of keys 2pc and 2pc + 1 for row prow
+    float s2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kk = 2 * pc + u, j = j0 + kk;
+      float a = -INFINITY;
+      if (j <= jmax) {
+        const float* kr = kb + (kk / pps) * 256 + (kk % pps) * hd;
+        const float* qr = sq + prow * HDM;
+        const int n4 = hd >> 2, st0 = kk % n4;  // staggered start: the keys of a row hit different banks
+        float d = 0.f;
+        for (int d0 = 0; d0 < n4; d0 += 8) {
+          float4 kv[8], qv[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            int e = d0 + x + st0;
+            e = (e >= n4 ? e - n4 : e) * 4;
+            kv[x] = float4{0.f, 0.f, 0.f, 0.f};
+            qv[x] = kv[x];
+            if (d0 + x < n4) {
+              kv[x] = *(const float4*)(kr + e);
+              qv[x] = *(const float4*)(qr + e);
+            }
+          }
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            d = fmaf(kv[x].x, qv[x].x, d);
+            d = fmaf(kv[x].y, qv[x].y, d);
+            d = fmaf(kv[x].z, qv[x].z, d);
+            d = fmaf(kv[x].w, qv[x].w, d);
+          }
+        }
+        a = d;
+      }
+      s2[u] = a;
+    }
+    // block max and the running rescale, per 16-lane row (one row = one query row)
+    float bm = fmaxf(s2[0], s2[1]);
+    bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bm), __float_as_int(bm), 0xB1, 0xF, 0xF, false)));
+    bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bm), __float_as_int(bm), 0x4E, 0xF, 0xF, false)));
+    bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bm), __float_as_int(bm), 0x141, 0xF, 0xF, false)));
+    bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bm), __float_as_int(bm), 0x140, 0xF, 0xF, false)));
+    const float mn = fmaxf(m, bm);                 // finite: key 0 of block 0 is always visible
+    const float corr = expf(m - mn);
+    const float e0 = expf(s2[0] - mn), e1 = expf(s2[1] - mn);
+    lsum = fmaf(lsum, corr, row_sum16(e0 + e1));
+    m = mn;
+    sp[prow * KB + 2 * pc] = e0;
+    sp[prow * KB + 2 * pc + 1] = e1;
+    lds_bar();
+    // P.V for row prow, dims pc * DPL .. + DPL (four keys' values loaded before they are used)
+    const int nvalid = min(KB, jend - j0);
+    const bool live = pc * DPL < hd;
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) acc[x] *= corr;
+    for (int k0 = 0; k0 < nvalid; k0 += 4) {
+      float pk[4], vv[4][DPL];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = k0 + u;
+        pk[u] = kk < nvalid ? sp[prow * KB + kk] : 0.f;
+        const float* vr = vb + (kk / pps) * 256 + (kk % pps) * hd + pc * DPL;
+#pragma unroll
+        for (int x = 0; x < DPL; x += (DPL >= 4 ? 4 : 2)) {
+          if (DPL >= 4) {
+            const float4 t4 = (kk < nvalid && live) ? *(const float4*)(vr + x) : float4{0.f, 0.f, 0.f, 0.f};
+            vv[u][x] = t4.x;
+            vv[u][x + 1] = t4.y;
+            vv[u][x + 2] = t4.z;
+            vv[u][x + 3] = t4.w;
+          } else {
+            const float2 t2 = (kk < nvalid && live) ? *(const float2*)(vr + x) : float2{0.f, 0.f};
+            vv[u][x] = t2.x;
+            vv[u][x + 1] = t2.y;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) acc[x] = fmaf(pk[u], vv[u][x], acc[x]);
+    }
+    lds_bar();  // this block's buffer is refilled next iteration, sp rewritten
+  }
+  const int hq = g * gs + prow / QB;
+  if (tq_p < T) {
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) {
+      const int e = pc * DPL + x;
+      if (e < hd) split_store(acc[x] * inv, Ohi, Olo, (size_t)tq_p * ldo + hq * hd + e);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ LM head on one row
+// x -> rmsnorm(x) * g -> logits = E . xn over rows [w * rpw, ...); per-workgroup (max, index) with
+// the lowest index among equal maxima
+__global__ void __launch_bounds__(256) pf_lmhead_kernel(const float* __restrict__ x, int D,
+                                                        const uint16_t* __restrict__ g, float eps,
+                                                        const uint16_t* __restrict__ E, int vocab,
+                                                        float* __restrict__ logits, float* __restrict__ part) {
+  extern __shared__ float xs[];
+  __shared__ float red[8];
+  __shared__ int redi[4];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) s = fmaf(x[i], x[i], s);
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  s = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(s / (float)D + eps);
+  for (int i = threadIdx.x; i < D; i += 256) xs[i] = x[i] * r * bf16f(g[i]);
+  __syncthreads();
+  const int rpw = (vocab + gridDim.x - 1) / gridDim.x;
+  const int v0 = blockIdx.x * rpw, v1 = min(vocab, v0 + rpw);
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  float best = -INFINITY;
+  int bidx = 0x7fffffff;
+  for (int v = v0 + wv; v < v1; v += 4) {
+    const uint16_t* er = E + (size_t)v * D;
+    float a = 0.f;
+    for (int k = l * 8; k < D; k += 512) {
+      const u32x4 wq = *(const u32x4*)(er + k);
+      a = fmaf(__uint_as_float(wq.x << 16), xs[k], a);
+      a = fmaf(__uint_as_float(wq.x & 0xffff0000u), xs[k + 1], a);
+      a = fmaf(__uint_as_float(wq.y << 16), xs[k + 2], a);
+      a = fmaf(__uint_as_float(wq.y & 0xffff0000u), xs[k + 3], a);
+      a = fmaf(__uint_as_float(wq.z << 16), xs[k + 4], a);
+      a = fmaf(__uint_as_float(wq.z & 0xffff0000u), xs[k + 5], a);
+      a = fmaf(__uint_as_float(wq.w << 16), xs[k + 6], a);
+      a = fmaf(__uint_as_float(wq.w & 0xffff0000u), xs[k + 7], a);
+    }
+    a = wave_sum(a);
+    if (logits && l == 0) logits[v] = a;
+    if (a > best || (a == best && v < bidx)) {
+      best = a;
+      bidx = v;
+    }
+  }
+  __syncthreads();
+  if (l == 0) {
+    red[4 + wv] = best;
+    redi[wv] = bidx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < 4; ++i)
+      if (red[4 + i] > best || (red[4 + i] == best && redi[i] < bidx)) {
+        best = red[4 + i];
+        bidx = redi[i];
+      }
+    part[2 * blockIdx.x] = best;
+    part[2 * blockIdx.x + 1] = __int_as_float(bidx);
+  }
+}
+
+__global__ void pf_finish_kernel(const float* __restrict__ part, int n, int32_t* __restrict__ next, MkCtl* ctl,
+                                 int32_t pos) {
+  if (threadIdx.x != 0) return;
+  float b = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = 0; i < n; ++i) {
+    const float v = part[2 * i];
+    const int vi = __float_as_int(part[2 * i + 1]);
+    if (v > b || (v == b && vi < bi)) {
+      b = v;
+      bi = vi;
+    }
+  }
+  next[0] = bi;
+  ctl->pos = pos;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------ launchers
+#define MK_LAUNCH_OK() (hipGetLastError() == hipSuccess ? 0 : -1)
+
+extern "C" int mk_pf_embed(const int32_t* tok, int T, const uint16_t* embed, int D, int vocab, float* X, MkCtl* ctl,
+                           void* stream) {
+  hipLaunchKernelGGL(pf_embed_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, tok, T, embed, D, vocab, X, ctl);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_rms_split(const float* X, int T, int D, const uint16_t* g, float eps, uint16_t* Ahi,
+                               uint16_t* Alo, int lda, void* stream) {
+  hipLaunchKernelGGL(pf_rms_split_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, X, D, g, eps, Ahi, Alo, lda);
+  return MK_LAUNCH_OK();
+}
+
+template <int BM, int BN>
+static int launch_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W, int N,
+                       float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, hipStream_t s) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int grid = ((tiles + 7) / 8) * 8;
+  const size_t lds = (size_t)STAGES * (2 * BM + BN) * BK * 2;
+  if (epi == 0)
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 0>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+                       Hhi, Hlo, ldh);
+  else if (epi == 1)
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 1>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+                       Hhi, Hlo, ldh);
+  else
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 2>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+                       Hhi, Hlo, ldh);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W,
+                          int N, float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, void* stream) {
+  // large tiles when they alone fill the chip, otherwise 64 x 64 tiles for more workgroups
+  const int big = ((M + 127) / 128) * ((N + 127) / 128);
+  if (big >= 200)
+    return launch_gemm<128, 128>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, (hipStream_t)stream);
+  return launch_gemm<64, 64>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, (hipStream_t)stream);
+}
+
+extern "C" int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB,
+                             void* stream) {
+  hipLaunchKernelGGL(pf_dn_prep_kernel, dim3(T * H), dim3(64), 0, (hipStream_t)stream, Y, ldy, H, dk, dv, l2eps, QK, AB);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk,
+                             int dv, uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream) {
+  const dim3 grid(H * ((dv + 7) / 8));
+  hipStream_t s = (hipStream_t)stream;
+  if (dk <= 32)
+    hipLaunchKernelGGL(pf_dn_scan_kernel<1>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+  else if (dk <= 64)
+    hipLaunchKernelGGL(pf_dn_scan_kernel<2>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+  else if (dk <= 128)
+    hipLaunchKernelGGL(pf_dn_scan_kernel<4>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+  else
+    hipLaunchKernelGGL(pf_dn_scan_kernel<8>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, int max_ctx,
+                              const float* rcos, const float* rsin, float* Q, float* Kc, float* Vc, void* stream) {
+  hipLaunchKernelGGL(pf_att_rope_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, Y, ldy, p0, nq, nkv, hd, max_ctx,
+                     rcos, rsin, Q, Kc, Vc);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,
+                               int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream) {
+  const int gs = nq / nkv, QB = 16 / gs;
+  const int lpp = hd / 4, pps = 64 / lpp, nsl = (KB + pps - 1) / pps;
+  const size_t lds = ((size_t)2 * 2 * nsl * 256 + 16 * HDM + 16 * KB + 16) * 4;
+  const dim3 grid(nkv * ((T + QB - 1) / QB));
+  hipStream_t s = (hipStream_t)stream;
+  const int dpl = (hd + 15) / 16;
+  if (dpl <= 2)
+    hipLaunchKernelGGL(pf_attention_kernel<2>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
+  else if (dpl <= 4)
+    hipLaunchKernelGGL(pf_attention_kernel<4>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
+  else if (dpl <= 8)
+    hipLaunchKernelGGL(pf_attention_kernel<8>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
+  else
+    hipLaunchKernelGGL(pf_attention_kernel<16>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo,
+                       ldo);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_lmhead(const float* x, int D, const uint16_t* g, float eps, const uint16_t* E, int vocab,
+                            float* logits, float* part, int nwg, void* stream) {
+  hipLaunchKernelGGL(pf_lmhead_kernel, dim3(nwg), dim3(256), (size_t)D * 4, (hipStream_t)stream, x, D, g, eps, E, vocab,
+                     logits, part);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_finish(const float* part, int nwg, int32_t* next, MkCtl* ctl, int32_t pos, void* stream) {
+  hipLaunchKernelGGL(pf_finish_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, part, nwg, next, ctl, pos);
+  return MK_LAUNCH_OK();
+}
