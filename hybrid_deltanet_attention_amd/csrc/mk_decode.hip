@@ -218,19 +218,17 @@ struct Tracer {
   LS unsigned long long* lbuf;   // timestamps are kept in LDS while the kernel runs ...
   MK_G unsigned long long* buf;  // ... and copied here at the end (null: tracing off)
   int n;
-  // wall-clock stamps: lane 0 of wave 0 (a streaming wave) at [n], lane 0 of the first polling
-  // wave at [MK_TRACE_EVENTS / 2 + n]
+  // wall-clock stamps of lane 0 of wave 0 (a streaming wave)
   __device__ __forceinline__ void mark() {
     if (buf) {
-      if ((threadIdx.x == 0 || threadIdx.x == NCT) && n < MK_TRACE_EVENTS / 2)
-        lbuf[(threadIdx.x == 0 ? 0 : MK_TRACE_EVENTS / 2) + n] = wall_clock64();
+      if (threadIdx.x == 0 && n < MK_TRACE_EVENTS) lbuf[n] = wall_clock64();
       ++n;
     }
   }
   __device__ __forceinline__ void flush() {
     if (buf) {
       wg_bar();
-      for (int i = tid(); i < MK_TRACE_EVENTS; i += MK_NT) buf[i] = lbuf[i];
+      for (int i = tid(); i < MK_TRACE_EVENTS; i += MK_NT) buf[i] = i < n ? lbuf[i] : 0ull;
     }
   }
 };
@@ -441,52 +439,140 @@ __device__ __forceinline__ void issue_units(RegUnits<N>& r, const Gemv& g, int u
 // on the streaming waves (ALL_STREAM: on every wave; only where no poll is pending).
 // PAIRS == false: epi(row, value) once per row; PAIRS == true: epi(pair, v_even, v_odd) once per
 // row pair (slices hold whole pairs).  The epilogue runs on streaming threads (EPI_ALL: on all).
-// Unit partials of one row chunk -> red[row * S + segment].
+// This lane's activations for 512-column segment s: slot k holds columns s*512 + k*128 + 8*(lane%16).
+struct XSlice {
+  float4 v[USLOTS][2];
+};
+__device__ __forceinline__ void load_x(XSlice& x, const LS float* xin, int s, int K) {
+#pragma unroll
+  for (int k = 0; k < USLOTS; ++k) {
+    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
+    x.v[k][0] = float4{0.f, 0.f, 0.f, 0.f};
+    x.v[k][1] = x.v[k][0];
+    if (col < K) {
+      x.v[k][0] = *(const LS float4*)(xin + col);
+      x.v[k][1] = *(const LS float4*)(xin + col + 4);
+    }
+  }
+}
+__device__ __forceinline__ float dot8r(u32x4 w, float4 a, float4 b) {
+  float acc = bf_lo(w.x) * a.x;
+  acc = fmaf(bf_hi(w.x), a.y, acc);
+  acc = fmaf(bf_lo(w.y), a.z, acc);
+  acc = fmaf(bf_hi(w.y), a.w, acc);
+  acc = fmaf(bf_lo(w.z), b.x, acc);
+  acc = fmaf(bf_hi(w.z), b.y, acc);
+  acc = fmaf(bf_lo(w.w), b.z, acc);
+  acc = fmaf(bf_hi(w.w), b.w, acc);
+  return acc;
+}
+// unit partial from its four 16-byte weight pieces (columns past K are skipped: their weights were
+// never copied)
+__device__ __forceinline__ float unit_dot_x(int s, int K, const u32x4* w, const XSlice& x) {
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < USLOTS; ++k) {
+    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
+    if (col < K) acc += dot8r(w[k], x.v[k][0], x.v[k][1]);
+  }
+  return acc;
+}
+
+// Segment-major split of a GEMV's units over a set of NWS waves (this wave is ws): with S <= NWS
+// segments, wave ws takes segment ws % S and every nj-th row block from ws / S; otherwise segments
+// ws, ws + NWS, ... with every row block.  A wave keeps its segment's activations in registers.
+struct SegPlan {
+  int s0, sstep, j, nj;
+  __device__ __forceinline__ void init(int S, int ws, int NWS) {
+    if (S <= NWS) {
+      s0 = ws % S;
+      sstep = S;
+      j = ws / S;
+      nj = (NWS - s0 + S - 1) / S;
+    } else {
+      s0 = ws;
+      sstep = NWS;
+      j = 0;
+      nj = 1;
+    }
+  }
+};
+
+// Unit partials of one row chunk -> red[row * S + segment].  Units u = rb * S + s < nst come from
+// the LDS stage (every wave), the rest stream through registers (streaming waves; ALL_STREAM: all).
 template <bool ALL_STREAM>
 __device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int K, int nst, const LS float* xin,
-                                           const LS u32x4* stage, LS float* red) {
+                                              const LS u32x4* stage, LS float* red) {
   Gemv g;
   g.init(uni_ptr(W), uni(R), uni(K));
   nst = uni(nst);
-  const int U = g.units();
-    // staged units, two per wave per round
-    for (int u0 = wave(); u0 < nst; u0 += 2 * MK_NWAVE) {
-      const int u1 = u0 + MK_NWAVE;
-      u32x4 w0[USLOTS], w1[USLOTS];
+  const int S = g.S, RB = (g.R + 3) >> 2;
+  {
+    SegPlan sp;
+    sp.init(S, wave(), MK_NWAVE);
+    for (int s = sp.s0; s < S; s += sp.sstep) {
+      if (sp.j * S + s >= nst) break;
+      XSlice x;
+      load_x(x, xin, s, g.K);
+      for (int rb = sp.j; rb * S + s < nst; rb += 2 * sp.nj) {
+        const int u0 = rb * S + s, u1 = (rb + sp.nj) * S + s;
+        const bool h1 = u1 < nst;
+        u32x4 w0[USLOTS], w1[USLOTS];
 #pragma unroll
-      for (int k = 0; k < USLOTS; ++k) {
-        w0[k] = stage[(u0 * USLOTS + k) * SLOT + lane()];
-        w1[k] = u1 < nst ? stage[(u1 * USLOTS + k) * SLOT + lane()] : u32x4{0u, 0u, 0u, 0u};
-      }
-      float a0 = unit_dot(g, u0, w0, xin);
-      float a1 = u1 < nst ? unit_dot(g, u1, w1, xin) : 0.f;
-      a0 = row_sum16(a0);
-      a1 = row_sum16(a1);
-      put_partial(g, u0, a0, red);
-      if (u1 < nst) put_partial(g, u1, a1, red);
-    }
-    // the rest through registers, two units per batch, two batches in flight
-    if (ALL_STREAM || streamer()) {
-      const int nsw = ALL_STREAM ? MK_NWAVE : NCW;
-      const int first = nst + wave();
-      if (first < U) {
-        RegUnits<2> cur, nxt;
-        issue_units<2>(cur, g, first, nsw, U);
-        keep_issued();
-        for (int u = first; u < U; u += 2 * nsw) {
-          issue_units<2>(nxt, g, u + 2 * nsw, nsw, U);
-          keep_issued();
-          float a0 = unit_dot(g, u, cur.c, xin);
-          float a1 = u + nsw < U ? unit_dot(g, u + nsw, cur.c + USLOTS, xin) : 0.f;
-          a0 = row_sum16(a0);
-          a1 = row_sum16(a1);
-          put_partial(g, u, a0, red);
-          if (u + nsw < U) put_partial(g, u + nsw, a1, red);
-#pragma unroll
-          for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = nxt.c[i];
+        for (int k = 0; k < USLOTS; ++k) {
+          w0[k] = stage[(u0 * USLOTS + k) * SLOT + lane()];
+          w1[k] = h1 ? stage[(u1 * USLOTS + k) * SLOT + lane()] : u32x4{0u, 0u, 0u, 0u};
         }
+        float a0 = unit_dot_x(s, g.K, w0, x);
+        float a1 = h1 ? unit_dot_x(s, g.K, w1, x) : 0.f;
+        a0 = row_sum16(a0);
+        a1 = row_sum16(a1);
+        put_partial(g, u0, a0, red);
+        if (h1) put_partial(g, u1, a1, red);
       }
     }
+  }
+  if (ALL_STREAM || streamer()) {
+    const int NSW = ALL_STREAM ? MK_NWAVE : NCW;
+    SegPlan sp;
+    sp.init(S, wave(), NSW);
+    for (int s = sp.s0; s < S; s += sp.sstep) {
+      // first row block of this wave's sequence whose unit is past the stage
+      int rb = sp.j;
+      if (rb * S + s < nst) rb += ((nst - s - rb * S + S - 1) / S + sp.nj - 1) / sp.nj * sp.nj;
+      if (rb >= RB) continue;
+      XSlice x;
+      load_x(x, xin, s, g.K);
+      const int step = sp.nj;
+      auto issue2 = [&](RegUnits<2>& r, int rb0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int rbi = rb0 + i * step;
+#pragma unroll
+          for (int k = 0; k < USLOTS; ++k) {
+            const MK_G uint16_t* a = rbi < RB ? g.addr(rbi * S + s, k) : nullptr;
+            r.c[i * USLOTS + k] = a ? ldw(a) : u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      };
+      RegUnits<2> cur, nxt;
+      issue2(cur, rb);
+      keep_issued();
+      for (; rb < RB; rb += 2 * step) {
+        issue2(nxt, rb + 2 * step);
+        keep_issued();
+        const bool h1 = rb + step < RB;
+        float a0 = unit_dot_x(s, g.K, cur.c, x);
+        float a1 = h1 ? unit_dot_x(s, g.K, cur.c + USLOTS, x) : 0.f;
+        a0 = row_sum16(a0);
+        a1 = row_sum16(a1);
+        put_partial(g, rb * S + s, a0, red);
+        if (h1) put_partial(g, (rb + step) * S + s, a1, red);
+#pragma unroll
+        for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = nxt.c[i];
+      }
+    }
+  }
 }
 
 template <bool PAIRS, bool EPI_ALL, bool ALL_STREAM, typename Epi>
