@@ -206,11 +206,9 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   p.lds_flag = take(4);
   o = (o + 1) / 2 * 2;
   p.lds_trace = take(2 * MK_TRACE_EVENTS);
-  o = (o + 255) / 256 * 256;  // 1 KB aligned stages
-  p.lds_stA = take(MK_STAGE_A_SLOTS * 256);
-  p.lds_stB = take(MK_STAGE_B_SLOTS * 256);
-  // at least 96 KB so that only one workgroup fits per compute unit
-  p.lds_floats = std::max(o, 96 * 1024 / 4);
+  // the prefetch stages are a static array of the kernel (MK_STAGE_A_SLOTS + MK_STAGE_B_SLOTS KB,
+  // more than half the LDS of a compute unit, so one workgroup fits per unit)
+  p.lds_floats = o;
 }
 
 }  // namespace

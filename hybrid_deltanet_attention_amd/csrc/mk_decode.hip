@@ -26,6 +26,11 @@
 
 typedef unsigned int u32;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+// Native vector types for LDS accesses: loads of HIP's float4 / uint2 structs are split and merged
+// again late in code generation, which drops what the compiler knows about the accessed LDS object
+// and makes it wait for every outstanding LDS-DMA copy before the read.
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 // LDS pointers are kept in address space 3 so every access is a ds_* instruction
 #if defined(__HIP_DEVICE_COMPILE__)
 #define LS __attribute__((address_space(3)))
@@ -124,19 +129,75 @@ __device__ __forceinline__ void dma16(const MK_G void* src, LS void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-// 8 BF16 weights . 8 FP32 activations (activations 16-byte aligned)
-__device__ __forceinline__ float dot8(u32x4 w, const LS float* x) {
-  const float4 a = *(const LS float4*)x;
-  const float4 b = *(const LS float4*)(x + 4);
-  float acc = bf_lo(w.x) * a.x;
-  acc = fmaf(bf_hi(w.x), a.y, acc);
-  acc = fmaf(bf_lo(w.y), a.z, acc);
-  acc = fmaf(bf_hi(w.y), a.w, acc);
-  acc = fmaf(bf_lo(w.z), b.x, acc);
-  acc = fmaf(bf_hi(w.z), b.y, acc);
-  acc = fmaf(bf_lo(w.w), b.z, acc);
-  acc = fmaf(bf_hi(w.w), b.w, acc);
-  return acc;
+// The LDS regions that LDS-DMA fills (the two prefetch stages) live in their own static array; every
+// other LDS region lives in the dynamic array and is written only by ds_* stores.  The compiler can
+// then prove that reads of the dynamic regions never race a copy and issues them without waiting.
+// Reads of the stage regions go through the asm blocks below: left to the compiler, each would wait
+// for every outstanding vector-memory operation of the wave, the prefetches for later phases
+// included.  That the copies a read needs have landed is ensured by the explicit vmcnt waits before
+// the barrier that precedes the read.  Each block waits for its own reads.
+__shared__ __attribute__((aligned(1024))) u32x4 g_stage[(MK_STAGE_A_SLOTS + MK_STAGE_B_SLOTS) * SLOT];
+
+__device__ __forceinline__ u32 lds_addr(const LS void* p) { return (u32)(size_t)p; }
+
+// four 16-byte reads at p, p + 1 KB, p + 2 KB, p + 3 KB (one GEMV unit)
+__device__ __forceinline__ void stage_unit(const LS u32x4* p, u32x4 (&w)[USLOTS]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+      : "v"(lds_addr(p))
+      : "memory");
+}
+// two units
+__device__ __forceinline__ void stage_units2(const LS u32x4* p, const LS u32x4* q, u32x4 (&w)[USLOTS],
+                                             u32x4 (&v)[USLOTS]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "ds_read_b128 %5, %9 offset:1024\n\t"
+      "ds_read_b128 %6, %9 offset:2048\n\t"
+      "ds_read_b128 %7, %9 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(lds_addr(p)), "v"(lds_addr(q))
+      : "memory");
+}
+// four floats at independent addresses
+__device__ __forceinline__ void stage_f32x4(const LS float* a, const LS float* b, const LS float* c,
+                                            const LS float* d, float (&o)[4]) {
+  asm volatile(
+      "ds_read_b32 %0, %4\n\t"
+      "ds_read_b32 %1, %5\n\t"
+      "ds_read_b32 %2, %6\n\t"
+      "ds_read_b32 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(lds_addr(a)), "v"(lds_addr(b)), "v"(lds_addr(c)), "v"(lds_addr(d))
+      : "memory");
+}
+// eight float4 at independent addresses
+__device__ __forceinline__ void stage_f4x8(const LS float* const (&a)[8], f32x4 (&o)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(lds_addr(a[0])), "v"(lds_addr(a[1])), "v"(lds_addr(a[2])), "v"(lds_addr(a[3])), "v"(lds_addr(a[4])),
+        "v"(lds_addr(a[5])), "v"(lds_addr(a[6])), "v"(lds_addr(a[7]))
+      : "memory");
 }
 
 template <int CTRL, int ROW_MASK>
@@ -197,7 +258,7 @@ struct Lds {
   LS uint16_t* gain;    // BF16 RMSNorm gains [2 (layer parity)][2][D]
   LS float* rope;       // cos [hd/2], sin [hd/2] at this launch's position
   LS float* x;          // residual [D]
-  LS float* xn;         // normalised residual [D]
+  LS u32* xn;           // normalised residual [D], hi/lo BF16 pairs
   LS float* vec;        // gathered mixer output / FFN hidden, argmax records
   LS float* att;        // gathered DeltaNet / attention inputs, combine staging, GEMV unit partials
   LS float* scr;        // small reductions
@@ -233,6 +294,28 @@ struct Tracer {
   }
 };
 
+// GEMV activations are held as BF16 hi + lo pairs (see the GEMV section).
+__device__ __forceinline__ u32 bf16_rne_bits(float f) {
+  const u32 u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// v -> (hi, lo) BF16 bit patterns with v = hi + lo + O(2^-17 |v|)
+__device__ __forceinline__ void split_hl(float v, u32& h, u32& l) {
+  h = bf16_rne_bits(v);
+  l = bf16_rne_bits(v - __uint_as_float(h << 16));
+}
+// word offsets (u32) of the hi and lo pair holding column c, c even
+__device__ __forceinline__ int hl_word(int c) { return (c >> 3) * 8 + ((c & 7) >> 1); }
+// columns c, c + 1 (c even) -> hi/lo pair words
+__device__ __forceinline__ void put_hl2(LS u32* hl, int c, float v0, float v1) {
+  u32 h0, l0, h1, l1;
+  split_hl(v0, h0, l0);
+  split_hl(v1, h1, l1);
+  const int o = hl_word(c);
+  hl[o] = h0 | (h1 << 16);
+  hl[o + 4] = l0 | (l1 << 16);
+}
+
 // ------------------------------------------------------------------------ exchanges (polling waves)
 // Poll n records, record f at src(f); use(f, value) once its epoch matches.  Polling threads keep
 // PB loads in flight each.  Every thread calls it; streaming threads return at once.
@@ -241,7 +324,8 @@ __device__ __forceinline__ bool gather_map(const Ctx& cx, int n, SrcFn src, UseF
   if (streamer()) return true;
   const u32 e = cx.epoch;
   const int pl = tid() - NCT;
-  for (int base = 0; base < n; base += NPT * PB) {
+  bool ok = true;
+  for (int base = 0; ok && base < n; base += NPT * PB) {
     u32 pending = 0;
 #pragma unroll
     for (int k = 0; k < PB; ++k)
@@ -260,22 +344,27 @@ __device__ __forceinline__ bool gather_map(const Ctx& cx, int n, SrcFn src, UseF
         }
       if (pending) {
         ++spins;
-        if ((spins & 255u) == 0 && err_seen(cx)) return false;
-        if (spins > MK_SPIN_LIMIT) {
-          set_err(cx, 1u);
-          return false;
+        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
+          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
+          ok = false;
+          break;
         }
       }
     }
   }
-  return true;
+  // Every poll load has been used (or abandoned) by now; the wait, free here, tells the compiler
+  // so.  Loads it cannot match with a use look outstanding to it, and a later reuse of their
+  // registers would wait for all vector-memory operations, prefetch copies included.
+  wait_vm<0>();
+  return ok;
 }
 
 // Contiguous records src[0..n) -> dst[0..n), two records per 16-byte device-coherent load.  Each
 // 8-byte record is read whole (it sits in one aligned 8-byte word), so a pair is complete once
 // both halves carry the epoch.
+template <bool HL>
 __device__ __forceinline__ bool gather_vec_impl(MK_G MkCtl* ctl, u32 epoch, const MK_G mk_u64* src, int n,
-                                            LS float* dst) {
+                                                LS float* dst) {
   Ctx cx;
   cx.ctl = uni_ptr(ctl);
   cx.epoch = (u32)uni((int)epoch);
@@ -285,7 +374,8 @@ __device__ __forceinline__ bool gather_vec_impl(MK_G MkCtl* ctl, u32 epoch, cons
   const int pl = tid() - NCT;
   const int np = (n + 1) >> 1;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, np * 16, 0x00020000);
-  for (int base = 0; base < np; base += NPT * PB) {
+  bool ok = true;
+  for (int base = 0; ok && base < np; base += NPT * PB) {
     u32 pending = 0;
 #pragma unroll
     for (int k = 0; k < PB; ++k)
@@ -302,35 +392,71 @@ __device__ __forceinline__ bool gather_vec_impl(MK_G MkCtl* ctl, u32 epoch, cons
         const int j = base + k * NPT + pl;
         const bool two = 2 * j + 1 < n;
         if (((pending >> k) & 1u) && v[k].y == e && (!two || v[k].w == e)) {
-          dst[2 * j] = __uint_as_float(v[k].x);
-          if (two) dst[2 * j + 1] = __uint_as_float(v[k].z);
+          if (HL) {
+            put_hl2((LS u32*)dst, 2 * j, __uint_as_float(v[k].x), two ? __uint_as_float(v[k].z) : 0.f);
+          } else {
+            dst[2 * j] = __uint_as_float(v[k].x);
+            if (two) dst[2 * j + 1] = __uint_as_float(v[k].z);
+          }
           pending &= ~(1u << k);
         }
       }
       if (pending) {
         ++spins;
-        if ((spins & 255u) == 0 && err_seen(cx)) return false;
-        if (spins > MK_SPIN_LIMIT) {
-          set_err(cx, 1u);
-          return false;
+        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
+          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
+          ok = false;
+          break;
         }
       }
     }
   }
-  return true;
+  wait_vm<0>();  // as in gather_map
+  return ok;
 }
 
 __device__ __forceinline__ bool gather_vec(const Ctx& cx, const MK_G mk_u64* src, int n, LS float* dst) {
   if (streamer()) return true;
-  return gather_vec_impl(cx.ctl, cx.epoch, src, n, dst);
+  return gather_vec_impl<false>(cx.ctl, cx.epoch, src, n, dst);
+}
+// the same into the GEMV activation layout (hi/lo BF16 pairs); n even
+__device__ __forceinline__ bool gather_hl(const Ctx& cx, const MK_G mk_u64* src, int n, LS u32* dst) {
+  if (streamer()) return true;
+  return gather_vec_impl<true>(cx.ctl, cx.epoch, src, n, (LS float*)dst);
+}
+// FP32 v[0..n) (n a multiple of 8) -> the GEMV activation layout in place, by all threads: each
+// group of 8 values is rewritten as its hi and lo pairs.  Between barriers.
+__device__ __forceinline__ void to_hl(LS float* v, int n) {
+  for (int gidx = tid(); gidx < (n >> 3); gidx += MK_NT) {
+    LS f32x4* p = (LS f32x4*)(v + 8 * gidx);
+    const f32x4 a = p[0], b = p[1];
+    u32 h[8], l[8];
+    split_hl(a.x, h[0], l[0]);
+    split_hl(a.y, h[1], l[1]);
+    split_hl(a.z, h[2], l[2]);
+    split_hl(a.w, h[3], l[3]);
+    split_hl(b.x, h[4], l[4]);
+    split_hl(b.y, h[5], l[5]);
+    split_hl(b.z, h[6], l[6]);
+    split_hl(b.w, h[7], l[7]);
+    LS u32x4* q = (LS u32x4*)p;
+    q[0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    q[1] = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+  }
 }
 
 // ------------------------------------------------------------------------ GEMV
 // out[r] = W[r] . x for the R rows of a workgroup's slice (row stride K).  A unit is 4 rows x 512
-// columns (4 KB of BF16): 16 lanes per row, each lane 8 columns of each of the unit's four 128-column
-// slots, so one wave instruction reads 4 rows x 256 contiguous bytes.  A unit's partial is reduced
-// over its 16 lanes in a fixed DPP order and parked in LDS; a row's value adds its 512-column
-// segment partials in segment order, so it does not depend on how rows are split over workgroups.
+// columns (4 KB of BF16): slot k (1 KB) is row k's 512 columns, contiguous in memory, and lane l holds
+// columns 8l .. 8l+7 of all four rows, so a lane needs only its own 8 activations.  Activations are
+// kept in LDS as BF16 hi + lo pairs (x = hi + lo to about 2^-17 relative): per group of 8 columns,
+// 16 bytes of hi pairs then 16 bytes of lo pairs.  Products go through v_dot2c_f32_bf16 (exact BF16
+// products, FP32 accumulation), two per weight pair.  A unit's four row partials are reduced over the
+// wave in a fixed order (lane-half swaps, then a 16-lane DPP row sum) and parked in LDS; a row's
+// value adds its 512-column segment partials in segment order, so it does not depend on how rows
+// are split over workgroups.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 struct Gemv {
   const MK_G uint16_t* W;
   int R, K, S;  // rows, columns, 512-column segments
@@ -342,15 +468,15 @@ struct Gemv {
   }
   __device__ __forceinline__ int units() const { return ((R + 3) >> 2) * S; }
   __device__ __forceinline__ int chunk_rows() const { return max(4, (MK_RED_CAP / S) & ~3); }
-  // this lane's 16 bytes of slot k of unit u; null outside the matrix
+  // this lane's 16 bytes of slot k (row 4 rb + k) of unit u; null outside the matrix
   __device__ __forceinline__ const MK_G uint16_t* addr(int u, int k) const {
     const int rb = u / S, s = u - rb * S;
-    const int row = rb * 4 + (lane() >> 4);
-    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
+    const int row = rb * 4 + k;
+    const int col = s * 512 + lane() * 8;
     return (row < R && col < K) ? W + (size_t)row * K + col : nullptr;
   }
-  // slot k of unit u holds columns of the matrix (uniform over the wave)
-  __device__ __forceinline__ bool live(int u, int k) const { return (u % S) * 512 + k * 128 < K; }
+  // slot k of unit u holds a row of the matrix (uniform over the wave)
+  __device__ __forceinline__ bool live(int u, int k) const { return (u / S) * 4 + k < R; }
 };
 
 // Units staged for g: the first min(units of its first row chunk, cap) units.
@@ -372,7 +498,7 @@ __device__ __forceinline__ int gemv_stage_impl(const MK_G uint16_t* W, int R, in
     if (g.live(u, c)) {
       const MK_G uint16_t* a = g.addr(u, c);
       if (a) dma16(a, stage + (u * USLOTS + c) * SLOT);
-      ++cnt;  // lanes 0..15 (the unit's first row) are always live here, so the copy is issued
+      ++cnt;  // lane 0 (the segment's first 8 columns) is always inside the matrix here
     }
   }
   return cnt;
@@ -381,17 +507,6 @@ __device__ __forceinline__ int gemv_stage_impl(const MK_G uint16_t* W, int R, in
 __device__ __forceinline__ int gemv_stage(const Gemv& g, LS u32x4* stage, int cap) {
   if (!streamer()) return 0;
   return gemv_stage_impl(g.W, g.R, g.K, stage, cap);
-}
-
-__device__ __forceinline__ float unit_dot(const Gemv& g, int u, const u32x4* w, const LS float* x) {
-  const int s = u % g.S;
-  float acc = 0.f;
-#pragma unroll
-  for (int k = 0; k < USLOTS; ++k) {
-    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
-    if (col < g.K) acc += dot8(w[k], x + col);
-  }
-  return acc;
 }
 
 __device__ __forceinline__ void put_partial(const Gemv& g, int u, float v, LS float* red) {
@@ -421,61 +536,53 @@ struct RegUnits {
   u32x4 c[N * USLOTS];
 };
 
-template <int N>
-__device__ __forceinline__ void issue_units(RegUnits<N>& r, const Gemv& g, int u0, int stride, int uend) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int u = u0 + i * stride;
-#pragma unroll
-    for (int k = 0; k < USLOTS; ++k) {
-      const MK_G uint16_t* a = u < uend ? g.addr(u, k) : nullptr;
-      r.c[i * USLOTS + k] = a ? ldw(a) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-// The staged units must be complete and visible (their streaming waves waited for their copies
-// before the barrier that precedes this call).  Units beyond the stage stream through registers,
-// on the streaming waves (ALL_STREAM: on every wave; only where no poll is pending).
-// PAIRS == false: epi(row, value) once per row; PAIRS == true: epi(pair, v_even, v_odd) once per
-// row pair (slices hold whole pairs).  The epilogue runs on streaming threads (EPI_ALL: on all).
-// This lane's activations for 512-column segment s: slot k holds columns s*512 + k*128 + 8*(lane%16).
+// This lane's activations for 512-column segment s: hi and lo pairs of columns s*512 + 8 lane ...
 struct XSlice {
-  float4 v[USLOTS][2];
+  u32x4 h, l;
 };
-__device__ __forceinline__ void load_x(XSlice& x, const LS float* xin, int s, int K) {
-#pragma unroll
-  for (int k = 0; k < USLOTS; ++k) {
-    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
-    x.v[k][0] = float4{0.f, 0.f, 0.f, 0.f};
-    x.v[k][1] = x.v[k][0];
-    if (col < K) {
-      x.v[k][0] = *(const LS float4*)(xin + col);
-      x.v[k][1] = *(const LS float4*)(xin + col + 4);
-    }
+__device__ __forceinline__ void load_x(XSlice& x, const LS u32* hl, int s, int K) {
+  const int col = s * 512 + lane() * 8;
+  x.h = u32x4{0u, 0u, 0u, 0u};
+  x.l = x.h;
+  if (col < K) {
+    const LS u32x4* p = (const LS u32x4*)(hl + (col >> 3) * 8);
+    x.h = p[0];
+    x.l = p[1];
   }
 }
-__device__ __forceinline__ float dot8r(u32x4 w, float4 a, float4 b) {
-  float acc = bf_lo(w.x) * a.x;
-  acc = fmaf(bf_hi(w.x), a.y, acc);
-  acc = fmaf(bf_lo(w.y), a.z, acc);
-  acc = fmaf(bf_hi(w.y), a.w, acc);
-  acc = fmaf(bf_lo(w.z), b.x, acc);
-  acc = fmaf(bf_hi(w.z), b.y, acc);
-  acc = fmaf(bf_lo(w.w), b.z, acc);
-  acc = fmaf(bf_hi(w.w), b.w, acc);
-  return acc;
+__device__ __forceinline__ float dot2(u32 w, u32 x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), acc, false);
 }
-// unit partial from its four 16-byte weight pieces (columns past K are skipped: their weights were
-// never copied)
+// one row's 8 weights . this lane's 8 activations (hi then lo)
+__device__ __forceinline__ float dot8hl(u32x4 w, const XSlice& x) {
+  float a = dot2(w.x, x.h.x, 0.f);
+  a = dot2(w.y, x.h.y, a);
+  a = dot2(w.z, x.h.z, a);
+  a = dot2(w.w, x.h.w, a);
+  a = dot2(w.x, x.l.x, a);
+  a = dot2(w.y, x.l.y, a);
+  a = dot2(w.z, x.l.z, a);
+  return dot2(w.w, x.l.w, a);
+}
+// Four per-lane row partials -> in every lane of 16-lane row i, row i's sum over the wave: rows 0/1
+// and 2/3 trade lane halves (permlane32 swap), then rows 0/1 and 2/3 trade 16-lane rows (permlane16
+// swap), then a DPP sum within each 16-lane row.
+__device__ __forceinline__ float reduce_rows4(float a0, float a1, float a2, float a3) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a2), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a3), false, false);
+  const float p = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float q = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(q), false, false);
+  return row_sum16(__uint_as_float(t[0]) + __uint_as_float(t[1]));
+}
+// unit partial (row 4 rb + lane / 16 in 16-lane row lane / 16) from its four row slots; lanes past
+// column K add nothing (their weights were never copied)
 __device__ __forceinline__ float unit_dot_x(int s, int K, const u32x4* w, const XSlice& x) {
-  float acc = 0.f;
+  const bool in = s * 512 + lane() * 8 < K;
+  float a[USLOTS];
 #pragma unroll
-  for (int k = 0; k < USLOTS; ++k) {
-    const int col = s * 512 + k * 128 + (lane() & 15) * 8;
-    if (col < K) acc += dot8r(w[k], x.v[k][0], x.v[k][1]);
-  }
-  return acc;
+  for (int k = 0; k < USLOTS; ++k) a[k] = in ? dot8hl(w[k], x) : 0.f;
+  return reduce_rows4(a[0], a[1], a[2], a[3]);
 }
 
 // Segment-major split of a GEMV's units over a set of NWS waves (this wave is ws): with S <= NWS
@@ -500,8 +607,9 @@ struct SegPlan {
 
 // Unit partials of one row chunk -> red[row * S + segment].  Units u = rb * S + s < nst come from
 // the LDS stage (every wave), the rest stream through registers (streaming waves; ALL_STREAM: all).
+// xin: activations in hi/lo layout.
 template <bool ALL_STREAM>
-__device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int K, int nst, const LS float* xin,
+__device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int K, int nst, const LS u32* xin,
                                               const LS u32x4* stage, LS float* red) {
   Gemv g;
   g.init(uni_ptr(W), uni(R), uni(K));
@@ -518,15 +626,15 @@ __device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int
         const int u0 = rb * S + s, u1 = (rb + sp.nj) * S + s;
         const bool h1 = u1 < nst;
         u32x4 w0[USLOTS], w1[USLOTS];
+        if (h1) {
+          stage_units2(stage + u0 * USLOTS * SLOT + lane(), stage + u1 * USLOTS * SLOT + lane(), w0, w1);
+        } else {
+          stage_unit(stage + u0 * USLOTS * SLOT + lane(), w0);
 #pragma unroll
-        for (int k = 0; k < USLOTS; ++k) {
-          w0[k] = stage[(u0 * USLOTS + k) * SLOT + lane()];
-          w1[k] = h1 ? stage[(u1 * USLOTS + k) * SLOT + lane()] : u32x4{0u, 0u, 0u, 0u};
+          for (int k = 0; k < USLOTS; ++k) w1[k] = u32x4{0u, 0u, 0u, 0u};
         }
-        float a0 = unit_dot_x(s, g.K, w0, x);
-        float a1 = h1 ? unit_dot_x(s, g.K, w1, x) : 0.f;
-        a0 = row_sum16(a0);
-        a1 = row_sum16(a1);
+        const float a0 = unit_dot_x(s, g.K, w0, x);
+        const float a1 = h1 ? unit_dot_x(s, g.K, w1, x) : 0.f;
         put_partial(g, u0, a0, red);
         if (h1) put_partial(g, u1, a1, red);
       }
@@ -562,21 +670,24 @@ __device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int
         issue2(nxt, rb + 2 * step);
         keep_issued();
         const bool h1 = rb + step < RB;
-        float a0 = unit_dot_x(s, g.K, cur.c, x);
-        float a1 = h1 ? unit_dot_x(s, g.K, cur.c + USLOTS, x) : 0.f;
-        a0 = row_sum16(a0);
-        a1 = row_sum16(a1);
+        const float a0 = unit_dot_x(s, g.K, cur.c, x);
+        const float a1 = h1 ? unit_dot_x(s, g.K, cur.c + USLOTS, x) : 0.f;
         put_partial(g, rb * S + s, a0, red);
         if (h1) put_partial(g, (rb + step) * S + s, a1, red);
 #pragma unroll
         for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = nxt.c[i];
       }
+      // The last iteration's look-ahead loads are never used.  Waiting for them here, on the path
+      // that issued them, keeps them from looking outstanding afterwards, where the compiler would
+      // otherwise wait for all vector-memory operations (prefetch copies included) before reusing
+      // their registers.
+      wait_vm<0>();
     }
   }
 }
 
 template <bool PAIRS, bool EPI_ALL, bool ALL_STREAM, typename Epi>
-__device__ __forceinline__ void gemv(const Gemv& G, const LS float* xin, const LS u32x4* stage, int cap,
+__device__ __forceinline__ void gemv(const Gemv& G, const LS u32* xin, const LS u32x4* stage, int cap,
                                      LS float* red, Tracer& tr, Epi epi) {
   const int rc = G.chunk_rows();
   for (int r0 = 0; r0 < G.R; r0 += rc) {
@@ -600,20 +711,21 @@ __device__ __forceinline__ void gemv(const Gemv& G, const LS float* xin, const L
   }
 }
 
-// x -> xn = x / sqrt(mean x^2 + eps) * g.  Every wave sums the squares itself (same order in every
-// wave), so only the barrier that publishes xn is needed.
-__device__ __forceinline__ void rmsnorm(const LS float* x, const LS uint16_t* g, LS float* xn, int D, float eps,
+// x -> xn = x / sqrt(mean x^2 + eps) * g, written as hi/lo BF16 pairs (the GEMV activation layout).
+// Every wave sums the squares itself (same order in every wave), so only the barrier that
+// publishes xn is needed.
+__device__ __forceinline__ void rmsnorm(const LS float* x, const LS uint16_t* g, LS u32* xn, int D, float eps,
                                         Tracer& tr) {
   D = uni(D);
   const int D4 = D >> 2;  // D is a multiple of 8
-  const LS float4* x4 = (const LS float4*)x;
+  const LS f32x4* x4 = (const LS f32x4*)x;
   // four float4 loads in flight per lane before any of them is used
   float s = 0.f;
   for (int c0 = lane(); c0 < D4; c0 += 256) {
-    float4 v[4];
+    f32x4 v[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      v[k] = float4{0.f, 0.f, 0.f, 0.f};
+      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (c0 + 64 * k < D4) v[k] = x4[c0 + 64 * k];
     }
 #pragma unroll
@@ -628,30 +740,44 @@ __device__ __forceinline__ void rmsnorm(const LS float* x, const LS uint16_t* g,
   const float r = 1.0f / sqrtf(s / (float)D + eps);
   tr.mark();
   for (int c = tid(); c < D4; c += MK_NT) {
-    const float4 v = x4[c];
-    const uint2 gg = *(const LS uint2*)(g + 4 * c);
-    float4 o;
-    o.x = v.x * r * __uint_as_float(gg.x << 16);
-    o.y = v.y * r * __uint_as_float(gg.x & 0xffff0000u);
-    o.z = v.z * r * __uint_as_float(gg.y << 16);
-    o.w = v.w * r * __uint_as_float(gg.y & 0xffff0000u);
-    ((LS float4*)xn)[c] = o;
+    const f32x4 v = x4[c];
+    const u32x2 gg = *(const LS u32x2*)(g + 4 * c);
+    u32 h[4], l[4];
+    split_hl(v.x * r * __uint_as_float(gg.x << 16), h[0], l[0]);
+    split_hl(v.y * r * __uint_as_float(gg.x & 0xffff0000u), h[1], l[1]);
+    split_hl(v.z * r * __uint_as_float(gg.y << 16), h[2], l[2]);
+    split_hl(v.w * r * __uint_as_float(gg.y & 0xffff0000u), h[3], l[3]);
+    const int o = hl_word(4 * c);  // even: columns 4c .. 4c+3 fill two hi and two lo pair words
+    *(LS u32x2*)(xn + o) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *(LS u32x2*)(xn + o + 4) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
   }
   tr.mark();
   wg_bar();
 }
 
-// BF16 gains [n] -> LDS (streaming waves, one 1 KB copy per slot); returns copies issued by this wave
-__device__ __forceinline__ int gain_stage(const MK_G uint16_t* src, int n, LS uint16_t* dst) {
-  if (!streamer()) return 0;
-  const int bytes = 2 * n, nslots = (bytes + 1023) >> 10;
-  int cnt = 0;
-  for (int j = wave(); j < nslots; j += NCW) {
-    const int off = j * 1024 + lane() * 16;
-    if (off < bytes) dma16((const MK_G char*)src + off, (LS char*)dst + j * 1024);
-    ++cnt;
+// RMSNorm gains (BF16, n values, n a multiple of 8) -> LDS by the polling threads with plain loads:
+// issued before a poll (they complete under its latency) and stored after it.  Up to GAIN_REGS
+// 16-byte pieces per thread ride along; any remainder is copied after the poll.
+constexpr int GAIN_REGS = 2;
+struct GainCopy {
+  u32x4 r[GAIN_REGS];
+};
+__device__ __forceinline__ void gains_issue(const MK_G uint16_t* src, int n, GainCopy& gc) {
+  const int pieces = n >> 3, pl = tid() - NCT;
+#pragma unroll
+  for (int k = 0; k < GAIN_REGS; ++k) {
+    const int i = pl + k * NPT;
+    gc.r[k] = i < pieces ? *(const MK_G u32x4*)(src + 8 * i) : u32x4{0u, 0u, 0u, 0u};
   }
-  return cnt;
+}
+__device__ __forceinline__ void gains_store(const MK_G uint16_t* src, int n, const GainCopy& gc, LS uint16_t* dst) {
+  const int pieces = n >> 3, pl = tid() - NCT;
+#pragma unroll
+  for (int k = 0; k < GAIN_REGS; ++k) {
+    const int i = pl + k * NPT;
+    if (i < pieces) *(LS u32x4*)(dst + 8 * i) = gc.r[k];
+  }
+  for (int i = pl + GAIN_REGS * NPT; i < pieces; i += NPT) *(LS u32x4*)(dst + 8 * i) = *(const MK_G u32x4*)(src + 8 * i);
 }
 
 __device__ __forceinline__ MkLayerDev layer_desc(const LS MkLayerDev* d, int l) {
@@ -735,10 +861,19 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
         const bool staged = sl < st_slots;
         const LS float* srow = st + sl * 256 + (li % rps) * dk;
         float sr[4];
+        if (staged) {
+          const int l0 = lane();
+          stage_f32x4(srow + l0, srow + (l0 + 64 < dk ? l0 + 64 : 0), srow + (l0 + 128 < dk ? l0 + 128 : 0),
+                      srow + (l0 + 192 < dk ? l0 + 192 : 0), sr);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int e = lane() + 64 * t;
-          sr[t] = e < dk ? (staged ? srow[e] : L.S[(size_t)row * dk + e]) : 0.f;
+          for (int t = 0; t < 4; ++t)
+            if (lane() + 64 * t >= dk) sr[t] = 0.f;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int e = lane() + 64 * t;
+            sr[t] = e < dk ? L.S[(size_t)row * dk + e] : 0.f;
+          }
         }
         float kd = 0.f;
 #pragma unroll
@@ -887,18 +1022,20 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
         const int start = jj % n4;  // staggered start: the 16 positions of a row read different banks
         float a = 0.f;
         for (int d0 = 0; d0 < n4; d0 += 8) {
-          float4 kk[8], qq[8];
+          f32x4 kk[8], qq[8];
+          const LS float* ka[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             int dd = d0 + k + start;
             dd = (dd >= n4 ? dd - n4 : dd) * 4;
-            kk[k] = float4{0.f, 0.f, 0.f, 0.f};
-            qq[k] = kk[k];
-            if (d0 + k < n4) {
-              kk[k] = *(const LS float4*)(kr + dd);
-              qq[k] = *(const LS float4*)(qr + dd);
-            }
+            ka[k] = kr + (d0 + k < n4 ? dd : 0);
+            qq[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (d0 + k < n4) qq[k] = *(const LS f32x4*)(qr + dd);
           }
+          stage_f4x8(ka, kk);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (d0 + k >= n4) kk[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             a = fmaf(kk[k].x, qq[k].x, a);
@@ -926,11 +1063,18 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
       for (int o = tid(); o < gs * hd; o += NCT) {
         const int i = o / hd, d = o - i * hd;
         float pv[ATT_C], vv[ATT_C];
+        const LS float* va[ATT_C];
 #pragma unroll
         for (int jj = 0; jj < ATT_C; ++jj) {
           pv[jj] = pb[i * ATT_C + jj];  // zero beyond nj
-          vv[jj] = 0.f;
-          if (jj < nj) vv[jj] = (j0 + jj == pos) ? vpos[d] : stf[(ks + jj / pps) * 256 + (jj % pps) * hd + d];
+          va[jj] = (jj < nj && j0 + jj != pos) ? stf + (ks + jj / pps) * 256 + (jj % pps) * hd + d : vpos + d;
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < ATT_C; q4 += 4) {
+          float t4[4];
+          stage_f32x4(va[q4], va[q4 + 1], va[q4 + 2], va[q4 + 3], t4);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vv[q4 + k] = q4 + k < nj ? t4[k] : 0.f;
         }
         float a = 0.f;
 #pragma unroll
@@ -1023,13 +1167,13 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
   s.gain = (LS uint16_t*)(lds + p.lds_gain);
   s.rope = lds + p.lds_rope;
   s.x = lds + p.lds_x;
-  s.xn = lds + p.lds_xn;
+  s.xn = (LS u32*)(lds + p.lds_xn);
   s.vec = lds + p.lds_vec;
   s.att = lds + p.lds_att;
   s.scr = lds + p.lds_scr;
   s.flag = (LS int*)(lds + p.lds_flag);
-  s.stA = (LS u32x4*)(lds + p.lds_stA);
-  s.stB = (LS u32x4*)(lds + p.lds_stB);
+  s.stA = (LS u32x4*)g_stage;
+  s.stB = (LS u32x4*)g_stage + MK_STAGE_A_SLOTS * SLOT;
   const int D = p.D;
 
   Ctx cx;
@@ -1113,9 +1257,11 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
       {
         const bool ok = gather_vec(cx, L.ll_o, K, s.vec);
         if (wg_bar_or(s, !ok)) return;
+        to_hl(s.vec, K);
+        wg_bar();
       }
       tr.mark();
-      gemv<false, false, false>(gout, s.vec, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS, s.att, tr,
+      gemv<false, false, false>(gout, (const LS u32*)s.vec, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS, s.att, tr,
                                 [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     } else {
       K = p.nq * p.hd;
@@ -1136,22 +1282,18 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
       {
         const bool ok = gather_vec(cx, L.ll_o, K, s.vec);
         if (wg_bar_or(s, !ok)) return;
+        to_hl(s.vec, K);
+        wg_bar();
       }
       tr.mark();
-      gemv<false, false, false>(gout, s.vec, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS, s.att, tr,
+      gemv<false, false, false>(gout, (const LS u32*)s.vec, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS, s.att, tr,
                                 [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     }
     tr.mark();
     // down-projection units and the next layer's (or the final) gains -> stage B
     Gemv gdn;
     gdn.init(L.w_down + (size_t)d0 * p.ffn, d1 - d0, p.ffn);
-    int cntB = gemv_stage(gdn, s.stB, MK_STAGE_B_SLOTS / USLOTS);
-    LS uint16_t* gnext = s.gain + (size_t)((l + 1) & 1) * 2 * D;
-    if (l + 1 < p.n_layers) {
-      cntB += gain_stage(layer_desc(s.desc, l + 1).g12, 2 * D, gnext);
-    } else {
-      cntB += gain_stage(p.g_final, D, gnext);
-    }
+    const int cntB = gemv_stage(gdn, s.stB, MK_STAGE_B_SLOTS / USLOTS);
     {
       const bool ok = gather_vec(cx, L.ll_x1, D, s.x);
       if (streamer()) wait_vm_n(cntB);  // gate/up units (stage A)
@@ -1164,22 +1306,30 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
     });
     tr.mark();
     // next layer's input rows (or the LM head's) -> stage A
+    const MK_G uint16_t* Ln_g12 = nullptr;
     if (l + 1 < p.n_layers) {
       const MkLayerDev Ln = layer_desc(s.desc, l + 1);
       pair_range(Ln.rows_in, NW, w, P0, P1);
       gin.init(Ln.w_in + (size_t)2 * P0 * D, min(2 * P1, Ln.rows_in) - 2 * P0, D);
+      Ln_g12 = Ln.g12;
     } else {
       pair_range(p.vocab, NW, w, P0, P1);
       gin.init(p.embed + (size_t)2 * P0 * D, min(2 * P1, p.vocab) - 2 * P0, D);
     }
     cntA = gemv_stage(gin, s.stA, A_UNITS);
     {
-      const bool ok = gather_vec(cx, L.ll_h, p.ffn, s.vec);
-      if (streamer()) wait_vm_n(cntA);  // down units and gains (stage B)
+      // the next layer's gains (or the final norm's) ride along with the FFN hidden poll
+      const MK_G uint16_t* gsrc = l + 1 < p.n_layers ? Ln_g12 : p.g_final;
+      const int gn = (l + 1 < p.n_layers ? 2 : 1) * D;
+      GainCopy gc;
+      if (!streamer()) gains_issue(gsrc, gn, gc);
+      const bool ok = gather_hl(cx, L.ll_h, p.ffn, (LS u32*)s.vec);
+      if (!streamer()) gains_store(gsrc, gn, gc, s.gain + (size_t)((l + 1) & 1) * 2 * D);
+      if (streamer()) wait_vm_n(cntA);  // down units (stage B)
       if (wg_bar_or(s, !ok)) return;
     }
     tr.mark();
-    gemv<false, false, false>(gdn, s.vec, s.stB, MK_STAGE_B_SLOTS / USLOTS, s.att, tr,
+    gemv<false, false, false>(gdn, (const LS u32*)s.vec, s.stB, MK_STAGE_B_SLOTS / USLOTS, s.att, tr,
                               [&](int r, float v, float) { ll_put(L.ll_x2 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     tr.mark();
     {

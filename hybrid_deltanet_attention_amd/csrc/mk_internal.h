@@ -89,7 +89,7 @@ struct MkDecodeParams {
   MK_G unsigned long long* trace;
   // LDS carve (float offsets) and size
   int32_t lds_desc, lds_gain, lds_rope, lds_x, lds_xn, lds_vec, lds_att, lds_scr, lds_flag, lds_trace;
-  int32_t lds_stA, lds_stB, lds_floats;
+  int32_t lds_floats;
 };
 
 #ifdef __cplusplus
