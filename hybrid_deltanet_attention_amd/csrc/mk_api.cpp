@@ -96,7 +96,7 @@ struct Layout {
   int max_items;
   // prefill scratch: a chunk of up to pf_T tokens
   int pf_T, pf_lda, pf_ldy;
-  size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part;
+  size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part, pf_ch;
 };
 
 constexpr int PF_LM_WG = 512;  // workgroups of the prefill LM head
@@ -173,6 +173,8 @@ Layout make_layout(const mk_config& c) {
     L.pf_ab = take((size_t)T * H * 2 * 4);
     L.pf_q = take((size_t)T * c.n_q_heads * c.head_dim * 4);
     L.pf_part = take((size_t)PF_LM_WG * 2 * 4);
+    // chunked DeltaNet: per (64-token chunk, head) W and Bt [64][64], two decay vectors and gamma_C
+    L.pf_ch = take((size_t)((T + 63) / 64) * H * (2 * 64 * 64 + 2 * 64 + 4) * 4);
   }
   L.total = o;
   return L;
@@ -676,7 +678,8 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
         rc |= mk_pf_attention(Q, Kc, Vc, T, p0, nq, nkv, hd, c.max_ctx, Ahi, Alo, lda, st);
       } else {
         rc |= mk_pf_dn_prep(Y, ldy, T, H, dk, dv, c.l2_eps, QK, AB, st);
-        rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, Ahi, Alo, lda, st);
+        rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, Ahi, Alo, lda,
+                            (float*)(ws + L.pf_ch), st);
       }
       rc |= mk_pf_gemm(1, Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, nullptr, nullptr, 0, st);
       rc |= mk_pf_rms_split(X, T, D, g12 + D, c.rms_eps, Ahi, Alo, lda, st);

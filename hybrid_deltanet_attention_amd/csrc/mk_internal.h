@@ -110,7 +110,7 @@ int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M
                float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, void* stream);
 int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB, void* stream);
 int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk, int dv,
-                  uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream);
+                  uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream);
 int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, int max_ctx, const float* rcos,
                    const float* rsin, float* Q, float* Kc, float* Vc, void* stream);
 int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,

@@ -10,8 +10,8 @@
 //   * v_mfma_f32_32x32x16_bf16: a 256-thread workgroup computes a 128 x 128 output tile, each wave a
 //     64 x 64 block of 2 x 2 MFMA tiles, operands loaded straight from global memory (the tiles that
 //     share weight rows are placed on the same XCD so they share its L2);
-//   * the DeltaNet recurrence runs row-parallel (every row of every head's state evolves on its own:
-//     16 lanes per row, the state in registers), sequential over the chunk's tokens;
+//   * the DeltaNet recurrence runs in its chunked form (64-token chunks): the parts that do not
+//     depend on the state, for all chunks at once, then one state-carrying pass over the chunks;
 //   * causal attention is an online-softmax loop over the KV cache (previous context included).
 //
 // The DeltaNet state and the KV cache are left exactly as token-by-token decode would leave them.
@@ -23,6 +23,7 @@ typedef unsigned int u32;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -250,7 +251,7 @@ __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------------ DeltaNet
-// per (token, head): q, k L2-normalised -> QK[t][h][0..dk) = q, [dk..2dk) = k; AB[t][h] = (alpha, beta)
+// per (token, head): q, k L2-normalised -> QK[t][h][0..dk) = q, [dk..2dk) = k; AB[t][h] = (log alpha, beta)
 __global__ void __launch_bounds__(64) pf_dn_prep_kernel(const float* __restrict__ Y, int ldy, int H, int dk, int dv,
                                                         float l2eps, float* __restrict__ QK, float* __restrict__ AB) {
   const int t = blockIdx.x / H, h = blockIdx.x % H;
@@ -272,7 +273,7 @@ __global__ void __launch_bounds__(64) pf_dn_prep_kernel(const float* __restrict_
   }
   if (threadIdx.x == 0) {
     const int off_a = 2 * H * dk + H * dv;
-    AB[((size_t)t * H + h) * 2] = expf(-softplusf_(y[off_a + h]));
+    AB[((size_t)t * H + h) * 2] = -softplusf_(y[off_a + h]);  // log alpha
     AB[((size_t)t * H + h) * 2 + 1] = sigmoidf_(y[off_a + H + h]);
   }
 }
@@ -370,7 +371,7 @@ __global__ void __launch_bounds__(256) pf_dn_scan_kernel(float* __restrict__ S, 
           ko[j] = kp[j];
         }
       }
-      ao = sab[buf][tt][0];
+      ao = expf(sab[buf][tt][0]);
       bo = sab[buf][tt][1];
       vo = sv[buf][tt][rl];
     };
@@ -410,6 +411,314 @@ __global__ void __launch_bounds__(256) pf_dn_scan_kernel(float* __restrict__ S, 
       const int e = NE * c + j;
       if (e < dk) srow[e] = s[j];
     }
+  }
+}
+
+// ---- chunked (UT) form of the gated delta rule
+// Gated DeltaNet (Yang, Kautz, Hatamizadeh, ICLR 2025), chunkwise algorithm; derived here from the
+// recurrence S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T in row form (S is dv x dk).
+// Within a chunk of C tokens with state S0 on entry, gamma_t = prod_{i<=t} alpha_i and
+// G_tj = gamma_t / gamma_j (exp of a difference of cumulative log alphas, never above 1 for j <= t):
+//   (I + M) U = diag(beta) (V - diag(gamma) K S0^T),   M = strict lower part of diag(beta) (K K^T o G)
+//   O   = diag(gamma) Q S0^T + (lower part incl. diagonal of Q K^T o G) U
+//   S_C = gamma_C S0 + U^T diag(gamma_C / gamma) K
+// (rows of K, Q, V, U, O are tokens).  Everything that does not involve S0 -- K K^T, Q K^T, the
+// decays and W = (I + M)^{-1} diag(beta) -- is computed for all chunks in parallel
+// (pf_dn_cprep_kernel); the pass that carries the state runs chunk after chunk, each workgroup on
+// 8 rows of one head's state (pf_dn_cscan_kernel).
+constexpr int PC = 64;                          // tokens per chunk
+constexpr int PC_BLK = 2 * PC * PC + 2 * PC + 4;  // per (chunk, head): W, Bt [PC][PC], gam, dlt [PC], gamma_C
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float acc) {
+  acc = fmaf(a.x, b.x, acc);
+  acc = fmaf(a.y, b.y, acc);
+  acc = fmaf(a.z, b.z, acc);
+  return fmaf(a.w, b.w, acc);
+}
+
+// Per (chunk c, head h): W = (I + M)^{-1} diag(beta) and Bt = lower(Q K^T o G) incl. the diagonal
+// (both [t][j]), gam_t = gamma_t, dlt_t = gamma_last / gamma_t, gamma_last.  Tokens past the end of
+// the prompt have k = q = 0 and beta = 0, so their rows and columns come out zero.
+template <int DKM>
+__global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restrict__ QK, const float* __restrict__ AB,
+                                                          int T, int H, int dk, float* __restrict__ CH) {
+  __shared__ __attribute__((aligned(16))) float sk[PC][DKM + 4];
+  __shared__ __attribute__((aligned(16))) float sq[PC][DKM + 4];
+  __shared__ float sm[PC][PC + 1];
+  __shared__ float sg[PC], sbeta[PC];
+  const int h = blockIdx.x % H, c = blockIdx.x / H;
+  const int t0 = c * PC, Cn = min(PC, T - t0);
+  const int tid = threadIdx.x;
+  const int n4 = dk >> 2;
+  if (dk < DKM) {  // key columns past dk take part in the products as zeros
+    for (int f = tid; f < PC * (DKM + 4); f += 256) {
+      (&sk[0][0])[f] = 0.f;
+      (&sq[0][0])[f] = 0.f;
+    }
+    __syncthreads();
+  }
+  {
+    // every load of the chunk is issued before the first is used
+    constexpr int NL = PC * DKM / 4 / 256;
+    f32x4 rq[NL], rk[NL];
+#pragma unroll
+    for (int x = 0; x < NL; ++x) {
+      const int f = tid + 256 * x, t = f / n4, e = (f - t * n4) * 4;
+      rq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rk[x] = rq[x];
+      if (t < Cn) {
+        const float* src = QK + ((size_t)(t0 + t) * H + h) * 2 * dk;
+        rq[x] = *(const f32x4*)(src + e);
+        rk[x] = *(const f32x4*)(src + dk + e);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < NL; ++x) {
+      const int f = tid + 256 * x, t = f / n4, e = (f - t * n4) * 4;
+      if (t < PC) {
+        *(f32x4*)&sq[t][e] = rq[x];
+        *(f32x4*)&sk[t][e] = rk[x];
+      }
+    }
+  }
+  if (tid < PC) {
+    const bool in = tid < Cn;
+    const float* ab = AB + ((size_t)(t0 + (in ? tid : 0)) * H + h) * 2;
+    sg[tid] = in ? ab[0] : 0.f;
+    sbeta[tid] = in ? ab[1] : 0.f;
+  }
+  __syncthreads();
+  if (tid == 0) {  // cumulative log alpha, inclusive
+    float a = 0.f;
+    for (int t = 0; t < PC; ++t) {
+      a += sg[t];
+      sg[t] = a;
+    }
+  }
+  // 4 x 4 blocks of K K^T and Q K^T on and below the diagonal
+  const int tb = tid >> 4, jb = tid & 15;
+  float a[4][4], b[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[r][q] = b[r][q] = 0.f;
+  if (jb <= tb) {
+    // columns past dk are zero in LDS, so the loop runs over the compile-time width
+#pragma unroll 2
+    for (int e = 0; e < DKM; e += 4) {
+      f32x4 kt[4], qt[4], kj[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kt[r] = *(const f32x4*)&sk[4 * tb + r][e];
+        qt[r] = *(const f32x4*)&sq[4 * tb + r][e];
+        kj[r] = *(const f32x4*)&sk[4 * jb + r][e];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a[r][q] = dot4(kt[r], kj[q], a[r][q]);
+          b[r][q] = dot4(qt[r], kj[q], b[r][q]);
+        }
+    }
+  }
+  __syncthreads();  // cumulative log alphas are in place
+  float* blk = CH + ((size_t)c * H + h) * PC_BLK;
+  float* gW = blk;
+  float* gBt = blk + PC * PC;
+  float* gGam = blk + 2 * PC * PC;
+  float* gDlt = gGam + PC;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = 4 * tb + r, j = 4 * jb + q;
+      const float dec = j <= t ? expf(sg[t] - sg[j]) : 0.f;
+      sm[t][j] = j < t ? sbeta[t] * dec * a[r][q] : 0.f;
+      gBt[t * PC + j] = j <= t ? dec * b[r][q] : 0.f;
+    }
+  if (tid < PC) {
+    const float last = sg[Cn - 1];
+    gGam[tid] = expf(sg[tid]);
+    gDlt[tid] = expf(last - sg[tid]);
+    if (tid == 0) gDlt[PC] = expf(last);
+  }
+  __syncthreads();
+  // forward substitution, column j of W on 4 lanes (lane q holds rows q, q + 4, ...):
+  // W[j][j] = beta_j, W[t][j] = -sum_{j <= m < t} M[t][m] W[m][j] for t > j
+  const int j = tid >> 2, q = tid & 3;
+  float w[PC / 4];
+#pragma unroll
+  for (int k = 0; k < PC / 4; ++k) w[k] = (q + 4 * k == j) ? sbeta[j] : 0.f;
+#pragma unroll 1
+  for (int t = 1; t < PC; ++t) {
+    // M[t][m] = 0 for m >= t and W[m][j] = 0 for rows not yet reached, so no masking is needed
+    float mv[PC / 4];
+#pragma unroll
+    for (int k = 0; k < PC / 4; ++k) mv[k] = sm[t][q + 4 * k];
+    float part = 0.f;
+#pragma unroll
+    for (int k = 0; k < PC / 4; ++k) part = fmaf(mv[k], w[k], part);
+    part = dpp_add<0xB1>(part);  // quad_perm [1,0,3,2]
+    part = dpp_add<0x4E>(part);  // quad_perm [2,3,0,1]
+    if (t > j && (t & 3) == q) {
+#pragma unroll
+      for (int k = 0; k < PC / 4; ++k)
+        if (k == (t >> 2)) w[k] = -part;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PC / 4; ++k) gW[(q + 4 * k) * PC + j] = w[k];
+}
+
+// The state-carrying pass: workgroup = (head, 8 state rows), 512 threads (two waves per SIMD, so
+// LDS latency of one hides behind the other); chunk after chunk
+//   Z = K S0^T, P = Q S0^T (this workgroup's rows), R = V - diag(gam) Z, U = W R,
+//   O = diag(gam) P + Bt U -> outputs (hi/lo BF16), S <- gamma_C S + (diag(dlt) U)^T K.
+constexpr int CS_NT = 512;
+template <int DKM>
+__global__ void __launch_bounds__(CS_NT) pf_dn_cscan_kernel(float* __restrict__ S, const float* __restrict__ QK,
+                                                            const float* __restrict__ CH, const float* __restrict__ Y,
+                                                            int ldy, int T, int H, int dk, int dv,
+                                                            uint16_t* __restrict__ Ohi, uint16_t* __restrict__ Olo,
+                                                            int ldo) {
+  constexpr int RW = 8;
+  __shared__ __attribute__((aligned(16))) float sk[PC][DKM + 4];
+  __shared__ __attribute__((aligned(16))) float sq[PC][DKM + 4];
+  __shared__ __attribute__((aligned(16))) float sw[PC][PC + 4];
+  __shared__ __attribute__((aligned(16))) float sbt[PC][PC + 4];
+  __shared__ __attribute__((aligned(16))) float ss[RW][DKM + 4];
+  __shared__ float sv[PC][RW];
+  __shared__ __attribute__((aligned(16))) float sr[RW][PC + 4];  // row-major per state row
+  __shared__ __attribute__((aligned(16))) float su[RW][PC + 4];
+  __shared__ __attribute__((aligned(16))) float sgam[PC];
+  __shared__ __attribute__((aligned(16))) float sdlt[PC + 4];
+  const int rbs = (dv + RW - 1) / RW;
+  const int h = blockIdx.x / rbs, r0 = (blockIdx.x - h * rbs) * RW;
+  const int tid = threadIdx.x;
+  const int n4 = dk >> 2;
+  if (dk < DKM) {  // key columns past dk take part in the products as zeros
+    for (int f = tid; f < PC * (DKM + 4); f += CS_NT) {
+      (&sk[0][0])[f] = 0.f;
+      (&sq[0][0])[f] = 0.f;
+    }
+    for (int f = tid; f < RW * (DKM + 4); f += CS_NT) (&ss[0][0])[f] = 0.f;
+    __syncthreads();
+  }
+  for (int f = tid; f < RW * n4; f += CS_NT) {
+    const int i = f / n4, e = (f - i * n4) * 4;
+    *(f32x4*)&ss[i][e] = r0 + i < dv ? *(const f32x4*)(S + ((size_t)h * dv + r0 + i) * dk + e)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int off_v = 2 * H * dk + h * dv + r0;
+  const int nc = (T + PC - 1) / PC;
+  // thread roles: (token t, state row i) for the per-token products, (row ui, 2 key columns) for
+  // the state update
+  const int t = tid >> 3, i = tid & 7;
+  const int ui = tid >> 6, ue = 2 * (tid & 63);
+  // A chunk's operands are loaded into registers while the previous chunk computes.
+  constexpr int NL = PC * DKM / 4 / CS_NT, NM = PC * PC / 4 / CS_NT;
+  f32x4 rq[NL], rk[NL], rw[NM], rb[NM];
+  float rg = 0.f, rv = 0.f;
+  auto fetch = [&](int c) {
+    const int t0 = c * PC, Cn = min(PC, T - t0);
+    const float* blk = CH + ((size_t)c * H + h) * PC_BLK;
+#pragma unroll
+    for (int x = 0; x < NL; ++x) {
+      const int f = tid + CS_NT * x, tt = f / n4, e = (f - tt * n4) * 4;
+      rq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rk[x] = rq[x];
+      if (tt < Cn) {
+        const float* src = QK + ((size_t)(t0 + tt) * H + h) * 2 * dk;
+        rq[x] = *(const f32x4*)(src + e);
+        rk[x] = *(const f32x4*)(src + dk + e);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < NM; ++x) {
+      const int f = tid + CS_NT * x;
+      rw[x] = *(const f32x4*)(blk + 4 * f);
+      rb[x] = *(const f32x4*)(blk + PC * PC + 4 * f);
+    }
+    rg = tid <= 2 * PC ? blk[2 * PC * PC + tid] : 0.f;  // gam [0, PC), dlt [PC, 2 PC], gamma_C last
+    rv = (t < Cn && r0 + i < dv) ? Y[(size_t)(t0 + t) * ldy + off_v + i] : 0.f;
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int x = 0; x < NL; ++x) {
+      const int f = tid + CS_NT * x, tt = f / n4, e = (f - tt * n4) * 4;
+      if (tt < PC) {
+        *(f32x4*)&sq[tt][e] = rq[x];
+        *(f32x4*)&sk[tt][e] = rk[x];
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < NM; ++x) {
+      const int f = tid + CS_NT * x, tt = f / (PC / 4), jj = (f - tt * (PC / 4)) * 4;
+      *(f32x4*)&sw[tt][jj] = rw[x];
+      *(f32x4*)&sbt[tt][jj] = rb[x];
+    }
+    if (tid < PC) sgam[tid] = rg;
+    else if (tid <= 2 * PC) sdlt[tid - PC] = rg;
+    sv[t][i] = rv;
+  };
+  fetch(0);
+  for (int c = 0; c < nc; ++c) {
+    const int t0 = c * PC, Cn = min(PC, T - t0);
+    stash();
+    __syncthreads();
+    if (c + 1 < nc) fetch(c + 1);
+    // Z and P for token t, row i
+    float z = 0.f, p = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < DKM; e += 4) {  // columns past dk are zero in LDS
+      const f32x4 s0 = *(const f32x4*)&ss[i][e];
+      z = dot4(*(const f32x4*)&sk[t][e], s0, z);
+      p = dot4(*(const f32x4*)&sq[t][e], s0, p);
+    }
+    sr[i][t] = sv[t][i] - sgam[t] * z;
+    __syncthreads();
+    // U = W R.  W is lower triangular: every lane runs the full row (zeros above the diagonal), so
+    // the trip count is the same for all lanes.
+    {
+      float u = 0.f;
+#pragma unroll 4
+      for (int jj = 0; jj < PC; jj += 4) u = dot4(*(const f32x4*)&sw[t][jj], *(const f32x4*)&sr[i][jj], u);
+      su[i][t] = u;
+    }
+    __syncthreads();
+    // outputs
+    {
+      float y = sgam[t] * p;
+#pragma unroll 4
+      for (int jj = 0; jj < PC; jj += 4) y = dot4(*(const f32x4*)&sbt[t][jj], *(const f32x4*)&su[i][jj], y);
+      if (t < Cn && r0 + i < dv) split_store(y, Ohi, Olo, (size_t)(t0 + t) * ldo + h * dv + r0 + i);
+    }
+    // state update: row ui, key columns ue, ue + 1 (tokens past the prompt have u = 0)
+    if (ue < dk) {
+      float a0 = ss[ui][ue], a1 = ss[ui][ue + 1];
+      const float gc = sdlt[PC];
+      a0 *= gc;
+      a1 *= gc;
+#pragma unroll 4
+      for (int tt = 0; tt < PC; tt += 4) {
+        const f32x4 uu = *(const f32x4*)&su[ui][tt], dd = *(const f32x4*)&sdlt[tt];
+        const float cf[4] = {uu.x * dd.x, uu.y * dd.y, uu.z * dd.z, uu.w * dd.w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float2 k = *(const float2*)&sk[tt + x][ue];
+          a0 = fmaf(cf[x], k.x, a0);
+          a1 = fmaf(cf[x], k.y, a1);
+        }
+      }
+      ss[ui][ue] = a0;
+      ss[ui][ue + 1] = a1;
+    }
+    __syncthreads();  // ss, sk and the chunk matrices are rewritten by the next chunk
+  }
+  for (int f = tid; f < RW * n4; f += CS_NT) {
+    const int ri = f / n4, e = (f - ri * n4) * 4;
+    if (r0 + ri < dv) *(f32x4*)(S + ((size_t)h * dv + r0 + ri) * dk + e) = *(const f32x4*)&ss[ri][e];
   }
 }
 
@@ -735,17 +1044,24 @@ extern "C" int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int 
 }
 
 extern "C" int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk,
-                             int dv, uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream) {
-  const dim3 grid(H * ((dv + 7) / 8));
+                             int dv, uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (dk <= 32)
-    hipLaunchKernelGGL(pf_dn_scan_kernel<1>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
-  else if (dk <= 64)
-    hipLaunchKernelGGL(pf_dn_scan_kernel<2>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
-  else if (dk <= 128)
-    hipLaunchKernelGGL(pf_dn_scan_kernel<4>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
-  else
-    hipLaunchKernelGGL(pf_dn_scan_kernel<8>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+  if (dk <= 128) {
+    // chunked form: all chunks' W, Bt and decays in parallel, then the state pass
+    const int nc = (T + PC - 1) / PC;
+    const dim3 g1(nc * H), g2(H * ((dv + 7) / 8));
+    if (dk <= 64) {
+      hipLaunchKernelGGL(pf_dn_cprep_kernel<64>, g1, dim3(256), 0, s, QK, AB, T, H, dk, CH);
+      hipLaunchKernelGGL(pf_dn_cscan_kernel<64>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+    } else {
+      hipLaunchKernelGGL(pf_dn_cprep_kernel<128>, g1, dim3(256), 0, s, QK, AB, T, H, dk, CH);
+      hipLaunchKernelGGL(pf_dn_cscan_kernel<128>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+    }
+    return MK_LAUNCH_OK();
+  }
+  // wider keys: the token-by-token row-parallel recurrence
+  const dim3 grid(H * ((dv + 7) / 8));
+  hipLaunchKernelGGL(pf_dn_scan_kernel<8>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
   return MK_LAUNCH_OK();
 }
 
