@@ -253,7 +253,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} batch-1 decode after a {PROMPT}-token prompt, one launch per token",
                    "layers": cfg.n_layers, "deltanet_layers": cfg.n_deltanet_layers,

@@ -96,7 +96,7 @@ struct Layout {
   int max_items;
   // prefill scratch: a chunk of up to pf_T tokens
   int pf_T, pf_lda, pf_ldy;
-  size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part, pf_ch;
+  size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part, pf_ch, pf_sk;
 };
 
 constexpr int PF_LM_WG = 512;  // workgroups of the prefill LM head
@@ -175,6 +175,8 @@ Layout make_layout(const mk_config& c) {
     L.pf_part = take((size_t)PF_LM_WG * 2 * 4);
     // chunked DeltaNet: per (64-token chunk, head) W and Bt [64][64], two decay vectors and gamma_C
     L.pf_ch = take((size_t)((T + 63) / 64) * H * (2 * 64 * 64 + 2 * 64 + 4) * 4);
+    // split-K partials of the residual GEMMs: at most 256 work items of 128 x 128 outputs
+    L.pf_sk = take(PF_SPLITK_FLOATS * 4);
   }
   L.total = o;
   return L;
@@ -654,6 +656,8 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   float* AB = (float*)(ws + L.pf_ab);
   float* Q = (float*)(ws + L.pf_q);
   const int lda = L.pf_lda, ldy = L.pf_ldy;
+  float* PK = (float*)(ws + L.pf_sk);
+  const size_t PKN = PF_SPLITK_FLOATS;
   MkCtl* ctl = (MkCtl*)(ws + L.ctl);
   const float* rcos = (const float*)(ws + L.rope_cos);
   const float* rsin = (const float*)(ws + L.rope_sin);
@@ -670,7 +674,7 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
       const uint16_t* w_in = (const uint16_t*)(ws + lo.w_in);
       const uint16_t* w_out = (const uint16_t*)(ws + lo.w_out);
       rc |= mk_pf_rms_split(X, T, D, g12, c.rms_eps, Ahi, Alo, lda, st);
-      rc |= mk_pf_gemm(0, Ahi, Alo, lda, T, D, w_in, (int)lo.rows_in, Y, ldy, nullptr, nullptr, 0, st);
+      rc |= mk_pf_gemm(0, Ahi, Alo, lda, T, D, w_in, (int)lo.rows_in, Y, ldy, nullptr, nullptr, 0, PK, PKN, st);
       if (is_attention(c, l)) {
         float* Kc = (float*)(ws + lo.Kc);
         float* Vc = (float*)(ws + lo.Vc);
@@ -681,10 +685,12 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
         rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, Ahi, Alo, lda,
                             (float*)(ws + L.pf_ch), st);
       }
-      rc |= mk_pf_gemm(1, Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, nullptr, nullptr, 0, st);
+      rc |= mk_pf_gemm(1, Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, nullptr, nullptr, 0, PK, PKN, st);
       rc |= mk_pf_rms_split(X, T, D, g12 + D, c.rms_eps, Ahi, Alo, lda, st);
-      rc |= mk_pf_gemm(2, Ahi, Alo, lda, T, D, (const uint16_t*)(ws + lo.w_gu), 2 * F, nullptr, 0, Hhi, Hlo, F, st);
-      rc |= mk_pf_gemm(1, Hhi, Hlo, F, T, F, (const uint16_t*)(ws + lo.w_down), D, X, D, nullptr, nullptr, 0, st);
+      rc |= mk_pf_gemm(2, Ahi, Alo, lda, T, D, (const uint16_t*)(ws + lo.w_gu), 2 * F, nullptr, 0, Hhi, Hlo, F, PK, PKN,
+                       st);
+      rc |= mk_pf_gemm(1, Hhi, Hlo, F, T, F, (const uint16_t*)(ws + lo.w_down), D, X, D, nullptr, nullptr, 0, PK, PKN,
+                       st);
     }
     p0 += T;
   }

@@ -34,6 +34,8 @@ typedef unsigned long long mk_u64;
 #define MK_STAGE_B_SLOTS 32
 // GEMV unit partials held in LDS per row chunk.
 #define MK_RED_CAP 4096
+// Prefill split-K partial buffer (floats): 256 work items of 128 x 128 outputs.
+#define PF_SPLITK_FLOATS ((size_t)256 * 128 * 128)
 // Largest grid the exchange buffers are sized for.
 #define MK_MAX_GRID 1024
 
@@ -107,7 +109,7 @@ int mk_pf_embed(const int32_t* tok, int T, const uint16_t* embed, int D, int voc
 int mk_pf_rms_split(const float* X, int T, int D, const uint16_t* g, float eps, uint16_t* Ahi, uint16_t* Alo, int lda,
                     void* stream);
 int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W, int N,
-               float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, void* stream);
+               float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, float* P, size_t p_floats, void* stream);
 int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB, void* stream);
 int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk, int dv,
                   uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream);

@@ -18,6 +18,7 @@
 
 #include <hip/hip_runtime.h>
 #include "mk_internal.h"
+#include <algorithm>
 
 typedef unsigned int u32;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -98,14 +99,18 @@ __global__ void __launch_bounds__(256) pf_rms_split_kernel(const float* __restri
 // ------------------------------------------------------------------------ MFMA GEMM
 // C[M x N] (+)= (Ahi + Alo)[M x K] . W[N x K]^T.  K is a multiple of 8.
 // EPI 0: C = v;  EPI 1: C += v (residual);  EPI 2: columns (2c, 2c + 1) are (gate c, up c):
-// H[:, c] = silu(gate) * up, stored split into BF16 hi/lo.
+// H[:, c] = silu(gate) * up, stored split into BF16 hi/lo;  EPI 3: split-K partial, stored to
+// P[split][M][N] (K split into ksplit ranges of whole chunks; pf_splitk_add_kernel adds the partials
+// to C in split order, so the result does not depend on timing).
 //
 // A workgroup (4 waves, 2 x 2) computes a BM x BN tile; each wave a (BM/2) x (BN/2) block of 32 x 32
 // MFMA tiles.  K advances in chunks of 32 through a ring of STAGES LDS buffers filled with LDS-DMA
 // (a wave copy is 16 rows x 64 bytes); a wave waits only for its own copies of the chunk it is about
 // to use, and the barriers order LDS only, so later chunks stay in flight.
 constexpr int BK = 32;
-constexpr int STAGES = 4;
+// LDS ring depth: six 24 KB stages for 128 x 128 tiles (one workgroup per CU), four for 64 x 64
+template <int BM>
+constexpr int gemm_stages() { return BM >= 128 ? 6 : 4; }
 
 __device__ __forceinline__ void lds_bar() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -136,30 +141,33 @@ template <int BM, int BN, int EPI>
 __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict__ Ahi, const uint16_t* __restrict__ Alo,
                                                       int lda, int M, int K, const uint16_t* __restrict__ W, int N,
                                                       float* __restrict__ C, int ldc, uint16_t* __restrict__ Hhi,
-                                                      uint16_t* __restrict__ Hlo, int ldh) {
+                                                      uint16_t* __restrict__ Hlo, int ldh, int ksplit) {
   constexpr int TI = BM / 64, TJ = BN / 64;            // 32 x 32 tiles per wave in each direction
   constexpr int AC = BM / 16, BC = BN / 16;            // 1 KB copies per tile per chunk
   constexpr int CPW = (2 * AC + BC) / 4;               // copies per wave per chunk
   constexpr int SB = (2 * BM + BN) * BK * 2;           // bytes per stage
+  constexpr int STAGES = gemm_stages<BM>();
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int mb = (M + BM - 1) / BM, nb = (N + BN - 1) / BN;
-  const int tiles = mb * nb, per = (tiles + 7) / 8;
+  const int items = mb * nb * ksplit, per = (items + 7) / 8;
   const int w = blockIdx.x;
-  // tiles of one column block (same weight rows) go to one XCD (workgroup w runs on XCD w % 8)
-  const int tile = (w % 8) * per + w / 8;
-  if (tile >= tiles) return;
+  // work items of one column block (same weight rows) go to one XCD (workgroup w runs on XCD w % 8)
+  const int item = (w % 8) * per + w / 8;
+  if (item >= items) return;
+  const int tile = item / ksplit, split = item - tile * ksplit;
   const int m0 = (tile % mb) * BM, n0 = (tile / mb) * BN;
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int wr = wv >> 1, wc = wv & 1;
-  const int nchunk = (K + BK - 1) / BK;
+  const int nk = (K + BK - 1) / BK, kper = (nk + ksplit - 1) / ksplit;
+  const int cbeg = split * kper, nchunk = max(0, min(nk, cbeg + kper) - cbeg);
   // Copy q (0 .. 2AC + BC) of a chunk: tile part (A hi, A lo, B) and 16-row group; wave wv issues
   // copies wv * CPW .. + CPW.  Rows past M / N read the last row instead (their results are never
   // stored), so every copy has live lanes and each wave issues exactly CPW copies per chunk -- the
   // waits below count on that.  Columns past K are left out; a chunk that has them was zeroed by the
   // same wave first (its own 1 KB blocks only, so no other wave's copy can be overwritten).
-  auto issue = [&](int chunk) {
+  auto issue = [&](int chunk) {  // chunk: index within this work item's K range
     char* st = smem + (size_t)(chunk % STAGES) * SB;
-    const int k0 = chunk * BK;
+    const int k0 = (cbeg + chunk) * BK;
     const bool part_k = k0 + BK > K;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -190,7 +198,9 @@ __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict
   for (int c = 0; c < nchunk; ++c) {
     // this wave's copies of chunk c are done once at most (later chunks issued) copies remain
     const int later = min(STAGES - 2, nchunk - 1 - c);
-    if (later >= 2) wait_vm<2 * CPW>();
+    if (later >= 4) wait_vm<4 * CPW>();
+    else if (later == 3) wait_vm<3 * CPW>();
+    else if (later == 2) wait_vm<2 * CPW>();
     else if (later == 1) wait_vm<CPW>();
     else wait_vm<0>();
     lds_bar();
@@ -242,12 +252,31 @@ __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict
             const float h = v / (1.0f + expf(-v)) * u;
             split_store(h, Hhi, Hlo, (size_t)row * ldh + (col >> 1));
           }
+        } else if (EPI == 3) {
+          if (row < M && col < N) C[((size_t)split * M + row) * N + col] = v;
         } else if (row < M && col < N) {
           float* cp = C + (size_t)row * ldc + col;
           if (EPI == 1) *cp += v;
           else *cp = v;
         }
       }
+}
+
+// C[r][c] += sum over splits s (in order) of P[s][r][c]
+__global__ void __launch_bounds__(256) pf_splitk_add_kernel(const float* __restrict__ P, int ksplit, int M, int N,
+                                                            float* __restrict__ C, int ldc) {
+  const int idx = (blockIdx.x * 256 + threadIdx.x) * 4;  // N is a multiple of 4
+  if (idx >= M * N) return;
+  const int r = idx / N, c = idx - r * N;
+  f32x4 acc = *(const f32x4*)(C + (size_t)r * ldc + c);
+  for (int sp = 0; sp < ksplit; ++sp) {
+    const f32x4 v = *(const f32x4*)(P + (size_t)sp * M * N + idx);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *(f32x4*)(C + (size_t)r * ldc + c) = acc;
 }
 
 // ------------------------------------------------------------------------ DeltaNet
@@ -1012,29 +1041,53 @@ extern "C" int mk_pf_rms_split(const float* X, int T, int D, const uint16_t* g, 
 
 template <int BM, int BN>
 static int launch_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W, int N,
-                       float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, hipStream_t s) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int grid = ((tiles + 7) / 8) * 8;
-  const size_t lds = (size_t)STAGES * (2 * BM + BN) * BK * 2;
+                       float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, int ksplit, hipStream_t s) {
+  const int items = ((M + BM - 1) / BM) * ((N + BN - 1) / BN) * ksplit;
+  const int grid = ((items + 7) / 8) * 8;
+  const size_t lds = (size_t)gemm_stages<BM>() * (2 * BM + BN) * BK * 2;
   if (epi == 0)
     hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 0>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
-                       Hhi, Hlo, ldh);
+                       Hhi, Hlo, ldh, ksplit);
   else if (epi == 1)
     hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 1>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
-                       Hhi, Hlo, ldh);
-  else
+                       Hhi, Hlo, ldh, ksplit);
+  else if (epi == 2)
     hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 2>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
-                       Hhi, Hlo, ldh);
+                       Hhi, Hlo, ldh, ksplit);
+  else
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 3>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+                       Hhi, Hlo, ldh, ksplit);
   return MK_LAUNCH_OK();
 }
 
 extern "C" int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W,
-                          int N, float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, void* stream) {
-  // large tiles when they alone fill the chip, otherwise 64 x 64 tiles for more workgroups
+                          int N, float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, float* P, size_t p_floats,
+                          void* stream) {
+  hipStream_t s = (hipStream_t)stream;
   const int big = ((M + 127) / 128) * ((N + 127) / 128);
-  if (big >= 200)
-    return launch_gemm<128, 128>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, (hipStream_t)stream);
-  return launch_gemm<64, 64>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, (hipStream_t)stream);
+  if (big >= 200) {
+    // whole rounds of 256 workgroups times the tile area: a ragged last row block (M = 520 is four
+    // 128-row blocks and 8 rows) can cost a second round of 128 x 128 tiles, where 64 x 128 tiles
+    // fill two rounds of half the work
+    const int half = ((M + 63) / 64) * ((N + 127) / 128);
+    if ((half + 255) / 256 * 64 < (big + 255) / 256 * 128)
+      return launch_gemm<64, 128>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, 1, s);
+    return launch_gemm<128, 128>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, 1, s);
+  }
+  // too few large tiles to fill the chip: a residual update splits K over workgroups (partials in P,
+  // added to C in split order); other epilogues use small tiles
+  if (epi == 1 && P && N % 4 == 0) {
+    const int nk = (K + BK - 1) / BK;
+    int ks = std::min(std::max(1, 256 / big), std::max(1, nk / 4));
+    while (ks > 1 && (size_t)ks * M * N > p_floats) --ks;
+    if (ks > 1) {
+      launch_gemm<128, 128>(3, Ahi, Alo, lda, M, K, W, N, P, N, Hhi, Hlo, ldh, ks, s);
+      const int n4 = (M * N + 3) / 4;
+      hipLaunchKernelGGL(pf_splitk_add_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, P, ks, M, N, C, ldc);
+      return MK_LAUNCH_OK();
+    }
+  }
+  return launch_gemm<64, 64>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, 1, s);
 }
 
 extern "C" int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB,
