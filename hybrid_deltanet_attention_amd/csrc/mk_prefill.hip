@@ -137,16 +137,31 @@ __device__ __forceinline__ void wait_vm_n(int n) {
   else wait_vm<0>();
 }
 
+// Waves per workgroup in rows x columns of the tile: eight waves (4 x 2 for 128-row tiles, 2 x 4
+// for 64 x 128) where each still gets whole 32 x 32 blocks and the tile's copies split evenly,
+// else 2 x 2.  More waves per CU hide the LDS-read and barrier latency of the others.
+template <int BM, int BN>
+constexpr bool gemm_eight() { return (BM >= 128 || BN >= 128) && ((2 * (BM / 16) + BN / 16) % 8) == 0; }
+template <int BM, int BN>
+constexpr int gemm_wr() { return gemm_eight<BM, BN>() ? (BM >= 128 ? 4 : 2) : 2; }
+template <int BM, int BN>
+constexpr int gemm_wc() { return gemm_eight<BM, BN>() ? (BM >= 128 ? 2 : 4) : 2; }
+template <int BM, int BN>
+constexpr int gemm_threads() { return 64 * gemm_wr<BM, BN>() * gemm_wc<BM, BN>(); }
+
 template <int BM, int BN, int EPI>
-__global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict__ Ahi, const uint16_t* __restrict__ Alo,
-                                                      int lda, int M, int K, const uint16_t* __restrict__ W, int N,
-                                                      float* __restrict__ C, int ldc, uint16_t* __restrict__ Hhi,
-                                                      uint16_t* __restrict__ Hlo, int ldh, int ksplit) {
-  constexpr int TI = BM / 64, TJ = BN / 64;            // 32 x 32 tiles per wave in each direction
-  constexpr int AC = BM / 16, BC = BN / 16;            // 1 KB copies per tile per chunk
-  constexpr int CPW = (2 * AC + BC) / 4;               // copies per wave per chunk
+__global__ void __launch_bounds__((gemm_threads<BM, BN>())) pf_gemm_kernel(
+    const uint16_t* __restrict__ Ahi, const uint16_t* __restrict__ Alo, int lda, int M, int K,
+    const uint16_t* __restrict__ W, int N, float* __restrict__ C, int ldc, uint16_t* __restrict__ Hhi,
+    uint16_t* __restrict__ Hlo, int ldh, int ksplit) {
+  constexpr int WR = gemm_wr<BM, BN>(), WC = gemm_wc<BM, BN>(), NWV = WR * WC;
+  constexpr int TI = BM / (32 * WR), TJ = BN / (32 * WC);  // 32 x 32 tiles per wave in each direction
+  constexpr int AC = BM / 16, BC = BN / 16;                // 1 KB copies per tile per chunk
+  constexpr int CPW = (2 * AC + BC) / NWV;                 // copies per wave per chunk
+  static_assert(TI >= 1 && TJ >= 1 && CPW * NWV == 2 * AC + BC, "tile does not split over the waves");
   constexpr int SB = (2 * BM + BN) * BK * 2;           // bytes per stage
   constexpr int STAGES = gemm_stages<BM>();
+  static_assert(BK == 32, "the LDS chunk swizzle assumes four 16-byte k-chunks per row");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int mb = (M + BM - 1) / BM, nb = (N + BN - 1) / BN;
   const int items = mb * nb * ksplit, per = (items + 7) / 8;
@@ -157,7 +172,7 @@ __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict
   const int tile = item / ksplit, split = item - tile * ksplit;
   const int m0 = (tile % mb) * BM, n0 = (tile / mb) * BN;
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int wr = wv >> 1, wc = wv & 1;
+  const int wr = wv / WC, wc = wv % WC;  // this wave's (BM / WR) x (BN / WC) block
   const int nk = (K + BK - 1) / BK, kper = (nk + ksplit - 1) / ksplit;
   const int cbeg = split * kper, nchunk = max(0, min(nk, cbeg + kper) - cbeg);
   // Copy q (0 .. 2AC + BC) of a chunk: tile part (A hi, A lo, B) and 16-row group; wave wv issues
@@ -175,7 +190,9 @@ __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict
       const int part = q < AC ? 0 : (q < 2 * AC ? 1 : 2);
       const int grp = part == 0 ? q : (part == 1 ? q - AC : q - 2 * AC);
       const int r = grp * 16 + (l >> 2);
-      const int k = k0 + (l & 3) * 8;
+      // lane l fills LDS position (row r, 16-byte slot l & 3) with the row's k-chunk
+      // (l & 3) ^ ((r >> 2) & 3): sixteen consecutive rows then spread one chunk over all banks
+      const int k = k0 + (((l & 3) ^ ((r >> 2) & 3)) * 8);
       const uint16_t* src;
       if (part < 2) src = (part == 0 ? Ahi : Alo) + (size_t)min(m0 + r, M - 1) * lda + k;
       else src = W + (size_t)min(n0 + r, N - 1) * K + k;
@@ -213,18 +230,19 @@ __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict
     const char* sb = st + 2 * BM * BK * 2;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kb = (ks * 16 + 8 * (l >> 5)) * 2;  // byte offset of this lane's 8 k values in a row
+      const int kc = ks * 2 + (l >> 5);  // this lane's 8-wide k-chunk of the row
       bf16x8 fh[TI], fl[TI], fb[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int r = wr * (BM / 2) + i * 32 + (l & 31);
+        const int r = wr * (BM / WR) + i * 32 + (l & 31);
+        const int kb = (kc ^ ((r >> 2) & 3)) * 16;
         fh[i] = *(const bf16x8*)(sah + r * (BK * 2) + kb);
         fl[i] = *(const bf16x8*)(sal + r * (BK * 2) + kb);
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const int r = wc * (BN / 2) + j * 32 + (l & 31);
-        fb[j] = *(const bf16x8*)(sb + r * (BK * 2) + kb);
+        const int r = wc * (BN / WC) + j * 32 + (l & 31);
+        fb[j] = *(const bf16x8*)(sb + r * (BK * 2) + (kc ^ ((r >> 2) & 3)) * 16);
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i)
@@ -242,8 +260,8 @@ __global__ void __launch_bounds__(256) pf_gemm_kernel(const uint16_t* __restrict
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wr * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-        const int col = n0 + wc * (BN / 2) + j * 32 + (l & 31);
+        const int row = m0 + wr * (BM / WR) + i * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int col = n0 + wc * (BN / WC) + j * 32 + (l & 31);
         const float v = acc[i][j][r];
         if (EPI == 2) {
           // the odd neighbour lane holds the up value of the same hidden unit
@@ -1046,16 +1064,16 @@ static int launch_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int ld
   const int grid = ((items + 7) / 8) * 8;
   const size_t lds = (size_t)gemm_stages<BM>() * (2 * BM + BN) * BK * 2;
   if (epi == 0)
-    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 0>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 0>), dim3(grid), dim3(gemm_threads<BM, BN>()), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
                        Hhi, Hlo, ldh, ksplit);
   else if (epi == 1)
-    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 1>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 1>), dim3(grid), dim3(gemm_threads<BM, BN>()), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
                        Hhi, Hlo, ldh, ksplit);
   else if (epi == 2)
-    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 2>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 2>), dim3(grid), dim3(gemm_threads<BM, BN>()), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
                        Hhi, Hlo, ldh, ksplit);
   else
-    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 3>), dim3(grid), dim3(256), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
+    hipLaunchKernelGGL((pf_gemm_kernel<BM, BN, 3>), dim3(grid), dim3(gemm_threads<BM, BN>()), lds, s, Ahi, Alo, lda, M, K, W, N, C, ldc,
                        Hhi, Hlo, ldh, ksplit);
   return MK_LAUNCH_OK();
 }
