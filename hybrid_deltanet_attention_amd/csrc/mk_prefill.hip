@@ -25,6 +25,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// LDS is read through native vector types: loads of HIP's float4 / float2 structs are split and
+// merged again late in code generation, which drops what the compiler knows about the access and
+// makes it wait for every outstanding LDS-DMA copy -- the next block's prefetch included -- first.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -406,8 +410,8 @@ __global__ void __launch_bounds__(256) pf_dn_scan_kernel(float* __restrict__ S, 
       if constexpr (NE % 4 == 0) {
 #pragma unroll
         for (int j = 0; j < NE; j += 4) {
-          const float4 x = *(const float4*)(qp + j);
-          const float4 y = *(const float4*)(kp + j);
+          const f32x4 x = *(const f32x4*)(qp + j);
+          const f32x4 y = *(const f32x4*)(kp + j);
           qo[j] = x.x; qo[j + 1] = x.y; qo[j + 2] = x.z; qo[j + 3] = x.w;
           ko[j] = y.x; ko[j + 1] = y.y; ko[j + 2] = y.z; ko[j + 3] = y.w;
         }
@@ -753,7 +757,7 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_kernel(float* __restrict__ 
         const float cf[4] = {uu.x * dd.x, uu.y * dd.y, uu.z * dd.z, uu.w * dd.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const float2 k = *(const float2*)&sk[tt + x][ue];
+          const f32x2 k = *(const f32x2*)&sk[tt + x][ue];
           a0 = fmaf(cf[x], k.x, a0);
           a1 = fmaf(cf[x], k.y, a1);
         }
@@ -878,16 +882,16 @@ __global__ void __launch_bounds__(256) pf_attention_kernel(const float* __restri
         const int n4 = hd >> 2, st0 = kk % n4;  // staggered start: the keys of a row hit different banks
         float d = 0.f;
         for (int d0 = 0; d0 < n4; d0 += 8) {
-          float4 kv[8], qv[8];
+          f32x4 kv[8], qv[8];
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
             int e = d0 + x + st0;
             e = (e >= n4 ? e - n4 : e) * 4;
-            kv[x] = float4{0.f, 0.f, 0.f, 0.f};
+            kv[x] = f32x4{0.f, 0.f, 0.f, 0.f};
             qv[x] = kv[x];
             if (d0 + x < n4) {
-              kv[x] = *(const float4*)(kr + e);
-              qv[x] = *(const float4*)(qr + e);
+              kv[x] = *(const f32x4*)(kr + e);
+              qv[x] = *(const f32x4*)(qr + e);
             }
           }
 #pragma unroll
@@ -931,13 +935,13 @@ __global__ void __launch_bounds__(256) pf_attention_kernel(const float* __restri
 #pragma unroll
         for (int x = 0; x < DPL; x += (DPL >= 4 ? 4 : 2)) {
           if (DPL >= 4) {
-            const float4 t4 = (kk < nvalid && live) ? *(const float4*)(vr + x) : float4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 t4 = (kk < nvalid && live) ? *(const f32x4*)(vr + x) : f32x4{0.f, 0.f, 0.f, 0.f};
             vv[u][x] = t4.x;
             vv[u][x + 1] = t4.y;
             vv[u][x + 2] = t4.z;
             vv[u][x + 3] = t4.w;
           } else {
-            const float2 t2 = (kk < nvalid && live) ? *(const float2*)(vr + x) : float2{0.f, 0.f};
+            const f32x2 t2 = (kk < nvalid && live) ? *(const f32x2*)(vr + x) : f32x2{0.f, 0.f};
             vv[u][x] = t2.x;
             vv[u][x + 1] = t2.y;
           }
