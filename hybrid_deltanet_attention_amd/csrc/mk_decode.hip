@@ -23,6 +23,7 @@
 
 #include <hip/hip_runtime.h>
 #include "mk_internal.h"
+#include <type_traits>
 
 typedef unsigned int u32;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
@@ -855,47 +856,55 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
       const float beta = sigmoidf_(ab[1]);
       // rows of head h, local index li = row - s0, owned by streaming wave li % NCW
       const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
-      for (int li = lo + ((wave() - lo % NCW) + NCW) % NCW; li < hi; li += NCW) {
-        const int row = s0 + li;
-        const int sl = li / rps;
-        const bool staged = sl < st_slots;
-        const LS float* srow = st + sl * 256 + (li % rps) * dk;
-        float sr[4];
-        if (staged) {
-          const int l0 = lane();
-          stage_f32x4(srow + l0, srow + (l0 + 64 < dk ? l0 + 64 : 0), srow + (l0 + 128 < dk ? l0 + 128 : 0),
-                      srow + (l0 + 192 < dk ? l0 + 192 : 0), sr);
+      // Two copies of the row loop: when every row of this head is staged the loop issues no global
+      // load, so the compiler has no reason to wait on the vector-memory counter inside it -- a
+      // wait there would also wait for the previous row's state stores and record store.
+      auto rows = [&](auto staged_tag) {
+        constexpr bool STAGED = decltype(staged_tag)::value;
+        for (int li = lo + ((wave() - lo % NCW) + NCW) % NCW; li < hi; li += NCW) {
+          const int row = s0 + li;
+          const int sl = li / rps;
+          const LS float* srow = st + sl * 256 + (li % rps) * dk;
+          float sr[4];
+          if (STAGED) {
+            const int l0 = lane();
+            stage_f32x4(srow + l0, srow + (l0 + 64 < dk ? l0 + 64 : 0), srow + (l0 + 128 < dk ? l0 + 128 : 0),
+                        srow + (l0 + 192 < dk ? l0 + 192 : 0), sr);
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (lane() + 64 * t >= dk) sr[t] = 0.f;
-        } else {
+            for (int t = 0; t < 4; ++t)
+              if (lane() + 64 * t >= dk) sr[t] = 0.f;
+          } else {
+            const bool staged = sl < st_slots;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int e = lane() + 64 * t;
+              sr[t] = e < dk ? (staged ? srow[e] : L.S[(size_t)row * dk + e]) : 0.f;
+            }
+          }
+          float kd = 0.f;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int e = lane() + 64 * t;
-            sr[t] = e < dk ? L.S[(size_t)row * dk + e] : 0.f;
+            if (e < dk) kd = fmaf(sr[t], k[e] * sk, kd);
           }
-        }
-        float kd = 0.f;
+          kd = wave_sum(kd);
+          const float u = beta * (vr[row - h * dv - i0] - alpha * kd);
+          float od = 0.f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int e = lane() + 64 * t;
-          if (e < dk) kd = fmaf(sr[t], k[e] * sk, kd);
-        }
-        kd = wave_sum(kd);
-        const float u = beta * (vr[row - h * dv - i0] - alpha * kd);
-        float od = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int e = lane() + 64 * t;
-          if (e < dk) {
-            const float nv2 = fmaf(u, k[e] * sk, alpha * sr[t]);
-            L.S[(size_t)row * dk + e] = nv2;
-            od = fmaf(nv2, q[e] * sq, od);
+          for (int t = 0; t < 4; ++t) {
+            const int e = lane() + 64 * t;
+            if (e < dk) {
+              const float nv2 = fmaf(u, k[e] * sk, alpha * sr[t]);
+              L.S[(size_t)row * dk + e] = nv2;
+              od = fmaf(nv2, q[e] * sq, od);
+            }
           }
+          od = wave_sum(od);
+          if (lane() == 0) ll_put(L.ll_o + row, cx.epoch, od);
         }
-        od = wave_sum(od);
-        if (lane() == 0) ll_put(L.ll_o + row, cx.epoch, od);
-      }
+      };
+      if (lo >= hi || (hi - 1) / rps < st_slots) rows(std::true_type{});
+      else rows(std::false_type{});
     }
     tr.mark();
     wg_bar();  // s.att is reused by the next head
