@@ -154,6 +154,59 @@ def cpu_baseline(cfg, W, n_prompt=32, n_steps=6) -> dict:
                       f"(not timed); host os.cpu_count()={os.cpu_count()}"}
 
 
+def _energy_reader():
+    """A function returning the board's energy accumulator in joules (amdsmi), or an error string."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            return None, f"{len(handles)} GPUs visible to amdsmi; cannot tell which one runs the kernel"
+        h = handles[0]
+
+        def read():
+            e = amdsmi.amdsmi_get_energy_count(h)
+            return e["energy_accumulator"] * e["counter_resolution"] * 1e-6, e["timestamp"]
+        read()
+        return read, None
+    except Exception as ex:  # no amdsmi, no permission, no counter on this board
+        return None, f"energy counter unavailable: {type(ex).__name__}: {ex}"
+
+
+def energy_leg(m, prompt, tok, n_steps: int) -> dict:
+    """Tokens per joule of the decode loop from the board energy accumulator (whole board, idle
+    power included), over n_steps consecutive one-launch decode steps after the 512-token prompt."""
+    import torch
+    read, err = _energy_reader()
+    if read is None:
+        return {"status": err}
+    torch.cuda.synchronize()
+    time.sleep(0.25)
+    ei0, _ = read()
+    ti0 = time.perf_counter()
+    time.sleep(1.0)
+    ei1, _ = read()
+    idle_w = (ei1 - ei0) / (time.perf_counter() - ti0)
+    m.mk_reset()
+    m.mk_prefill(prompt[:PROMPT], PROMPT, tok)
+    m.mk_sync()
+    e0, _ = read()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        m.mk_decode_step(tok, tok)
+    m.mk_sync()
+    t1 = time.perf_counter()
+    e1, _ = read()
+    joules = e1 - e0
+    secs = t1 - t0
+    return {"tok_per_J": round(n_steps / joules, 2) if joules > 0 else None,
+            "avg_power_W": round(joules / secs, 1),
+            "idle_power_W": round(idle_w, 1),
+            "steps": n_steps, "seconds": round(secs, 3),
+            "context": f"positions {PROMPT}..{PROMPT + n_steps - 1}",
+            "counter": "amdsmi energy accumulator, whole board"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +215,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the pp520 prefill timing (profiling runs)")
     ap.add_argument("--config", default="hybrid_0p8b")
+    ap.add_argument("--energy-steps", type=int, default=1280,
+                    help="decode steps of the energy (tok/J) leg; 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for rocprofv3 byte counters)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -267,6 +322,10 @@ def main():
                                               "unit": "tok/s", "ms": round(pp_s * 1e3, 3)},
         "launches_per_token": 1,
     }
+    if args.energy_steps > 0:
+        n_e = min(args.energy_steps, cfg.max_ctx - PROMPT)
+        out["energy"] = energy_leg(m, prompt, tok, n_e)
+        print(f"[bench] energy: {out['energy']}", file=sys.stderr, flush=True)
     m.close()
     del m
     torch.cuda.empty_cache()

@@ -1,0 +1,43 @@
+"""Host-side pieces of bench.py that need no GPU: the argument contract, the algorithmic byte
+count of a decode launch, and the energy-counter reader's failure path."""
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+sys.path.insert(0, str(ROOT))
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_0p8b():
+    # 587,137,024 BF16 parameters outside the embedding-as-head (incl. gains) plus the tied head,
+    # the DeltaNet state read and written, and 12,288 bytes of FP32 KV per visible position
+    cfg = synth.get_config("hybrid_0p8b")
+    a = bench.algorithmic_bytes(cfg, 1000)
+    assert a["state"] == 18 * 16 * 128 * 128 * 4 * 2
+    assert a["kv"] == 12288 * 1000
+    assert a["lm_head"] == 2 * 151936 * 1024 + 6 * 1024
+    per_dn = 2 * ((2 * 16 * 128 + 16 * 128 + 2 * 16) * 1024 + 1024 * 2048 + 3 * 3584 * 1024) + 8 * 1024
+    per_att = 2 * ((8 + 4) * 128 * 1024 + 1024 * 1024 + 3 * 3584 * 1024) + 8 * 1024
+    assert a["weights"] == 18 * per_dn + 6 * per_att
+    assert a["total"] == a["weights"] + a["lm_head"] + a["state"] + a["kv"]
+
+
+def test_energy_reader_never_raises():
+    read, err = bench._energy_reader()
+    if read is None:
+        assert isinstance(err, str) and err
+    else:
+        j, _ = read()
+        assert j >= 0
