@@ -148,6 +148,41 @@ class Oracle:
         out["logits"] = self._head(X) if logits == "all" else self._head(X[-1])
         return out
 
+    # ------------------------------------------------------ speculative verify
+    def snapshot(self) -> dict:
+        return {"pos": self.pos, "S": {l: S.copy() for l, S in self.S.items()},
+                "Kc": {l: K.copy() for l, K in self.Kc.items()}, "Vc": {l: V.copy() for l, V in self.Vc.items()}}
+
+    def restore(self, snap: dict):
+        self.pos = snap["pos"]
+        self.S = {l: S.copy() for l, S in snap["S"].items()}
+        self.Kc = {l: K.copy() for l, K in snap["Kc"].items()}
+        self.Vc = {l: V.copy() for l, V in snap["Vc"].items()}
+
+    def verify(self, tokens) -> dict:
+        """Score the pending token and k drafts, tokens = [t0, d1..dk], from the current position.
+
+        Speculative decoding keeps the main model's greedy output exactly (Reddit follow-up on the
+        27B model, speculative-decoding paragraph): y_i is the greedy choice after feeding
+        tokens[0..i-1] one by one, the accepted count a is the longest prefix with d_i == y_i, and
+        the state and cache end as if only tokens[0..a] had been decoded (position advanced by
+        a + 1).  The caller emits y_1..y_{a+1}; y_{a+1} becomes the next pending token.
+        Returns {"y": [k+1] ints, "a": int, "logits": [k+1, vocab]}."""
+        tokens = [int(t) for t in tokens]
+        if not tokens:
+            raise ValueError("verify needs the pending token")
+        start = self.snapshot()
+        logits = np.stack([self.step(t) for t in tokens])
+        y = [self.argmax(lg) for lg in logits]
+        a = 0
+        while a < len(tokens) - 1 and tokens[a + 1] == y[a]:
+            a += 1
+        # roll back: the state after tokens[0..a] only
+        self.restore(start)
+        for t in tokens[: a + 1]:
+            self.step(t)
+        return {"y": y, "a": a, "logits": logits}
+
     # ------------------------------------------------------------- helpers
     @staticmethod
     def argmax(logits) -> int:

@@ -317,6 +317,63 @@ def pin_model_continuation():
         _close(o.step(toks[t]), full["logits"][t], 1e-10, f"continued position {t}")
 
 
+def _verify_setup(seed, n_prompt, n_greedy):
+    cfg = _tiny()
+    W = synth.make_weights(cfg, seed)
+    prompt = synth.make_prompt(cfg.vocab, n_prompt, seed)
+    o = om.Oracle(cfg, W)
+    # the greedy continuation, from the whole-sequence form (one forward pass per prefix)
+    seq = list(prompt)
+    for _ in range(n_greedy):
+        seq.append(int(np.argmax(o.forward(seq, logits="last")["logits"])))
+    return cfg, W, o, [int(t) for t in prompt], seq[n_prompt:]
+
+
+def _check_rolled_back(o, kept, what):
+    """o's state and cache == the whole-sequence form over the kept tokens"""
+    ref = o.forward(kept, logits="last")
+    assert o.pos == len(kept), f"{what}: position {o.pos} vs {len(kept)}"
+    for l, S in ref["S"].items():
+        _close(o.S[l], S, 1e-10, f"{what}: state layer {l}")
+    for l, (K, V) in ref["KV"].items():
+        _close(o.Kc[l][:, : len(kept)], K, 1e-12, f"{what}: K layer {l}")
+        _close(o.Vc[l][:, : len(kept)], V, 1e-12, f"{what}: V layer {l}")
+
+
+def pin_verify_accepts_greedy_drafts():
+    """drafts equal to the greedy continuation are all accepted; the choices are that continuation"""
+    cfg, W, o, prompt, cont = _verify_setup(5, 9, 6)
+    o.load_state(o.forward(prompt[:-1], logits="last"))
+    pending = prompt[-1]
+    k = 4
+    r = o.verify([pending] + cont[:k])
+    assert r["a"] == k, f"accepted {r['a']} of {k} greedy drafts"
+    assert r["y"] == cont[: k + 1], "greedy choices"
+    _check_rolled_back(o, prompt + cont[:k], "all accepted")
+
+
+def pin_verify_planted_mismatch():
+    """a draft that differs from the greedy choice at index j stops acceptance at a = j and
+    discards the state of every later position"""
+    cfg, W, o, prompt, cont = _verify_setup(6, 8, 5)
+    for j in (0, 2):
+        o.load_state(o.forward(prompt[:-1], logits="last"))
+        drafts = list(cont[:4])
+        drafts[j] = (drafts[j] + 1) % cfg.vocab
+        r = o.verify([prompt[-1]] + drafts)
+        assert r["a"] == j, f"planted mismatch at {j}: accepted {r['a']}"
+        assert r["y"][: j + 1] == cont[: j + 1]
+        _check_rolled_back(o, prompt + cont[:j], f"mismatch at {j}")
+
+
+def pin_verify_k0_is_one_step():
+    cfg, W, o, prompt, cont = _verify_setup(7, 6, 1)
+    o.load_state(o.forward(prompt[:-1], logits="last"))
+    r = o.verify([prompt[-1]])
+    assert r["a"] == 0 and r["y"] == cont[:1]
+    _check_rolled_back(o, prompt, "k = 0")
+
+
 def pin_argmax_lowest_index():
     lg = np.array([0.1, 0.7, 0.3, 0.7, -1.0])
     assert om.Oracle.argmax(lg) == 1

@@ -83,6 +83,23 @@ def _parallel_no_s0_decay(S0, Q, K, V, alpha, beta):
     return O, S_T - np.exp(g[-1]) * S0 + S0
 
 
+def _verify_variant(keep_extra=0, shift=0, rollback=True):
+    def verify(self, tokens):
+        tokens = [int(t) for t in tokens]
+        start = self.snapshot()
+        logits = np.stack([self.step(t) for t in tokens])
+        y = [self.argmax(lg) for lg in logits]
+        a = 0
+        while a + shift < len(tokens) - 1 and tokens[a + 1] == y[a + shift]:
+            a += 1
+        if rollback:
+            self.restore(start)
+            for t in tokens[: max(0, min(len(tokens), a + 1 + keep_extra))]:
+                self.step(t)
+        return {"y": y, "a": a, "logits": logits}
+    return verify
+
+
 _REAL_STEP = dn.delta_step
 _REAL_ROPE = prim.rope
 _REAL_RMS = prim.rmsnorm
@@ -104,6 +121,10 @@ MUTANTS = [
     ("attention: no 1/sqrt(hd)", [(att, "attend_one"), (om, "attend_one")], _attend_no_scale),
     ("attention: interleaved GQA groups", [(att, "attend_one"), (om, "attend_one")], _attend_wrong_group),
     ("parallel form: S0 not decayed", [(dn, "delta_parallel"), (om, "delta_parallel")], _parallel_no_s0_decay),
+    ("verify: no rollback", [(om.Oracle, "verify")], _verify_variant(rollback=False)),
+    ("verify: rollback keeps the accepted drafts only", [(om.Oracle, "verify")], _verify_variant(keep_extra=-1)),
+    ("verify: rollback keeps one token too many", [(om.Oracle, "verify")], _verify_variant(keep_extra=1)),
+    ("verify: draft compared with the next choice", [(om.Oracle, "verify")], _verify_variant(shift=1)),
 ]
 
 
