@@ -76,7 +76,8 @@ std::string check_config(const mk_config* c) {
   if (c->weight_dtype != MK_BF16) return "weight_dtype must be MK_BF16";
   if (c->kv_dtype != MK_F32) return "kv_dtype must be MK_F32";
   if (c->max_ctx <= 0 || c->max_ctx > (1 << 20)) return "max_ctx must be in [1, 2^20]";
-  if (c->max_verify_k < 0) return "max_verify_k must be >= 0";
+  if (c->max_verify_k < 0 || c->max_verify_k > MK_VERIFY_MAXT - 1)
+    return "max_verify_k must be in [0, " + std::to_string(MK_VERIFY_MAXT - 1) + "]";
   if (!(c->rms_eps > 0.f) || !(c->l2_eps > 0.f) || !(c->rope_theta > 0.f)) return "eps and rope_theta must be > 0";
   if (c->hidden > 16384 || c->ffn > 65536) return "hidden <= 16384 and ffn <= 65536";
   return "";
@@ -85,6 +86,8 @@ std::string check_config(const mk_config* c) {
 // ----------------------------------------------------------------------- workspace layout
 struct LayerOff {
   size_t w_in, w_out, w_gu, w_down, g12, S, Kc, Vc, ll_in, ll_part, ll_o, ll_x1, ll_h, ll_x2;
+  // speculative verify: records of vt positions ([t][n] per record vector) and state snapshots
+  size_t v_in, v_part, v_o, v_x1, v_h, v_x2, snap;
   int64_t rows_in, k_out;
 };
 
@@ -94,6 +97,10 @@ struct Layout {
   size_t xchg_begin, xchg_end;    // exchange records
   std::vector<LayerOff> layers;
   int max_items;
+  // speculative verify (vt = max_verify_k + 1 positions per launch; 0 when not configured)
+  int vt;
+  size_t vdescs, v_am, v_acc;
+  int64_t snap_stride;  // floats between the snapshots of consecutive positions
   // prefill scratch: a chunk of up to pf_T tokens
   int pf_T, pf_lda, pf_ldy;
   size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part, pf_ch, pf_sk;
@@ -152,7 +159,33 @@ Layout make_layout(const mk_config& c) {
     lo.ll_x2 = take(D * 8);
   }
   L.ll_am = take((size_t)2 * MK_MAX_GRID * 8);
+  L.vt = c.max_verify_k > 0 ? c.max_verify_k + 1 : 0;
+  if (L.vt) {
+    const size_t vt = (size_t)L.vt;
+    for (int l = 0; l < c.n_layers; ++l) {
+      LayerOff& lo = L.layers[l];
+      lo.v_in = take(vt * lo.rows_in * 8);
+      if (is_attention(c, l)) lo.v_part = take(vt * L.max_items * gs * (c.head_dim + 2) * 8);
+      lo.v_o = take(vt * lo.k_out * 8);
+      lo.v_x1 = take(vt * D * 8);
+      lo.v_h = take(vt * c.ffn * 8);
+      lo.v_x2 = take(vt * D * 8);
+    }
+    L.v_am = take(vt * 2 * MK_MAX_GRID * 8);
+    L.v_acc = take(256);
+  }
   L.xchg_end = o;
+  if (L.vt) {
+    L.vdescs = take(sizeof(MkLayerDev) * c.n_layers);
+    int n_dn = 0;
+    for (int l = 0; l < c.n_layers; ++l) n_dn += is_attention(c, l) ? 0 : 1;
+    const int64_t per = H * c.dn_dv * c.dn_dk;
+    L.snap_stride = n_dn * per;
+    const size_t base = take((size_t)c.max_verify_k * L.snap_stride * 4);
+    int j = 0;
+    for (int l = 0; l < c.n_layers; ++l)
+      if (!is_attention(c, l)) L.layers[l].snap = base + (size_t)(j++) * per * 4;
+  }
   L.scratch = take(4096);
   // prefill scratch
   {
@@ -193,6 +226,7 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   int att = 2 * c.dn_dk + 2 + c.dn_dv;
   att = std::max(att, gs * hd + 2 * hd + gs * C + 2 * gs);
   att = std::max(att, MK_RED_CAP);
+  att = std::max(att, 3 * ((c.max_ctx - 1 + C) / C));  // combine staging of one output, all chunks
   int o = 0;
   auto take = [&](int n) {
     const int at = o;
@@ -215,6 +249,40 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   p.lds_floats = o;
 }
 
+// LDS carve for the verify kernel (floats) at grid size `grid`: vt positions' residuals, RoPE rows
+// and vectors; the vector region also stages DeltaNet inputs, attention items, the combine and the
+// argmax records.  No prefetch stages.
+void lds_layout_verify(const mk_config& c, int grid, MkDecodeParams& p) {
+  const int vt = c.max_verify_k + 1;
+  const int D = c.hidden;
+  const int gs = c.n_q_heads / c.n_kv_heads;
+  const int hd = c.head_dim, C = MK_ATT_CHUNK;
+  const int nch_max = (c.max_ctx - 1 + C) / C;
+  int64_t vec = (int64_t)vt * std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, D));
+  vec = std::max(vec, (int64_t)vt * (2 * c.dn_dk + 2 + c.dn_dv));
+  vec = std::max(vec, (int64_t)vt * gs * hd + 2 * C * hd + vt * gs * C + 2 * vt * gs);
+  vec = std::max(vec, (int64_t)3 * vt * nch_max);
+  vec = std::max(vec, (int64_t)2 * vt * grid);
+  int o = 0;
+  auto take = [&](int64_t n) {
+    const int at = o;
+    o += (int)((n + 3) / 4 * 4);
+    return at;
+  };
+  p.lds_desc = take(c.n_layers * (int)(sizeof(MkLayerDev) / 4));
+  p.lds_gain = take(D);  // BF16 [2][D]
+  p.lds_rope = take(vt * hd);
+  p.lds_x = take((int64_t)vt * D);
+  p.lds_xn = -1;  // shares the vector region
+  p.lds_vec = take(vec);
+  p.vec_floats = (int32_t)((vec + 3) / 4 * 4);
+  p.lds_att = take(MK_RED_CAP);
+  p.lds_scr = take(2 * MK_VERIFY_MAXT * MK_NWAVE);
+  p.lds_flag = take(4);
+  p.lds_trace = take(MK_VERIFY_MAXT);  // the tokens
+  p.lds_floats = o;
+}
+
 }  // namespace
 
 struct mk_ctx {
@@ -225,10 +293,14 @@ struct mk_ctx {
   size_t ws_bytes = 0;
   Layout lay;
   MkDecodeParams base{};
+  MkDecodeParams vbase{};  // verify launches (valid when lay.vt > 0)
   int n_cu = 0;
   int grid = 0;
   bool loaded = false;
+  // positions enqueued so far; after a verify launch only an upper bound (the device decides how
+  // many drafts it keeps) until the next synchronising call reads the device's count
   int64_t pos_host = 0;
+  bool pos_exact = true;
   std::string err;
 };
 
@@ -246,6 +318,17 @@ int fail(mk_ctx* ctx, int code, const std::string& msg) {
     if (_e != hipSuccess)                                                                     \
       return fail((ctx), MK_E_HIP, std::string(#call) + ": " + hipGetErrorString(_e));        \
   } while (0)
+
+// The device's position -> the host count (synchronises).  Used where the host needs the exact
+// value after verify launches left it an upper bound.
+int refresh_position(mk_ctx* ctx) {
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
+  MkCtl ctl;
+  HIPCHK(ctx, hipMemcpy(&ctl, ctx->base.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
+  if (!ctl.err) ctx->pos_host = ctl.pos;
+  ctx->pos_exact = true;
+  return MK_OK;
+}
 
 int check_tensor_list(const mk_config& c, const mk_tensor* t, int32_t n, std::string& msg,
                       std::vector<int>* order) {
@@ -414,6 +497,38 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
     d.ll_h = (mk_u64*)(ctx->ws + lo.ll_h);
     d.ll_x2 = (mk_u64*)(ctx->ws + lo.ll_x2);
   }
+  // speculative verify: its own records (vt positions each), snapshots and LDS carve
+  std::vector<MkLayerDev> vdescs;
+  if (lay.vt) {
+    MkDecodeParams& v = ctx->vbase;
+    v = p;
+    v.layers = (const MkLayerDev*)(ctx->ws + lay.vdescs);
+    v.ll_am = (mk_u64*)(ctx->ws + lay.v_am);
+    v.ll_acc = (mk_u64*)(ctx->ws + lay.v_acc);
+    v.snap_stride = lay.snap_stride;
+    v.trace = nullptr;
+    lds_layout_verify(*cfg, ctx->grid, v);
+    const int vbytes = v.lds_floats * 4;
+    if (vbytes > (int)prop.sharedMemPerBlock || mk_verify_max_blocks_per_cu(&v, vbytes) < 1) {
+      const std::string m = "verify kernel needs " + std::to_string(vbytes) + " B of LDS for max_verify_k = " +
+                            std::to_string(cfg->max_verify_k) + "; device offers " +
+                            std::to_string(prop.sharedMemPerBlock);
+      delete ctx;
+      return fail_global(MK_E_OCCUPANCY, m);
+    }
+    vdescs = descs;
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const LayerOff& lo = lay.layers[l];
+      MkLayerDev& d = vdescs[l];
+      d.ll_in = (mk_u64*)(ctx->ws + lo.v_in);
+      d.ll_o = (mk_u64*)(ctx->ws + lo.v_o);
+      d.ll_x1 = (mk_u64*)(ctx->ws + lo.v_x1);
+      d.ll_h = (mk_u64*)(ctx->ws + lo.v_h);
+      d.ll_x2 = (mk_u64*)(ctx->ws + lo.v_x2);
+      if (d.kind == MK_LAYER_ATT) d.ll_part = (mk_u64*)(ctx->ws + lo.v_part);
+      else d.Ssnap = (float*)(ctx->ws + lo.snap);
+    }
+  }
   // RoPE tables: angle = pos * theta^(-2i/hd), evaluated in double, stored as float
   const int half = cfg->head_dim / 2;
   std::vector<float> cs((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
@@ -433,6 +548,9 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   };
   hip_ok(hipMemcpyAsync(ctx->ws + lay.descs, descs.data(), sizeof(MkLayerDev) * descs.size(), hipMemcpyHostToDevice,
                         ctx->stream), "copy layer descriptors");
+  if (lay.vt)
+    hip_ok(hipMemcpyAsync(ctx->ws + lay.vdescs, vdescs.data(), sizeof(MkLayerDev) * vdescs.size(),
+                          hipMemcpyHostToDevice, ctx->stream), "copy verify layer descriptors");
   hip_ok(hipMemcpyAsync(ctx->ws + lay.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, ctx->stream),
          "copy rope cos");
   hip_ok(hipMemcpyAsync(ctx->ws + lay.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, ctx->stream),
@@ -465,7 +583,14 @@ int mk_set_grid(mk_ctx* ctx, int32_t n) {
   lds_layout(ctx->cfg, n, q);
   if (mk_decode_max_blocks_per_cu(&q, q.lds_floats * 4) < 1)
     return fail(ctx, MK_E_OCCUPANCY, "decode kernel does not fit at this grid size");
+  MkDecodeParams v = ctx->vbase;
+  if (ctx->lay.vt) {
+    lds_layout_verify(ctx->cfg, n, v);
+    if (mk_verify_max_blocks_per_cu(&v, v.lds_floats * 4) < 1)
+      return fail(ctx, MK_E_OCCUPANCY, "verify kernel does not fit at this grid size");
+  }
   ctx->base = q;
+  ctx->vbase = v;
   ctx->grid = n;
   return MK_OK;
 }
@@ -486,6 +611,7 @@ int mk_reset(mk_ctx* ctx) {
     return fail(ctx, MK_E_HIP, "zero exchange launch failed");
   if (mk_launch_set_ctl(ctx->base.ctl, 0, 1, 1, ctx->stream)) return fail(ctx, MK_E_HIP, "set position launch failed");
   ctx->pos_host = 0;
+  ctx->pos_exact = true;
   return MK_OK;
 }
 
@@ -614,6 +740,7 @@ int mk_decode_step(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_
   if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
   if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
   if (!d_tok || !d_next) return fail(ctx, MK_E_INVALID, "d_tok and d_next are required");
+  if (ctx->pos_host + 1 > ctx->cfg.max_ctx && refresh_position(ctx) != MK_OK) return MK_E_HIP;
   if (ctx->pos_host + 1 > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "context is full");
   MkDecodeParams p = ctx->base;
   p.tok = d_tok;
@@ -628,6 +755,8 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
   if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
   if (!d_tokens || !d_next || n <= 0) return fail(ctx, MK_E_INVALID, "need d_tokens, d_next and n > 0");
+  // the prefill kernels take the start position from the host
+  if (!ctx->pos_exact && refresh_position(ctx) != MK_OK) return MK_E_HIP;
   if (ctx->pos_host + n > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "prompt does not fit the context");
   const mk_config& c = ctx->cfg;
   const int gs = c.n_q_heads / c.n_kv_heads;
@@ -713,9 +842,24 @@ int mk_set_trace(mk_ctx* ctx, void* d_trace, size_t bytes) {
   return MK_OK;
 }
 
-int mk_verify_k(mk_ctx* ctx, const int32_t*, int32_t, int32_t*, int32_t*) {
+int mk_verify_k(mk_ctx* ctx, const int32_t* d_tokens, int32_t k, int32_t* d_out, int32_t* d_n_accepted) {
   if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
-  return fail(ctx, MK_E_UNSUPPORTED, "speculative verify is not built");
+  if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
+  if (!d_tokens || !d_out || !d_n_accepted) return fail(ctx, MK_E_INVALID, "d_tokens, d_out and d_n_accepted are required");
+  if (ctx->lay.vt == 0) return fail(ctx, MK_E_INVALID, "the context was created with max_verify_k = 0");
+  if (k < 0 || k > ctx->cfg.max_verify_k)
+    return fail(ctx, MK_E_INVALID, "k must be in [0, " + std::to_string(ctx->cfg.max_verify_k) + "]");
+  if (ctx->pos_host + k + 1 > ctx->cfg.max_ctx && refresh_position(ctx) != MK_OK) return MK_E_HIP;
+  if (ctx->pos_host + k + 1 > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "the drafts do not fit the context");
+  MkDecodeParams p = ctx->vbase;
+  p.nt = k + 1;
+  p.vtok = d_tokens;
+  p.vout = d_out;
+  p.vacc = d_n_accepted;
+  if (mk_launch_verify(&p, ctx->grid, ctx->stream)) return fail(ctx, MK_E_HIP, "verify launch failed");
+  ctx->pos_host += k + 1;
+  ctx->pos_exact = false;
+  return MK_OK;
 }
 
 int mk_sync(mk_ctx* ctx) {
@@ -727,9 +871,10 @@ int mk_sync(mk_ctx* ctx) {
     // clear the flag so that the next launch starts clean; the sequence state is undefined now
     if (mk_launch_set_ctl(ctx->base.ctl, -1, 1, 0, ctx->stream) == 0) (void)hipStreamSynchronize(ctx->stream);
     if (ctl.err == 2u)
-      return fail(ctx, MK_E_INVALID, "a decode launch saw a token id outside [0, vocab) or a full context; call mk_reset");
+      return fail(ctx, MK_E_INVALID,
+                  "a decode or verify launch saw a token id outside [0, vocab) or a full context; call mk_reset");
 
-    return fail(ctx, MK_E_DEVICE_TIMEOUT, "a grid-wide wait inside the decode kernel gave up; call mk_reset");
+    return fail(ctx, MK_E_DEVICE_TIMEOUT, "a grid-wide wait inside a persistent kernel gave up; call mk_reset");
   }
   return MK_OK;
 }
@@ -740,6 +885,10 @@ int mk_get_position(mk_ctx* ctx, int32_t* pos) {
   MkCtl ctl;
   HIPCHK(ctx, hipMemcpy(&ctl, ctx->base.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
   *pos = ctl.pos;
+  if (!ctl.err) {
+    ctx->pos_host = ctl.pos;
+    ctx->pos_exact = true;
+  }
   return MK_OK;
 }
 

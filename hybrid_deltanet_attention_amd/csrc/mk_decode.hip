@@ -21,1136 +21,9 @@
 // later phases stay in flight across them.  Every wait is bounded: a wait that gives up sets
 // ctl->err and every workgroup leaves the kernel.
 
-#include <hip/hip_runtime.h>
-#include "mk_internal.h"
-#include <type_traits>
-
-typedef unsigned int u32;
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-// Native vector types for LDS accesses: loads of HIP's float4 / uint2 structs are split and merged
-// again late in code generation, which drops what the compiler knows about the accessed LDS object
-// and makes it wait for every outstanding LDS-DMA copy before the read.
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-// LDS pointers are kept in address space 3 so every access is a ds_* instruction
-#if defined(__HIP_DEVICE_COMPILE__)
-#define LS __attribute__((address_space(3)))
-#else
-#define LS
-#endif
+#include "mk_device.h"
 
 namespace {
-
-constexpr int NCW = MK_NCW;          // streaming waves 0..NCW-1
-constexpr int NCT = MK_NCT;          // streaming threads
-constexpr int NPT = MK_NT - MK_NCT;  // polling threads
-constexpr int SLOT = 64;             // u32x4 per 1 KB LDS slot
-constexpr int USLOTS = 4;            // slots per GEMV unit: 4 rows x 512 BF16 columns
-constexpr int A_UNITS = MK_STAGE_A_SLOTS / USLOTS;
-constexpr int PB = 8;                // poll loads in flight per lane
-constexpr int ATT_C = MK_ATT_CHUNK;
-
-// Compiler-only barrier: memory operations issued before it stay before it.
-__device__ __forceinline__ void keep_issued() { asm volatile("" ::: "memory"); }
-
-// Thread index the compiler cannot treat as loop-invariant: per-lane address arithmetic is
-// recomputed where it is used instead of being hoisted out of the layer loop and kept live.
-__device__ __forceinline__ int tid() {
-  int t = (int)threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
-}
-__device__ __forceinline__ int lane() { return tid() & 63; }
-__device__ __forceinline__ int wave() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
-__device__ __forceinline__ bool streamer() { return wave() < NCW; }
-
-// Values that are the same in every lane, made scalar again after a call boundary (arguments of
-// out-of-line functions arrive in vector registers).
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-template <typename T>
-__device__ __forceinline__ T* uni_ptr(T* p) {
-  const unsigned long long v = (unsigned long long)p;
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v), hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
-  return (T*)(((unsigned long long)hi << 32) | lo);
-}
-
-// contiguous balanced split of n items over parts: part i gets [split(n,parts,i), split(n,parts,i+1))
-__device__ __forceinline__ int split(int n, int parts, int i) { return (int)(((long long)n * i) / parts); }
-
-// Workgroup barrier ordering LDS only: it waits for this wave's LDS operations but not for its
-// global loads, stores or LDS-DMA copies.
-__device__ __forceinline__ void wg_bar() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  keep_issued();
-  __builtin_amdgcn_s_barrier();
-  keep_issued();
-}
-
-// vmcnt(N): at most N of this wave's vector memory operations still outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-// at most n outstanding (rounded down to a supported count: waiting for more is always correct)
-__device__ __forceinline__ void wait_vm_n(int n) {
-  n = __builtin_amdgcn_readfirstlane(n);
-  if (n >= 63) wait_vm<63>();
-  else if (n >= 48) wait_vm<48>();
-  else if (n >= 32) wait_vm<32>();
-  else if (n >= 24) wait_vm<24>();
-  else if (n >= 16) wait_vm<16>();
-  else if (n >= 12) wait_vm<12>();
-  else if (n >= 8) wait_vm<8>();
-  else if (n >= 6) wait_vm<6>();
-  else if (n >= 4) wait_vm<4>();
-  else if (n >= 3) wait_vm<3>();
-  else if (n >= 2) wait_vm<2>();
-  else if (n >= 1) wait_vm<1>();
-  else wait_vm<0>();
-}
-
-__device__ __forceinline__ void ll_put(MK_G mk_u64* p, u32 epoch, float v) {
-  __hip_atomic_store(p, ((mk_u64)epoch << 32) | (mk_u64)__float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ mk_u64 ld_dev(const MK_G mk_u64* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float bf_lo(u32 w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((u32)h << 16); }
-
-__device__ __forceinline__ u32x4 ldw(const MK_G uint16_t* p) { return __builtin_nontemporal_load((const MK_G u32x4*)p); }
-
-// Asynchronous global -> LDS copy (gfx950 LDS DMA): lane l's 16 bytes land at dst + 16 l; tracked
-// by vmcnt like a load.  Lanes that are switched off copy nothing.
-__device__ __forceinline__ void dma16(const MK_G void* src, LS void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-
-// The LDS regions that LDS-DMA fills (the two prefetch stages) live in their own static array; every
-// other LDS region lives in the dynamic array and is written only by ds_* stores.  The compiler can
-// then prove that reads of the dynamic regions never race a copy and issues them without waiting.
-// Reads of the stage regions go through the asm blocks below: left to the compiler, each would wait
-// for every outstanding vector-memory operation of the wave, the prefetches for later phases
-// included.  That the copies a read needs have landed is ensured by the explicit vmcnt waits before
-// the barrier that precedes the read.  Each block waits for its own reads.
-__shared__ __attribute__((aligned(1024))) u32x4 g_stage[(MK_STAGE_A_SLOTS + MK_STAGE_B_SLOTS) * SLOT];
-
-__device__ __forceinline__ u32 lds_addr(const LS void* p) { return (u32)(size_t)p; }
-
-// four 16-byte reads at p, p + 1 KB, p + 2 KB, p + 3 KB (one GEMV unit)
-__device__ __forceinline__ void stage_unit(const LS u32x4* p, u32x4 (&w)[USLOTS]) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:1024\n\t"
-      "ds_read_b128 %2, %4 offset:2048\n\t"
-      "ds_read_b128 %3, %4 offset:3072\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
-      : "v"(lds_addr(p))
-      : "memory");
-}
-// two units
-__device__ __forceinline__ void stage_units2(const LS u32x4* p, const LS u32x4* q, u32x4 (&w)[USLOTS],
-                                             u32x4 (&v)[USLOTS]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %9\n\t"
-      "ds_read_b128 %5, %9 offset:1024\n\t"
-      "ds_read_b128 %6, %9 offset:2048\n\t"
-      "ds_read_b128 %7, %9 offset:3072\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(lds_addr(p)), "v"(lds_addr(q))
-      : "memory");
-}
-// four floats at independent addresses
-__device__ __forceinline__ void stage_f32x4(const LS float* a, const LS float* b, const LS float* c,
-                                            const LS float* d, float (&o)[4]) {
-  asm volatile(
-      "ds_read_b32 %0, %4\n\t"
-      "ds_read_b32 %1, %5\n\t"
-      "ds_read_b32 %2, %6\n\t"
-      "ds_read_b32 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(lds_addr(a)), "v"(lds_addr(b)), "v"(lds_addr(c)), "v"(lds_addr(d))
-      : "memory");
-}
-// eight float4 at independent addresses
-__device__ __forceinline__ void stage_f4x8(const LS float* const (&a)[8], f32x4 (&o)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %9\n\t"
-      "ds_read_b128 %2, %10\n\t"
-      "ds_read_b128 %3, %11\n\t"
-      "ds_read_b128 %4, %12\n\t"
-      "ds_read_b128 %5, %13\n\t"
-      "ds_read_b128 %6, %14\n\t"
-      "ds_read_b128 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-      : "v"(lds_addr(a[0])), "v"(lds_addr(a[1])), "v"(lds_addr(a[2])), "v"(lds_addr(a[3])), "v"(lds_addr(a[4])),
-        "v"(lds_addr(a[5])), "v"(lds_addr(a[6])), "v"(lds_addr(a[7]))
-      : "memory");
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF,
-                                                              false)));
-}
-
-// Sum over each 16-lane row (quad swaps, half-row mirror, row mirror); every lane of the row ends
-// with the row's total.  Fixed order, so every call site is deterministic.
-__device__ __forceinline__ float row_sum16(float v) {
-  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
-  v = dpp_add<0x140, 0xF>(v);  // row_mirror
-  return v;
-}
-__device__ __forceinline__ float row_max16(float v) {
-  v = dpp_max<0xB1>(v);
-  v = dpp_max<0x4E>(v);
-  v = dpp_max<0x141>(v);
-  v = dpp_max<0x140>(v);
-  return v;
-}
-// Full-wave sum: row sums, then row broadcasts; the total lands in lane 63 and is broadcast.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row_sum16(v);
-  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = row_max16(v);
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-struct Ctx {
-  MK_G MkCtl* ctl;
-  u32 epoch;
-};
-
-__device__ __forceinline__ void set_err(const Ctx& cx, u32 code) {
-  __hip_atomic_store(&cx.ctl->err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool err_seen(const Ctx& cx) {
-  return __hip_atomic_load(&cx.ctl->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-}
-
-struct Lds {
-  LS MkLayerDev* desc;  // every layer's descriptor
-  LS uint16_t* gain;    // BF16 RMSNorm gains [2 (layer parity)][2][D]
-  LS float* rope;       // cos [hd/2], sin [hd/2] at this launch's position
-  LS float* x;          // residual [D]
-  LS u32* xn;           // normalised residual [D], hi/lo BF16 pairs
-  LS float* vec;        // gathered mixer output / FFN hidden, argmax records
-  LS float* att;        // gathered DeltaNet / attention inputs, combine staging, GEMV unit partials
-  LS float* scr;        // small reductions
-  LS int* flag;         // set once a wait gave up
-  LS u32x4* stA;        // prefetch stage A
-  LS u32x4* stB;        // prefetch stage B
-};
-
-// Workgroup barrier that also tells every thread whether any thread passed bad == true.  A wait
-// that gives up is final for the launch, so the flag is only ever raised.
-__device__ __forceinline__ bool wg_bar_or(const Lds& s, bool bad) {
-  if (bad) *s.flag = 1;
-  wg_bar();
-  return *s.flag != 0;
-}
-
-struct Tracer {
-  LS unsigned long long* lbuf;   // timestamps are kept in LDS while the kernel runs ...
-  MK_G unsigned long long* buf;  // ... and copied here at the end (null: tracing off)
-  int n;
-  // wall-clock stamps of lane 0 of wave 0 (a streaming wave)
-  __device__ __forceinline__ void mark() {
-    if (buf) {
-      if (threadIdx.x == 0 && n < MK_TRACE_EVENTS) lbuf[n] = wall_clock64();
-      ++n;
-    }
-  }
-  __device__ __forceinline__ void flush() {
-    if (buf) {
-      wg_bar();
-      for (int i = tid(); i < MK_TRACE_EVENTS; i += MK_NT) buf[i] = i < n ? lbuf[i] : 0ull;
-    }
-  }
-};
-
-// GEMV activations are held as BF16 hi + lo pairs (see the GEMV section).
-__device__ __forceinline__ u32 bf16_rne_bits(float f) {
-  const u32 u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-// v -> (hi, lo) BF16 bit patterns with v = hi + lo + O(2^-17 |v|)
-__device__ __forceinline__ void split_hl(float v, u32& h, u32& l) {
-  h = bf16_rne_bits(v);
-  l = bf16_rne_bits(v - __uint_as_float(h << 16));
-}
-// word offsets (u32) of the hi and lo pair holding column c, c even
-__device__ __forceinline__ int hl_word(int c) { return (c >> 3) * 8 + ((c & 7) >> 1); }
-// columns c, c + 1 (c even) -> hi/lo pair words
-__device__ __forceinline__ void put_hl2(LS u32* hl, int c, float v0, float v1) {
-  u32 h0, l0, h1, l1;
-  split_hl(v0, h0, l0);
-  split_hl(v1, h1, l1);
-  const int o = hl_word(c);
-  hl[o] = h0 | (h1 << 16);
-  hl[o + 4] = l0 | (l1 << 16);
-}
-
-// ------------------------------------------------------------------------ exchanges (polling waves)
-// Poll n records, record f at src(f); use(f, value) once its epoch matches.  Polling threads keep
-// PB loads in flight each.  Every thread calls it; streaming threads return at once.
-template <typename SrcFn, typename UseFn>
-__device__ __forceinline__ bool gather_map(const Ctx& cx, int n, SrcFn src, UseFn use) {
-  if (streamer()) return true;
-  const u32 e = cx.epoch;
-  const int pl = tid() - NCT;
-  bool ok = true;
-  for (int base = 0; ok && base < n; base += NPT * PB) {
-    u32 pending = 0;
-#pragma unroll
-    for (int k = 0; k < PB; ++k)
-      if (base + k * NPT + pl < n) pending |= 1u << k;
-    u32 spins = 0;
-    while (pending) {
-      mk_u64 v[PB];
-#pragma unroll
-      for (int k = 0; k < PB; ++k)
-        if ((pending >> k) & 1u) v[k] = ld_dev(src(base + k * NPT + pl));
-#pragma unroll
-      for (int k = 0; k < PB; ++k)
-        if (((pending >> k) & 1u) && (u32)(v[k] >> 32) == e) {
-          use(base + k * NPT + pl, __uint_as_float((u32)v[k]));
-          pending &= ~(1u << k);
-        }
-      if (pending) {
-        ++spins;
-        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
-          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
-          ok = false;
-          break;
-        }
-      }
-    }
-  }
-  // Every poll load has been used (or abandoned) by now; the wait, free here, tells the compiler
-  // so.  Loads it cannot match with a use look outstanding to it, and a later reuse of their
-  // registers would wait for all vector-memory operations, prefetch copies included.
-  wait_vm<0>();
-  return ok;
-}
-
-// Contiguous records src[0..n) -> dst[0..n), two records per 16-byte device-coherent load.  Each
-// 8-byte record is read whole (it sits in one aligned 8-byte word), so a pair is complete once
-// both halves carry the epoch.
-template <bool HL>
-__device__ __forceinline__ bool gather_vec_impl(MK_G MkCtl* ctl, u32 epoch, const MK_G mk_u64* src, int n,
-                                                LS float* dst) {
-  Ctx cx;
-  cx.ctl = uni_ptr(ctl);
-  cx.epoch = (u32)uni((int)epoch);
-  src = uni_ptr(src);
-  n = uni(n);
-  const u32 e = cx.epoch;
-  const int pl = tid() - NCT;
-  const int np = (n + 1) >> 1;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, np * 16, 0x00020000);
-  bool ok = true;
-  for (int base = 0; ok && base < np; base += NPT * PB) {
-    u32 pending = 0;
-#pragma unroll
-    for (int k = 0; k < PB; ++k)
-      if (base + k * NPT + pl < np) pending |= 1u << k;
-    u32 spins = 0;
-    while (pending) {
-      u32x4 v[PB];
-#pragma unroll
-      for (int k = 0; k < PB; ++k)
-        if ((pending >> k) & 1u)
-          v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + k * NPT + pl) * 16, 0, 16 /* sc1 */);
-#pragma unroll
-      for (int k = 0; k < PB; ++k) {
-        const int j = base + k * NPT + pl;
-        const bool two = 2 * j + 1 < n;
-        if (((pending >> k) & 1u) && v[k].y == e && (!two || v[k].w == e)) {
-          if (HL) {
-            put_hl2((LS u32*)dst, 2 * j, __uint_as_float(v[k].x), two ? __uint_as_float(v[k].z) : 0.f);
-          } else {
-            dst[2 * j] = __uint_as_float(v[k].x);
-            if (two) dst[2 * j + 1] = __uint_as_float(v[k].z);
-          }
-          pending &= ~(1u << k);
-        }
-      }
-      if (pending) {
-        ++spins;
-        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
-          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
-          ok = false;
-          break;
-        }
-      }
-    }
-  }
-  wait_vm<0>();  // as in gather_map
-  return ok;
-}
-
-__device__ __forceinline__ bool gather_vec(const Ctx& cx, const MK_G mk_u64* src, int n, LS float* dst) {
-  if (streamer()) return true;
-  return gather_vec_impl<false>(cx.ctl, cx.epoch, src, n, dst);
-}
-// the same into the GEMV activation layout (hi/lo BF16 pairs); n even
-__device__ __forceinline__ bool gather_hl(const Ctx& cx, const MK_G mk_u64* src, int n, LS u32* dst) {
-  if (streamer()) return true;
-  return gather_vec_impl<true>(cx.ctl, cx.epoch, src, n, (LS float*)dst);
-}
-// FP32 v[0..n) (n a multiple of 8) -> the GEMV activation layout in place, by all threads: each
-// group of 8 values is rewritten as its hi and lo pairs.  Between barriers.
-__device__ __forceinline__ void to_hl(LS float* v, int n) {
-  for (int gidx = tid(); gidx < (n >> 3); gidx += MK_NT) {
-    LS f32x4* p = (LS f32x4*)(v + 8 * gidx);
-    const f32x4 a = p[0], b = p[1];
-    u32 h[8], l[8];
-    split_hl(a.x, h[0], l[0]);
-    split_hl(a.y, h[1], l[1]);
-    split_hl(a.z, h[2], l[2]);
-    split_hl(a.w, h[3], l[3]);
-    split_hl(b.x, h[4], l[4]);
-    split_hl(b.y, h[5], l[5]);
-    split_hl(b.z, h[6], l[6]);
-    split_hl(b.w, h[7], l[7]);
-    LS u32x4* q = (LS u32x4*)p;
-    q[0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    q[1] = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
-  }
-}
-
-// ------------------------------------------------------------------------ GEMV
-// out[r] = W[r] . x for the R rows of a workgroup's slice (row stride K).  A unit is 4 rows x 512
-// columns (4 KB of BF16): slot k (1 KB) is row k's 512 columns, contiguous in memory, and lane l holds
-// columns 8l .. 8l+7 of all four rows, so a lane needs only its own 8 activations.  Activations are
-// kept in LDS as BF16 hi + lo pairs (x = hi + lo to about 2^-17 relative): per group of 8 columns,
-// 16 bytes of hi pairs then 16 bytes of lo pairs.  Products go through v_dot2c_f32_bf16 (exact BF16
-// products, FP32 accumulation), two per weight pair.  A unit's four row partials are reduced over the
-// wave in a fixed order (lane-half swaps, then a 16-lane DPP row sum) and parked in LDS; a row's
-// value adds its 512-column segment partials in segment order, so it does not depend on how rows
-// are split over workgroups.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-struct Gemv {
-  const MK_G uint16_t* W;
-  int R, K, S;  // rows, columns, 512-column segments
-  __device__ __forceinline__ void init(const MK_G uint16_t* W_, int R_, int K_) {
-    W = W_;
-    R = R_;
-    K = K_;
-    S = (K + 511) >> 9;
-  }
-  __device__ __forceinline__ int units() const { return ((R + 3) >> 2) * S; }
-  __device__ __forceinline__ int chunk_rows() const { return max(4, (MK_RED_CAP / S) & ~3); }
-  // this lane's 16 bytes of slot k (row 4 rb + k) of unit u; null outside the matrix
-  __device__ __forceinline__ const MK_G uint16_t* addr(int u, int k) const {
-    const int rb = u / S, s = u - rb * S;
-    const int row = rb * 4 + k;
-    const int col = s * 512 + lane() * 8;
-    return (row < R && col < K) ? W + (size_t)row * K + col : nullptr;
-  }
-  // slot k of unit u holds a row of the matrix (uniform over the wave)
-  __device__ __forceinline__ bool live(int u, int k) const { return (u / S) * 4 + k < R; }
-};
-
-// Units staged for g: the first min(units of its first row chunk, cap) units.
-__device__ __forceinline__ int staged_units(const Gemv& g, int cap) {
-  Gemv c0 = g;
-  c0.R = min(g.R, g.chunk_rows());
-  return min(c0.units(), cap);
-}
-
-// First units of g -> stage slots [4u, 4u + 4): streaming wave c copies slot c of every unit.
-// Returns the number of copies this wave issued.
-__device__ __forceinline__ int gemv_stage_impl(const MK_G uint16_t* W, int R, int K, LS u32x4* stage, int cap) {
-  Gemv g;
-  g.init(uni_ptr(W), uni(R), uni(K));
-  const int n = staged_units(g, uni(cap));
-  const int c = wave();
-  int cnt = 0;
-  for (int u = 0; u < n; ++u) {
-    if (g.live(u, c)) {
-      const MK_G uint16_t* a = g.addr(u, c);
-      if (a) dma16(a, stage + (u * USLOTS + c) * SLOT);
-      ++cnt;  // lane 0 (the segment's first 8 columns) is always inside the matrix here
-    }
-  }
-  return cnt;
-}
-
-__device__ __forceinline__ int gemv_stage(const Gemv& g, LS u32x4* stage, int cap) {
-  if (!streamer()) return 0;
-  return gemv_stage_impl(g.W, g.R, g.K, stage, cap);
-}
-
-__device__ __forceinline__ void put_partial(const Gemv& g, int u, float v, LS float* red) {
-  if ((lane() & 15) == 0) {
-    const int rb = u / g.S, s = u - rb * g.S;
-    const int row = rb * 4 + (lane() >> 4);
-    if (row < g.R) red[row * g.S + s] = v;
-  }
-}
-
-// a row's segment partials added in segment order; loads are issued eight at a time
-__device__ __forceinline__ float seg_sum(const LS float* p, int S) {
-  float v = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float t[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) t[k] = s0 + k < S ? p[s0 + k] : 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (s0 + k < S) v += t[k];
-  }
-  return v;
-}
-
-template <int N>
-struct RegUnits {
-  u32x4 c[N * USLOTS];
-};
-
-// This lane's activations for 512-column segment s: hi and lo pairs of columns s*512 + 8 lane ...
-struct XSlice {
-  u32x4 h, l;
-};
-__device__ __forceinline__ void load_x(XSlice& x, const LS u32* hl, int s, int K) {
-  const int col = s * 512 + lane() * 8;
-  x.h = u32x4{0u, 0u, 0u, 0u};
-  x.l = x.h;
-  if (col < K) {
-    const LS u32x4* p = (const LS u32x4*)(hl + (col >> 3) * 8);
-    x.h = p[0];
-    x.l = p[1];
-  }
-}
-__device__ __forceinline__ float dot2(u32 w, u32 x, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), acc, false);
-}
-// one row's 8 weights . this lane's 8 activations (hi then lo)
-__device__ __forceinline__ float dot8hl(u32x4 w, const XSlice& x) {
-  float a = dot2(w.x, x.h.x, 0.f);
-  a = dot2(w.y, x.h.y, a);
-  a = dot2(w.z, x.h.z, a);
-  a = dot2(w.w, x.h.w, a);
-  a = dot2(w.x, x.l.x, a);
-  a = dot2(w.y, x.l.y, a);
-  a = dot2(w.z, x.l.z, a);
-  return dot2(w.w, x.l.w, a);
-}
-// Four per-lane row partials -> in every lane of 16-lane row i, row i's sum over the wave: rows 0/1
-// and 2/3 trade lane halves (permlane32 swap), then rows 0/1 and 2/3 trade 16-lane rows (permlane16
-// swap), then a DPP sum within each 16-lane row.
-__device__ __forceinline__ float reduce_rows4(float a0, float a1, float a2, float a3) {
-  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a2), false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a3), false, false);
-  const float p = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-  const float q = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
-  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(q), false, false);
-  return row_sum16(__uint_as_float(t[0]) + __uint_as_float(t[1]));
-}
-// unit partial (row 4 rb + lane / 16 in 16-lane row lane / 16) from its four row slots; lanes past
-// column K add nothing (their weights were never copied)
-__device__ __forceinline__ float unit_dot_x(int s, int K, const u32x4* w, const XSlice& x) {
-  const bool in = s * 512 + lane() * 8 < K;
-  float a[USLOTS];
-#pragma unroll
-  for (int k = 0; k < USLOTS; ++k) a[k] = in ? dot8hl(w[k], x) : 0.f;
-  return reduce_rows4(a[0], a[1], a[2], a[3]);
-}
-
-// Segment-major split of a GEMV's units over a set of NWS waves (this wave is ws): with S <= NWS
-// segments, wave ws takes segment ws % S and every nj-th row block from ws / S; otherwise segments
-// ws, ws + NWS, ... with every row block.  A wave keeps its segment's activations in registers.
-struct SegPlan {
-  int s0, sstep, j, nj;
-  __device__ __forceinline__ void init(int S, int ws, int NWS) {
-    if (S <= NWS) {
-      s0 = ws % S;
-      sstep = S;
-      j = ws / S;
-      nj = (NWS - s0 + S - 1) / S;
-    } else {
-      s0 = ws;
-      sstep = NWS;
-      j = 0;
-      nj = 1;
-    }
-  }
-};
-
-// Unit partials of one row chunk -> red[row * S + segment].  Units u = rb * S + s < nst come from
-// the LDS stage (every wave), the rest stream through registers (streaming waves; ALL_STREAM: all).
-// xin: activations in hi/lo layout.
-template <bool ALL_STREAM>
-__device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int K, int nst, const LS u32* xin,
-                                              const LS u32x4* stage, LS float* red) {
-  Gemv g;
-  g.init(uni_ptr(W), uni(R), uni(K));
-  nst = uni(nst);
-  const int S = g.S, RB = (g.R + 3) >> 2;
-  {
-    SegPlan sp;
-    sp.init(S, wave(), MK_NWAVE);
-    for (int s = sp.s0; s < S; s += sp.sstep) {
-      if (sp.j * S + s >= nst) break;
-      XSlice x;
-      load_x(x, xin, s, g.K);
-      for (int rb = sp.j; rb * S + s < nst; rb += 2 * sp.nj) {
-        const int u0 = rb * S + s, u1 = (rb + sp.nj) * S + s;
-        const bool h1 = u1 < nst;
-        u32x4 w0[USLOTS], w1[USLOTS];
-        if (h1) {
-          stage_units2(stage + u0 * USLOTS * SLOT + lane(), stage + u1 * USLOTS * SLOT + lane(), w0, w1);
-        } else {
-          stage_unit(stage + u0 * USLOTS * SLOT + lane(), w0);
-#pragma unroll
-          for (int k = 0; k < USLOTS; ++k) w1[k] = u32x4{0u, 0u, 0u, 0u};
-        }
-        const float a0 = unit_dot_x(s, g.K, w0, x);
-        const float a1 = h1 ? unit_dot_x(s, g.K, w1, x) : 0.f;
-        put_partial(g, u0, a0, red);
-        if (h1) put_partial(g, u1, a1, red);
-      }
-    }
-  }
-  if (ALL_STREAM || streamer()) {
-    const int NSW = ALL_STREAM ? MK_NWAVE : NCW;
-    SegPlan sp;
-    sp.init(S, wave(), NSW);
-    for (int s = sp.s0; s < S; s += sp.sstep) {
-      // first row block of this wave's sequence whose unit is past the stage
-      int rb = sp.j;
-      if (rb * S + s < nst) rb += ((nst - s - rb * S + S - 1) / S + sp.nj - 1) / sp.nj * sp.nj;
-      if (rb >= RB) continue;
-      XSlice x;
-      load_x(x, xin, s, g.K);
-      const int step = sp.nj;
-      auto issue2 = [&](RegUnits<2>& r, int rb0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int rbi = rb0 + i * step;
-#pragma unroll
-          for (int k = 0; k < USLOTS; ++k) {
-            const MK_G uint16_t* a = rbi < RB ? g.addr(rbi * S + s, k) : nullptr;
-            r.c[i * USLOTS + k] = a ? ldw(a) : u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      };
-      RegUnits<2> cur, nxt;
-      issue2(cur, rb);
-      keep_issued();
-      for (; rb < RB; rb += 2 * step) {
-        issue2(nxt, rb + 2 * step);
-        keep_issued();
-        const bool h1 = rb + step < RB;
-        const float a0 = unit_dot_x(s, g.K, cur.c, x);
-        const float a1 = h1 ? unit_dot_x(s, g.K, cur.c + USLOTS, x) : 0.f;
-        put_partial(g, rb * S + s, a0, red);
-        if (h1) put_partial(g, (rb + step) * S + s, a1, red);
-#pragma unroll
-        for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = nxt.c[i];
-      }
-      // The last iteration's look-ahead loads are never used.  Waiting for them here, on the path
-      // that issued them, keeps them from looking outstanding afterwards, where the compiler would
-      // otherwise wait for all vector-memory operations (prefetch copies included) before reusing
-      // their registers.
-      wait_vm<0>();
-    }
-  }
-}
-
-template <bool PAIRS, bool EPI_ALL, bool ALL_STREAM, typename Epi>
-__device__ __forceinline__ void gemv(const Gemv& G, const LS u32* xin, const LS u32x4* stage, int cap,
-                                     LS float* red, Tracer& tr, Epi epi) {
-  const int rc = G.chunk_rows();
-  for (int r0 = 0; r0 < G.R; r0 += rc) {
-    Gemv g;
-    g.init(G.W + (size_t)r0 * G.K, min(rc, G.R - r0), G.K);
-    const int nst = r0 == 0 ? min(g.units(), cap) : 0;
-    gemv_partials<ALL_STREAM>(g.W, g.R, g.K, nst, xin, stage, red);
-    tr.mark();
-    wg_bar();
-    tr.mark();
-    const int stride = EPI_ALL ? MK_NT : NCT;
-    if (EPI_ALL || streamer()) {
-      if (PAIRS) {
-        for (int t = tid(); t < g.R / 2; t += stride) epi(r0 / 2 + t, seg_sum(red + (2 * t) * g.S, g.S),
-                                                          seg_sum(red + (2 * t + 1) * g.S, g.S));
-      } else {
-        for (int t = tid(); t < g.R; t += stride) epi(r0 + t, seg_sum(red + t * g.S, g.S), 0.f);
-      }
-    }
-    if (r0 + rc < G.R) wg_bar();  // red is reused by the next chunk
-  }
-}
-
-// x -> xn = x / sqrt(mean x^2 + eps) * g, written as hi/lo BF16 pairs (the GEMV activation layout).
-// Every wave sums the squares itself (same order in every wave), so only the barrier that
-// publishes xn is needed.
-__device__ __forceinline__ void rmsnorm(const LS float* x, const LS uint16_t* g, LS u32* xn, int D, float eps,
-                                        Tracer& tr) {
-  D = uni(D);
-  const int D4 = D >> 2;  // D is a multiple of 8
-  const LS f32x4* x4 = (const LS f32x4*)x;
-  // four float4 loads in flight per lane before any of them is used
-  float s = 0.f;
-  for (int c0 = lane(); c0 < D4; c0 += 256) {
-    f32x4 v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (c0 + 64 * k < D4) v[k] = x4[c0 + 64 * k];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      s = fmaf(v[k].x, v[k].x, s);
-      s = fmaf(v[k].y, v[k].y, s);
-      s = fmaf(v[k].z, v[k].z, s);
-      s = fmaf(v[k].w, v[k].w, s);
-    }
-  }
-  s = wave_sum(s);
-  const float r = 1.0f / sqrtf(s / (float)D + eps);
-  tr.mark();
-  for (int c = tid(); c < D4; c += MK_NT) {
-    const f32x4 v = x4[c];
-    const u32x2 gg = *(const LS u32x2*)(g + 4 * c);
-    u32 h[4], l[4];
-    split_hl(v.x * r * __uint_as_float(gg.x << 16), h[0], l[0]);
-    split_hl(v.y * r * __uint_as_float(gg.x & 0xffff0000u), h[1], l[1]);
-    split_hl(v.z * r * __uint_as_float(gg.y << 16), h[2], l[2]);
-    split_hl(v.w * r * __uint_as_float(gg.y & 0xffff0000u), h[3], l[3]);
-    const int o = hl_word(4 * c);  // even: columns 4c .. 4c+3 fill two hi and two lo pair words
-    *(LS u32x2*)(xn + o) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    *(LS u32x2*)(xn + o + 4) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-  }
-  tr.mark();
-  wg_bar();
-}
-
-// RMSNorm gains (BF16, n values, n a multiple of 8) -> LDS by the polling threads with plain loads:
-// issued before a poll (they complete under its latency) and stored after it.  Up to GAIN_REGS
-// 16-byte pieces per thread ride along; any remainder is copied after the poll.
-constexpr int GAIN_REGS = 2;
-struct GainCopy {
-  u32x4 r[GAIN_REGS];
-};
-__device__ __forceinline__ void gains_issue(const MK_G uint16_t* src, int n, GainCopy& gc) {
-  const int pieces = n >> 3, pl = tid() - NCT;
-#pragma unroll
-  for (int k = 0; k < GAIN_REGS; ++k) {
-    const int i = pl + k * NPT;
-    gc.r[k] = i < pieces ? *(const MK_G u32x4*)(src + 8 * i) : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-__device__ __forceinline__ void gains_store(const MK_G uint16_t* src, int n, const GainCopy& gc, LS uint16_t* dst) {
-  const int pieces = n >> 3, pl = tid() - NCT;
-#pragma unroll
-  for (int k = 0; k < GAIN_REGS; ++k) {
-    const int i = pl + k * NPT;
-    if (i < pieces) *(LS u32x4*)(dst + 8 * i) = gc.r[k];
-  }
-  for (int i = pl + GAIN_REGS * NPT; i < pieces; i += NPT) *(LS u32x4*)(dst + 8 * i) = *(const MK_G u32x4*)(src + 8 * i);
-}
-
-__device__ __forceinline__ MkLayerDev layer_desc(const LS MkLayerDev* d, int l) {
-  MkLayerDev out;
-  const LS u32* src = (const LS u32*)(d + l);
-  u32* dst = (u32*)&out;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(MkLayerDev) / 4); ++i) dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
-  return out;
-}
-
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
-__device__ __forceinline__ float softplusf_(float z) { return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z))); }
-
-// ------------------------------------------------------------------------ DeltaNet
-// state rows [s0, s1) -> stage slots: dk/4 lanes per row, 64/(dk/4) rows per slot.  Returns copies
-// issued by this wave.
-__device__ __forceinline__ int state_stage(const MkDecodeParams& p, const MkLayerDev& L, int s0, int s1,
-                                           LS u32x4* stage, int max_slots) {
-  if (!streamer()) return 0;
-  const int lpr = p.dk >> 2, rps = 64 / lpr;
-  const int nslots = min((s1 - s0 + rps - 1) / rps, max_slots);
-  int cnt = 0;
-  for (int j = wave(); j < nslots; j += NCW) {
-    const int r = s0 + j * rps + lane() / lpr;
-    if (lane() < rps * lpr && r < s1) dma16(L.S + (size_t)r * p.dk + (lane() % lpr) * 4, stage + j * SLOT);
-    ++cnt;  // the slot's first row is always in range
-  }
-  return cnt;
-}
-
-// gated delta rule on rows [s0, s1) of S; o = S q read after the update -> records.  Rows of
-// staged slots come from LDS, the rest straight from HBM.  Streaming waves own the rows.
-__device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                         int s0, int s1, int st_slots, int wait_after, Tracer& tr) {
-  const int H = p.H, dk = p.dk, dv = p.dv;
-  const int lpr = dk >> 2, rps = 64 / lpr;
-  LS float* q = s.att;
-  LS float* k = s.att + dk;
-  LS float* ab = s.att + 2 * dk;
-  LS float* vr = s.att + 2 * dk + 2;
-  const LS float* st = (const LS float*)s.stB;
-  const MK_G mk_u64* in = L.ll_in;
-  const int off_k = H * dk, off_v = 2 * H * dk, off_a = 2 * H * dk + H * dv, off_b = off_a + H;
-  bool first = true;
-  const int h0 = s0 < s1 ? s0 / dv : 0, h1 = s0 < s1 ? (s1 - 1) / dv : -1;
-  for (int h = h0; h <= h1; ++h) {
-    const int i0 = max(s0, h * dv) - h * dv, i1 = min(s1, (h + 1) * dv) - h * dv;
-    const int nv = i1 - i0;
-    const int n = 2 * dk + 2 + nv;
-    const bool ok = gather_map(cx, n, [=](int f) {
-      if (f < dk) return in + h * dk + f;
-      if (f < 2 * dk) return in + off_k + h * dk + (f - dk);
-      if (f == 2 * dk) return in + off_a + h;
-      if (f == 2 * dk + 1) return in + off_b + h;
-      return in + off_v + h * dv + i0 + (f - 2 * dk - 2);
-    }, [=](int f, float v) { s.att[f] = v; });
-    tr.mark();
-    if (first && streamer()) wait_vm_n(wait_after);  // the staged state rows
-    first = false;
-    tr.mark();
-    if (wg_bar_or(s, !ok)) return false;
-    tr.mark();
-    if (streamer()) {
-      float qq = 0.f, kk = 0.f;
-      for (int e = lane(); e < dk; e += 64) {
-        qq = fmaf(q[e], q[e], qq);
-        kk = fmaf(k[e], k[e], kk);
-      }
-      qq = wave_sum(qq);
-      kk = wave_sum(kk);
-      const float sq = 1.0f / sqrtf(qq + p.l2_eps);
-      const float sk = 1.0f / sqrtf(kk + p.l2_eps);
-      const float alpha = expf(-softplusf_(ab[0]));
-      const float beta = sigmoidf_(ab[1]);
-      // rows of head h, local index li = row - s0, owned by streaming wave li % NCW
-      const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
-      // Two copies of the row loop: when every row of this head is staged the loop issues no global
-      // load, so the compiler has no reason to wait on the vector-memory counter inside it -- a
-      // wait there would also wait for the previous row's state stores and record store.
-      auto rows = [&](auto staged_tag) {
-        constexpr bool STAGED = decltype(staged_tag)::value;
-        for (int li = lo + ((wave() - lo % NCW) + NCW) % NCW; li < hi; li += NCW) {
-          const int row = s0 + li;
-          const int sl = li / rps;
-          const LS float* srow = st + sl * 256 + (li % rps) * dk;
-          float sr[4];
-          if (STAGED) {
-            const int l0 = lane();
-            stage_f32x4(srow + l0, srow + (l0 + 64 < dk ? l0 + 64 : 0), srow + (l0 + 128 < dk ? l0 + 128 : 0),
-                        srow + (l0 + 192 < dk ? l0 + 192 : 0), sr);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (lane() + 64 * t >= dk) sr[t] = 0.f;
-          } else {
-            const bool staged = sl < st_slots;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int e = lane() + 64 * t;
-              sr[t] = e < dk ? (staged ? srow[e] : L.S[(size_t)row * dk + e]) : 0.f;
-            }
-          }
-          float kd = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int e = lane() + 64 * t;
-            if (e < dk) kd = fmaf(sr[t], k[e] * sk, kd);
-          }
-          kd = wave_sum(kd);
-          const float u = beta * (vr[row - h * dv - i0] - alpha * kd);
-          float od = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int e = lane() + 64 * t;
-            if (e < dk) {
-              const float nv2 = fmaf(u, k[e] * sk, alpha * sr[t]);
-              L.S[(size_t)row * dk + e] = nv2;
-              od = fmaf(nv2, q[e] * sq, od);
-            }
-          }
-          od = wave_sum(od);
-          if (lane() == 0) ll_put(L.ll_o + row, cx.epoch, od);
-        }
-      };
-      if (lo >= hi || (hi - 1) / rps < st_slots) rows(std::true_type{});
-      else rows(std::false_type{});
-    }
-    tr.mark();
-    wg_bar();  // s.att is reused by the next head
-  }
-  if (first && streamer()) wait_vm_n(wait_after);
-  return true;
-}
-
-// ------------------------------------------------------------------------ attention
-// K and V rows of work item `it` (16 positions of one KV head) -> stage slots [0, ks) (K) and
-// [ks, 2 ks) (V); hd/4 lanes per position.  Only positions already in the cache (< pos) are
-// copied; position pos comes from the exchange records.  Returns copies issued by this wave.
-__device__ __forceinline__ int kv_slots(int hd) {
-  const int pps = 64 / (hd >> 2);
-  return (ATT_C + pps - 1) / pps;
-}
-__device__ __forceinline__ int kv_stage(const MkDecodeParams& p, const MkLayerDev& L, int it, int pos,
-                                        LS u32x4* stage) {
-  if (!streamer()) return 0;
-  const int lpp = p.hd >> 2, pps = 64 / lpp, ks = kv_slots(p.hd);
-  const int c = it / p.nkv, g = it - c * p.nkv;
-  const int j0 = c * ATT_C, jend = min(pos, j0 + ATT_C);
-  int cnt = 0;
-  for (int q = wave(); q < 2 * ks; q += NCW) {
-    const int v = q >= ks ? 1 : 0;
-    const int sl = q - v * ks;
-    const int j = j0 + sl * pps + lane() / lpp;
-    if (lane() < pps * lpp && j < jend)
-      dma16((v ? L.Vc : L.Kc) + ((size_t)g * p.max_ctx + j) * p.hd + (lane() % lpp) * 4, stage + q * SLOT);
-    if (j0 + sl * pps < jend) ++cnt;
-  }
-  return cnt;
-}
-
-// q/k/v rows in RoPE pair order: rotate q and k at position pos, append k and v to the cache
-__device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                        const Gemv& g, int P0, int pos, Tracer& tr) {
-  const int hd = p.hd, half = hd / 2;
-  MK_G mk_u64* llq = L.ll_in;
-  MK_G mk_u64* llk = L.ll_in + p.nq * hd;
-  MK_G mk_u64* llv = llk + p.nkv * hd;
-  const int nqp = p.nq * half, nkp = p.nkv * half;
-  gemv<true, false, false>(g, s.xn, s.stA, A_UNITS, s.att, tr, [&](int pl, float x1, float x2) {
-    const int P = P0 + pl;
-    if (P < nqp + nkp) {
-      const bool isq = P < nqp;
-      const int Q = isq ? P : P - nqp;
-      const int hh = Q / half, m = Q - hh * half;
-      const float c = s.rope[m], sv = s.rope[half + m];
-      const float y1 = x1 * c - x2 * sv;
-      const float y2 = x2 * c + x1 * sv;
-      if (isq) {
-        ll_put(llq + hh * hd + m, cx.epoch, y1);
-        ll_put(llq + hh * hd + m + half, cx.epoch, y2);
-      } else {
-        const size_t co = ((size_t)hh * p.max_ctx + pos) * hd + m;
-        ll_put(llk + hh * hd + m, cx.epoch, y1);
-        ll_put(llk + hh * hd + m + half, cx.epoch, y2);
-        L.Kc[co] = y1;
-        L.Kc[co + half] = y2;
-      }
-    } else {
-      const int Q = P - nqp - nkp;
-      const int hh = Q / half, m = Q - hh * half;
-      const size_t co = ((size_t)hh * p.max_ctx + pos) * hd + m;
-      ll_put(llv + hh * hd + m, cx.epoch, x1);
-      ll_put(llv + hh * hd + m + half, cx.epoch, x2);
-      L.Vc[co] = x1;
-      L.Vc[co + half] = x2;
-    }
-  });
-}
-
-// Split-K partial softmax attention.  Item = (chunk of 16 positions, KV head g); for each of the
-// gs query heads of group g it emits (max m, sum l, acc[hd]) over its positions.  Scores: one thread
-// per (head, position), a 16-lane DPP row per head for the max and the sum.
-__device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                          int NW, int w, int pos, int wait_first, Tracer& tr) {
-  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv;
-  const int Lpos = pos + 1;
-  const int items = ((Lpos + ATT_C - 1) / ATT_C) * nkv;
-  const float scale = 1.0f / sqrtf((float)hd);
-  const int lpp = hd >> 2, pps = 64 / lpp, ks = kv_slots(hd);
-  LS float* qv = s.att;                // [gs][hd]
-  LS float* kpos = qv + gs * hd;       // [hd]
-  LS float* vpos = kpos + hd;          // [hd]
-  LS float* pb = vpos + hd;            // [gs][16] probabilities (unnormalised)
-  LS float* ml = pb + gs * ATT_C;      // [gs][2]
-  const LS float* stf = (const LS float*)s.stB;
-  const MK_G mk_u64* llq = L.ll_in;
-  const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
-  const MK_G mk_u64* llv = llk + nkv * hd;
-  (void)lpp;
-  for (int it = w; it < items; it += NW) {
-    const int c = it / nkv, g = it - c * nkv;
-    const int j0 = c * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
-    const bool has_pos = j0 + nj == Lpos;
-    if (it != w) kv_stage(p, L, it, pos, s.stB);
-    const int n = gs * hd + (has_pos ? 2 * hd : 0);
-    const bool ok = gather_map(cx, n, [=](int f) {
-      if (f < gs * hd) return llq + g * gs * hd + f;
-      if (f < gs * hd + hd) return llk + g * hd + (f - gs * hd);
-      return llv + g * hd + (f - gs * hd - hd);
-    }, [=](int f, float v) { s.att[f] = v; });
-    tr.mark();
-    if (streamer()) {
-      if (it == w) wait_vm_n(wait_first);
-      else wait_vm<0>();
-    }
-    tr.mark();
-    if (wg_bar_or(s, !ok)) return false;
-    tr.mark();
-    // scores, softmax numerators, row max and sum (whole rows of 16 lanes take part in the DPP)
-    const int t = tid();
-    if (t < gs * ATT_C) {
-      const int i = t >> 4, jj = t & 15;
-      const bool valid = jj < nj;
-      float sc = -INFINITY;
-      if (valid) {
-        const int j = j0 + jj;
-        const LS float* kr = j == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
-        const LS float* qr = qv + i * hd;
-        const int n4 = hd >> 2;
-        const int start = jj % n4;  // staggered start: the 16 positions of a row read different banks
-        float a = 0.f;
-        for (int d0 = 0; d0 < n4; d0 += 8) {
-          f32x4 kk[8], qq[8];
-          const LS float* ka[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            int dd = d0 + k + start;
-            dd = (dd >= n4 ? dd - n4 : dd) * 4;
-            ka[k] = kr + (d0 + k < n4 ? dd : 0);
-            qq[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (d0 + k < n4) qq[k] = *(const LS f32x4*)(qr + dd);
-          }
-          stage_f4x8(ka, kk);
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (d0 + k >= n4) kk[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            a = fmaf(kk[k].x, qq[k].x, a);
-            a = fmaf(kk[k].y, qq[k].y, a);
-            a = fmaf(kk[k].z, qq[k].z, a);
-            a = fmaf(kk[k].w, qq[k].w, a);
-          }
-        }
-        sc = a * scale;
-      }
-      const float m = row_max16(sc);
-      const float e = valid ? expf(sc - m) : 0.f;
-      const float l = row_sum16(e);
-      pb[i * ATT_C + jj] = e;
-      if (jj == 0) {
-        ml[2 * i] = m;
-        ml[2 * i + 1] = l;
-      }
-    }
-    tr.mark();
-    wg_bar();
-    tr.mark();
-    if (streamer()) {
-      MK_G mk_u64* part = L.ll_part + (size_t)it * gs * (hd + 2);
-      for (int o = tid(); o < gs * hd; o += NCT) {
-        const int i = o / hd, d = o - i * hd;
-        float pv[ATT_C], vv[ATT_C];
-        const LS float* va[ATT_C];
-#pragma unroll
-        for (int jj = 0; jj < ATT_C; ++jj) {
-          pv[jj] = pb[i * ATT_C + jj];  // zero beyond nj
-          va[jj] = (jj < nj && j0 + jj != pos) ? stf + (ks + jj / pps) * 256 + (jj % pps) * hd + d : vpos + d;
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < ATT_C; q4 += 4) {
-          float t4[4];
-          stage_f32x4(va[q4], va[q4 + 1], va[q4 + 2], va[q4 + 3], t4);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) vv[q4 + k] = q4 + k < nj ? t4[k] : 0.f;
-        }
-        float a = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < ATT_C; ++jj) a = fmaf(pv[jj], vv[jj], a);
-        ll_put(part + i * (hd + 2) + 2 + d, cx.epoch, a);
-      }
-      if (tid() < 2 * gs) ll_put(part + (tid() >> 1) * (hd + 2) + (tid() & 1), cx.epoch, ml[tid()]);
-    }
-    wg_bar();  // LDS and the KV slots are reused by the next item
-  }
-  if (w >= items && streamer()) wait_vm_n(wait_first);
-  return true;
-}
-
-// log-sum-exp merge (in chunk order) of the partials for o[o0..o1) -> records
-__device__ __forceinline__ bool att_combine(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                            int o0, int o1, int pos) {
-  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv;
-  const int nch = (pos + ATT_C) / ATT_C;
-  const int nown = o1 - o0;
-  if (nown <= 0) return true;
-  LS float* stage = s.att;
-  const int vpp = max(1, MK_RED_CAP / (3 * nch));
-  const MK_G mk_u64* part = L.ll_part;
-  for (int v0 = 0; v0 < nown; v0 += vpp) {
-    const int vn = min(vpp, nown - v0);
-    const int n = vn * nch * 3;
-    const bool ok = gather_map(cx, n, [=](int f) {
-      const int which = f % 3;
-      const int vc = f / 3;
-      const int v = vc / nch, c = vc - v * nch;
-      const int fo = o0 + v0 + v;
-      const int i = fo / hd, d = fo - i * hd;
-      const int g = i / gs, il = i - g * gs;
-      const MK_G mk_u64* rec = part + ((size_t)(c * nkv + g) * gs + il) * (hd + 2);
-      return rec + (which == 2 ? 2 + d : which);
-    }, [=](int f, float v) { stage[f] = v; });
-    if (wg_bar_or(s, !ok)) return false;
-    if (streamer()) {
-      // a wave per output: lanes over chunks, then wave reductions (fixed order)
-      for (int v = wave(); v < vn; v += NCW) {
-        const LS float* base = stage + (size_t)v * nch * 3;
-        float M = -INFINITY;
-        for (int c = lane(); c < nch; c += 64) M = fmaxf(M, base[3 * c]);
-        M = wave_max(M);
-        float num = 0.f, den = 0.f;
-        for (int c = lane(); c < nch; c += 64) {
-          const float e = expf(base[3 * c] - M);
-          den = fmaf(e, base[3 * c + 1], den);
-          num = fmaf(e, base[3 * c + 2], num);
-        }
-        num = wave_sum(num);
-        den = wave_sum(den);
-        if (lane() == 0) ll_put(L.ll_o + o0 + v0 + v, cx.epoch, num / den);
-      }
-    }
-    wg_bar();
-  }
-  return true;
-}
-
-// pair range [p0, p1) of the workgroup over the (R + 1) / 2 row pairs of a matrix
-__device__ __forceinline__ void pair_range(int R, int NW, int w, int& p0, int& p1) {
-  const int np = (R + 1) / 2;
-  p0 = split(np, NW, w);
-  p1 = split(np, NW, w + 1);
-}
 
 // ------------------------------------------------------------------------------------------
 // the megakernel.  The body is compiled once per model shape it is specialised for (every size a

@@ -38,6 +38,8 @@ typedef unsigned long long mk_u64;
 #define PF_SPLITK_FLOATS ((size_t)256 * 128 * 128)
 // Largest grid the exchange buffers are sized for.
 #define MK_MAX_GRID 1024
+// Positions one speculative-verify launch scores (the pending token and up to 5 drafts).
+#define MK_VERIFY_MAXT 6
 
 // Device-resident control block (first 256 bytes of the workspace).
 struct MkCtl {
@@ -68,6 +70,7 @@ struct MkLayerDev {
   MK_G mk_u64* ll_x1;            // residual after the mixer [D]
   MK_G mk_u64* ll_h;             // FFN hidden [ffn]
   MK_G mk_u64* ll_x2;            // residual after the FFN [D]
+  MK_G float* Ssnap;             // verify only: DeltaNet state after position t at Ssnap + t * snap_stride
 };
 
 struct MkDecodeParams {
@@ -92,6 +95,15 @@ struct MkDecodeParams {
   // LDS carve (float offsets) and size
   int32_t lds_desc, lds_gain, lds_rope, lds_x, lds_xn, lds_vec, lds_att, lds_scr, lds_flag, lds_trace;
   int32_t lds_floats;
+  // speculative verify (layers then points at the verify descriptors, whose records hold
+  // MK_VERIFY_MAXT positions: [t][n] for every record vector of n values)
+  int32_t nt;                    // positions scored: the pending token and nt - 1 drafts
+  int32_t vec_floats;            // floats of the LDS vector region
+  int64_t snap_stride;           // floats between DeltaNet state snapshots of consecutive positions
+  MK_G const int32_t* vtok;      // [nt] device tokens
+  MK_G int32_t* vout;            // [nt] greedy choice after each position
+  MK_G int32_t* vacc;            // accepted drafts
+  MK_G mk_u64* ll_acc;           // accepted-count record
 };
 
 #ifdef __cplusplus
@@ -99,6 +111,8 @@ extern "C" {
 #endif
 // Launchers implemented in the .hip files (host side).
 int mk_launch_decode(const MkDecodeParams* p, int n_wg, void* stream);
+int mk_launch_verify(const MkDecodeParams* p, int n_wg, void* stream);
+int mk_verify_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
 int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_perm, int64_t rows,
                            int64_t cols, void* stream);
 int mk_launch_zero(void* dst, int64_t bytes, void* stream);

@@ -51,7 +51,9 @@ enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4 };
 /* Model shape.  All fields are required (there is no default constructor on purpose).
  * Constraints checked by mk_workspace_bytes / mk_create: every size > 0; hidden, ffn, H*dk and
  * H*dv multiples of 8; dk, dv even and head_dim a multiple of 4, all <= 256; n_q_heads a multiple of n_kv_heads;
- * attn_slot < period; tied_embeddings == 1; weight_dtype == MK_BF16; kv_dtype == MK_F32. */
+ * attn_slot < period; tied_embeddings == 1; weight_dtype == MK_BF16; kv_dtype == MK_F32;
+ * 0 <= max_verify_k <= 5 (each unit adds one position's records, one DeltaNet state snapshot and
+ * LDS; mk_create returns MK_E_OCCUPANCY if the verify kernel's LDS does not fit). */
 typedef struct {
   int32_t n_layers, hidden, ffn, vocab;
   int32_t period, attn_slot;                       /* attention layers: l % period == attn_slot */
@@ -59,7 +61,7 @@ typedef struct {
   int32_t n_q_heads, n_kv_heads, head_dim;         /* grouped-query attention                   */
   int32_t tied_embeddings, weight_dtype, kv_dtype;
   int32_t max_ctx;                                 /* positions the KV cache holds              */
-  int32_t max_verify_k;                            /* drafts per mk_verify_k call (0 = none)    */
+  int32_t max_verify_k;                            /* drafts per mk_verify_k call, 0..5 (0 = none) */
   float rms_eps, l2_eps, rope_theta;
 } mk_config;
 
@@ -115,8 +117,20 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
  * MK_E_CTX_FULL (checked against the host's count of enqueued positions). */
 int mk_decode_step(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_logits);
 
-/* Speculative verify: score [pending, d1..dk] (d_tokens[0..k]) and accept the longest prefix of
- * drafts that equals the greedy choices.  Not built yet: returns MK_E_UNSUPPORTED. */
+/* Speculative verify as ONE kernel launch (Reddit follow-up on the 27B model, speculative-decoding
+ * paragraph: several drafted tokens checked per pass, the main model's greedy output kept exactly).
+ * d_tokens[0..k] = [pending, d1..dk] (device int32; the pending token is the last greedy choice, not
+ * yet fed).  The launch runs positions pos .. pos+k and writes the greedy choice after each to
+ * d_out[0..k] (device int32 [k+1]); a = the number of leading drafts with d_i == d_out[i-1] goes to
+ * d_n_accepted[0].  The sequence keeps [pending, d1..da]: the position advances by a + 1 and the
+ * DeltaNet states and KV cache are exactly those of a + 1 decode steps; d_out[0..a] are the tokens
+ * to emit and d_out[a] is the next pending token.  Every choice equals, bit for bit, the one
+ * mk_decode_step makes at that position with the same grid size.
+ * Requires a context created with max_verify_k >= 1 and 0 <= k <= max_verify_k (MK_E_INVALID
+ * otherwise); MK_E_CTX_FULL if k + 1 positions do not fit; a draft id outside [0, vocab) is
+ * reported by the next mk_sync (MK_E_INVALID) and nothing is written.  Afterwards the host learns
+ * the accepted count only through d_n_accepted; the next mk_prefill, mk_get_position or
+ * full-context check synchronises to read the device's position. */
 int mk_verify_k(mk_ctx* ctx, const int32_t* d_tokens, int32_t k, int32_t* d_out, int32_t* d_n_accepted);
 
 /* Position 0, zero DeltaNet states and KV cache (weights kept).  Enqueued on the stream. */
