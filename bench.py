@@ -207,6 +207,61 @@ def energy_leg(m, prompt, tok, n_steps: int) -> dict:
             "counter": "amdsmi energy accumulator, whole board"}
 
 
+def verify_leg(cfg, W, m_dec, prompt, tok, k: int, n_launch: int) -> dict:
+    """mk_verify_k timing at the decode workload: the pending token and k drafts per launch, after the
+    512-token prompt.  Greedy drafts are the model's own continuation (from decode launches), so every
+    launch accepts all k; random drafts are almost always rejected.  Tokens are prepared on the
+    device before the timed loop, so the launches run back to back."""
+    import torch
+    from hybrid_deltanet_attention_amd import Model
+    dev = torch.device("cuda:0")
+    # greedy continuation g[0..]: g[0] is the pending token after the prompt
+    m_dec.mk_reset()
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    m_dec.mk_prefill(prompt[:PROMPT], PROMPT, nxt)
+    n_g = (k + 1) * n_launch
+    g = torch.zeros(n_g, dtype=torch.int32, device=dev)
+    g[0:1].copy_(nxt)
+    for i in range(1, n_g):
+        m_dec.mk_decode_step(g[i - 1:i], g[i:i + 1])
+    m_dec.mk_sync()
+    mv = Model(cfg, device=0, max_verify_k=k)
+    mv.mk_load_weights(W)
+    stream = mv.stream
+    out = torch.zeros((n_launch, k + 1), dtype=torch.int32, device=dev)
+    acc = torch.zeros(n_launch, dtype=torch.int32, device=dev)
+    rnd = torch.tensor(np.random.default_rng([SEED, 2]).integers(0, cfg.vocab, size=(n_launch, k + 1)),
+                       dtype=torch.int32, device=dev)
+    res = {}
+    for label, src in (("greedy_drafts", None), ("random_drafts", rnd)):
+        mv.mk_reset()
+        mv.mk_prefill(prompt[:PROMPT], PROMPT, nxt)
+        for i in range(2):  # warm-up launches, then back to the prompt's end
+            mv.mk_verify_k(g[0:k + 1], k, out[0], acc[0:1])
+        mv.mk_reset()
+        mv.mk_prefill(prompt[:PROMPT], PROMPT, nxt)
+        mv.mk_sync()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
+        torch.cuda.synchronize()
+        for i in range(n_launch):
+            toks = g[i * (k + 1):(i + 1) * (k + 1)] if src is None else src[i]
+            ev[i][0].record(stream)
+            mv.mk_verify_k(toks, k, out[i], acc[i:i + 1])
+            ev[i][1].record(stream)
+        mv.mk_sync()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        region = ev[0][0].elapsed_time(ev[-1][1]) / 1e3
+        a = acc.cpu().numpy()
+        emitted = int((a + 1).sum())
+        res[label] = {"us_per_launch": round(us, 2), "mean_accepted": round(float(a.mean()), 3),
+                      "tok_per_s": round(emitted / region, 1), "launches": n_launch}
+        if src is None:
+            res[label]["all_accepted"] = bool((a == k).all())
+    mv.close()
+    return {"k": k, "positions_per_launch": k + 1, "context": f"after the {PROMPT}-token prompt", **res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +270,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the pp520 prefill timing (profiling runs)")
     ap.add_argument("--config", default="hybrid_0p8b")
+    ap.add_argument("--verify-k", type=int, default=5, help="drafts per mk_verify_k launch in the verify leg; 0 skips it")
     ap.add_argument("--energy-steps", type=int, default=1280,
                     help="decode steps of the energy (tok/J) leg; 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -322,6 +378,10 @@ def main():
                                               "unit": "tok/s", "ms": round(pp_s * 1e3, 3)},
         "launches_per_token": 1,
     }
+    if args.verify_k > 0:
+        out["verify"] = verify_leg(cfg, W, m, prompt, tok, args.verify_k, 64)
+        out["verify"]["decode_us_per_launch"] = round(avg_launch * 1e6, 2)
+        print(f"[bench] verify: {out['verify']}", file=sys.stderr, flush=True)
     if args.energy_steps > 0:
         n_e = min(args.energy_steps, cfg.max_ctx - PROMPT)
         out["energy"] = energy_leg(m, prompt, tok, n_e)

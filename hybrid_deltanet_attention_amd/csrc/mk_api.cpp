@@ -273,13 +273,14 @@ void lds_layout_verify(const mk_config& c, int grid, MkDecodeParams& p) {
   p.lds_gain = take(D);  // BF16 [2][D]
   p.lds_rope = take(vt * hd);
   p.lds_x = take((int64_t)vt * D);
-  p.lds_xn = -1;  // shares the vector region
   p.lds_vec = take(vec);
   p.vec_floats = (int32_t)((vec + 3) / 4 * 4);
   p.lds_att = take(MK_RED_CAP);
   p.lds_scr = take(2 * MK_VERIFY_MAXT * MK_NWAVE);
   p.lds_flag = take(4);
-  p.lds_trace = take(MK_VERIFY_MAXT);  // the tokens
+  p.lds_xn = take(MK_VERIFY_MAXT);  // the tokens (the normalised activations share the vector region)
+  o = (o + 1) / 2 * 2;
+  p.lds_trace = take(2 * MK_TRACE_EVENTS);
   p.lds_floats = o;
 }
 
@@ -506,7 +507,6 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
     v.ll_am = (mk_u64*)(ctx->ws + lay.v_am);
     v.ll_acc = (mk_u64*)(ctx->ws + lay.v_acc);
     v.snap_stride = lay.snap_stride;
-    v.trace = nullptr;
     lds_layout_verify(*cfg, ctx->grid, v);
     const int vbytes = v.lds_floats * 4;
     if (vbytes > (int)prop.sharedMemPerBlock || mk_verify_max_blocks_per_cu(&v, vbytes) < 1) {
@@ -839,6 +839,7 @@ int mk_set_trace(mk_ctx* ctx, void* d_trace, size_t bytes) {
   if (d_trace && bytes < (size_t)ctx->grid * MK_TRACE_EVENTS * 8)
     return fail(ctx, MK_E_INVALID, "trace buffer needs grid * " + std::to_string(MK_TRACE_EVENTS) + " * 8 bytes");
   ctx->base.trace = (unsigned long long*)d_trace;
+  ctx->vbase.trace = (unsigned long long*)d_trace;
   return MK_OK;
 }
 

@@ -273,20 +273,15 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
     const bool ok = gather_vec(cx, p.ll_am, 2 * NW, s.vec);
     if (wg_bar_or(s, !ok)) return;
   }
-  if (tid() == 0) {
-    float b = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = 0; i < NW; ++i) {
-      const float ob = s.vec[2 * i];
-      const int oi = __float_as_int(s.vec[2 * i + 1]);
-      if (ob > b || (ob == b && oi < bi)) {
-        b = ob;
-        bi = oi;
-      }
+  if (wave() == 0) {
+    float b;
+    int bi;
+    wave_argmax(s.vec, NW, b, bi);
+    if (lane() == 0) {
+      p.next[0] = bi;
+      p.ctl->pos = pos + 1;
+      p.ctl->step = cx.epoch + 1u;
     }
-    p.next[0] = bi;
-    p.ctl->pos = pos + 1;
-    p.ctl->step = cx.epoch + 1u;
   }
   tr.mark();
   tr.flush();

@@ -1129,6 +1129,31 @@ __device__ __forceinline__ bool att_combine(const MkDecodeParams& p, const MkLay
   return true;
 }
 
+// Argmax over n (value, index) pairs rec[2i], rec[2i+1] (index as float bits) by one wave: the
+// largest value, the lowest index among equal values -- a total order, so the winner does not
+// depend on how the pairs are split over lanes.  The result is in every lane.
+__device__ __forceinline__ void wave_argmax(const LS float* rec, int n, float& b, int& bi) {
+  b = -INFINITY;
+  bi = 0x7fffffff;
+  for (int i = lane(); i < n; i += 64) {
+    const float ob = rec[2 * i];
+    const int oi = __float_as_int(rec[2 * i + 1]);
+    if (ob > b || (ob == b && oi < bi)) {
+      b = ob;
+      bi = oi;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ob = __shfl_xor(b, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (ob > b || (ob == b && oi < bi)) {
+      b = ob;
+      bi = oi;
+    }
+  }
+}
+
 // pair range [p0, p1) of the workgroup over the (R + 1) / 2 row pairs of a matrix
 __device__ __forceinline__ void pair_range(int R, int NW, int w, int& p0, int& p1) {
   const int np = (R + 1) / 2;

@@ -30,17 +30,195 @@
 namespace {
 
 constexpr int VT = MK_VERIFY_MAXT;
+constexpr int PBV = 16;  // poll loads in flight per thread in the verify gathers
+
+// The verify kernel prefetches nothing into LDS, so all 512 threads poll, PBV loads each (the
+// decode kernel's gathers use its 256 polling threads, 8 loads each): the nt-position record
+// vectors are gathered in about as few memory round trips as the decode kernel's single-position
+// ones.  (Keeping polls off the waves that store, as the decode kernel does, measured slower here:
+// the extra poll rounds and the halved row parallelism cost more than the store waits they save.)
+// Same contracts as gather_map / gather_vec / gather_hl.
+template <typename SrcFn, typename UseFn>
+__device__ __forceinline__ bool gather_map_all(const Ctx& cx, int n, SrcFn src, UseFn use) {
+  const u32 e = cx.epoch;
+  const int pl = tid();
+  bool ok = true;
+  for (int base = 0; ok && base < n; base += MK_NT * PBV) {
+    u32 pending = 0;
+#pragma unroll
+    for (int k = 0; k < PBV; ++k)
+      if (base + k * MK_NT + pl < n) pending |= 1u << k;
+    // record addresses once per round, not per poll
+    const MK_G mk_u64* ad[PBV];
+#pragma unroll
+    for (int k = 0; k < PBV; ++k) ad[k] = ((pending >> k) & 1u) ? src(base + k * MK_NT + pl) : nullptr;
+    u32 spins = 0;
+    while (pending) {
+      mk_u64 v[PBV];
+#pragma unroll
+      for (int k = 0; k < PBV; ++k)
+        if ((pending >> k) & 1u) v[k] = ld_dev(ad[k]);
+#pragma unroll
+      for (int k = 0; k < PBV; ++k)
+        if (((pending >> k) & 1u) && (u32)(v[k] >> 32) == e) {
+          use(base + k * MK_NT + pl, __uint_as_float((u32)v[k]));
+          pending &= ~(1u << k);
+        }
+      if (pending) {
+        ++spins;
+        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
+          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
+          ok = false;
+          break;
+        }
+      }
+    }
+  }
+  wait_vm<0>();
+  return ok;
+}
+
+template <bool HL>
+__device__ __forceinline__ bool gather_vec_all(const Ctx& cx, const MK_G mk_u64* src, int n, LS float* dst) {
+  src = uni_ptr(src);
+  n = uni(n);
+  const u32 e = cx.epoch;
+  const int pl = tid();
+  const int np = (n + 1) >> 1;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, np * 16, 0x00020000);
+  bool ok = true;
+  for (int base = 0; ok && base < np; base += MK_NT * PBV) {
+    u32 pending = 0;
+#pragma unroll
+    for (int k = 0; k < PBV; ++k)
+      if (base + k * MK_NT + pl < np) pending |= 1u << k;
+    u32 spins = 0;
+    while (pending) {
+      u32x4 v[PBV];
+#pragma unroll
+      for (int k = 0; k < PBV; ++k)
+        if ((pending >> k) & 1u)
+          v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + k * MK_NT + pl) * 16, 0, 16 /* sc1 */);
+#pragma unroll
+      for (int k = 0; k < PBV; ++k) {
+        const int j = base + k * MK_NT + pl;
+        const bool two = 2 * j + 1 < n;
+        if (((pending >> k) & 1u) && v[k].y == e && (!two || v[k].w == e)) {
+          if (HL) {
+            put_hl2((LS u32*)dst, 2 * j, __uint_as_float(v[k].x), two ? __uint_as_float(v[k].z) : 0.f);
+          } else {
+            dst[2 * j] = __uint_as_float(v[k].x);
+            if (two) dst[2 * j + 1] = __uint_as_float(v[k].z);
+          }
+          pending &= ~(1u << k);
+        }
+      }
+      if (pending) {
+        ++spins;
+        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
+          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
+          ok = false;
+          break;
+        }
+      }
+    }
+  }
+  wait_vm<0>();
+  return ok;
+}
+
+// RMSNorm of nt residuals x[t] -> xn[t] (hi/lo BF16 pairs).  Wave t forms position t's sum of
+// squares exactly as every wave of the decode kernel's rmsnorm does; then all threads scale.
+// Ends with a barrier.
+__device__ __forceinline__ void rmsnorm_v(const LS float* x, const LS uint16_t* g, LS u32* xn, int D, float eps,
+                                          int nt, LS float* rs) {
+  D = uni(D);
+  const int D4 = D >> 2;
+  if (wave() < nt) {
+    const LS f32x4* x4 = (const LS f32x4*)(x + wave() * D);
+    float s = 0.f;
+    for (int c0 = lane(); c0 < D4; c0 += 256) {
+      f32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c0 + 64 * k < D4) v[k] = x4[c0 + 64 * k];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s = fmaf(v[k].x, v[k].x, s);
+        s = fmaf(v[k].y, v[k].y, s);
+        s = fmaf(v[k].z, v[k].z, s);
+        s = fmaf(v[k].w, v[k].w, s);
+      }
+    }
+    s = wave_sum(s);
+    if (lane() == 0) rs[wave()] = 1.0f / sqrtf(s / (float)D + eps);
+  }
+  wg_bar();
+  for (int i = tid(); i < nt * D4; i += MK_NT) {
+    const int t = i / D4, c = i - t * D4;
+    const float r = rs[t];
+    const f32x4 v = ((const LS f32x4*)(x + t * D))[c];
+    const u32x2 gg = *(const LS u32x2*)(g + 4 * c);
+    u32 h[4], l[4];
+    split_hl(v.x * r * __uint_as_float(gg.x << 16), h[0], l[0]);
+    split_hl(v.y * r * __uint_as_float(gg.x & 0xffff0000u), h[1], l[1]);
+    split_hl(v.z * r * __uint_as_float(gg.y << 16), h[2], l[2]);
+    split_hl(v.w * r * __uint_as_float(gg.y & 0xffff0000u), h[3], l[3]);
+    LS u32* xo = xn + t * D;
+    const int o = hl_word(4 * c);
+    *(LS u32x2*)(xo + o) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *(LS u32x2*)(xo + o + 4) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  }
+  wg_bar();
+}
 
 // GEMV over nt activation vectors (position t's at xin + t * xs words, hi/lo layout).  Every wave
 // streams its units from HBM through registers (two units of look-ahead) and applies each to all
 // nt vectors.  A row's value at a position is the same sum, in the same order, as the decode
 // kernel's GEMV forms.  The streaming threads then call epi(row, t, v, 0) or, with PAIRS,
 // epi(pair, t, v_even_row, v_odd_row).
+//
+// A wave's first two units can be loaded ahead with gemv_v_pre, before the exchange that delivers
+// the GEMV's input, so that their HBM latency runs under the exchange (the loads have no address
+// dependence on the input).  gemv_v then starts from them.
+struct GemvPre {
+  RegUnits<2> r;
+};
+
+// rows of one chunk: the unit partials of all nt positions fit MK_RED_CAP
+__device__ __forceinline__ int gemv_v_rows(int S, int nt) { return max(4, (MK_RED_CAP / (S * nt)) & ~3); }
+
+__device__ __forceinline__ void gemv_v_issue2(const Gemv& g, int RB, int s, int step, RegUnits<2>& r, int rb0) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rbi = rb0 + i * step;
+#pragma unroll
+    for (int k = 0; k < USLOTS; ++k) {
+      const MK_G uint16_t* a = rbi < RB ? g.addr(rbi * g.S + s, k) : nullptr;
+      r.c[i * USLOTS + k] = a ? ldw(a) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void gemv_v_pre(const Gemv& G, int nt, GemvPre& pre) {
+  const int S = uni(G.S);
+  Gemv g;
+  g.init(uni_ptr(G.W), uni(min(gemv_v_rows(S, uni(nt)), G.R)), uni(G.K));
+  const int RB = (g.R + 3) >> 2;
+  SegPlan sp;
+  sp.init(S, wave(), MK_NWAVE);
+  if (sp.s0 < S && sp.j < RB) gemv_v_issue2(g, RB, sp.s0, sp.nj, pre.r, sp.j);
+  keep_issued();
+}
+
 template <bool PAIRS, typename Epi>
-__device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs, int nt, LS float* red, Epi epi) {
+__device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs, int nt, LS float* red,
+                                       const GemvPre& pre, Epi epi) {
   const int S = uni(G.S);
   nt = uni(nt);
-  const int rc = max(4, (MK_RED_CAP / (S * nt)) & ~3);
+  const int rc = gemv_v_rows(S, nt);
   for (int r0 = 0; r0 < G.R; r0 += rc) {
     Gemv g;
     g.init(uni_ptr(G.W + (size_t)r0 * G.K), uni(min(rc, G.R - r0)), uni(G.K));
@@ -59,22 +237,16 @@ __device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs,
         if (t < nt) load_x(x[t], xin + t * xs, s, g.K);
       }
       const int step = sp.nj;
-      auto issue2 = [&](RegUnits<2>& r, int rb0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int rbi = rb0 + i * step;
-#pragma unroll
-          for (int k = 0; k < USLOTS; ++k) {
-            const MK_G uint16_t* a = rbi < RB ? g.addr(rbi * S + s, k) : nullptr;
-            r.c[i * USLOTS + k] = a ? ldw(a) : u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      };
       RegUnits<2> cur, nxt;
-      issue2(cur, rb);
-      keep_issued();
+      if (r0 == 0 && s == sp.s0) {
+#pragma unroll
+        for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = pre.r.c[i];
+      } else {
+        gemv_v_issue2(g, RB, s, step, cur, rb);
+        keep_issued();
+      }
       for (; rb < RB; rb += 2 * step) {
-        issue2(nxt, rb + 2 * step);
+        gemv_v_issue2(g, RB, s, step, nxt, rb + 2 * step);
         keep_issued();
         const bool h1 = rb + step < RB;
 #pragma unroll
@@ -114,20 +286,28 @@ __device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs,
 
 // Gated delta rule for nt positions on rows [s0, s1) of S, read from the main buffer once.  After
 // position t a row goes to snapshot t (t < nt - 1) or back to the main buffer (t = nt - 1), and
-// o_t = S_t q_t goes to the records.  Every wave owns rows (local index li % 8); norms and gates
-// are computed by every wave, all in the decode kernel's order.
+// o_t = S_t q_t goes to the records.  Every wave owns rows (local index li % 8); wave t forms
+// position t's norms and gates; all in the decode kernel's order.
 __device__ __forceinline__ bool dn_state_v(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                           LS float* buf, int s0, int s1, int nt) {
+                                           LS float* buf, LS float* nrm, int s0, int s1, int nt) {
   const int H = p.H, dk = p.dk, dv = p.dv, K = H * dv;
   const int rows_in = L.rows_in;
   const MK_G mk_u64* in = L.ll_in;
   const int off_k = H * dk, off_v = 2 * H * dk, off_a = 2 * H * dk + H * dv, off_b = off_a + H;
   const int h0 = s0 < s1 ? s0 / dv : 0, h1 = s0 < s1 ? (s1 - 1) / dv : -1;
+  // this wave's first row (local index = wave) is loaded before the first gather, so its HBM
+  // latency runs under the exchange
+  float pre[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane() + 64 * c;
+    pre[c] = (wave() < s1 - s0 && e < dk) ? L.S[(size_t)(s0 + wave()) * dk + e] : 0.f;
+  }
   for (int h = h0; h <= h1; ++h) {
     const int i0 = max(s0, h * dv) - h * dv, i1 = min(s1, (h + 1) * dv) - h * dv;
     const int nv = i1 - i0;
     const int per = 2 * dk + 2 + nv;  // per position: q, k, a, b, this workgroup's v rows
-    const bool ok = gather_map(cx, nt * per, [=](int f) {
+    const bool ok = gather_map_all(cx, nt * per, [=](int f) {
       const int t = f / per, g = f - t * per;
       const MK_G mk_u64* b = in + (size_t)t * rows_in;
       if (g < dk) return b + h * dk + g;
@@ -137,24 +317,35 @@ __device__ __forceinline__ bool dn_state_v(const MkDecodeParams& p, const MkLaye
       return b + off_v + h * dv + i0 + (g - 2 * dk - 2);
     }, [=](int f, float v) { buf[f] = v; });
     if (wg_bar_or(s, !ok)) return false;
+    // wave t: position t's norms and gates -> nrm[4 t ..]
+    if (wave() < nt) {
+      const int t = wave();
+      const LS float* q = buf + t * per;
+      const LS float* k = q + dk;
+      float qq = 0.f, kk = 0.f;
+      for (int e = lane(); e < dk; e += 64) {
+        qq = fmaf(q[e], q[e], qq);
+        kk = fmaf(k[e], k[e], kk);
+      }
+      qq = wave_sum(qq);
+      kk = wave_sum(kk);
+      if (lane() == 0) {
+        nrm[4 * t] = 1.0f / sqrtf(qq + p.l2_eps);
+        nrm[4 * t + 1] = 1.0f / sqrtf(kk + p.l2_eps);
+        nrm[4 * t + 2] = expf(-softplusf_(q[2 * dk]));
+        nrm[4 * t + 3] = sigmoidf_(q[2 * dk + 1]);
+      }
+    }
+    wg_bar();
     float sq[VT], sk[VT], al[VT], be[VT];
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
       sq[t] = sk[t] = al[t] = be[t] = 0.f;
       if (t < nt) {
-        const LS float* q = buf + t * per;
-        const LS float* k = q + dk;
-        float qq = 0.f, kk = 0.f;
-        for (int e = lane(); e < dk; e += 64) {
-          qq = fmaf(q[e], q[e], qq);
-          kk = fmaf(k[e], k[e], kk);
-        }
-        qq = wave_sum(qq);
-        kk = wave_sum(kk);
-        sq[t] = 1.0f / sqrtf(qq + p.l2_eps);
-        sk[t] = 1.0f / sqrtf(kk + p.l2_eps);
-        al[t] = expf(-softplusf_(q[2 * dk]));
-        be[t] = sigmoidf_(q[2 * dk + 1]);
+        sq[t] = nrm[4 * t];
+        sk[t] = nrm[4 * t + 1];
+        al[t] = nrm[4 * t + 2];
+        be[t] = nrm[4 * t + 3];
       }
     }
     const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
@@ -164,7 +355,7 @@ __device__ __forceinline__ bool dn_state_v(const MkDecodeParams& p, const MkLaye
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e = lane() + 64 * c;
-        sr[c] = e < dk ? L.S[(size_t)row * dk + e] : 0.f;
+        sr[c] = li == wave() ? pre[c] : (e < dk ? L.S[(size_t)row * dk + e] : 0.f);
       }
 #pragma unroll
       for (int t = 0; t < VT; ++t) {
@@ -205,10 +396,10 @@ __device__ __forceinline__ bool dn_state_v(const MkDecodeParams& p, const MkLaye
 // q/k/v rows (RoPE pair order) for nt positions: rotate q and k at position pos + t, append k and v
 // to the cache at pos + t, publish all three.
 __device__ __forceinline__ void att_qkv_v(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                          const Gemv& g, int P0, int pos, int nt) {
+                                          const Gemv& g, const GemvPre& pre, int P0, int pos, int nt) {
   const int hd = p.hd, half = hd / 2, rows_in = L.rows_in;
   const int nqp = p.nq * half, nkp = p.nkv * half;
-  gemv_v<true>(g, s.xn, p.D, nt, s.att, [&](int pl, int t, float x1, float x2) {
+  gemv_v<true>(g, s.xn, p.D, nt, s.att, pre, [&](int pl, int t, float x1, float x2) {
     const int P = P0 + pl;
     MK_G mk_u64* llq = L.ll_in + (size_t)t * rows_in;
     MK_G mk_u64* llk = llq + p.nq * hd;
@@ -272,7 +463,7 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
     const int nnew = max(0, jend - jnew);
     const int nqr = (nt - tmin) * gs * hd;
     const int nkvr = nnew * hd;
-    const bool ok = gather_map(cx, nqr + 2 * nkvr, [=](int f) {
+    const bool ok = gather_map_all(cx, nqr + 2 * nkvr, [=](int f) {
       if (f < nqr) {
         const int tt = f / (gs * hd), r = f - tt * gs * hd;
         return llq + (size_t)(tmin + tt) * rows_in + g * gs * hd + r;
@@ -408,7 +599,7 @@ __device__ __forceinline__ bool att_combine_v(const MkDecodeParams& p, const MkL
   const int vpp = max(1, cap / (3 * tot));
   for (int v0 = 0; v0 < nown; v0 += vpp) {
     const int vn = min(vpp, nown - v0);
-    const bool ok = gather_map(cx, vn * 3 * tot, [=](int f) {
+    const bool ok = gather_map_all(cx, vn * 3 * tot, [=](int f) {
       const int cf = f / (3 * vn);  // chunk slots of the positions before, in units of vn * 3 records
       int t = 0;
       while (t + 1 < nt && comb_before(pos, t + 1) <= cf) ++t;
@@ -480,7 +671,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   s.flag = (LS int*)(lds + p.lds_flag);
   s.stA = nullptr;
   s.stB = nullptr;
-  LS int* toks = (LS int*)(lds + p.lds_trace);  // the verify carve keeps the tokens where tracing would go
+  LS int* toks = (LS int*)(lds + p.lds_xn);  // the verify carve keeps the tokens in the xn slot
   const int D = p.D, F = p.ffn;
   const int vcap = uni(p.vec_floats);  // floats of the vector region
 
@@ -500,7 +691,9 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
     if (w == 0 && tid() == 0) set_err(cx, 2u);
     return;
   }
-  Tracer tr{nullptr, nullptr, 0};
+  Tracer tr{(LS unsigned long long*)(lds + p.lds_trace), p.trace ? p.trace + (size_t)w * MK_TRACE_EVENTS : nullptr,
+            0};
+  tr.mark();
   {
     const int nw = p.n_layers * (int)(sizeof(MkLayerDev) / 4);
     const MK_G u32* dsrc = (const MK_G u32*)p.layers;
@@ -522,76 +715,106 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   const int d0 = split(D, NW, w), d1 = split(D, NW, w + 1);
   const int j0 = split(F, NW, w), j1 = split(F, NW, w + 1);
   int P0, P1;
+  // the in-projection (or LM-head) rows of layer l
+  auto input_rows = [&](int l, Gemv& g) {
+    if (l < p.n_layers) {
+      const MkLayerDev Ln = layer_desc(s.desc, l);
+      pair_range(Ln.rows_in, NW, w, P0, P1);
+      g.init(Ln.w_in + (size_t)2 * P0 * D, min(2 * P1, Ln.rows_in) - 2 * P0, D);
+    } else {
+      pair_range(p.vocab, NW, w, P0, P1);
+      g.init(p.embed + (size_t)2 * P0 * D, min(2 * P1, p.vocab) - 2 * P0, D);
+    }
+  };
+  wg_bar();  // descriptors
+  GemvPre pre;  // the next GEMV's first units, loaded before the exchange that precedes it
+  Gemv gin;
+  input_rows(0, gin);
+  gemv_v_pre(gin, nt, pre);
   for (int l = 0; l < p.n_layers; ++l) {
-    wg_bar();
     const MkLayerDev L = layer_desc(s.desc, l);
     load_gains(L.g12, 2 * D, s.gain);
     wg_bar();
-    for (int t = 0; t < nt; ++t) rmsnorm(s.x + t * D, s.gain, s.xn + t * D, D, p.rms_eps, tr);
-    pair_range(L.rows_in, NW, w, P0, P1);
-    Gemv gin;
-    gin.init(L.w_in + (size_t)2 * P0 * D, min(2 * P1, L.rows_in) - 2 * P0, D);
+    tr.mark();
+    rmsnorm_v(s.x, s.gain, s.xn, D, p.rms_eps, nt, s.scr);
+    tr.mark();
     int K;
+    Gemv gout;
     if (L.kind == MK_LAYER_DN) {
       K = p.H * p.dv;
       MK_G mk_u64* dst = L.ll_in + 2 * P0;
       const int rin = L.rows_in;
-      gemv_v<false>(gin, s.xn, D, nt, s.att,
+      gemv_v<false>(gin, s.xn, D, nt, s.att, pre,
                     [&](int r, int t, float v, float) { ll_put(dst + (size_t)t * rin + r, cx.epoch, v); });
+      tr.mark();
+      gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
+      gemv_v_pre(gout, nt, pre);
       const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
-      if (!dn_state_v(p, L, cx, s, s.vec, s0, s1, nt)) return;
+      if (!dn_state_v(p, L, cx, s, s.vec, s.scr, s0, s1, nt)) return;
     } else {
       K = p.nq * p.hd;
-      att_qkv_v(p, L, cx, s, gin, P0, pos, nt);
+      att_qkv_v(p, L, cx, s, gin, pre, P0, pos, nt);
+      tr.mark();
+      gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
+      gemv_v_pre(gout, nt, pre);
       if (!att_items_v(p, L, cx, s, s.vec, NW, w, pos, nt)) return;
       const int o0 = split(K, NW, w), o1 = split(K, NW, w + 1);
       if (!att_combine_v(p, L, cx, s, s.vec, vcap, o0, o1, pos, nt)) return;
     }
+    tr.mark();
     // mixer outputs of every position -> out-projection rows + residual -> records
     {
-      const bool ok = gather_vec(cx, L.ll_o, nt * K, s.vec);
+      const bool ok = gather_vec_all<false>(cx, L.ll_o, nt * K, s.vec);
       if (wg_bar_or(s, !ok)) return;
       for (int t = 0; t < nt; ++t) to_hl(s.vec + t * K, K);
       wg_bar();
     }
-    Gemv gout;
-    gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
-    gemv_v<false>(gout, (const LS u32*)s.vec, K, nt, s.att, [&](int r, int t, float v, float) {
+    tr.mark();
+    gemv_v<false>(gout, (const LS u32*)s.vec, K, nt, s.att, pre, [&](int r, int t, float v, float) {
       ll_put(L.ll_x1 + (size_t)t * D + d0 + r, cx.epoch, s.x[t * D + d0 + r] + v);
     });
-    {
-      const bool ok = gather_vec(cx, L.ll_x1, nt * D, s.x);
-      if (wg_bar_or(s, !ok)) return;
-    }
-    for (int t = 0; t < nt; ++t) rmsnorm(s.x + t * D, s.gain + D, s.xn + t * D, D, p.rms_eps, tr);
+    tr.mark();
     Gemv ggu;
     ggu.init(L.w_gu + (size_t)2 * j0 * D, 2 * (j1 - j0), D);
-    gemv_v<true>(ggu, s.xn, D, nt, s.att, [&](int j, int t, float gv, float uv) {
-      ll_put(L.ll_h + (size_t)t * F + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
-    });
+    gemv_v_pre(ggu, nt, pre);
     {
-      const bool ok = gather_hl(cx, L.ll_h, nt * F, (LS u32*)s.vec);
+      const bool ok = gather_vec_all<false>(cx, L.ll_x1, nt * D, s.x);
       if (wg_bar_or(s, !ok)) return;
     }
+    tr.mark();
+    rmsnorm_v(s.x, s.gain + D, s.xn, D, p.rms_eps, nt, s.scr);
+    tr.mark();
+    gemv_v<true>(ggu, s.xn, D, nt, s.att, pre, [&](int j, int t, float gv, float uv) {
+      ll_put(L.ll_h + (size_t)t * F + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
+    });
+    tr.mark();
     Gemv gdn;
     gdn.init(L.w_down + (size_t)d0 * F, d1 - d0, F);
-    gemv_v<false>(gdn, (const LS u32*)s.vec, F, nt, s.att, [&](int r, int t, float v, float) {
+    gemv_v_pre(gdn, nt, pre);
+    {
+      const bool ok = gather_vec_all<true>(cx, L.ll_h, nt * F, s.vec);
+      if (wg_bar_or(s, !ok)) return;
+    }
+    tr.mark();
+    gemv_v<false>(gdn, (const LS u32*)s.vec, F, nt, s.att, pre, [&](int r, int t, float v, float) {
       ll_put(L.ll_x2 + (size_t)t * D + d0 + r, cx.epoch, s.x[t * D + d0 + r] + v);
     });
+    tr.mark();
+    input_rows(l + 1, gin);
+    gemv_v_pre(gin, nt, pre);
     {
-      const bool ok = gather_vec(cx, L.ll_x2, nt * D, s.x);
+      const bool ok = gather_vec_all<false>(cx, L.ll_x2, nt * D, s.x);
       if (wg_bar_or(s, !ok)) return;
     }
   }
 
+  tr.mark();
   // final norm + tied LM head + per-position argmax (lowest index among equal maxima)
   load_gains(p.g_final, D, s.gain);
   wg_bar();
-  for (int t = 0; t < nt; ++t) rmsnorm(s.x + t * D, s.gain, s.xn + t * D, D, p.rms_eps, tr);
-  pair_range(p.vocab, NW, w, P0, P1);
+  rmsnorm_v(s.x, s.gain, s.xn, D, p.rms_eps, nt, s.scr);
   {
-    Gemv ghead;
-    ghead.init(p.embed + (size_t)2 * P0 * D, min(2 * P1, p.vocab) - 2 * P0, D);
+    const Gemv ghead = gin;  // the LM-head rows, first units already loaded
     float best[VT];
     int bidx[VT];
 #pragma unroll
@@ -600,7 +823,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
       bidx[t] = 0x7fffffff;
     }
     const int v0 = 2 * P0;
-    gemv_v<false>(ghead, s.xn, D, nt, s.att, [&](int r, int t, float v, float) {
+    gemv_v<false>(ghead, s.xn, D, nt, s.att, pre, [&](int r, int t, float v, float) {
       const int idx = v0 + r;
       if (v > best[t] || (v == best[t] && idx < bidx[t])) {
         best[t] = v;
@@ -624,6 +847,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
       }
     }
   }
+  tr.mark();
   wg_bar();
   if (tid() < nt) {
     const int t = tid();
@@ -642,61 +866,71 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   }
   // workgroup 0: greedy choices, accepted count, outputs, new position
   if (w == 0) {
-    const bool ok = gather_vec(cx, p.ll_am, nt * 2 * NW, s.vec);
+    const bool ok = gather_vec_all<false>(cx, p.ll_am, nt * 2 * NW, s.vec);
     if (wg_bar_or(s, !ok)) return;
-    if (tid() == 0) {
-      int y[VT];
-#pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        y[t] = 0;
-        if (t < nt) {
-          float b = -INFINITY;
-          int bi = 0x7fffffff;
-          for (int i = 0; i < NW; ++i) {
-            const float ob = s.vec[t * 2 * NW + 2 * i];
-            const int oi = __float_as_int(s.vec[t * 2 * NW + 2 * i + 1]);
-            if (ob > b || (ob == b && oi < bi)) {
-              b = ob;
-              bi = oi;
-            }
-          }
-          y[t] = bi;
-          p.vout[t] = bi;
-        }
+    // wave t: position t's choice
+    if (wave() < nt) {
+      float b;
+      int bi;
+      wave_argmax(s.vec + wave() * 2 * NW, NW, b, bi);
+      if (lane() == 0) {
+        p.vout[wave()] = bi;
+        ((LS int*)s.scr)[wave()] = bi;
       }
+    }
+    wg_bar();
+    if (tid() == 0) {
       int a = 0;
-#pragma unroll
-      for (int t = 0; t + 1 < VT; ++t)
-        if (a == t && t + 1 < nt && toks[t + 1] == y[t]) ++a;
+      while (a + 1 < nt && toks[a + 1] == ((LS int*)s.scr)[a]) ++a;
       *p.vacc = a;
       ll_put(p.ll_acc, cx.epoch, __int_as_float(a));
       p.ctl->pos = pos + a + 1;
     }
   }
+  tr.mark();
   // every workgroup: the accepted count, then its DeltaNet rows back to the state after position a
   {
-    const bool ok = gather_vec(cx, p.ll_acc, 1, s.scr);
+    const bool ok = gather_vec_all<false>(cx, p.ll_acc, 1, s.scr);
     if (wg_bar_or(s, !ok)) return;
   }
   const int a = uni(__float_as_int(s.scr[0]));
   if (a + 1 < nt) {
     const int K = p.H * p.dv, dk = p.dk;
     const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
-    for (int l = 0; l < p.n_layers; ++l) {
-      const MkLayerDev L = layer_desc(s.desc, l);
-      if (L.kind != MK_LAYER_DN) continue;
-      const MK_G float* src = L.Ssnap + (size_t)a * p.snap_stride;
-      // the threads that wrote each snapshot element in dn_state_v copy it
-      for (int li = wave(); li < s1 - s0; li += MK_NWAVE) {
-        const size_t ro = (size_t)(s0 + li) * dk;
+    // The threads that wrote each snapshot element in dn_state_v copy it.  Loads for CB layers are
+    // issued before their stores: a load issued after a store would wait for that store too.
+    constexpr int CB = 8;
+    for (int li = wave(); li < s1 - s0; li += MK_NWAVE) {
+      const size_t ro = (size_t)(s0 + li) * dk;
+      for (int l0 = 0; l0 < p.n_layers; l0 += CB) {
+        float v[CB][4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = lane() + 64 * c;
-          if (e < dk) L.S[ro + e] = src[ro + e];
+        for (int i = 0; i < CB; ++i) {
+          const int l = l0 + i;
+          const MkLayerDev L = layer_desc(s.desc, min(l, p.n_layers - 1));
+          const bool dn = l < p.n_layers && L.kind == MK_LAYER_DN;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = lane() + 64 * c;
+            v[i][c] = (dn && e < dk) ? L.Ssnap[(size_t)a * p.snap_stride + ro + e] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+          const int l = l0 + i;
+          const MkLayerDev L = layer_desc(s.desc, min(l, p.n_layers - 1));
+          const bool dn = l < p.n_layers && L.kind == MK_LAYER_DN;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = lane() + 64 * c;
+            if (dn && e < dk) L.S[ro + e] = v[i][c];
+          }
         }
       }
     }
   }
+  tr.mark();
+  tr.flush();
   if (w == 0) {
     wait_vm<0>();
     wg_bar();
