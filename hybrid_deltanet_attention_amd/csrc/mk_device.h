@@ -650,7 +650,11 @@ __device__ __forceinline__ void gemv_partials(const MK_G uint16_t* W, int R, int
       };
       RegUnits<2> cur, nxt;
       issue2(cur, rb);
-      keep_issued();
+      // Nothing may look outstanding in cur when the loop starts: these loads are conditional, and
+      // a register the compiler cannot place in the load queue makes it wait for every load, the
+      // look-ahead ones included, before each unit.  (The stage copies this wave issued for the
+      // same GEMV were waited for before the barrier that preceded it.)
+      wait_vm<0>();
       for (; rb < RB; rb += 2 * step) {
         issue2(nxt, rb + 2 * step);
         keep_issued();

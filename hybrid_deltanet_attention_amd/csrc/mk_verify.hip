@@ -243,8 +243,11 @@ __device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs,
         for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = pre.r.c[i];
       } else {
         gemv_v_issue2(g, RB, s, step, cur, rb);
-        keep_issued();
       }
+      // Nothing may look outstanding in cur when the loop starts: the loads above are conditional,
+      // and a register the compiler cannot place in the load queue makes it wait for every load,
+      // the look-ahead ones included, before each unit.
+      wait_vm<0>();
       for (; rb < RB; rb += 2 * step) {
         gemv_v_issue2(g, RB, s, step, nxt, rb + 2 * step);
         keep_issued();
