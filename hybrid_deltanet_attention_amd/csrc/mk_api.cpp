@@ -263,6 +263,7 @@ void lds_layout_verify(const mk_config& c, int grid, MkDecodeParams& p) {
   vec = std::max(vec, (int64_t)vt * gs * hd + 2 * C * hd + vt * gs * C + 2 * vt * gs);
   vec = std::max(vec, (int64_t)3 * vt * nch_max);
   vec = std::max(vec, (int64_t)2 * vt * grid);
+  vec = std::max(vec, (int64_t)vt * D + 2 * vt * MK_NCT);  // LM head: activations + running argmax
   int o = 0;
   auto take = [&](int64_t n) {
     const int at = o;

@@ -229,13 +229,6 @@ __device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs,
     for (int s = sp.s0; s < S; s += sp.sstep) {
       int rb = sp.j;
       if (rb >= RB) continue;
-      XSlice x[VT];
-#pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        x[t].h = u32x4{0u, 0u, 0u, 0u};
-        x[t].l = x[t].h;
-        if (t < nt) load_x(x[t], xin + t * xs, s, g.K);
-      }
       const int step = sp.nj;
       RegUnits<2> cur, nxt;
       if (r0 == 0 && s == sp.s0) {
@@ -252,14 +245,16 @@ __device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs,
         gemv_v_issue2(g, RB, s, step, nxt, rb + 2 * step);
         keep_issued();
         const bool h1 = rb + step < RB;
-#pragma unroll
-        for (int t = 0; t < VT; ++t) {
-          if (t < nt) {
-            const float a0 = unit_dot_x(s, g.K, cur.c, x[t]);
-            const float a1 = h1 ? unit_dot_x(s, g.K, cur.c + USLOTS, x[t]) : 0.f;
-            put_partial(g, rb * S + s, a0, red + t * blk);
-            if (h1) put_partial(g, (rb + step) * S + s, a1, red + t * blk);
-          }
+        // positions in a loop, not unrolled: the kernel's code must stay small enough for the
+        // instruction cache, and each position reads its 32 bytes of activations from LDS
+#pragma unroll 2
+        for (int t = 0; t < nt; ++t) {
+          XSlice x;
+          load_x(x, xin + t * xs, s, g.K);
+          const float a0 = unit_dot_x(s, g.K, cur.c, x);
+          const float a1 = h1 ? unit_dot_x(s, g.K, cur.c + USLOTS, x) : 0.f;
+          put_partial(g, rb * S + s, a0, red + t * blk);
+          if (h1) put_partial(g, (rb + step) * S + s, a1, red + t * blk);
         }
 #pragma unroll
         for (int i = 0; i < 2 * USLOTS; ++i) cur.c[i] = nxt.c[i];
@@ -270,17 +265,14 @@ __device__ __forceinline__ void gemv_v(const Gemv& G, const LS u32* xin, int xs,
     }
     wg_bar();
     if (streamer()) {
-#pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        if (t < nt) {
-          const LS float* rt = red + t * blk;
-          if (PAIRS) {
-            for (int j = tid(); j < g.R / 2; j += NCT)
-              epi(r0 / 2 + j, t, seg_sum(rt + (2 * j) * S, S), seg_sum(rt + (2 * j + 1) * S, S));
-          } else {
-            for (int j = tid(); j < g.R; j += NCT) epi(r0 + j, t, seg_sum(rt + j * S, S), 0.f);
-          }
-        }
+      // (position, row) pairs spread over the streaming threads, so the positions' epilogues run
+      // side by side
+      const int nr = PAIRS ? g.R / 2 : g.R;
+      for (int i = tid(); i < nt * nr; i += NCT) {
+        const int t = i / nr, j = i - t * nr;
+        const LS float* rt = red + t * blk;
+        if (PAIRS) epi(r0 / 2 + j, t, seg_sum(rt + (2 * j) * S, S), seg_sum(rt + (2 * j + 1) * S, S));
+        else epi(r0 + j, t, seg_sum(rt + j * S, S), 0.f);
       }
     }
     wg_bar();  // red is reused by the next chunk
@@ -340,17 +332,6 @@ __device__ __forceinline__ bool dn_state_v(const MkDecodeParams& p, const MkLaye
       }
     }
     wg_bar();
-    float sq[VT], sk[VT], al[VT], be[VT];
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      sq[t] = sk[t] = al[t] = be[t] = 0.f;
-      if (t < nt) {
-        sq[t] = nrm[4 * t];
-        sk[t] = nrm[4 * t + 1];
-        al[t] = nrm[4 * t + 2];
-        be[t] = nrm[4 * t + 3];
-      }
-    }
     const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
     for (int li = lo + ((wave() - lo % MK_NWAVE) + MK_NWAVE) % MK_NWAVE; li < hi; li += MK_NWAVE) {
       const int row = s0 + li;
@@ -360,35 +341,34 @@ __device__ __forceinline__ bool dn_state_v(const MkDecodeParams& p, const MkLaye
         const int e = lane() + 64 * c;
         sr[c] = li == wave() ? pre[c] : (e < dk ? L.S[(size_t)row * dk + e] : 0.f);
       }
+#pragma unroll 1
+      for (int t = 0; t < nt; ++t) {
+        const float sq = nrm[4 * t], sk = nrm[4 * t + 1], al = nrm[4 * t + 2], be = nrm[4 * t + 3];
+        const LS float* q = buf + t * per;
+        const LS float* k = q + dk;
+        const LS float* vr = q + 2 * dk + 2;
+        float kd = 0.f;
 #pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        if (t < nt) {
-          const LS float* q = buf + t * per;
-          const LS float* k = q + dk;
-          const LS float* vr = q + 2 * dk + 2;
-          float kd = 0.f;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int e = lane() + 64 * c;
-            if (e < dk) kd = fmaf(sr[c], k[e] * sk[t], kd);
-          }
-          kd = wave_sum(kd);
-          const float u = be[t] * (vr[row - h * dv - i0] - al[t] * kd);
-          MK_G float* dst = t + 1 < nt ? L.Ssnap + (size_t)t * p.snap_stride : L.S;
-          float od = 0.f;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int e = lane() + 64 * c;
-            if (e < dk) {
-              const float nv2 = fmaf(u, k[e] * sk[t], al[t] * sr[c]);
-              sr[c] = nv2;
-              dst[(size_t)row * dk + e] = nv2;
-              od = fmaf(nv2, q[e] * sq[t], od);
-            }
-          }
-          od = wave_sum(od);
-          if (lane() == 0) ll_put(L.ll_o + (size_t)t * K + row, cx.epoch, od);
+        for (int c = 0; c < 4; ++c) {
+          const int e = lane() + 64 * c;
+          if (e < dk) kd = fmaf(sr[c], k[e] * sk, kd);
         }
+        kd = wave_sum(kd);
+        const float u = be * (vr[row - h * dv - i0] - al * kd);
+        MK_G float* dst = t + 1 < nt ? L.Ssnap + (size_t)t * p.snap_stride : L.S;
+        float od = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int e = lane() + 64 * c;
+          if (e < dk) {
+            const float nv2 = fmaf(u, k[e] * sk, al * sr[c]);
+            sr[c] = nv2;
+            dst[(size_t)row * dk + e] = nv2;
+            od = fmaf(nv2, q[e] * sq, od);
+          }
+        }
+        od = wave_sum(od);
+        if (lane() == 0) ll_put(L.ll_o + (size_t)t * K + row, cx.epoch, od);
       }
     }
     wg_bar();  // buf is reused by the next head
@@ -818,57 +798,55 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   rmsnorm_v(s.x, s.gain, s.xn, D, p.rms_eps, nt, s.scr);
   {
     const Gemv ghead = gin;  // the LM-head rows, first units already loaded
-    float best[VT];
-    int bidx[VT];
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      best[t] = -INFINITY;
-      bidx[t] = 0x7fffffff;
+    // running argmax per (position, streaming thread) in LDS, after the normalised activations
+    LS float* amv = s.vec + nt * D;
+    LS int* ami = (LS int*)(amv + nt * NCT);
+    for (int i = tid(); i < nt * NCT; i += MK_NT) {
+      amv[i] = -INFINITY;
+      ami[i] = 0x7fffffff;
     }
+    wg_bar();
     const int v0 = 2 * P0;
     gemv_v<false>(ghead, s.xn, D, nt, s.att, pre, [&](int r, int t, float v, float) {
       const int idx = v0 + r;
-      if (v > best[t] || (v == best[t] && idx < bidx[t])) {
-        best[t] = v;
-        bidx[t] = idx;
+      const int c = t * NCT + tid();
+      if (v > amv[c] || (v == amv[c] && idx < ami[c])) {
+        amv[c] = v;
+        ami[c] = idx;
       }
     });
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
+    tr.mark();
+    // wave t: the workgroup's winner for position t (largest value, lowest index)
+    if (wave() < nt) {
+      const int t = wave();
+      float b = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int i = lane(); i < NCT; i += 64) {
+        const float ob = amv[t * NCT + i];
+        const int oi = ami[t * NCT + i];
+        if (ob > b || (ob == b && oi < bi)) {
+          b = ob;
+          bi = oi;
+        }
+      }
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) {
-        const float ob = __shfl_xor(best[t], m, 64);
-        const int oi = __shfl_xor(bidx[t], m, 64);
-        if (ob > best[t] || (ob == best[t] && oi < bidx[t])) {
-          best[t] = ob;
-          bidx[t] = oi;
+        const float ob = __shfl_xor(b, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        if (ob > b || (ob == b && oi < bi)) {
+          b = ob;
+          bi = oi;
         }
       }
       if (lane() == 0) {
-        s.scr[2 * (t * MK_NWAVE + wave())] = best[t];
-        s.scr[2 * (t * MK_NWAVE + wave()) + 1] = __int_as_float(bidx[t]);
+        ll_put(p.ll_am + (size_t)t * 2 * NW + 2 * w, cx.epoch, b);
+        ll_put(p.ll_am + (size_t)t * 2 * NW + 2 * w + 1, cx.epoch, __int_as_float(bi));
       }
     }
-  }
-  tr.mark();
-  wg_bar();
-  if (tid() < nt) {
-    const int t = tid();
-    float b = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = 0; i < MK_NWAVE; ++i) {
-      const float ob = s.scr[2 * (t * MK_NWAVE + i)];
-      const int oi = __float_as_int(s.scr[2 * (t * MK_NWAVE + i) + 1]);
-      if (ob > b || (ob == b && oi < bi)) {
-        b = ob;
-        bi = oi;
-      }
-    }
-    ll_put(p.ll_am + (size_t)t * 2 * NW + 2 * w, cx.epoch, b);
-    ll_put(p.ll_am + (size_t)t * 2 * NW + 2 * w + 1, cx.epoch, __int_as_float(bi));
   }
   // workgroup 0: greedy choices, accepted count, outputs, new position
   if (w == 0) {
+    wg_bar();  // the running-argmax cells are read before the gather reuses the region
     const bool ok = gather_vec_all<false>(cx, p.ll_am, nt * 2 * NW, s.vec);
     if (wg_bar_or(s, !ok)) return;
     // wave t: position t's choice
