@@ -173,9 +173,11 @@ def _energy_reader():
         return None, f"energy counter unavailable: {type(ex).__name__}: {ex}"
 
 
-def energy_leg(m, prompt, tok, n_steps: int) -> dict:
+def energy_leg(m, prompt, tok, n_steps: int, min_seconds: float = 4.0) -> dict:
     """Tokens per joule of the decode loop from the board energy accumulator (whole board, idle
-    power included), over n_steps consecutive one-launch decode steps after the 512-token prompt."""
+    power included).  The accumulator advances in coarse steps, so the window spans at least
+    min_seconds: rounds of (512-token prefill, n_steps one-launch decode steps), repeated.  The
+    prefills are inside the window (about 1 % of its time) and count no tokens."""
     import torch
     read, err = _energy_reader()
     if read is None:
@@ -184,26 +186,29 @@ def energy_leg(m, prompt, tok, n_steps: int) -> dict:
     time.sleep(0.25)
     ei0, _ = read()
     ti0 = time.perf_counter()
-    time.sleep(1.0)
+    time.sleep(2.0)
     ei1, _ = read()
     idle_w = (ei1 - ei0) / (time.perf_counter() - ti0)
-    m.mk_reset()
-    m.mk_prefill(prompt[:PROMPT], PROMPT, tok)
-    m.mk_sync()
     e0, _ = read()
     t0 = time.perf_counter()
-    for _ in range(n_steps):
-        m.mk_decode_step(tok, tok)
-    m.mk_sync()
+    steps = rounds = 0
+    while time.perf_counter() - t0 < min_seconds:
+        m.mk_reset()
+        m.mk_prefill(prompt[:PROMPT], PROMPT, tok)
+        for _ in range(n_steps):
+            m.mk_decode_step(tok, tok)
+        m.mk_sync()
+        steps += n_steps
+        rounds += 1
     t1 = time.perf_counter()
     e1, _ = read()
     joules = e1 - e0
     secs = t1 - t0
-    return {"tok_per_J": round(n_steps / joules, 2) if joules > 0 else None,
+    return {"tok_per_J": round(steps / joules, 3) if joules > 0 else None,
             "avg_power_W": round(joules / secs, 1),
             "idle_power_W": round(idle_w, 1),
-            "steps": n_steps, "seconds": round(secs, 3),
-            "context": f"positions {PROMPT}..{PROMPT + n_steps - 1}",
+            "steps": steps, "rounds": rounds, "seconds": round(secs, 3),
+            "context": f"positions {PROMPT}..{PROMPT + n_steps - 1}, a 512-token prefill before each round",
             "counter": "amdsmi energy accumulator, whole board"}
 
 

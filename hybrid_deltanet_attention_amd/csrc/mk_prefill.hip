@@ -989,25 +989,47 @@ __global__ void __launch_bounds__(256) pf_lmhead_kernel(const float* __restrict_
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
   float best = -INFINITY;
   int bidx = 0x7fffffff;
-  for (int v = v0 + wv; v < v1; v += 4) {
-    const uint16_t* er = E + (size_t)v * D;
-    float a = 0.f;
+  // each wave takes 4 rows at a time: their loads are in flight together and their four wave
+  // reductions overlap; rows are visited in increasing order within a wave
+  constexpr int RW = 4;
+  for (int vb = v0 + wv * RW; vb < v1; vb += 4 * RW) {
+    float a[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) a[i] = 0.f;
     for (int k = l * 8; k < D; k += 512) {
-      const u32x4 wq = *(const u32x4*)(er + k);
-      a = fmaf(__uint_as_float(wq.x << 16), xs[k], a);
-      a = fmaf(__uint_as_float(wq.x & 0xffff0000u), xs[k + 1], a);
-      a = fmaf(__uint_as_float(wq.y << 16), xs[k + 2], a);
-      a = fmaf(__uint_as_float(wq.y & 0xffff0000u), xs[k + 3], a);
-      a = fmaf(__uint_as_float(wq.z << 16), xs[k + 4], a);
-      a = fmaf(__uint_as_float(wq.z & 0xffff0000u), xs[k + 5], a);
-      a = fmaf(__uint_as_float(wq.w << 16), xs[k + 6], a);
-      a = fmaf(__uint_as_float(wq.w & 0xffff0000u), xs[k + 7], a);
+      u32x4 wq[RW];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const int v = min(vb + i, v1 - 1);
+        wq[i] = *(const u32x4*)(E + (size_t)v * D + k);
+      }
+      float xk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xk[j] = xs[k + j];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        a[i] = fmaf(__uint_as_float(wq[i].x << 16), xk[0], a[i]);
+        a[i] = fmaf(__uint_as_float(wq[i].x & 0xffff0000u), xk[1], a[i]);
+        a[i] = fmaf(__uint_as_float(wq[i].y << 16), xk[2], a[i]);
+        a[i] = fmaf(__uint_as_float(wq[i].y & 0xffff0000u), xk[3], a[i]);
+        a[i] = fmaf(__uint_as_float(wq[i].z << 16), xk[4], a[i]);
+        a[i] = fmaf(__uint_as_float(wq[i].z & 0xffff0000u), xk[5], a[i]);
+        a[i] = fmaf(__uint_as_float(wq[i].w << 16), xk[6], a[i]);
+        a[i] = fmaf(__uint_as_float(wq[i].w & 0xffff0000u), xk[7], a[i]);
+      }
     }
-    a = wave_sum(a);
-    if (logits && l == 0) logits[v] = a;
-    if (a > best || (a == best && v < bidx)) {
-      best = a;
-      bidx = v;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) a[i] = wave_sum(a[i]);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int v = vb + i;
+      if (v < v1) {
+        if (logits && l == 0) logits[v] = a[i];
+        if (a[i] > best || (a[i] == best && v < bidx)) {
+          best = a[i];
+          bidx = v;
+        }
+      }
     }
   }
   __syncthreads();
@@ -1029,10 +1051,11 @@ __global__ void __launch_bounds__(256) pf_lmhead_kernel(const float* __restrict_
 
 __global__ void pf_finish_kernel(const float* __restrict__ part, int n, int32_t* __restrict__ next, MkCtl* ctl,
                                  int32_t pos) {
-  if (threadIdx.x != 0) return;
+  // one wave: lanes over the partial winners, then a shuffle tree (largest value, lowest index)
+  const int l = threadIdx.x;
   float b = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = 0; i < n; ++i) {
+  for (int i = l; i < n; i += 64) {
     const float v = part[2 * i];
     const int vi = __float_as_int(part[2 * i + 1]);
     if (v > b || (v == b && vi < bi)) {
@@ -1040,8 +1063,19 @@ __global__ void pf_finish_kernel(const float* __restrict__ part, int n, int32_t*
       bi = vi;
     }
   }
-  next[0] = bi;
-  ctl->pos = pos;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ob = __shfl_xor(b, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (ob > b || (ob == b && oi < bi)) {
+      b = ob;
+      bi = oi;
+    }
+  }
+  if (l == 0) {
+    next[0] = bi;
+    ctl->pos = pos;
+  }
 }
 
 }  // namespace
