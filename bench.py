@@ -212,6 +212,43 @@ def energy_leg(m, prompt, tok, n_steps: int, min_seconds: float = 4.0) -> dict:
             "counter": "amdsmi energy accumulator, whole board"}
 
 
+def long_context_leg(cfg_name: str, W, ctx: int, n_steps: int) -> dict:
+    """Decode at a long context: a ctx-token prompt through the GPU prefill, then n_steps timed
+    one-launch decode steps with the KV cache that large (same weights, a 32,768-position cache)."""
+    import torch
+    import synth
+    from hybrid_deltanet_attention_amd import Model
+    cfg = synth.get_config(cfg_name, max_ctx=32768)
+    dev = torch.device("cuda:0")
+    m = Model(cfg, device=0)
+    m.mk_load_weights(W)
+    prompt = torch.tensor(synth.make_prompt(cfg.vocab, ctx, SEED + 7), device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    t0 = time.perf_counter()
+    m.mk_prefill(prompt, ctx, tok)
+    m.mk_sync()
+    pre_s = time.perf_counter() - t0
+    for _ in range(4):
+        m.mk_decode_step(tok, tok)
+    m.mk_sync()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    for i in range(n_steps):
+        ev[i][0].record(m.stream)
+        m.mk_decode_step(tok, tok)
+        ev[i][1].record(m.stream)
+    m.mk_sync()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    region = ev[0][0].elapsed_time(ev[-1][1]) / 1e3
+    L0 = ctx + 5
+    bytes_per = float(np.mean([algorithmic_bytes(cfg, L0 + i)["total"] for i in range(n_steps)]))
+    gbs = bytes_per / (us * 1e-6) / 1e9
+    m.close()
+    return {"context": ctx, "prefill_s": round(pre_s, 3), "us_per_launch": round(us, 2),
+            "tok_per_s": round(n_steps / region, 1), "bytes_per_launch": int(bytes_per),
+            "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "kv": "fp32"}
+
+
 def verify_leg(cfg, W, m_dec, prompt, tok, k: int, n_launch: int) -> dict:
     """mk_verify_k timing at the decode workload: the pending token and k drafts per launch, after the
     512-token prompt.  Greedy drafts are the model's own continuation (from decode launches), so every
@@ -275,6 +312,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the pp520 prefill timing (profiling runs)")
     ap.add_argument("--config", default="hybrid_0p8b")
+    ap.add_argument("--long-context", type=int, default=30000,
+                    help="prompt length of the long-context decode leg (32,768-position cache); 0 skips it")
     ap.add_argument("--verify-k", type=int, default=5, help="drafts per mk_verify_k launch in the verify leg; 0 skips it")
     ap.add_argument("--energy-steps", type=int, default=1280,
                     help="decode steps of the energy (tok/J) leg; 0 skips it")
@@ -387,6 +426,9 @@ def main():
         out["verify"] = verify_leg(cfg, W, m, prompt, tok, args.verify_k, 64)
         out["verify"]["decode_us_per_launch"] = round(avg_launch * 1e6, 2)
         print(f"[bench] verify: {out['verify']}", file=sys.stderr, flush=True)
+    if args.long_context > 0:
+        out["long_context"] = long_context_leg(args.config, W, min(args.long_context, 32768 - 64), 32)
+        print(f"[bench] long context: {out['long_context']}", file=sys.stderr, flush=True)
     if args.energy_steps > 0:
         n_e = min(args.energy_steps, cfg.max_ctx - PROMPT)
         out["energy"] = energy_leg(m, prompt, tok, n_e)

@@ -224,9 +224,9 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   const int vec = std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid));
   // gathered DeltaNet inputs (one head), attention item inputs, combine staging, GEMV unit partials
   int att = 2 * c.dn_dk + 2 + c.dn_dv;
-  att = std::max(att, gs * hd + 2 * hd + gs * C + 2 * gs);
+  att = std::max(att, 2 * gs * hd + 2 * hd + gs * C + 6 * gs);  // attention items, running merge included
   att = std::max(att, MK_RED_CAP);
-  att = std::max(att, 3 * ((c.max_ctx - 1 + C) / C));  // combine staging of one output, all chunks
+  att = std::max(att, 3 * 129);  // combine staging of one output: at most 128 items per KV head (+1)
   int o = 0;
   auto take = [&](int n) {
     const int at = o;
@@ -257,11 +257,10 @@ void lds_layout_verify(const mk_config& c, int grid, MkDecodeParams& p) {
   const int D = c.hidden;
   const int gs = c.n_q_heads / c.n_kv_heads;
   const int hd = c.head_dim, C = MK_ATT_CHUNK;
-  const int nch_max = (c.max_ctx - 1 + C) / C;
   int64_t vec = (int64_t)vt * std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, D));
   vec = std::max(vec, (int64_t)vt * (2 * c.dn_dk + 2 + c.dn_dv));
-  vec = std::max(vec, (int64_t)vt * gs * hd + 2 * C * hd + vt * gs * C + 2 * vt * gs);
-  vec = std::max(vec, (int64_t)3 * vt * nch_max);
+  vec = std::max(vec, (int64_t)2 * vt * gs * hd + 2 * C * hd + vt * gs * C + 6 * vt * gs);  // items + merge
+  vec = std::max(vec, (int64_t)3 * vt * 129);  // combine staging of one output: <= 128 items per KV head
   vec = std::max(vec, (int64_t)2 * vt * grid);
   vec = std::max(vec, (int64_t)vt * D + 2 * vt * MK_NCT);  // LM head: activations + running argmax
   int o = 0;
@@ -453,6 +452,9 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   p.hd = cfg->head_dim;
   p.max_ctx = cfg->max_ctx;
   p.max_items = lay.max_items;
+  // at most 128 split-K attention items per KV head at full context; one chunk per item up to
+  // 2,048 positions
+  p.att_cpi = std::max(1, (cfg->max_ctx + 2047) / 2048);
   p.rms_eps = cfg->rms_eps;
   p.l2_eps = cfg->l2_eps;
   p.layers = (const MkLayerDev*)(ctx->ws + lay.descs);

@@ -149,10 +149,13 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
       K = p.nq * p.hd;
       att_qkv(p, L, cx, s, gin, P0, pos, tr);
       tr.mark();
-      // K/V rows of the first work item and the out-projection units -> stage B; gate/up -> stage A
-      const int boff = (2 * kv_slots(p.hd) + 3) & ~3;
-      const int items = ((pos + ATT_C) / ATT_C) * p.nkv;
-      if (w < items) kv_stage(p, L, w, pos, s.stB);
+      // K/V rows of the first two work items -> stage A (free until the gate/up units), the
+      // out-projection units -> stage B
+      const int boff = 0;
+      for (int kc = 0; kc + 1 < kv_nbuf(p.hd) || kc == 0; ++kc) {
+        const int cn = att_chunk_at(p, NW, w, pos, kc);
+        if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd) * SLOT);
+      }
       gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
       gemv_stage(gout, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS);
       if (!att_items(p, L, cx, s, NW, w, pos, 0, tr)) return;

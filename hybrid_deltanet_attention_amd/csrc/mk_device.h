@@ -969,128 +969,213 @@ __device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDe
 // Split-K partial softmax attention.  Item = (chunk of 16 positions, KV head g); for each of the
 // gs query heads of group g it emits (max m, sum l, acc[hd]) over its positions.  Scores: one thread
 // per (head, position), a 16-lane DPP row per head for the max and the sum.
+// KV stage slots of one 16-position chunk, rounded to whole GEMV units
+__device__ __forceinline__ int kv_buf_slots(int hd) { return (2 * kv_slots(hd) + 3) & ~3; }
+// chunk buffers in stage A (up to 3: the copies of the next two chunks run while one is used)
+__device__ __forceinline__ int kv_nbuf(int hd) { return max(1, min(3, MK_STAGE_A_SLOTS / kv_buf_slots(hd))); }
+
+// Split-K attention over positions 0..pos.  A work item is (block of p.att_cpi 16-position chunks,
+// KV head g); item it = block * nkv + g.  Chunk by chunk, the item computes for each of the gs query
+// heads of group g the scores of its positions (one thread per (head, position), a 16-lane DPP row
+// per head for the max and the sum), the softmax numerators and acc[d] = sum p v_d; chunks after
+// the first of the item are merged into the running (max, sum, acc) in chunk order:
+//   M' = max(M, m), f = exp(M - M'), f' = exp(m - M'), acc' = acc f + a f', sum' = sum f + l f'.
+// The item publishes (M, sum, acc[hd]) per head.  With att_cpi = 1 an item is one chunk.
+// Staging: stage A holds nb = kv_nbuf(hd) chunk buffers; chunk k of the workgroup's sequence uses
+// buffer k % nb.  The caller has issued the copies of chunks 0 .. max(nb - 2, 0); when chunk k
+// starts it issues chunk k + nb - 1 into the buffer chunk k - 1 has finished with (chunk 0 issues
+// chunk nb - 1 into the last, unused buffer), then waits until only the copies of the chunks after
+// k may remain (chunk 0 waits for all of them).  Queries are gathered once per KV head; the keys and
+// values of position pos only by the chunk that holds it.
+__device__ __forceinline__ int att_items_count(const MkDecodeParams& p, int pos) {
+  const int nch = (pos + ATT_C) / ATT_C;
+  return ((nch + p.att_cpi - 1) / p.att_cpi) * p.nkv;
+}
+// chunk-level index (chunk * nkv + g) of chunk k of workgroup w's sequence (its items in order,
+// each item's chunks in order); -1 past the end
+__device__ __forceinline__ int att_chunk_at(const MkDecodeParams& p, int NW, int w, int pos, int k) {
+  const int items = att_items_count(p, pos);
+  const int nch = (pos + ATT_C) / ATT_C;
+  for (int it = w; it < items; it += NW) {
+    const int blk = it / p.nkv, g = it - blk * p.nkv;
+    const int c0 = blk * p.att_cpi, n = min(nch, c0 + p.att_cpi) - c0;
+    if (k < n) return (c0 + k) * p.nkv + g;
+    k -= n;
+  }
+  return -1;
+}
 __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                           int NW, int w, int pos, int wait_first, Tracer& tr) {
-  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv;
+  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, cpi = p.att_cpi;
   const int Lpos = pos + 1;
-  const int items = ((Lpos + ATT_C - 1) / ATT_C) * nkv;
+  const int nch = (Lpos + ATT_C - 1) / ATT_C;
+  const int items = att_items_count(p, pos);
   const float scale = 1.0f / sqrtf((float)hd);
   const int lpp = hd >> 2, pps = 64 / lpp, ks = kv_slots(hd);
+  const int nb = kv_nbuf(hd);
+  const int kvb = kv_buf_slots(hd);
+  int cnt0 = 0, cnt1 = 0, cnt2 = 0;  // copies this wave issued for the chunk in buffers 0, 1, 2
   LS float* qv = s.att;                // [gs][hd]
   LS float* kpos = qv + gs * hd;       // [hd]
   LS float* vpos = kpos + hd;          // [hd]
   LS float* pb = vpos + hd;            // [gs][16] probabilities (unnormalised)
-  LS float* ml = pb + gs * ATT_C;      // [gs][2]
-  const LS float* stf = (const LS float*)s.stB;
+  LS float* ml = pb + gs * ATT_C;      // [gs][2] this chunk's max and sum
+  LS float* racc = ml + 2 * gs;        // [gs][hd] running acc of the item
+  LS float* rml = racc + gs * hd;      // [2 (chunk parity)][gs][2] running max and sum
   const MK_G mk_u64* llq = L.ll_in;
   const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   const MK_G mk_u64* llv = llk + nkv * hd;
   (void)lpp;
+  int gq = -1;  // KV head whose queries are in qv
+  int k = 0;    // chunk sequence number in this workgroup (stage buffer)
   for (int it = w; it < items; it += NW) {
-    const int c = it / nkv, g = it - c * nkv;
-    const int j0 = c * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
-    const bool has_pos = j0 + nj == Lpos;
-    if (it != w) kv_stage(p, L, it, pos, s.stB);
-    const int n = gs * hd + (has_pos ? 2 * hd : 0);
-    const bool ok = gather_map(cx, n, [=](int f) {
-      if (f < gs * hd) return llq + g * gs * hd + f;
-      if (f < gs * hd + hd) return llk + g * hd + (f - gs * hd);
-      return llv + g * hd + (f - gs * hd - hd);
-    }, [=](int f, float v) { s.att[f] = v; });
-    tr.mark();
-    if (streamer()) {
-      if (it == w) wait_vm_n(wait_first);
-      else wait_vm<0>();
-    }
-    tr.mark();
-    if (wg_bar_or(s, !ok)) return false;
-    tr.mark();
-    // scores, softmax numerators, row max and sum (whole rows of 16 lanes take part in the DPP)
-    const int t = tid();
-    if (t < gs * ATT_C) {
-      const int i = t >> 4, jj = t & 15;
-      const bool valid = jj < nj;
-      float sc = -INFINITY;
-      if (valid) {
-        const int j = j0 + jj;
-        const LS float* kr = j == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
-        const LS float* qr = qv + i * hd;
-        const int n4 = hd >> 2;
-        const int start = jj % n4;  // staggered start: the 16 positions of a row read different banks
-        float a = 0.f;
-        for (int d0 = 0; d0 < n4; d0 += 8) {
-          f32x4 kk[8], qq[8];
-          const LS float* ka[8];
+    const int blk = it / nkv, g = it - blk * nkv;
+    const int c0 = blk * cpi, c1 = min(nch, c0 + cpi);
+    for (int c = c0; c < c1; ++c, ++k) {
+      const int j0 = c * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
+      const bool has_pos = j0 + nj == Lpos;
+      const LS float* stf = (const LS float*)(s.stA + (k % nb) * kvb * SLOT);
+      int pending = 0;  // copies issued after this chunk's that may stay outstanding
+      if (k > 0 || nb > 1) {
+        const int kn = k + nb - 1, bn = kn % nb;
+        const int cn = att_chunk_at(p, NW, w, pos, kn);
+        const int nc = cn >= 0 ? kv_stage(p, L, cn, pos, s.stA + bn * kvb * SLOT) : 0;
+        if (bn == 0) cnt0 = nc;
+        else if (bn == 1) cnt1 = nc;
+        else cnt2 = nc;
+        for (int j = 1; j < nb; ++j) {
+          const int b = (k + j) % nb;
+          pending += b == 0 ? cnt0 : (b == 1 ? cnt1 : cnt2);
+        }
+      }
+      const bool need_q = g != gq;
+      gq = g;
+      const int qoff = need_q ? 0 : gs * hd;  // records skipped
+      const int n = gs * hd + (has_pos ? 2 * hd : 0) - qoff;
+      const bool ok = gather_map(cx, n, [=](int f) {
+        f += qoff;
+        if (f < gs * hd) return llq + g * gs * hd + f;
+        if (f < gs * hd + hd) return llk + g * hd + (f - gs * hd);
+        return llv + g * hd + (f - gs * hd - hd);
+      }, [=](int f, float v) { s.att[f + qoff] = v; });
+      tr.mark();
+      if (streamer()) {
+        if (k == 0) wait_vm_n(wait_first);
+        else wait_vm_n(pending);
+      }
+      tr.mark();
+      if (wg_bar_or(s, !ok)) return false;
+      tr.mark();
+      // scores, softmax numerators, row max and sum (whole rows of 16 lanes take part in the DPP)
+      const int t = tid();
+      if (t < gs * ATT_C) {
+        const int i = t >> 4, jj = t & 15;
+        const bool valid = jj < nj;
+        float sc = -INFINITY;
+        if (valid) {
+          const int j = j0 + jj;
+          const LS float* kr = j == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
+          const LS float* qr = qv + i * hd;
+          const int n4 = hd >> 2;
+          const int start = jj % n4;  // staggered start: the 16 positions of a row read different banks
+          float a = 0.f;
+          for (int d0 = 0; d0 < n4; d0 += 8) {
+            f32x4 kk[8], qq[8];
+            const LS float* ka[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            int dd = d0 + k + start;
-            dd = (dd >= n4 ? dd - n4 : dd) * 4;
-            ka[k] = kr + (d0 + k < n4 ? dd : 0);
-            qq[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (d0 + k < n4) qq[k] = *(const LS f32x4*)(qr + dd);
+            for (int x = 0; x < 8; ++x) {
+              int dd = d0 + x + start;
+              dd = (dd >= n4 ? dd - n4 : dd) * 4;
+              ka[x] = kr + (d0 + x < n4 ? dd : 0);
+              qq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+              if (d0 + x < n4) qq[x] = *(const LS f32x4*)(qr + dd);
+            }
+            stage_f4x8(ka, kk);
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+              if (d0 + x >= n4) kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+              a = fmaf(kk[x].x, qq[x].x, a);
+              a = fmaf(kk[x].y, qq[x].y, a);
+              a = fmaf(kk[x].z, qq[x].z, a);
+              a = fmaf(kk[x].w, qq[x].w, a);
+            }
           }
-          stage_f4x8(ka, kk);
+          sc = a * scale;
+        }
+        const float m = row_max16(sc);
+        const float e = valid ? expf(sc - m) : 0.f;
+        const float l = row_sum16(e);
+        pb[i * ATT_C + jj] = e;
+        if (jj == 0) {
+          ml[2 * i] = m;
+          ml[2 * i + 1] = l;
+        }
+      }
+      tr.mark();
+      wg_bar();
+      tr.mark();
+      if (streamer()) {
+        const bool first = c == c0, last = c + 1 == c1;
+        const LS float* rin = rml + (k & 1) * 2 * gs;       // running (max, sum) before this chunk
+        LS float* rout = rml + ((k + 1) & 1) * 2 * gs;      // ... and after it
+        MK_G mk_u64* part = L.ll_part + (size_t)it * gs * (hd + 2);
+        for (int o = tid(); o < gs * hd; o += NCT) {
+          const int i = o / hd, d = o - i * hd;
+          float pv[ATT_C], vv[ATT_C];
+          const LS float* va[ATT_C];
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (d0 + k >= n4) kk[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int jj = 0; jj < ATT_C; ++jj) {
+            pv[jj] = pb[i * ATT_C + jj];  // zero beyond nj
+            va[jj] = (jj < nj && j0 + jj != pos) ? stf + (ks + jj / pps) * 256 + (jj % pps) * hd + d : vpos + d;
+          }
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            a = fmaf(kk[k].x, qq[k].x, a);
-            a = fmaf(kk[k].y, qq[k].y, a);
-            a = fmaf(kk[k].z, qq[k].z, a);
-            a = fmaf(kk[k].w, qq[k].w, a);
+          for (int q4 = 0; q4 < ATT_C; q4 += 4) {
+            float t4[4];
+            stage_f32x4(va[q4], va[q4 + 1], va[q4 + 2], va[q4 + 3], t4);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) vv[q4 + x] = q4 + x < nj ? t4[x] : 0.f;
+          }
+          float a = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < ATT_C; ++jj) a = fmaf(pv[jj], vv[jj], a);
+          float M = ml[2 * i], S = ml[2 * i + 1];
+          if (!first) {
+            const float Mr = rin[2 * i], Sr = rin[2 * i + 1];
+            const float Mn = fmaxf(Mr, M);
+            const float f = expf(Mr - Mn), f1 = expf(M - Mn);
+            a = fmaf(racc[o], f, a * f1);
+            S = fmaf(Sr, f, S * f1);
+            M = Mn;
+          }
+          if (last) {
+            ll_put(part + i * (hd + 2) + 2 + d, cx.epoch, a);
+            if (d == 0) {
+              ll_put(part + i * (hd + 2), cx.epoch, M);
+              ll_put(part + i * (hd + 2) + 1, cx.epoch, S);
+            }
+          } else {
+            racc[o] = a;
+            if (d == 0) {
+              rout[2 * i] = M;
+              rout[2 * i + 1] = S;
+            }
           }
         }
-        sc = a * scale;
       }
-      const float m = row_max16(sc);
-      const float e = valid ? expf(sc - m) : 0.f;
-      const float l = row_sum16(e);
-      pb[i * ATT_C + jj] = e;
-      if (jj == 0) {
-        ml[2 * i] = m;
-        ml[2 * i + 1] = l;
-      }
+      wg_bar();  // LDS and the KV slots are reused by the next chunk
     }
-    tr.mark();
-    wg_bar();
-    tr.mark();
-    if (streamer()) {
-      MK_G mk_u64* part = L.ll_part + (size_t)it * gs * (hd + 2);
-      for (int o = tid(); o < gs * hd; o += NCT) {
-        const int i = o / hd, d = o - i * hd;
-        float pv[ATT_C], vv[ATT_C];
-        const LS float* va[ATT_C];
-#pragma unroll
-        for (int jj = 0; jj < ATT_C; ++jj) {
-          pv[jj] = pb[i * ATT_C + jj];  // zero beyond nj
-          va[jj] = (jj < nj && j0 + jj != pos) ? stf + (ks + jj / pps) * 256 + (jj % pps) * hd + d : vpos + d;
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < ATT_C; q4 += 4) {
-          float t4[4];
-          stage_f32x4(va[q4], va[q4 + 1], va[q4 + 2], va[q4 + 3], t4);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) vv[q4 + k] = q4 + k < nj ? t4[k] : 0.f;
-        }
-        float a = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < ATT_C; ++jj) a = fmaf(pv[jj], vv[jj], a);
-        ll_put(part + i * (hd + 2) + 2 + d, cx.epoch, a);
-      }
-      if (tid() < 2 * gs) ll_put(part + (tid() >> 1) * (hd + 2) + (tid() & 1), cx.epoch, ml[tid()]);
-    }
-    wg_bar();  // LDS and the KV slots are reused by the next item
   }
   if (w >= items && streamer()) wait_vm_n(wait_first);
   return true;
 }
 
-// log-sum-exp merge (in chunk order) of the partials for o[o0..o1) -> records
+// log-sum-exp merge (in item order) of the item partials for o[o0..o1) -> records
 __device__ __forceinline__ bool att_combine(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                             int o0, int o1, int pos) {
   const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv;
-  const int nch = (pos + ATT_C) / ATT_C;
+  const int nch = att_items_count(p, pos) / nkv;  // items per KV head
   const int nown = o1 - o0;
   if (nown <= 0) return true;
   LS float* stage = s.att;

@@ -78,6 +78,7 @@ struct MkDecodeParams {
   int32_t n_layers, D, ffn, vocab;
   int32_t H, dk, dv, nq, nkv, hd;
   int32_t max_ctx, max_items;
+  int32_t att_cpi;               // 16-position chunks per split-K attention work item
   float rms_eps, l2_eps;
   MK_G const uint16_t* embed;    // [vocab][D]
   MK_G const uint16_t* g_final;  // BF16 final RMSNorm gain [D]

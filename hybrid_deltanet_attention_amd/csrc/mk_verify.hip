@@ -417,145 +417,177 @@ __device__ __forceinline__ void att_qkv_v(const MkDecodeParams& p, const MkLayer
   });
 }
 
-// Split-K attention items over positions 0 .. pos + nt - 1.  Item (16-position chunk c, KV head g)
-// serves positions t >= tmin (those whose window reaches the chunk); keys and values of positions
-// already in the cache (< pos) are loaded by the streaming waves, those of this launch's positions
-// come from the records.  For each served position and query head of the group it emits (max,
-// sum, acc[hd]) over the chunk's positions <= pos + t, computed exactly as a decode item would.
+// Split-K attention items over positions 0 .. pos + nt - 1, with the decode kernel's items: (block
+// of att_cpi 16-position chunks, KV head g).  A chunk serves the positions t >= tmin whose window
+// reaches it; keys and values of positions already in the cache (< pos) are loaded by the streaming
+// waves, those of this launch's positions come from the records.  Per served position and query
+// head the chunk's (max, sum, acc) are formed exactly as a decode chunk forms them and merged into
+// the position's running values for the item in chunk order, with the decode kernel's formula; a
+// position publishes its (max, sum, acc[hd]) at its last chunk of the item.
 __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                             LS float* sc, int NW, int w, int pos, int nt) {
-  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, C = ATT_C, rows_in = L.rows_in;
+  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, C = ATT_C, rows_in = L.rows_in, cpi = p.att_cpi;
   const int Lmax = pos + nt;
-  const int items = ((Lmax + C - 1) / C) * nkv;
+  const int nch = (Lmax + C - 1) / C;
+  const int items = ((nch + cpi - 1) / cpi) * nkv;
   const float scale = 1.0f / sqrtf((float)hd);
-  LS float* qv = sc;                 // [nt][gs][hd]
-  LS float* kc = qv + nt * gs * hd;  // [C][hd]
-  LS float* vc = kc + C * hd;        // [C][hd]
-  LS float* pb = vc + C * hd;        // [nt][gs][C] probabilities (unnormalised)
-  LS float* ml = pb + nt * gs * C;   // [nt][gs][2]
+  LS float* qv = sc;                   // [nt][gs][hd]
+  LS float* kc = qv + nt * gs * hd;    // [C][hd]
+  LS float* vc = kc + C * hd;          // [C][hd]
+  LS float* pb = vc + C * hd;          // [nt][gs][C] probabilities (unnormalised)
+  LS float* ml = pb + nt * gs * C;     // [nt][gs][2] this chunk's max and sum
+  LS float* racc = ml + 2 * nt * gs;   // [nt][gs][hd] running acc of the item
+  LS float* rml = racc + nt * gs * hd; // [2 (chunk parity)][nt][gs][2] running max and sum
   const MK_G mk_u64* llq = L.ll_in;
   const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   const MK_G mk_u64* llv = llk + nkv * hd;
   const size_t tstride = (size_t)p.max_items * gs * (hd + 2);  // partial records per position
+  int gq = -1;  // KV head whose queries are in qv
+  int k = 0;    // chunk sequence number in this workgroup (running-value parity)
   for (int it = w; it < items; it += NW) {
-    const int c = it / nkv, g = it - c * nkv;
-    const int j0 = c * C;
-    const int tmin = max(0, j0 - pos);
-    const int jend = min(Lmax, j0 + C);
-    const int jnew = max(j0, pos);
-    const int nnew = max(0, jend - jnew);
-    const int nqr = (nt - tmin) * gs * hd;
-    const int nkvr = nnew * hd;
-    const bool ok = gather_map_all(cx, nqr + 2 * nkvr, [=](int f) {
-      if (f < nqr) {
-        const int tt = f / (gs * hd), r = f - tt * gs * hd;
-        return llq + (size_t)(tmin + tt) * rows_in + g * gs * hd + r;
-      }
-      f -= nqr;
-      const int sel = f >= nkvr ? 1 : 0;
-      f -= sel * nkvr;
-      const int jj = f / hd, d = f - jj * hd;
-      return (sel ? llv : llk) + (size_t)(jnew + jj - pos) * rows_in + g * hd + d;
-    }, [=](int f, float v) {
-      if (f < nqr) {
-        qv[tmin * gs * hd + f] = v;
-      } else {
+    const int blk = it / nkv, g = it - blk * nkv;
+    const int c0 = blk * cpi, c1 = min(nch, c0 + cpi);
+    for (int c = c0; c < c1; ++c, ++k) {
+      const int j0 = c * C;
+      const int tmin = max(0, j0 - pos);
+      const int jend = min(Lmax, j0 + C);
+      const int jnew = max(j0, pos);
+      const int nnew = max(0, jend - jnew);
+      const int nqr = g != gq ? nt * gs * hd : 0;  // queries: once per KV head
+      gq = g;
+      const int nkvr = nnew * hd;
+      const bool ok = gather_map_all(cx, nqr + 2 * nkvr, [=](int f) {
+        if (f < nqr) {
+          const int tt = f / (gs * hd), r = f - tt * gs * hd;
+          return llq + (size_t)tt * rows_in + g * gs * hd + r;
+        }
         f -= nqr;
         const int sel = f >= nkvr ? 1 : 0;
         f -= sel * nkvr;
         const int jj = f / hd, d = f - jj * hd;
-        (sel ? vc : kc)[(jnew - j0 + jj) * hd + d] = v;
+        return (sel ? llv : llk) + (size_t)(jnew + jj - pos) * rows_in + g * hd + d;
+      }, [=](int f, float v) {
+        if (f < nqr) {
+          qv[f] = v;
+        } else {
+          f -= nqr;
+          const int sel = f >= nkvr ? 1 : 0;
+          f -= sel * nkvr;
+          const int jj = f / hd, d = f - jj * hd;
+          (sel ? vc : kc)[(jnew - j0 + jj) * hd + d] = v;
+        }
+      });
+      if (streamer()) {
+        const int nold = min(pos, jend) - j0;  // cached positions of the chunk (may be <= 0)
+        const int h4 = hd >> 2;
+        for (int x = tid(); x < nold * h4; x += NCT) {
+          const int jj = x / h4, d = (x - jj * h4) * 4;
+          const size_t gi = ((size_t)g * p.max_ctx + j0 + jj) * hd + d;
+          const f32x4 kk = *(const MK_G f32x4*)(L.Kc + gi);
+          const f32x4 vv = *(const MK_G f32x4*)(L.Vc + gi);
+          *(LS f32x4*)(kc + jj * hd + d) = kk;
+          *(LS f32x4*)(vc + jj * hd + d) = vv;
+        }
       }
-    });
-    if (streamer()) {
-      const int nold = min(pos, jend) - j0;  // cached positions of the chunk (may be <= 0)
-      const int h4 = hd >> 2;
-      for (int i = tid(); i < nold * h4; i += NCT) {
-        const int jj = i / h4, d = (i - jj * h4) * 4;
-        const size_t gi = ((size_t)g * p.max_ctx + j0 + jj) * hd + d;
-        const f32x4 kk = *(const MK_G f32x4*)(L.Kc + gi);
-        const f32x4 vv = *(const MK_G f32x4*)(L.Vc + gi);
-        *(LS f32x4*)(kc + jj * hd + d) = kk;
-        *(LS f32x4*)(vc + jj * hd + d) = vv;
-      }
-    }
-    if (wg_bar_or(s, !ok)) return false;
-    // scores, softmax numerators, row max and sum: one thread per (position, head, slot), whole
-    // 16-lane rows
-    const int nrow = (nt - tmin) * gs * C;
-    for (int b0 = 0; b0 < nrow; b0 += MK_NT) {
-      const int f = b0 + tid();
-      if (f < nrow) {
-        const int tt = f / (gs * C), r = f - tt * gs * C;
-        const int i = r / C, jj = r - i * C;
-        const int t = tmin + tt;
-        const int nj = min(pos + t + 1, j0 + C) - j0;
-        const bool valid = jj < nj;
-        float scv = -INFINITY;
-        if (valid) {
-          const LS float* kr = kc + jj * hd;
-          const LS float* qr = qv + (t * gs + i) * hd;
-          const int n4 = hd >> 2;
-          const int start = jj % n4;
-          float a = 0.f;
-          for (int d0 = 0; d0 < n4; d0 += 8) {
-            f32x4 kk[8], qq[8];
+      if (wg_bar_or(s, !ok)) return false;
+      // scores, softmax numerators, row max and sum: one thread per (position, head, slot), whole
+      // 16-lane rows
+      const int nrow = (nt - tmin) * gs * C;
+      for (int b0 = 0; b0 < nrow; b0 += MK_NT) {
+        const int f = b0 + tid();
+        if (f < nrow) {
+          const int tt = f / (gs * C), r = f - tt * gs * C;
+          const int i = r / C, jj = r - i * C;
+          const int t = tmin + tt;
+          const int nj = min(pos + t + 1, j0 + C) - j0;
+          const bool valid = jj < nj;
+          float scv = -INFINITY;
+          if (valid) {
+            const LS float* kr = kc + jj * hd;
+            const LS float* qr = qv + (t * gs + i) * hd;
+            const int n4 = hd >> 2;
+            const int start = jj % n4;
+            float a = 0.f;
+            for (int d0 = 0; d0 < n4; d0 += 8) {
+              f32x4 kk[8], qq[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              int dd = d0 + k + start;
-              dd = (dd >= n4 ? dd - n4 : dd) * 4;
-              kk[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-              qq[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-              if (d0 + k < n4) {
-                kk[k] = *(const LS f32x4*)(kr + dd);
-                qq[k] = *(const LS f32x4*)(qr + dd);
+              for (int x = 0; x < 8; ++x) {
+                int dd = d0 + x + start;
+                dd = (dd >= n4 ? dd - n4 : dd) * 4;
+                kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                qq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (d0 + x < n4) {
+                  kk[x] = *(const LS f32x4*)(kr + dd);
+                  qq[x] = *(const LS f32x4*)(qr + dd);
+                }
+              }
+#pragma unroll
+              for (int x = 0; x < 8; ++x) {
+                a = fmaf(kk[x].x, qq[x].x, a);
+                a = fmaf(kk[x].y, qq[x].y, a);
+                a = fmaf(kk[x].z, qq[x].z, a);
+                a = fmaf(kk[x].w, qq[x].w, a);
               }
             }
+            scv = a * scale;
+          }
+          const float m = row_max16(scv);
+          const float e = valid ? expf(scv - m) : 0.f;
+          const float l = row_sum16(e);
+          pb[(t * gs + i) * C + jj] = e;
+          if (jj == 0) {
+            ml[2 * (t * gs + i)] = m;
+            ml[2 * (t * gs + i) + 1] = l;
+          }
+        }
+      }
+      wg_bar();
+      if (streamer()) {
+        const LS float* rin = rml + (k & 1) * 2 * nt * gs;   // running (max, sum) before this chunk
+        LS float* rout = rml + ((k + 1) & 1) * 2 * nt * gs;  // ... and after it
+        for (int o = tid(); o < (nt - tmin) * gs * hd; o += NCT) {
+          const int tt = o / (gs * hd), r = o - tt * gs * hd;
+          const int i = r / hd, d = r - i * hd;
+          const int t = tmin + tt;
+          const int ti = t * gs + i;
+          const int nj = min(pos + t + 1, j0 + C) - j0;
+          float a = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              a = fmaf(kk[k].x, qq[k].x, a);
-              a = fmaf(kk[k].y, qq[k].y, a);
-              a = fmaf(kk[k].z, qq[k].z, a);
-              a = fmaf(kk[k].w, qq[k].w, a);
+          for (int jj = 0; jj < ATT_C; ++jj) {
+            const float pv = pb[ti * C + jj];
+            const float vv = jj < nj ? vc[jj * hd + d] : 0.f;
+            a = fmaf(pv, vv, a);
+          }
+          // position t's chunks of this item: c0 .. its last visible chunk
+          const bool first = c == c0;
+          const bool last = c + 1 == min(c1, (pos + t) / C + 1);
+          float M = ml[2 * ti], S = ml[2 * ti + 1];
+          if (!first) {
+            const float Mr = rin[2 * ti], Sr = rin[2 * ti + 1];
+            const float Mn = fmaxf(Mr, M);
+            const float f = expf(Mr - Mn), f1 = expf(M - Mn);
+            a = fmaf(racc[ti * hd + d], f, a * f1);
+            S = fmaf(Sr, f, S * f1);
+            M = Mn;
+          }
+          if (last) {
+            MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2) + i * (hd + 2);
+            ll_put(part + 2 + d, cx.epoch, a);
+            if (d == 0) {
+              ll_put(part, cx.epoch, M);
+              ll_put(part + 1, cx.epoch, S);
+            }
+          } else {
+            racc[ti * hd + d] = a;
+            if (d == 0) {
+              rout[2 * ti] = M;
+              rout[2 * ti + 1] = S;
             }
           }
-          scv = a * scale;
-        }
-        const float m = row_max16(scv);
-        const float e = valid ? expf(scv - m) : 0.f;
-        const float l = row_sum16(e);
-        pb[(t * gs + i) * C + jj] = e;
-        if (jj == 0) {
-          ml[2 * (t * gs + i)] = m;
-          ml[2 * (t * gs + i) + 1] = l;
         }
       }
+      wg_bar();  // LDS is reused by the next chunk
     }
-    wg_bar();
-    if (streamer()) {
-      for (int o = tid(); o < (nt - tmin) * gs * hd; o += NCT) {
-        const int tt = o / (gs * hd), r = o - tt * gs * hd;
-        const int i = r / hd, d = r - i * hd;
-        const int t = tmin + tt;
-        const int nj = min(pos + t + 1, j0 + C) - j0;
-        float a = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < ATT_C; ++jj) {
-          const float pv = pb[(t * gs + i) * C + jj];
-          const float vv = jj < nj ? vc[jj * hd + d] : 0.f;
-          a = fmaf(pv, vv, a);
-        }
-        MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2);
-        ll_put(part + i * (hd + 2) + 2 + d, cx.epoch, a);
-      }
-      for (int o = tid(); o < (nt - tmin) * gs * 2; o += NCT) {
-        const int tt = o / (gs * 2), r = o - tt * gs * 2;
-        const int t = tmin + tt;
-        MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2);
-        ll_put(part + (r >> 1) * (hd + 2) + (r & 1), cx.epoch, ml[2 * t * gs + r]);
-      }
-    }
-    wg_bar();  // LDS is reused by the next item
   }
   return true;
 }
@@ -564,20 +596,24 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
 // one gather serves all positions.  Position t (at pos + t) merges (pos + t) / 16 + 1 chunks; its
 // staging block of vn outputs starts after the blocks of positions 0..t-1.  cap: floats of LDS
 // staging available.
-__device__ __forceinline__ int comb_nch(int pos, int t) { return (pos + t + ATT_C) / ATT_C; }
-// chunks of positions 0 .. t-1 together
-__device__ __forceinline__ int comb_before(int pos, int t) {
+// items per KV head that position t (at pos + t) merges
+__device__ __forceinline__ int comb_nch(int pos, int t, int cpi) {
+  const int nch = (pos + t + ATT_C) / ATT_C;
+  return (nch + cpi - 1) / cpi;
+}
+// items of positions 0 .. t-1 together
+__device__ __forceinline__ int comb_before(int pos, int t, int cpi) {
   int n = 0;
-  for (int u = 0; u < t; ++u) n += comb_nch(pos, u);
+  for (int u = 0; u < t; ++u) n += comb_nch(pos, u, cpi);
   return n;
 }
 __device__ __forceinline__ bool att_combine_v(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx,
                                               const Lds& s, LS float* stage, int cap, int o0, int o1, int pos,
                                               int nt) {
-  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, K = p.nq * hd;
+  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, K = p.nq * hd, cpi = p.att_cpi;
   const int nown = o1 - o0;
   if (nown <= 0) return true;
-  const int tot = comb_before(pos, nt);
+  const int tot = comb_before(pos, nt, cpi);
   const size_t tstride = (size_t)p.max_items * gs * (hd + 2);
   const int vpp = max(1, cap / (3 * tot));
   for (int v0 = 0; v0 < nown; v0 += vpp) {
@@ -585,9 +621,9 @@ __device__ __forceinline__ bool att_combine_v(const MkDecodeParams& p, const MkL
     const bool ok = gather_map_all(cx, vn * 3 * tot, [=](int f) {
       const int cf = f / (3 * vn);  // chunk slots of the positions before, in units of vn * 3 records
       int t = 0;
-      while (t + 1 < nt && comb_before(pos, t + 1) <= cf) ++t;
-      f -= 3 * vn * comb_before(pos, t);
-      const int n = comb_nch(pos, t);
+      while (t + 1 < nt && comb_before(pos, t + 1, cpi) <= cf) ++t;
+      f -= 3 * vn * comb_before(pos, t, cpi);
+      const int n = comb_nch(pos, t, cpi);
       const int which = f % 3;
       const int vc = f / 3;
       const int v = vc / n, c = vc - v * n;
@@ -601,8 +637,8 @@ __device__ __forceinline__ bool att_combine_v(const MkDecodeParams& p, const MkL
     if (streamer()) {
       for (int pr = wave(); pr < nt * vn; pr += NCW) {
         const int t = pr / vn, v = pr - t * vn;
-        const int n = comb_nch(pos, t);
-        const LS float* bp = stage + 3 * vn * comb_before(pos, t) + (size_t)v * n * 3;
+        const int n = comb_nch(pos, t, cpi);
+        const LS float* bp = stage + 3 * vn * comb_before(pos, t, cpi) + (size_t)v * n * 3;
         float M = -INFINITY;
         for (int c = lane(); c < n; c += 64) M = fmaxf(M, bp[3 * c]);
         M = wave_max(M);

@@ -67,6 +67,13 @@ def test_tiny_mha():
     _check_run(cfg, W, synth.make_prompt(cfg.vocab, 9, 4), 12)
 
 
+def test_tiny_multi_chunk_attention_items():
+    # a cache of 8,192 positions: each split-K attention item merges 4 chunks of 16 positions
+    cfg = synth.get_config("tiny", max_ctx=8192)
+    W = synth.make_weights(cfg, 8)
+    _check_run(cfg, W, synth.make_prompt(cfg.vocab, 150, 8), 24)
+
+
 def test_tiny_ragged_shapes():
     # sizes that are not multiples of the 512-column segment, odd head counts, long attention chunks
     cfg = synth.get_config("tiny", hidden=200, ffn=328, dn_heads=3, dn_dk=32, dn_dv=48, n_q_heads=6,

@@ -150,6 +150,15 @@ def test_tiny_k0_and_odd_grid():
     assert _check_against_decode(cfg, W, prompt, lambda c: c, 4, grid=37, label="grid 37") == 4
 
 
+def test_tiny_multi_chunk_attention_items():
+    """a cache of 8,192 positions: split-K attention items of 4 chunks, merged inside the item"""
+    cfg = synth.get_config("tiny", max_ctx=8192)
+    W = synth.make_weights(cfg, 10)
+    prompt = synth.make_prompt(cfg.vocab, 150, 10)
+    assert _check_against_decode(cfg, W, prompt, lambda c: c, 5, label="cpi 4 greedy") == 5
+    _check_against_decode(cfg, W, prompt, lambda c: synth.make_drafts(cfg.vocab, len(c), 10), 5, label="cpi 4 random")
+
+
 def test_tiny_ragged_shapes():
     cfg = synth.get_config("tiny", hidden=200, ffn=328, dn_heads=3, dn_dk=32, dn_dv=48, n_q_heads=6,
                            n_kv_heads=3, head_dim=40, vocab=1000, n_layers=5, max_ctx=80)
