@@ -24,6 +24,7 @@ typedef unsigned int u32;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // LDS is read through native vector types: loads of HIP's float4 / float2 structs are split and
 // merged again late in code generation, which drops what the compiler knows about the access and
@@ -965,6 +966,214 @@ __global__ void __launch_bounds__(256) pf_attention_kernel(const float* __restri
   }
 }
 
+// ------------------------------------------------------------------------ attention on MFMA
+// Causal attention for the chunk's queries over cache positions 0 .. p0 + t on
+// v_mfma_f32_32x32x16_bf16, every operand split into BF16 hi + lo and each product formed as
+// hi.hi + hi.lo + lo.hi (the lo.lo term is below 2^-16 relative).  A workgroup (4 waves) takes one
+// KV head g, 32 consecutive queries and up to 4 query heads of the group, one per wave.  Key blocks
+// of 32 positions go through LDS as BF16 hi/lo, keys as [key][dim] and values transposed as
+// [dim][key]; the next block's loads are in flight while the current one is used.  Per block and
+// wave:
+//   S^T = K Q^T (32 keys x 32 queries): a lane holds 16 keys of one query, so the query's max and
+//   sum take its 16 registers and the partner lane l ^ 32;
+//   online softmax: m' = max(m, max_j s), P = exp(S - m'), l' = l e^(m - m') + sum P, O *= e^(m - m');
+//   O += P V (32 queries x HD in HD / 32 accumulator tiles), P through LDS as BF16 hi/lo.
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8& h, bf16x8& lo) {
+  u32x4 hw, lw;
+  uint16_t hb[8], lb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hb[i] = f2bf(v[i]);
+    lb[i] = f2bf(v[i] - bf16f(hb[i]));
+  }
+  hw = u32x4{hb[0] | ((u32)hb[1] << 16), hb[2] | ((u32)hb[3] << 16), hb[4] | ((u32)hb[5] << 16), hb[6] | ((u32)hb[7] << 16)};
+  lw = u32x4{lb[0] | ((u32)lb[1] << 16), lb[2] | ((u32)lb[3] << 16), lb[4] | ((u32)lb[5] << 16), lb[6] | ((u32)lb[7] << 16)};
+  h = __builtin_bit_cast(bf16x8, hw);
+  lo = __builtin_bit_cast(bf16x8, lw);
+}
+
+template <int HD>
+__global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restrict__ Q, const float* __restrict__ Kc,
+                                                           const float* __restrict__ Vc, int T, int p0, int nq, int nkv,
+                                                           int max_ctx, uint16_t* __restrict__ Ohi,
+                                                           uint16_t* __restrict__ Olo, int ldo) {
+  constexpr int KS = HD / 16;         // k-steps of S^T
+  constexpr int DT = HD / 32;         // accumulator tiles of O
+  constexpr int LPT = 32 * HD / 256;  // floats of K (and of V) per thread and block
+  static_assert(LPT % 4 == 0, "whole 16-byte loads");
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  uint16_t* Kh = (uint16_t*)sm;     // [32][HD]
+  uint16_t* Kl = Kh + 32 * HD;
+  uint16_t* Vh = Kl + 32 * HD;      // [HD][32]
+  uint16_t* Vl = Vh + HD * 32;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  char* wb = (char*)(Vl + HD * 32) + wv * (4 * 32 * 32 + 2 * 32 * 4);
+  uint16_t* Ph = (uint16_t*)wb;     // [32 queries][32 keys]
+  uint16_t* Pl = Ph + 32 * 32;
+  float* cr = (float*)(Pl + 32 * 32);  // [32] rescale of the running output
+  float* lsm = cr + 32;                // [32] final sums
+  const int gs = nq / nkv, nquad = (gs + 3) / 4, ntile = (T + 31) / 32;
+  int b = blockIdx.x;
+  const int tile = b % ntile;
+  b /= ntile;
+  const int quad = b % nquad, g = b / nquad;
+  const int il = quad * 4 + wv;
+  const bool live = il < gs;
+  const int hq = g * gs + min(il, gs - 1);
+  const int t0 = tile * 32;
+  const int tq = t0 + (l & 31);                   // this lane's query
+  const int jend = p0 + min(T, t0 + 32);          // keys [0, jend)
+  const int Pq = tq < T ? p0 + tq : jend - 1;     // its last visible key (rows past T see all)
+  const int nblk = (jend + 31) / 32;
+  const float scale = 1.0f / sqrtf((float)HD);
+  const int hi32 = l >> 5;
+  // Q fragments: B operand of S^T (column = query, k = dims)
+  bf16x8 qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float v[8];
+    const float* qp = Q + ((size_t)min(tq, T - 1) * nq + hq) * HD + ks * 16 + hi32 * 8;
+    const f32x4 a = *(const f32x4*)qp, c = *(const f32x4*)(qp + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    split8(v, qh[ks], ql[ks]);
+  }
+  // K / V block loads: thread -> LPT / 4 pieces of K and of V
+  f32x4 kr[LPT / 4], vr[LPT / 4];
+  auto load_blk = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < LPT / 4; ++i) {
+      const int e = (i * 256 + tid) * 4;
+      const int key = e / HD, d = e - key * HD;
+      const int j = min(blk * 32 + key, jend - 1);
+      const size_t gi = ((size_t)g * max_ctx + j) * HD + d;
+      kr[i] = *(const f32x4*)(Kc + gi);
+      vr[i] = *(const f32x4*)(Vc + gi);
+    }
+  };
+  auto store_blk = [&]() {
+#pragma unroll
+    for (int i = 0; i < LPT / 4; ++i) {
+      const int e = (i * 256 + tid) * 4;
+      const int key = e / HD, d = e - key * HD;
+      const float kv[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+      const float vv[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+      uint16_t kh[4], kl[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        kh[x] = f2bf(kv[x]);
+        kl[x] = f2bf(kv[x] - bf16f(kh[x]));
+        const uint16_t h = f2bf(vv[x]);
+        Vh[(d + x) * 32 + key] = h;
+        Vl[(d + x) * 32 + key] = f2bf(vv[x] - bf16f(h));
+      }
+      *(u32x2*)(Kh + key * HD + d) = u32x2{kh[0] | ((u32)kh[1] << 16), kh[2] | ((u32)kh[3] << 16)};
+      *(u32x2*)(Kl + key * HD + d) = u32x2{kl[0] | ((u32)kl[1] << 16), kl[2] | ((u32)kl[3] << 16)};
+    }
+  };
+  f32x16 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;
+  load_blk(0);
+  store_blk();
+  lds_bar();
+  for (int kb = 0; kb < nblk; ++kb) {
+    if (kb + 1 < nblk) load_blk(kb + 1);  // in flight during this block
+    if (live) {
+      f32x16 st = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int kd = ks * 16 + hi32 * 8;
+        const bf16x8 kh = *(const bf16x8*)(Kh + (l & 31) * HD + kd);
+        const bf16x8 kl = *(const bf16x8*)(Kl + (l & 31) * HD + kd);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[ks], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[ks], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[ks], st, 0, 0, 0);
+      }
+      // register r: key kb*32 + 8 (r / 4) + 4 (l / 32) + r % 4 of query tq
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kb * 32 + 8 * (r >> 2) + 4 * hi32 + (r & 3);
+        st[r] = j <= Pq ? st[r] * scale : -INFINITY;
+        mloc = fmaxf(mloc, st[r]);
+      }
+      const float mb = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float mn = fmaxf(m, mb);  // finite: key 0 is visible to every query
+      const float corr = expf(m - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint16_t h[4], lo[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float pv = expf(st[r4 * 4 + x] - mn);  // 0 for masked keys
+          ls += pv;
+          h[x] = f2bf(pv);
+          lo[x] = f2bf(pv - bf16f(h[x]));
+        }
+        const int o = (l & 31) * 32 + 8 * r4 + 4 * hi32;
+        *(u32x2*)(Ph + o) = u32x2{h[0] | ((u32)h[1] << 16), h[2] | ((u32)h[3] << 16)};
+        *(u32x2*)(Pl + o) = u32x2{lo[0] | ((u32)lo[1] << 16), lo[2] | ((u32)lo[3] << 16)};
+      }
+      lsum = fmaf(lsum, corr, ls + __shfl_xor(ls, 32, 64));
+      m = mn;
+      if (l < 32) cr[l] = corr;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's P and rescale writes are done
+      asm volatile("" ::: "memory");
+      // O rows (queries) of register r: 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 c4 = *(const f32x4*)(cr + 8 * r4 + 4 * hi32);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          O[dt][r4 * 4 + 0] *= c4.x;
+          O[dt][r4 * 4 + 1] *= c4.y;
+          O[dt][r4 * 4 + 2] *= c4.z;
+          O[dt][r4 * 4 + 3] *= c4.w;
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kq = s2 * 16 + hi32 * 8;
+        const bf16x8 ph = *(const bf16x8*)(Ph + (l & 31) * 32 + kq);
+        const bf16x8 pl = *(const bf16x8*)(Pl + (l & 31) * 32 + kq);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 vh = *(const bf16x8*)(Vh + (dt * 32 + (l & 31)) * 32 + kq);
+          const bf16x8 vl = *(const bf16x8*)(Vl + (dt * 32 + (l & 31)) * 32 + kq);
+          O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, vh, O[dt], 0, 0, 0);
+          O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, vl, O[dt], 0, 0, 0);
+          O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vh, O[dt], 0, 0, 0);
+        }
+      }
+    }
+    lds_bar();  // every wave is done with this block's K / V
+    if (kb + 1 < nblk) {
+      store_blk();
+      lds_bar();
+    }
+  }
+  if (!live) return;
+  if (l < 32) lsm[l] = lsum;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const f32x4 l4 = *(const f32x4*)(lsm + 8 * r4 + 4 * hi32);
+    const float inv[4] = {1.0f / l4.x, 1.0f / l4.y, 1.0f / l4.z, 1.0f / l4.w};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int t = t0 + 8 * r4 + 4 * hi32 + x;
+      if (t < T) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          split_store(O[dt][r4 * 4 + x] * inv[x], Ohi, Olo, (size_t)t * ldo + hq * HD + dt * 32 + (l & 31));
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------ LM head on one row
 // x -> rmsnorm(x) * g -> logits = E . xn over rows [w * rpw, ...); per-workgroup (max, index) with
 // the lowest index among equal maxima
@@ -1183,6 +1392,18 @@ extern "C" int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, in
 
 extern "C" int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,
                                int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream) {
+  if (hd == 64 || hd == 128) {
+    // MFMA path: workgroups = KV heads x groups of 4 query heads x 32-query tiles
+    const int gs = nq / nkv;
+    const dim3 grid(nkv * ((gs + 3) / 4) * ((T + 31) / 32));
+    const size_t lds = (size_t)4 * 32 * hd * 2 + 4 * (4 * 32 * 32 + 2 * 32 * 4);
+    hipStream_t st = (hipStream_t)stream;
+    if (hd == 64)
+      hipLaunchKernelGGL(pf_attn_mfma_kernel<64>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo);
+    else
+      hipLaunchKernelGGL(pf_attn_mfma_kernel<128>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo);
+    return MK_LAUNCH_OK();
+  }
   const int gs = nq / nkv, QB = 16 / gs;
   const int lpp = hd / 4, pps = 64 / lpp, nsl = (KB + pps - 1) / pps;
   const size_t lds = ((size_t)2 * 2 * nsl * 256 + 16 * HDM + 16 * KB + 16) * 4;
