@@ -811,7 +811,7 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
         float* Kc = (float*)(ws + lo.Kc);
         float* Vc = (float*)(ws + lo.Vc);
         rc |= mk_pf_att_rope(Y, ldy, T, p0, nq, nkv, hd, c.max_ctx, rcos, rsin, Q, Kc, Vc, st);
-        rc |= mk_pf_attention(Q, Kc, Vc, T, p0, nq, nkv, hd, c.max_ctx, Ahi, Alo, lda, st);
+        rc |= mk_pf_attention(Q, Kc, Vc, T, p0, nq, nkv, hd, c.max_ctx, Ahi, Alo, lda, PK, PKN, st);
       } else {
         rc |= mk_pf_dn_prep(Y, ldy, T, H, dk, dv, c.l2_eps, QK, AB, st);
         rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, Ahi, Alo, lda,

@@ -131,7 +131,7 @@ int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, in
 int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, int max_ctx, const float* rcos,
                    const float* rsin, float* Q, float* Kc, float* Vc, void* stream);
 int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,
-                    int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream);
+                    int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, float* P, size_t p_floats, void* stream);
 int mk_pf_lmhead(const float* x, int D, const uint16_t* g, float eps, const uint16_t* E, int vocab, float* logits,
                  float* part, int nwg, void* stream);
 int mk_pf_finish(const float* part, int nwg, int32_t* next, MkCtl* ctl, int32_t pos, void* stream);

@@ -996,7 +996,8 @@ template <int HD>
 __global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restrict__ Q, const float* __restrict__ Kc,
                                                            const float* __restrict__ Vc, int T, int p0, int nq, int nkv,
                                                            int max_ctx, uint16_t* __restrict__ Ohi,
-                                                           uint16_t* __restrict__ Olo, int ldo) {
+                                                           uint16_t* __restrict__ Olo, int ldo, int nsplit,
+                                                           float* __restrict__ part) {
   constexpr int KS = HD / 16;         // k-steps of S^T
   constexpr int DT = HD / 32;         // accumulator tiles of O
   constexpr int LPT = 32 * HD / 256;  // floats of K (and of V) per thread and block
@@ -1014,6 +1015,8 @@ __global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restri
   float* lsm = cr + 32;                // [32] final sums
   const int gs = nq / nkv, nquad = (gs + 3) / 4, ntile = (T + 31) / 32;
   int b = blockIdx.x;
+  const int split = b % nsplit;
+  b /= nsplit;
   const int tile = b % ntile;
   b /= ntile;
   const int quad = b % nquad, g = b / nquad;
@@ -1024,7 +1027,10 @@ __global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restri
   const int tq = t0 + (l & 31);                   // this lane's query
   const int jend = p0 + min(T, t0 + 32);          // keys [0, jend)
   const int Pq = tq < T ? p0 + tq : jend - 1;     // its last visible key (rows past T see all)
-  const int nblk = (jend + 31) / 32;
+  const int nall = (jend + 31) / 32;
+  // key blocks of this split: [kb0, kb0 + nblk)
+  const int kper = (nall + nsplit - 1) / nsplit;
+  const int kb0 = min(nall, split * kper), nblk = min(nall, kb0 + kper) - kb0;
   const float scale = 1.0f / sqrtf((float)HD);
   const int hi32 = l >> 5;
   // Q fragments: B operand of S^T (column = query, k = dims)
@@ -1074,11 +1080,13 @@ __global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restri
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
   float m = -INFINITY, lsum = 0.f;
-  load_blk(0);
-  store_blk();
+  if (nblk > 0) {
+    load_blk(kb0);
+    store_blk();
+  }
   lds_bar();
-  for (int kb = 0; kb < nblk; ++kb) {
-    if (kb + 1 < nblk) load_blk(kb + 1);  // in flight during this block
+  for (int kb = kb0; kb < kb0 + nblk; ++kb) {
+    if (kb + 1 < kb0 + nblk) load_blk(kb + 1);  // in flight during this block
     if (live) {
       f32x16 st = f32x16{};
 #pragma unroll
@@ -1149,12 +1157,28 @@ __global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restri
       }
     }
     lds_bar();  // every wave is done with this block's K / V
-    if (kb + 1 < nblk) {
+    if (kb + 1 < kb0 + nblk) {
       store_blk();
       lds_bar();
     }
   }
   if (!live) return;
+  if (nsplit > 1) {
+    // unnormalised partial of this split: per query row (max, sum, O[HD]); a split without keys
+    // leaves (-inf, 0, 0)
+    float* pp = part + ((size_t)(tile * nq + hq) * nsplit + split) * 32 * (HD + 2);
+    if (l < 32) {
+      pp[l * (HD + 2)] = m;
+      pp[l * (HD + 2) + 1] = lsum;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) pp[row * (HD + 2) + 2 + dt * 32 + (l & 31)] = O[dt][r];
+    }
+    return;
+  }
   if (l < 32) lsm[l] = lsum;
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("" ::: "memory");
@@ -1171,6 +1195,28 @@ __global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restri
           split_store(O[dt][r4 * 4 + x] * inv[x], Ohi, Olo, (size_t)t * ldo + hq * HD + dt * 32 + (l & 31));
       }
     }
+  }
+}
+
+// Key-split partials -> output: per (query, head), splits merged in order:
+// M = max_s m_s, O = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s; written as BF16 hi/lo.
+__global__ void __launch_bounds__(256) pf_attn_merge_kernel(const float* __restrict__ part, int T, int nq, int hd,
+                                                            int nsplit, uint16_t* __restrict__ Ohi,
+                                                            uint16_t* __restrict__ Olo, int ldo) {
+  const int t = blockIdx.x, hq = blockIdx.y;
+  if (t >= T) return;
+  const int tile = t >> 5, row = t & 31;
+  const float* base = part + ((size_t)(tile * nq + hq) * nsplit) * 32 * (hd + 2) + (size_t)row * (hd + 2);
+  const size_t sstride = (size_t)32 * (hd + 2);
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, base[sp * sstride]);
+  float den = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) den = fmaf(expf(base[sp * sstride] - M), base[sp * sstride + 1], den);
+  const float inv = 1.0f / den;
+  for (int d = threadIdx.x; d < hd; d += 256) {
+    float num = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) num = fmaf(expf(base[sp * sstride] - M), base[sp * sstride + 2 + d], num);
+    split_store(num * inv, Ohi, Olo, (size_t)t * ldo + hq * hd + d);
   }
 }
 
@@ -1391,17 +1437,30 @@ extern "C" int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, in
 }
 
 extern "C" int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,
-                               int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, void* stream) {
+                               int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, float* P, size_t p_floats,
+                               void* stream) {
   if (hd == 64 || hd == 128) {
-    // MFMA path: workgroups = KV heads x groups of 4 query heads x 32-query tiles
-    const int gs = nq / nkv;
-    const dim3 grid(nkv * ((gs + 3) / 4) * ((T + 31) / 32));
+    // MFMA path: workgroups = KV heads x groups of 4 query heads x 32-query tiles x key splits.
+    // Split the keys when that brings the grid nearer one workgroup per compute unit (256), as far
+    // as the partial buffer holds (its partials are merged before anything else uses it).
+    const int gs = nq / nkv, ntile = (T + 31) / 32;
+    const int base_wg = nkv * ((gs + 3) / 4) * ntile;
+    const size_t per_split = (size_t)ntile * nq * 32 * (hd + 2);
+    int nsplit = std::max(1, std::min(256 / base_wg, (p0 + T + 31) / 32));
+    nsplit = (int)std::min<size_t>((size_t)nsplit, std::max<size_t>(1, p_floats / per_split));
+    if (!P) nsplit = 1;
+    const dim3 grid(base_wg * nsplit);
     const size_t lds = (size_t)4 * 32 * hd * 2 + 4 * (4 * 32 * 32 + 2 * 32 * 4);
     hipStream_t st = (hipStream_t)stream;
     if (hd == 64)
-      hipLaunchKernelGGL(pf_attn_mfma_kernel<64>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo);
+      hipLaunchKernelGGL(pf_attn_mfma_kernel<64>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo,
+                         nsplit, P);
     else
-      hipLaunchKernelGGL(pf_attn_mfma_kernel<128>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo);
+      hipLaunchKernelGGL(pf_attn_mfma_kernel<128>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo,
+                         nsplit, P);
+    if (nsplit > 1)
+      hipLaunchKernelGGL(pf_attn_merge_kernel, dim3(T, nq), dim3(hd <= 128 ? 128 : 256), 0, st, P, T, nq, hd, nsplit, Ohi,
+                         Olo, ldo);
     return MK_LAUNCH_OK();
   }
   const int gs = nq / nkv, QB = 16 / gs;
