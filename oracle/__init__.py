@@ -20,6 +20,10 @@ FP32 accumulation).  The pages give no equations; the readings used here are:
 * Block: pre-norm residual, RMSNorm (eps 1e-6, gain after normalising), SwiGLU
   FFN, final RMSNorm, tied LM head, greedy argmax with the lowest index on ties.
 
+* 4-bit weights (the 27B-scale model): groups of 32 columns with an FP16 scale d and
+  offset m, weight = d*q + m (``quant.py`` decodes the byte layout; the decoded values
+  are exact in float64, so the oracle runs on the stored weights exactly).
+
 Everything runs in float64 by default (``dtype`` may be set to float32 for the
 float32-vs-float64 gap check).  Functions that run the model two independent
 ways -- ``Oracle.step`` (token by token, recurrent DeltaNet, KV cache) and
@@ -33,8 +37,9 @@ from .deltanet import (gates, delta_step, delta_recurrent, delta_explicit_produc
 from .attention import attend_one, causal_attention
 from .model import Oracle
 from .metrics import rel_l2, mean_kl, top1_agreement
+from .quant import q4g32_dequant, q4g32_dequant_rows
 
 __all__ = ["rmsnorm", "l2norm", "sigmoid", "softplus", "silu", "rope_angles", "rope", "softmax",
            "bf16_decode", "gates", "delta_step", "delta_recurrent", "delta_explicit_product",
            "delta_parallel", "delta_chunked", "attend_one", "causal_attention", "Oracle",
-           "rel_l2", "mean_kl", "top1_agreement"]
+           "rel_l2", "mean_kl", "top1_agreement", "q4g32_dequant", "q4g32_dequant_rows"]

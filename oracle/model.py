@@ -24,13 +24,75 @@ import numpy as np
 from .primitives import bf16_decode, rmsnorm, l2norm, silu, rope_angles, rope
 from .deltanet import gates, delta_step, delta_parallel
 from .attention import attend_one, causal_attention
+from .quant import q4g32_dequant, q4g32_dequant_rows
+
+
+def matrix_shape(cfg, name: str) -> tuple:
+    """Logical [rows, cols] of a weight matrix by name (rows = outputs, cols = inputs)."""
+    D = cfg.hidden
+    if name == "embed":
+        return (cfg.vocab, D)
+    part = name.split(".", 1)[1]
+    H, dk, dv, hd = cfg.dn_heads, cfg.dn_dk, cfg.dn_dv, cfg.head_dim
+    shapes = {"dn.wqkv": (2 * H * dk + H * dv, D), "dn.wa": (H, D), "dn.wb": (H, D), "dn.wo": (D, H * dv),
+              "attn.wq": (cfg.n_q_heads * hd, D), "attn.wk": (cfg.n_kv_heads * hd, D),
+              "attn.wv": (cfg.n_kv_heads * hd, D), "attn.wo": (D, cfg.n_q_heads * hd),
+              "ffn.wg": (cfg.ffn, D), "ffn.wu": (cfg.ffn, D), "ffn.wd": (D, cfg.ffn)}
+    return shapes[part]
+
+
+class Weights:
+    """Weight values by name.  BF16 tensors (uint16 bit patterns) are decoded once; 4-bit Q4G32
+    matrices (uint8 buffers) are decoded when used, and kept only while the decoded total stays
+    under `cache_bytes` (the 27B-scale matrices would not fit otherwise)."""
+
+    def __init__(self, cfg, weight_bits: dict, dtype, cache_bytes: int = 1 << 31):
+        self.cfg = cfg
+        self.dtype = dtype
+        self.dec = {}
+        self.q4 = {}
+        self.cache_left = cache_bytes
+        for name, bits in weight_bits.items():
+            if np.asarray(bits).dtype == np.uint8:
+                self.q4[name] = (bits, matrix_shape(cfg, name))
+            else:
+                self.dec[name] = bf16_decode(bits, dtype)
+
+    def __getitem__(self, name):
+        if name in self.dec:
+            return self.dec[name]
+        buf, (R, K) = self.q4[name]
+        w = q4g32_dequant(buf, R, K, self.dtype)
+        if w.nbytes <= self.cache_left:
+            self.cache_left -= w.nbytes
+            self.dec[name] = w
+        return w
+
+    def rows(self, name, idx):
+        """Selected rows of a matrix (the embedding lookup)."""
+        if name in self.dec:
+            return self.dec[name][idx].copy()
+        buf, (R, K) = self.q4[name]
+        return q4g32_dequant_rows(buf, R, K, idx, self.dtype)
+
+    def lin(self, name, x, block: int = 16384):
+        """x @ W.T; a 4-bit matrix that is not kept is decoded a block of rows at a time (each output
+        is still one row's dot product)."""
+        if name in self.dec or name not in self.q4:
+            return x @ self[name].T
+        buf, (R, K) = self.q4[name]
+        out = np.empty(x.shape[:-1] + (R,), dtype=np.result_type(x, self.dtype))
+        for r0 in range(0, R, block):
+            r1 = min(R, r0 + block)
+            out[..., r0:r1] = x @ q4g32_dequant_rows(buf, R, K, slice(r0, r1), self.dtype).T
+        return out
 
 
 class Oracle:
     def __init__(self, cfg, weight_bits: dict, dtype=np.float64):
         self.cfg = cfg
         self.dtype = dtype
-        self.W = {name: bf16_decode(bits, dtype) for name, bits in weight_bits.items()}
+        self.W = Weights(cfg, weight_bits, dtype)
         self.reset()
 
     # ---------------------------------------------------------------- state
@@ -90,7 +152,7 @@ class Oracle:
 
     def _head(self, x):
         xf = rmsnorm(x, self.W["final_norm"], self.cfg.rms_eps)
-        return xf @ self.W["embed"].T
+        return self.W.lin("embed", xf)
 
     # --------------------------------------------------- one token (O1 form)
     def step(self, tok: int) -> np.ndarray:
@@ -99,7 +161,7 @@ class Oracle:
         p = self.pos
         if p >= c.max_ctx:
             raise ValueError("context full")
-        x = self.W["embed"][int(tok)].copy()
+        x = self.W.rows("embed", int(tok))
         for l in range(c.n_layers):
             h = rmsnorm(x, self.W[f"l{l}.norm1"], c.rms_eps)
             if c.is_attention(l):
@@ -124,7 +186,7 @@ class Oracle:
         tokens = np.asarray(tokens)
         T = tokens.shape[0]
         positions = np.arange(T)
-        X = self.W["embed"][tokens].copy()
+        X = self.W.rows("embed", tokens)
         S_out, KV_out = {}, {}
         for l in range(c.n_layers):
             Hn = rmsnorm(X, self.W[f"l{l}.norm1"], c.rms_eps)

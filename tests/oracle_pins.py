@@ -18,6 +18,7 @@ import oracle.primitives as prim
 import oracle.deltanet as dn
 import oracle.attention as att
 import oracle.model as om
+import oracle.quant as oq
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -393,5 +394,76 @@ def pin_fp32_vs_fp64_gap():
     for l in o64.S:
         assert mt.rel_l2(o32.S[l], o64.S[l]) < 1e-5
 
+
+
+# ------------------------------------------------------------ 4-bit weights
+def pin_q4g32_hand_example():
+    """A hand-built byte image decodes to the values its codes and block parameters define."""
+    with open(os.path.join(GOLDEN, "q4g32_hand.json")) as f:
+        g = json.load(f)
+    buf = np.frombuffer(bytes.fromhex(g["codes_hex"] + g["params_hex"]), dtype=np.uint8)
+    W = oq.q4g32_dequant(buf, g["rows"], g["cols"])
+    j = np.arange(32)
+    want0 = np.concatenate([0.5 * (j % 16) - 2.0, 0.25 * (j % 16) + 1.0])
+    want1 = np.concatenate([2.0 * (15 - j % 16) - 16.0, np.full(32, 0.5)])
+    _close(W, np.stack([want0, want1]), 0.0, "q4g32 hand example")
+    # single rows through the row path
+    _close(oq.q4g32_dequant_rows(buf, 2, 64, np.array([1])), want1[None], 0.0, "q4g32 row 1")
+
+
+def pin_q4g32_quantizer_roundtrip():
+    """The library's host quantizer against the oracle's decoder: every weight comes back within
+    half a step (plus the FP16 rounding of d and m), constant groups come back exactly, and the
+    group extremes map to codes 0 and 15."""
+    from hybrid_deltanet_attention_amd.quant import quantize_q4g32
+    rng = np.random.default_rng(5)
+    R, K = 6, 128
+    w = (rng.standard_normal((R, K)) * 0.02).astype(np.float32)
+    w[2, 32:64] = np.float32(0.375)  # a constant group: d = 0, every weight equals m
+    buf = quantize_q4g32(w)
+    W = oq.q4g32_dequant(buf, R, K)
+    g = w.reshape(R, K // 32, 32).astype(np.float64)
+    d = (g.max(-1) - g.min(-1)) / 15.0
+    bound = 0.5 * d + 16 * d * 2.0 ** -11 + np.abs(g.min(-1)) * 2.0 ** -11
+    err = np.abs(W.reshape(R, K // 32, 32) - g).max(-1)
+    assert np.all(err <= bound + 1e-12), f"q4g32 round trip error {err.max():.3e} over its bound"
+    _close(W[2, 32:64], np.full(32, 0.375), 0.0, "constant group")
+    words, _ = oq.q4g32_split(buf, R, K)
+    q = oq.q4g32_codes(words).reshape(R, K // 32, 32)
+    live = np.ones((R, K // 32), bool)
+    live[2, 1] = False
+    assert np.all(q.max(-1)[live] == 15) and np.all(q.min(-1)[live] == 0), "group extremes must map to 15 and 0"
+    assert np.all(q[2, 1] == 0), "a constant group has code 0 throughout"
+
+
+def pin_q4g32_model_equals_bf16_model():
+    """A model whose 4-bit weights decode to BF16-exact values gives the same logits as the model
+    built from those BF16 values (the oracle's lazy decode, row lookup and blocked LM head)."""
+    from hybrid_deltanet_attention_amd.quant import pack_q4g32
+    cfg = synth.get_config("tiny").with_(n_layers=2, attn_slot=1, period=2, vocab=512, max_ctx=16)
+    rng = np.random.default_rng(9)
+    q4, bf = {}, {}
+    for name, shape, kind in synth.tensor_manifest(cfg):
+        if kind == "gain":
+            bf[name] = q4[name] = synth.bf16_round(np.ones(shape, np.float32))
+            continue
+        R, K = shape
+        q = rng.integers(0, 16, size=(R, K))
+        d = np.where(rng.random((R, K // 32)) < 0.5, 2.0 ** -8, 2.0 ** -7)
+        m = -8.0 * d
+        q4[name] = pack_q4g32(q, d.astype(np.float16), m.astype(np.float16))
+        vals = (q.reshape(R, K // 32, 32) - 8.0) * d[..., None]
+        bf[name] = synth.bf16_round(vals.reshape(R, K).astype(np.float32))
+    a = om.Oracle(cfg, q4)
+    a.W.cache_left = 0  # decode on every use
+    b = om.Oracle(cfg, bf)
+    toks = [3, 17, 400]
+    fa, fb = a.forward(toks), b.forward(toks)
+    _close(fa["logits"], fb["logits"], 0.0, "q4 vs bf16 forward logits")
+    _close(a.W.lin("embed", fa["logits"][:, :cfg.hidden], block=100),
+           fa["logits"][:, :cfg.hidden] @ b.W["embed"].T, 1e-12, "blocked LM head")
+    a.load_state(fa)
+    b.load_state(fb)
+    _close(a.step(5), b.step(5), 0.0, "q4 vs bf16 step logits")
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -11,6 +11,7 @@ import oracle.primitives as prim
 import oracle.deltanet as dn
 import oracle.attention as att
 import oracle.model as om
+import oracle.quant as oq
 from oracle_pins import ALL_PINS
 
 
@@ -100,6 +101,25 @@ def _verify_variant(keep_extra=0, shift=0, rollback=True):
     return verify
 
 
+def _q4_codes_halves_swapped(words):
+    words = np.asarray(words, dtype=np.uint32)
+    return _REAL_Q4_CODES((words >> np.uint32(16)) | (words << np.uint32(16)))
+
+
+def _q4_codes_nibbles_in_order(words):
+    # columns taken as the 8 nibbles in bit order (no even / odd split across the half-words)
+    words = np.asarray(words, dtype=np.uint32)
+    q = np.stack([(words >> np.uint32(4 * j)) & np.uint32(0xF) for j in range(8)], axis=-1).astype(np.uint8)
+    return q.reshape(words.shape[:-1] + (words.shape[-1] * 8,))
+
+
+def _q4_split_params_swapped(buf, R, K):
+    words, params = _REAL_Q4_SPLIT(buf, R, K)
+    return words, params[..., ::-1]
+
+
+_REAL_Q4_CODES = oq.q4g32_codes
+_REAL_Q4_SPLIT = oq.q4g32_split
 _REAL_STEP = dn.delta_step
 _REAL_ROPE = prim.rope
 _REAL_RMS = prim.rmsnorm
@@ -125,6 +145,9 @@ MUTANTS = [
     ("verify: rollback keeps the accepted drafts only", [(om.Oracle, "verify")], _verify_variant(keep_extra=-1)),
     ("verify: rollback keeps one token too many", [(om.Oracle, "verify")], _verify_variant(keep_extra=1)),
     ("verify: draft compared with the next choice", [(om.Oracle, "verify")], _verify_variant(shift=1)),
+    ("q4: code half-words swapped", [(oq, "q4g32_codes")], _q4_codes_halves_swapped),
+    ("q4: nibbles read in bit order", [(oq, "q4g32_codes")], _q4_codes_nibbles_in_order),
+    ("q4: scale and offset swapped", [(oq, "q4g32_split")], _q4_split_params_swapped),
 ]
 
 

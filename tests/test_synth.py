@@ -44,3 +44,22 @@ def test_prompts():
     assert p.dtype == np.int32 and p.shape == (16,) and p.min() >= 0 and p.max() < 4096
     assert np.array_equal(p, synth.make_prompt(4096, 16, 0))
     assert not np.array_equal(p, synth.make_prompt(4096, 16, 1))
+
+
+def test_q4_weights_deterministic_and_sized():
+    cfg = synth.get_config("tiny")
+    a = synth.make_q4_weights(cfg, 0)
+    b = synth.make_q4_weights(cfg, 0)
+    c = synth.make_q4_weights(cfg, 1)
+    for name, shape, kind in synth.tensor_manifest(cfg):
+        if kind == "matrix":
+            assert a[name].dtype == np.uint8 and a[name].size == synth.q4_nbytes(*shape) == shape[0] * shape[1] * 5 // 8
+        else:
+            assert a[name].dtype == np.uint16 and a[name].shape == shape
+        assert np.array_equal(a[name], b[name])
+    assert not np.array_equal(a["embed"], c["embed"])
+    # block parameters: d near 0.0054, m near -7.5 d
+    R, K = cfg.vocab, cfg.hidden
+    dm = a["embed"][R * K // 2:].view("<f2").reshape(-1, 2).astype(np.float64)
+    assert 0.004 < dm[:, 0].mean() < 0.007 and np.all(dm[:, 0] > 0)
+    assert abs((dm[:, 1] + 7.5 * dm[:, 0]).mean()) < 1e-4
