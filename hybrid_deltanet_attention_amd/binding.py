@@ -15,7 +15,7 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 MK_OK = 0
-MK_BF16, MK_F32, MK_F16, MK_I32 = 1, 2, 3, 4
+MK_BF16, MK_F32, MK_F16, MK_I32, MK_Q4G32 = 1, 2, 3, 4, 5
 STATUS = {
     0: "MK_OK", -1: "MK_E_INVALID", -2: "MK_E_SHAPE", -3: "MK_E_DTYPE", -4: "MK_E_NAME",
     -5: "MK_E_ORDER", -6: "MK_E_CTX_FULL", -7: "MK_E_NO_DEVICE", -8: "MK_E_OCCUPANCY",
@@ -102,14 +102,15 @@ def _check(rc: int, ctx=None):
         raise MkError(rc, _err(ctx))
 
 
-def mk_config_from(cfg, max_verify_k: int = 0) -> mk_config:
-    """Marshal a model shape (any object with the synth.ModelConfig attributes) into the C struct."""
+def mk_config_from(cfg, max_verify_k: int = 0, weight_dtype: int = MK_BF16) -> mk_config:
+    """Marshal a model shape (any object with the synth.ModelConfig attributes) into the C struct.
+    weight_dtype: MK_BF16, or MK_Q4G32 for 4-bit block-quantised matrices."""
     c = mk_config()
     for f in ("n_layers", "hidden", "ffn", "vocab", "period", "attn_slot", "dn_heads", "dn_dk",
               "dn_dv", "n_q_heads", "n_kv_heads", "head_dim", "max_ctx"):
         setattr(c, f, int(getattr(cfg, f)))
     c.tied_embeddings = 1 if getattr(cfg, "tied", True) else 0
-    c.weight_dtype = MK_BF16
+    c.weight_dtype = int(weight_dtype)
     c.kv_dtype = MK_F32
     c.max_verify_k = max_verify_k
     c.rms_eps = float(cfg.rms_eps)
@@ -126,8 +127,25 @@ def mk_workspace_bytes(cfg) -> int:
     return int(n)
 
 
-def _tensor_array(weights: dict, keep: list):
-    """weights: name -> numpy uint16 array (host) or torch uint16/int16/bfloat16 CUDA tensor."""
+def matrix_shapes(cfg) -> dict:
+    """Logical [out, in] shape of every weight matrix of the model, by manifest name."""
+    D, H, hd = cfg.hidden, cfg.dn_heads, cfg.head_dim
+    out = {"embed": (cfg.vocab, D)}
+    for l in range(cfg.n_layers):
+        p = f"l{l}."
+        if l % cfg.period == cfg.attn_slot:
+            out.update({p + "attn.wq": (cfg.n_q_heads * hd, D), p + "attn.wk": (cfg.n_kv_heads * hd, D),
+                        p + "attn.wv": (cfg.n_kv_heads * hd, D), p + "attn.wo": (D, cfg.n_q_heads * hd)})
+        else:
+            out.update({p + "dn.wqkv": (2 * H * cfg.dn_dk + H * cfg.dn_dv, D), p + "dn.wa": (H, D),
+                        p + "dn.wb": (H, D), p + "dn.wo": (D, H * cfg.dn_dv)})
+        out.update({p + "ffn.wg": (cfg.ffn, D), p + "ffn.wu": (cfg.ffn, D), p + "ffn.wd": (D, cfg.ffn)})
+    return out
+
+
+def _tensor_array(weights: dict, keep: list, q4_shapes: dict | None = None):
+    """weights: name -> numpy uint16 array (host) or torch uint16/int16/bfloat16 CUDA tensor; with
+    q4_shapes, a flat uint8 array (host) or CUDA tensor is a Q4G32 matrix of that logical shape."""
     arr = (mk_tensor * len(weights))()
     for i, (name, w) in enumerate(weights.items()):
         t = arr[i]
@@ -141,6 +159,9 @@ def _tensor_array(weights: dict, keep: list):
             t.data = a.ctypes.data
             t.on_device = 0
             shape = a.shape
+            if a.dtype == np.uint8 and q4_shapes is not None and name in q4_shapes:
+                t.dtype = MK_Q4G32
+                shape = q4_shapes[name]
         else:  # torch tensor
             import torch
             a = w.contiguous()
@@ -149,27 +170,31 @@ def _tensor_array(weights: dict, keep: list):
             t.data = a.data_ptr()
             t.on_device = 1 if a.is_cuda else 0
             shape = tuple(a.shape)
+            if a.dtype == torch.uint8 and q4_shapes is not None and name in q4_shapes:
+                t.dtype = MK_Q4G32
+                shape = q4_shapes[name]
         t.ndim = len(shape)
         for d in range(4):
             t.shape[d] = int(shape[d]) if d < len(shape) else 0
     return arr
 
 
-def mk_check_tensors(cfg, weights: dict) -> None:
-    c = mk_config_from(cfg)
+def mk_check_tensors(cfg, weights: dict, weight_dtype: int = MK_BF16) -> None:
+    c = mk_config_from(cfg, weight_dtype=weight_dtype)
     keep: list = []
-    arr = _tensor_array(weights, keep)
+    arr = _tensor_array(weights, keep, matrix_shapes(cfg) if weight_dtype == MK_Q4G32 else None)
     _check(load_library().mk_check_tensors(ctypes.byref(c), arr, len(weights)))
 
 
 class Model:
     """A context on one device: workspace (torch uint8 tensor), stream, loaded weights."""
 
-    def __init__(self, cfg, device: int = 0, stream=None, max_verify_k: int = 0):
+    def __init__(self, cfg, device: int = 0, stream=None, max_verify_k: int = 0, weight_dtype: int = MK_BF16):
         import torch
         self.lib = load_library()
         self.cfg = cfg
-        self.c = mk_config_from(cfg, max_verify_k)
+        self.weight_dtype = int(weight_dtype)
+        self.c = mk_config_from(cfg, max_verify_k, weight_dtype)
         self.device = device
         nbytes = mk_workspace_bytes(self.c)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=f"cuda:{device}")
@@ -183,7 +208,7 @@ class Model:
     # ---- C entry points, same names
     def mk_load_weights(self, weights: dict):
         keep: list = []
-        arr = _tensor_array(weights, keep)
+        arr = _tensor_array(weights, keep, matrix_shapes(self.cfg) if self.weight_dtype == MK_Q4G32 else None)
         _check(self.lib.mk_load_weights(self.ctx, arr, len(weights)), self.ctx)
 
     def mk_prefill(self, d_tokens, n: int, d_next, d_logits=None):

@@ -73,7 +73,13 @@ std::string check_config(const mk_config* c) {
   if (c->n_q_heads / c->n_kv_heads > 32) return "at most 32 query heads per KV head";
   if (c->dn_dk > 256 || c->dn_dv > 256 || c->head_dim > 256) return "dn_dk, dn_dv, head_dim must be <= 256";
   if (c->tied_embeddings != 1) return "only tied embeddings are supported";
-  if (c->weight_dtype != MK_BF16) return "weight_dtype must be MK_BF16";
+  if (c->weight_dtype != MK_BF16 && c->weight_dtype != MK_Q4G32) return "weight_dtype must be MK_BF16 or MK_Q4G32";
+  if (c->weight_dtype == MK_Q4G32) {
+    if (c->hidden % 32 || c->ffn % 32 || (c->dn_heads * c->dn_dv) % 32 || (c->n_q_heads * c->head_dim) % 32)
+      return "MK_Q4G32 needs hidden, ffn, dn_heads*dn_dv and n_q_heads*head_dim to be multiples of 32";
+    if (c->hidden > 8192) return "MK_Q4G32 needs hidden <= 8192";
+    if (c->max_verify_k != 0) return "speculative verify needs BF16 weights: max_verify_k must be 0 with MK_Q4G32";
+  }
   if (c->kv_dtype != MK_F32) return "kv_dtype must be MK_F32";
   if (c->max_ctx <= 0 || c->max_ctx > (1 << 20)) return "max_ctx must be in [1, 2^20]";
   if (c->max_verify_k < 0 || c->max_verify_k > MK_VERIFY_MAXT - 1)
@@ -118,23 +124,28 @@ Layout make_layout(const mk_config& c) {
   };
   const int64_t D = c.hidden, H = c.dn_heads, half = c.head_dim / 2;
   const int gs = c.n_q_heads / c.n_kv_heads;
+  const bool q4 = c.weight_dtype == MK_Q4G32;
+  // bytes of a weight matrix [R][K]: BF16, or Q4G32 codes + (d, m) words
+  auto wbytes = [&](int64_t R, int64_t K) -> size_t {
+    return q4 ? (size_t)(R * K / 2 + R * (K / 32) * 4) : (size_t)(R * K * 2);
+  };
   L.max_items = ((c.max_ctx + MK_ATT_CHUNK - 1) / MK_ATT_CHUNK) * c.n_kv_heads;
   L.ctl = take(sizeof(MkCtl));
   L.descs = take(sizeof(MkLayerDev) * c.n_layers);
   L.rope_cos = take((size_t)c.max_ctx * half * 4);
   L.rope_sin = take((size_t)c.max_ctx * half * 4);
   L.g_final = take(D * 2);
-  L.embed = take((size_t)c.vocab * D * 2);
+  L.embed = take(wbytes(c.vocab, D));
   L.layers.resize(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
     LayerOff& lo = L.layers[l];
     const bool att = is_attention(c, l);
     lo.rows_in = att ? (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim : 2 * H * c.dn_dk + H * c.dn_dv + 2 * H;
     lo.k_out = att ? (int64_t)c.n_q_heads * c.head_dim : H * c.dn_dv;
-    lo.w_in = take((size_t)lo.rows_in * D * 2);
-    lo.w_out = take((size_t)D * lo.k_out * 2);
-    lo.w_gu = take((size_t)2 * c.ffn * D * 2);
-    lo.w_down = take((size_t)D * c.ffn * 2);
+    lo.w_in = take(wbytes(lo.rows_in, D));
+    lo.w_out = take(wbytes(D, lo.k_out));
+    lo.w_gu = take(wbytes(2 * (int64_t)c.ffn, D));
+    lo.w_down = take(wbytes(D, c.ffn));
     lo.g12 = take(D * 4);  // BF16 [2][D]
   }
   L.state_begin = o;
@@ -187,8 +198,8 @@ Layout make_layout(const mk_config& c) {
       if (!is_attention(c, l)) L.layers[l].snap = base + (size_t)(j++) * per * 4;
   }
   L.scratch = take(4096);
-  // prefill scratch
-  {
+  // prefill scratch (4-bit models run their prompts through the decode kernel and need none)
+  if (!q4) {
     const int64_t T = std::min(c.max_ctx, 1024);
     const int64_t kmax = std::max(std::max(D, (int64_t)c.ffn), std::max(H * c.dn_dv, (int64_t)c.n_q_heads * c.head_dim));
     const int64_t ndn = 2 * H * c.dn_dk + H * c.dn_dv + 2 * H;
@@ -246,6 +257,38 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   p.lds_trace = take(2 * MK_TRACE_EVENTS);
   // the prefetch stages are a static array of the kernel (MK_STAGE_A_SLOTS + MK_STAGE_B_SLOTS KB,
   // more than half the LDS of a compute unit, so one workgroup fits per unit)
+  p.lds_floats = o;
+}
+
+// LDS carve for the 4-bit decode kernel (floats): two layer descriptors, no gains (read from global memory),
+// the normalised activations share the vector region, unit partials hold Q4_RED_CAP floats; its
+// static stage (48 KB) holds the DeltaNet state rows and the attention KV chunks.
+void lds_layout_q4(const mk_config& c, int grid, MkDecodeParams& p) {
+  const int D = c.hidden;
+  const int gs = c.n_q_heads / c.n_kv_heads;
+  const int hd = c.head_dim, C = MK_ATT_CHUNK;
+  const int vec = std::max(std::max(std::max(c.ffn, D), c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid));
+  int att = 2 * c.dn_dk + 2 + c.dn_dv;
+  att = std::max(att, 2 * gs * hd + 2 * hd + gs * C + 6 * gs);
+  att = std::max(att, 2048);  // Q4_RED_CAP
+  att = std::max(att, 3 * 129);
+  int o = 0;
+  auto take = [&](int n) {
+    const int at = o;
+    o += (n + 3) / 4 * 4;
+    return at;
+  };
+  p.lds_desc = take(2 * (int)(sizeof(MkLayerDev) / 4));  // this layer's and the next one's
+  p.lds_gain = 0;
+  p.lds_rope = take(hd);
+  p.lds_x = take(D);
+  p.lds_vec = take(vec);
+  p.lds_xn = p.lds_vec;
+  p.lds_att = take(att);
+  p.lds_scr = take(4 * MK_NWAVE);
+  p.lds_flag = take(4);
+  o = (o + 1) / 2 * 2;
+  p.lds_trace = take(2 * MK_TRACE_EVENTS);
   p.lds_floats = o;
 }
 
@@ -356,11 +399,13 @@ int check_tensor_list(const mk_config& c, const mk_tensor* t, int32_t n, std::st
       return MK_E_NAME;
     }
     seen[it->second] = i;
-    if (t[i].dtype != MK_BF16) {
-      msg = std::string("tensor '") + t[i].name + "' has dtype " + std::to_string(t[i].dtype) + ", expected MK_BF16";
+    const TensorSpec& sp = man[it->second];
+    const int want = (c.weight_dtype == MK_Q4G32 && sp.shape.size() == 2) ? MK_Q4G32 : MK_BF16;
+    if (t[i].dtype != want) {
+      msg = std::string("tensor '") + t[i].name + "' has dtype " + std::to_string(t[i].dtype) + ", expected " +
+            (want == MK_Q4G32 ? "MK_Q4G32" : "MK_BF16");
       return MK_E_DTYPE;
     }
-    const TensorSpec& sp = man[it->second];
     bool same = (int)sp.shape.size() == t[i].ndim;
     for (size_t d = 0; same && d < sp.shape.size(); ++d) same = (t[i].shape[d] == sp.shape[d]);
     if (!same) {
@@ -465,10 +510,13 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   p.rope_sin = (const float*)(ctx->ws + lay.rope_sin);
   p.ctl = (MkCtl*)(ctx->ws + lay.ctl);
   p.ll_am = (mk_u64*)(ctx->ws + lay.ll_am);
-  lds_layout(*cfg, ctx->grid, p);
+  p.wq4 = cfg->weight_dtype == MK_Q4G32 ? 1 : 0;
+  if (p.wq4) lds_layout_q4(*cfg, ctx->grid, p);
+  else lds_layout(*cfg, ctx->grid, p);
 
   const int lds_bytes = p.lds_floats * 4;
-  if (lds_bytes > (int)prop.sharedMemPerBlock || mk_decode_max_blocks_per_cu(&p, lds_bytes) < 1) {
+  const int fits = p.wq4 ? mk_decode_q4_max_blocks_per_cu(&p, lds_bytes) : mk_decode_max_blocks_per_cu(&p, lds_bytes);
+  if (lds_bytes > (int)prop.sharedMemPerBlock || fits < 1) {
     const std::string m = "decode kernel needs " + std::to_string(lds_bytes) + " B of LDS; device offers " +
                           std::to_string(prop.sharedMemPerBlock);
     delete ctx;
@@ -583,8 +631,9 @@ int mk_set_grid(mk_ctx* ctx, int32_t n) {
   if (n < 1 || n > ctx->n_cu || n > MK_MAX_GRID)
     return fail(ctx, MK_E_INVALID, "grid must be in [1, " + std::to_string(std::min(ctx->n_cu, MK_MAX_GRID)) + "]");
   MkDecodeParams q = ctx->base;
-  lds_layout(ctx->cfg, n, q);
-  if (mk_decode_max_blocks_per_cu(&q, q.lds_floats * 4) < 1)
+  if (q.wq4) lds_layout_q4(ctx->cfg, n, q);
+  else lds_layout(ctx->cfg, n, q);
+  if ((q.wq4 ? mk_decode_q4_max_blocks_per_cu(&q, q.lds_floats * 4) : mk_decode_max_blocks_per_cu(&q, q.lds_floats * 4)) < 1)
     return fail(ctx, MK_E_OCCUPANCY, "decode kernel does not fit at this grid size");
   MkDecodeParams v = ctx->vbase;
   if (ctx->lay.vt) {
@@ -627,13 +676,17 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
   if (rc != MK_OK) return fail(ctx, rc, msg);
   HIPCHK(ctx, hipSetDevice(ctx->device));
   const std::vector<TensorSpec> man = manifest(c);
+  const bool q4 = c.weight_dtype == MK_Q4G32;
+  // bytes of a tensor as stored: BF16 gains and matrices, or Q4G32 matrices
+  auto tbytes = [&](const std::vector<int64_t>& shape) -> size_t {
+    if (q4 && shape.size() == 2) return (size_t)(shape[0] * shape[1] / 2 + shape[0] * (shape[1] / 32) * 4);
+    size_t b = 2;
+    for (int64_t d : shape) b *= (size_t)d;
+    return b;
+  };
   // stage host tensors through one device buffer sized for the largest tensor
   size_t max_bytes = 0;
-  for (size_t i = 0; i < man.size(); ++i) {
-    size_t b = 2;
-    for (int64_t d : man[i].shape) b *= (size_t)d;
-    max_bytes = std::max(max_bytes, b);
-  }
+  for (size_t i = 0; i < man.size(); ++i) max_bytes = std::max(max_bytes, tbytes(man[i].shape));
   void* stage = nullptr;
   int32_t* d_perm = nullptr;
   HIPCHK(ctx, hipMalloc(&stage, max_bytes));
@@ -657,25 +710,50 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
       if (man[i].name == name) return t[order[i]];
     return t[0];  // unreachable: the list was checked
   };
-  auto copy_plain = [&](const std::string& name, size_t dst_off) -> int {
-    const mk_tensor& tt = tensor(name);
-    size_t bytes = 2;
-    for (int d = 0; d < tt.ndim; ++d) bytes *= (size_t)tt.shape[d];
-    if (tt.on_device)
-      return hipMemcpyAsync(ctx->ws + dst_off, tt.data, bytes, hipMemcpyDeviceToDevice, ctx->stream) == hipSuccess
-                 ? MK_OK : MK_E_HIP;
-    return hipMemcpyAsync(ctx->ws + dst_off, tt.data, bytes, hipMemcpyHostToDevice, ctx->stream) == hipSuccess
+  auto copy_bytes = [&](const mk_tensor& tt, size_t src_off, size_t dst_off, size_t bytes) -> int {
+    const hipMemcpyKind k = tt.on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+    return hipMemcpyAsync(ctx->ws + dst_off, (const char*)tt.data + src_off, bytes, k, ctx->stream) == hipSuccess
                ? MK_OK : MK_E_HIP;
   };
-  // rows of `name` go to dst rows perm[r] (dst is a matrix with the same row length)
-  auto copy_perm = [&](const std::string& name, size_t dst_off, const std::vector<int32_t>& perm) -> int {
+  // a gain vector, or a whole matrix that is a region of its own
+  auto copy_plain = [&](const std::string& name, size_t dst_off) -> int {
     const mk_tensor& tt = tensor(name);
-    const int64_t rows = tt.shape[0], cols = tt.shape[1];
+    std::vector<int64_t> shape(tt.shape, tt.shape + tt.ndim);
+    return copy_bytes(tt, 0, dst_off, tbytes(shape));
+  };
+  // Matrix `name` [R][K] -> rows row0 .. row0 + R of the region at dst_off that holds a matrix of
+  // Rtot rows and K columns; with perm, source row r goes to region row row0 + perm[r].  Q4G32
+  // regions are all rows' codes followed by all rows' (d, m) words, so the two parts move
+  // separately.
+  auto put_rows = [&](const std::string& name, size_t dst_off, int64_t Rtot, int64_t row0,
+                      const std::vector<int32_t>* perm) -> int {
+    const mk_tensor& tt = tensor(name);
+    const int64_t R = tt.shape[0], K = tt.shape[1];
+    // (bytes per row, source offset, destination offset) of each part
+    struct Part {
+      int64_t row_bytes;
+      size_t src, dst;
+    };
+    std::vector<Part> parts;
+    if (q4) {
+      parts.push_back({K / 2, 0, dst_off + (size_t)(row0 * (K / 2))});
+      parts.push_back({(K / 32) * 4, (size_t)(R * (K / 2)), dst_off + (size_t)(Rtot * (K / 2) + row0 * (K / 32) * 4)});
+    } else {
+      parts.push_back({K * 2, 0, dst_off + (size_t)(row0 * K * 2)});
+    }
+    if (!perm) {
+      for (const Part& pt : parts)
+        if (copy_bytes(tt, pt.src, pt.dst, (size_t)(R * pt.row_bytes))) return MK_E_HIP;
+      return MK_OK;
+    }
+    std::vector<int64_t> shape(tt.shape, tt.shape + tt.ndim);
     const void* src = nullptr;
-    if (src_of(tt, (size_t)rows * cols * 2, &src)) return MK_E_HIP;
-    if (hipMemcpyAsync(d_perm, perm.data(), rows * 4, hipMemcpyHostToDevice, ctx->stream) != hipSuccess) return MK_E_HIP;
-    if (mk_launch_permute_rows((const uint16_t*)src, (uint16_t*)(ctx->ws + dst_off), d_perm, rows, cols, ctx->stream))
-      return MK_E_HIP;
+    if (src_of(tt, tbytes(shape), &src)) return MK_E_HIP;
+    if (hipMemcpyAsync(d_perm, perm->data(), R * 4, hipMemcpyHostToDevice, ctx->stream) != hipSuccess) return MK_E_HIP;
+    for (const Part& pt : parts)
+      if (mk_launch_permute_rows((const uint16_t*)((const char*)src + pt.src), (uint16_t*)(ctx->ws + pt.dst), d_perm,
+                                 R, pt.row_bytes / 2, ctx->stream))
+        return MK_E_HIP;
     // the staging buffers are reused by the next tensor
     return hipStreamSynchronize(ctx->stream) == hipSuccess ? MK_OK : MK_E_HIP;
   };
@@ -698,17 +776,16 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
           for (int d = 0; d < hd; ++d) pm[(size_t)h * hd + d] = h * hd + 2 * (d % half) + d / half;
         return pm;
       };
-      rc = copy_perm(p + "attn.wq", lo.w_in, pair_perm(c.n_q_heads));
-      if (!rc) rc = copy_perm(p + "attn.wk", lo.w_in + (size_t)c.n_q_heads * hd * D * 2, pair_perm(c.n_kv_heads));
-      if (!rc)
-        rc = copy_perm(p + "attn.wv", lo.w_in + (size_t)(c.n_q_heads + c.n_kv_heads) * hd * D * 2,
-                       pair_perm(c.n_kv_heads));
+      const std::vector<int32_t> pq = pair_perm(c.n_q_heads), pk = pair_perm(c.n_kv_heads);
+      rc = put_rows(p + "attn.wq", lo.w_in, lo.rows_in, 0, &pq);
+      if (!rc) rc = put_rows(p + "attn.wk", lo.w_in, lo.rows_in, (int64_t)c.n_q_heads * hd, &pk);
+      if (!rc) rc = put_rows(p + "attn.wv", lo.w_in, lo.rows_in, (int64_t)(c.n_q_heads + c.n_kv_heads) * hd, &pk);
       if (!rc) rc = copy_plain(p + "attn.wo", lo.w_out);
     } else {
       const int64_t nqkv = 2 * H * c.dn_dk + H * c.dn_dv;
-      rc = copy_plain(p + "dn.wqkv", lo.w_in);
-      if (!rc) rc = copy_plain(p + "dn.wa", lo.w_in + (size_t)nqkv * D * 2);
-      if (!rc) rc = copy_plain(p + "dn.wb", lo.w_in + (size_t)(nqkv + H) * D * 2);
+      rc = put_rows(p + "dn.wqkv", lo.w_in, lo.rows_in, 0, nullptr);
+      if (!rc) rc = put_rows(p + "dn.wa", lo.w_in, lo.rows_in, nqkv, nullptr);
+      if (!rc) rc = put_rows(p + "dn.wb", lo.w_in, lo.rows_in, nqkv + H, nullptr);
       if (!rc) rc = copy_plain(p + "dn.wo", lo.w_out);
     }
     if (rc) break;
@@ -717,8 +794,8 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
       pg[j] = 2 * j;
       pu[j] = 2 * j + 1;
     }
-    rc = copy_perm(p + "ffn.wg", lo.w_gu, pg);
-    if (!rc) rc = copy_perm(p + "ffn.wu", lo.w_gu, pu);
+    rc = put_rows(p + "ffn.wg", lo.w_gu, 2 * (int64_t)c.ffn, 0, &pg);
+    if (!rc) rc = put_rows(p + "ffn.wu", lo.w_gu, 2 * (int64_t)c.ffn, 0, &pu);
     if (!rc) rc = copy_plain(p + "ffn.wd", lo.w_down);
   }
   const hipError_t se = hipStreamSynchronize(ctx->stream);
@@ -749,7 +826,8 @@ int mk_decode_step(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_
   p.tok = d_tok;
   p.next = d_next;
   p.logits = d_logits;
-  if (mk_launch_decode(&p, ctx->grid, ctx->stream)) return fail(ctx, MK_E_HIP, "decode launch failed");
+  if ((p.wq4 ? mk_launch_decode_q4(&p, ctx->grid, ctx->stream) : mk_launch_decode(&p, ctx->grid, ctx->stream)))
+    return fail(ctx, MK_E_HIP, "decode launch failed");
   ctx->pos_host += 1;
   return MK_OK;
 }
@@ -763,8 +841,9 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   if (ctx->pos_host + n > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "prompt does not fit the context");
   const mk_config& c = ctx->cfg;
   const int gs = c.n_q_heads / c.n_kv_heads;
-  if (16 % gs != 0) {
-    // shapes the prefill attention tiling does not cover: token-by-token through the decode kernel
+  if (16 % gs != 0 || ctx->base.wq4) {
+    // 4-bit weights, or shapes the prefill attention tiling does not cover: token by token through
+    // the decode kernel
     int32_t* scratch_tok = (int32_t*)(ctx->ws + ctx->lay.scratch) + 8;
     for (int32_t i = 0; i < n; ++i) {
       const bool last = (i == n - 1);

@@ -56,6 +56,7 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
   s.flag = (LS int*)(lds + p.lds_flag);
   s.stA = (LS u32x4*)g_stage;
   s.stB = (LS u32x4*)g_stage + MK_STAGE_A_SLOTS * SLOT;
+  s.a_slots = MK_STAGE_A_SLOTS;
   const int D = p.D;
 
   Ctx cx;
@@ -152,7 +153,7 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
       // K/V rows of the first two work items -> stage A (free until the gate/up units), the
       // out-projection units -> stage B
       const int boff = 0;
-      for (int kc = 0; kc + 1 < kv_nbuf(p.hd) || kc == 0; ++kc) {
+      for (int kc = 0; kc + 1 < kv_nbuf(p.hd, s.a_slots) || kc == 0; ++kc) {
         const int cn = att_chunk_at(p, NW, w, pos, kc);
         if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd) * SLOT);
       }

@@ -250,6 +250,7 @@ struct Lds {
   LS int* flag;         // set once a wait gave up
   LS u32x4* stA;        // prefetch stage A
   LS u32x4* stB;        // prefetch stage B
+  int a_slots;          // 1 KB slots of stage A
 };
 
 // Workgroup barrier that also tells every thread whether any thread passed bad == true.  A wait
@@ -928,14 +929,16 @@ __device__ __forceinline__ int kv_stage(const MkDecodeParams& p, const MkLayerDe
 }
 
 // q/k/v rows in RoPE pair order: rotate q and k at position pos, append k and v to the cache
-__device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                        const Gemv& g, int P0, int pos, Tracer& tr) {
+// `run(epi)` performs the in-projection GEMV of this workgroup's row pairs with epilogue epi.
+template <typename Run>
+__device__ __forceinline__ void att_qkv_run(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
+                                            int P0, int pos, Run run) {
   const int hd = p.hd, half = hd / 2;
   MK_G mk_u64* llq = L.ll_in;
   MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   MK_G mk_u64* llv = llk + p.nkv * hd;
   const int nqp = p.nq * half, nkp = p.nkv * half;
-  gemv<true, false, false>(g, s.xn, s.stA, A_UNITS, s.att, tr, [&](int pl, float x1, float x2) {
+  run([&](int pl, float x1, float x2) {
     const int P = P0 + pl;
     if (P < nqp + nkp) {
       const bool isq = P < nqp;
@@ -966,13 +969,19 @@ __device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDe
   });
 }
 
+__device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
+                                        const Gemv& g, int P0, int pos, Tracer& tr) {
+  att_qkv_run(p, L, cx, s, P0, pos,
+              [&](auto epi) { gemv<true, false, false>(g, s.xn, s.stA, A_UNITS, s.att, tr, epi); });
+}
+
 // Split-K partial softmax attention.  Item = (chunk of 16 positions, KV head g); for each of the
 // gs query heads of group g it emits (max m, sum l, acc[hd]) over its positions.  Scores: one thread
 // per (head, position), a 16-lane DPP row per head for the max and the sum.
 // KV stage slots of one 16-position chunk, rounded to whole GEMV units
 __device__ __forceinline__ int kv_buf_slots(int hd) { return (2 * kv_slots(hd) + 3) & ~3; }
 // chunk buffers in stage A (up to 3: the copies of the next two chunks run while one is used)
-__device__ __forceinline__ int kv_nbuf(int hd) { return max(1, min(3, MK_STAGE_A_SLOTS / kv_buf_slots(hd))); }
+__device__ __forceinline__ int kv_nbuf(int hd, int a_slots) { return max(1, min(3, a_slots / kv_buf_slots(hd))); }
 
 // Split-K attention over positions 0..pos.  A work item is (block of p.att_cpi 16-position chunks,
 // KV head g); item it = block * nkv + g.  Chunk by chunk, the item computes for each of the gs query
@@ -1012,7 +1021,7 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
   const int items = att_items_count(p, pos);
   const float scale = 1.0f / sqrtf((float)hd);
   const int lpp = hd >> 2, pps = 64 / lpp, ks = kv_slots(hd);
-  const int nb = kv_nbuf(hd);
+  const int nb = kv_nbuf(hd, s.a_slots);
   const int kvb = kv_buf_slots(hd);
   int cnt0 = 0, cnt1 = 0, cnt2 = 0;  // copies this wave issued for the chunk in buffers 0, 1, 2
   LS float* qv = s.att;                // [gs][hd]

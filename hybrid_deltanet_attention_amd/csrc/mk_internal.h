@@ -105,6 +105,9 @@ struct MkDecodeParams {
   MK_G int32_t* vout;            // [nt] greedy choice after each position
   MK_G int32_t* vacc;            // accepted drafts
   MK_G mk_u64* ll_acc;           // accepted-count record
+  // weight format: 0 = BF16, 1 = Q4G32 (every matrix is its 4-bit codes followed by its (d, m)
+  // words; the norm gains stay BF16)
+  int32_t wq4;
 };
 
 #ifdef __cplusplus
@@ -113,6 +116,8 @@ extern "C" {
 // Launchers implemented in the .hip files (host side).
 int mk_launch_decode(const MkDecodeParams* p, int n_wg, void* stream);
 int mk_launch_verify(const MkDecodeParams* p, int n_wg, void* stream);
+int mk_launch_decode_q4(const MkDecodeParams* p, int n_wg, void* stream);
+int mk_decode_q4_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
 int mk_verify_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
 int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_perm, int64_t rows,
                            int64_t cols, void* stream);

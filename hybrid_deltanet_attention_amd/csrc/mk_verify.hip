@@ -689,6 +689,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   s.scr = lds + p.lds_scr;
   s.flag = (LS int*)(lds + p.lds_flag);
   s.stA = nullptr;
+  s.a_slots = 0;
   s.stB = nullptr;
   LS int* toks = (LS int*)(lds + p.lds_xn);  // the verify carve keeps the tokens in the xn slot
   const int D = p.D, F = p.ffn;

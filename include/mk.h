@@ -46,14 +46,25 @@ enum mk_status {
   MK_E_UNSUPPORTED = -11    /* valid request this build does not implement */
 };
 
-enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4 };
+/* MK_Q4G32: 4-bit block-quantised weights, the storage of the pages' 27B-scale model (megakernel
+ * follow-up posts, page 3, quantisation-support paragraph: 4-bit weights in blocks with a scale).
+ * A matrix W [R, K] (K a multiple of 32) is R*K*5/8 bytes: first the codes, K/2 bytes per row,
+ * rows in order -- in row r, columns 8i .. 8i+7 sit in the little-endian 32-bit word at byte
+ * r*K/2 + 4i, column 8i+2j in the nibble at bit 4j and column 8i+2j+1 in the nibble at bit 16+4j
+ * (j = 0..3) -- then one 4-byte word per (row, group of 32 columns), row-major: the IEEE binary16
+ * scale d in the low half, the binary16 offset m in the high half.  The weight is d*q + m for its
+ * 4-bit code q.  The mk_tensor shape is the logical [R, K]. */
+enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4, MK_Q4G32 = 5 };
 
 /* Model shape.  All fields are required (there is no default constructor on purpose).
  * Constraints checked by mk_workspace_bytes / mk_create: every size > 0; hidden, ffn, H*dk and
  * H*dv multiples of 8; dk, dv even and head_dim a multiple of 4, all <= 256; n_q_heads a multiple of n_kv_heads;
- * attn_slot < period; tied_embeddings == 1; weight_dtype == MK_BF16; kv_dtype == MK_F32;
+ * attn_slot < period; tied_embeddings == 1; kv_dtype == MK_F32;
  * 0 <= max_verify_k <= 5 (each unit adds one position's records, one DeltaNet state snapshot and
- * LDS; mk_create returns MK_E_OCCUPANCY if the verify kernel's LDS does not fit). */
+ * LDS; mk_create returns MK_E_OCCUPANCY if the verify kernel's LDS does not fit).
+ * weight_dtype is MK_BF16 or MK_Q4G32.  MK_Q4G32 also needs hidden, ffn, H*dv and nq*head_dim to
+ * be multiples of 32, hidden <= 8192 and max_verify_k == 0; its prompts run one decode launch per
+ * token (the prefill kernels take BF16 weights). */
 typedef struct {
   int32_t n_layers, hidden, ffn, vocab;
   int32_t period, attn_slot;                       /* attention layers: l % period == attn_slot */
@@ -97,7 +108,9 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
               void* hip_stream, mk_ctx** out);
 
 /* Copy all model tensors into the workspace in the kernel's layout.  Every manifest name must
- * appear exactly once with dtype MK_BF16 and the manifest shape; the whole list is checked
+ * appear exactly once with the manifest shape and dtype: MK_BF16 for everything, or, when the
+ * config's weight_dtype is MK_Q4G32, MK_Q4G32 for the matrices (embed and every l{l}.* weight
+ * matrix) and MK_BF16 for the norm gains; the whole list is checked
  * before anything is copied (MK_E_NAME / MK_E_DTYPE / MK_E_SHAPE name the offending tensor).
  * Then resets the sequence state and runs one warm-up launch.  Synchronous. */
 int mk_load_weights(mk_ctx* ctx, const mk_tensor* tensors, int32_t n);

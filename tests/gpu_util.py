@@ -13,9 +13,10 @@ def torch_cuda():
     return torch
 
 
-def new_model(cfg, weights, grid=None):
+def new_model(cfg, weights, grid=None, weight_dtype=None):
     from hybrid_deltanet_attention_amd import Model
-    m = Model(cfg, device=0)
+    from hybrid_deltanet_attention_amd.binding import MK_BF16
+    m = Model(cfg, device=0, weight_dtype=MK_BF16 if weight_dtype is None else weight_dtype)
     m.mk_load_weights(weights)
     if grid is not None:
         m.mk_set_grid(grid)
@@ -46,8 +47,10 @@ def run_teacher_forced(m, prompt, fed, want_logits=True):
     return pre_logits, pre_next, out_l, out_n
 
 
-def oracle_reference(cfg, weights, prompt, n_steps):
+def oracle_reference(cfg, weights, prompt, n_steps, cache_bytes=None):
     from oracle import Oracle
     o = Oracle(cfg, weights)
+    if cache_bytes is not None:
+        o.W.cache_left = cache_bytes  # keep every decoded 4-bit matrix (wide models)
     fed, logits, last = o.greedy(prompt, n_steps)
     return o, fed, logits, last

@@ -142,3 +142,31 @@ def test_null_context_calls_fail_cleanly(lib):
     assert lib.mk_verify_k(None, None, 0, None, None) in (-1, -11)
     assert lib.mk_state_bytes(None, 0) == 0
     lib.mk_destroy(None)
+
+
+def test_q4_config_and_tensor_checks(lib):
+    """4-bit weights: the matrices must come as MK_Q4G32 (gains as MK_BF16), widths must be
+    multiples of 32, and speculative verify stays BF16-only."""
+    import synth
+    from hybrid_deltanet_attention_amd import binding as b
+    cfg = synth.get_config("tiny")
+    W = synth.make_q4_weights(cfg, 0)
+    b.mk_check_tensors(cfg, W, weight_dtype=b.MK_Q4G32)
+    with pytest.raises(b.MkError) as e:
+        b.mk_check_tensors(cfg, synth.make_weights(cfg, 0), weight_dtype=b.MK_Q4G32)
+    assert e.value.code == -3 and "MK_Q4G32" in str(e.value)
+    with pytest.raises(b.MkError) as e:
+        b.mk_check_tensors(cfg, W)  # a 4-bit buffer offered to a BF16 model
+    assert e.value.code == -3
+    q4 = b.mk_workspace_bytes(b.mk_config_from(cfg, weight_dtype=b.MK_Q4G32))
+    bf = b.mk_workspace_bytes(b.mk_config_from(cfg))
+    assert q4 < bf, "4-bit weights take less workspace"
+    for bad in (dict(hidden=200), dict(ffn=776)):
+        with pytest.raises(b.MkError):
+            b.mk_workspace_bytes(b.mk_config_from(synth.get_config("tiny", **bad), weight_dtype=b.MK_Q4G32))
+    with pytest.raises(b.MkError):
+        b.mk_workspace_bytes(b.mk_config_from(cfg, max_verify_k=1, weight_dtype=b.MK_Q4G32))
+    # 27B-scale: 14.08 GB of 4-bit weights (0.625 B per weight) plus state, cache and records
+    c27 = synth.get_config("hybrid_27b", max_ctx=2048)
+    n = b.mk_workspace_bytes(b.mk_config_from(c27, weight_dtype=b.MK_Q4G32))
+    assert 14.0e9 < n < 14.6e9

@@ -17,9 +17,9 @@ STATE_TOL = 1e-3
 KL_TOL = 1e-3
 
 
-def _check_run(cfg, W, prompt, n_steps, grid=None):
-    o, fed, ref_logits, ref_last = oracle_reference(cfg, W, prompt, n_steps)
-    m = new_model(cfg, W, grid)
+def _check_run(cfg, W, prompt, n_steps, grid=None, weight_dtype=None, oracle_cache=None):
+    o, fed, ref_logits, ref_last = oracle_reference(cfg, W, prompt, n_steps, oracle_cache)
+    m = new_model(cfg, W, grid, weight_dtype)
     pre_l, pre_n, dec_l, dec_n = run_teacher_forced(m, prompt, fed)
     print(f"[{cfg.name} grid={m.mk_get_grid()}] prefill logits rel-L2 {rel_l2(pre_l, ref_last):.2e}", flush=True)
     assert rel_l2(pre_l, ref_last) <= LOGIT_TOL
@@ -44,8 +44,9 @@ def _check_run(cfg, W, prompt, n_steps, grid=None):
             print(f"  layer {l} state rel-L2 {e:.2e}", flush=True)
             assert e <= STATE_TOL
     assert m.mk_get_position() == len(prompt) + n_steps
+    states = {l: m.mk_read_state(l).copy() for l in range(cfg.n_layers)}
     m.close()
-    return dec_l
+    return dec_l, states
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
