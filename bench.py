@@ -108,8 +108,10 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "reps": 4}), flush=True)
 
 
-def algorithmic_bytes(cfg, L: int) -> dict:
-    """Bytes one decode launch must move at context length L (positions 0..L-1 visible)."""
+def algorithmic_bytes(cfg, L: int, wb: float = 2.0) -> dict:
+    """Bytes one decode launch must move at context length L (positions 0..L-1 visible); wb is the
+    bytes per weight of the matrices (2 for BF16, 0.625 for 4-bit codes with an FP16 scale and
+    offset per 32 weights)."""
     D, H = cfg.hidden, cfg.dn_heads
     w = 0
     state = 0
@@ -123,8 +125,8 @@ def algorithmic_bytes(cfg, L: int) -> dict:
             rows_in = 2 * H * cfg.dn_dk + H * cfg.dn_dv + 2 * H
             kout = H * cfg.dn_dv
             state += 2 * H * cfg.dn_dv * cfg.dn_dk * 4       # read + write
-        w += 2 * (rows_in * D + D * kout + 3 * cfg.ffn * D) + 2 * 4 * D
-    head = 2 * cfg.vocab * D + 4 * D + 2 * D                 # tied LM head, final gain, embedding row
+        w += wb * (rows_in * D + D * kout + 3 * cfg.ffn * D) + 2 * 4 * D
+    head = wb * cfg.vocab * D + 4 * D + wb * D               # tied LM head, final gain, embedding row
     return {"weights": w, "lm_head": head, "state": state, "kv": kv, "total": w + head + state + kv}
 
 
@@ -249,6 +251,55 @@ def long_context_leg(cfg_name: str, W, ctx: int, n_steps: int) -> dict:
             "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "kv": "fp32"}
 
 
+def q4_27b_leg(ctx: int, n_steps: int) -> dict:
+    """The 27B-scale hybrid from 4-bit Q4G32 weights (64 layers, hidden 5120, 0.625 B per weight,
+    14.08 GB): a ctx-token random prompt through the decode kernel (one launch per token), then
+    n_steps timed one-launch decode steps.  Weights are drawn in the storage format (seeded)."""
+    import torch
+    import synth
+    from hybrid_deltanet_attention_amd import Model
+    from hybrid_deltanet_attention_amd.binding import MK_Q4G32
+    cfg = synth.get_config("hybrid_27b", max_ctx=2048)
+    assert ctx + n_steps + 8 <= cfg.max_ctx
+    print(f"[bench] 27B-scale 4-bit: generating weights", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    W = synth.make_q4_weights(cfg, SEED)
+    gen_s = time.perf_counter() - t0
+    m = Model(cfg, device=0, weight_dtype=MK_Q4G32)
+    m.mk_load_weights(W)
+    del W
+    print(f"[bench] 27B-scale 4-bit: weights drawn in {gen_s:.1f} s and loaded", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    prompt = torch.tensor(synth.make_prompt(cfg.vocab, ctx, SEED + 11), device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    t0 = time.perf_counter()
+    m.mk_prefill(prompt, ctx, tok)
+    m.mk_sync()
+    pre_s = time.perf_counter() - t0
+    for _ in range(4):
+        m.mk_decode_step(tok, tok)
+    m.mk_sync()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for i in range(n_steps):
+        ev[i][0].record(m.stream)
+        m.mk_decode_step(tok, tok)
+        ev[i][1].record(m.stream)
+    m.mk_sync()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    region = ev[0][0].elapsed_time(ev[-1][1]) / 1e3
+    L0 = ctx + 5
+    bytes_per = float(np.mean([algorithmic_bytes(cfg, L0 + i, 0.625)["total"] for i in range(n_steps)]))
+    gbs = bytes_per / (us * 1e-6) / 1e9
+    m.close()
+    return {"workload": f"hybrid_27b 4-bit (Q4G32) batch-1 decode after a {ctx}-token prompt",
+            "layers": cfg.n_layers, "hidden": cfg.hidden, "ffn": cfg.ffn, "weights_GB": 14.08,
+            "prompt_s": round(pre_s, 3), "us_per_launch": round(us, 2), "tok_per_s": round(n_steps / region, 1),
+            "steps": n_steps, "bytes_per_launch": int(bytes_per), "achieved_GBs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def verify_leg(cfg, W, m_dec, prompt, tok, k: int, n_launch: int) -> dict:
     """mk_verify_k timing at the decode workload: the pending token and k drafts per launch, after the
     512-token prompt.  Greedy drafts are the model's own continuation (from decode launches), so every
@@ -315,6 +366,8 @@ def main():
     ap.add_argument("--long-context", type=int, default=30000,
                     help="prompt length of the long-context decode leg (32,768-position cache); 0 skips it")
     ap.add_argument("--verify-k", type=int, default=5, help="drafts per mk_verify_k launch in the verify leg; 0 skips it")
+    ap.add_argument("--q4-steps", type=int, default=64,
+                    help="timed decode steps of the 27B-scale 4-bit leg (1,024-token prompt); 0 skips it")
     ap.add_argument("--energy-steps", type=int, default=1280,
                     help="decode steps of the energy (tok/J) leg; 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -436,6 +489,10 @@ def main():
     m.close()
     del m
     torch.cuda.empty_cache()
+    if args.q4_steps > 0:
+        out["q4_27b"] = q4_27b_leg(1024, args.q4_steps)
+        print(f"[bench] 27B-scale 4-bit: {out['q4_27b']}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, W)

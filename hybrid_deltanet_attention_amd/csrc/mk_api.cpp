@@ -959,6 +959,11 @@ int mk_sync(mk_ctx* ctx) {
 
     return fail(ctx, MK_E_DEVICE_TIMEOUT, "a grid-wide wait inside a persistent kernel gave up; call mk_reset");
   }
+  // every completed launch advances the device position; a launch that left early does not
+  if (ctx->pos_exact && (int64_t)ctl.pos != ctx->pos_host)
+    return fail(ctx, MK_E_DEVICE_TIMEOUT,
+                "the device position (" + std::to_string(ctl.pos) + ") is behind the enqueued positions (" +
+                    std::to_string(ctx->pos_host) + "): a launch ended early; call mk_reset");
   return MK_OK;
 }
 

@@ -52,6 +52,7 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
   s.xn = (LS u32*)(lds + p.lds_xn);
   s.vec = lds + p.lds_vec;
   s.att = lds + p.lds_att;
+  s.att_cap = MK_RED_CAP;
   s.scr = lds + p.lds_scr;
   s.flag = (LS int*)(lds + p.lds_flag);
   s.stA = (LS u32x4*)g_stage;

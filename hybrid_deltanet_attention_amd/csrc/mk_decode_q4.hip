@@ -44,6 +44,7 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
   s.vec = lds + p.lds_vec;
   s.xn = (LS u32*)s.vec;  // normalised activations share the vector region
   s.att = lds + p.lds_att;
+  s.att_cap = Q4_RED_CAP;
   s.scr = lds + p.lds_scr;
   s.flag = (LS int*)(lds + p.lds_flag);
   s.stA = (LS u32x4*)g_stage_q4;

@@ -246,6 +246,7 @@ struct Lds {
   LS u32* xn;           // normalised residual [D], hi/lo BF16 pairs
   LS float* vec;        // gathered mixer output / FFN hidden, argmax records
   LS float* att;        // gathered DeltaNet / attention inputs, combine staging, GEMV unit partials
+  int att_cap;          // floats of the att region available to the combine staging
   LS float* scr;        // small reductions
   LS int* flag;         // set once a wait gave up
   LS u32x4* stA;        // prefetch stage A
@@ -1188,7 +1189,7 @@ __device__ __forceinline__ bool att_combine(const MkDecodeParams& p, const MkLay
   const int nown = o1 - o0;
   if (nown <= 0) return true;
   LS float* stage = s.att;
-  const int vpp = max(1, MK_RED_CAP / (3 * nch));
+  const int vpp = max(1, s.att_cap / (3 * nch));  // outputs staged per round
   const MK_G mk_u64* part = L.ll_part;
   for (int v0 = 0; v0 < nown; v0 += vpp) {
     const int vn = min(vpp, nown - v0);

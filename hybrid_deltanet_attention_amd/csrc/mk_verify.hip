@@ -686,6 +686,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   s.vec = lds + p.lds_vec;
   s.xn = (LS u32*)s.vec;  // normalised activations share the vector region (never live together)
   s.att = lds + p.lds_att;
+  s.att_cap = MK_RED_CAP;
   s.scr = lds + p.lds_scr;
   s.flag = (LS int*)(lds + p.lds_flag);
   s.stA = nullptr;

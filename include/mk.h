@@ -149,7 +149,9 @@ int mk_verify_k(mk_ctx* ctx, const int32_t* d_tokens, int32_t k, int32_t* d_out,
 /* Position 0, zero DeltaNet states and KV cache (weights kept).  Enqueued on the stream. */
 int mk_reset(mk_ctx* ctx);
 
-/* Wait for the stream; returns MK_E_DEVICE_TIMEOUT if a kernel reported a failed grid wait. */
+/* Wait for the stream; returns MK_E_DEVICE_TIMEOUT if a kernel reported a failed grid wait, or
+ * if the device position is behind the positions enqueued since the last exact count (a launch
+ * that ended early); the sequence state is then undefined until mk_reset. */
 int mk_sync(mk_ctx* ctx);
 
 /* Current position as the device holds it (synchronises). */

@@ -41,6 +41,14 @@ def test_q4_ragged_shapes():
     _check_run(cfg, W, synth.make_prompt(cfg.vocab, 9, 6), 6, grid=37, weight_dtype=MK_Q4G32)
 
 
+def test_q4_long_prompt_small_grid():
+    # 23 attention items per KV head and 32 combine outputs per workgroup: the combine stages its
+    # partials in several rounds through the 4-bit kernel's smaller partials region
+    cfg = synth.get_config("tiny", max_ctx=512)
+    W = synth.make_q4_weights(cfg, 9)
+    _check_run(cfg, W, synth.make_prompt(cfg.vocab, 360, 9), 8, grid=8, weight_dtype=MK_Q4G32)
+
+
 def _slice_cfg(n_layers):
     return synth.get_config("hybrid_27b", n_layers=n_layers, max_ctx=64)
 
