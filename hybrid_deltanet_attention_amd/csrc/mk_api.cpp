@@ -77,7 +77,8 @@ std::string check_config(const mk_config* c) {
   if (c->weight_dtype == MK_Q4G32) {
     if (c->hidden % 32 || c->ffn % 32 || (c->dn_heads * c->dn_dv) % 32 || (c->n_q_heads * c->head_dim) % 32)
       return "MK_Q4G32 needs hidden, ffn, dn_heads*dn_dv and n_q_heads*head_dim to be multiples of 32";
-    if (c->hidden > 8192) return "MK_Q4G32 needs hidden <= 8192";
+    if (c->hidden > 8192 || c->ffn > 20480 || c->dn_heads * c->dn_dv > 20480 || c->n_q_heads * c->head_dim > 20480)
+      return "MK_Q4G32 needs hidden <= 8192 and ffn, dn_heads*dn_dv, n_q_heads*head_dim <= 20480";
     if (c->max_verify_k != 0) return "speculative verify needs BF16 weights: max_verify_k must be 0 with MK_Q4G32";
   }
   if (c->kv_dtype != MK_F32) return "kv_dtype must be MK_F32";
@@ -125,9 +126,9 @@ Layout make_layout(const mk_config& c) {
   const int64_t D = c.hidden, H = c.dn_heads, half = c.head_dim / 2;
   const int gs = c.n_q_heads / c.n_kv_heads;
   const bool q4 = c.weight_dtype == MK_Q4G32;
-  // bytes of a weight matrix [R][K]: BF16, or Q4G32 codes + (d, m) words
+  // bytes of a weight matrix [R][K]: BF16, or Q4G32 tiles (rows padded to a multiple of 4)
   auto wbytes = [&](int64_t R, int64_t K) -> size_t {
-    return q4 ? (size_t)(R * K / 2 + R * (K / 32) * 4) : (size_t)(R * K * 2);
+    return q4 ? (size_t)((R + 3) / 4 * 4 * K * 5 / 8) : (size_t)(R * K * 2);
   };
   L.max_items = ((c.max_ctx + MK_ATT_CHUNK - 1) / MK_ATT_CHUNK) * c.n_kv_heads;
   L.ctl = take(sizeof(MkCtl));
@@ -710,36 +711,62 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
       if (man[i].name == name) return t[order[i]];
     return t[0];  // unreachable: the list was checked
   };
-  auto copy_bytes = [&](const mk_tensor& tt, size_t src_off, size_t dst_off, size_t bytes) -> int {
+  // 4-bit matrices are assembled in their input layout in a device buffer, then tiled into place
+  char* asm_buf = nullptr;
+  if (q4) {
+    size_t mb = 0;
+    for (int l = 0; l < c.n_layers; ++l) {
+      const LayerOff& lo = lay.layers[l];
+      mb = std::max(mb, (size_t)(lo.rows_in * c.hidden * 5 / 8));
+      mb = std::max(mb, (size_t)(c.hidden * lo.k_out * 5 / 8));
+    }
+    mb = std::max(mb, (size_t)(2 * (int64_t)c.ffn * c.hidden * 5 / 8));
+    mb = std::max(mb, (size_t)((int64_t)c.vocab * c.hidden * 5 / 8));
+    if (hipMalloc(&asm_buf, mb) != hipSuccess) {
+      (void)hipFree(stage);
+      (void)hipFree(d_perm);
+      return fail(ctx, MK_E_HIP, "hipMalloc 4-bit assembly buffer failed");
+    }
+  }
+  auto copy_bytes = [&](const mk_tensor& tt, size_t src_off, char* dst, size_t bytes) -> int {
     const hipMemcpyKind k = tt.on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
-    return hipMemcpyAsync(ctx->ws + dst_off, (const char*)tt.data + src_off, bytes, k, ctx->stream) == hipSuccess
-               ? MK_OK : MK_E_HIP;
+    return hipMemcpyAsync(dst, (const char*)tt.data + src_off, bytes, k, ctx->stream) == hipSuccess ? MK_OK : MK_E_HIP;
+  };
+  // assembled matrix (asm_buf) of R rows, K columns -> its tiled region
+  auto tile = [&](size_t dst_off, int64_t R, int64_t K) -> int {
+    if (mk_launch_q4_tile(asm_buf, R, K, ctx->ws + dst_off, ctx->stream)) return MK_E_HIP;
+    return hipStreamSynchronize(ctx->stream) == hipSuccess ? MK_OK : MK_E_HIP;  // asm_buf is reused
   };
   // a gain vector, or a whole matrix that is a region of its own
   auto copy_plain = [&](const std::string& name, size_t dst_off) -> int {
     const mk_tensor& tt = tensor(name);
     std::vector<int64_t> shape(tt.shape, tt.shape + tt.ndim);
-    return copy_bytes(tt, 0, dst_off, tbytes(shape));
+    if (q4 && tt.ndim == 2) {
+      if (copy_bytes(tt, 0, asm_buf, tbytes(shape))) return MK_E_HIP;
+      return tile(dst_off, tt.shape[0], tt.shape[1]);
+    }
+    return copy_bytes(tt, 0, ctx->ws + dst_off, tbytes(shape));
   };
-  // Matrix `name` [R][K] -> rows row0 .. row0 + R of the region at dst_off that holds a matrix of
-  // Rtot rows and K columns; with perm, source row r goes to region row row0 + perm[r].  Q4G32
-  // regions are all rows' codes followed by all rows' (d, m) words, so the two parts move
-  // separately.
-  auto put_rows = [&](const std::string& name, size_t dst_off, int64_t Rtot, int64_t row0,
+  // Matrix `name` [R][K] -> rows row0 .. row0 + R of the matrix at `base` that has Rtot rows and K
+  // columns (the workspace region for BF16, the assembly buffer for Q4G32, whose input layout is
+  // all rows' codes followed by all rows' (d, m) words, so the two parts move separately); with
+  // perm, source row r goes to row row0 + perm[r].
+  auto put_rows = [&](const std::string& name, char* base, int64_t Rtot, int64_t row0,
                       const std::vector<int32_t>* perm) -> int {
     const mk_tensor& tt = tensor(name);
     const int64_t R = tt.shape[0], K = tt.shape[1];
-    // (bytes per row, source offset, destination offset) of each part
+    // (bytes per row, source offset, destination) of each part
     struct Part {
       int64_t row_bytes;
-      size_t src, dst;
+      size_t src;
+      char* dst;
     };
     std::vector<Part> parts;
     if (q4) {
-      parts.push_back({K / 2, 0, dst_off + (size_t)(row0 * (K / 2))});
-      parts.push_back({(K / 32) * 4, (size_t)(R * (K / 2)), dst_off + (size_t)(Rtot * (K / 2) + row0 * (K / 32) * 4)});
+      parts.push_back({K / 2, 0, base + (size_t)(row0 * (K / 2))});
+      parts.push_back({(K / 32) * 4, (size_t)(R * (K / 2)), base + (size_t)(Rtot * (K / 2) + row0 * (K / 32) * 4)});
     } else {
-      parts.push_back({K * 2, 0, dst_off + (size_t)(row0 * K * 2)});
+      parts.push_back({K * 2, 0, base + (size_t)(row0 * K * 2)});
     }
     if (!perm) {
       for (const Part& pt : parts)
@@ -751,12 +778,13 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
     if (src_of(tt, tbytes(shape), &src)) return MK_E_HIP;
     if (hipMemcpyAsync(d_perm, perm->data(), R * 4, hipMemcpyHostToDevice, ctx->stream) != hipSuccess) return MK_E_HIP;
     for (const Part& pt : parts)
-      if (mk_launch_permute_rows((const uint16_t*)((const char*)src + pt.src), (uint16_t*)(ctx->ws + pt.dst), d_perm,
-                                 R, pt.row_bytes / 2, ctx->stream))
+      if (mk_launch_permute_rows((const uint16_t*)((const char*)src + pt.src), (uint16_t*)pt.dst, d_perm, R,
+                                 pt.row_bytes / 2, ctx->stream))
         return MK_E_HIP;
     // the staging buffers are reused by the next tensor
     return hipStreamSynchronize(ctx->stream) == hipSuccess ? MK_OK : MK_E_HIP;
   };
+  auto mat_base = [&](size_t region) { return q4 ? asm_buf : ctx->ws + region; };
 
   const int64_t D = c.hidden, H = c.dn_heads;
   const int hd = c.head_dim, half = hd / 2;
@@ -777,15 +805,19 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
         return pm;
       };
       const std::vector<int32_t> pq = pair_perm(c.n_q_heads), pk = pair_perm(c.n_kv_heads);
-      rc = put_rows(p + "attn.wq", lo.w_in, lo.rows_in, 0, &pq);
-      if (!rc) rc = put_rows(p + "attn.wk", lo.w_in, lo.rows_in, (int64_t)c.n_q_heads * hd, &pk);
-      if (!rc) rc = put_rows(p + "attn.wv", lo.w_in, lo.rows_in, (int64_t)(c.n_q_heads + c.n_kv_heads) * hd, &pk);
+      char* base = mat_base(lo.w_in);
+      rc = put_rows(p + "attn.wq", base, lo.rows_in, 0, &pq);
+      if (!rc) rc = put_rows(p + "attn.wk", base, lo.rows_in, (int64_t)c.n_q_heads * hd, &pk);
+      if (!rc) rc = put_rows(p + "attn.wv", base, lo.rows_in, (int64_t)(c.n_q_heads + c.n_kv_heads) * hd, &pk);
+      if (!rc && q4) rc = tile(lo.w_in, lo.rows_in, D);
       if (!rc) rc = copy_plain(p + "attn.wo", lo.w_out);
     } else {
       const int64_t nqkv = 2 * H * c.dn_dk + H * c.dn_dv;
-      rc = put_rows(p + "dn.wqkv", lo.w_in, lo.rows_in, 0, nullptr);
-      if (!rc) rc = put_rows(p + "dn.wa", lo.w_in, lo.rows_in, nqkv, nullptr);
-      if (!rc) rc = put_rows(p + "dn.wb", lo.w_in, lo.rows_in, nqkv + H, nullptr);
+      char* base = mat_base(lo.w_in);
+      rc = put_rows(p + "dn.wqkv", base, lo.rows_in, 0, nullptr);
+      if (!rc) rc = put_rows(p + "dn.wa", base, lo.rows_in, nqkv, nullptr);
+      if (!rc) rc = put_rows(p + "dn.wb", base, lo.rows_in, nqkv + H, nullptr);
+      if (!rc && q4) rc = tile(lo.w_in, lo.rows_in, D);
       if (!rc) rc = copy_plain(p + "dn.wo", lo.w_out);
     }
     if (rc) break;
@@ -794,13 +826,16 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* t, int32_t n) {
       pg[j] = 2 * j;
       pu[j] = 2 * j + 1;
     }
-    rc = put_rows(p + "ffn.wg", lo.w_gu, 2 * (int64_t)c.ffn, 0, &pg);
-    if (!rc) rc = put_rows(p + "ffn.wu", lo.w_gu, 2 * (int64_t)c.ffn, 0, &pu);
+    char* base = mat_base(lo.w_gu);
+    rc = put_rows(p + "ffn.wg", base, 2 * (int64_t)c.ffn, 0, &pg);
+    if (!rc) rc = put_rows(p + "ffn.wu", base, 2 * (int64_t)c.ffn, 0, &pu);
+    if (!rc && q4) rc = tile(lo.w_gu, 2 * (int64_t)c.ffn, D);
     if (!rc) rc = copy_plain(p + "ffn.wd", lo.w_down);
   }
   const hipError_t se = hipStreamSynchronize(ctx->stream);
   (void)hipFree(stage);
   (void)hipFree(d_perm);
+  if (asm_buf) (void)hipFree(asm_buf);
   if (rc) return fail(ctx, rc, "copying weights failed");
   if (se != hipSuccess) return fail(ctx, MK_E_HIP, std::string("weight copy: ") + hipGetErrorString(se));
   ctx->loaded = true;

@@ -6,7 +6,9 @@
 // Same grid, wave roles and exchange records as the BF16 decode kernel (mk_decode.hip).  What
 // differs is sized for wide models whose weights dominate every phase:
 //  * every GEMV streams its 4-bit units through registers on all eight waves (mk_q4.h); weights
-//    are not staged in LDS;
+//    are not staged in LDS.  Before each exchange the streaming waves take and load their first
+//    units of the GEMV that follows it (the polling waves keep their queues for the polls), so
+//    HBM keeps streaming while the records travel;
 //  * the LDS keeps the residual, one vector region (normalised activations, gathered mixer output
 //    or FFN hidden -- never live together), the unit partials and two layer descriptors (the next
 //    one is fetched by the polling waves during a gather); RMSNorm gains are read from global
@@ -42,7 +44,7 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
   s.rope = lds + p.lds_rope;
   s.x = lds + p.lds_x;
   s.vec = lds + p.lds_vec;
-  s.xn = (LS u32*)s.vec;  // normalised activations share the vector region
+  s.xn = (LS u32*)s.vec;  // packed activations (q4_pack) share the vector region
   s.att = lds + p.lds_att;
   s.att_cap = Q4_RED_CAP;
   s.scr = lds + p.lds_scr;
@@ -50,6 +52,12 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
   s.stA = (LS u32x4*)g_stage_q4;
   s.stB = (LS u32x4*)g_stage_q4 + Q4_STAGE_A * SLOT;
   s.a_slots = Q4_STAGE_A;
+  // GEMV unit counters, alternating from one GEMV to the next (in-projection, gate/up and LM head
+  // on c0; out and down projections on c1), so a GEMV can be primed before the previous one's
+  // counter is cleared
+  LS int* c0 = s.flag + 1;
+  LS int* c1 = s.flag + 2;
+  Q4Ring q;
   const int D = p.D;
 
   Ctx cx;
@@ -66,34 +74,61 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
   tr.mark();
 
   // launch start: the token's embedding row (decoded), the RoPE row
-  q4_embed_row(p.embed, p.vocab, D, tok, s.x);
+  q4_embed_row(p.embed, D, tok, s.x);
   {
     const int half = p.hd / 2;
     for (int i = tid(); i < half; i += MK_NT) {
       s.rope[i] = p.rope_cos[(size_t)pos * half + i];
       s.rope[half + i] = p.rope_sin[(size_t)pos * half + i];
     }
-    if (tid() == 0) *s.flag = 0;
+    if (tid() == 0) {
+      *s.flag = 0;
+      *c0 = 0;
+      *c1 = 0;
+    }
     const MK_G u32* dsrc = (const MK_G u32*)p.layers;
     for (int i = tid(); i < (int)(sizeof(MkLayerDev) / 4); i += MK_NT) ((LS u32*)s.desc)[i] = dsrc[i];
   }
   wg_bar();
 
-  const int d0 = split(D, NW, w), d1 = split(D, NW, w + 1);
-  const int j0 = split(p.ffn, NW, w), j1 = split(p.ffn, NW, w + 1);
+  // row slices in whole 4-row blocks of the tiled matrices: residual-sized projections (out, down)
+  // and FFN hidden pairs (one block = gate and up rows of two hidden units)
+  const int d0 = 4 * split(D >> 2, NW, w), d1 = 4 * split(D >> 2, NW, w + 1);
+  const int j0 = 2 * split(p.ffn >> 1, NW, w), j1 = 2 * split(p.ffn >> 1, NW, w + 1);
+  // this workgroup's in-projection rows of a layer: whole 4-row blocks; P0 = first row pair
+  auto in_slice = [&](const MkLayerDev& Lx, GemvQ4& g, int& P0) {
+    const int nbi = (Lx.rows_in + 3) >> 2;
+    const int B0 = split(nbi, NW, w), B1 = split(nbi, NW, w + 1);
+    P0 = 2 * B0;
+    g.init(Lx.w_in, B0, max(0, min(4 * B1, Lx.rows_in) - 4 * B0), D);
+  };
+  auto head_slice = [&](GemvQ4& g, int& v0) {
+    const int nbv = (p.vocab + 3) >> 2;
+    const int B0 = split(nbv, NW, w), B1 = split(nbv, NW, w + 1);
+    v0 = 4 * B0;
+    g.init(p.embed, B0, max(0, min(4 * B1, p.vocab) - 4 * B0), D);
+  };
+  {
+    // layer 0's in-projection units, while the first norm runs
+    GemvQ4 g;
+    int P0;
+    in_slice(layer_desc(s.desc, 0), g, P0);
+    if (streamer()) gemv_q4_prime(g, c0, q);
+  }
   for (int l = 0; l < p.n_layers; ++l) {
     const MkLayerDev L = layer_desc(s.desc, l & 1);
-    rmsnorm_gg(s.x, L.g12, s.xn, D, p.rms_eps, tr);
+    rmsnorm_gg(s.x, L.g12, s.vec, D, p.rms_eps, tr);
+    q4_pack(s.vec, D);
     tr.mark();
-    int P0, P1;
-    pair_range(L.rows_in, NW, w, P0, P1);
+    int P0;
     GemvQ4 gin;
-    gin.init(L.w_in, L.rows_in, 2 * P0, min(2 * P1, L.rows_in) - 2 * P0, D);
+    in_slice(L, gin, P0);
     int K;  // mixer output width
     if (L.kind == MK_LAYER_DN) {
       K = p.H * p.dv;
       MK_G mk_u64* dst = L.ll_in + 2 * P0;
-      gemv_q4<false, false>(gin, s.xn, s.att, tr, [&](int r, float v, float) { ll_put(dst + r, cx.epoch, v); });
+      gemv_q4<false, false>(gin, s.xn, s.att, c0, q, streamer(), tr,
+                            [&](int r, float v, float) { ll_put(dst + r, cx.epoch, v); });
       tr.mark();
       // this workgroup's state rows -> stage B while the in-projection records travel
       const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
@@ -104,7 +139,8 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
       tr.mark();
     } else {
       K = p.nq * p.hd;
-      att_qkv_run(p, L, cx, s, P0, pos, [&](auto epi) { gemv_q4<true, false>(gin, s.xn, s.att, tr, epi); });
+      att_qkv_run(p, L, cx, s, P0, pos,
+                  [&](auto epi) { gemv_q4<true, false>(gin, s.xn, s.att, c0, q, streamer(), tr, epi); });
       tr.mark();
       // K/V rows of the first work items -> stage A
       for (int kc = 0; kc + 1 < kv_nbuf(p.hd, s.a_slots) || kc == 0; ++kc) {
@@ -118,20 +154,21 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
       tr.mark();
     }
     // mixer output -> out-projection rows + residual -> records
+    GemvQ4 gout;
+    gout.init(L.w_out, d0 >> 2, d1 - d0, K);
+    if (streamer()) gemv_q4_prime(gout, c1, q);
     {
       const bool ok = gather_vec(cx, L.ll_o, K, s.vec);
       if (wg_bar_or(s, !ok)) return;
-      to_hl(s.vec, K);
-      wg_bar();
+      q4_pack(s.vec, K);
     }
     tr.mark();
-    {
-      GemvQ4 gout;
-      gout.init(L.w_out, D, d0, d1 - d0, K);
-      gemv_q4<false, false>(gout, (const LS u32*)s.vec, s.att, tr,
-                            [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
-    }
+    gemv_q4<false, false>(gout, (const LS u32*)s.vec, s.att, c1, q, streamer(), tr,
+                          [&](int r, float v, float) { ll_put(L.ll_x1 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     tr.mark();
+    GemvQ4 ggu;
+    ggu.init(L.w_gu, j0 >> 1, 2 * (j1 - j0), D);
+    if (streamer()) gemv_q4_prime(ggu, c0, q);
     {
       // the polling threads fetch the next layer's descriptor under this gather's latency
       constexpr int NDW = (int)(sizeof(MkLayerDev) / 4);
@@ -144,27 +181,32 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
       if (wg_bar_or(s, !ok)) return;
     }
     tr.mark();
-    rmsnorm_gg(s.x, L.g12 + D, s.xn, D, p.rms_eps, tr);
-    {
-      GemvQ4 ggu;
-      ggu.init(L.w_gu, 2 * p.ffn, 2 * j0, 2 * (j1 - j0), D);
-      gemv_q4<true, false>(ggu, s.xn, s.att, tr, [&](int j, float gv, float uv) {
-        ll_put(L.ll_h + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
-      });
-    }
+    rmsnorm_gg(s.x, L.g12 + D, s.vec, D, p.rms_eps, tr);
+    q4_pack(s.vec, D);
+    gemv_q4<true, false>(ggu, s.xn, s.att, c0, q, streamer(), tr, [&](int j, float gv, float uv) {
+      ll_put(L.ll_h + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
+    });
     tr.mark();
+    GemvQ4 gdn;
+    gdn.init(L.w_down, d0 >> 2, d1 - d0, p.ffn);
+    if (streamer()) gemv_q4_prime(gdn, c1, q);
     {
-      const bool ok = gather_hl(cx, L.ll_h, p.ffn, (LS u32*)s.vec);
+      const bool ok = gather_vec(cx, L.ll_h, p.ffn, s.vec);
       if (wg_bar_or(s, !ok)) return;
+      q4_pack(s.vec, p.ffn);
     }
     tr.mark();
+    gemv_q4<false, false>(gdn, (const LS u32*)s.vec, s.att, c1, q, streamer(), tr,
+                          [&](int r, float v, float) { ll_put(L.ll_x2 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
+    tr.mark();
+    // the next layer's in-projection units (or the LM head's) while the residual travels
     {
-      GemvQ4 gdn;
-      gdn.init(L.w_down, D, d0, d1 - d0, p.ffn);
-      gemv_q4<false, false>(gdn, (const LS u32*)s.vec, s.att, tr,
-                            [&](int r, float v, float) { ll_put(L.ll_x2 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
+      GemvQ4 g;
+      int i0;
+      if (l + 1 < p.n_layers) in_slice(layer_desc(s.desc, (l + 1) & 1), g, i0);
+      else head_slice(g, i0);
+      if (streamer()) gemv_q4_prime(g, c0, q);
     }
-    tr.mark();
     {
       const bool ok = gather_vec(cx, L.ll_x2, D, s.x);
       if (wg_bar_or(s, !ok)) return;
@@ -173,16 +215,15 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
   }
 
   // final norm + tied LM head + argmax (lowest index among equal maxima)
-  rmsnorm_gg(s.x, p.g_final, s.xn, D, p.rms_eps, tr);
+  rmsnorm_gg(s.x, p.g_final, s.vec, D, p.rms_eps, tr);
+  q4_pack(s.vec, D);
   float best = -INFINITY;
   int bidx = 0x7fffffff;
   {
-    int P0, P1;
-    pair_range(p.vocab, NW, w, P0, P1);
     GemvQ4 gl;
-    gl.init(p.embed, p.vocab, 2 * P0, min(2 * P1, p.vocab) - 2 * P0, D);
-    const int v0 = 2 * P0;
-    gemv_q4<false, true>(gl, s.xn, s.att, tr, [&](int r, float v, float) {
+    int v0;
+    head_slice(gl, v0);
+    gemv_q4<false, true>(gl, s.xn, s.att, c0, q, streamer(), tr, [&](int r, float v, float) {
       const int idx = v0 + r;
       if (p.logits) p.logits[idx] = v;
       if (v > best || (v == best && idx < bidx)) {
@@ -261,6 +302,40 @@ DecodeKernel pick_q4_kernel(const MkDecodeParams& p) {
   return mk_decode_q4_kernel;
 }
 }  // namespace
+
+// Load time: a Q4G32 matrix in its input layout (codes, then (d, m) words) -> the tiled layout of
+// mk_q4.h.  One thread per (4-row block, 32-column block); rows past R are zero.
+__global__ void mk_q4_tile_kernel(const uint8_t* __restrict__ src, int64_t R, int64_t K, uint8_t* __restrict__ dst) {
+  const int64_t G = K >> 5, nt = ((R + 3) >> 2) * G;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nt; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = t / G, g = t - b * G;
+    u32x4 out[5];
+    u32 pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = 4 * b + r;
+      out[r] = u32x4{0u, 0u, 0u, 0u};
+      pw[r] = 0u;
+      if (row < R) {
+        out[r] = *(const u32x4*)(src + row * (K >> 1) + g * 16);
+        pw[r] = *(const u32*)(src + R * (K >> 1) + (row * G + g) * 4);
+      }
+    }
+    out[4] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+    // segment s of row block b: five planes of ng 16-byte pieces
+    const int64_t s = g >> 6, l = g & 63, ng = G - 64 * s < 64 ? G - 64 * s : 64;
+    uint8_t* seg = dst + (b * G + 64 * s) * Q4_TILE;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) *(u32x4*)(seg + i * ng * 16 + l * 16) = out[i];
+  }
+}
+
+extern "C" int mk_launch_q4_tile(const void* src, int64_t R, int64_t K, void* dst, void* stream) {
+  if (R <= 0) return 0;
+  hipLaunchKernelGGL(mk_q4_tile_kernel, dim3(1024), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)src, R, K,
+                     (uint8_t*)dst);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 extern "C" int mk_launch_decode_q4(const MkDecodeParams* p, int n_wg, void* stream) {
   hipLaunchKernelGGL(pick_q4_kernel(*p), dim3(n_wg), dim3(MK_NT), (size_t)p->lds_floats * 4, (hipStream_t)stream, *p);

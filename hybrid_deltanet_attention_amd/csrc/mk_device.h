@@ -411,6 +411,57 @@ __device__ __forceinline__ bool gather_hl(const Ctx& cx, const MK_G mk_u64* src,
   if (streamer()) return true;
   return gather_vec_impl<true>(cx.ctl, cx.epoch, src, n, (LS float*)dst);
 }
+// The same gather by all MK_NT threads with PBX polls in flight each, for kernels whose streaming
+// waves hold no prefetch copies while they wait.
+template <bool HL, int PBX>
+__device__ __forceinline__ bool gather_vec_all(const Ctx& cx, const MK_G mk_u64* src, int n, LS float* dst) {
+  src = uni_ptr(src);
+  n = uni(n);
+  const u32 e = cx.epoch;
+  const int pl = tid();
+  const int np = (n + 1) >> 1;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, np * 16, 0x00020000);
+  bool ok = true;
+  for (int base = 0; ok && base < np; base += MK_NT * PBX) {
+    u32 pending = 0;
+#pragma unroll
+    for (int k = 0; k < PBX; ++k)
+      if (base + k * MK_NT + pl < np) pending |= 1u << k;
+    u32 spins = 0;
+    while (pending) {
+      u32x4 v[PBX];
+#pragma unroll
+      for (int k = 0; k < PBX; ++k)
+        if ((pending >> k) & 1u)
+          v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + k * MK_NT + pl) * 16, 0, 16 /* sc1 */);
+#pragma unroll
+      for (int k = 0; k < PBX; ++k) {
+        const int j = base + k * MK_NT + pl;
+        const bool two = 2 * j + 1 < n;
+        if (((pending >> k) & 1u) && v[k].y == e && (!two || v[k].w == e)) {
+          if (HL) {
+            put_hl2((LS u32*)dst, 2 * j, __uint_as_float(v[k].x), two ? __uint_as_float(v[k].z) : 0.f);
+          } else {
+            dst[2 * j] = __uint_as_float(v[k].x);
+            if (two) dst[2 * j + 1] = __uint_as_float(v[k].z);
+          }
+          pending &= ~(1u << k);
+        }
+      }
+      if (pending) {
+        ++spins;
+        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
+          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
+          ok = false;
+          break;
+        }
+      }
+    }
+  }
+  wait_vm<0>();
+  return ok;
+}
+
 // FP32 v[0..n) (n a multiple of 8) -> the GEMV activation layout in place, by all threads: each
 // group of 8 values is rewritten as its hi and lo pairs.  Between barriers.
 __device__ __forceinline__ void to_hl(LS float* v, int n) {

@@ -105,8 +105,8 @@ struct MkDecodeParams {
   MK_G int32_t* vout;            // [nt] greedy choice after each position
   MK_G int32_t* vacc;            // accepted drafts
   MK_G mk_u64* ll_acc;           // accepted-count record
-  // weight format: 0 = BF16, 1 = Q4G32 (every matrix is its 4-bit codes followed by its (d, m)
-  // words; the norm gains stay BF16)
+  // weight format: 0 = BF16, 1 = Q4G32 (every matrix tiled in 80-byte (4 rows x 32 columns)
+  // tiles of codes and (d, m) words; the norm gains stay BF16)
   int32_t wq4;
 };
 
@@ -118,6 +118,8 @@ int mk_launch_decode(const MkDecodeParams* p, int n_wg, void* stream);
 int mk_launch_verify(const MkDecodeParams* p, int n_wg, void* stream);
 int mk_launch_decode_q4(const MkDecodeParams* p, int n_wg, void* stream);
 int mk_decode_q4_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
+// Q4G32 input layout [R][K] -> the decode kernel's tiled layout (ceil(R/4) * K/32 tiles of 80 bytes)
+int mk_launch_q4_tile(const void* src, int64_t R, int64_t K, void* dst, void* stream);
 int mk_verify_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
 int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_perm, int64_t rows,
                            int64_t cols, void* stream);

@@ -1,5 +1,5 @@
 // 4-bit block-quantised weights (Q4G32) in the persistent decode kernel: the GEMV over them, the
-// embedding row and RMSNorm with gains read from global memory.
+// embedding row, RMSNorm with gains read from global memory and the activation packing.
 //
 // The pages' 27B-scale system decodes from 4-bit weights in blocks with a per-block scale
 // (megakernel follow-up posts, page 3, quantisation-support paragraph).  Here a block is 32
@@ -7,6 +7,14 @@
 // is its codes (K/2 bytes per row; in the little-endian word at byte 4i of a row, column 8i + 2j
 // is the nibble at bit 4j and column 8i + 2j + 1 the nibble at bit 16 + 4j) followed by its (d, m)
 // pairs, one 32-bit word per (row, block), d in the low half.
+//
+// In the workspace every 4-bit matrix is tiled (mk_launch_q4_tile): rows are taken four at a time
+// (the last block padded with zero rows); row block b takes G * 80 bytes at b G 80 (G = K / 32
+// column blocks), in segments of 64 column blocks (the last may be shorter, n blocks).  Segment s
+// of row block b starts at byte s * 64 * 80 of the row block and holds five planes of n * 16
+// bytes: plane k < 4 is row 4b + k's 16 code bytes of each column block in order, plane 4 the four
+// rows' (d, m) words of each column block.  A GEMV unit is one segment of one row block: five
+// 16-byte loads per lane, each wave-wide load one contiguous plane, the unit one 5 KB span.
 #pragma once
 
 #include "mk_device.h"
@@ -16,32 +24,35 @@ namespace {
 constexpr int Q4_COLS = 2048;    // columns of a 4-bit GEMV unit (32 per lane)
 constexpr int Q4_RED_CAP = 2048; // unit partials held in LDS per row chunk
 
-// (d, m) words of a Q4G32 matrix with R rows and K columns whose codes start at W
-__device__ __forceinline__ const MK_G u32* q4_params(const MK_G uint16_t* W, int R, int K) {
-  return (const MK_G u32*)((const MK_G uint8_t*)W + (size_t)R * (size_t)(K >> 1));
-}
+constexpr int Q4_TILE = 80;  // bytes per (4-row block, 32-column block) tile
 
 // ---------------------------------------------------------------------------------- GEMV
 // out[r] = W[r] . x over a workgroup's slice of rows.  A unit is 4 rows x 2048 columns: lane l
-// holds columns 32 l .. 32 l + 31 of the unit's segment -- 16 bytes of codes and one (d, m) word
-// per row -- and the hi/lo BF16 pairs of its 32 activations.  One AND/OR turns a code word into
-// BF16 pairs (128 + q_even, 128 + q_odd) (BF16 0x4300 is 128 and its low 7 bits are the
-// significand), so v_dot2c_f32_bf16 forms sum_j (128 + q_j) x_j exactly per product with FP32
-// accumulation, and a block contributes  d * sum_j (128 + q_j) x_j + (m - 128 d) * sum_j x_j.
-// Units are numbered segment-major (u = s * RB + rb) and split into contiguous, balanced ranges
-// over all eight waves; a wave reloads its activations only when its range crosses a segment.
-// Row partials are reduced over the wave in the same fixed order as the BF16 GEMV, and a row's
-// value adds its segment partials in segment order.
+// holds columns 32 l .. 32 l + 31 of the unit's segment (one 32-column block): 16 bytes of codes
+// and one (d, m) word per row.  The activations come as 16-bit integers per block,
+// T_j = rint(x_j / s_g) with s_g = max_j |x_j| / 30000, split into four signed 4-bit digits laid
+// out like the codes (q4_pack), so v_dot8_i32_i4 forms sum_j (q_j - 8) D_kj for eight columns at a
+// time in exact integer arithmetic, and a block contributes
+//   d s_g sum_j (q_j - 8) T_j + (m + 8 d) sum_j x_j.
+// Units are numbered row-block-major (u = rb * S + s), so that the workgroup streams its slice of
+// rows front to back; the eight waves take them in that order from a workgroup counter in LDS, so
+// they finish together whatever each wave's memory latency, and
+// each wave keeps Q4_RING units' loads in flight (buffer loads: a unit past the last or a column
+// past K reads zeros without touching memory, so every iteration issues the same loads).  A unit's
+// partial does not depend on which wave computes it.  Row partials are reduced over the wave in
+// the fixed order of the BF16 GEMV, and a row's value adds its segment partials in segment order.
+constexpr int Q4_XW = 20;   // LDS words per 32-column block of packed activations
+constexpr int Q4_RING = 4;  // units in flight per wave
+constexpr float Q4_TMAX = 30000.0f;
+
 struct GemvQ4 {
-  const MK_G uint8_t* C;  // codes of the slice's first row
-  const MK_G u32* P;      // (d, m) words of the slice's first row
+  const MK_G uint8_t* T;  // tiles of the slice's first row block
   int R, K, S;            // rows, columns, 2048-column segments
-  // rows [row0, row0 + R) of the matrix whose codes start at W and that has Rtot rows, K columns
-  __device__ __forceinline__ void init(const MK_G uint16_t* W, int Rtot, int row0, int R_, int K_) {
+  // rows [4 b0, 4 b0 + R) of the tiled matrix at W with K columns
+  __device__ __forceinline__ void init(const MK_G uint16_t* W, int b0, int R_, int K_) {
     K = K_;
     R = R_;
-    C = (const MK_G uint8_t*)W + (size_t)row0 * (size_t)(K_ >> 1);
-    P = q4_params(W, Rtot, K_) + (size_t)row0 * (size_t)(K_ >> 5);
+    T = (const MK_G uint8_t*)W + (size_t)b0 * (size_t)(K_ >> 5) * Q4_TILE;
     S = (K_ + Q4_COLS - 1) / Q4_COLS;
   }
   __device__ __forceinline__ int chunk_rows() const { return max(4, (Q4_RED_CAP / S) & ~3); }
@@ -50,49 +61,28 @@ struct GemvQ4 {
 // this lane's part of one unit: codes of its 32 columns in each of the 4 rows, and their (d, m)
 struct Q4Unit {
   u32x4 c[4];
-  u32 p[4];
+  u32x4 p;
 };
 
-// Loads of unit (rb, s) for this lane.  Rows past R and columns past K read row 0 / column 0 of the
-// slice (always inside the matrix); their results are never used (rows past R are not stored,
-// columns past K meet zero activations).
-__device__ __forceinline__ void q4_issue(const GemvQ4& g, int rb, int s, Q4Unit& u) {
-  const int col = s * Q4_COLS + lane() * 32;
-  const int cc = col < g.K ? col : 0;
-  const size_t kb = (size_t)(g.K >> 1), kg = (size_t)(g.K >> 5);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int row = rb * 4 + k;
-    const size_t rr = row < g.R ? (size_t)row : 0;
-    u.c[k] = __builtin_nontemporal_load((const MK_G u32x4*)(g.C + rr * kb + (cc >> 1)));
-    u.p[k] = __builtin_nontemporal_load(g.P + rr * kg + (cc >> 5));
-  }
-}
-
-// this lane's 32 activations of segment s (hi/lo pairs, 8 words per 8 columns) and their sum
+// this lane's block of packed activations: digit words [8-column word i][digit k], s_g, sum x
 struct Q4X {
-  u32x4 w[8];
-  float sum;
+  u32x4 w[4];
+  float s, sum;
 };
-__device__ __forceinline__ void q4_load_x(Q4X& x, const LS u32* hl, int s, int K) {
+__device__ __forceinline__ void q4_load_x(Q4X& x, const LS u32* xp, int s, int K) {
   const int col = s * Q4_COLS + lane() * 32;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x.w[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < 4; ++i) x.w[i] = u32x4{0u, 0u, 0u, 0u};
+  x.s = 0.f;
+  x.sum = 0.f;
   if (col < K) {
-    const LS u32x4* p = (const LS u32x4*)(hl + (col >> 3) * 8);
+    const LS u32* b = xp + (col >> 5) * Q4_XW;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x.w[i] = p[i];
+    for (int i = 0; i < 4; ++i) x.w[i] = ((const LS u32x4*)b)[i];
+    const u32x2 g = *(const LS u32x2*)(b + 16);
+    x.s = __uint_as_float(g.x);
+    x.sum = __uint_as_float(g.y);
   }
-  // sum of hi + lo over the 32 columns, through the dot unit with weights (1, 1)
-  float a = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a = dot2(x.w[i].x, 0x3F803F80u, a);
-    a = dot2(x.w[i].y, 0x3F803F80u, a);
-    a = dot2(x.w[i].z, 0x3F803F80u, a);
-    a = dot2(x.w[i].w, 0x3F803F80u, a);
-  }
-  x.sum = a;
 }
 
 __device__ __forceinline__ float f16_lo(u32 w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
@@ -100,20 +90,18 @@ __device__ __forceinline__ float f16_hi(u32 w) { return (float)__builtin_bit_cas
 
 // one row's 32 weights of this lane . its 32 activations
 __device__ __forceinline__ float q4_row(u32x4 c, u32 pw, const Q4X& x) {
-  float acc = 0.f;
+  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32 v = c[i];
-    const u32x4 xh = x.w[2 * i], xl = x.w[2 * i + 1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32 b = ((v >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
-      acc = dot2(b, xh[j], acc);
-      acc = dot2(b, xl[j], acc);
-    }
+    const int v = (int)(c[i] ^ 0x88888888u);  // codes q - 8 as signed nibbles
+    a0 = __builtin_amdgcn_sdot8(v, (int)x.w[i].x, a0, false);
+    a1 = __builtin_amdgcn_sdot8(v, (int)x.w[i].y, a1, false);
+    a2 = __builtin_amdgcn_sdot8(v, (int)x.w[i].z, a2, false);
+    a3 = __builtin_amdgcn_sdot8(v, (int)x.w[i].w, a3, false);
   }
+  const int S = a0 + (a1 << 4) + (a2 << 8) + (a3 << 12);  // sum (q - 8) T, |S| < 2^23
   const float d = f16_lo(pw), m = f16_hi(pw);
-  return fmaf(d, acc, fmaf(-128.0f, d, m) * x.sum);
+  return fmaf(d * x.s, (float)S, fmaf(8.0f, d, m) * x.sum);
 }
 
 __device__ __forceinline__ void q4_put_partial(const GemvQ4& g, int rb, int s, float v, LS float* red) {
@@ -123,70 +111,125 @@ __device__ __forceinline__ void q4_put_partial(const GemvQ4& g, int rb, int s, f
   }
 }
 
-// Unit partials of one row chunk -> red[row * S + segment], all eight waves streaming.
-__device__ __forceinline__ void gemv_q4_partials(const GemvQ4& g0, const LS u32* xin, LS float* red) {
+// A wave's units in flight: their loads and unit numbers.
+struct Q4Ring {
+  Q4Unit r[Q4_RING];
+  int uk[Q4_RING];
+};
+
+// Unit sources of one row chunk (uniform values).
+struct Q4Src {
+  __amdgpu_buffer_rsrc_t rt;
+  int RB, U, G, S, K, R;
+  __device__ __forceinline__ void init(const GemvQ4& g0) {
+    const MK_G uint8_t* T = uni_ptr(g0.T);
+    R = uni(g0.R);
+    K = uni(g0.K);
+    S = uni(g0.S);
+    RB = (R + 3) >> 2;
+    U = RB * S;
+    G = K >> 5;
+    rt = __builtin_amdgcn_make_buffer_rsrc((void*)T, 0, RB * G * Q4_TILE, 0x00020000);
+  }
+  __device__ __forceinline__ int grab(LS int* ctr) const {
+    int v = 0;
+    if (lane() == 0) v = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(v);
+  }
+  // loads of unit u (zeros for u >= U or column blocks past K)
+  __device__ __forceinline__ void issue(Q4Unit& r, int u) const {
+    constexpr int OOB = 0x7ffffff0;  // past the resource: the load returns zeros
+    const int rb = u / S, s = u - rb * S;
+    const int ng = min(64, G - 64 * s);  // column blocks in this segment
+    const bool live = u < U && lane() < ng;
+    const int o = rb * G * Q4_TILE + s * 64 * Q4_TILE + lane() * 16;
+    const int pl = ng * 16;  // plane bytes
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      r.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rt, live ? o + k * pl : OOB, 0, 2 /* nt */);
+    r.p = __builtin_amdgcn_raw_buffer_load_b128(rt, live ? o + 4 * pl : OOB, 0, 2 /* nt */);
+  }
+};
+
+// The first Q4_RING units of g's first row chunk for this wave: taken from the counter and their
+// loads issued.  Weights do not depend on activations, so a wave primes the next GEMV before it
+// waits for that GEMV's inputs.
+__device__ __forceinline__ void gemv_q4_prime(const GemvQ4& g, LS int* ctr, Q4Ring& q) {
+  GemvQ4 c0 = g;
+  c0.R = min(g.R, g.chunk_rows());
+  Q4Src src;
+  src.init(c0);
+#pragma unroll
+  for (int k = 0; k < Q4_RING; ++k) {
+    q.uk[k] = src.grab(ctr);
+    src.issue(q.r[k], q.uk[k]);
+  }
+}
+
+// Unit partials of one row chunk -> red[row * S + segment], all eight waves streaming; ctr is the
+// LDS unit counter (zero before the first grab; gemv_q4 clears it again after the partials).
+// primed: this wave's ring already holds its first units (gemv_q4_prime).
+__device__ __forceinline__ void gemv_q4_partials(const GemvQ4& g0, const LS u32* xin, LS float* red, LS int* ctr,
+                                                 Q4Ring& q, bool primed) {
+  Q4Src src;
+  src.init(g0);
   GemvQ4 g = g0;
-  g.C = uni_ptr(g0.C);
-  g.P = uni_ptr(g0.P);
-  g.R = uni(g0.R);
-  g.K = uni(g0.K);
-  g.S = uni(g0.S);
-  const int RB = (g.R + 3) >> 2, U = RB * g.S;
-  const int u0 = split(U, MK_NWAVE, wave()), u1 = split(U, MK_NWAVE, wave() + 1);
-  if (u0 >= u1) return;
+  g.R = src.R;
+  g.K = src.K;
+  g.S = src.S;
+  const int U = src.U;
   Q4X x;
   int xs = -1;
-  auto issue2 = [&](Q4Unit (&r)[2], int u) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ui = u + i;
-      if (ui < u1) {
-        const int s = ui / RB;
-        q4_issue(g, ui - s * RB, s, r[i]);
-      }
-    }
-  };
   auto unit = [&](const Q4Unit& r, int u) {
-    const int s = u / RB, rb = u - s * RB;
+    const int rb = u / g.S, s = u - rb * g.S;
     if (s != xs) {
       q4_load_x(x, xin, s, g.K);
       xs = s;
     }
-    const float a0 = q4_row(r.c[0], r.p[0], x);
-    const float a1 = q4_row(r.c[1], r.p[1], x);
-    const float a2 = q4_row(r.c[2], r.p[2], x);
-    const float a3 = q4_row(r.c[3], r.p[3], x);
+    const float a0 = q4_row(r.c[0], r.p.x, x);
+    const float a1 = q4_row(r.c[1], r.p.y, x);
+    const float a2 = q4_row(r.c[2], r.p.z, x);
+    const float a3 = q4_row(r.c[3], r.p.w, x);
     q4_put_partial(g, rb, s, reduce_rows4(a0, a1, a2, a3), red);
   };
-  Q4Unit cur[2], nxt[2];
-  issue2(cur, u0);
-  // nothing may look outstanding in cur when the loop starts (conditional loads; see the BF16 GEMV)
-  wait_vm<0>();
-  for (int u = u0; u < u1; u += 2) {
-    issue2(nxt, u + 2);
-    keep_issued();
-    unit(cur[0], u);
-    if (u + 1 < u1) unit(cur[1], u + 1);
+  if (!primed) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) cur[i] = nxt[i];
+    for (int k = 0; k < Q4_RING; ++k) {
+      q.uk[k] = src.grab(ctr);
+      src.issue(q.r[k], q.uk[k]);
+    }
   }
-  // the look-ahead loads past the range were never issued; wait for any still counted
+  // each wave's grabs increase, so once its oldest unit is past U every later one is too
+  while (q.uk[0] < U) {
+#pragma unroll
+    for (int k = 0; k < Q4_RING; ++k) {
+      const bool live = q.uk[k] < U;
+      if (live) unit(q.r[k], q.uk[k]);
+      q.uk[k] = live ? src.grab(ctr) : U;
+      src.issue(q.r[k], q.uk[k]);
+    }
+  }
+  // the last loads of the ring read zeros; wait for them before the registers are reused
   wait_vm<0>();
 }
 
 // W . x over the slice, then epi(row, value, 0) (or, PAIRS, epi(pair, row 2 pair, row 2 pair + 1))
 // by the streaming threads (their stores stay off the polling waves' queues).
+// q / primed: as for gemv_q4_partials (the prime covers the first row chunk).
 template <bool PAIRS, bool EPI_ALL, typename Epi>
-__device__ __forceinline__ void gemv_q4(const GemvQ4& G, const LS u32* xin, LS float* red, Tracer& tr, Epi epi) {
+__device__ __forceinline__ void gemv_q4(const GemvQ4& G, const LS u32* xin, LS float* red, LS int* ctr, Q4Ring& q,
+                                        bool primed, Tracer& tr, Epi epi) {
   const int rc = G.chunk_rows();
-  for (int r0 = 0; r0 < G.R; r0 += rc) {
+  // at least one pass, also for an empty slice: the counter must be cleared behind the prime's
+  // grabs and the primed loads waited for
+  for (int r0 = 0; r0 == 0 || r0 < G.R; r0 += rc) {
     GemvQ4 g = G;
-    g.C = G.C + (size_t)r0 * (size_t)(G.K >> 1);
-    g.P = G.P + (size_t)r0 * (size_t)(G.K >> 5);
-    g.R = min(rc, G.R - r0);
-    gemv_q4_partials(g, xin, red);
+    g.T = G.T + (size_t)(r0 >> 2) * (size_t)(G.K >> 5) * Q4_TILE;  // rc is a multiple of 4
+    g.R = max(0, min(rc, G.R - r0));
+    gemv_q4_partials(g, xin, red, ctr, q, primed && r0 == 0);
     tr.mark();
     wg_bar();
+    if (tid() == 0) *ctr = 0;  // the next use comes after at least one more barrier
     tr.mark();
     const int stride = EPI_ALL ? MK_NT : NCT;
     if (EPI_ALL || streamer()) {
@@ -201,14 +244,17 @@ __device__ __forceinline__ void gemv_q4(const GemvQ4& G, const LS u32* xin, LS f
   }
 }
 
-// Row `tok` of a Q4G32 matrix [vocab][D] -> x[0..D) in FP32 (d q + m: exact in FP32 for these
-// widths), one code word (8 columns) per thread.
-__device__ __forceinline__ void q4_embed_row(const MK_G uint16_t* E, int vocab, int D, int tok, LS float* x) {
-  const MK_G u32* codes = (const MK_G u32*)((const MK_G uint8_t*)E + (size_t)tok * (size_t)(D >> 1));
-  const MK_G u32* par = q4_params(E, vocab, D) + (size_t)tok * (size_t)(D >> 5);
+// Row `tok` of the tiled 4-bit embedding [vocab][D] -> x[0..D) in FP32 (d q + m: exact in FP32
+// for these widths), one code word (8 columns) per thread.
+__device__ __forceinline__ void q4_embed_row(const MK_G uint16_t* E, int D, int tok, LS float* x) {
+  const int G = D >> 5;
+  const MK_G uint8_t* rowb = (const MK_G uint8_t*)E + (size_t)(tok >> 2) * (size_t)G * Q4_TILE;
+  const int r = tok & 3;
   for (int i = tid(); i < (D >> 3); i += MK_NT) {
-    const u32 v = codes[i];
-    const u32 pw = par[i >> 2];
+    const int gi = i >> 2, s = gi >> 6, l = gi & 63, ng = min(64, G - 64 * s);
+    const MK_G uint8_t* seg = rowb + (size_t)s * 64 * Q4_TILE;
+    const u32 v = *(const MK_G u32*)(seg + r * ng * 16 + l * 16 + 4 * (i & 3));
+    const u32 pw = *(const MK_G u32*)(seg + 4 * ng * 16 + l * 16 + 4 * r);
     const float d = f16_lo(pw), m = f16_hi(pw);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -218,18 +264,23 @@ __device__ __forceinline__ void q4_embed_row(const MK_G uint16_t* E, int vocab, 
   }
 }
 
-// RMSNorm as in rmsnorm(), the BF16 gains read from global memory (issued before the sum of
-// squares so their latency overlaps it).  D <= 4 * MK_NT * Q4_GAIN_IT.
-constexpr int Q4_GAIN_IT = 4;
-__device__ __forceinline__ void rmsnorm_gg(const LS float* x, const MK_G uint16_t* g, LS u32* xn, int D, float eps,
+// x -> xf = x / sqrt(mean x^2 + eps) * g in FP32 (packed for the GEMV by q4_pack).  Every wave
+// sums the squares itself (same order in every wave); the polling threads read the BF16 gains
+// from global memory (issued before the sum) and write xf, so the streaming waves, whose queues
+// may hold the next GEMV's primed loads, issue no load here.  D <= 4 * NPT * Q4_GAIN_IT.
+constexpr int Q4_GAIN_IT = 8;
+__device__ __forceinline__ void rmsnorm_gg(const LS float* x, const MK_G uint16_t* g, LS float* xf, int D, float eps,
                                            Tracer& tr) {
   D = uni(D);
   const int D4 = D >> 2;
+  const int pl = tid() - NCT;
   u32x2 gg[Q4_GAIN_IT];
+  if (!streamer()) {
 #pragma unroll
-  for (int k = 0; k < Q4_GAIN_IT; ++k) {
-    const int c = tid() + k * MK_NT;
-    gg[k] = c < D4 ? *(const MK_G u32x2*)(g + 4 * c) : u32x2{0u, 0u};
+    for (int k = 0; k < Q4_GAIN_IT; ++k) {
+      const int c = pl + k * NPT;
+      gg[k] = c < D4 ? *(const MK_G u32x2*)(g + 4 * c) : u32x2{0u, 0u};
+    }
   }
   const LS f32x4* x4 = (const LS f32x4*)x;
   float s = 0.f;
@@ -251,22 +302,80 @@ __device__ __forceinline__ void rmsnorm_gg(const LS float* x, const MK_G uint16_
   s = wave_sum(s);
   const float r = 1.0f / sqrtf(s / (float)D + eps);
   tr.mark();
+  if (!streamer()) {
 #pragma unroll
-  for (int k = 0; k < Q4_GAIN_IT; ++k) {
-    const int c = tid() + k * MK_NT;
-    if (c < D4) {
-      const f32x4 v = x4[c];
-      u32 h[4], l[4];
-      split_hl(v.x * r * __uint_as_float(gg[k].x << 16), h[0], l[0]);
-      split_hl(v.y * r * __uint_as_float(gg[k].x & 0xffff0000u), h[1], l[1]);
-      split_hl(v.z * r * __uint_as_float(gg[k].y << 16), h[2], l[2]);
-      split_hl(v.w * r * __uint_as_float(gg[k].y & 0xffff0000u), h[3], l[3]);
-      const int o = hl_word(4 * c);
-      *(LS u32x2*)(xn + o) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *(LS u32x2*)(xn + o + 4) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    for (int k = 0; k < Q4_GAIN_IT; ++k) {
+      const int c = pl + k * NPT;
+      if (c < D4) {
+        const f32x4 v = x4[c];
+        ((LS f32x4*)xf)[c] =
+            f32x4{v.x * r * __uint_as_float(gg[k].x << 16), v.y * r * __uint_as_float(gg[k].x & 0xffff0000u),
+                  v.z * r * __uint_as_float(gg[k].y << 16), v.w * r * __uint_as_float(gg[k].y & 0xffff0000u)};
+      }
     }
   }
   tr.mark();
+  wg_bar();
+}
+
+// FP32 v[0..n) (n a multiple of 32) -> in place, the GEMV's packed activations: block g of 32
+// columns takes words [20 g, 20 g + 20): 16 digit words (8-column word i, digit k at 4 i + k; in a
+// digit word, column 2t's digit is the nibble at bit 4t and column 2t + 1's the nibble at bit
+// 16 + 4t, as in the code words), then s_g and sum_j x_j.  T_j = rint(x_j / s_g), |T_j| <= 30000,
+// is written as sum_k D_k 16^k with digits D_k in [-8, 7]: the nibbles of T + 0x8888, each XOR 8.
+// A quad of lanes handles a block (8 columns per lane); all blocks are read before any is written
+// (the packed form is smaller, so block g's words overlap only blocks <= g).  Between barriers,
+// by all threads; n <= 8 * MK_NT * Q4_PACK_IT.
+constexpr int Q4_PACK_IT = 5;
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v = v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void q4_pack(LS float* v, int n) {
+  n = uni(n);
+  const int n8 = n >> 3;
+  u32x4 dg[Q4_PACK_IT];
+  u32x2 gp[Q4_PACK_IT];
+#pragma unroll
+  for (int it = 0; it < Q4_PACK_IT; ++it) {
+    const int i = it * MK_NT + tid();
+    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, b = a;
+    if (i < n8) {
+      a = ((const LS f32x4*)v)[2 * i];
+      b = ((const LS f32x4*)v)[2 * i + 1];
+    }
+    const float mx = quad_max(fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                                    fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w)))));
+    const float sm = quad_sum(((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w)));
+    const float inv = mx > 0.f ? Q4_TMAX / mx : 0.f;
+    // rint(x * inv) + 0x8888 from the bits of x * inv + 1.5 * 2^23 (round to nearest even)
+    auto u16 = [&](float e) { return __float_as_uint(fmaf(e, inv, 12582912.0f)) + (0x8888u - 0x4B400000u); };
+    u32 P0 = u16(a.x) | (u16(a.y) << 16), P1 = u16(a.z) | (u16(a.w) << 16);
+    u32 P2 = u16(b.x) | (u16(b.y) << 16), P3 = u16(b.z) | (u16(b.w) << 16);
+    // 4 x 4 nibble transpose in both 16-bit halves: row t (P_t) holds the digits of columns 2t and
+    // 2t + 1; afterwards row k holds digit k of every column
+    u32 t;
+    t = ((P0 >> 8) ^ P2) & 0x00FF00FFu; P2 ^= t; P0 ^= t << 8;
+    t = ((P1 >> 8) ^ P3) & 0x00FF00FFu; P3 ^= t; P1 ^= t << 8;
+    t = ((P0 >> 4) ^ P1) & 0x0F0F0F0Fu; P1 ^= t; P0 ^= t << 4;
+    t = ((P2 >> 4) ^ P3) & 0x0F0F0F0Fu; P3 ^= t; P2 ^= t << 4;
+    dg[it] = u32x4{P0 ^ 0x88888888u, P1 ^ 0x88888888u, P2 ^ 0x88888888u, P3 ^ 0x88888888u};
+    gp[it] = u32x2{__float_as_uint(mx * (1.0f / Q4_TMAX)), __float_as_uint(sm)};
+  }
+  wg_bar();
+#pragma unroll
+  for (int it = 0; it < Q4_PACK_IT; ++it) {
+    const int i = it * MK_NT + tid();
+    if (i < n8) {
+      LS u32* b = (LS u32*)v + (i >> 2) * Q4_XW;
+      ((LS u32x4*)b)[i & 3] = dg[it];
+      if ((i & 3) == 0) *(LS u32x2*)(b + 16) = gp[it];
+    }
+  }
   wg_bar();
 }
 

@@ -78,55 +78,6 @@ __device__ __forceinline__ bool gather_map_all(const Ctx& cx, int n, SrcFn src, 
   return ok;
 }
 
-template <bool HL>
-__device__ __forceinline__ bool gather_vec_all(const Ctx& cx, const MK_G mk_u64* src, int n, LS float* dst) {
-  src = uni_ptr(src);
-  n = uni(n);
-  const u32 e = cx.epoch;
-  const int pl = tid();
-  const int np = (n + 1) >> 1;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, np * 16, 0x00020000);
-  bool ok = true;
-  for (int base = 0; ok && base < np; base += MK_NT * PBV) {
-    u32 pending = 0;
-#pragma unroll
-    for (int k = 0; k < PBV; ++k)
-      if (base + k * MK_NT + pl < np) pending |= 1u << k;
-    u32 spins = 0;
-    while (pending) {
-      u32x4 v[PBV];
-#pragma unroll
-      for (int k = 0; k < PBV; ++k)
-        if ((pending >> k) & 1u)
-          v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + k * MK_NT + pl) * 16, 0, 16 /* sc1 */);
-#pragma unroll
-      for (int k = 0; k < PBV; ++k) {
-        const int j = base + k * MK_NT + pl;
-        const bool two = 2 * j + 1 < n;
-        if (((pending >> k) & 1u) && v[k].y == e && (!two || v[k].w == e)) {
-          if (HL) {
-            put_hl2((LS u32*)dst, 2 * j, __uint_as_float(v[k].x), two ? __uint_as_float(v[k].z) : 0.f);
-          } else {
-            dst[2 * j] = __uint_as_float(v[k].x);
-            if (two) dst[2 * j + 1] = __uint_as_float(v[k].z);
-          }
-          pending &= ~(1u << k);
-        }
-      }
-      if (pending) {
-        ++spins;
-        if (((spins & 255u) == 0 && err_seen(cx)) || spins > MK_SPIN_LIMIT) {
-          if (spins > MK_SPIN_LIMIT) set_err(cx, 1u);
-          ok = false;
-          break;
-        }
-      }
-    }
-  }
-  wait_vm<0>();
-  return ok;
-}
-
 // RMSNorm of nt residuals x[t] -> xn[t] (hi/lo BF16 pairs).  Wave t forms position t's sum of
 // squares exactly as every wave of the decode kernel's rmsnorm does; then all threads scale.
 // Ends with a barrier.
@@ -785,7 +736,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
     tr.mark();
     // mixer outputs of every position -> out-projection rows + residual -> records
     {
-      const bool ok = gather_vec_all<false>(cx, L.ll_o, nt * K, s.vec);
+      const bool ok = gather_vec_all<false, PBV>(cx, L.ll_o, nt * K, s.vec);
       if (wg_bar_or(s, !ok)) return;
       for (int t = 0; t < nt; ++t) to_hl(s.vec + t * K, K);
       wg_bar();
@@ -799,7 +750,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
     ggu.init(L.w_gu + (size_t)2 * j0 * D, 2 * (j1 - j0), D);
     gemv_v_pre(ggu, nt, pre);
     {
-      const bool ok = gather_vec_all<false>(cx, L.ll_x1, nt * D, s.x);
+      const bool ok = gather_vec_all<false, PBV>(cx, L.ll_x1, nt * D, s.x);
       if (wg_bar_or(s, !ok)) return;
     }
     tr.mark();
@@ -813,7 +764,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
     gdn.init(L.w_down + (size_t)d0 * F, d1 - d0, F);
     gemv_v_pre(gdn, nt, pre);
     {
-      const bool ok = gather_vec_all<true>(cx, L.ll_h, nt * F, s.vec);
+      const bool ok = gather_vec_all<true, PBV>(cx, L.ll_h, nt * F, s.vec);
       if (wg_bar_or(s, !ok)) return;
     }
     tr.mark();
@@ -824,7 +775,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
     input_rows(l + 1, gin);
     gemv_v_pre(gin, nt, pre);
     {
-      const bool ok = gather_vec_all<false>(cx, L.ll_x2, nt * D, s.x);
+      const bool ok = gather_vec_all<false, PBV>(cx, L.ll_x2, nt * D, s.x);
       if (wg_bar_or(s, !ok)) return;
     }
   }
@@ -885,7 +836,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   // workgroup 0: greedy choices, accepted count, outputs, new position
   if (w == 0) {
     wg_bar();  // the running-argmax cells are read before the gather reuses the region
-    const bool ok = gather_vec_all<false>(cx, p.ll_am, nt * 2 * NW, s.vec);
+    const bool ok = gather_vec_all<false, PBV>(cx, p.ll_am, nt * 2 * NW, s.vec);
     if (wg_bar_or(s, !ok)) return;
     // wave t: position t's choice
     if (wave() < nt) {
@@ -909,7 +860,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   tr.mark();
   // every workgroup: the accepted count, then its DeltaNet rows back to the state after position a
   {
-    const bool ok = gather_vec_all<false>(cx, p.ll_acc, 1, s.scr);
+    const bool ok = gather_vec_all<false, PBV>(cx, p.ll_acc, 1, s.scr);
     if (wg_bar_or(s, !ok)) return;
   }
   const int a = uni(__float_as_int(s.scr[0]));

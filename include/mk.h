@@ -63,7 +63,8 @@ enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4, MK_Q4G32 = 5 };
  * 0 <= max_verify_k <= 5 (each unit adds one position's records, one DeltaNet state snapshot and
  * LDS; mk_create returns MK_E_OCCUPANCY if the verify kernel's LDS does not fit).
  * weight_dtype is MK_BF16 or MK_Q4G32.  MK_Q4G32 also needs hidden, ffn, H*dv and nq*head_dim to
- * be multiples of 32, hidden <= 8192 and max_verify_k == 0; its prompts run one decode launch per
+ * be multiples of 32, hidden <= 8192, those other widths <= 20480 and max_verify_k == 0; its
+ * prompts run one decode launch per
  * token (the prefill kernels take BF16 weights). */
 typedef struct {
   int32_t n_layers, hidden, ffn, vocab;
