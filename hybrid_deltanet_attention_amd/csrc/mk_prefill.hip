@@ -477,7 +477,7 @@ __global__ void __launch_bounds__(256) pf_dn_scan_kernel(float* __restrict__ S, 
 // (rows of K, Q, V, U, O are tokens).  Everything that does not involve S0 -- K K^T, Q K^T, the
 // decays and W = (I + M)^{-1} diag(beta) -- is computed for all chunks in parallel
 // (pf_dn_cprep_kernel); the pass that carries the state runs chunk after chunk, each workgroup on
-// 8 rows of one head's state (pf_dn_cscan_kernel).
+// 16 rows of one head's state (pf_dn_cscan_mfma_kernel).
 constexpr int PC = 64;                          // tokens per chunk
 constexpr int PC_BLK = 2 * PC * PC + 2 * PC + 4;  // per (chunk, head): W, Bt [PC][PC], gam, dlt [PC], gamma_C
 
@@ -623,38 +623,73 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
   for (int k = 0; k < PC / 4; ++k) gW[(q + 4 * k) * PC + j] = w[k];
 }
 
-// The state-carrying pass: workgroup = (head, 8 state rows), 512 threads (two waves per SIMD, so
-// LDS latency of one hides behind the other); chunk after chunk
-//   Z = K S0^T, P = Q S0^T (this workgroup's rows), R = V - diag(gam) Z, U = W R,
-//   O = diag(gam) P + Bt U -> outputs (hi/lo BF16), S <- gamma_C S + (diag(dlt) U)^T K.
+// The state-carrying pass, chunk after chunk with state S0 on entry:
+//   Z = K S0^T, P = Q S0^T, R = V - diag(gam) Z, U = W R,
+//   O = diag(gam) P + Bt U -> outputs (hi/lo BF16), S <- gamma_C S0 + (diag(dlt) U)^T K.
 constexpr int CS_NT = 512;
+// On the FP32 matrix cores (v_mfma_f32_16x16x4_f32: exact FP32 products, FP32 sums): workgroup =
+// (head, 16 state rows), 8 waves.  The products are formed transposed, rows of
+// the state as the 16-row M side:
+//   Z^T = S0 K^T, P^T = S0 Q^T           waves 0-3 / 4-7, one 16-token block each
+//   R^T = V^T - Z^T diag(gam)            waves 0-3, in registers -> LDS
+//   U^T = R^T W^T                        waves 0-3
+//   O^T = P^T diag(gam) + U^T Bt^T       waves 4-7 -> outputs (hi/lo BF16)
+//   S   = gamma_C S0 + (U^T diag(dlt)) K one 16-column block of keys per wave
+// Per chunk the operands move through LDS once per MFMA fragment instead of once per output.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// c + A B^T over NK shared columns, A and B given by this lane's row (arow: M-side row lane % 16,
+// brow: N-side row lane % 16).  Within each 16-column block, lane group lk = lane / 16 reads its
+// four contiguous columns 4 lk .. 4 lk + 3 with one 16-byte load and feeds them to four MFMAs (the
+// k-th MFMA of the block takes column 4 lk + k from every lane group: a partition of the block).
+// Two accumulators alternate between blocks so consecutive MFMAs do not wait for each other.
+template <int NK>
+__device__ __forceinline__ f32x4 mfma_rows(const float* arow, const float* brow, f32x4 c) {
+  const int lk = (threadIdx.x & 63) >> 4;
+  f32x4 acc[2] = {c, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int m = 0; m < NK / 16; ++m) {
+    const f32x4 a = *(const f32x4*)(arow + 16 * m + 4 * lk);
+    const f32x4 b = *(const f32x4*)(brow + 16 * m + 4 * lk);
+    f32x4& d = acc[m & 1];
+    d = mfma4(a.x, b.x, d);
+    d = mfma4(a.y, b.y, d);
+    d = mfma4(a.z, b.z, d);
+    d = mfma4(a.w, b.w, d);
+  }
+  return acc[0] + acc[1];
+}
+constexpr int CM_RW = 16;
 template <int DKM>
-__global__ void __launch_bounds__(CS_NT) pf_dn_cscan_kernel(float* __restrict__ S, const float* __restrict__ QK,
-                                                            const float* __restrict__ CH, const float* __restrict__ Y,
-                                                            int ldy, int T, int H, int dk, int dv,
-                                                            uint16_t* __restrict__ Ohi, uint16_t* __restrict__ Olo,
-                                                            int ldo) {
-  constexpr int RW = 8;
-  __shared__ __attribute__((aligned(16))) float sk[PC][DKM + 4];
-  __shared__ __attribute__((aligned(16))) float sq[PC][DKM + 4];
-  __shared__ __attribute__((aligned(16))) float sw[PC][PC + 4];
-  __shared__ __attribute__((aligned(16))) float sbt[PC][PC + 4];
-  __shared__ __attribute__((aligned(16))) float ss[RW][DKM + 4];
+__global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restrict__ S, const float* __restrict__ QK,
+                                                                 const float* __restrict__ CH,
+                                                                 const float* __restrict__ Y, int ldy, int T, int H,
+                                                                 int dk, int dv, uint16_t* __restrict__ Ohi,
+                                                                 uint16_t* __restrict__ Olo, int ldo) {
+  constexpr int RW = CM_RW, LK = DKM + 4, LC = PC + 4;
+  __shared__ __attribute__((aligned(16))) float sk[PC][LK];
+  __shared__ __attribute__((aligned(16))) float sq[PC][LK];
+  __shared__ __attribute__((aligned(16))) float sw[PC][LC];
+  __shared__ __attribute__((aligned(16))) float sbt[PC][LC];
+  __shared__ __attribute__((aligned(16))) float ss[RW][LK];
+  __shared__ __attribute__((aligned(16))) float sr[RW][LC];
+  __shared__ __attribute__((aligned(16))) float su[RW][LC];
   __shared__ float sv[PC][RW];
-  __shared__ __attribute__((aligned(16))) float sr[RW][PC + 4];  // row-major per state row
-  __shared__ __attribute__((aligned(16))) float su[RW][PC + 4];
   __shared__ __attribute__((aligned(16))) float sgam[PC];
   __shared__ __attribute__((aligned(16))) float sdlt[PC + 4];
-  const int rbs = (dv + RW - 1) / RW;
-  const int h = blockIdx.x / rbs, r0 = (blockIdx.x - h * rbs) * RW;
-  const int tid = threadIdx.x;
+  // workgroup b takes head b % H and row block b / H: the row blocks of one head share an XCD
+  // (workgroups are dealt to the 8 XCDs round-robin), so that head's chunk operands are fetched
+  // into one L2 rather than into eight
+  const int h = blockIdx.x % H, r0 = (blockIdx.x / H) * RW;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, lr = l & 15, lk = l >> 4;
   const int n4 = dk >> 2;
   if (dk < DKM) {  // key columns past dk take part in the products as zeros
-    for (int f = tid; f < PC * (DKM + 4); f += CS_NT) {
+    for (int f = tid; f < PC * LK; f += CS_NT) {
       (&sk[0][0])[f] = 0.f;
       (&sq[0][0])[f] = 0.f;
     }
-    for (int f = tid; f < RW * (DKM + 4); f += CS_NT) (&ss[0][0])[f] = 0.f;
+    for (int f = tid; f < RW * LK; f += CS_NT) (&ss[0][0])[f] = 0.f;
     __syncthreads();
   }
   for (int f = tid; f < RW * n4; f += CS_NT) {
@@ -664,15 +699,22 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_kernel(float* __restrict__ 
   }
   const int off_v = 2 * H * dk + h * dv + r0;
   const int nc = (T + PC - 1) / PC;
-  // thread roles: (token t, state row i) for the per-token products, (row ui, 2 key columns) for
-  // the state update
-  const int t = tid >> 3, i = tid & 7;
-  const int ui = tid >> 6, ue = 2 * (tid & 63);
-  // A chunk's operands are loaded into registers while the previous chunk computes.
-  constexpr int NL = PC * DKM / 4 / CS_NT, NM = PC * PC / 4 / CS_NT;
-  f32x4 rq[NL], rk[NL], rw[NM], rb[NM];
-  float rg = 0.f, rv = 0.f;
-  auto fetch = [&](int c) {
+  // a chunk's operands are loaded into registers two chunks ahead (two register sets, used in
+  // turn; the chunk index is clamped so every set is always loaded and the load counts stay uniform)
+  constexpr int NL = PC * DKM / 4 / CS_NT, NM = PC * PC / 4 / CS_NT, NV = PC * RW / CS_NT;
+  struct Ops {
+    f32x4 rq[NL], rk[NL], rw[NM], rb[NM];
+    float rg, rv[NV];
+  };
+  Ops oa, ob;
+  auto fetch = [&](Ops& o, int c) {
+    c = min(c, nc - 1);
+    f32x4(&rq)[NL] = o.rq;
+    f32x4(&rk)[NL] = o.rk;
+    f32x4(&rw)[NM] = o.rw;
+    f32x4(&rb)[NM] = o.rb;
+    float& rg = o.rg;
+    float(&rv)[NV] = o.rv;
     const int t0 = c * PC, Cn = min(PC, T - t0);
     const float* blk = CH + ((size_t)c * H + h) * PC_BLK;
 #pragma unroll
@@ -693,9 +735,19 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_kernel(float* __restrict__ 
       rb[x] = *(const f32x4*)(blk + PC * PC + 4 * f);
     }
     rg = tid <= 2 * PC ? blk[2 * PC * PC + tid] : 0.f;  // gam [0, PC), dlt [PC, 2 PC], gamma_C last
-    rv = (t < Cn && r0 + i < dv) ? Y[(size_t)(t0 + t) * ldy + off_v + i] : 0.f;
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      const int f = tid + CS_NT * x, tt = f / RW, i = f - tt * RW;
+      rv[x] = (tt < Cn && r0 + i < dv) ? Y[(size_t)(t0 + tt) * ldy + off_v + i] : 0.f;
+    }
   };
-  auto stash = [&]() {
+  auto stash = [&](const Ops& o) {
+    const f32x4(&rq)[NL] = o.rq;
+    const f32x4(&rk)[NL] = o.rk;
+    const f32x4(&rw)[NM] = o.rw;
+    const f32x4(&rb)[NM] = o.rb;
+    const float rg = o.rg;
+    const float(&rv)[NV] = o.rv;
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
       const int f = tid + CS_NT * x, tt = f / n4, e = (f - tt * n4) * 4;
@@ -712,61 +764,72 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_kernel(float* __restrict__ 
     }
     if (tid < PC) sgam[tid] = rg;
     else if (tid <= 2 * PC) sdlt[tid - PC] = rg;
-    sv[t][i] = rv;
-  };
-  fetch(0);
-  for (int c = 0; c < nc; ++c) {
-    const int t0 = c * PC, Cn = min(PC, T - t0);
-    stash();
-    __syncthreads();
-    if (c + 1 < nc) fetch(c + 1);
-    // Z and P for token t, row i
-    float z = 0.f, p = 0.f;
-#pragma unroll 8
-    for (int e = 0; e < DKM; e += 4) {  // columns past dk are zero in LDS
-      const f32x4 s0 = *(const f32x4*)&ss[i][e];
-      z = dot4(*(const f32x4*)&sk[t][e], s0, z);
-      p = dot4(*(const f32x4*)&sq[t][e], s0, p);
-    }
-    sr[i][t] = sv[t][i] - sgam[t] * z;
-    __syncthreads();
-    // U = W R.  W is lower triangular: every lane runs the full row (zeros above the diagonal), so
-    // the trip count is the same for all lanes.
-    {
-      float u = 0.f;
-#pragma unroll 4
-      for (int jj = 0; jj < PC; jj += 4) u = dot4(*(const f32x4*)&sw[t][jj], *(const f32x4*)&sr[i][jj], u);
-      su[i][t] = u;
-    }
-    __syncthreads();
-    // outputs
-    {
-      float y = sgam[t] * p;
-#pragma unroll 4
-      for (int jj = 0; jj < PC; jj += 4) y = dot4(*(const f32x4*)&sbt[t][jj], *(const f32x4*)&su[i][jj], y);
-      if (t < Cn && r0 + i < dv) split_store(y, Ohi, Olo, (size_t)(t0 + t) * ldo + h * dv + r0 + i);
-    }
-    // state update: row ui, key columns ue, ue + 1 (tokens past the prompt have u = 0)
-    if (ue < dk) {
-      float a0 = ss[ui][ue], a1 = ss[ui][ue + 1];
-      const float gc = sdlt[PC];
-      a0 *= gc;
-      a1 *= gc;
-#pragma unroll 4
-      for (int tt = 0; tt < PC; tt += 4) {
-        const f32x4 uu = *(const f32x4*)&su[ui][tt], dd = *(const f32x4*)&sdlt[tt];
-        const float cf[4] = {uu.x * dd.x, uu.y * dd.y, uu.z * dd.z, uu.w * dd.w};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const f32x2 k = *(const f32x2*)&sk[tt + x][ue];
-          a0 = fmaf(cf[x], k.x, a0);
-          a1 = fmaf(cf[x], k.y, a1);
+    for (int x = 0; x < NV; ++x) {
+      const int f = tid + CS_NT * x, tt = f / RW, i = f - tt * RW;
+      sv[tt][i] = rv[x];
+    }
+  };
+  const int nb = wv & 3, tok = 16 * nb + lr;  // this wave's 16-token block, this lane's token
+  fetch(oa, 0);
+  fetch(ob, 1);
+  auto chunk = [&](int c, Ops& o) {
+    const int t0 = c * PC, Cn = min(PC, T - t0);
+    stash(o);
+    __syncthreads();
+    fetch(o, c + 2);
+    // Z^T (waves 0-3) or P^T (waves 4-7) for tokens 16 nb ..: lane holds rows 4 lk + r, token tok
+    const f32x4 zp = mfma_rows<DKM>(&ss[lr][0], wv < 4 ? &sk[tok][0] : &sq[tok][0], f32x4{0.f, 0.f, 0.f, 0.f});
+    if (wv < 4) {
+      const float g = sgam[tok];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sr[4 * lk + r][tok] = sv[tok][4 * lk + r] - g * zp[r];
+    }
+    __syncthreads();
+    if (wv < 4) {
+      const f32x4 u = mfma_rows<PC>(&sr[lr][0], &sw[tok][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) su[4 * lk + r][tok] = u[r];
+    }
+    __syncthreads();
+    if (wv >= 4) {
+      const float g = sgam[tok];
+      const f32x4 o = mfma_rows<PC>(&su[lr][0], &sbt[tok][0], f32x4{g * zp[0], g * zp[1], g * zp[2], g * zp[3]});
+      if (tok < Cn) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * lk + r;
+          if (r0 + row < dv) split_store(o[r], Ohi, Olo, (size_t)(t0 + tok) * ldo + h * dv + r0 + row);
         }
       }
-      ss[ui][ue] = a0;
-      ss[ui][ue + 1] = a1;
+    }
+    // state update: key columns 16 eb .. 16 eb + 15 per wave (tokens past the prompt have u = 0)
+    for (int eb = wv; eb < DKM / 16; eb += 8) {
+      const int e = 16 * eb + lr;
+      const float gc = sdlt[PC];
+      f32x4 acc[2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[0][r] = gc * ss[4 * lk + r][e];
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < PC / 16; ++m) {
+        const int tb = 16 * m + 4 * lk;  // this lane group's four tokens of the block
+        const f32x4 uu = *(const f32x4*)&su[lr][tb], dd = *(const f32x4*)&sdlt[tb];
+        f32x4& d = acc[m & 1];
+        d = mfma4(dd.x * uu.x, sk[tb][e], d);
+        d = mfma4(dd.y * uu.y, sk[tb + 1][e], d);
+        d = mfma4(dd.z * uu.z, sk[tb + 2][e], d);
+        d = mfma4(dd.w * uu.w, sk[tb + 3][e], d);
+      }
+      const f32x4 st = acc[0] + acc[1];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss[4 * lk + r][e] = st[r];
     }
     __syncthreads();  // ss, sk and the chunk matrices are rewritten by the next chunk
+  };
+  for (int c = 0; c < nc; c += 2) {
+    chunk(c, oa);
+    if (c + 1 < nc) chunk(c + 1, ob);
   }
   for (int f = tid; f < RW * n4; f += CS_NT) {
     const int ri = f / n4, e = (f - ri * n4) * 4;
@@ -1413,13 +1476,15 @@ extern "C" int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const f
   if (dk <= 128) {
     // chunked form: all chunks' W, Bt and decays in parallel, then the state pass
     const int nc = (T + PC - 1) / PC;
-    const dim3 g1(nc * H), g2(H * ((dv + 7) / 8));
+    const dim3 g1(nc * H), g2(H * ((dv + CM_RW - 1) / CM_RW));
     if (dk <= 64) {
       hipLaunchKernelGGL(pf_dn_cprep_kernel<64>, g1, dim3(256), 0, s, QK, AB, T, H, dk, CH);
-      hipLaunchKernelGGL(pf_dn_cscan_kernel<64>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+      hipLaunchKernelGGL(pf_dn_cscan_mfma_kernel<64>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo,
+                         ldo);
     } else {
       hipLaunchKernelGGL(pf_dn_cprep_kernel<128>, g1, dim3(256), 0, s, QK, AB, T, H, dk, CH);
-      hipLaunchKernelGGL(pf_dn_cscan_kernel<128>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
+      hipLaunchKernelGGL(pf_dn_cscan_mfma_kernel<128>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo,
+                         ldo);
     }
     return MK_LAUNCH_OK();
   }
