@@ -488,6 +488,31 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float acc) {
   return fmaf(a.w, b.w, acc);
 }
 
+// FP32 matrix-core helpers (v_mfma_f32_16x16x4_f32: exact FP32 products, FP32 sums).
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// c + A B^T over NK shared columns, A and B given by this lane's row (arow: M-side row lane % 16,
+// brow: N-side row lane % 16).  Within each 16-column block, lane group lk = lane / 16 reads its
+// four contiguous columns 4 lk .. 4 lk + 3 with one 16-byte load and feeds them to four MFMAs (the
+// k-th MFMA of the block takes column 4 lk + k from every lane group: a partition of the block).
+// Two accumulators alternate between blocks so consecutive MFMAs do not wait for each other.
+template <int NK>
+__device__ __forceinline__ f32x4 mfma_rows(const float* arow, const float* brow, f32x4 c) {
+  const int lk = (threadIdx.x & 63) >> 4;
+  f32x4 acc[2] = {c, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int m = 0; m < NK / 16; ++m) {
+    const f32x4 a = *(const f32x4*)(arow + 16 * m + 4 * lk);
+    const f32x4 b = *(const f32x4*)(brow + 16 * m + 4 * lk);
+    f32x4& d = acc[m & 1];
+    d = mfma4(a.x, b.x, d);
+    d = mfma4(a.y, b.y, d);
+    d = mfma4(a.z, b.z, d);
+    d = mfma4(a.w, b.w, d);
+  }
+  return acc[0] + acc[1];
+}
 // Per (chunk c, head h): W = (I + M)^{-1} diag(beta) and Bt = lower(Q K^T o G) incl. the diagonal
 // (both [t][j]), gam_t = gamma_t, dlt_t = gamma_last / gamma_t, gamma_last.  Tokens past the end of
 // the prompt have k = q = 0 and beta = 0, so their rows and columns come out zero.
@@ -496,7 +521,9 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
                                                           int T, int H, int dk, float* __restrict__ CH) {
   __shared__ __attribute__((aligned(16))) float sk[PC][DKM + 4];
   __shared__ __attribute__((aligned(16))) float sq[PC][DKM + 4];
-  __shared__ float sm[PC][PC + 1];
+  __shared__ float sm[PC][PC + 1];  // M, strictly lower
+  __shared__ float sx[PC][PC + 1];  // (I + M)^{-1}
+  __shared__ float st[3][16][17];   // block-row partial sums
   __shared__ float sg[PC], sbeta[PC];
   const int h = blockIdx.x % H, c = blockIdx.x / H;
   const int t0 = c * PC, Cn = min(PC, T - t0);
@@ -547,32 +574,16 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
       sg[t] = a;
     }
   }
-  // 4 x 4 blocks of K K^T and Q K^T on and below the diagonal
-  const int tb = tid >> 4, jb = tid & 15;
-  float a[4][4], b[4][4];
+  // K K^T and Q K^T on and below the diagonal, 16 x 16 blocks on the matrix cores: task = (matrix,
+  // lower-triangle block); a lane holds rows 16 bt + 4 lk + r of column 16 bj + lr
+  const int wv = tid >> 6, lane64 = tid & 63, lr = lane64 & 15, lk = lane64 >> 4;
+  f32x4 acc[5];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a[r][q] = b[r][q] = 0.f;
-  if (jb <= tb) {
-    // columns past dk are zero in LDS, so the loop runs over the compile-time width
-#pragma unroll 2
-    for (int e = 0; e < DKM; e += 4) {
-      f32x4 kt[4], qt[4], kj[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        kt[r] = *(const f32x4*)&sk[4 * tb + r][e];
-        qt[r] = *(const f32x4*)&sq[4 * tb + r][e];
-        kj[r] = *(const f32x4*)&sk[4 * jb + r][e];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          a[r][q] = dot4(kt[r], kj[q], a[r][q]);
-          b[r][q] = dot4(qt[r], kj[q], b[r][q]);
-        }
-    }
+  for (int x = 0; x < 5; ++x) {
+    const int task = wv + 4 * x, mat = task / 10, bb = task - mat * 10;
+    const int bt = bb >= 6 ? 3 : (bb >= 3 ? 2 : (bb >= 1 ? 1 : 0)), bj = bb - bt * (bt + 1) / 2;
+    acc[x] = mfma_rows<DKM>(mat ? &sq[16 * bt + lr][0] : &sk[16 * bt + lr][0], &sk[16 * bj + lr][0],
+                            f32x4{0.f, 0.f, 0.f, 0.f});
   }
   __syncthreads();  // cumulative log alphas are in place
   float* blk = CH + ((size_t)c * H + h) * PC_BLK;
@@ -581,14 +592,25 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
   float* gGam = blk + 2 * PC * PC;
   float* gDlt = gGam + PC;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int x = 0; x < 5; ++x) {
+    const int task = wv + 4 * x, mat = task / 10, bb = task - mat * 10;
+    const int bt = bb >= 6 ? 3 : (bb >= 3 ? 2 : (bb >= 1 ? 1 : 0)), bj = bb - bt * (bt + 1) / 2;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = 4 * tb + r, j = 4 * jb + q;
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * bt + 4 * lk + r, j = 16 * bj + lr;
       const float dec = j <= t ? expf(sg[t] - sg[j]) : 0.f;
-      sm[t][j] = j < t ? sbeta[t] * dec * a[r][q] : 0.f;
-      gBt[t * PC + j] = j <= t ? dec * b[r][q] : 0.f;
+      if (mat == 0) sm[t][j] = j < t ? sbeta[t] * dec * acc[x][r] : 0.f;
+      else gBt[t * PC + j] = j <= t ? dec * acc[x][r] : 0.f;
     }
+  }
+  // blocks above the diagonal
+  for (int f = tid; f < PC * PC; f += 256) {
+    const int t = f / PC, j = f - t * PC;
+    if ((j >> 4) > (t >> 4)) {
+      sm[t][j] = 0.f;
+      gBt[f] = 0.f;
+    }
+  }
   if (tid < PC) {
     const float last = sg[Cn - 1];
     gGam[tid] = expf(sg[tid]);
@@ -596,31 +618,48 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
     if (tid == 0) gDlt[PC] = expf(last);
   }
   __syncthreads();
-  // forward substitution, column j of W on 4 lanes (lane q holds rows q, q + 4, ...):
-  // W[j][j] = beta_j, W[t][j] = -sum_{j <= m < t} M[t][m] W[m][j] for t > j
-  const int j = tid >> 2, q = tid & 3;
-  float w[PC / 4];
+  // W = (I + M)^{-1} diag(beta), M strictly lower.  X = (I + M)^{-1} by blocks of 16: the four
+  // diagonal blocks by forward substitution (one wave each, a lane per column), then block row by
+  // block row X_ij = -X_ii sum_{j <= m < i} M_im X_mj.
+  if (lane64 < 16) {
+    const int o = 16 * wv, j = lane64;
+    float x[16];
 #pragma unroll
-  for (int k = 0; k < PC / 4; ++k) w[k] = (q + 4 * k == j) ? sbeta[j] : 0.f;
-#pragma unroll 1
-  for (int t = 1; t < PC; ++t) {
-    // M[t][m] = 0 for m >= t and W[m][j] = 0 for rows not yet reached, so no masking is needed
-    float mv[PC / 4];
+    for (int t = 0; t < 16; ++t) {
+      float v = t == j ? 1.f : 0.f;
 #pragma unroll
-    for (int k = 0; k < PC / 4; ++k) mv[k] = sm[t][q + 4 * k];
-    float part = 0.f;
+      for (int m = 0; m < t; ++m) v = fmaf(-sm[o + t][o + m], x[m], v);  // x[m] = 0 for m < j
+      x[t] = t < j ? 0.f : v;
+    }
 #pragma unroll
-    for (int k = 0; k < PC / 4; ++k) part = fmaf(mv[k], w[k], part);
-    part = dpp_add<0xB1>(part);  // quad_perm [1,0,3,2]
-    part = dpp_add<0x4E>(part);  // quad_perm [2,3,0,1]
-    if (t > j && (t & 3) == q) {
+    for (int t = 0; t < 16; ++t) sx[o + t][o + j] = x[t];
+  }
+  __syncthreads();
+  {
+    const int r = tid >> 4, cc = tid & 15;
+    for (int i = 1; i < 4; ++i) {
+      // T_j = sum_{j <= m < i} M_im X_mj for every j < i
+      for (int j = 0; j < i; ++j) {
+        float v = 0.f;
+        for (int m = j; m < i; ++m)
 #pragma unroll
-      for (int k = 0; k < PC / 4; ++k)
-        if (k == (t >> 2)) w[k] = -part;
+          for (int s2 = 0; s2 < 16; ++s2) v = fmaf(sm[16 * i + r][16 * m + s2], sx[16 * m + s2][16 * j + cc], v);
+        st[j][r][cc] = v;
+      }
+      __syncthreads();
+      for (int j = 0; j < i; ++j) {
+        float v = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) v = fmaf(sx[16 * i + r][16 * i + s2], st[j][s2][cc], v);
+        sx[16 * i + r][16 * j + cc] = -v;
+      }
+      __syncthreads();
     }
   }
-#pragma unroll
-  for (int k = 0; k < PC / 4; ++k) gW[(q + 4 * k) * PC + j] = w[k];
+  for (int f = tid; f < PC * PC; f += 256) {
+    const int t = f / PC, j = f - t * PC;
+    gW[f] = j <= t ? sx[t][j] * sbeta[j] : 0.f;
+  }
 }
 
 // The state-carrying pass, chunk after chunk with state S0 on entry:
@@ -636,30 +675,6 @@ constexpr int CS_NT = 512;
 //   O^T = P^T diag(gam) + U^T Bt^T       waves 4-7 -> outputs (hi/lo BF16)
 //   S   = gamma_C S0 + (U^T diag(dlt)) K one 16-column block of keys per wave
 // Per chunk the operands move through LDS once per MFMA fragment instead of once per output.
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-// c + A B^T over NK shared columns, A and B given by this lane's row (arow: M-side row lane % 16,
-// brow: N-side row lane % 16).  Within each 16-column block, lane group lk = lane / 16 reads its
-// four contiguous columns 4 lk .. 4 lk + 3 with one 16-byte load and feeds them to four MFMAs (the
-// k-th MFMA of the block takes column 4 lk + k from every lane group: a partition of the block).
-// Two accumulators alternate between blocks so consecutive MFMAs do not wait for each other.
-template <int NK>
-__device__ __forceinline__ f32x4 mfma_rows(const float* arow, const float* brow, f32x4 c) {
-  const int lk = (threadIdx.x & 63) >> 4;
-  f32x4 acc[2] = {c, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int m = 0; m < NK / 16; ++m) {
-    const f32x4 a = *(const f32x4*)(arow + 16 * m + 4 * lk);
-    const f32x4 b = *(const f32x4*)(brow + 16 * m + 4 * lk);
-    f32x4& d = acc[m & 1];
-    d = mfma4(a.x, b.x, d);
-    d = mfma4(a.y, b.y, d);
-    d = mfma4(a.z, b.z, d);
-    d = mfma4(a.w, b.w, d);
-  }
-  return acc[0] + acc[1];
-}
 constexpr int CM_RW = 16;
 template <int DKM>
 __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restrict__ S, const float* __restrict__ QK,
