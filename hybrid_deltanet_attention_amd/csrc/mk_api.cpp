@@ -914,12 +914,14 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   for (int c0 = 0; c0 < n && !rc; c0 += T) {
     T = std::min(L.pf_T, n - c0);
     rc |= mk_pf_embed(d_tokens + c0, T, embed, D, c.vocab, X, ctl, st);
+    rc |= mk_pf_rms_split(X, T, D, (const uint16_t*)(ws + L.layers[0].g12), c.rms_eps, Ahi, Alo, lda, st);
     for (int l = 0; l < c.n_layers && !rc; ++l) {
       const LayerOff& lo = L.layers[l];
       const uint16_t* g12 = (const uint16_t*)(ws + lo.g12);
       const uint16_t* w_in = (const uint16_t*)(ws + lo.w_in);
       const uint16_t* w_out = (const uint16_t*)(ws + lo.w_out);
-      rc |= mk_pf_rms_split(X, T, D, g12, c.rms_eps, Ahi, Alo, lda, st);
+      // the next layer's input norm rides on this layer's last residual add
+      const uint16_t* g_next = l + 1 < c.n_layers ? (const uint16_t*)(ws + L.layers[l + 1].g12) : nullptr;
       rc |= mk_pf_gemm(0, Ahi, Alo, lda, T, D, w_in, (int)lo.rows_in, Y, ldy, nullptr, nullptr, 0, PK, PKN, st);
       if (is_attention(c, l)) {
         float* Kc = (float*)(ws + lo.Kc);
@@ -931,12 +933,12 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
         rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, Ahi, Alo, lda,
                             (float*)(ws + L.pf_ch), st);
       }
-      rc |= mk_pf_gemm(1, Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, nullptr, nullptr, 0, PK, PKN, st);
-      rc |= mk_pf_rms_split(X, T, D, g12 + D, c.rms_eps, Ahi, Alo, lda, st);
+      rc |= mk_pf_gemm_res(Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, PK, PKN, g12 + D, c.rms_eps, Ahi, Alo,
+                           lda, st);
       rc |= mk_pf_gemm(2, Ahi, Alo, lda, T, D, (const uint16_t*)(ws + lo.w_gu), 2 * F, nullptr, 0, Hhi, Hlo, F, PK, PKN,
                        st);
-      rc |= mk_pf_gemm(1, Hhi, Hlo, F, T, F, (const uint16_t*)(ws + lo.w_down), D, X, D, nullptr, nullptr, 0, PK, PKN,
-                       st);
+      rc |= mk_pf_gemm_res(Hhi, Hlo, F, T, F, (const uint16_t*)(ws + lo.w_down), D, X, D, PK, PKN, g_next, c.rms_eps,
+                           Ahi, Alo, lda, st);
     }
     p0 += T;
   }

@@ -132,6 +132,10 @@ int mk_pf_rms_split(const float* X, int T, int D, const uint16_t* g, float eps, 
                     void* stream);
 int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W, int N,
                float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, float* P, size_t p_floats, void* stream);
+// residual GEMM C += A W^T; with g (else NULL) the updated rows are then RMS-normalised into (Nhi, Nlo)
+int mk_pf_gemm_res(const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W, int N,
+                   float* C, int ldc, float* P, size_t p_floats, const uint16_t* g, float eps, uint16_t* Nhi,
+                   uint16_t* Nlo, int ldn, void* stream);
 int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB, void* stream);
 int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk, int dv,
                   uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream);

@@ -286,20 +286,44 @@ __global__ void __launch_bounds__((gemm_threads<BM, BN>())) pf_gemm_kernel(
 }
 
 // C[r][c] += sum over splits s (in order) of P[s][r][c]
+// One workgroup per row r: C[r] += the ksplit partials, added in split order.  With a gain g the
+// updated row is then RMS-normalised (eps, gain after normalising) into the split-bf16 operand
+// (Ahi, Alo) of the next projection, so the residual add and the next block's norm share one pass.
 __global__ void __launch_bounds__(256) pf_splitk_add_kernel(const float* __restrict__ P, int ksplit, int M, int N,
-                                                            float* __restrict__ C, int ldc) {
-  const int idx = (blockIdx.x * 256 + threadIdx.x) * 4;  // N is a multiple of 4
-  if (idx >= M * N) return;
-  const int r = idx / N, c = idx - r * N;
-  f32x4 acc = *(const f32x4*)(C + (size_t)r * ldc + c);
-  for (int sp = 0; sp < ksplit; ++sp) {
-    const f32x4 v = *(const f32x4*)(P + (size_t)sp * M * N + idx);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+                                                            float* __restrict__ C, int ldc,
+                                                            const uint16_t* __restrict__ g, float eps,
+                                                            uint16_t* __restrict__ Ahi, uint16_t* __restrict__ Alo,
+                                                            int lda) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;  // N is a multiple of 4
+  float* c = C + (size_t)r * ldc;
+  float ss = 0.f;
+  for (int j = threadIdx.x * 4; j < N; j += 1024) {
+    f32x4 acc = *(const f32x4*)(c + j);
+    for (int sp = 0; sp < ksplit; ++sp) {
+      const f32x4 v = *(const f32x4*)(P + ((size_t)sp * M + r) * N + j);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *(f32x4*)(c + j) = acc;
+    ss = fmaf(acc.x, acc.x, fmaf(acc.y, acc.y, fmaf(acc.z, acc.z, fmaf(acc.w, acc.w, ss))));
   }
-  *(f32x4*)(C + (size_t)r * ldc + c) = acc;
+  if (!g) return;
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = red[0] + red[1] + red[2] + red[3];
+  const float rn = 1.0f / sqrtf(ss / (float)N + eps);
+  for (int j = threadIdx.x * 4; j < N; j += 1024) {
+    const f32x4 a = *(const f32x4*)(c + j);  // this thread's own store above
+    const size_t o = (size_t)r * lda + j;
+    split_store(a.x * rn * bf16f(g[j]), Ahi, Alo, o);
+    split_store(a.y * rn * bf16f(g[j + 1]), Ahi, Alo, o + 1);
+    split_store(a.z * rn * bf16f(g[j + 2]), Ahi, Alo, o + 2);
+    split_store(a.w * rn * bf16f(g[j + 3]), Ahi, Alo, o + 3);
+  }
 }
 
 // ------------------------------------------------------------------------ DeltaNet
@@ -1449,6 +1473,15 @@ static int launch_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int ld
   return MK_LAUNCH_OK();
 }
 
+// number of K ranges for a split-K residual GEMM: enough workgroups for the chip, at least four
+// BK-column K steps per range, and the partials within p_floats
+static int splitk_parts(int M, int K, int N, int big, size_t p_floats) {
+  const int nk = (K + BK - 1) / BK;
+  int ks = std::min(std::max(1, 256 / big), std::max(1, nk / 4));
+  while (ks > 1 && (size_t)ks * M * N > p_floats) --ks;
+  return ks;
+}
+
 extern "C" int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W,
                           int N, float* C, int ldc, uint16_t* Hhi, uint16_t* Hlo, int ldh, float* P, size_t p_floats,
                           void* stream) {
@@ -1466,17 +1499,31 @@ extern "C" int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int
   // too few large tiles to fill the chip: a residual update splits K over workgroups (partials in P,
   // added to C in split order); other epilogues use small tiles
   if (epi == 1 && P && N % 4 == 0) {
-    const int nk = (K + BK - 1) / BK;
-    int ks = std::min(std::max(1, 256 / big), std::max(1, nk / 4));
-    while (ks > 1 && (size_t)ks * M * N > p_floats) --ks;
+    const int ks = splitk_parts(M, K, N, big, p_floats);
     if (ks > 1) {
       launch_gemm<128, 128>(3, Ahi, Alo, lda, M, K, W, N, P, N, Hhi, Hlo, ldh, ks, s);
-      const int n4 = (M * N + 3) / 4;
-      hipLaunchKernelGGL(pf_splitk_add_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, P, ks, M, N, C, ldc);
+      hipLaunchKernelGGL(pf_splitk_add_kernel, dim3(M), dim3(256), 0, s, P, ks, M, N, C, ldc, nullptr, 0.f, nullptr,
+                         nullptr, 0);
       return MK_LAUNCH_OK();
     }
   }
   return launch_gemm<64, 64>(epi, Ahi, Alo, lda, M, K, W, N, C, ldc, Hhi, Hlo, ldh, 1, s);
+}
+
+extern "C" int mk_pf_gemm_res(const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W,
+                              int N, float* C, int ldc, float* P, size_t p_floats, const uint16_t* g, float eps,
+                              uint16_t* Nhi, uint16_t* Nlo, int ldn, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int big = ((M + 127) / 128) * ((N + 127) / 128);
+  const int ks = (big < 200 && P && N % 4 == 0) ? splitk_parts(M, K, N, big, p_floats) : 1;
+  if (ks > 1) {
+    launch_gemm<128, 128>(3, Ahi, Alo, lda, M, K, W, N, P, N, nullptr, nullptr, 0, ks, s);
+    hipLaunchKernelGGL(pf_splitk_add_kernel, dim3(M), dim3(256), 0, s, P, ks, M, N, C, ldc, g, eps, Nhi, Nlo, ldn);
+    return MK_LAUNCH_OK();
+  }
+  int rc = mk_pf_gemm(1, Ahi, Alo, lda, M, K, W, N, C, ldc, nullptr, nullptr, 0, nullptr, 0, stream);
+  if (g) rc |= mk_pf_rms_split(C, M, N, g, eps, Nhi, Nlo, ldn, stream);
+  return rc;
 }
 
 extern "C" int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB,
