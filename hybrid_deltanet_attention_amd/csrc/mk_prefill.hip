@@ -109,13 +109,15 @@ __global__ void __launch_bounds__(256) pf_rms_split_kernel(const float* __restri
 // to C in split order, so the result does not depend on timing).
 //
 // A workgroup (4 waves, 2 x 2) computes a BM x BN tile; each wave a (BM/2) x (BN/2) block of 32 x 32
-// MFMA tiles.  K advances in chunks of 32 through a ring of STAGES LDS buffers filled with LDS-DMA
-// (a wave copy is 16 rows x 64 bytes); a wave waits only for its own copies of the chunk it is about
+// MFMA tiles.  K advances in chunks of 64 through a ring of STAGES LDS buffers filled with LDS-DMA
+// (a wave copy is 8 rows x 128 bytes); a wave waits only for its own copies of the chunk it is about
 // to use, and the barriers order LDS only, so later chunks stay in flight.
-constexpr int BK = 32;
-// LDS ring depth: six 24 KB stages for 128 x 128 tiles (one workgroup per CU), four for 64 x 64
+constexpr int BK = 64;
+// LDS ring depth: two stages (one chunk loads while the other is used).  Deeper rings measured no
+// faster: 64-wide chunks already halve the barriers per product, and two 32 KB stages of a 64 x 128
+// tile leave room for two workgroups per CU
 template <int BM>
-constexpr int gemm_stages() { return BM >= 128 ? 6 : 4; }
+constexpr int gemm_stages() { return 2; }
 
 __device__ __forceinline__ void lds_bar() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -146,7 +148,7 @@ __device__ __forceinline__ void wait_vm_n(int n) {
 // for 64 x 128) where each still gets whole 32 x 32 blocks and the tile's copies split evenly,
 // else 2 x 2.  More waves per CU hide the LDS-read and barrier latency of the others.
 template <int BM, int BN>
-constexpr bool gemm_eight() { return (BM >= 128 || BN >= 128) && ((2 * (BM / 16) + BN / 16) % 8) == 0; }
+constexpr bool gemm_eight() { return (BM >= 128 || BN >= 128) && ((2 * (BM / 8) + BN / 8) % 8) == 0; }
 template <int BM, int BN>
 constexpr int gemm_wr() { return gemm_eight<BM, BN>() ? (BM >= 128 ? 4 : 2) : 2; }
 template <int BM, int BN>
@@ -161,12 +163,12 @@ __global__ void __launch_bounds__((gemm_threads<BM, BN>())) pf_gemm_kernel(
     uint16_t* __restrict__ Hlo, int ldh, int ksplit) {
   constexpr int WR = gemm_wr<BM, BN>(), WC = gemm_wc<BM, BN>(), NWV = WR * WC;
   constexpr int TI = BM / (32 * WR), TJ = BN / (32 * WC);  // 32 x 32 tiles per wave in each direction
-  constexpr int AC = BM / 16, BC = BN / 16;                // 1 KB copies per tile per chunk
+  constexpr int AC = BM / 8, BC = BN / 8;                // 1 KB copies per tile per chunk
   constexpr int CPW = (2 * AC + BC) / NWV;                 // copies per wave per chunk
   static_assert(TI >= 1 && TJ >= 1 && CPW * NWV == 2 * AC + BC, "tile does not split over the waves");
   constexpr int SB = (2 * BM + BN) * BK * 2;           // bytes per stage
   constexpr int STAGES = gemm_stages<BM>();
-  static_assert(BK == 32, "the LDS chunk swizzle assumes four 16-byte k-chunks per row");
+  static_assert(BK == 64, "the LDS chunk swizzle assumes eight 16-byte k-chunks per row");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int mb = (M + BM - 1) / BM, nb = (N + BN - 1) / BN;
   const int items = mb * nb * ksplit, per = (items + 7) / 8;
@@ -180,7 +182,7 @@ __global__ void __launch_bounds__((gemm_threads<BM, BN>())) pf_gemm_kernel(
   const int wr = wv / WC, wc = wv % WC;  // this wave's (BM / WR) x (BN / WC) block
   const int nk = (K + BK - 1) / BK, kper = (nk + ksplit - 1) / ksplit;
   const int cbeg = split * kper, nchunk = max(0, min(nk, cbeg + kper) - cbeg);
-  // Copy q (0 .. 2AC + BC) of a chunk: tile part (A hi, A lo, B) and 16-row group; wave wv issues
+  // Copy q (0 .. 2AC + BC) of a chunk: tile part (A hi, A lo, B) and 8-row group; wave wv issues
   // copies wv * CPW .. + CPW.  Rows past M / N read the last row instead (their results are never
   // stored), so every copy has live lanes and each wave issues exactly CPW copies per chunk -- the
   // waits below count on that.  Columns past K are left out; a chunk that has them was zeroed by the
@@ -194,10 +196,10 @@ __global__ void __launch_bounds__((gemm_threads<BM, BN>())) pf_gemm_kernel(
       const int q = wv * CPW + i;
       const int part = q < AC ? 0 : (q < 2 * AC ? 1 : 2);
       const int grp = part == 0 ? q : (part == 1 ? q - AC : q - 2 * AC);
-      const int r = grp * 16 + (l >> 2);
-      // lane l fills LDS position (row r, 16-byte slot l & 3) with the row's k-chunk
-      // (l & 3) ^ ((r >> 2) & 3): sixteen consecutive rows then spread one chunk over all banks
-      const int k = k0 + (((l & 3) ^ ((r >> 2) & 3)) * 8);
+      const int r = grp * 8 + (l >> 3);
+      // lane l fills LDS position (row r, 16-byte slot l & 7) with the row's k-chunk
+      // (l & 7) ^ (r & 7): eight consecutive rows then spread one chunk over all banks
+      const int k = k0 + (((l & 7) ^ (r & 7)) * 8);
       const uint16_t* src;
       if (part < 2) src = (part == 0 ? Ahi : Alo) + (size_t)min(m0 + r, M - 1) * lda + k;
       else src = W + (size_t)min(n0 + r, N - 1) * K + k;
@@ -240,14 +242,14 @@ __global__ void __launch_bounds__((gemm_threads<BM, BN>())) pf_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const int r = wr * (BM / WR) + i * 32 + (l & 31);
-        const int kb = (kc ^ ((r >> 2) & 3)) * 16;
+        const int kb = (kc ^ (r & 7)) * 16;
         fh[i] = *(const bf16x8*)(sah + r * (BK * 2) + kb);
         fl[i] = *(const bf16x8*)(sal + r * (BK * 2) + kb);
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int r = wc * (BN / WC) + j * 32 + (l & 31);
-        fb[j] = *(const bf16x8*)(sb + r * (BK * 2) + (kc ^ ((r >> 2) & 3)) * 16);
+        fb[j] = *(const bf16x8*)(sb + r * (BK * 2) + (kc ^ (r & 7)) * 16);
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i)
@@ -285,7 +287,6 @@ __global__ void __launch_bounds__((gemm_threads<BM, BN>())) pf_gemm_kernel(
       }
 }
 
-// C[r][c] += sum over splits s (in order) of P[s][r][c]
 // One workgroup per row r: C[r] += the ksplit partials, added in split order.  With a gain g the
 // updated row is then RMS-normalised (eps, gain after normalising) into the split-bf16 operand
 // (Ahi, Alo) of the next projection, so the residual add and the next block's norm share one pass.
