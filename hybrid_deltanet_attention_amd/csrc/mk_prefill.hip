@@ -538,6 +538,28 @@ __device__ __forceinline__ f32x4 mfma_rows(const float* arow, const float* brow,
   }
   return acc[0] + acc[1];
 }
+// 16 x 16 blocks in LDS (row strides lda, ldb) on one wave: c + A B, with lane (lr = lane % 16,
+// lk = lane / 16) holding rows 4 lk .. 4 lk + 3 of column lr of the result (the MFMA's output
+// layout); the s-th MFMA takes k = 4 s + lk from every lane
+__device__ __forceinline__ f32x4 mm16(const float* A, int lda, const float* B, int ldb, f32x4 c) {
+  const int lr = threadIdx.x & 15, lk = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = mfma4(A[lr * lda + 4 * s + lk], B[(4 * s + lk) * ldb + lr], c);
+  return c;
+}
+// store / load a block in that layout (stores scaled by f)
+__device__ __forceinline__ void put16(float* D, int ld, f32x4 v, float f) {
+  const int lr = threadIdx.x & 15, lk = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) D[(4 * lk + r) * ld + lr] = f * v[r];
+}
+__device__ __forceinline__ f32x4 get16(const float* D, int ld) {
+  const int lr = threadIdx.x & 15, lk = (threadIdx.x & 63) >> 4;
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = D[(4 * lk + r) * ld + lr];
+  return v;
+}
 // Per (chunk c, head h): W = (I + M)^{-1} diag(beta) and Bt = lower(Q K^T o G) incl. the diagonal
 // (both [t][j]), gam_t = gamma_t, dlt_t = gamma_last / gamma_t, gamma_last.  Tokens past the end of
 // the prompt have k = q = 0 and beta = 0, so their rows and columns come out zero.
@@ -548,7 +570,6 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
   __shared__ __attribute__((aligned(16))) float sq[PC][DKM + 4];
   __shared__ float sm[PC][PC + 1];  // M, strictly lower
   __shared__ float sx[PC][PC + 1];  // (I + M)^{-1}
-  __shared__ float st[3][16][17];   // block-row partial sums
   __shared__ float sg[PC], sbeta[PC];
   const int h = blockIdx.x % H, c = blockIdx.x / H;
   const int t0 = c * PC, Cn = min(PC, T - t0);
@@ -643,43 +664,48 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
     if (tid == 0) gDlt[PC] = expf(last);
   }
   __syncthreads();
-  // W = (I + M)^{-1} diag(beta), M strictly lower.  X = (I + M)^{-1} by blocks of 16: the four
-  // diagonal blocks by forward substitution (one wave each, a lane per column), then block row by
-  // block row X_ij = -X_ii sum_{j <= m < i} M_im X_mj.
-  if (lane64 < 16) {
-    const int o = 16 * wv, j = lane64;
-    float x[16];
+  // W = (I + M)^{-1} diag(beta), M strictly lower.  X = (I + M)^{-1} by blocks of 16 on the matrix
+  // cores.  Diagonal block N = M_ii (nilpotent, N^16 = 0), one wave each:
+  //   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
+  // (the factors are polynomials in N, so they commute).  Then block row by block row
+  //   X_ij = -X_ii T_ij,  T_ij = sum_{j <= m < i} M_im X_mj,  one wave per j.
+  // The waves' 16 x 16 scratch blocks reuse the query tile, which is no longer read.
+  float* scr = &sq[0][0] + wv * 3 * 256;
+  {
+    float* X = scr;           // running product
+    float* Pw = scr + 256;    // N^(2^p)
+    const float* Nb = &sm[16 * wv][16 * wv];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float v = t == j ? 1.f : 0.f;
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane64 + 64 * q, rr = e >> 4, cc = e & 15;
+      X[e] = (rr == cc ? 1.f : 0.f) - Nb[rr * (PC + 1) + cc];
+    }
+    const float* A = Nb;
+    int ld = PC + 1;
 #pragma unroll
-      for (int m = 0; m < t; ++m) v = fmaf(-sm[o + t][o + m], x[m], v);  // x[m] = 0 for m < j
-      x[t] = t < j ? 0.f : v;
+    for (int p = 0; p < 3; ++p) {
+      const f32x4 sq2 = mm16(A, ld, A, ld, f32x4{0.f, 0.f, 0.f, 0.f});  // N^(2^(p+1))
+      put16(Pw, 16, sq2, 1.f);
+      A = Pw;
+      ld = 16;
+      put16(X, 16, mm16(X, 16, Pw, 16, get16(X, 16)), 1.f);  // X (I + N^(2^(p+1)))
     }
 #pragma unroll
-    for (int t = 0; t < 16; ++t) sx[o + t][o + j] = x[t];
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane64 + 64 * q, rr = e >> 4, cc = e & 15;
+      sx[16 * wv + rr][16 * wv + cc] = X[e];
+    }
   }
   __syncthreads();
-  {
-    const int r = tid >> 4, cc = tid & 15;
-    for (int i = 1; i < 4; ++i) {
-      // T_j = sum_{j <= m < i} M_im X_mj for every j < i
-      for (int j = 0; j < i; ++j) {
-        float v = 0.f;
-        for (int m = j; m < i; ++m)
-#pragma unroll
-          for (int s2 = 0; s2 < 16; ++s2) v = fmaf(sm[16 * i + r][16 * m + s2], sx[16 * m + s2][16 * j + cc], v);
-        st[j][r][cc] = v;
-      }
-      __syncthreads();
-      for (int j = 0; j < i; ++j) {
-        float v = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) v = fmaf(sx[16 * i + r][16 * i + s2], st[j][s2][cc], v);
-        sx[16 * i + r][16 * j + cc] = -v;
-      }
-      __syncthreads();
+  for (int i = 1; i < 4; ++i) {
+    const int j = wv;
+    if (j < i) {
+      f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = j; m < i; ++m) t4 = mm16(&sm[16 * i][16 * m], PC + 1, &sx[16 * m][16 * j], PC + 1, t4);
+      put16(scr, 16, t4, 1.f);
+      put16(&sx[16 * i][16 * j], PC + 1, mm16(&sx[16 * i][16 * i], PC + 1, scr, 16, f32x4{0.f, 0.f, 0.f, 0.f}), -1.f);
     }
+    __syncthreads();
   }
   for (int f = tid; f < PC * PC; f += 256) {
     const int t = f / PC, j = f - t * PC;
