@@ -207,7 +207,7 @@ Layout make_layout(const mk_config& c) {
     const int64_t natt = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
     L.pf_T = (int)T;
     L.pf_lda = (int)((kmax + 7) / 8 * 8);
-    L.pf_ldy = (int)std::max(ndn, natt);
+    L.pf_ldy = (int)((std::max(ndn, natt) + 3) / 4 * 4);  // rows 16-byte aligned
     L.pf_x = take((size_t)T * D * 4);
     L.pf_ahi = take((size_t)T * L.pf_lda * 2);
     L.pf_alo = take((size_t)T * L.pf_lda * 2);
@@ -929,8 +929,7 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
         rc |= mk_pf_att_rope(Y, ldy, T, p0, nq, nkv, hd, c.max_ctx, rcos, rsin, Q, Kc, Vc, st);
         rc |= mk_pf_attention(Q, Kc, Vc, T, p0, nq, nkv, hd, c.max_ctx, Ahi, Alo, lda, PK, PKN, st);
       } else {
-        rc |= mk_pf_dn_prep(Y, ldy, T, H, dk, dv, c.l2_eps, QK, AB, st);
-        rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, Ahi, Alo, lda,
+        rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, c.l2_eps, Ahi, Alo, lda,
                             (float*)(ws + L.pf_ch), st);
       }
       rc |= mk_pf_gemm_res(Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, PK, PKN, g12 + D, c.rms_eps, Ahi, Alo,

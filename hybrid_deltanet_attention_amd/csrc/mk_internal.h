@@ -136,8 +136,9 @@ int mk_pf_gemm(int epi, const uint16_t* Ahi, const uint16_t* Alo, int lda, int M
 int mk_pf_gemm_res(const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int K, const uint16_t* W, int N,
                    float* C, int ldc, float* P, size_t p_floats, const uint16_t* g, float eps, uint16_t* Nhi,
                    uint16_t* Nlo, int ldn, void* stream);
-int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB, void* stream);
-int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk, int dv,
+// DeltaNet mixer over T prompt tokens from the in-projection Y: normalised q, k (QK) and gates
+// (AB, wide keys only) are produced on the way
+int mk_pf_dn_scan(float* S, float* QK, float* AB, const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps,
                   uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream);
 int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, int max_ctx, const float* rcos,
                    const float* rsin, float* Q, float* Kc, float* Vc, void* stream);

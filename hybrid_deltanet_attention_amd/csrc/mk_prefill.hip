@@ -560,12 +560,14 @@ __device__ __forceinline__ f32x4 get16(const float* D, int ld) {
   for (int r = 0; r < 4; ++r) v[r] = D[(4 * lk + r) * ld + lr];
   return v;
 }
-// Per (chunk c, head h): W = (I + M)^{-1} diag(beta) and Bt = lower(Q K^T o G) incl. the diagonal
-// (both [t][j]), gam_t = gamma_t, dlt_t = gamma_last / gamma_t, gamma_last.  Tokens past the end of
-// the prompt have k = q = 0 and beta = 0, so their rows and columns come out zero.
+// Per (chunk c, head h): the chunk's L2-normalised q and k (written to QK for the state pass), then
+// W = (I + M)^{-1} diag(beta) and Bt = lower(Q K^T o G) incl. the diagonal (both [t][j]),
+// gam_t = gamma_t, dlt_t = gamma_last / gamma_t, gamma_last.  Tokens past the end of the prompt
+// have k = q = 0 and beta = 0, so their rows and columns come out zero.
 template <int DKM>
-__global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restrict__ QK, const float* __restrict__ AB,
-                                                          int T, int H, int dk, float* __restrict__ CH) {
+__global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restrict__ Y, int ldy, int T, int H, int dk,
+                                                          int dv, float l2eps, float* __restrict__ QK,
+                                                          float* __restrict__ CH) {
   __shared__ __attribute__((aligned(16))) float sk[PC][DKM + 4];
   __shared__ __attribute__((aligned(16))) float sq[PC][DKM + 4];
   __shared__ float sm[PC][PC + 1];  // M, strictly lower
@@ -592,9 +594,9 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
       rq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
       rk[x] = rq[x];
       if (t < Cn) {
-        const float* src = QK + ((size_t)(t0 + t) * H + h) * 2 * dk;
+        const float* src = Y + (size_t)(t0 + t) * ldy + h * dk;
         rq[x] = *(const f32x4*)(src + e);
-        rk[x] = *(const f32x4*)(src + dk + e);
+        rk[x] = *(const f32x4*)(src + H * dk + e);
       }
     }
 #pragma unroll
@@ -606,11 +608,30 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
       }
     }
   }
-  if (tid < PC) {
+  if (tid < PC) {  // log alpha = -softplus(a), beta = sigmoid(b)
     const bool in = tid < Cn;
-    const float* ab = AB + ((size_t)(t0 + (in ? tid : 0)) * H + h) * 2;
-    sg[tid] = in ? ab[0] : 0.f;
-    sbeta[tid] = in ? ab[1] : 0.f;
+    const float* ab = Y + (size_t)(t0 + (in ? tid : 0)) * ldy + 2 * H * dk + H * dv + h;
+    sg[tid] = in ? -softplusf_(ab[0]) : 0.f;
+    sbeta[tid] = in ? sigmoidf_(ab[H]) : 0.f;
+  }
+  __syncthreads();
+  {
+    // L2 normalisation: two lanes per (token, q or k) row, each summing every other 4-element group
+    const int row = tid >> 1, t = row >> 1, half = tid & 1;
+    float* v = (row & 1) ? &sk[t][0] : &sq[t][0];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 4 * half; e < DKM; e += 8) ss = dot4(*(const f32x4*)(v + e), *(const f32x4*)(v + e), ss);
+    ss += __shfl_xor(ss, 1);
+    const float rn = 1.0f / sqrtf(ss + l2eps);
+    float* o = QK + ((size_t)(t0 + t) * H + h) * 2 * dk + ((row & 1) ? dk : 0);
+#pragma unroll
+    for (int e = 4 * half; e < DKM; e += 8) {
+      const f32x4 a = *(const f32x4*)(v + e);
+      const f32x4 b = f32x4{a.x * rn, a.y * rn, a.z * rn, a.w * rn};
+      *(f32x4*)(v + e) = b;
+      if (t < Cn && e < dk) *(f32x4*)(o + e) = b;
+    }
   }
   __syncthreads();
   if (tid == 0) {  // cumulative log alpha, inclusive
@@ -1553,31 +1574,27 @@ extern "C" int mk_pf_gemm_res(const uint16_t* Ahi, const uint16_t* Alo, int lda,
   return rc;
 }
 
-extern "C" int mk_pf_dn_prep(const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps, float* QK, float* AB,
-                             void* stream) {
-  hipLaunchKernelGGL(pf_dn_prep_kernel, dim3(T * H), dim3(64), 0, (hipStream_t)stream, Y, ldy, H, dk, dv, l2eps, QK, AB);
-  return MK_LAUNCH_OK();
-}
-
-extern "C" int mk_pf_dn_scan(float* S, const float* QK, const float* AB, const float* Y, int ldy, int T, int H, int dk,
-                             int dv, uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream) {
+extern "C" int mk_pf_dn_scan(float* S, float* QK, float* AB, const float* Y, int ldy, int T, int H, int dk, int dv,
+                             float l2eps, uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (dk <= 128) {
     // chunked form: all chunks' W, Bt and decays in parallel, then the state pass
     const int nc = (T + PC - 1) / PC;
     const dim3 g1(nc * H), g2(H * ((dv + CM_RW - 1) / CM_RW));
     if (dk <= 64) {
-      hipLaunchKernelGGL(pf_dn_cprep_kernel<64>, g1, dim3(256), 0, s, QK, AB, T, H, dk, CH);
+      hipLaunchKernelGGL(pf_dn_cprep_kernel<64>, g1, dim3(256), 0, s, Y, ldy, T, H, dk, dv, l2eps, QK, CH);
       hipLaunchKernelGGL(pf_dn_cscan_mfma_kernel<64>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo,
                          ldo);
     } else {
-      hipLaunchKernelGGL(pf_dn_cprep_kernel<128>, g1, dim3(256), 0, s, QK, AB, T, H, dk, CH);
+      hipLaunchKernelGGL(pf_dn_cprep_kernel<128>, g1, dim3(256), 0, s, Y, ldy, T, H, dk, dv, l2eps, QK, CH);
       hipLaunchKernelGGL(pf_dn_cscan_mfma_kernel<128>, g2, dim3(CS_NT), 0, s, S, QK, CH, Y, ldy, T, H, dk, dv, Ohi, Olo,
                          ldo);
     }
     return MK_LAUNCH_OK();
   }
-  // wider keys: the token-by-token row-parallel recurrence
+  // wider keys: normalised q, k and the gates per token, then the token-by-token row-parallel
+  // recurrence
+  hipLaunchKernelGGL(pf_dn_prep_kernel, dim3(T * H), dim3(64), 0, s, Y, ldy, H, dk, dv, l2eps, QK, AB);
   const dim3 grid(H * ((dv + 7) / 8));
   hipLaunchKernelGGL(pf_dn_scan_kernel<8>, grid, dim3(256), 0, s, S, QK, AB, Y, ldy, T, H, dk, dv, Ohi, Olo, ldo);
   return MK_LAUNCH_OK();

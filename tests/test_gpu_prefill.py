@@ -3,8 +3,9 @@
 Prefill leaves the DeltaNet state and the KV cache exactly where token-by-token decode would, and
 returns the last position's logits and greedy token.  Cases: a prompt alone (state and cache
 checked right after prefill), a prompt longer than one prefill chunk (1024 tokens), a prefill that
-continues a context built by an earlier prefill and decode steps, and a head grouping the prefill
-attention tiling does not cover (handled token by token).  Bars as in test_gpu_parity.
+continues a context built by an earlier prefill and decode steps, a head grouping the prefill
+attention tiling does not cover (handled token by token), and DeltaNet key widths that do not fill
+the chunk kernels' tiles or exceed them.  Bars as in test_gpu_parity.
 """
 import numpy as np
 import pytest
@@ -122,4 +123,23 @@ def test_prefill_head_grouping_outside_the_tiling():
     lg, nxt = _prefill(m, prompt)
     assert rel_l2(lg, fwd["logits"]) <= LOGIT_TOL
     _check_state(m, cfg, fwd, 12)
+    m.close()
+
+
+@pytest.mark.parametrize("heads,dk,dv", [(3, 48, 40), (2, 96, 64), (2, 192, 64)])
+def test_prefill_key_widths(heads, dk, dv):
+    # keys narrower than the chunk kernels' 64 / 128-wide tiles (zero-padded columns), and keys wider
+    # than 128 (token-by-token recurrence with its own normalisation pass); 100 tokens = one whole
+    # chunk and a ragged one
+    cfg = synth.get_config("tiny", dn_heads=heads, dn_dk=dk, dn_dv=dv)
+    W = synth.make_weights(cfg, 7)
+    prompt = synth.make_prompt(cfg.vocab, 100, 7)
+    fwd = Oracle(cfg, W).forward(prompt, logits="last")
+    m = new_model(cfg, W)
+    lg, nxt = _prefill(m, prompt)
+    e = rel_l2(lg, fwd["logits"])
+    print(f"[dn heads {heads} dk {dk} dv {dv}] logits rel-L2 {e:.2e}", flush=True)
+    assert e <= LOGIT_TOL
+    assert nxt == int(np.argmax(lg))
+    _check_state(m, cfg, fwd, 100)
     m.close()
