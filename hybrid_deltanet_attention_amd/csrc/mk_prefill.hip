@@ -560,7 +560,8 @@ __device__ __forceinline__ f32x4 get16(const float* D, int ld) {
   for (int r = 0; r < 4; ++r) v[r] = D[(4 * lk + r) * ld + lr];
   return v;
 }
-// Per (chunk c, head h): the chunk's L2-normalised q and k (written to QK for the state pass), then
+// Per (chunk c, head h): the chunk's L2-normalised q and k (written to QK for the state pass, head
+// major: QK[h][t][q | k], so a head's chunk is one contiguous 64 KB block), then
 // W = (I + M)^{-1} diag(beta) and Bt = lower(Q K^T o G) incl. the diagonal (both [t][j]),
 // gam_t = gamma_t, dlt_t = gamma_last / gamma_t, gamma_last.  Tokens past the end of the prompt
 // have k = q = 0 and beta = 0, so their rows and columns come out zero.
@@ -624,7 +625,7 @@ __global__ void __launch_bounds__(256) pf_dn_cprep_kernel(const float* __restric
     for (int e = 4 * half; e < DKM; e += 8) ss = dot4(*(const f32x4*)(v + e), *(const f32x4*)(v + e), ss);
     ss += __shfl_xor(ss, 1);
     const float rn = 1.0f / sqrtf(ss + l2eps);
-    float* o = QK + ((size_t)(t0 + t) * H + h) * 2 * dk + ((row & 1) ? dk : 0);
+    float* o = QK + ((size_t)h * T + t0 + t) * 2 * dk + ((row & 1) ? dk : 0);
 #pragma unroll
     for (int e = 4 * half; e < DKM; e += 8) {
       const f32x4 a = *(const f32x4*)(v + e);
@@ -810,7 +811,7 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
       rq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
       rk[x] = rq[x];
       if (tt < Cn) {
-        const float* src = QK + ((size_t)(t0 + tt) * H + h) * 2 * dk;
+        const float* src = QK + ((size_t)h * T + t0 + tt) * 2 * dk;
         rq[x] = *(const f32x4*)(src + e);
         rk[x] = *(const f32x4*)(src + dk + e);
       }
