@@ -37,7 +37,8 @@ KERNEL = "mk_decode_kernel"
 # measured HBM traffic of the decode kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE), valid only for the
 # kernel source it was measured on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_0p8b_traffic.json")
-KERNEL_SOURCES = ["hybrid_deltanet_attention_amd/csrc/mk_decode.hip", "hybrid_deltanet_attention_amd/csrc/mk_internal.h"]
+KERNEL_SOURCES = ["hybrid_deltanet_attention_amd/csrc/mk_decode.hip", "hybrid_deltanet_attention_amd/csrc/mk_device.h",
+                  "hybrid_deltanet_attention_amd/csrc/mk_internal.h"]
 COPY_BYTES = 1 << 30
 
 
