@@ -788,7 +788,10 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
   const int off_v = 2 * H * dk + h * dv + r0;
   const int nc = (T + PC - 1) / PC;
   // a chunk's operands are loaded into registers two chunks ahead (two register sets, used in
-  // turn; the chunk index is clamped so every set is always loaded and the load counts stay uniform)
+  // turn; the chunk index is clamped so every set is always loaded and the load counts stay uniform).
+  // Every load is unconditional -- rows past the chunk and rows past dv read a valid row and are
+  // zeroed when stashed: a register whose load sits behind a branch cannot be placed in the in-order
+  // load count, and the wait before its use then also drains the loads of the later chunks.
   constexpr int NL = PC * DKM / 4 / CS_NT, NM = PC * PC / 4 / CS_NT, NV = PC * RW / CS_NT;
   struct Ops {
     f32x4 rq[NL], rk[NL], rw[NM], rb[NM];
@@ -807,14 +810,10 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
     const float* blk = CH + ((size_t)c * H + h) * PC_BLK;
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
-      const int f = tid + CS_NT * x, tt = f / n4, e = (f - tt * n4) * 4;
-      rq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-      rk[x] = rq[x];
-      if (tt < Cn) {
-        const float* src = QK + ((size_t)h * T + t0 + tt) * 2 * dk;
-        rq[x] = *(const f32x4*)(src + e);
-        rk[x] = *(const f32x4*)(src + dk + e);
-      }
+      const int f = tid + CS_NT * x, tt = min(f / n4, Cn - 1), e = (f - (f / n4) * n4) * 4;
+      const float* src = QK + ((size_t)h * T + t0 + tt) * 2 * dk;
+      rq[x] = *(const f32x4*)(src + e);
+      rk[x] = *(const f32x4*)(src + dk + e);
     }
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
@@ -822,14 +821,14 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
       rw[x] = *(const f32x4*)(blk + 4 * f);
       rb[x] = *(const f32x4*)(blk + PC * PC + 4 * f);
     }
-    rg = tid <= 2 * PC ? blk[2 * PC * PC + tid] : 0.f;  // gam [0, PC), dlt [PC, 2 PC], gamma_C last
+    rg = blk[2 * PC * PC + min(tid, 2 * PC)];  // gam [0, PC), dlt [PC, 2 PC], gamma_C last
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
-      const int f = tid + CS_NT * x, tt = f / RW, i = f - tt * RW;
-      rv[x] = (tt < Cn && r0 + i < dv) ? Y[(size_t)(t0 + tt) * ldy + off_v + i] : 0.f;
+      const int f = tid + CS_NT * x, tt = min(f / RW, Cn - 1), i = min(f - (f / RW) * RW, dv - 1 - r0);
+      rv[x] = Y[(size_t)(t0 + tt) * ldy + off_v + i];
     }
   };
-  auto stash = [&](const Ops& o) {
+  auto stash = [&](const Ops& o, int Cn) {
     const f32x4(&rq)[NL] = o.rq;
     const f32x4(&rk)[NL] = o.rk;
     const f32x4(&rw)[NM] = o.rw;
@@ -839,9 +838,10 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
       const int f = tid + CS_NT * x, tt = f / n4, e = (f - tt * n4) * 4;
+      const bool in = tt < Cn;
       if (tt < PC) {
-        *(f32x4*)&sq[tt][e] = rq[x];
-        *(f32x4*)&sk[tt][e] = rk[x];
+        *(f32x4*)&sq[tt][e] = in ? rq[x] : f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)&sk[tt][e] = in ? rk[x] : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
@@ -855,7 +855,7 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
       const int f = tid + CS_NT * x, tt = f / RW, i = f - tt * RW;
-      sv[tt][i] = rv[x];
+      sv[tt][i] = (tt < Cn && r0 + i < dv) ? rv[x] : 0.f;
     }
   };
   const int nb = wv & 3, tok = 16 * nb + lr;  // this wave's 16-token block, this lane's token
@@ -863,7 +863,7 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
   fetch(ob, 1);
   auto chunk = [&](int c, Ops& o) {
     const int t0 = c * PC, Cn = min(PC, T - t0);
-    stash(o);
+    stash(o, Cn);
     __syncthreads();
     fetch(o, c + 2);
     // Z^T (waves 0-3) or P^T (waves 4-7) for tokens 16 nb ..: lane holds rows 4 lk + r, token tok
