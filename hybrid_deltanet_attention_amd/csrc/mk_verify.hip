@@ -1,8 +1,9 @@
 // Speculative verify of the hybrid decoder as ONE persistent kernel launch on gfx950: the pending
 // token and up to five drafted tokens are scored in a single pass (Reddit follow-up on the 27B
-// model, speculative-decoding paragraph: several drafts checked per pass for about the cost of one,
-// the main model's greedy output kept exactly; news-aggregator page: whole speculative-decoding
-// cycles fused into one launch).
+// model, "Speed" and speculative-decoding paragraphs: the speed-up comes from scoring a batch of
+// drafts in one pass whose cost stays close to that of a single token, and the output equals the
+// main model's greedy choices; news-aggregator page: the whole draft-and-check cycle runs fused
+// in one launch).
 //
 // The launch runs the decode kernel's per-position arithmetic on nt = k + 1 positions at once:
 //  - every GEMV streams each weight row from HBM once and applies it to all nt activation vectors;

@@ -53,7 +53,9 @@ enum mk_status {
  * r*K/2 + 4i, column 8i+2j in the nibble at bit 4j and column 8i+2j+1 in the nibble at bit 16+4j
  * (j = 0..3) -- then one 4-byte word per (row, group of 32 columns), row-major: the IEEE binary16
  * scale d in the low half, the binary16 offset m in the high half.  The weight is d*q + m for its
- * 4-bit code q.  The mk_tensor shape is the logical [R, K]. */
+ * 4-bit code q.  The mk_tensor shape is the logical [R, K].
+ * Values: MK_I32 (4) names int32 data such as token ids, so the 4-bit format takes the next free
+ * value, 5; the numbers are part of the ABI and never change. */
 enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4, MK_Q4G32 = 5 };
 
 /* Model shape.  All fields are required (there is no default constructor on purpose).
@@ -108,7 +110,9 @@ size_t mk_workspace_bytes(const mk_config* cfg);
 int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t workspace_bytes,
               void* hip_stream, mk_ctx** out);
 
-/* Copy all model tensors into the workspace in the kernel's layout.  Every manifest name must
+/* Copy all model tensors into the workspace in the kernel's layout.  The follow-up post on the
+ * 27B megakernel (page 3, "Since the first post" paragraph) has its loader check every tensor's
+ * type and its server warm up before taking requests; this call does both.  Every manifest name must
  * appear exactly once with the manifest shape and dtype: MK_BF16 for everything, or, when the
  * config's weight_dtype is MK_Q4G32, MK_Q4G32 for the matrices (embed and every l{l}.* weight
  * matrix) and MK_BF16 for the norm gains; the whole list is checked
@@ -119,7 +123,11 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* tensors, int32_t n);
 /* Same checks as mk_load_weights, for a configuration alone; needs no device or context. */
 int mk_check_tensors(const mk_config* cfg, const mk_tensor* tensors, int32_t n);
 
-/* Process n prompt tokens d_tokens[0..n) starting at the current position; writes the greedy
+/* Prefill: the prompt-processing side of the luce-megakernel announcement's results table (page 1,
+ * the pp520 column: a 520-token prompt processed at once).  Runs the prompt through the same model
+ * with multi-token kernels (matrix-core GEMMs, the DeltaNet recurrence in chunked form, causal
+ * attention) and leaves the DeltaNet states and KV cache exactly where token-by-token decode would.
+ * Process n prompt tokens d_tokens[0..n) starting at the current position; writes the greedy
  * next token (argmax of the last position's logits, lowest index on ties) to d_next[0] and, if
  * d_logits != NULL, that position's logits [vocab] as FP32.  Advances the position by n.
  * Errors: MK_E_ORDER (no weights), MK_E_INVALID (n <= 0 or null pointers), MK_E_CTX_FULL. */

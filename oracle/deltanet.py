@@ -89,9 +89,11 @@ def delta_parallel(S0, Q, K, V, alpha, beta):
     """Whole-sequence form for one head: S0 [dv, dk], Q/K [T, dk], V [T, dv], alpha/beta [T]."""
     T = K.shape[0]
     g = np.cumsum(np.log(alpha))                 # log gamma_t
-    G = np.exp(g[:, None] - g[None, :])          # gamma_t / gamma_j (only the lower triangle is used)
     lower = np.tril(np.ones((T, T), dtype=bool))
     strict = np.tril(np.ones((T, T), dtype=bool), -1)
+    # gamma_t / gamma_j for j <= t; the upper triangle is masked to exp(-inf) = 0 before
+    # exponentiating, so its positive log differences never overflow
+    G = np.exp(np.where(lower, g[:, None] - g[None, :], -np.inf))
     gamma = np.exp(g)
     KK = np.where(strict, (K @ K.T) * G, 0.0)
     M = np.eye(T, dtype=K.dtype) + beta[:, None] * KK

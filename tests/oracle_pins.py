@@ -375,6 +375,95 @@ def pin_verify_k0_is_one_step():
     _check_rolled_back(o, prompt, "k = 0")
 
 
+def _micro_model(name):
+    """One of the hand-worked one-layer models of tests/golden/micro_models.json: its config and
+    its weights as BF16 bit patterns (every stored value must be exact in BF16)."""
+    with open(os.path.join(GOLDEN, "micro_models.json")) as f:
+        g = json.load(f)
+    m = g["models"][name]
+    cfg = synth.get_config("tiny").with_(name="micro", **g["config_common"], **m["config"])
+    W = {}
+    for wname, shape, _ in synth.tensor_manifest(cfg):
+        vals = np.asarray(m["weights"][wname], dtype=np.float32)
+        assert vals.shape == tuple(shape), f"{wname}: {vals.shape} vs manifest {shape}"
+        W[wname] = synth.bf16_round(vals)
+        assert np.array_equal(prim.bf16_decode(W[wname]), vals.astype(np.float64)), f"{wname} not BF16-exact"
+    return cfg, W, g["tokens"], m
+
+
+def pin_micro_model_deltanet_golden():
+    """A one-layer DeltaNet model run by hand (tests/golden/micro_models.json): logits and state
+    after each of two tokens, through both the token-by-token and the whole-sequence forms, and
+    the FFN and head stages on the hand values."""
+    cfg, W, toks, m = _micro_model("deltanet")
+    o = om.Oracle(cfg, W)
+    for t, st in zip(toks, m["steps"]):
+        _close(o.step(t), st["logits"], 1e-12, f"micro deltanet logits (token {t})")
+        _close(o.S[0][0], st["S"], 1e-12, f"micro deltanet state (token {t})")
+        _close(o._ffn(0, np.array(st["x1"])), st["x2"], 1e-12, f"micro deltanet FFN (token {t})")
+        _close(o._head(np.array(st["x2"])), st["logits"], 1e-12, f"micro deltanet head (token {t})")
+    fwd = o.forward(toks)
+    _close(fwd["logits"], [st["logits"] for st in m["steps"]], 1e-12, "micro deltanet forward logits")
+    _close(fwd["S"][0][0], m["steps"][-1]["S"], 1e-12, "micro deltanet forward state")
+
+
+def pin_micro_model_attention_golden():
+    """A one-layer attention model run by hand: logits after each of two tokens (so RoPE turns the
+    second query and key), the rotated key cache and the values, through both forms."""
+    cfg, W, toks, m = _micro_model("attention")
+    o = om.Oracle(cfg, W)
+    for t, st in zip(toks, m["steps"]):
+        _close(o.step(t), st["logits"], 1e-12, f"micro attention logits (token {t})")
+        _close(o._ffn(0, np.array(st["x1"])), st["x2"], 1e-12, f"micro attention FFN (token {t})")
+    _close(o.Kc[0][0, :2], m["kv_cache"]["K"], 1e-12, "micro attention K cache")
+    _close(o.Vc[0][0, :2], m["kv_cache"]["V"], 1e-12, "micro attention V cache")
+    fwd = o.forward(toks)
+    _close(fwd["logits"], [st["logits"] for st in m["steps"]], 1e-12, "micro attention forward logits")
+    _close(fwd["KV"][0][0][0], m["kv_cache"]["K"], 1e-12, "micro attention forward K")
+
+
+def pin_model_without_residual_writes():
+    """With every mixer output projection and every FFN down projection zero, no layer writes to
+    the residual stream, so the logits are the tied head on the normalised embedding alone:
+    logits = E (E[tok] / rms(E[tok]) * g_final), whatever the other weights.  Distinct random
+    gains make the final gain distinguishable from the layers' ones."""
+    cfg = _tiny()
+    W = synth.make_weights(cfg, 8, gain_noise=0.3)
+    for name in W:
+        if name.endswith(".wo") or name.endswith(".ffn.wd"):
+            W[name] = np.zeros_like(W[name])
+    E = prim.bf16_decode(W["embed"])
+    gf = prim.bf16_decode(W["final_norm"])
+    toks = synth.make_prompt(cfg.vocab, 5, 8)
+    o = om.Oracle(cfg, W)
+    fwd = o.forward(toks)
+    for i, t in enumerate(toks):
+        x = E[t]
+        want = E @ (x / math.sqrt(float(np.mean(x * x)) + cfg.rms_eps) * gf)
+        _close(o.step(t), want, 1e-12, f"head on the embedding (token {t})")
+        _close(fwd["logits"][i], want, 1e-12, f"forward head on the embedding (position {i})")
+
+
+def pin_ffn_linear_in_up_projection():
+    """SwiGLU multiplies silu(W_g h) by the linear W_u h, so the FFN's residual contribution is
+    linear in W_u (doubling W_u doubles it) and vanishes when W_u = 0, but not when W_g is merely
+    scaled (silu is not linear)."""
+    cfg = _tiny()
+    W = synth.make_weights(cfg, 9)
+    x = np.random.default_rng(19).standard_normal(cfg.hidden)
+    base = om.Oracle(cfg, W)._ffn(0, x) - x
+    W2 = dict(W)
+    W2["l0.ffn.wu"] = synth.bf16_round(prim.bf16_decode(W["l0.ffn.wu"]).astype(np.float32) * 2)
+    _close(om.Oracle(cfg, W2)._ffn(0, x) - x, 2 * base, 1e-12, "FFN linear in W_u")
+    W3 = dict(W)
+    W3["l0.ffn.wu"] = np.zeros_like(W["l0.ffn.wu"])
+    _close(om.Oracle(cfg, W3)._ffn(0, x) - x, np.zeros_like(x), 0.0, "W_u = 0 makes the FFN inert")
+    W4 = dict(W)
+    W4["l0.ffn.wg"] = synth.bf16_round(prim.bf16_decode(W["l0.ffn.wg"]).astype(np.float32) * 2)
+    assert np.max(np.abs(om.Oracle(cfg, W4)._ffn(0, x) - x - 2 * base)) > 1e-6 * np.max(np.abs(base)), \
+        "the gate enters through silu, not linearly"
+
+
 def pin_argmax_lowest_index():
     lg = np.array([0.1, 0.7, 0.3, 0.7, -1.0])
     assert om.Oracle.argmax(lg) == 1

@@ -118,6 +118,56 @@ def _q4_split_params_swapped(buf, R, K):
     return words, params[..., ::-1]
 
 
+def _ffn_silu_on_up(self, l, x):
+    c = self.cfg
+    h = prim.rmsnorm(x, self.W[f"l{l}.norm2"], c.rms_eps)
+    gte = h @ self.W[f"l{l}.ffn.wg"].T
+    up = h @ self.W[f"l{l}.ffn.wu"].T
+    return x + (gte * prim.silu(up)) @ self.W[f"l{l}.ffn.wd"].T
+
+
+def _head_no_final_norm(self, x):
+    return self.W.lin("embed", x)
+
+
+def _head_layer_gain(self, x):
+    last = self.cfg.n_layers - 1
+    return self.W.lin("embed", prim.rmsnorm(x, self.W[f"l{last}.norm2"], self.cfg.rms_eps))
+
+
+def _dn_project_variant(swap_gates=False, swap_qk=False):
+    def project(self, l, h):
+        c = self.cfg
+        H, dk, dv = c.dn_heads, c.dn_dk, c.dn_dv
+        qkv = h @ self.W[f"l{l}.dn.wqkv"].T
+        q = qkv[..., : H * dk].reshape(*h.shape[:-1], H, dk)
+        k = qkv[..., H * dk: 2 * H * dk].reshape(*h.shape[:-1], H, dk)
+        v = qkv[..., 2 * H * dk:].reshape(*h.shape[:-1], H, dv)
+        if swap_qk:
+            q, k = k, q
+        a = h @ self.W[f"l{l}.dn.w{'b' if swap_gates else 'a'}"].T
+        b = h @ self.W[f"l{l}.dn.w{'a' if swap_gates else 'b'}"].T
+        alpha, beta = dn.gates(a, b)
+        return prim.l2norm(q, c.l2_eps), prim.l2norm(k, c.l2_eps), v, alpha, beta
+    return project
+
+
+def _attn_project_variant(rope_v=False, swap_kv=False, q_unrotated=False):
+    def project(self, l, h, positions):
+        c = self.cfg
+        q = (h @ self.W[f"l{l}.attn.wq"].T).reshape(*h.shape[:-1], c.n_q_heads, c.head_dim)
+        k = (h @ self.W[f"l{l}.attn.wk"].T).reshape(*h.shape[:-1], c.n_kv_heads, c.head_dim)
+        v = (h @ self.W[f"l{l}.attn.wv"].T).reshape(*h.shape[:-1], c.n_kv_heads, c.head_dim)
+        if swap_kv:
+            k, v = v, k
+        cos, sin = prim.rope_angles(c.head_dim, c.rope_theta, positions, self.dtype)
+        cos, sin = cos[..., None, :], sin[..., None, :]
+        qr = q if q_unrotated else prim.rope(q, cos, sin)
+        vr = prim.rope(v, cos, sin) if rope_v else v
+        return qr, prim.rope(k, cos, sin), vr
+    return project
+
+
 _REAL_Q4_CODES = oq.q4g32_codes
 _REAL_Q4_SPLIT = oq.q4g32_split
 _REAL_STEP = dn.delta_step
@@ -145,6 +195,15 @@ MUTANTS = [
     ("verify: rollback keeps the accepted drafts only", [(om.Oracle, "verify")], _verify_variant(keep_extra=-1)),
     ("verify: rollback keeps one token too many", [(om.Oracle, "verify")], _verify_variant(keep_extra=1)),
     ("verify: draft compared with the next choice", [(om.Oracle, "verify")], _verify_variant(shift=1)),
+    ("ffn: silu on up instead of gate", [(om.Oracle, "_ffn")], _ffn_silu_on_up),
+    ("head: final RMSNorm dropped", [(om.Oracle, "_head")], _head_no_final_norm),
+    ("head: a layer gain in place of the final gain", [(om.Oracle, "_head")], _head_layer_gain),
+    ("deltanet: alpha and beta from swapped wa/wb rows", [(om.Oracle, "_dn_project")],
+     _dn_project_variant(swap_gates=True)),
+    ("deltanet: q and k slices of wqkv swapped", [(om.Oracle, "_dn_project")], _dn_project_variant(swap_qk=True)),
+    ("attention: RoPE applied to v", [(om.Oracle, "_attn_project")], _attn_project_variant(rope_v=True)),
+    ("attention: k and v swapped", [(om.Oracle, "_attn_project")], _attn_project_variant(swap_kv=True)),
+    ("attention: q left unrotated", [(om.Oracle, "_attn_project")], _attn_project_variant(q_unrotated=True)),
     ("q4: code half-words swapped", [(oq, "q4g32_codes")], _q4_codes_halves_swapped),
     ("q4: nibbles read in bit order", [(oq, "q4g32_codes")], _q4_codes_nibbles_in_order),
     ("q4: scale and offset swapped", [(oq, "q4g32_split")], _q4_split_params_swapped),
