@@ -76,11 +76,13 @@ class Weights:
         return q4g32_dequant_rows(buf, R, K, idx, self.dtype)
 
     def lin(self, name, x, block: int = 16384):
-        """x @ W.T; a 4-bit matrix that is not kept is decoded a block of rows at a time (each output
-        is still one row's dot product)."""
+        """x @ W.T; a 4-bit matrix is decoded whole and kept when it fits the cache budget, else
+        decoded a block of rows at a time (each output is still one row's dot product)."""
         if name in self.dec or name not in self.q4:
             return x @ self[name].T
         buf, (R, K) = self.q4[name]
+        if R * K * np.dtype(self.dtype).itemsize <= self.cache_left:
+            return x @ self[name].T
         out = np.empty(x.shape[:-1] + (R,), dtype=np.result_type(x, self.dtype))
         for r0 in range(0, R, block):
             r1 = min(R, r0 + block)

@@ -41,3 +41,20 @@ def test_energy_reader_never_raises():
     else:
         j, _ = read()
         assert j >= 0
+
+
+def test_prefill_flops_0p8b_pp520():
+    # the prefill's algorithmic work at pp520: GEMMs 2 x 431,554,560 layer weights x 520 tokens,
+    # chunked DeltaNet about 9.96 MFLOP per full 64-token chunk and head (8 full chunks + one of 8
+    # tokens, 16 heads, 18 layers), causal attention 2 x 2 x 128 x (520 x 521 / 2) x 8 heads x 6
+    # layers, and the LM head on one row
+    cfg = synth.get_config("hybrid_0p8b")
+    f = bench.prefill_flops(cfg, 520)
+    assert f["gemm"] == 2 * 520 * 431554560
+    assert f["attention"] == 2 * 2 * 128 * (520 * 521 / 2) * 8 * 6
+    assert f["lm_head"] == 2 * 151936 * 1024
+    full = 2 * 64 * 64 * 128 * 2 + 2 * 64 * 128 * 128 * 3 + 64 * 64 * 128 + 2 * 64 * 64 * 128
+    assert full == 9961472
+    tail = 2 * 8 * 8 * 128 * 2 + 2 * 8 * 128 * 128 * 3 + 8 * 8 * 128 + 2 * 8 * 8 * 128
+    assert f["deltanet"] == 18 * 16 * (8 * full + tail)
+    assert abs(f["total"] / 1e9 - 475.65) < 0.01

@@ -49,22 +49,28 @@ def test_q4_long_prompt_small_grid():
     _check_run(cfg, W, synth.make_prompt(cfg.vocab, 360, 9), 8, grid=8, weight_dtype=MK_Q4G32)
 
 
-def _slice_cfg(n_layers):
-    return synth.get_config("hybrid_27b", n_layers=n_layers, max_ctx=64)
+def _slice_cfg(n_layers, max_ctx=64):
+    return synth.get_config("hybrid_27b", n_layers=n_layers, max_ctx=max_ctx)
 
 
 PROMPT_27B = 8
-STEPS_27B = 4
 
 
-def test_q4_27b_width_slice_and_full_depth():
-    cfg4 = _slice_cfg(4)
+@pytest.mark.timeout(1200)
+def test_q4_27b_width_slice_1k_context():
+    """a 4-layer slice at 27B width: a 1,024-token prompt then 32 decode steps against the oracle
+    (the oracle keeps the decoded slice, about 17 GB in float64, and runs the prompt in its
+    whole-sequence form)"""
+    cfg4 = _slice_cfg(4, max_ctx=1024 + 32)
     W4 = synth.make_q4_weights(cfg4, 0)
-    prompt = synth.make_prompt(cfg4.vocab, PROMPT_27B, 0)
-    print(f"[27B width, 4 layers] prompt {PROMPT_27B}, {STEPS_27B} steps", flush=True)
-    _check_run(cfg4, W4, prompt, STEPS_27B, weight_dtype=MK_Q4G32, oracle_cache=1 << 36)
-    del W4
+    prompt = synth.make_prompt(cfg4.vocab, 1024, 1)
+    print("[27B width, 4 layers] prompt 1024, 32 steps", flush=True)
+    _check_run(cfg4, W4, prompt, 32, weight_dtype=MK_Q4G32, oracle_cache=1 << 36)
 
+
+def test_q4_27b_full_depth_against_slice():
+    cfg4 = _slice_cfg(4)
+    prompt = synth.make_prompt(cfg4.vocab, PROMPT_27B, 0)
     # the full-depth model: its first four layers are the slice's tensors (same generator, manifest
     # order); feed it the same tokens
     torch = torch_cuda()
