@@ -24,7 +24,7 @@ STATUS = {
 
 # every symbol include/mk.h declares
 EXPORTS = ["mk_workspace_bytes", "mk_create", "mk_load_weights", "mk_check_tensors", "mk_prefill",
-           "mk_decode_step", "mk_verify_k", "mk_reset", "mk_sync", "mk_get_position",
+           "mk_decode_step", "mk_decode_step_noalloc", "mk_verify_k", "mk_reset", "mk_sync", "mk_get_position",
            "mk_state_bytes", "mk_read_state", "mk_write_state", "mk_set_grid", "mk_get_grid",
            "mk_set_trace", "mk_last_error", "mk_destroy"]
 
@@ -71,6 +71,7 @@ def load_library():
         "mk_check_tensors": (ctypes.c_int, [P, P, I32]),
         "mk_prefill": (ctypes.c_int, [P, P, I32, P, P]),
         "mk_decode_step": (ctypes.c_int, [P, P, P, P]),
+        "mk_decode_step_noalloc": (ctypes.c_int, [P, P, P, P]),
         "mk_verify_k": (ctypes.c_int, [P, P, I32, P, P]),
         "mk_reset": (ctypes.c_int, [P]),
         "mk_sync": (ctypes.c_int, [P]),
@@ -216,6 +217,9 @@ class Model:
 
     def mk_decode_step(self, d_tok, d_next, d_logits=None):
         _check(self.lib.mk_decode_step(self.ctx, _ptr(d_tok), _ptr(d_next), _ptr(d_logits)), self.ctx)
+
+    def mk_decode_step_noalloc(self, d_tok, d_next, d_logits=None):
+        _check(self.lib.mk_decode_step_noalloc(self.ctx, _ptr(d_tok), _ptr(d_next), _ptr(d_logits)), self.ctx)
 
     def mk_verify_k(self, d_tokens, k: int, d_out, d_n_accepted):
         _check(self.lib.mk_verify_k(self.ctx, _ptr(d_tokens), int(k), _ptr(d_out), _ptr(d_n_accepted)), self.ctx)

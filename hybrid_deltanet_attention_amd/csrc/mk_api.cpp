@@ -100,6 +100,9 @@ struct LayerOff {
 
 struct Layout {
   size_t ctl, descs, rope_cos, rope_sin, g_final, embed, ll_am, scratch, total;
+  // mk_decode_step_noalloc: layer descriptors whose records point into the static scratch array,
+  // and the bytes of decode records (from xchg_begin) that array must hold
+  size_t ndescs, na_bytes;
   size_t state_begin, state_end;  // DeltaNet states + KV caches
   size_t xchg_begin, xchg_end;    // exchange records
   std::vector<LayerOff> layers;
@@ -171,6 +174,7 @@ Layout make_layout(const mk_config& c) {
     lo.ll_x2 = take(D * 8);
   }
   L.ll_am = take((size_t)2 * MK_MAX_GRID * 8);
+  L.na_bytes = o - L.xchg_begin;  // the decode kernel's records: what mk_decode_step_noalloc keeps in static scratch
   L.vt = c.max_verify_k > 0 ? c.max_verify_k + 1 : 0;
   if (L.vt) {
     const size_t vt = (size_t)L.vt;
@@ -198,6 +202,7 @@ Layout make_layout(const mk_config& c) {
     for (int l = 0; l < c.n_layers; ++l)
       if (!is_attention(c, l)) L.layers[l].snap = base + (size_t)(j++) * per * 4;
   }
+  L.ndescs = take(sizeof(MkLayerDev) * c.n_layers);
   L.scratch = take(4096);
   // prefill scratch (4-bit models run their prompts through the decode kernel and need none)
   if (!q4) {
@@ -339,6 +344,9 @@ struct mk_ctx {
   Layout lay;
   MkDecodeParams base{};
   MkDecodeParams vbase{};  // verify launches (valid when lay.vt > 0)
+  MkDecodeParams nbase{};  // mk_decode_step_noalloc launches (valid when na_fits)
+  char* na_scratch = nullptr;  // this device's static record array
+  bool na_fits = false;
   int n_cu = 0;
   int grid = 0;
   bool loaded = false;
@@ -581,6 +589,35 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
       else d.Ssnap = (float*)(ctx->ws + lo.snap);
     }
   }
+  // the decode kernel's records in the static scratch array (mk_decode_step_noalloc): the array's
+  // device address on this device, looked up once per device with the device current
+  {
+    void* sp = nullptr;
+    const char* serr = "";
+    if (mk_noalloc_scratch(device, &sp, &serr) != 0) {
+      delete ctx;
+      return fail_global(MK_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + serr);
+    }
+    ctx->na_scratch = (char*)sp;
+    ctx->na_fits = lay.na_bytes <= (size_t)MK_NOALLOC_SCRATCH_BYTES;
+  }
+  std::vector<MkLayerDev> ndescs;
+  if (ctx->na_fits) {
+    auto rebase = [&](mk_u64* q) { return q ? (mk_u64*)(ctx->na_scratch + ((char*)q - (ctx->ws + lay.xchg_begin))) : q; };
+    ndescs = descs;
+    for (MkLayerDev& d : ndescs) {
+      d.ll_in = rebase(d.ll_in);
+      d.ll_part = rebase(d.ll_part);
+      d.ll_o = rebase(d.ll_o);
+      d.ll_x1 = rebase(d.ll_x1);
+      d.ll_h = rebase(d.ll_h);
+      d.ll_x2 = rebase(d.ll_x2);
+    }
+    MkDecodeParams& q = ctx->nbase;
+    q = p;
+    q.layers = (const MkLayerDev*)(ctx->ws + lay.ndescs);
+    q.ll_am = rebase(p.ll_am);
+  }
   // RoPE tables: angle = pos * theta^(-2i/hd), evaluated in double, stored as float
   const int half = cfg->head_dim / 2;
   std::vector<float> cs((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
@@ -603,6 +640,9 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   if (lay.vt)
     hip_ok(hipMemcpyAsync(ctx->ws + lay.vdescs, vdescs.data(), sizeof(MkLayerDev) * vdescs.size(),
                           hipMemcpyHostToDevice, ctx->stream), "copy verify layer descriptors");
+  if (ctx->na_fits)
+    hip_ok(hipMemcpyAsync(ctx->ws + lay.ndescs, ndescs.data(), sizeof(MkLayerDev) * ndescs.size(),
+                          hipMemcpyHostToDevice, ctx->stream), "copy static-record layer descriptors");
   hip_ok(hipMemcpyAsync(ctx->ws + lay.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, ctx->stream),
          "copy rope cos");
   hip_ok(hipMemcpyAsync(ctx->ws + lay.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, ctx->stream),
@@ -644,6 +684,12 @@ int mk_set_grid(mk_ctx* ctx, int32_t n) {
   }
   ctx->base = q;
   ctx->vbase = v;
+  if (ctx->na_fits) {
+    const MkDecodeParams keep = ctx->nbase;
+    ctx->nbase = q;
+    ctx->nbase.layers = keep.layers;
+    ctx->nbase.ll_am = keep.ll_am;
+  }
   ctx->grid = n;
   return MK_OK;
 }
@@ -867,6 +913,30 @@ int mk_decode_step(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_
   return MK_OK;
 }
 
+int mk_decode_step_noalloc(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_logits) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  if (!ctx->na_fits)
+    return fail(ctx, MK_E_UNSUPPORTED, "this model's decode records need " + std::to_string(ctx->lay.na_bytes) +
+                                            " bytes; the static scratch array holds " +
+                                            std::to_string((size_t)MK_NOALLOC_SCRATCH_BYTES));
+  if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
+  if (!d_tok || !d_next) return fail(ctx, MK_E_INVALID, "d_tok and d_next are required");
+  if (ctx->pos_host + 1 > ctx->cfg.max_ctx && refresh_position(ctx) != MK_OK) return MK_E_HIP;
+  if (ctx->pos_host + 1 > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "context is full");
+  MkDecodeParams p = ctx->nbase;
+  p.tok = d_tok;
+  p.next = d_next;
+  p.logits = d_logits;
+  // the array holds the last call's records, possibly another context's with a matching epoch:
+  // clear the part this launch polls (a fill kernel, no memset node)
+  if (mk_launch_zero(ctx->na_scratch, (int64_t)ctx->lay.na_bytes, ctx->stream))
+    return fail(ctx, MK_E_HIP, "clearing the static records failed");
+  if ((p.wq4 ? mk_launch_decode_q4(&p, ctx->grid, ctx->stream) : mk_launch_decode(&p, ctx->grid, ctx->stream)))
+    return fail(ctx, MK_E_HIP, "decode launch failed");
+  ctx->pos_host += 1;
+  return MK_OK;
+}
+
 int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next, float* d_logits) {
   if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
   if (!ctx->loaded) return fail(ctx, MK_E_ORDER, "weights are not loaded");
@@ -958,6 +1028,7 @@ int mk_set_trace(mk_ctx* ctx, void* d_trace, size_t bytes) {
     return fail(ctx, MK_E_INVALID, "trace buffer needs grid * " + std::to_string(MK_TRACE_EVENTS) + " * 8 bytes");
   ctx->base.trace = (unsigned long long*)d_trace;
   ctx->vbase.trace = (unsigned long long*)d_trace;
+  ctx->nbase.trace = (unsigned long long*)d_trace;
   return MK_OK;
 }
 

@@ -40,6 +40,8 @@ typedef unsigned long long mk_u64;
 #define MK_MAX_GRID 1024
 // Positions one speculative-verify launch scores (the pending token and up to 5 drafts).
 #define MK_VERIFY_MAXT 6
+// Bytes of the static exchange-record array behind mk_decode_step_noalloc (mk_noalloc.hip).
+#define MK_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 // Device-resident control block (first 256 bytes of the workspace).
 struct MkCtl {
@@ -126,6 +128,8 @@ int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_
 int mk_launch_zero(void* dst, int64_t bytes, void* stream);
 int mk_launch_set_ctl(MkCtl* ctl, int32_t pos, int reset_err, int bump_step, void* stream);
 int mk_decode_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
+// device address of the static exchange-record array (mk_noalloc.hip), looked up once per device
+int mk_noalloc_scratch(int device, void** out, const char** err);
 // prefill kernels (mk_prefill.hip); all return 0 or -1 (launch error)
 int mk_pf_embed(const int32_t* tok, int T, const uint16_t* embed, int D, int vocab, float* X, MkCtl* ctl, void* stream);
 int mk_pf_rms_split(const float* X, int T, int D, const uint16_t* g, float eps, uint16_t* Ahi, uint16_t* Alo, int lda,

@@ -139,6 +139,18 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
  * MK_E_CTX_FULL (checked against the host's count of enqueued positions). */
 int mk_decode_step(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_logits);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): mk_decode_step with the decode kernel's scratch -- its
+ * exchange records and argmax records -- held in a static device array of the library
+ * (MK_NOALLOC_SCRATCH_BYTES = 16 MiB per device, kept until the process ends) instead of the
+ * workspace.  It allocates nothing and makes no allocating library call; its inputs, outputs and
+ * the model state (weights, DeltaNet states, KV cache, position) stay where mk_decode_step has
+ * them, and its results are bit-identical to mk_decode_step's.  Every context on a device shares
+ * the one array; each call clears the part it uses before launching, and calls that overlap on
+ * one device (several streams, several contexts at once) race.  Errors: as mk_decode_step, plus
+ * MK_E_UNSUPPORTED when the model's records exceed the array (the message gives both sizes). */
+int mk_decode_step_noalloc(mk_ctx* ctx, const int32_t* d_tok, int32_t* d_next, float* d_logits);
+
 /* Speculative verify as ONE kernel launch (Reddit follow-up on the 27B model, speculative-decoding
  * paragraph: several drafted tokens checked per pass, the main model's greedy output kept exactly).
  * d_tokens[0..k] = [pending, d1..dk] (device int32; the pending token is the last greedy choice, not
