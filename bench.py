@@ -109,26 +109,29 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "reps": 4}), flush=True)
 
 
-def algorithmic_bytes(cfg, L: int, wb: float = 2.0) -> dict:
+KV_BYTES = {"f32": 4.0, "f16": 2.0, "q8": 1.0 + 4.0 / 32}  # per cached value (int8: code + a scale per 32)
+
+
+def algorithmic_bytes(cfg, L: int, wb: float = 2.0, kv: str = "f32") -> dict:
     """Bytes one decode launch must move at context length L (positions 0..L-1 visible); wb is the
     bytes per weight of the matrices (2 for BF16, 0.625 for 4-bit codes with an FP16 scale and
-    offset per 32 weights)."""
+    offset per 32 weights); kv the KV cache's element type."""
     D, H = cfg.hidden, cfg.dn_heads
     w = 0
     state = 0
-    kv = 0
+    kvb = 0
     for l in range(cfg.n_layers):
         if cfg.is_attention(l):
             rows_in = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
             kout = cfg.n_q_heads * cfg.head_dim
-            kv += 2 * cfg.n_kv_heads * cfg.head_dim * 4 * L  # K and V: L-1 positions read, 1 written
+            kvb += 2 * cfg.n_kv_heads * cfg.head_dim * KV_BYTES[kv] * L  # K and V: L-1 positions read, 1 written
         else:
             rows_in = 2 * H * cfg.dn_dk + H * cfg.dn_dv + 2 * H
             kout = H * cfg.dn_dv
             state += 2 * H * cfg.dn_dv * cfg.dn_dk * 4       # read + write
         w += wb * (rows_in * D + D * kout + 3 * cfg.ffn * D) + 2 * 4 * D
     head = wb * cfg.vocab * D + 4 * D + wb * D               # tied LM head, final gain, embedding row
-    return {"weights": w, "lm_head": head, "state": state, "kv": kv, "total": w + head + state + kv}
+    return {"weights": w, "lm_head": head, "state": state, "kv": kvb, "total": w + head + state + kvb}
 
 
 def prefill_flops(cfg, T: int, chunk: int = 64) -> dict:
@@ -289,15 +292,18 @@ def energy_leg(m, prompt, tok, n_steps: int, min_seconds: float = 4.0) -> dict:
             "counter": "amdsmi energy accumulator, whole board"}
 
 
-def long_context_leg(cfg_name: str, W, ctx: int, n_steps: int) -> dict:
+def long_context_leg(cfg_name: str, W, ctx: int, n_steps: int, kv: str = "f32") -> dict:
     """Decode at a long context: a ctx-token prompt through the GPU prefill, then n_steps timed
-    one-launch decode steps with the KV cache that large (same weights, a 32,768-position cache)."""
+    one-launch decode steps with the KV cache that large (same weights; the cache holds the next
+    multiple of 32,768 positions and stores kv: "f32", "f16" or "q8")."""
     import torch
     import synth
     from hybrid_deltanet_attention_amd import Model
-    cfg = synth.get_config(cfg_name, max_ctx=32768)
+    from hybrid_deltanet_attention_amd.binding import MK_F32, MK_F16, MK_Q8
+    max_ctx = 32768 * ((ctx + 64 + 32767) // 32768)
+    cfg = synth.get_config(cfg_name, max_ctx=max_ctx)
     dev = torch.device("cuda:0")
-    m = Model(cfg, device=0)
+    m = Model(cfg, device=0, kv_dtype={"f32": MK_F32, "f16": MK_F16, "q8": MK_Q8}[kv])
     m.mk_load_weights(W)
     prompt = torch.tensor(synth.make_prompt(cfg.vocab, ctx, SEED + 7), device=dev)
     tok = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -318,12 +324,12 @@ def long_context_leg(cfg_name: str, W, ctx: int, n_steps: int) -> dict:
     us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
     region = ev[0][0].elapsed_time(ev[-1][1]) / 1e3
     L0 = ctx + 5
-    bytes_per = float(np.mean([algorithmic_bytes(cfg, L0 + i)["total"] for i in range(n_steps)]))
+    bytes_per = float(np.mean([algorithmic_bytes(cfg, L0 + i, kv=kv)["total"] for i in range(n_steps)]))
     gbs = bytes_per / (us * 1e-6) / 1e9
     m.close()
-    return {"context": ctx, "prefill_s": round(pre_s, 3), "us_per_launch": round(us, 2),
-            "tok_per_s": round(n_steps / region, 1), "bytes_per_launch": int(bytes_per),
-            "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "kv": "fp32"}
+    return {"context": ctx, "kv": kv, "max_ctx": max_ctx, "prefill_s": round(pre_s, 3),
+            "us_per_launch": round(us, 2), "tok_per_s": round(n_steps / region, 1), "bytes_per_launch": int(bytes_per),
+            "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def q4_27b_leg(ctx: int, n_steps: int) -> dict:
@@ -455,7 +461,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the pp520 prefill timing (profiling runs)")
     ap.add_argument("--config", default="hybrid_0p8b")
     ap.add_argument("--long-context", type=int, default=30000,
-                    help="prompt length of the long-context decode leg (32,768-position cache); 0 skips it")
+                    help="prompt length of the long-context decode legs: a binary16 cache at this length and an "
+                         "int8 cache at 96,000 positions (the pages keep fp16 to about 80K, 8-bit above); 0 skips them")
     ap.add_argument("--verify-k", type=int, default=5, help="drafts per mk_verify_k launch in the verify leg; 0 skips it")
     ap.add_argument("--q4-steps", type=int, default=64,
                     help="timed decode steps of the 27B-scale 4-bit leg (1,024-token prompt); 0 skips it")
@@ -575,7 +582,8 @@ def main():
         out["verify"]["decode_us_per_launch"] = round(avg_launch * 1e6, 2)
         print(f"[bench] verify: {out['verify']}", file=sys.stderr, flush=True)
     if args.long_context > 0:
-        out["long_context"] = long_context_leg(args.config, W, min(args.long_context, 32768 - 64), 32)
+        out["long_context"] = [long_context_leg(args.config, W, min(args.long_context, 32768 - 64), 32, "f16"),
+                               long_context_leg(args.config, W, 96000, 32, "q8")]
         print(f"[bench] long context: {out['long_context']}", file=sys.stderr, flush=True)
     if args.energy_steps > 0:
         n_e = min(args.energy_steps, cfg.max_ctx - PROMPT)

@@ -15,7 +15,7 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 MK_OK = 0
-MK_BF16, MK_F32, MK_F16, MK_I32, MK_Q4G32 = 1, 2, 3, 4, 5
+MK_BF16, MK_F32, MK_F16, MK_I32, MK_Q4G32, MK_Q8 = 1, 2, 3, 4, 5, 6
 STATUS = {
     0: "MK_OK", -1: "MK_E_INVALID", -2: "MK_E_SHAPE", -3: "MK_E_DTYPE", -4: "MK_E_NAME",
     -5: "MK_E_ORDER", -6: "MK_E_CTX_FULL", -7: "MK_E_NO_DEVICE", -8: "MK_E_OCCUPANCY",
@@ -103,16 +103,17 @@ def _check(rc: int, ctx=None):
         raise MkError(rc, _err(ctx))
 
 
-def mk_config_from(cfg, max_verify_k: int = 0, weight_dtype: int = MK_BF16) -> mk_config:
+def mk_config_from(cfg, max_verify_k: int = 0, weight_dtype: int = MK_BF16, kv_dtype: int = MK_F32) -> mk_config:
     """Marshal a model shape (any object with the synth.ModelConfig attributes) into the C struct.
-    weight_dtype: MK_BF16, or MK_Q4G32 for 4-bit block-quantised matrices."""
+    weight_dtype: MK_BF16, or MK_Q4G32 for 4-bit block-quantised matrices; kv_dtype: MK_F32, MK_F16
+    or MK_Q8 (the KV cache's element type)."""
     c = mk_config()
     for f in ("n_layers", "hidden", "ffn", "vocab", "period", "attn_slot", "dn_heads", "dn_dk",
               "dn_dv", "n_q_heads", "n_kv_heads", "head_dim", "max_ctx"):
         setattr(c, f, int(getattr(cfg, f)))
     c.tied_embeddings = 1 if getattr(cfg, "tied", True) else 0
     c.weight_dtype = int(weight_dtype)
-    c.kv_dtype = MK_F32
+    c.kv_dtype = int(kv_dtype)
     c.max_verify_k = max_verify_k
     c.rms_eps = float(cfg.rms_eps)
     c.l2_eps = float(cfg.l2_eps)
@@ -190,12 +191,14 @@ def mk_check_tensors(cfg, weights: dict, weight_dtype: int = MK_BF16) -> None:
 class Model:
     """A context on one device: workspace (torch uint8 tensor), stream, loaded weights."""
 
-    def __init__(self, cfg, device: int = 0, stream=None, max_verify_k: int = 0, weight_dtype: int = MK_BF16):
+    def __init__(self, cfg, device: int = 0, stream=None, max_verify_k: int = 0, weight_dtype: int = MK_BF16,
+                 kv_dtype: int = MK_F32):
         import torch
         self.lib = load_library()
         self.cfg = cfg
         self.weight_dtype = int(weight_dtype)
-        self.c = mk_config_from(cfg, max_verify_k, weight_dtype)
+        self.kv_dtype = int(kv_dtype)
+        self.c = mk_config_from(cfg, max_verify_k, weight_dtype, kv_dtype)
         self.device = device
         nbytes = mk_workspace_bytes(self.c)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=f"cuda:{device}")

@@ -33,6 +33,16 @@ struct TensorSpec {
 
 bool is_attention(const mk_config& c, int l) { return l % c.period == c.attn_slot; }
 
+// KV cache element type of the kernels for a config's kv_dtype
+int kv_type(int kv_dtype) { return kv_dtype == MK_F16 ? MK_KV_F16 : (kv_dtype == MK_Q8 ? MK_KV_Q8 : MK_KV_F32); }
+size_t kv_elem_bytes(int kvt) { return kvt == MK_KV_F32 ? 4 : (kvt == MK_KV_F16 ? 2 : 1); }
+// stage slots of one KV chunk buffer, as the decode kernels count them (mk_device.h)
+int kv_buf_slots_host(int hd, int kvt) {
+  const int lpp = (int)(hd * kv_elem_bytes(kvt)) / 16, pps = 64 / lpp;
+  const int ks = (MK_ATT_CHUNK + pps - 1) / pps;
+  return (2 * ks + (kvt == MK_KV_Q8 ? 1 : 0) + 3) & ~3;
+}
+
 std::vector<TensorSpec> manifest(const mk_config& c) {
   std::vector<TensorSpec> m;
   const int64_t D = c.hidden, H = c.dn_heads;
@@ -81,7 +91,18 @@ std::string check_config(const mk_config* c) {
       return "MK_Q4G32 needs hidden <= 8192 and ffn, dn_heads*dn_dv, n_q_heads*head_dim <= 20480";
     if (c->max_verify_k != 0) return "speculative verify needs BF16 weights: max_verify_k must be 0 with MK_Q4G32";
   }
-  if (c->kv_dtype != MK_F32) return "kv_dtype must be MK_F32";
+  if (c->kv_dtype != MK_F32 && c->kv_dtype != MK_F16 && c->kv_dtype != MK_Q8)
+    return "kv_dtype must be MK_F32, MK_F16 or MK_Q8";
+  if (c->kv_dtype == MK_F16 && c->head_dim % 8) return "an MK_F16 KV cache needs head_dim to be a multiple of 8";
+  if (c->kv_dtype == MK_Q8 && c->head_dim % MK_KV_Q8_BLOCK)
+    return "an MK_Q8 KV cache needs head_dim to be a multiple of 32";
+  if (c->kv_dtype != MK_F32) {
+    // the decode kernels stage compact chunks next to one FP32 chunk buffer in their KV stage
+    const int kvt = kv_type(c->kv_dtype);
+    const int a_slots = c->weight_dtype == MK_Q4G32 ? 32 : MK_STAGE_A_SLOTS;
+    if (kv_buf_slots_host(c->head_dim, MK_KV_F32) + kv_buf_slots_host(c->head_dim, kvt) > a_slots)
+      return "head_dim too large for a compact KV cache with these weights";
+  }
   if (c->max_ctx <= 0 || c->max_ctx > (1 << 20)) return "max_ctx must be in [1, 2^20]";
   if (c->max_verify_k < 0 || c->max_verify_k > MK_VERIFY_MAXT - 1)
     return "max_verify_k must be in [0, " + std::to_string(MK_VERIFY_MAXT - 1) + "]";
@@ -92,7 +113,7 @@ std::string check_config(const mk_config* c) {
 
 // ----------------------------------------------------------------------- workspace layout
 struct LayerOff {
-  size_t w_in, w_out, w_gu, w_down, g12, S, Kc, Vc, ll_in, ll_part, ll_o, ll_x1, ll_h, ll_x2;
+  size_t w_in, w_out, w_gu, w_down, g12, S, Kc, Vc, Ks, Vs, ll_in, ll_part, ll_o, ll_x1, ll_h, ll_x2;
   // speculative verify: records of vt positions ([t][n] per record vector) and state snapshots
   size_t v_in, v_part, v_o, v_x1, v_h, v_x2, snap;
   int64_t rows_in, k_out;
@@ -114,6 +135,7 @@ struct Layout {
   // prefill scratch: a chunk of up to pf_T tokens
   int pf_T, pf_lda, pf_ldy;
   size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part, pf_ch, pf_sk;
+  size_t pf_kvf;  // compact KV caches: a chunk's rotated keys and values in FP32, [2][nkv][T][hd]
 };
 
 constexpr int PF_LM_WG = 512;  // workgroups of the prefill LM head
@@ -156,8 +178,15 @@ Layout make_layout(const mk_config& c) {
   for (int l = 0; l < c.n_layers; ++l) {
     LayerOff& lo = L.layers[l];
     if (is_attention(c, l)) {
-      lo.Kc = take((size_t)c.n_kv_heads * c.max_ctx * c.head_dim * 4);
-      lo.Vc = take((size_t)c.n_kv_heads * c.max_ctx * c.head_dim * 4);
+      const size_t eb = kv_elem_bytes(kv_type(c.kv_dtype));
+      lo.Kc = take((size_t)c.n_kv_heads * c.max_ctx * c.head_dim * eb);
+      lo.Vc = take((size_t)c.n_kv_heads * c.max_ctx * c.head_dim * eb);
+      if (c.kv_dtype == MK_Q8) {
+        // 16-byte copies of a chunk's scale rows may reach up to 12 bytes past the last row
+        const size_t sb = (size_t)c.n_kv_heads * c.max_ctx * (c.head_dim / MK_KV_Q8_BLOCK) * 4 + 256;
+        lo.Ks = take(sb);
+        lo.Vs = take(sb);
+      }
     } else {
       lo.S = take((size_t)H * c.dn_dv * c.dn_dk * 4);
     }
@@ -227,6 +256,7 @@ Layout make_layout(const mk_config& c) {
     L.pf_ch = take((size_t)((T + 63) / 64) * H * (2 * 64 * 64 + 2 * 64 + 4) * 4);
     // split-K partials of the residual GEMMs: at most 256 work items of 128 x 128 outputs
     L.pf_sk = take(PF_SPLITK_FLOATS * 4);
+    if (c.kv_dtype != MK_F32) L.pf_kvf = take((size_t)2 * T * c.n_kv_heads * c.head_dim * 4);
   }
   L.total = o;
   return L;
@@ -520,6 +550,7 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
   p.ctl = (MkCtl*)(ctx->ws + lay.ctl);
   p.ll_am = (mk_u64*)(ctx->ws + lay.ll_am);
   p.wq4 = cfg->weight_dtype == MK_Q4G32 ? 1 : 0;
+  p.kvt = kv_type(cfg->kv_dtype);
   if (p.wq4) lds_layout_q4(*cfg, ctx->grid, p);
   else lds_layout(*cfg, ctx->grid, p);
 
@@ -548,6 +579,10 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
     if (d.kind == MK_LAYER_ATT) {
       d.Kc = (float*)(ctx->ws + lo.Kc);
       d.Vc = (float*)(ctx->ws + lo.Vc);
+      if (cfg->kv_dtype == MK_Q8) {
+        d.Ks = (float*)(ctx->ws + lo.Ks);
+        d.Vs = (float*)(ctx->ws + lo.Vs);
+      }
       d.ll_part = (mk_u64*)(ctx->ws + lo.ll_part);
     } else {
       d.S = (float*)(ctx->ws + lo.S);
@@ -946,9 +981,10 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   if (ctx->pos_host + n > ctx->cfg.max_ctx) return fail(ctx, MK_E_CTX_FULL, "prompt does not fit the context");
   const mk_config& c = ctx->cfg;
   const int gs = c.n_q_heads / c.n_kv_heads;
-  if (16 % gs != 0 || ctx->base.wq4) {
-    // 4-bit weights, or shapes the prefill attention tiling does not cover: token by token through
-    // the decode kernel
+  const int kvt = ctx->base.kvt;
+  if (16 % gs != 0 || ctx->base.wq4 || (kvt != MK_KV_F32 && c.head_dim != 64 && c.head_dim != 128)) {
+    // 4-bit weights, or shapes the prefill attention tiling does not cover (compact KV caches are
+    // read by the matrix-core attention only): token by token through the decode kernel
     int32_t* scratch_tok = (int32_t*)(ctx->ws + ctx->lay.scratch) + 8;
     for (int32_t i = 0; i < n; ++i) {
       const bool last = (i == n - 1);
@@ -996,8 +1032,19 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
       if (is_attention(c, l)) {
         float* Kc = (float*)(ws + lo.Kc);
         float* Vc = (float*)(ws + lo.Vc);
-        rc |= mk_pf_att_rope(Y, ldy, T, p0, nq, nkv, hd, c.max_ctx, rcos, rsin, Q, Kc, Vc, st);
-        rc |= mk_pf_attention(Q, Kc, Vc, T, p0, nq, nkv, hd, c.max_ctx, Ahi, Alo, lda, PK, PKN, st);
+        if (kvt == MK_KV_F32) {
+          rc |= mk_pf_att_rope(Y, ldy, T, p0, nq, nkv, hd, rcos, rsin, Q, Kc, Vc, c.max_ctx, p0, st);
+        } else {
+          // rotated rows of this chunk in FP32, then stored in the cache type
+          float* Kf = (float*)(ws + L.pf_kvf);
+          float* Vf = Kf + (size_t)nkv * T * hd;
+          rc |= mk_pf_att_rope(Y, ldy, T, p0, nq, nkv, hd, rcos, rsin, Q, Kf, Vf, T, 0, st);
+          rc |= mk_pf_kv_pack(Kf, Vf, T, nkv, hd, kvt, Kc, Vc, (float*)(ws + lo.Ks), (float*)(ws + lo.Vs), c.max_ctx,
+                              p0, st);
+        }
+        rc |= mk_pf_attention(Q, Kc, Vc, kvt, kvt == MK_KV_Q8 ? (const float*)(ws + lo.Ks) : nullptr,
+                              kvt == MK_KV_Q8 ? (const float*)(ws + lo.Vs) : nullptr, T, p0, nq, nkv, hd, c.max_ctx,
+                              Ahi, Alo, lda, PK, PKN, st);
       } else {
         rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, c.l2_eps, Ahi, Alo, lda,
                             (float*)(ws + L.pf_ch), st);
@@ -1100,11 +1147,32 @@ int mk_read_state(mk_ctx* ctx, int32_t layer, void* dst) {
   HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
   const LayerOff& lo = ctx->lay.layers[layer];
   const size_t b = mk_state_bytes(ctx, layer);
-  if (is_attention(ctx->cfg, layer)) {
+  if (!is_attention(ctx->cfg, layer)) {
+    HIPCHK(ctx, hipMemcpy(dst, ctx->ws + lo.S, b, hipMemcpyDeviceToHost));
+    return MK_OK;
+  }
+  const mk_config& c = ctx->cfg;
+  const int kvt = kv_type(c.kv_dtype);
+  if (kvt == MK_KV_F32) {
     HIPCHK(ctx, hipMemcpy(dst, ctx->ws + lo.Kc, b / 2, hipMemcpyDeviceToHost));
     HIPCHK(ctx, hipMemcpy((char*)dst + b / 2, ctx->ws + lo.Vc, b / 2, hipMemcpyDeviceToHost));
-  } else {
-    HIPCHK(ctx, hipMemcpy(dst, ctx->ws + lo.S, b, hipMemcpyDeviceToHost));
+    return MK_OK;
+  }
+  // compact caches: the stored values, decoded to FP32
+  const size_t n = (size_t)c.n_kv_heads * c.max_ctx * c.head_dim, nb = n / MK_KV_Q8_BLOCK;
+  std::vector<char> raw(n * kv_elem_bytes(kvt));
+  std::vector<float> sc(kvt == MK_KV_Q8 ? nb : 0);
+  for (int v = 0; v < 2; ++v) {
+    HIPCHK(ctx, hipMemcpy(raw.data(), ctx->ws + (v ? lo.Vc : lo.Kc), raw.size(), hipMemcpyDeviceToHost));
+    float* out = (float*)dst + v * n;
+    if (kvt == MK_KV_F16) {
+      const _Float16* h = (const _Float16*)raw.data();
+      for (size_t i = 0; i < n; ++i) out[i] = (float)h[i];
+    } else {
+      HIPCHK(ctx, hipMemcpy(sc.data(), ctx->ws + (v ? lo.Vs : lo.Ks), nb * 4, hipMemcpyDeviceToHost));
+      const signed char* q = (const signed char*)raw.data();
+      for (size_t i = 0; i < n; ++i) out[i] = (float)q[i] * sc[i / MK_KV_Q8_BLOCK];
+    }
   }
   return MK_OK;
 }
@@ -1115,11 +1183,39 @@ int mk_write_state(mk_ctx* ctx, int32_t layer, const void* src) {
   HIPCHK(ctx, hipStreamSynchronize(ctx->stream));
   const LayerOff& lo = ctx->lay.layers[layer];
   const size_t b = mk_state_bytes(ctx, layer);
-  if (is_attention(ctx->cfg, layer)) {
+  if (!is_attention(ctx->cfg, layer)) {
+    HIPCHK(ctx, hipMemcpy(ctx->ws + lo.S, src, b, hipMemcpyHostToDevice));
+    return MK_OK;
+  }
+  const mk_config& c = ctx->cfg;
+  const int kvt = kv_type(c.kv_dtype);
+  if (kvt == MK_KV_F32) {
     HIPCHK(ctx, hipMemcpy(ctx->ws + lo.Kc, src, b / 2, hipMemcpyHostToDevice));
     HIPCHK(ctx, hipMemcpy(ctx->ws + lo.Vc, (const char*)src + b / 2, b / 2, hipMemcpyHostToDevice));
-  } else {
-    HIPCHK(ctx, hipMemcpy(ctx->ws + lo.S, src, b, hipMemcpyHostToDevice));
+    return MK_OK;
+  }
+  // compact caches: FP32 values -> the cache type (nearest binary16; int8 blocks as the kernels form them)
+  const size_t n = (size_t)c.n_kv_heads * c.max_ctx * c.head_dim, nb = n / MK_KV_Q8_BLOCK;
+  std::vector<char> raw(n * kv_elem_bytes(kvt));
+  std::vector<float> sc(kvt == MK_KV_Q8 ? nb : 0);
+  for (int v = 0; v < 2; ++v) {
+    const float* in = (const float*)src + v * n;
+    if (kvt == MK_KV_F16) {
+      _Float16* h = (_Float16*)raw.data();
+      for (size_t i = 0; i < n; ++i) h[i] = (_Float16)in[i];
+    } else {
+      signed char* q = (signed char*)raw.data();
+      for (size_t bi = 0; bi < nb; ++bi) {
+        float m = 0.f;
+        for (int i = 0; i < MK_KV_Q8_BLOCK; ++i) m = std::fmax(m, std::fabs(in[bi * MK_KV_Q8_BLOCK + i]));
+        const float s = m / 127.0f;
+        sc[bi] = s;
+        for (int i = 0; i < MK_KV_Q8_BLOCK; ++i)
+          q[bi * MK_KV_Q8_BLOCK + i] = (signed char)(int)(s > 0.f ? std::nearbyint(in[bi * MK_KV_Q8_BLOCK + i] / s) : 0.f);
+      }
+      HIPCHK(ctx, hipMemcpy(ctx->ws + (v ? lo.Vs : lo.Ks), sc.data(), nb * 4, hipMemcpyHostToDevice));
+    }
+    HIPCHK(ctx, hipMemcpy(ctx->ws + (v ? lo.Vc : lo.Kc), raw.data(), raw.size(), hipMemcpyHostToDevice));
   }
   return MK_OK;
 }

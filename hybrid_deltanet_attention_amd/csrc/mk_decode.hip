@@ -30,9 +30,11 @@ namespace {
 // compile-time constant, so divisions and trip counts fold) and once generically (sizes read from
 // the parameters); the host picks the instance that matches the model.
 // ------------------------------------------------------------------------------------------
-template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_>
+template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, bool KV_COMPACT>
 __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
   MkDecodeParams p = p0;
+  // instances for an FP32 KV cache compile without the compact-row code
+  if (!KV_COMPACT) p.kvt = MK_KV_F32;
   if (D_) p.D = D_;
   if (FFN_) p.ffn = FFN_;
   if (H_) p.H = H_;
@@ -154,9 +156,9 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
       // K/V rows of the first two work items -> stage A (free until the gate/up units), the
       // out-projection units -> stage B
       const int boff = 0;
-      for (int kc = 0; kc + 1 < kv_nbuf(p.hd, s.a_slots) || kc == 0; ++kc) {
+      for (int kc = 0; kc + 1 < kv_nbuf(p.hd, p.kvt, s.a_slots) || kc == 0; ++kc) {
         const int cn = att_chunk_at(p, NW, w, pos, kc);
-        if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd) * SLOT);
+        if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd, p.kvt) * SLOT);
       }
       gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
       gemv_stage(gout, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS);
@@ -296,15 +298,22 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
 
 // generic shape
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
-  decode_body<0, 0, 0, 0, 0, 0, 0, 0>(p);
+  decode_body<0, 0, 0, 0, 0, 0, 0, 0, false>(p);
 }
 // hidden 1024, FFN 3584, 16 DeltaNet heads of 128, 8 Q / 2 KV heads of 128 (the 0.8B-shaped hybrid)
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h1024(MkDecodeParams p) {
-  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128>(p);
+  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128, false>(p);
 }
 // hidden 256, FFN 768, 4 DeltaNet heads of 64, 4 Q / 2 KV heads of 64 (the tiny hybrid)
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h256(MkDecodeParams p) {
-  decode_body<256, 768, 4, 64, 64, 4, 2, 64>(p);
+  decode_body<256, 768, 4, 64, 64, 4, 2, 64, false>(p);
+}
+// binary16 or int8 KV cache: generic shape, and the 0.8B-shaped hybrid
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_kvc(MkDecodeParams p) {
+  decode_body<0, 0, 0, 0, 0, 0, 0, 0, true>(p);
+}
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h1024_kvc(MkDecodeParams p) {
+  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128, true>(p);
 }
 
 namespace {
@@ -315,7 +324,9 @@ bool shape_is(const MkDecodeParams& p) {
 }
 typedef void (*DecodeKernel)(MkDecodeParams);
 DecodeKernel pick_kernel(const MkDecodeParams& p) {
-  if (shape_is<1024, 3584, 16, 128, 128, 8, 2, 128>(p)) return mk_decode_kernel_h1024;
+  const bool h1024 = shape_is<1024, 3584, 16, 128, 128, 8, 2, 128>(p);
+  if (p.kvt != MK_KV_F32) return h1024 ? mk_decode_kernel_h1024_kvc : mk_decode_kernel_kvc;
+  if (h1024) return mk_decode_kernel_h1024;
   if (shape_is<256, 768, 4, 64, 64, 4, 2, 64>(p)) return mk_decode_kernel_h256;
   return mk_decode_kernel;
 }

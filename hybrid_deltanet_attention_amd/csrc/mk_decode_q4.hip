@@ -24,9 +24,10 @@ constexpr int Q4_STAGE_A = 32;  // KV chunk buffers (1 KB slots)
 constexpr int Q4_STAGE_B = 16;  // DeltaNet state rows
 __shared__ __attribute__((aligned(1024))) u32x4 g_stage_q4[(Q4_STAGE_A + Q4_STAGE_B) * SLOT];
 
-template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_>
+template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, bool KV_COMPACT>
 __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
   MkDecodeParams p = p0;
+  if (!KV_COMPACT) p.kvt = MK_KV_F32;
   if (D_) p.D = D_;
   if (FFN_) p.ffn = FFN_;
   if (H_) p.H = H_;
@@ -143,9 +144,9 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
                   [&](auto epi) { gemv_q4<true, false>(gin, s.xn, s.att, c0, q, streamer(), tr, epi); });
       tr.mark();
       // K/V rows of the first work items -> stage A
-      for (int kc = 0; kc + 1 < kv_nbuf(p.hd, s.a_slots) || kc == 0; ++kc) {
+      for (int kc = 0; kc + 1 < kv_nbuf(p.hd, p.kvt, s.a_slots) || kc == 0; ++kc) {
         const int cn = att_chunk_at(p, NW, w, pos, kc);
-        if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd) * SLOT);
+        if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd, p.kvt) * SLOT);
       }
       if (!att_items(p, L, cx, s, NW, w, pos, 0, tr)) return;
       tr.mark();
@@ -286,20 +287,27 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
 
 // generic shape
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel(MkDecodeParams p) {
-  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0>(p);
+  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0, false>(p);
 }
 // hidden 5120, FFN 17408, 32 DeltaNet heads of 128, 24 Q / 4 KV heads of 128 (the 27B-scale hybrid)
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_h5120(MkDecodeParams p) {
-  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128>(p);
+  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128, false>(p);
+}
+// binary16 or int8 KV cache
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_kvc(MkDecodeParams p) {
+  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0, true>(p);
+}
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_h5120_kvc(MkDecodeParams p) {
+  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128, true>(p);
 }
 
 namespace {
 typedef void (*DecodeKernel)(MkDecodeParams);
 DecodeKernel pick_q4_kernel(const MkDecodeParams& p) {
-  if (p.D == 5120 && p.ffn == 17408 && p.H == 32 && p.dk == 128 && p.dv == 128 && p.nq == 24 && p.nkv == 4 &&
-      p.hd == 128)
-    return mk_decode_q4_kernel_h5120;
-  return mk_decode_q4_kernel;
+  const bool h5120 = p.D == 5120 && p.ffn == 17408 && p.H == 32 && p.dk == 128 && p.dv == 128 && p.nq == 24 &&
+                     p.nkv == 4 && p.hd == 128;
+  if (p.kvt != MK_KV_F32) return h5120 ? mk_decode_q4_kernel_h5120_kvc : mk_decode_q4_kernel_kvc;
+  return h5120 ? mk_decode_q4_kernel_h5120 : mk_decode_q4_kernel;
 }
 }  // namespace
 

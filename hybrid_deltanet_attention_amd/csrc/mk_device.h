@@ -955,17 +955,28 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
 }
 
 // ------------------------------------------------------------------------ attention
-// K and V rows of work item `it` (16 positions of one KV head) -> stage slots [0, ks) (K) and
-// [ks, 2 ks) (V); hd/4 lanes per position.  Only positions already in the cache (< pos) are
-// copied; position pos comes from the exchange records.  Returns copies issued by this wave.
-__device__ __forceinline__ int kv_slots(int hd) {
-  const int pps = 64 / (hd >> 2);
+// KV cache rows.  A row holds the head_dim values of one position of one KV head in the cache type
+// kvt: FP32, binary16, or int8 codes with one FP32 scale per 32 values kept in a separate scale row
+// (Ks / Vs, hd / 32 floats per position).  Attention always works on FP32 rows in LDS: a chunk of
+// FP32 rows is copied there as is; compact rows are copied there compact and then expanded.
+__device__ __forceinline__ int kv_rowbytes(int hd, int kvt) {
+  return kvt == MK_KV_F32 ? 4 * hd : (kvt == MK_KV_F16 ? 2 * hd : hd);
+}
+// 1 KB stage slots holding the K (or V) rows of one 16-position chunk
+__device__ __forceinline__ int kv_slots(int hd, int kvt = MK_KV_F32) {
+  const int lpp = kv_rowbytes(hd, kvt) >> 4, pps = 64 / lpp;
   return (ATT_C + pps - 1) / pps;
 }
+// K and V rows (and, for int8 rows, the chunk's K and V scales in one more slot) of work item `it`
+// (16 positions of one KV head) -> stage slots [0, ks) (K), [ks, 2 ks) (V), 2 ks (scales: K at byte
+// 0, V at byte 512); a row is copied by rowbytes / 16 lanes.  Only positions already in the cache
+// (< pos) are copied; position pos comes from the exchange records.  Returns copies issued by this
+// wave.
 __device__ __forceinline__ int kv_stage(const MkDecodeParams& p, const MkLayerDev& L, int it, int pos,
                                         LS u32x4* stage) {
   if (!streamer()) return 0;
-  const int lpp = p.hd >> 2, pps = 64 / lpp, ks = kv_slots(p.hd);
+  const int kvt = p.kvt;
+  const int rb = kv_rowbytes(p.hd, kvt), lpp = rb >> 4, pps = 64 / lpp, ks = kv_slots(p.hd, kvt);
   const int c = it / p.nkv, g = it - c * p.nkv;
   const int j0 = c * ATT_C, jend = min(pos, j0 + ATT_C);
   int cnt = 0;
@@ -974,10 +985,113 @@ __device__ __forceinline__ int kv_stage(const MkDecodeParams& p, const MkLayerDe
     const int sl = q - v * ks;
     const int j = j0 + sl * pps + lane() / lpp;
     if (lane() < pps * lpp && j < jend)
-      dma16((v ? L.Vc : L.Kc) + ((size_t)g * p.max_ctx + j) * p.hd + (lane() % lpp) * 4, stage + q * SLOT);
+      dma16((const MK_G char*)(v ? L.Vc : L.Kc) + ((size_t)g * p.max_ctx + j) * rb + (lane() % lpp) * 16,
+            stage + q * SLOT);
     if (j0 + sl * pps < jend) ++cnt;
   }
+  if (kvt == MK_KV_Q8 && wave() == (2 * ks) % NCW) {
+    // the chunk's scale rows are contiguous: 16 positions x hd / 32 floats for K, then for V
+    const int fpp = p.hd / MK_KV_Q8_BLOCK, nl = (ATT_C * fpp + 3) >> 2;
+    const int v = lane() >= 32 ? 1 : 0, l = lane() - 32 * v;
+    if (l < nl && j0 + (4 * l) / fpp < jend)
+      dma16((v ? L.Vs : L.Ks) + ((size_t)g * p.max_ctx + j0) * fpp + 4 * l, stage + 2 * ks * SLOT);
+    if (j0 < jend) ++cnt;
+  }
   return cnt;
+}
+
+// LDS reads of a stage region (asm, each waits for its own reads; see the stage notes above)
+__device__ __forceinline__ u32x2 stage_b64(const LS void* p) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32 stage_b32(const LS void* p) {
+  u32 v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ void stage_write_f4(LS void* p, f32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ float half_bits_f32(u32 h) {
+  _Float16 x;
+  __builtin_memcpy(&x, &h, 2);
+  return (float)x;
+}
+__device__ __forceinline__ float f16_round(float x) { return (float)(_Float16)x; }
+__device__ __forceinline__ float i8_f32(u32 w, int b) { return (float)(int)(signed char)(w >> (8 * b)); }
+
+// The compact rows of a staged chunk (positions j0 .. j0 + nold - 1) -> FP32 rows laid out as a FP32
+// chunk buffer (what kv_stage copies for an FP32 cache), four values per thread at a time.
+__device__ __forceinline__ void kv_expand(int hd, int kvt, const LS u32x4* cmp, LS u32x4* f32, int nold) {
+  const int rb = kv_rowbytes(hd, kvt), ppsc = 1024 / rb, ksc = kv_slots(hd, kvt);
+  const int pps32 = 1024 / (4 * hd), ks32 = kv_slots(hd, MK_KV_F32);
+  const int n4 = hd >> 2, fpp = hd / MK_KV_Q8_BLOCK;
+  const LS char* cb = (const LS char*)cmp;
+  const LS float* scl = (const LS float*)(cmp + 2 * ksc * SLOT);
+  for (int x = tid(); x < 2 * nold * n4; x += MK_NT) {
+    const int v = x >= nold * n4 ? 1 : 0;
+    const int r = x - v * nold * n4, jj = r / n4, d = (r - jj * n4) * 4;
+    const LS char* src = cb + (v * ksc + jj / ppsc) * 1024 + (jj % ppsc) * rb;
+    f32x4 o;
+    if (kvt == MK_KV_F16) {
+      const u32x2 h = stage_b64(src + 2 * d);
+      o = f32x4{half_bits_f32(h.x & 0xffffu), half_bits_f32(h.x >> 16), half_bits_f32(h.y & 0xffffu),
+                half_bits_f32(h.y >> 16)};
+    } else {
+      const u32 c = stage_b32(src + d);
+      const float sc = __uint_as_float(stage_b32(scl + v * 128 + jj * fpp + d / MK_KV_Q8_BLOCK));
+      o = f32x4{i8_f32(c, 0) * sc, i8_f32(c, 1) * sc, i8_f32(c, 2) * sc, i8_f32(c, 3) * sc};
+    }
+    stage_write_f4((LS float*)f32 + (v * ks32 + jj / pps32) * 256 + (jj % pps32) * hd + d, o);
+  }
+}
+
+// Key and value rows of this launch's positions pos0 .. pos0 + nr - 1, gathered from the exchange
+// records in FP32 (row r of K at kb + r hd, of V at vb + r hd, in LDS), take the values the cache will
+// hold -- so this launch uses exactly what later launches read back -- and the streaming threads
+// append them to the cache.  scr: 2 nr hd / 32 floats of LDS scratch.  Contains workgroup barriers;
+// every thread calls it with the same arguments.
+__device__ __forceinline__ void kv_round_append(const MkDecodeParams& p, const MkLayerDev& L, LS float* kb,
+                                                LS float* vb, int nr, LS float* scr, int g, int pos0) {
+  const int hd = p.hd, kvt = p.kvt, nblk = hd / MK_KV_Q8_BLOCK, ne = nr * hd;
+  const size_t row0 = (size_t)g * p.max_ctx + pos0;
+  if (kvt == MK_KV_F16) {
+    for (int e = tid(); e < 2 * ne; e += MK_NT) {
+      const int v = e >= ne ? 1 : 0;
+      LS float* x = (v ? vb : kb) + (e - v * ne);
+      *x = f16_round(*x);
+    }
+    wg_bar();
+    if (streamer())
+      for (int e = tid(); e < 2 * ne; e += NCT) {
+        const int v = e >= ne ? 1 : 0, r = e - v * ne;
+        ((MK_G _Float16*)(v ? L.Vc : L.Kc))[row0 * hd + r] = (_Float16)(v ? vb : kb)[r];
+      }
+    return;
+  }
+  // int8: scale of each block of 32 = max |x| / 127, code = rint(x / scale) (0 when the block is 0)
+  for (int b = tid(); b < 2 * nr * nblk; b += MK_NT) {
+    const int v = b >= nr * nblk ? 1 : 0, rb = b - v * nr * nblk;
+    const LS float* x = (v ? vb : kb) + rb * MK_KV_Q8_BLOCK;
+    float m = 0.f;
+    for (int i = 0; i < MK_KV_Q8_BLOCK; ++i) m = fmaxf(m, fabsf(x[i]));
+    const float sc = m / 127.0f;
+    scr[b] = sc;
+    if (streamer()) (v ? L.Vs : L.Ks)[row0 * nblk + rb] = sc;
+  }
+  wg_bar();
+  if (streamer())
+    for (int e = tid(); e < 2 * ne; e += NCT) {
+      const int v = e >= ne ? 1 : 0, r = e - v * ne;
+      LS float* x = (v ? vb : kb) + r;
+      const float sc = scr[v * nr * nblk + r / MK_KV_Q8_BLOCK];
+      const float c = sc > 0.f ? rintf(*x / sc) : 0.f;
+      ((MK_G signed char*)(v ? L.Vc : L.Kc))[row0 * hd + r] = (signed char)(int)c;
+      *x = c * sc;
+    }
+  wg_bar();
 }
 
 // q/k/v rows in RoPE pair order: rotate q and k at position pos, append k and v to the cache
@@ -1006,8 +1120,10 @@ __device__ __forceinline__ void att_qkv_run(const MkDecodeParams& p, const MkLay
         const size_t co = ((size_t)hh * p.max_ctx + pos) * hd + m;
         ll_put(llk + hh * hd + m, cx.epoch, y1);
         ll_put(llk + hh * hd + m + half, cx.epoch, y2);
-        L.Kc[co] = y1;
-        L.Kc[co + half] = y2;
+        if (p.kvt == MK_KV_F32) {  // compact rows are appended by the attention item holding pos
+          L.Kc[co] = y1;
+          L.Kc[co + half] = y2;
+        }
       }
     } else {
       const int Q = P - nqp - nkp;
@@ -1015,8 +1131,10 @@ __device__ __forceinline__ void att_qkv_run(const MkDecodeParams& p, const MkLay
       const size_t co = ((size_t)hh * p.max_ctx + pos) * hd + m;
       ll_put(llv + hh * hd + m, cx.epoch, x1);
       ll_put(llv + hh * hd + m + half, cx.epoch, x2);
-      L.Vc[co] = x1;
-      L.Vc[co + half] = x2;
+      if (p.kvt == MK_KV_F32) {
+        L.Vc[co] = x1;
+        L.Vc[co + half] = x2;
+      }
     }
   });
 }
@@ -1030,10 +1148,17 @@ __device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDe
 // Split-K partial softmax attention.  Item = (chunk of 16 positions, KV head g); for each of the
 // gs query heads of group g it emits (max m, sum l, acc[hd]) over its positions.  Scores: one thread
 // per (head, position), a 16-lane DPP row per head for the max and the sum.
-// KV stage slots of one 16-position chunk, rounded to whole GEMV units
-__device__ __forceinline__ int kv_buf_slots(int hd) { return (2 * kv_slots(hd) + 3) & ~3; }
-// chunk buffers in stage A (up to 3: the copies of the next two chunks run while one is used)
-__device__ __forceinline__ int kv_nbuf(int hd, int a_slots) { return max(1, min(3, a_slots / kv_buf_slots(hd))); }
+// KV stage slots of one 16-position chunk (K rows, V rows, and for int8 rows a slot of scales),
+// rounded to whole GEMV units
+__device__ __forceinline__ int kv_buf_slots(int hd, int kvt = MK_KV_F32) {
+  return (2 * kv_slots(hd, kvt) + (kvt == MK_KV_Q8 ? 1 : 0) + 3) & ~3;
+}
+// chunk buffers in stage A (up to 3: the copies of the next two chunks run while one is used); with
+// compact rows the FP32 buffer they are expanded into takes the space after them
+__device__ __forceinline__ int kv_nbuf(int hd, int kvt, int a_slots) {
+  const int room = kvt == MK_KV_F32 ? a_slots : a_slots - kv_buf_slots(hd);
+  return max(1, min(3, room / kv_buf_slots(hd, kvt)));
+}
 
 // Split-K attention over positions 0..pos.  A work item is (block of p.att_cpi 16-position chunks,
 // KV head g); item it = block * nkv + g.  Chunk by chunk, the item computes for each of the gs query
@@ -1073,8 +1198,11 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
   const int items = att_items_count(p, pos);
   const float scale = 1.0f / sqrtf((float)hd);
   const int lpp = hd >> 2, pps = 64 / lpp, ks = kv_slots(hd);
-  const int nb = kv_nbuf(hd, s.a_slots);
-  const int kvb = kv_buf_slots(hd);
+  const int kvt = p.kvt;
+  const int nb = kv_nbuf(hd, kvt, s.a_slots);
+  const int kvb = kv_buf_slots(hd, kvt);
+  // compact rows are expanded into the FP32 buffer after the chunk buffers
+  LS u32x4* const f32buf = s.stA + nb * kvb * SLOT;
   int cnt0 = 0, cnt1 = 0, cnt2 = 0;  // copies this wave issued for the chunk in buffers 0, 1, 2
   LS float* qv = s.att;                // [gs][hd]
   LS float* kpos = qv + gs * hd;       // [hd]
@@ -1095,7 +1223,7 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
     for (int c = c0; c < c1; ++c, ++k) {
       const int j0 = c * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
       const bool has_pos = j0 + nj == Lpos;
-      const LS float* stf = (const LS float*)(s.stA + (k % nb) * kvb * SLOT);
+      const LS float* stf = (const LS float*)(kvt == MK_KV_F32 ? s.stA + (k % nb) * kvb * SLOT : f32buf);
       int pending = 0;  // copies issued after this chunk's that may stay outstanding
       if (k > 0 || nb > 1) {
         const int kn = k + nb - 1, bn = kn % nb;
@@ -1126,6 +1254,11 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
       }
       tr.mark();
       if (wg_bar_or(s, !ok)) return false;
+      if (kvt != MK_KV_F32) {
+        kv_expand(hd, kvt, s.stA + (k % nb) * kvb * SLOT, f32buf, nj - (has_pos ? 1 : 0));
+        if (has_pos) kv_round_append(p, L, kpos, vpos, 1, pb, g, pos);  // barriers inside
+        else wg_bar();
+      }
       tr.mark();
       // scores, softmax numerators, row max and sum (whole rows of 16 lanes take part in the DPP)
       const int t = tid();

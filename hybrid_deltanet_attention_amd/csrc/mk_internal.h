@@ -40,6 +40,13 @@ typedef unsigned long long mk_u64;
 #define MK_MAX_GRID 1024
 // Positions one speculative-verify launch scores (the pending token and up to 5 drafts).
 #define MK_VERIFY_MAXT 6
+// KV cache element types (MkDecodeParams::kvt): rows of head_dim FP32 values; rows of binary16
+// values; rows of int8 codes with one FP32 scale per 32 values (value = code * scale) in Ks / Vs.
+#define MK_KV_F32 0
+#define MK_KV_F16 1
+#define MK_KV_Q8 2
+// values per int8 KV scale
+#define MK_KV_Q8_BLOCK 32
 // Bytes of the static exchange-record array behind mk_decode_step_noalloc (mk_noalloc.hip).
 #define MK_NOALLOC_SCRATCH_BYTES (16u << 20)
 
@@ -64,8 +71,10 @@ struct MkLayerDev {
   MK_G const uint16_t* w_down;   // [D][ffn]
   MK_G const uint16_t* g12;      // BF16 RMSNorm gains [2][D]: pre-mixer, then pre-FFN
   MK_G float* S;                 // DeltaNet: [H][dv][dk]
-  MK_G float* Kc;                // attention: [nkv][max_ctx][hd]
-  MK_G float* Vc;                // attention: [nkv][max_ctx][hd]
+  MK_G float* Kc;                // attention: [nkv][max_ctx][hd] elements of the cache type (kvt)
+  MK_G float* Vc;                // attention: [nkv][max_ctx][hd] elements of the cache type (kvt)
+  MK_G float* Ks;                // int8 cache: scales [nkv][max_ctx][hd / 32] of Kc (else null)
+  MK_G float* Vs;                // int8 cache: scales [nkv][max_ctx][hd / 32] of Vc (else null)
   MK_G mk_u64* ll_in;            // records. DeltaNet: [rows_in]; attention: q [nq*hd], k [nkv*hd], v [nkv*hd]
   MK_G mk_u64* ll_part;          // attention partial records [max_items][gs][hd + 2]
   MK_G mk_u64* ll_o;             // mixer outputs [H*dv] or [nq*hd]
@@ -110,6 +119,8 @@ struct MkDecodeParams {
   // weight format: 0 = BF16, 1 = Q4G32 (every matrix tiled in 80-byte (4 rows x 32 columns)
   // tiles of codes and (d, m) words; the norm gains stay BF16)
   int32_t wq4;
+  // KV cache element type: MK_KV_F32, MK_KV_F16 or MK_KV_Q8
+  int32_t kvt;
 };
 
 #ifdef __cplusplus
@@ -144,10 +155,16 @@ int mk_pf_gemm_res(const uint16_t* Ahi, const uint16_t* Alo, int lda, int M, int
 // (AB, wide keys only) are produced on the way
 int mk_pf_dn_scan(float* S, float* QK, float* AB, const float* Y, int ldy, int T, int H, int dk, int dv, float l2eps,
                   uint16_t* Ohi, uint16_t* Olo, int ldo, float* CH, void* stream);
-int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, int max_ctx, const float* rcos,
-                   const float* rsin, float* Q, float* Kc, float* Vc, void* stream);
-int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,
-                    int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, float* P, size_t p_floats, void* stream);
+// rotated k and v of the chunk's positions p0 + t -> K/V rows (kv_stride rows per head, row kv_pos0 + t)
+int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, const float* rcos,
+                   const float* rsin, float* Q, float* K, float* V, int kv_stride, int kv_pos0, void* stream);
+// FP32 rows [nkv][T][hd] -> the compact cache (kvt MK_KV_F16 or MK_KV_Q8) at positions p0 ..
+int mk_pf_kv_pack(const float* Kf, const float* Vf, int T, int nkv, int hd, int kvt, void* Kc, void* Vc, float* Ks,
+                  float* Vs, int max_ctx, int p0, void* stream);
+// causal attention over the cache (element type kvt; Ks / Vs the int8 scales, else NULL)
+int mk_pf_attention(const float* Q, const void* Kc, const void* Vc, int kvt, const float* Ks, const float* Vs, int T,
+                    int p0, int nq, int nkv, int hd, int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, float* P,
+                    size_t p_floats, void* stream);
 int mk_pf_lmhead(const float* x, int D, const uint16_t* g, float eps, const uint16_t* E, int vocab, float* logits,
                  float* part, int nwg, void* stream);
 int mk_pf_finish(const float* part, int nwg, int32_t* next, MkCtl* ctl, int32_t pos, void* stream);

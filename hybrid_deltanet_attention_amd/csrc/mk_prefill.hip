@@ -927,12 +927,14 @@ __global__ void __launch_bounds__(CS_NT) pf_dn_cscan_mfma_kernel(float* __restri
 
 // ------------------------------------------------------------------------ attention
 // q/k/v columns of Y are in RoPE pair order per head (2m, 2m + 1) = (dim m, dim m + hd/2).  Rotate q
-// and k at positions p0 + t, write k and v to the cache, q to Q[t][head][hd] in natural order.
-__global__ void pf_att_rope_kernel(const float* __restrict__ Y, int ldy, int p0, int nq, int nkv, int hd, int max_ctx,
+// and k at positions p0 + t, write q to Q[t][head][hd] in natural order and k and v to the rows
+// kv_pos0 + t of K / V ([head][kv_stride][hd]: the FP32 cache itself, or the chunk's rows when the
+// cache is compact).
+__global__ void pf_att_rope_kernel(const float* __restrict__ Y, int ldy, int p0, int nq, int nkv, int hd,
                                    const float* __restrict__ rcos, const float* __restrict__ rsin, float* __restrict__ Q,
-                                   float* __restrict__ Kc, float* __restrict__ Vc) {
+                                   float* __restrict__ K, float* __restrict__ V, int kv_stride, int kv_pos0) {
   const int t = blockIdx.x;
-  const int half = hd / 2, pos = p0 + t;
+  const int half = hd / 2, pos = p0 + t, kp = kv_pos0 + t;
   const float* y = Y + (size_t)t * ldy;
   const int npairs = (nq + 2 * nkv) * half;
   for (int P = threadIdx.x; P < npairs; P += blockDim.x) {
@@ -946,14 +948,44 @@ __global__ void pf_att_rope_kernel(const float* __restrict__ Y, int ldy, int p0,
         qo[m] = y1;
         qo[m + half] = y2;
       } else {
-        float* ko = Kc + ((size_t)(hh - nq) * max_ctx + pos) * hd;
+        float* ko = K + ((size_t)(hh - nq) * kv_stride + kp) * hd;
         ko[m] = y1;
         ko[m + half] = y2;
       }
     } else {
-      float* vo = Vc + ((size_t)(hh - nq - nkv) * max_ctx + pos) * hd;
+      float* vo = V + ((size_t)(hh - nq - nkv) * kv_stride + kp) * hd;
       vo[m] = x1;
       vo[m + half] = x2;
+    }
+  }
+}
+
+// A compact KV cache's rows at positions p0 .. p0 + T - 1 from the chunk's FP32 rows [nkv][T][hd]:
+// binary16 (nearest), or int8 codes with one scale per 32 values (s = max|x| / 127, code =
+// rint(x / s)), exactly as the decode kernels form them.  One workgroup per (position, KV head); a
+// block of 32 values is 32 consecutive lanes of one wave.
+__global__ void __launch_bounds__(256) pf_kv_pack_kernel(const float* __restrict__ Kf, const float* __restrict__ Vf,
+                                                         int T, int hd, int kvt, void* __restrict__ Kc,
+                                                         void* __restrict__ Vc, float* __restrict__ Ks,
+                                                         float* __restrict__ Vs, int max_ctx, int p0) {
+  const int t = blockIdx.x, g = blockIdx.y;
+  const size_t src = ((size_t)g * T + t) * hd, dst = ((size_t)g * max_ctx + p0 + t) * hd;
+  for (int e0 = 0; e0 < 2 * hd; e0 += blockDim.x) {
+    const int e = e0 + (int)threadIdx.x;  // every lane of a block of 32 takes part in its reduction
+    const bool in = e < 2 * hd;
+    const int v = e >= hd ? 1 : 0, d = e - v * hd;
+    const float x = in ? (v ? Vf : Kf)[src + d] : 0.f;
+    if (kvt == MK_KV_F16) {
+      if (in) ((_Float16*)(v ? Vc : Kc))[dst + d] = (_Float16)x;
+    } else {
+      float m = fabsf(x);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+      const float sc = m / 127.0f;
+      if (in) {
+        ((signed char*)(v ? Vc : Kc))[dst + d] = (signed char)(int)(sc > 0.f ? rintf(x / sc) : 0.f);
+        if ((d & (MK_KV_Q8_BLOCK - 1)) == 0) (v ? Vs : Ks)[dst / MK_KV_Q8_BLOCK + d / MK_KV_Q8_BLOCK] = sc;
+      }
     }
   }
 }
@@ -1143,9 +1175,10 @@ __device__ __forceinline__ void split8(const float (&v)[8], bf16x8& h, bf16x8& l
   lo = __builtin_bit_cast(bf16x8, lw);
 }
 
-template <int HD>
-__global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restrict__ Q, const float* __restrict__ Kc,
-                                                           const float* __restrict__ Vc, int T, int p0, int nq, int nkv,
+template <int HD, int KVT>
+__global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restrict__ Q, const void* __restrict__ Kc,
+                                                           const void* __restrict__ Vc, const float* __restrict__ Ks,
+                                                           const float* __restrict__ Vs, int T, int p0, int nq, int nkv,
                                                            int max_ctx, uint16_t* __restrict__ Ohi,
                                                            uint16_t* __restrict__ Olo, int ldo, int nsplit,
                                                            float* __restrict__ part) {
@@ -1203,8 +1236,22 @@ __global__ void __launch_bounds__(256) pf_attn_mfma_kernel(const float* __restri
       const int key = e / HD, d = e - key * HD;
       const int j = min(blk * 32 + key, jend - 1);
       const size_t gi = ((size_t)g * max_ctx + j) * HD + d;
-      kr[i] = *(const f32x4*)(Kc + gi);
-      vr[i] = *(const f32x4*)(Vc + gi);
+      if (KVT == MK_KV_F32) {
+        kr[i] = *(const f32x4*)((const float*)Kc + gi);
+        vr[i] = *(const f32x4*)((const float*)Vc + gi);
+      } else if (KVT == MK_KV_F16) {
+        const _Float16* kh = (const _Float16*)Kc + gi;
+        const _Float16* vh = (const _Float16*)Vc + gi;
+        kr[i] = f32x4{(float)kh[0], (float)kh[1], (float)kh[2], (float)kh[3]};
+        vr[i] = f32x4{(float)vh[0], (float)vh[1], (float)vh[2], (float)vh[3]};
+      } else {
+        const u32 kq = *(const u32*)((const signed char*)Kc + gi), vq = *(const u32*)((const signed char*)Vc + gi);
+        const float ks = Ks[gi / MK_KV_Q8_BLOCK], vs = Vs[gi / MK_KV_Q8_BLOCK];
+        kr[i] = f32x4{(float)(int)(signed char)kq * ks, (float)(int)(signed char)(kq >> 8) * ks,
+                      (float)(int)(signed char)(kq >> 16) * ks, (float)(int)(signed char)(kq >> 24) * ks};
+        vr[i] = f32x4{(float)(int)(signed char)vq * vs, (float)(int)(signed char)(vq >> 8) * vs,
+                      (float)(int)(signed char)(vq >> 16) * vs, (float)(int)(signed char)(vq >> 24) * vs};
+      }
     }
   };
   auto store_blk = [&]() {
@@ -1601,16 +1648,24 @@ extern "C" int mk_pf_dn_scan(float* S, float* QK, float* AB, const float* Y, int
   return MK_LAUNCH_OK();
 }
 
-extern "C" int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, int max_ctx,
-                              const float* rcos, const float* rsin, float* Q, float* Kc, float* Vc, void* stream) {
-  hipLaunchKernelGGL(pf_att_rope_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, Y, ldy, p0, nq, nkv, hd, max_ctx,
-                     rcos, rsin, Q, Kc, Vc);
+extern "C" int mk_pf_att_rope(const float* Y, int ldy, int T, int p0, int nq, int nkv, int hd, const float* rcos,
+                              const float* rsin, float* Q, float* K, float* V, int kv_stride, int kv_pos0,
+                              void* stream) {
+  hipLaunchKernelGGL(pf_att_rope_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, Y, ldy, p0, nq, nkv, hd, rcos,
+                     rsin, Q, K, V, kv_stride, kv_pos0);
   return MK_LAUNCH_OK();
 }
 
-extern "C" int mk_pf_attention(const float* Q, const float* Kc, const float* Vc, int T, int p0, int nq, int nkv, int hd,
-                               int max_ctx, uint16_t* Ohi, uint16_t* Olo, int ldo, float* P, size_t p_floats,
-                               void* stream) {
+extern "C" int mk_pf_kv_pack(const float* Kf, const float* Vf, int T, int nkv, int hd, int kvt, void* Kc, void* Vc,
+                             float* Ks, float* Vs, int max_ctx, int p0, void* stream) {
+  hipLaunchKernelGGL(pf_kv_pack_kernel, dim3(T, nkv), dim3(256), 0, (hipStream_t)stream, Kf, Vf, T, hd, kvt, Kc, Vc,
+                     Ks, Vs, max_ctx, p0);
+  return MK_LAUNCH_OK();
+}
+
+extern "C" int mk_pf_attention(const float* Q, const void* Kc, const void* Vc, int kvt, const float* Ks,
+                               const float* Vs, int T, int p0, int nq, int nkv, int hd, int max_ctx, uint16_t* Ohi,
+                               uint16_t* Olo, int ldo, float* P, size_t p_floats, void* stream) {
   if (hd == 64 || hd == 128) {
     // MFMA path: workgroups = KV heads x groups of 4 query heads x 32-query tiles x key splits.
     // Split the keys when that brings the grid nearer one workgroup per compute unit (256), as far
@@ -1624,31 +1679,41 @@ extern "C" int mk_pf_attention(const float* Q, const float* Kc, const float* Vc,
     const dim3 grid(base_wg * nsplit);
     const size_t lds = (size_t)4 * 32 * hd * 2 + 4 * (4 * 32 * 32 + 2 * 32 * 4);
     hipStream_t st = (hipStream_t)stream;
-    if (hd == 64)
-      hipLaunchKernelGGL(pf_attn_mfma_kernel<64>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo,
-                         nsplit, P);
-    else
-      hipLaunchKernelGGL(pf_attn_mfma_kernel<128>, grid, dim3(256), lds, st, Q, Kc, Vc, T, p0, nq, nkv, max_ctx, Ohi, Olo, ldo,
-                         nsplit, P);
+#define MK_PF_ATT(HDV, KVTV)                                                                                        \
+  hipLaunchKernelGGL((pf_attn_mfma_kernel<HDV, KVTV>), grid, dim3(256), lds, st, Q, Kc, Vc, Ks, Vs, T, p0, nq, nkv, \
+                     max_ctx, Ohi, Olo, ldo, nsplit, P)
+    if (hd == 64) {
+      if (kvt == MK_KV_F16) MK_PF_ATT(64, MK_KV_F16);
+      else if (kvt == MK_KV_Q8) MK_PF_ATT(64, MK_KV_Q8);
+      else MK_PF_ATT(64, MK_KV_F32);
+    } else {
+      if (kvt == MK_KV_F16) MK_PF_ATT(128, MK_KV_F16);
+      else if (kvt == MK_KV_Q8) MK_PF_ATT(128, MK_KV_Q8);
+      else MK_PF_ATT(128, MK_KV_F32);
+    }
+#undef MK_PF_ATT
     if (nsplit > 1)
       hipLaunchKernelGGL(pf_attn_merge_kernel, dim3(T, nq), dim3(hd <= 128 ? 128 : 256), 0, st, P, T, nq, hd, nsplit, Ohi,
                          Olo, ldo);
     return MK_LAUNCH_OK();
   }
+  if (kvt != MK_KV_F32) return -1;  // compact caches take the matrix-core path or token-by-token decode
   const int gs = nq / nkv, QB = 16 / gs;
   const int lpp = hd / 4, pps = 64 / lpp, nsl = (KB + pps - 1) / pps;
   const size_t lds = ((size_t)2 * 2 * nsl * 256 + 16 * HDM + 16 * KB + 16) * 4;
   const dim3 grid(nkv * ((T + QB - 1) / QB));
   hipStream_t s = (hipStream_t)stream;
   const int dpl = (hd + 15) / 16;
+  const float* Kf = (const float*)Kc;
+  const float* Vf = (const float*)Vc;
   if (dpl <= 2)
-    hipLaunchKernelGGL(pf_attention_kernel<2>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
+    hipLaunchKernelGGL(pf_attention_kernel<2>, grid, dim3(256), lds, s, Q, Kf, Vf, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
   else if (dpl <= 4)
-    hipLaunchKernelGGL(pf_attention_kernel<4>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
+    hipLaunchKernelGGL(pf_attention_kernel<4>, grid, dim3(256), lds, s, Q, Kf, Vf, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
   else if (dpl <= 8)
-    hipLaunchKernelGGL(pf_attention_kernel<8>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
+    hipLaunchKernelGGL(pf_attention_kernel<8>, grid, dim3(256), lds, s, Q, Kf, Vf, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo, ldo);
   else
-    hipLaunchKernelGGL(pf_attention_kernel<16>, grid, dim3(256), lds, s, Q, Kc, Vc, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo,
+    hipLaunchKernelGGL(pf_attention_kernel<16>, grid, dim3(256), lds, s, Q, Kf, Vf, T, p0, nq, nkv, hd, max_ctx, Ohi, Olo,
                        ldo);
   return MK_LAUNCH_OK();
 }

@@ -354,8 +354,10 @@ __device__ __forceinline__ void att_qkv_v(const MkDecodeParams& p, const MkLayer
         const size_t co = ((size_t)hh * p.max_ctx + pos + t) * hd + m;
         ll_put(llk + hh * hd + m, cx.epoch, y1);
         ll_put(llk + hh * hd + m + half, cx.epoch, y2);
-        L.Kc[co] = y1;
-        L.Kc[co + half] = y2;
+        if (p.kvt == MK_KV_F32) {  // compact rows are appended by the attention items
+          L.Kc[co] = y1;
+          L.Kc[co + half] = y2;
+        }
       }
     } else {
       const int Q = P - nqp - nkp;
@@ -363,8 +365,10 @@ __device__ __forceinline__ void att_qkv_v(const MkDecodeParams& p, const MkLayer
       const size_t co = ((size_t)hh * p.max_ctx + pos + t) * hd + m;
       ll_put(llv + hh * hd + m, cx.epoch, x1);
       ll_put(llv + hh * hd + m + half, cx.epoch, x2);
-      L.Vc[co] = x1;
-      L.Vc[co + half] = x2;
+      if (p.kvt == MK_KV_F32) {
+        L.Vc[co] = x1;
+        L.Vc[co + half] = x2;
+      }
     }
   });
 }
@@ -435,13 +439,33 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
         for (int x = tid(); x < nold * h4; x += NCT) {
           const int jj = x / h4, d = (x - jj * h4) * 4;
           const size_t gi = ((size_t)g * p.max_ctx + j0 + jj) * hd + d;
-          const f32x4 kk = *(const MK_G f32x4*)(L.Kc + gi);
-          const f32x4 vv = *(const MK_G f32x4*)(L.Vc + gi);
+          f32x4 kk, vv;
+          if (p.kvt == MK_KV_F32) {
+            kk = *(const MK_G f32x4*)(L.Kc + gi);
+            vv = *(const MK_G f32x4*)(L.Vc + gi);
+          } else if (p.kvt == MK_KV_F16) {
+            // the decode kernel's expansion of the same rows (mk_device.h, kv_expand)
+            const u32x2 a = *(const MK_G u32x2*)((const MK_G _Float16*)L.Kc + gi);
+            const u32x2 b = *(const MK_G u32x2*)((const MK_G _Float16*)L.Vc + gi);
+            kk = f32x4{half_bits_f32(a.x & 0xffffu), half_bits_f32(a.x >> 16), half_bits_f32(a.y & 0xffffu),
+                       half_bits_f32(a.y >> 16)};
+            vv = f32x4{half_bits_f32(b.x & 0xffffu), half_bits_f32(b.x >> 16), half_bits_f32(b.y & 0xffffu),
+                       half_bits_f32(b.y >> 16)};
+          } else {
+            const u32 a = *(const MK_G u32*)((const MK_G signed char*)L.Kc + gi);
+            const u32 b = *(const MK_G u32*)((const MK_G signed char*)L.Vc + gi);
+            const float ks = L.Ks[gi / MK_KV_Q8_BLOCK], vs = L.Vs[gi / MK_KV_Q8_BLOCK];
+            kk = f32x4{i8_f32(a, 0) * ks, i8_f32(a, 1) * ks, i8_f32(a, 2) * ks, i8_f32(a, 3) * ks};
+            vv = f32x4{i8_f32(b, 0) * vs, i8_f32(b, 1) * vs, i8_f32(b, 2) * vs, i8_f32(b, 3) * vs};
+          }
           *(LS f32x4*)(kc + jj * hd + d) = kk;
           *(LS f32x4*)(vc + jj * hd + d) = vv;
         }
       }
       if (wg_bar_or(s, !ok)) return false;
+      // this launch's positions in the chunk take the cache's values and are appended (barriers inside)
+      if (p.kvt != MK_KV_F32 && nnew > 0)
+        kv_round_append(p, L, kc + (jnew - j0) * hd, vc + (jnew - j0) * hd, nnew, pb, g, jnew);
       // scores, softmax numerators, row max and sum: one thread per (position, head, slot), whole
       // 16-lane rows
       const int nrow = (nt - tmin) * gs * C;
@@ -615,9 +639,10 @@ __device__ __forceinline__ void load_gains(const MK_G uint16_t* src, int n, LS u
   for (int i = tid(); i < (n >> 3); i += MK_NT) *(LS u32x4*)(dst + 8 * i) = *(const MK_G u32x4*)(src + 8 * i);
 }
 
-template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_>
+template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, bool KV_COMPACT>
 __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   MkDecodeParams p = p0;
+  if (!KV_COMPACT) p.kvt = MK_KV_F32;
   if (D_) p.D = D_;
   if (FFN_) p.ffn = FFN_;
   if (H_) p.H = H_;
@@ -912,16 +937,21 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
 }  // namespace
 
 __global__ void __launch_bounds__(MK_NT, 1) mk_verify_kernel(MkDecodeParams p) {
-  verify_body<0, 0, 0, 0, 0, 0, 0, 0>(p);
+  verify_body<0, 0, 0, 0, 0, 0, 0, 0, false>(p);
 }
 // hidden 1024, FFN 3584, 16 DeltaNet heads of 128, 8 Q / 2 KV heads of 128 (the 0.8B-shaped hybrid)
 __global__ void __launch_bounds__(MK_NT, 1) mk_verify_kernel_h1024(MkDecodeParams p) {
-  verify_body<1024, 3584, 16, 128, 128, 8, 2, 128>(p);
+  verify_body<1024, 3584, 16, 128, 128, 8, 2, 128, false>(p);
+}
+// binary16 or int8 KV cache
+__global__ void __launch_bounds__(MK_NT, 1) mk_verify_kernel_kvc(MkDecodeParams p) {
+  verify_body<0, 0, 0, 0, 0, 0, 0, 0, true>(p);
 }
 
 namespace {
 typedef void (*VerifyKernel)(MkDecodeParams);
 VerifyKernel pick_verify(const MkDecodeParams& p) {
+  if (p.kvt != MK_KV_F32) return mk_verify_kernel_kvc;
   if (p.D == 1024 && p.ffn == 3584 && p.H == 16 && p.dk == 128 && p.dv == 128 && p.nq == 8 && p.nkv == 2 &&
       p.hd == 128)
     return mk_verify_kernel_h1024;

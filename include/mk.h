@@ -56,12 +56,21 @@ enum mk_status {
  * 4-bit code q.  The mk_tensor shape is the logical [R, K].
  * Values: MK_I32 (4) names int32 data such as token ids, so the 4-bit format takes the next free
  * value, 5; the numbers are part of the ABI and never change. */
-enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4, MK_Q4G32 = 5 };
+enum mk_dtype { MK_BF16 = 1, MK_F32 = 2, MK_F16 = 3, MK_I32 = 4, MK_Q4G32 = 5, MK_Q8 = 6 };
+/* MK_Q8 (a KV cache type): each key or value row of head_dim values is stored as int8 codes, and each
+ * block of 32 consecutive values of a row has one FP32 scale s = max|x| / 127 of that block; a value
+ * is stored as rint(x / s) (0 when s = 0) and read back as code * s. */
 
 /* Model shape.  All fields are required (there is no default constructor on purpose).
  * Constraints checked by mk_workspace_bytes / mk_create: every size > 0; hidden, ffn, H*dk and
  * H*dv multiples of 8; dk, dv even and head_dim a multiple of 4, all <= 256; n_q_heads a multiple of n_kv_heads;
- * attn_slot < period; tied_embeddings == 1; kv_dtype == MK_F32;
+ * attn_slot < period; tied_embeddings == 1;
+ * kv_dtype: MK_F32, MK_F16 (head_dim a multiple of 8) or MK_Q8 (head_dim a multiple of 32) -- the
+ * element type of the KV cache.  The follow-up post on the 27B megakernel (page 3, "Limits"
+ * paragraph) keeps its cache in fp16 up to about 80K positions and in an 8-bit format above; a
+ * context picks one type for its whole cache.  Keys and values are rounded to the cache type as
+ * they are appended, and attention (the appending position included) reads the stored values.
+ * With 4-bit weights a compact cache needs head_dim <= 128;
  * 0 <= max_verify_k <= 5 (each unit adds one position's records, one DeltaNet state snapshot and
  * LDS; mk_create returns MK_E_OCCUPANCY if the verify kernel's LDS does not fit).
  * weight_dtype is MK_BF16 or MK_Q4G32.  MK_Q4G32 also needs hidden, ffn, H*dv and nq*head_dim to
@@ -180,7 +189,9 @@ int mk_get_position(mk_ctx* ctx, int32_t* pos);
 
 /* Copy one layer's recurrent state to/from host memory (synchronises).  DeltaNet layer: S as
  * FP32 [dn_heads][dn_dv][dn_dk] (row i of head h maps keys to value dimension i).  Attention
- * layer: K then V as FP32 [n_kv_heads][max_ctx][head_dim] each (keys already rotated).
+ * layer: K then V as FP32 [n_kv_heads][max_ctx][head_dim] each (keys already rotated); with a
+ * compact cache the stored values decoded to FP32 on read, and FP32 values rounded to the cache
+ * type (nearest binary16, or int8 blocks formed as above) on write.
  * mk_state_bytes gives the byte count for `layer`, or 0 if it is out of range. */
 size_t mk_state_bytes(const mk_ctx* ctx, int32_t layer);
 int mk_read_state(mk_ctx* ctx, int32_t layer, void* dst);

@@ -34,12 +34,12 @@ matrix) -- are pinned against each other and against closed forms in
 from .primitives import rmsnorm, l2norm, sigmoid, softplus, silu, rope_angles, rope, softmax, bf16_decode
 from .deltanet import (gates, delta_step, delta_recurrent, delta_explicit_product,
                        delta_parallel, delta_chunked)
-from .attention import attend_one, causal_attention
+from .attention import attend_one, causal_attention, kv_round, KV_DTYPES
 from .model import Oracle
 from .metrics import rel_l2, mean_kl, top1_agreement
 from .quant import q4g32_dequant, q4g32_dequant_rows
 
 __all__ = ["rmsnorm", "l2norm", "sigmoid", "softplus", "silu", "rope_angles", "rope", "softmax",
            "bf16_decode", "gates", "delta_step", "delta_recurrent", "delta_explicit_product",
-           "delta_parallel", "delta_chunked", "attend_one", "causal_attention", "Oracle",
+           "delta_parallel", "delta_chunked", "attend_one", "causal_attention", "kv_round", "KV_DTYPES", "Oracle",
            "rel_l2", "mean_kl", "top1_agreement", "q4g32_dequant", "q4g32_dequant_rows"]

@@ -48,3 +48,35 @@ def causal_attention(Q, K, V):
         s = np.where(mask, s, -np.inf)
         O[:, i, :] = softmax(s, axis=-1) @ V[:, g, :]
     return O
+
+
+KV_DTYPES = ("f32", "f16", "q8")
+Q8_BLOCK = 32
+
+
+def kv_round(x, kv: str):
+    """Values a key or value row takes once stored in the KV cache.
+
+    The pages keep the 27B model's cache in fp16 up to about 80K positions and in an 8-bit format
+    above (Reddit follow-up on the 27B model, "Limits" paragraph).  "f32": unchanged.  "f16": the
+    IEEE binary16 value nearest the float32 value (ties to even).  "q8": blocks of 32 consecutive
+    values along the last axis share a float32 scale s = max|x| / 127; each value is stored as the
+    integer code rint(x / s) (ties to even; 0 when s = 0) and read back as code * s.  The rounding
+    decisions are taken in float32, the precision of the cache; the result is returned in x's dtype."""
+    x = np.asarray(x)
+    if kv == "f32":
+        return x
+    x32 = x.astype(np.float32)
+    if kv == "f16":
+        return x32.astype(np.float16).astype(x.dtype)
+    if kv != "q8":
+        raise ValueError(f"unknown KV cache type {kv!r}")
+    hd = x.shape[-1]
+    if hd % Q8_BLOCK:
+        raise ValueError("q8 cache rows need a multiple of 32 values")
+    b = x32.reshape(*x.shape[:-1], hd // Q8_BLOCK, Q8_BLOCK)
+    s = np.max(np.abs(b), axis=-1, keepdims=True) / np.float32(127.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        code = np.where(s > 0, np.rint(b / np.where(s > 0, s, np.float32(1.0))), np.float32(0.0))
+    return (code * s).reshape(x.shape).astype(x.dtype)
+

@@ -23,7 +23,7 @@ import numpy as np
 
 from .primitives import bf16_decode, rmsnorm, l2norm, silu, rope_angles, rope
 from .deltanet import gates, delta_step, delta_parallel
-from .attention import attend_one, causal_attention
+from .attention import attend_one, causal_attention, kv_round, KV_DTYPES
 from .quant import q4g32_dequant, q4g32_dequant_rows
 
 
@@ -91,9 +91,16 @@ class Weights:
 
 
 class Oracle:
-    def __init__(self, cfg, weight_bits: dict, dtype=np.float64):
+    """kv: the KV cache's storage type ("f32", "f16" or "q8", see ``attention.kv_round``); keys and
+    values are rounded to it when they enter the cache, so attention, including the current
+    position's own key and value, always sees the stored values."""
+
+    def __init__(self, cfg, weight_bits: dict, dtype=np.float64, kv: str = "f32"):
+        if kv not in KV_DTYPES:
+            raise ValueError(f"unknown KV cache type {kv!r}")
         self.cfg = cfg
         self.dtype = dtype
+        self.kv = kv
         self.W = Weights(cfg, weight_bits, dtype)
         self.reset()
 
@@ -168,8 +175,8 @@ class Oracle:
             h = rmsnorm(x, self.W[f"l{l}.norm1"], c.rms_eps)
             if c.is_attention(l):
                 q, k, v = self._attn_project(l, h, p)
-                self.Kc[l][:, p] = k
-                self.Vc[l][:, p] = v
+                self.Kc[l][:, p] = kv_round(k, self.kv)
+                self.Vc[l][:, p] = kv_round(v, self.kv)
                 o = attend_one(q, self.Kc[l][:, : p + 1], self.Vc[l][:, : p + 1])
                 x = x + o.reshape(-1) @ self.W[f"l{l}.attn.wo"].T
             else:
@@ -194,6 +201,7 @@ class Oracle:
             Hn = rmsnorm(X, self.W[f"l{l}.norm1"], c.rms_eps)
             if c.is_attention(l):
                 Q, K, V = self._attn_project(l, Hn, positions)
+                K, V = kv_round(K, self.kv), kv_round(V, self.kv)
                 O = causal_attention(Q, K, V)
                 KV_out[l] = (np.transpose(K, (1, 0, 2)).copy(), np.transpose(V, (1, 0, 2)).copy())
                 X = X + O.reshape(T, -1) @ self.W[f"l{l}.attn.wo"].T

@@ -13,10 +13,11 @@ def torch_cuda():
     return torch
 
 
-def new_model(cfg, weights, grid=None, weight_dtype=None):
+def new_model(cfg, weights, grid=None, weight_dtype=None, kv_dtype=None, max_verify_k=0):
     from hybrid_deltanet_attention_amd import Model
-    from hybrid_deltanet_attention_amd.binding import MK_BF16
-    m = Model(cfg, device=0, weight_dtype=MK_BF16 if weight_dtype is None else weight_dtype)
+    from hybrid_deltanet_attention_amd.binding import MK_BF16, MK_F32
+    m = Model(cfg, device=0, weight_dtype=MK_BF16 if weight_dtype is None else weight_dtype,
+              kv_dtype=MK_F32 if kv_dtype is None else kv_dtype, max_verify_k=max_verify_k)
     m.mk_load_weights(weights)
     if grid is not None:
         m.mk_set_grid(grid)
@@ -47,9 +48,9 @@ def run_teacher_forced(m, prompt, fed, want_logits=True):
     return pre_logits, pre_next, out_l, out_n
 
 
-def oracle_reference(cfg, weights, prompt, n_steps, cache_bytes=None):
+def oracle_reference(cfg, weights, prompt, n_steps, cache_bytes=None, kv="f32"):
     from oracle import Oracle
-    o = Oracle(cfg, weights)
+    o = Oracle(cfg, weights, kv=kv)
     if cache_bytes is not None:
         o.W.cache_left = cache_bytes  # keep every decoded 4-bit matrix (wide models)
     fed, logits, last = o.greedy(prompt, n_steps)

@@ -464,6 +464,65 @@ def pin_ffn_linear_in_up_projection():
         "the gate enters through silu, not linearly"
 
 
+def pin_kv_f16_rounding():
+    """binary16 keeps 10 fraction bits: 1 + 2^-11 lies halfway between 1 and 1 + 2^-10 and goes to
+    the even neighbour 1; 1 + 3 * 2^-11 lies halfway between 1 + 2^-10 and 1 + 2^-9 and goes to
+    1 + 2^-9; 65504 is the largest finite value; 2^-24 is the smallest subnormal and 2^-26 rounds
+    to 0."""
+    x = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65504.0, -3.0, 2.0 ** -24, 2.0 ** -26])
+    _close(att.kv_round(x, "f16"), [1.0, 1 + 2.0 ** -9, 65504.0, -3.0, 2.0 ** -24, 0.0], 0.0, "f16 cache rounding")
+    _close(att.kv_round(x, "f32"), x, 0.0, "f32 cache keeps the values")
+
+
+def pin_kv_q8_hand_example():
+    """int8 cache rows: blocks of 32 share s = max|x| / 127 and store rint(x / s), ties to even.
+    Block 0 has max 127, so s = 1 and the codes are the values rounded (0.5 -> 0, 1.5 -> 2,
+    2.5 -> 2, -63.5 -> -64); block 1 is zero; block 2 is block 0 times 2^-7 (same codes, s = 2^-7);
+    block 3 has a single nonzero value -4 (s = 4 / 127, code -127)."""
+    row = np.zeros(128)
+    row[:6] = [127.0, -63.5, 0.5, 1.5, 2.5, -0.5]
+    row[64:70] = row[:6] * 2.0 ** -7
+    row[100] = -4.0
+    want = np.zeros(128)
+    want[:6] = [127.0, -64.0, 0.0, 2.0, 2.0, -0.0]
+    want[64:70] = want[:6] * 2.0 ** -7
+    want[100] = -4.0
+    got = att.kv_round(row, "q8")
+    _close(got, want, 1e-6, "q8 hand example")
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((5, 64)) * np.array([1.0, 1e-3, 30.0, 1.0, 7.0])[:, None]
+    y = att.kv_round(x, "q8")
+    s = np.abs(x.reshape(5, 2, 32)).max(-1) / 127
+    assert np.all(np.abs(y - x).reshape(5, 2, 32) <= s[..., None] * (0.5 + 1e-6)), "q8 error above half a step"
+
+
+def pin_model_kv_cache_types():
+    """with an f16 or q8 cache, token-by-token decode still equals the whole-sequence form (both
+    round keys and values as they enter the cache), the cache holds representable values only,
+    and the logits move away from the f32 cache's by a small amount"""
+    cfg = _tiny()
+    W = synth.make_weights(cfg, 24)
+    toks = synth.make_prompt(cfg.vocab, 10, 24)
+    base = om.Oracle(cfg, W).forward(toks)["logits"]
+    for kv in ("f16", "q8"):
+        o = om.Oracle(cfg, W, kv=kv)
+        fwd = o.forward(toks, logits="all")
+        step_logits = np.stack([o.step(t) for t in toks])
+        _close(step_logits, fwd["logits"], 1e-10, f"{kv}: logits O1 vs O2")
+        for l, (K, V) in fwd["KV"].items():
+            _close(o.Kc[l][:, :10], K, 1e-12, f"{kv}: K layer {l}")
+            _close(o.Vc[l][:, :10], V, 1e-12, f"{kv}: V layer {l}")
+            if kv == "f16":
+                assert np.array_equal(K, K.astype(np.float16).astype(np.float64)), "f16 cache holds binary16 values"
+            else:
+                b = K.reshape(*K.shape[:-1], -1, 32)
+                sc = np.abs(b).max(-1, keepdims=True) / 127
+                q = np.where(sc > 0, b / np.where(sc > 0, sc, 1), 0)
+                assert np.max(np.abs(q - np.rint(q))) < 1e-4, "q8 cache holds code * scale"
+        d = float(np.max(np.abs(fwd["logits"] - base)))
+        assert 0.0 < d < 1e-2 * float(np.max(np.abs(base))), f"{kv}: cache rounding moves logits by {d:.2e}"
+
+
 def pin_argmax_lowest_index():
     lg = np.array([0.1, 0.7, 0.3, 0.7, -1.0])
     assert om.Oracle.argmax(lg) == 1

@@ -168,6 +168,26 @@ def _attn_project_variant(rope_v=False, swap_kv=False, q_unrotated=False):
     return project
 
 
+def _kv_round_variant(mode):
+    def kv_round(x, kv):
+        x = np.asarray(x)
+        if kv == "f16" and mode == "f16_truncated":
+            b = x.astype(np.float32).astype(np.float16)
+            up = np.abs(b.astype(np.float32)) > np.abs(x.astype(np.float32))
+            b = np.where(up, np.nextafter(b, np.float16(0)), b)
+            return b.astype(x.dtype)
+        if kv == "q8" and mode in ("q8_floor", "q8_row_scale"):
+            x32 = x.astype(np.float32)
+            if mode == "q8_row_scale":
+                s = np.max(np.abs(x32), axis=-1, keepdims=True) / np.float32(127)
+                return (np.rint(x32 / np.where(s > 0, s, 1)) * s).astype(x.dtype)
+            b = x32.reshape(*x.shape[:-1], -1, 32)
+            s = np.max(np.abs(b), axis=-1, keepdims=True) / np.float32(127)
+            return (np.floor(b / np.where(s > 0, s, 1)) * s).reshape(x.shape).astype(x.dtype)
+        return _REAL_KV_ROUND(x, kv)
+    return kv_round
+
+
 _REAL_Q4_CODES = oq.q4g32_codes
 _REAL_Q4_SPLIT = oq.q4g32_split
 _REAL_STEP = dn.delta_step
@@ -175,6 +195,7 @@ _REAL_ROPE = prim.rope
 _REAL_RMS = prim.rmsnorm
 _REAL_ATTEND = att.attend_one
 _REAL_PAR = dn.delta_parallel
+_REAL_KV_ROUND = att.kv_round
 
 # (label, [(module, attribute), ...], replacement)
 MUTANTS = [
@@ -204,6 +225,9 @@ MUTANTS = [
     ("attention: RoPE applied to v", [(om.Oracle, "_attn_project")], _attn_project_variant(rope_v=True)),
     ("attention: k and v swapped", [(om.Oracle, "_attn_project")], _attn_project_variant(swap_kv=True)),
     ("attention: q left unrotated", [(om.Oracle, "_attn_project")], _attn_project_variant(q_unrotated=True)),
+    ("kv cache: f16 truncated", [(att, "kv_round"), (om, "kv_round")], _kv_round_variant("f16_truncated")),
+    ("kv cache: q8 codes floored", [(att, "kv_round"), (om, "kv_round")], _kv_round_variant("q8_floor")),
+    ("kv cache: q8 one scale per row", [(att, "kv_round"), (om, "kv_round")], _kv_round_variant("q8_row_scale")),
     ("q4: code half-words swapped", [(oq, "q4g32_codes")], _q4_codes_halves_swapped),
     ("q4: nibbles read in bit order", [(oq, "q4g32_codes")], _q4_codes_nibbles_in_order),
     ("q4: scale and offset swapped", [(oq, "q4g32_split")], _q4_split_params_swapped),
