@@ -97,6 +97,63 @@ def summarize_pmc(dirs: dict) -> dict:
             "bytes_per_launch": int(kf * 1024 * sf + kw * 1024 * sw)}
 
 
+SIMDS = 1024  # 256 compute units x 4 SIMDs
+MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES",
+                 "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def _kernel_durations(trace_dir):
+    """kernel name -> (calls, average ns) from a rocprofv3 --kernel-trace --stats csv folder"""
+    import csv
+    out = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]))
+    if not out:
+        raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
+    return out
+
+
+def _is_kernel(name: str, k: str) -> bool:
+    """a profiler's kernel name (with namespace, template arguments and signature) is kernel k"""
+    return any(pre + k + post in " " + name for pre in (" ", "::") for post in ("<", "("))
+
+
+def summarize_mfma(pmc_dir, trace_dir, kernels=("pf_gemm_kernel", "pf_dn_cscan_mfma_kernel", "pf_dn_cprep_kernel",
+                                                 "pf_attn_mfma_kernel"), clock_ghz: float = 2.4) -> str:
+    """Matrix-core counters per prefill kernel family.  MFMA FLOP = MOPS x 512.  SQ_VALU_MFMA_BUSY_CYCLES
+    counts matrix-core cycles at the peak rate (here 0.5 cycle per MOP, 1024 BF16 FLOP per SIMD and
+    cycle), summed over the 1024 SIMDs, so busy / (cycles x 1024) is the fraction of the matrix-core
+    peak a kernel reaches.  Two cycle counts: GRBM_GUI_ACTIVE (the csv sums it over the 8 XCDs;
+    rocprof's MfmaUtil takes the largest, about the sum / 8) and the kernel's average duration from
+    the kernel trace of the same command x the 2.4 GHz clock."""
+    rows = _counter_rows(pmc_dir)
+    durs = _kernel_durations(trace_dir)
+    lines = [f"{'kernel (all template instances)':26s} {'disp':>5s} {'MFMA GFLOP':>11s} {'BF16 MOPS':>9s} "
+             f"{'util(GUI) %':>11s} {'util(dur) %':>11s} {'avg us':>8s} {'MFMA TFLOP/s':>12s}"]
+    for k in kernels:
+        per = {}
+        for r in rows:
+            if _is_kernel(r["Kernel_Name"], k):
+                d = per.setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if not per:
+            continue
+        n = len(per)
+        mean = lambda c: float(np.mean([d.get(c, 0.0) for d in per.values()]))
+        mops_bf, mops_f32 = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean("SQ_INSTS_VALU_MFMA_MOPS_F32")
+        busy, gui = mean("SQ_VALU_MFMA_BUSY_CYCLES"), mean("GRBM_GUI_ACTIVE")
+        flop = (mops_bf + mops_f32) * 512
+        calls = sum(c for name, (c, _) in durs.items() if _is_kernel(name, k))
+        ns = sum(c * a for name, (c, a) in durs.items() if _is_kernel(name, k)) / max(calls, 1)
+        u_gui = 100.0 * busy / (gui / 8 * SIMDS) if gui else float("nan")
+        u_dur = 100.0 * busy / (ns * clock_ghz * SIMDS) if ns else float("nan")
+        lines.append(f"{k:26s} {n:5d} {flop / 1e9:11.3f} {mops_bf / max(mops_bf + mops_f32, 1):9.2f} {u_gui:11.2f} "
+                     f"{u_dur:11.2f} {ns / 1e3:8.2f} {flop / (ns * 1e-9) / 1e12 if ns else float('nan'):12.2f}")
+    return "\n".join(lines)
+
+
 def copy_calibration():
     """A plain device-to-device copy of 1 GiB, 4 times: the reference for the byte counters."""
     import torch
@@ -470,9 +527,15 @@ def main():
                     help="decode steps of the energy (tok/J) leg; 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for rocprofv3 byte counters)")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "TRACE_DIR"),
+                    help="matrix-core counter summary of the prefill kernels from a rocprofv3 --pmc folder and a "
+                         "--kernel-trace --stats folder of the same command")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn four rocprofv3 --pmc output folders into the traffic summary JSON")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        print(summarize_mfma(*args.summarize_mfma))
+        return
     if args.summarize_pmc:
         f, w, cf, cw = args.summarize_pmc
         print(json.dumps(summarize_pmc({"fetch": f, "write": w, "copy_fetch": cf, "copy_write": cw}), indent=1))
