@@ -89,7 +89,6 @@ std::string check_config(const mk_config* c) {
       return "MK_Q4G32 needs hidden, ffn, dn_heads*dn_dv and n_q_heads*head_dim to be multiples of 32";
     if (c->hidden > 8192 || c->ffn > 20480 || c->dn_heads * c->dn_dv > 20480 || c->n_q_heads * c->head_dim > 20480)
       return "MK_Q4G32 needs hidden <= 8192 and ffn, dn_heads*dn_dv, n_q_heads*head_dim <= 20480";
-    if (c->max_verify_k != 0) return "speculative verify needs BF16 weights: max_verify_k must be 0 with MK_Q4G32";
   }
   if (c->kv_dtype != MK_F32 && c->kv_dtype != MK_F16 && c->kv_dtype != MK_Q8)
     return "kv_dtype must be MK_F32, MK_F16 or MK_Q8";
@@ -363,6 +362,49 @@ void lds_layout_verify(const mk_config& c, int grid, MkDecodeParams& p) {
   p.lds_floats = o;
 }
 
+// LDS carve for the 4-bit verify kernel (floats): descriptors, RoPE rows, this workgroup's residual
+// rows of each position, the GEMV partials and the LM head's running argmax, and the vector region
+// (packed activations of a column group for every position; a gathered residual; DeltaNet, attention
+// and combine scratch) taking what is left of the compute unit's 160 KB.  Returns "" or the reason
+// the carve does not fit.
+constexpr int MK_LDS_FLOATS = 160 * 1024 / 4;
+std::string lds_layout_verify_q4(const mk_config& c, int grid, MkDecodeParams& p) {
+  const int vt = c.max_verify_k + 1, D = c.hidden, hd = c.head_dim, C = MK_ATT_CHUNK;
+  const int gs = c.n_q_heads / c.n_kv_heads;
+  const int rst = 4 * ((D / 4 + grid - 1) / grid);
+  int o = 0;
+  auto take = [&](int64_t n) {
+    const int at = o;
+    o += (int)((n + 3) / 4 * 4);
+    return at;
+  };
+  p.lds_desc = take(c.n_layers * (int)(sizeof(MkLayerDev) / 4));
+  p.lds_gain = 0;
+  p.lds_rope = take(vt * hd);
+  p.lds_x = take((int64_t)vt * rst);
+  p.rstride = rst;
+  p.lds_att = take(MK_RED_CAP + 2 * vt * MK_NCT);
+  p.lds_scr = take(2 * MK_VERIFY_MAXT * MK_NWAVE);
+  p.lds_flag = take(4);
+  p.lds_xn = take(MK_VERIFY_MAXT);
+  o = (o + 1) / 2 * 2;
+  p.lds_trace = take(2 * MK_TRACE_EVENTS);
+  const int vec = (MK_LDS_FLOATS - o) / 4 * 4;
+  p.lds_vec = take(vec);
+  p.vec_floats = vec;
+  p.lds_floats = o;
+  int64_t need = (int64_t)(vt - 1) * (2048 / 32) * 20 + 2048;                           // one column group
+  need = std::max<int64_t>(need, D);                                                      // a residual
+  need = std::max<int64_t>(need, (int64_t)vt * (2 * c.dn_dk + 2 + c.dn_dv));              // DeltaNet inputs
+  need = std::max<int64_t>(need, (int64_t)2 * vt * gs * hd + 2 * C * hd + vt * gs * C + 6 * vt * gs);  // items
+  need = std::max<int64_t>(need, (int64_t)3 * vt * 129);                                  // combine staging
+  need = std::max<int64_t>(need, (int64_t)2 * vt * grid);                                 // argmax records
+  if (vec < need)
+    return "4-bit verify needs " + std::to_string(need * 4) + " B of vector LDS; " + std::to_string((int64_t)vec * 4) +
+           " B are left";
+  return "";
+}
+
 }  // namespace
 
 struct mk_ctx {
@@ -602,9 +644,16 @@ int mk_create(const mk_config* cfg, int device, void* d_workspace, size_t worksp
     v.ll_am = (mk_u64*)(ctx->ws + lay.v_am);
     v.ll_acc = (mk_u64*)(ctx->ws + lay.v_acc);
     v.snap_stride = lay.snap_stride;
-    lds_layout_verify(*cfg, ctx->grid, v);
+    std::string why;
+    if (p.wq4) why = lds_layout_verify_q4(*cfg, ctx->grid, v);
+    else lds_layout_verify(*cfg, ctx->grid, v);
     const int vbytes = v.lds_floats * 4;
-    if (vbytes > (int)prop.sharedMemPerBlock || mk_verify_max_blocks_per_cu(&v, vbytes) < 1) {
+    if (!why.empty()) {
+      delete ctx;
+      return fail_global(MK_E_OCCUPANCY, why);
+    }
+    if (vbytes > (int)prop.sharedMemPerBlock ||
+        (p.wq4 ? mk_verify_q4_max_blocks_per_cu(&v, vbytes) : mk_verify_max_blocks_per_cu(&v, vbytes)) < 1) {
       const std::string m = "verify kernel needs " + std::to_string(vbytes) + " B of LDS for max_verify_k = " +
                             std::to_string(cfg->max_verify_k) + "; device offers " +
                             std::to_string(prop.sharedMemPerBlock);
@@ -713,8 +762,13 @@ int mk_set_grid(mk_ctx* ctx, int32_t n) {
     return fail(ctx, MK_E_OCCUPANCY, "decode kernel does not fit at this grid size");
   MkDecodeParams v = ctx->vbase;
   if (ctx->lay.vt) {
-    lds_layout_verify(ctx->cfg, n, v);
-    if (mk_verify_max_blocks_per_cu(&v, v.lds_floats * 4) < 1)
+    if (v.wq4) {
+      const std::string why = lds_layout_verify_q4(ctx->cfg, n, v);
+      if (!why.empty()) return fail(ctx, MK_E_OCCUPANCY, why);
+    } else {
+      lds_layout_verify(ctx->cfg, n, v);
+    }
+    if ((v.wq4 ? mk_verify_q4_max_blocks_per_cu(&v, v.lds_floats * 4) : mk_verify_max_blocks_per_cu(&v, v.lds_floats * 4)) < 1)
       return fail(ctx, MK_E_OCCUPANCY, "verify kernel does not fit at this grid size");
   }
   ctx->base = q;
@@ -1093,7 +1147,8 @@ int mk_verify_k(mk_ctx* ctx, const int32_t* d_tokens, int32_t k, int32_t* d_out,
   p.vtok = d_tokens;
   p.vout = d_out;
   p.vacc = d_n_accepted;
-  if (mk_launch_verify(&p, ctx->grid, ctx->stream)) return fail(ctx, MK_E_HIP, "verify launch failed");
+  if ((p.wq4 ? mk_launch_verify_q4(&p, ctx->grid, ctx->stream) : mk_launch_verify(&p, ctx->grid, ctx->stream)))
+    return fail(ctx, MK_E_HIP, "verify launch failed");
   ctx->pos_host += k + 1;
   ctx->pos_exact = false;
   return MK_OK;

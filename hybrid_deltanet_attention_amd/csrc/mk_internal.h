@@ -121,6 +121,8 @@ struct MkDecodeParams {
   int32_t wq4;
   // KV cache element type: MK_KV_F32, MK_KV_F16 or MK_KV_Q8
   int32_t kvt;
+  // 4-bit verify: floats between the positions of a workgroup's residual rows in LDS
+  int32_t rstride;
 };
 
 #ifdef __cplusplus
@@ -134,6 +136,8 @@ int mk_decode_q4_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
 // Q4G32 input layout [R][K] -> the decode kernel's tiled layout (ceil(R/4) * K/32 tiles of 80 bytes)
 int mk_launch_q4_tile(const void* src, int64_t R, int64_t K, void* dst, void* stream);
 int mk_verify_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
+int mk_launch_verify_q4(const MkDecodeParams* p, int n_wg, void* stream);
+int mk_verify_q4_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes);
 int mk_launch_permute_rows(const uint16_t* src, uint16_t* dst, const int32_t* d_perm, int64_t rows,
                            int64_t cols, void* stream);
 int mk_launch_zero(void* dst, int64_t bytes, void* stream);

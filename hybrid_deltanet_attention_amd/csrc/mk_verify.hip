@@ -26,7 +26,7 @@
 // Unlike the decode kernel no weights are prefetched into LDS: the LDS holds nt positions'
 // residuals and vectors instead, and all eight waves stream their GEMV units through registers.
 
-#include "mk_device.h"
+#include "mk_q4.h"
 
 namespace {
 
@@ -328,48 +328,54 @@ __device__ __forceinline__ bool dn_state_v(const MkDecodeParams& p, const MkLaye
   return true;
 }
 
+// One q/k/v row pair (RoPE pair order) of position t: rotate q and k at position pos + t, append k
+// and v to an FP32 cache at pos + t (compact caches are appended by the attention items), publish.
+__device__ __forceinline__ void att_qkv_v_put(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx,
+                                              const Lds& s, int P, int t, int pos, float x1, float x2) {
+  const int hd = p.hd, half = hd / 2, rows_in = L.rows_in;
+  const int nqp = p.nq * half, nkp = p.nkv * half;
+  MK_G mk_u64* llq = L.ll_in + (size_t)t * rows_in;
+  MK_G mk_u64* llk = llq + p.nq * hd;
+  MK_G mk_u64* llv = llk + p.nkv * hd;
+  const LS float* rp = s.rope + t * hd;
+  if (P < nqp + nkp) {
+    const bool isq = P < nqp;
+    const int Q = isq ? P : P - nqp;
+    const int hh = Q / half, m = Q - hh * half;
+    const float c = rp[m], sv = rp[half + m];
+    const float y1 = x1 * c - x2 * sv;
+    const float y2 = x2 * c + x1 * sv;
+    if (isq) {
+      ll_put(llq + hh * hd + m, cx.epoch, y1);
+      ll_put(llq + hh * hd + m + half, cx.epoch, y2);
+    } else {
+      const size_t co = ((size_t)hh * p.max_ctx + pos + t) * hd + m;
+      ll_put(llk + hh * hd + m, cx.epoch, y1);
+      ll_put(llk + hh * hd + m + half, cx.epoch, y2);
+      if (p.kvt == MK_KV_F32) {  // compact rows are appended by the attention items
+        L.Kc[co] = y1;
+        L.Kc[co + half] = y2;
+      }
+    }
+  } else {
+    const int Q = P - nqp - nkp;
+    const int hh = Q / half, m = Q - hh * half;
+    const size_t co = ((size_t)hh * p.max_ctx + pos + t) * hd + m;
+    ll_put(llv + hh * hd + m, cx.epoch, x1);
+    ll_put(llv + hh * hd + m + half, cx.epoch, x2);
+    if (p.kvt == MK_KV_F32) {
+      L.Vc[co] = x1;
+      L.Vc[co + half] = x2;
+    }
+  }
+}
+
 // q/k/v rows (RoPE pair order) for nt positions: rotate q and k at position pos + t, append k and v
 // to the cache at pos + t, publish all three.
 __device__ __forceinline__ void att_qkv_v(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                           const Gemv& g, const GemvPre& pre, int P0, int pos, int nt) {
-  const int hd = p.hd, half = hd / 2, rows_in = L.rows_in;
-  const int nqp = p.nq * half, nkp = p.nkv * half;
   gemv_v<true>(g, s.xn, p.D, nt, s.att, pre, [&](int pl, int t, float x1, float x2) {
-    const int P = P0 + pl;
-    MK_G mk_u64* llq = L.ll_in + (size_t)t * rows_in;
-    MK_G mk_u64* llk = llq + p.nq * hd;
-    MK_G mk_u64* llv = llk + p.nkv * hd;
-    const LS float* rp = s.rope + t * hd;
-    if (P < nqp + nkp) {
-      const bool isq = P < nqp;
-      const int Q = isq ? P : P - nqp;
-      const int hh = Q / half, m = Q - hh * half;
-      const float c = rp[m], sv = rp[half + m];
-      const float y1 = x1 * c - x2 * sv;
-      const float y2 = x2 * c + x1 * sv;
-      if (isq) {
-        ll_put(llq + hh * hd + m, cx.epoch, y1);
-        ll_put(llq + hh * hd + m + half, cx.epoch, y2);
-      } else {
-        const size_t co = ((size_t)hh * p.max_ctx + pos + t) * hd + m;
-        ll_put(llk + hh * hd + m, cx.epoch, y1);
-        ll_put(llk + hh * hd + m + half, cx.epoch, y2);
-        if (p.kvt == MK_KV_F32) {  // compact rows are appended by the attention items
-          L.Kc[co] = y1;
-          L.Kc[co + half] = y2;
-        }
-      }
-    } else {
-      const int Q = P - nqp - nkp;
-      const int hh = Q / half, m = Q - hh * half;
-      const size_t co = ((size_t)hh * p.max_ctx + pos + t) * hd + m;
-      ll_put(llv + hh * hd + m, cx.epoch, x1);
-      ll_put(llv + hh * hd + m + half, cx.epoch, x2);
-      if (p.kvt == MK_KV_F32) {
-        L.Vc[co] = x1;
-        L.Vc[co + half] = x2;
-      }
-    }
+    att_qkv_v_put(p, L, cx, s, P0 + pl, t, pos, x1, x2);
   });
 }
 
@@ -639,6 +645,88 @@ __device__ __forceinline__ void load_gains(const MK_G uint16_t* src, int n, LS u
   for (int i = tid(); i < (n >> 3); i += MK_NT) *(LS u32x4*)(dst + 8 * i) = *(const MK_G u32x4*)(src + 8 * i);
 }
 
+// Workgroup 0 takes the greedy choices y_1..y_nt from every workgroup's per-position (max, index)
+// records, counts the accepted drafts a, writes the outputs and the new position and publishes a;
+// then every workgroup restores its DeltaNet rows to the state after position a.  Shared by the BF16
+// and 4-bit verify kernels.
+__device__ __forceinline__ void verify_accept_rollback(const MkDecodeParams& p, const Ctx& cx, const Lds& s,
+                                                       const LS int* toks, int NW, int w, int pos, int nt,
+                                                       Tracer& tr) {
+  // workgroup 0: greedy choices, accepted count, outputs, new position
+  if (w == 0) {
+    wg_bar();  // the running-argmax cells are read before the gather reuses the region
+    const bool ok = gather_vec_all<false, PBV>(cx, p.ll_am, nt * 2 * NW, s.vec);
+    if (wg_bar_or(s, !ok)) return;
+    // wave t: position t's choice
+    if (wave() < nt) {
+      float b;
+      int bi;
+      wave_argmax(s.vec + wave() * 2 * NW, NW, b, bi);
+      if (lane() == 0) {
+        p.vout[wave()] = bi;
+        ((LS int*)s.scr)[wave()] = bi;
+      }
+    }
+    wg_bar();
+    if (tid() == 0) {
+      int a = 0;
+      while (a + 1 < nt && toks[a + 1] == ((LS int*)s.scr)[a]) ++a;
+      *p.vacc = a;
+      ll_put(p.ll_acc, cx.epoch, __int_as_float(a));
+      p.ctl->pos = pos + a + 1;
+    }
+  }
+  tr.mark();
+  // every workgroup: the accepted count, then its DeltaNet rows back to the state after position a
+  {
+    const bool ok = gather_vec_all<false, PBV>(cx, p.ll_acc, 1, s.scr);
+    if (wg_bar_or(s, !ok)) return;
+  }
+  const int a = uni(__float_as_int(s.scr[0]));
+  if (a + 1 < nt) {
+    const int K = p.H * p.dv, dk = p.dk;
+    const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
+    // The threads that wrote each snapshot element in dn_state_v copy it.  Loads for CB layers are
+    // issued before their stores: a load issued after a store would wait for that store too.
+    constexpr int CB = 8;
+    for (int li = wave(); li < s1 - s0; li += MK_NWAVE) {
+      const size_t ro = (size_t)(s0 + li) * dk;
+      for (int l0 = 0; l0 < p.n_layers; l0 += CB) {
+        float v[CB][4];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+          const int l = l0 + i;
+          const MkLayerDev L = layer_desc(s.desc, min(l, p.n_layers - 1));
+          const bool dn = l < p.n_layers && L.kind == MK_LAYER_DN;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = lane() + 64 * c;
+            v[i][c] = (dn && e < dk) ? L.Ssnap[(size_t)a * p.snap_stride + ro + e] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+          const int l = l0 + i;
+          const MkLayerDev L = layer_desc(s.desc, min(l, p.n_layers - 1));
+          const bool dn = l < p.n_layers && L.kind == MK_LAYER_DN;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = lane() + 64 * c;
+            if (dn && e < dk) L.S[ro + e] = v[i][c];
+          }
+        }
+      }
+    }
+  }
+  tr.mark();
+  tr.flush();
+  if (w == 0) {
+    wait_vm<0>();
+    wg_bar();
+    if (tid() == 0) p.ctl->step = cx.epoch + 1u;
+  }
+}
+
 template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, bool KV_COMPACT>
 __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
   MkDecodeParams p = p0;
@@ -859,79 +947,462 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
       }
     }
   }
-  // workgroup 0: greedy choices, accepted count, outputs, new position
-  if (w == 0) {
-    wg_bar();  // the running-argmax cells are read before the gather reuses the region
-    const bool ok = gather_vec_all<false, PBV>(cx, p.ll_am, nt * 2 * NW, s.vec);
-    if (wg_bar_or(s, !ok)) return;
-    // wave t: position t's choice
-    if (wave() < nt) {
-      float b;
-      int bi;
-      wave_argmax(s.vec + wave() * 2 * NW, NW, b, bi);
-      if (lane() == 0) {
-        p.vout[wave()] = bi;
-        ((LS int*)s.scr)[wave()] = bi;
+  verify_accept_rollback(p, cx, s, toks, NW, w, pos, nt, tr);
+}
+
+// ================================================================ 4-bit (Q4G32) speculative verify
+// The same launch for 4-bit weights: the 4-bit decode kernel's arithmetic on nt positions (the
+// activations of every position packed per 32-column block as that kernel packs them, the same
+// unit sums, wave reduction and segment order; DeltaNet rows, attention items and combine as in
+// the BF16 verify above), so every choice equals, bit for bit, the one a 4-bit decode launch makes.
+// At the 27B-scale widths nt positions' residuals and FFN hidden vectors do not fit a workgroup's
+// LDS, so:
+//  - the residual lives in the exchange records (the mixer and FFN outputs are published as the
+//    residual after the add, as in decode); a workgroup keeps only its own rows per position (xr),
+//    and gathers a position's whole residual when its RMSNorm scale is formed;
+//  - every GEMV runs over column groups of whole 2048-column segments, as many as the packed
+//    activations of all nt positions fit the vector region; a group's activations are gathered (or
+//    normalised) and packed, its units applied to every position, and a row's segment partials
+//    summed in segment order once all groups are done.  Every weight is read once.
+constexpr int Q4V_CTR = 1;  // the GEMV unit counter sits after the abort flag
+
+// words of packed activations for n columns (n a multiple of 32)
+__device__ __forceinline__ int q4v_pw(int n) { return (n >> 5) * Q4_XW; }
+
+// segments per column group: the unpacked floats of the group's last position after the packed
+// words of the others, (nt - 1) * pw(cols) + cols <= cap
+__device__ __forceinline__ int q4v_group_segs(int cap, int nt) {
+  return max(1, cap / ((nt - 1) * q4v_pw(Q4_COLS) + Q4_COLS));
+}
+
+// rows of one chunk: the segment partials of all nt positions fit MK_RED_CAP (whole 4-row blocks)
+__device__ __forceinline__ int q4v_rows(int S, int nt) { return max(4, (MK_RED_CAP / (S * nt)) & ~3); }
+
+// Unit sources of a (row chunk, column group): units u = rb * Sg + (s - sg0), s in [sg0, sg0 + Sg).
+struct Q4SrcV {
+  __amdgpu_buffer_rsrc_t rt;
+  int U, G, Sg, sg0;
+  __device__ __forceinline__ void init(const GemvQ4& g, int sg0_, int Sg_) {
+    const MK_G uint8_t* T = uni_ptr(g.T);
+    const int R = uni(g.R), RB = (R + 3) >> 2;
+    G = uni(g.K) >> 5;
+    sg0 = uni(sg0_);
+    Sg = uni(Sg_);
+    U = RB * Sg;
+    rt = __builtin_amdgcn_make_buffer_rsrc((void*)T, 0, RB * G * Q4_TILE, 0x00020000);
+  }
+  __device__ __forceinline__ void issue(Q4Unit& r, int u) const {
+    constexpr int OOB = 0x7ffffff0;  // past the resource: the load returns zeros
+    const int rb = u / Sg, s = sg0 + (u - rb * Sg);
+    const int ng = min(64, G - 64 * s);
+    const bool live = u < U && lane() < ng;
+    const int o = rb * G * Q4_TILE + s * 64 * Q4_TILE + lane() * 16;
+    const int pl = ng * 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      r.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rt, live ? o + k * pl : OOB, 0, 2 /* nt */);
+    r.p = __builtin_amdgcn_raw_buffer_load_b128(rt, live ? o + 4 * pl : OOB, 0, 2 /* nt */);
+  }
+};
+
+__device__ __forceinline__ int q4v_grab(LS int* ctr) {
+  int v = 0;
+  if (lane() == 0) v = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Partials of the units of rows [0, g.R) x segments [sg0, sg0 + Sg) for nt positions -> red[t][row][s]
+// (S segments per row).  Position t's packed activations of the group start at P + t * pstride
+// words; xp_t is shifted back so that column c's block is found at (c >> 5) * Q4_XW.  All eight
+// waves take units from the LDS counter, Q4_RING in flight each (as gemv_q4_partials).
+__device__ __forceinline__ void q4v_partials(const GemvQ4& g, int sg0, int Sg, const LS u32* P, int pstride, int nt,
+                                             LS float* red, LS int* ctr) {
+  Q4SrcV src;
+  src.init(g, sg0, Sg);
+  const int R = uni(g.R), K = uni(g.K), S = uni(g.S), U = src.U;
+  const int blk = R * S;
+  const LS u32* xb = P - (sg0 * Q4_COLS >> 5) * Q4_XW;
+  Q4Ring q;
+#pragma unroll
+  for (int k = 0; k < Q4_RING; ++k) {
+    q.uk[k] = q4v_grab(ctr);
+    src.issue(q.r[k], q.uk[k]);
+  }
+  while (q.uk[0] < U) {
+#pragma unroll
+    for (int k = 0; k < Q4_RING; ++k) {
+      const bool live = q.uk[k] < U;
+      if (live) {
+        const int u = q.uk[k], rb = u / Sg, s = sg0 + (u - rb * Sg);
+#pragma unroll 1
+        for (int t = 0; t < nt; ++t) {
+          Q4X x;
+          q4_load_x(x, xb + t * pstride, s, K);
+          const float a0 = q4_row(q.r[k].c[0], q.r[k].p.x, x);
+          const float a1 = q4_row(q.r[k].c[1], q.r[k].p.y, x);
+          const float a2 = q4_row(q.r[k].c[2], q.r[k].p.z, x);
+          const float a3 = q4_row(q.r[k].c[3], q.r[k].p.w, x);
+          const float v = reduce_rows4(a0, a1, a2, a3);
+          if ((lane() & 15) == 0) {
+            const int row = rb * 4 + (lane() >> 4);
+            if (row < R) red[t * blk + row * S + s] = v;
+          }
+        }
       }
-    }
-    wg_bar();
-    if (tid() == 0) {
-      int a = 0;
-      while (a + 1 < nt && toks[a + 1] == ((LS int*)s.scr)[a]) ++a;
-      *p.vacc = a;
-      ll_put(p.ll_acc, cx.epoch, __int_as_float(a));
-      p.ctl->pos = pos + a + 1;
+      q.uk[k] = live ? q4v_grab(ctr) : U;
+      src.issue(q.r[k], q.uk[k]);
     }
   }
+  wait_vm<0>();  // the ring's last loads read zeros; wait for them before the registers are reused
+}
+
+// W . x_t over a workgroup's rows for nt positions.  pack(c0, n, P, pstride) fills the packed
+// activations of columns [c0, c0 + n) of every position (position t at P + t * pstride words), ends
+// with a barrier and returns false when a wait gave up (the same in every thread); epi(row, t, v, 0)
+// or, PAIRS, epi(pair, t, v_even, v_odd) runs on the streaming threads once a row chunk's groups are
+// done.  Returns false when a pack failed.
+template <bool PAIRS, typename Pack, typename Epi>
+__device__ __forceinline__ bool gemv_q4_v(const GemvQ4& G, int nt, LS float* P, int pcap, LS float* red, LS int* ctr,
+                                          Pack pack, Epi epi) {
+  const int S = uni(G.S), K = uni(G.K);
+  nt = uni(nt);
+  const int gs = min(S, q4v_group_segs(pcap, nt));
+  const int ngroups = (S + gs - 1) / gs;
+  const int rc = q4v_rows(S, nt);
+  for (int r0 = 0; r0 == 0 || r0 < G.R; r0 += rc) {
+    GemvQ4 g = G;
+    g.T = G.T + (size_t)(r0 >> 2) * (size_t)(K >> 5) * Q4_TILE;
+    g.R = max(0, min(rc, G.R - r0));
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const int sg0 = gi * gs, Sg = min(gs, S - sg0);
+      const int c0 = sg0 * Q4_COLS, n = min(K, (sg0 + Sg) * Q4_COLS) - c0;
+      const int pstride = q4v_pw(n);
+      if ((ngroups > 1 || r0 == 0) && !pack(c0, n, P, pstride)) return false;  // one group: packed once
+      if (g.R > 0) q4v_partials(g, sg0, Sg, (const LS u32*)P, pstride, nt, red, ctr);
+      wg_bar();
+      if (tid() == 0) *ctr = 0;  // the next grab comes after at least one more barrier
+    }
+    if (streamer()) {
+      const int nr = PAIRS ? g.R / 2 : g.R, blk = g.R * S;
+      for (int i = tid(); i < nt * nr; i += NCT) {
+        const int t = i / nr, j = i - t * nr;
+        const LS float* rt = red + t * blk;
+        if (PAIRS) epi(r0 / 2 + j, t, seg_sum(rt + (2 * j) * S, S), seg_sum(rt + (2 * j + 1) * S, S));
+        else epi(r0 + j, t, seg_sum(rt + j * S, S), 0.f);
+      }
+    }
+    wg_bar();  // red (and P, for the next chunk's groups) are reused
+  }
+  return true;
+}
+
+// Columns [c0, c0 + n) of a 4-bit embedding row -> dst[0..n) in FP32 (q4_embed_row's values).
+__device__ __forceinline__ void q4_embed_cols(const MK_G uint16_t* E, int D, int tok, int c0, int n, LS float* dst) {
+  const int G = D >> 5;
+  const MK_G uint8_t* rowb = (const MK_G uint8_t*)E + (size_t)(tok >> 2) * (size_t)G * Q4_TILE;
+  const int r = tok & 3;
+  for (int i = tid() + (c0 >> 3); i < ((c0 + n) >> 3); i += MK_NT) {
+    const int gi = i >> 2, s = gi >> 6, l = gi & 63, ng = min(64, G - 64 * s);
+    const MK_G uint8_t* seg = rowb + (size_t)s * 64 * Q4_TILE;
+    const u32 v = *(const MK_G u32*)(seg + r * ng * 16 + l * 16 + 4 * (i & 3));
+    const u32 pw = *(const MK_G u32*)(seg + 4 * ng * 16 + l * 16 + 4 * r);
+    const float d = f16_lo(pw), m = f16_hi(pw);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dst[8 * i - c0 + 2 * j] = fmaf(d, (float)((v >> (4 * j)) & 15u), m);
+      dst[8 * i - c0 + 2 * j + 1] = fmaf(d, (float)((v >> (16 + 4 * j)) & 15u), m);
+    }
+  }
+}
+
+// Position t's residual columns [c0, c0 + n) -> dst: the embedding row of token tok (first layer,
+// src == nullptr) or records src[t][D].  Every thread calls it; ends with a barrier.
+__device__ __forceinline__ bool q4v_residual(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D, int tok,
+                                            const MK_G mk_u64* src, int t, int c0, int n, LS float* dst) {
+  bool ok = true;
+  if (src) ok = gather_vec_all<false, PBV>(cx, src + (size_t)t * D + c0, n, dst);
+  else q4_embed_cols(E, D, tok, c0, n, dst);
+  return !wg_bar_or(s, !ok);
+}
+
+// RMSNorm scales of nt residuals (rs[t] = 1 / sqrt(mean x_t^2 + eps), the sum of squares formed
+// exactly as the 4-bit decode kernel's rmsnorm_gg forms it) and this workgroup's residual rows
+// [d0, d1) of each position -> xr[t * rstride ..].  tmp: D floats of LDS.
+__device__ __forceinline__ bool q4v_norm_scales(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D,
+                                                const LS int* toks, const MK_G mk_u64* src, int nt, float eps,
+                                                LS float* tmp, LS float* rs, LS float* xr, int rstride, int d0,
+                                                int d1) {
+  const int D4 = D >> 2;
+  for (int t = 0; t < nt; ++t) {
+    if (!q4v_residual(cx, s, E, D, toks[t], src, t, 0, D, tmp)) return false;
+    if (wave() == 0) {
+      const LS f32x4* x4 = (const LS f32x4*)tmp;
+      float sq = 0.f;
+      for (int c0 = lane(); c0 < D4; c0 += 256) {
+        f32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (c0 + 64 * k < D4) v[k] = x4[c0 + 64 * k];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          sq = fmaf(v[k].x, v[k].x, sq);
+          sq = fmaf(v[k].y, v[k].y, sq);
+          sq = fmaf(v[k].z, v[k].z, sq);
+          sq = fmaf(v[k].w, v[k].w, sq);
+        }
+      }
+      sq = wave_sum(sq);
+      if (lane() == 0) rs[t] = 1.0f / sqrtf(sq / (float)D + eps);
+    }
+    for (int r = tid(); r < d1 - d0; r += MK_NT) xr[t * rstride + r] = tmp[d0 + r];
+    wg_bar();
+  }
+  return true;
+}
+
+// Packed normalised activations of columns [c0, c0 + n) for every position: x * rs[t] * g, as
+// rmsnorm_gg scales, then q4_pack.
+__device__ __forceinline__ bool q4v_pack_norm(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D,
+                                              const LS int* toks, const MK_G mk_u64* src, int nt,
+                                              const MK_G uint16_t* g, const LS float* rs, int c0, int n, LS float* P,
+                                              int pstride) {
+  for (int t = 0; t < nt; ++t) {
+    LS float* pt = P + t * pstride;
+    if (!q4v_residual(cx, s, E, D, toks[t], src, t, c0, n, pt)) return false;
+    const float r = rs[t];
+    for (int i = tid(); i < (n >> 2); i += MK_NT) {
+      const f32x4 v = ((LS f32x4*)pt)[i];
+      const u32x2 gg = *(const MK_G u32x2*)(g + c0 + 4 * i);
+      ((LS f32x4*)pt)[i] = f32x4{v.x * r * __uint_as_float(gg.x << 16), v.y * r * __uint_as_float(gg.x & 0xffff0000u),
+                                 v.z * r * __uint_as_float(gg.y << 16), v.w * r * __uint_as_float(gg.y & 0xffff0000u)};
+    }
+    wg_bar();
+    q4_pack(pt, n);
+  }
+  return true;
+}
+
+// Packed record vectors: columns [c0, c0 + n) of src[t][stride] for every position.
+__device__ __forceinline__ bool q4v_pack_records(const Ctx& cx, const Lds& s, const MK_G mk_u64* src, int stride,
+                                                 int nt, int c0, int n, LS float* P, int pstride) {
+  for (int t = 0; t < nt; ++t) {
+    LS float* pt = P + t * pstride;
+    const bool ok = gather_vec_all<false, PBV>(cx, src + (size_t)t * stride + c0, n, pt);
+    if (wg_bar_or(s, !ok)) return false;
+    q4_pack(pt, n);
+  }
+  return true;
+}
+
+__device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
+  extern __shared__ float lds_raw[];
+  LS float* lds = (LS float*)lds_raw;
+  const int NW = (int)gridDim.x, w = (int)blockIdx.x;
+  const int nt = uni(p.nt);
+  Lds s;
+  s.desc = (LS MkLayerDev*)(lds + p.lds_desc);
+  s.gain = nullptr;
+  s.rope = lds + p.lds_rope;
+  s.x = lds + p.lds_x;     // this workgroup's residual rows [t][rstride]
+  s.vec = lds + p.lds_vec; // packed activations, gathered vectors, DeltaNet / attention / combine scratch
+  s.xn = (LS u32*)s.vec;
+  s.att = lds + p.lds_att; // GEMV partials
+  s.att_cap = MK_RED_CAP;
+  s.scr = lds + p.lds_scr;
+  s.flag = (LS int*)(lds + p.lds_flag);
+  s.stA = nullptr;
+  s.a_slots = 0;
+  s.stB = nullptr;
+  LS int* toks = (LS int*)(lds + p.lds_xn);
+  LS int* ctr = s.flag + Q4V_CTR;
+  LS float* rs = s.scr + 2 * VT * MK_NWAVE - VT;  // RMSNorm scales, after the reduction cells
+  const int D = p.D, F = p.ffn;
+  const int pcap = uni(p.vec_floats);
+  const int rstride = uni(p.rstride);  // residual rows per position
+
+  Ctx cx;
+  cx.ctl = p.ctl;
+  cx.epoch = p.ctl->step;
+  const int pos = p.ctl->pos;
+  bool bad = nt < 1 || nt > VT || pos < 0 || pos + nt > p.max_ctx;
+  for (int t = 0; t < VT; ++t)
+    if (t < nt) {
+      const int tk = p.vtok[t];
+      bad = bad || tk < 0 || tk >= p.vocab;
+    }
+  if (bad) {
+    if (w == 0 && tid() == 0) set_err(cx, 2u);
+    return;
+  }
+  Tracer tr{(LS unsigned long long*)(lds + p.lds_trace), p.trace ? p.trace + (size_t)w * MK_TRACE_EVENTS : nullptr,
+            0};
   tr.mark();
-  // every workgroup: the accepted count, then its DeltaNet rows back to the state after position a
   {
-    const bool ok = gather_vec_all<false, PBV>(cx, p.ll_acc, 1, s.scr);
-    if (wg_bar_or(s, !ok)) return;
+    const int nw = p.n_layers * (int)(sizeof(MkLayerDev) / 4);
+    const MK_G u32* dsrc = (const MK_G u32*)p.layers;
+    for (int i = tid(); i < nw; i += MK_NT) ((LS u32*)s.desc)[i] = dsrc[i];
+    if (tid() < nt) toks[tid()] = p.vtok[tid()];
+    const int half = p.hd / 2;
+    for (int i = tid(); i < nt * half; i += MK_NT) {
+      const int t = i / half, m = i - t * half;
+      s.rope[t * p.hd + m] = p.rope_cos[(size_t)(pos + t) * half + m];
+      s.rope[t * p.hd + half + m] = p.rope_sin[(size_t)(pos + t) * half + m];
+    }
+    if (tid() == 0) {
+      *s.flag = 0;
+      *ctr = 0;
+    }
   }
-  const int a = uni(__float_as_int(s.scr[0]));
-  if (a + 1 < nt) {
-    const int K = p.H * p.dv, dk = p.dk;
-    const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
-    // The threads that wrote each snapshot element in dn_state_v copy it.  Loads for CB layers are
-    // issued before their stores: a load issued after a store would wait for that store too.
-    constexpr int CB = 8;
-    for (int li = wave(); li < s1 - s0; li += MK_NWAVE) {
-      const size_t ro = (size_t)(s0 + li) * dk;
-      for (int l0 = 0; l0 < p.n_layers; l0 += CB) {
-        float v[CB][4];
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-          const int l = l0 + i;
-          const MkLayerDev L = layer_desc(s.desc, min(l, p.n_layers - 1));
-          const bool dn = l < p.n_layers && L.kind == MK_LAYER_DN;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int e = lane() + 64 * c;
-            v[i][c] = (dn && e < dk) ? L.Ssnap[(size_t)a * p.snap_stride + ro + e] : 0.f;
+  wg_bar();
+
+  // the 4-bit decode kernel's row slices: residual-sized projections and FFN pairs in whole 4-row
+  // blocks, in-projection and LM-head rows by 4-row blocks
+  const int d0 = 4 * split(D >> 2, NW, w), d1 = min(D, 4 * split(D >> 2, NW, w + 1));
+  const int j0 = 2 * split(F >> 1, NW, w), j1 = 2 * split(F >> 1, NW, w + 1);
+  auto in_slice = [&](const MkLayerDev& Lx, GemvQ4& g, int& P0) {
+    const int nbi = (Lx.rows_in + 3) >> 2;
+    const int B0 = split(nbi, NW, w), B1 = split(nbi, NW, w + 1);
+    P0 = 2 * B0;
+    g.init(Lx.w_in, B0, max(0, min(4 * B1, Lx.rows_in) - 4 * B0), D);
+  };
+  const MK_G mk_u64* xsrc = nullptr;  // the residual's records (null: the embedding rows)
+  for (int l = 0; l < p.n_layers; ++l) {
+    const MkLayerDev L = layer_desc(s.desc, l);
+    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, rs, s.x, rstride, d0, d1)) return;
+    tr.mark();
+    auto pack_in = [&](int c0, int n, LS float* P, int ps) {
+      return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12, rs, c0, n, P, ps);
+    };
+    int P0;
+    GemvQ4 gin;
+    in_slice(L, gin, P0);
+    int K;
+    if (L.kind == MK_LAYER_DN) {
+      K = p.H * p.dv;
+      const int rin = L.rows_in;
+      MK_G mk_u64* dst = L.ll_in + 2 * P0;
+      if (!gemv_q4_v<false>(gin, nt, s.vec, pcap, s.att, ctr, pack_in,
+                            [&](int r, int t, float v, float) { ll_put(dst + (size_t)t * rin + r, cx.epoch, v); }))
+        return;
+      tr.mark();
+      const int s0 = split(K, NW, w), s1 = split(K, NW, w + 1);
+      if (!dn_state_v(p, L, cx, s, s.vec, s.scr, s0, s1, nt)) return;
+    } else {
+      K = p.nq * p.hd;
+      if (!gemv_q4_v<true>(gin, nt, s.vec, pcap, s.att, ctr, pack_in, [&](int pl, int t, float x1, float x2) {
+            att_qkv_v_put(p, L, cx, s, P0 + pl, t, pos, x1, x2);
+          }))
+        return;
+      tr.mark();
+      if (!att_items_v(p, L, cx, s, s.vec, NW, w, pos, nt)) return;
+      const int o0 = split(K, NW, w), o1 = split(K, NW, w + 1);
+      if (!att_combine_v(p, L, cx, s, s.vec, pcap, o0, o1, pos, nt)) return;
+    }
+    tr.mark();
+    // mixer outputs -> out-projection rows + residual -> records (the residual after the mixer)
+    {
+      GemvQ4 gout;
+      gout.init(L.w_out, d0 >> 2, d1 - d0, K);
+      if (!gemv_q4_v<false>(
+              gout, nt, s.vec, pcap, s.att, ctr,
+              [&](int c0, int n, LS float* P, int ps) { return q4v_pack_records(cx, s, L.ll_o, K, nt, c0, n, P, ps); },
+              [&](int r, int t, float v, float) {
+                ll_put(L.ll_x1 + (size_t)t * D + d0 + r, cx.epoch, s.x[t * rstride + r] + v);
+              }))
+        return;
+    }
+    tr.mark();
+    xsrc = L.ll_x1;
+    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, rs, s.x, rstride, d0, d1)) return;
+    {
+      GemvQ4 ggu;
+      ggu.init(L.w_gu, j0 >> 1, 2 * (j1 - j0), D);
+      if (!gemv_q4_v<true>(
+              ggu, nt, s.vec, pcap, s.att, ctr,
+              [&](int c0, int n, LS float* P, int ps) {
+                return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12 + D, rs, c0, n, P, ps);
+              },
+              [&](int j, int t, float gv, float uv) {
+                ll_put(L.ll_h + (size_t)t * F + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
+              }))
+        return;
+    }
+    tr.mark();
+    {
+      GemvQ4 gdn;
+      gdn.init(L.w_down, d0 >> 2, d1 - d0, F);
+      if (!gemv_q4_v<false>(
+              gdn, nt, s.vec, pcap, s.att, ctr,
+              [&](int c0, int n, LS float* P, int ps) { return q4v_pack_records(cx, s, L.ll_h, F, nt, c0, n, P, ps); },
+              [&](int r, int t, float v, float) {
+                ll_put(L.ll_x2 + (size_t)t * D + d0 + r, cx.epoch, s.x[t * rstride + r] + v);
+              }))
+        return;
+    }
+    tr.mark();
+    xsrc = L.ll_x2;
+  }
+
+  // final norm + tied LM head + per-position argmax (lowest index among equal maxima)
+  if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, rs, s.x, rstride, d0, d1)) return;
+  {
+    LS float* amv = s.att + MK_RED_CAP;  // running argmax per (position, streaming thread)
+    LS int* ami = (LS int*)(amv + nt * NCT);
+    for (int i = tid(); i < nt * NCT; i += MK_NT) {
+      amv[i] = -INFINITY;
+      ami[i] = 0x7fffffff;
+    }
+    wg_bar();
+    const int nbv = (p.vocab + 3) >> 2;
+    const int B0 = split(nbv, NW, w), B1 = split(nbv, NW, w + 1);
+    const int v0 = 4 * B0;
+    GemvQ4 gl;
+    gl.init(p.embed, B0, max(0, min(4 * B1, p.vocab) - 4 * B0), D);
+    const bool hok = gemv_q4_v<false>(
+        gl, nt, s.vec, pcap, s.att, ctr,
+        [&](int c0, int n, LS float* P, int ps) {
+          return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, p.g_final, rs, c0, n, P, ps);
+        },
+        [&](int r, int t, float v, float) {
+                       const int idx = v0 + r;
+                       const int c = t * NCT + tid();
+          if (v > amv[c] || (v == amv[c] && idx < ami[c])) {
+            amv[c] = v;
+            ami[c] = idx;
           }
+        });
+    if (!hok) return;
+    tr.mark();
+    if (wave() < nt) {
+      const int t = wave();
+      float b = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int i = lane(); i < NCT; i += 64) {
+        const float ob = amv[t * NCT + i];
+        const int oi = ami[t * NCT + i];
+        if (ob > b || (ob == b && oi < bi)) {
+          b = ob;
+          bi = oi;
         }
+      }
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-          const int l = l0 + i;
-          const MkLayerDev L = layer_desc(s.desc, min(l, p.n_layers - 1));
-          const bool dn = l < p.n_layers && L.kind == MK_LAYER_DN;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int e = lane() + 64 * c;
-            if (dn && e < dk) L.S[ro + e] = v[i][c];
-          }
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ob = __shfl_xor(b, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        if (ob > b || (ob == b && oi < bi)) {
+          b = ob;
+          bi = oi;
         }
+      }
+      if (lane() == 0) {
+        ll_put(p.ll_am + (size_t)t * 2 * NW + 2 * w, cx.epoch, b);
+        ll_put(p.ll_am + (size_t)t * 2 * NW + 2 * w + 1, cx.epoch, __int_as_float(bi));
       }
     }
   }
-  tr.mark();
-  tr.flush();
-  if (w == 0) {
-    wait_vm<0>();
-    wg_bar();
-    if (tid() == 0) p.ctl->step = cx.epoch + 1u;
-  }
+  verify_accept_rollback(p, cx, s, toks, NW, w, pos, nt, tr);
 }
 
 }  // namespace
@@ -958,6 +1429,20 @@ VerifyKernel pick_verify(const MkDecodeParams& p) {
   return mk_verify_kernel;
 }
 }  // namespace
+
+// 4-bit weights (any KV cache type)
+__global__ void __launch_bounds__(MK_NT, 1) mk_verify_q4_kernel(MkDecodeParams p) { verify_q4_body(p); }
+
+extern "C" int mk_launch_verify_q4(const MkDecodeParams* p, int n_wg, void* stream) {
+  hipLaunchKernelGGL(mk_verify_q4_kernel, dim3(n_wg), dim3(MK_NT), (size_t)p->lds_floats * 4, (hipStream_t)stream, *p);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+extern "C" int mk_verify_q4_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mk_verify_q4_kernel, MK_NT, lds_bytes) != hipSuccess) return 0;
+  return nb;
+}
 
 extern "C" int mk_launch_verify(const MkDecodeParams* p, int n_wg, void* stream) {
   hipLaunchKernelGGL(pick_verify(*p), dim3(n_wg), dim3(MK_NT), (size_t)p->lds_floats * 4, (hipStream_t)stream, *p);

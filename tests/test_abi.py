@@ -164,8 +164,8 @@ def test_q4_config_and_tensor_checks(lib):
     for bad in (dict(hidden=200), dict(ffn=776)):
         with pytest.raises(b.MkError):
             b.mk_workspace_bytes(b.mk_config_from(synth.get_config("tiny", **bad), weight_dtype=b.MK_Q4G32))
-    with pytest.raises(b.MkError):
-        b.mk_workspace_bytes(b.mk_config_from(cfg, max_verify_k=1, weight_dtype=b.MK_Q4G32))
+    # speculative verify with 4-bit weights: the verify records and DeltaNet snapshots add workspace
+    assert b.mk_workspace_bytes(b.mk_config_from(cfg, max_verify_k=1, weight_dtype=b.MK_Q4G32)) > q4
     # 27B-scale: 14.08 GB of 4-bit weights (0.625 B per weight) plus state, cache and records
     c27 = synth.get_config("hybrid_27b", max_ctx=2048)
     n = b.mk_workspace_bytes(b.mk_config_from(c27, weight_dtype=b.MK_Q4G32))

@@ -18,9 +18,9 @@ pytestmark = pytest.mark.gpu
 STATE_TOL = 1e-3
 
 
-def _verify_model(cfg, W, max_k, grid=None, kv_dtype=2):
+def _verify_model(cfg, W, max_k, grid=None, kv_dtype=2, weight_dtype=1):
     from hybrid_deltanet_attention_amd import Model
-    m = Model(cfg, device=0, max_verify_k=max_k, kv_dtype=kv_dtype)
+    m = Model(cfg, device=0, max_verify_k=max_k, kv_dtype=kv_dtype, weight_dtype=weight_dtype)
     m.mk_load_weights(W)
     if grid is not None:
         m.mk_set_grid(grid)
@@ -78,10 +78,10 @@ def _same_state(mv, mr, cfg, pos, what):
         assert np.array_equal(a, b), f"{what}: layer {l} differs from sequential decode"
 
 
-def _check_against_decode(cfg, W, prompt, drafts_of, k, grid=None, label="", kv_dtype=2):
+def _check_against_decode(cfg, W, prompt, drafts_of, k, grid=None, label="", kv_dtype=2, weight_dtype=1):
     """drafts_of(greedy continuation) -> drafts; verify == sequential decode, bitwise"""
-    mr = new_model(cfg, W, grid, kv_dtype=kv_dtype)
-    mv = _verify_model(cfg, W, max(k, 1), grid, kv_dtype)
+    mr = new_model(cfg, W, grid, weight_dtype=weight_dtype, kv_dtype=kv_dtype)
+    mv = _verify_model(cfg, W, max(k, 1), grid, kv_dtype, weight_dtype)
     pend = _prefill(mr, prompt)
     assert _prefill(mv, prompt) == pend
     # greedy continuation from the reference (k tokens after the pending one)
