@@ -389,7 +389,64 @@ def long_context_leg(cfg_name: str, W, ctx: int, n_steps: int, kv: str = "f32") 
             "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def q4_27b_leg(ctx: int, n_steps: int) -> dict:
+def q4_27b_verify_leg(W, ctx: int, n_launch: int, k: int = 5) -> dict:
+    """Speculative verify of the 27B-scale 4-bit hybrid against a long context: the pending token and k
+    random drafts scored per mk_verify_k launch at position ctx of a 32,768-position binary16 KV cache
+    (the pages keep fp16 KV up to about 80K).  The context's DeltaNet states and KV entries are
+    synthetic (seeded normal values written with mk_write_state, then mk_set_position): the pass's
+    work does not depend on their values, and a 30K-token prompt through one decode launch per token
+    would take minutes.  Random drafts are almost always rejected, so each launch advances one
+    position; its cost is the same whatever is accepted."""
+    import torch
+    import synth
+    from hybrid_deltanet_attention_amd import Model
+    from hybrid_deltanet_attention_amd.binding import MK_Q4G32, MK_F16
+    cfg = synth.get_config("hybrid_27b", max_ctx=32768)
+    assert ctx + 4 * n_launch + 8 <= cfg.max_ctx
+    m = Model(cfg, device=0, weight_dtype=MK_Q4G32, max_verify_k=k, kv_dtype=MK_F16)
+    m.mk_load_weights(W)
+    rng = np.random.default_rng([SEED, 21])
+    kv = (rng.standard_normal((2, cfg.n_kv_heads, cfg.max_ctx, cfg.head_dim), dtype=np.float32) * np.float32(0.5))
+    st = (rng.standard_normal((cfg.dn_heads, cfg.dn_dv, cfg.dn_dk), dtype=np.float32) * np.float32(0.05))
+    for l in range(cfg.n_layers):
+        m.mk_write_state(l, kv if cfg.is_attention(l) else st)
+    del kv, st
+    m.mk_set_position(ctx)
+    m.mk_sync()
+    dev = torch.device("cuda:0")
+    toks = torch.tensor(rng.integers(0, cfg.vocab, size=(n_launch + 2, k + 1)), dtype=torch.int32, device=dev)
+    out = torch.zeros((n_launch + 2, k + 1), dtype=torch.int32, device=dev)
+    acc = torch.zeros(n_launch + 2, dtype=torch.int32, device=dev)
+    for i in range(2):
+        m.mk_verify_k(toks[i], k, out[i], acc[i:i + 1])
+    m.mk_sync()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
+    torch.cuda.synchronize()
+    for i in range(n_launch):
+        ev[i][0].record(m.stream)
+        m.mk_verify_k(toks[i + 2], k, out[i + 2], acc[i + 2:i + 3])
+        ev[i][1].record(m.stream)
+    m.mk_sync()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    a = acc[2:].cpu().numpy()
+    # algorithmic bytes of a pass: the weights once, the KV cache read at ~ctx positions, the DeltaNet
+    # state read and written; the k state snapshots the rollback needs are written as well
+    b = algorithmic_bytes(cfg, ctx + k + 1, 0.625, kv="f16")
+    snaps = k * b["state"] // 2
+    bytes_pass = b["total"]
+    gbs = bytes_pass / (us * 1e-6) / 1e9
+    m.close()
+    return {"workload": f"hybrid_27b 4-bit verify, pending token + {k} random drafts at position {ctx} "
+                        "(32,768-position binary16 KV cache, synthetic context)",
+            "us_per_pass": round(us, 1), "positions_per_pass": k + 1, "mean_accepted": round(float(a.mean()), 3),
+            "tok_per_s_measured": round(float((a + 1).sum()) / (n_launch * us * 1e-6), 1),
+            "tok_per_s_all_accepted": round((k + 1) / (us * 1e-6), 1), "launches": n_launch,
+            "bytes_per_pass": int(bytes_pass), "snapshot_bytes": int(snaps), "achieved_GBs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def q4_27b_leg(ctx: int, n_steps: int, verify_ctx: int = 30000) -> dict:
     """The 27B-scale hybrid from 4-bit Q4G32 weights (64 layers, hidden 5120, 0.625 B per weight,
     14.08 GB): a ctx-token random prompt through the decode kernel (one launch per token), then
     n_steps timed one-launch decode steps.  Weights are drawn in the storage format (seeded)."""
@@ -405,7 +462,6 @@ def q4_27b_leg(ctx: int, n_steps: int) -> dict:
     gen_s = time.perf_counter() - t0
     m = Model(cfg, device=0, weight_dtype=MK_Q4G32)
     m.mk_load_weights(W)
-    del W
     print(f"[bench] 27B-scale 4-bit: weights drawn in {gen_s:.1f} s and loaded", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     prompt = torch.tensor(synth.make_prompt(cfg.vocab, ctx, SEED + 11), device=dev)
@@ -431,11 +487,18 @@ def q4_27b_leg(ctx: int, n_steps: int) -> dict:
     bytes_per = float(np.mean([algorithmic_bytes(cfg, L0 + i, 0.625)["total"] for i in range(n_steps)]))
     gbs = bytes_per / (us * 1e-6) / 1e9
     m.close()
+    del m
+    torch.cuda.empty_cache()
+    ver = None
+    if verify_ctx > 0:
+        print(f"[bench] 27B-scale 4-bit: verify at position {verify_ctx}", file=sys.stderr, flush=True)
+        ver = q4_27b_verify_leg(W, verify_ctx, 16)
+    del W
     return {"workload": f"hybrid_27b 4-bit (Q4G32) batch-1 decode after a {ctx}-token prompt",
             "layers": cfg.n_layers, "hidden": cfg.hidden, "ffn": cfg.ffn, "weights_GB": 14.08,
             "prompt_s": round(pre_s, 3), "us_per_launch": round(us, 2), "tok_per_s": round(n_steps / region, 1),
             "steps": n_steps, "bytes_per_launch": int(bytes_per), "achieved_GBs": round(gbs, 1),
-            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "verify": ver}
 
 
 def verify_leg(cfg, W, m_dec, prompt, tok, k: int, n_launch: int) -> dict:

@@ -24,7 +24,7 @@ STATUS = {
 
 # every symbol include/mk.h declares
 EXPORTS = ["mk_workspace_bytes", "mk_create", "mk_load_weights", "mk_check_tensors", "mk_prefill",
-           "mk_decode_step", "mk_decode_step_noalloc", "mk_verify_k", "mk_reset", "mk_sync", "mk_get_position",
+           "mk_decode_step", "mk_decode_step_noalloc", "mk_verify_k", "mk_reset", "mk_sync", "mk_get_position", "mk_set_position",
            "mk_state_bytes", "mk_read_state", "mk_write_state", "mk_set_grid", "mk_get_grid",
            "mk_set_trace", "mk_last_error", "mk_destroy"]
 
@@ -76,6 +76,7 @@ def load_library():
         "mk_reset": (ctypes.c_int, [P]),
         "mk_sync": (ctypes.c_int, [P]),
         "mk_get_position": (ctypes.c_int, [P, P]),
+        "mk_set_position": (ctypes.c_int, [P, I32]),
         "mk_state_bytes": (SZ, [P, I32]),
         "mk_read_state": (ctypes.c_int, [P, I32, P]),
         "mk_write_state": (ctypes.c_int, [P, I32, P]),
@@ -237,6 +238,9 @@ class Model:
         v = ctypes.c_int32()
         _check(self.lib.mk_get_position(self.ctx, ctypes.byref(v)), self.ctx)
         return v.value
+
+    def mk_set_position(self, pos: int):
+        _check(self.lib.mk_set_position(self.ctx, int(pos)), self.ctx)
 
     def mk_read_state(self, layer: int) -> np.ndarray:
         n = self.lib.mk_state_bytes(self.ctx, layer)

@@ -393,8 +393,7 @@ std::string lds_layout_verify_q4(const mk_config& c, int grid, MkDecodeParams& p
   p.lds_vec = take(vec);
   p.vec_floats = vec;
   p.lds_floats = o;
-  int64_t need = (int64_t)(vt - 1) * (2048 / 32) * 20 + 2048;                           // one column group
-  need = std::max<int64_t>(need, D);                                                      // a residual
+  int64_t need = (int64_t)vt * 2048;                                                      // one column group
   need = std::max<int64_t>(need, (int64_t)vt * (2 * c.dn_dk + 2 + c.dn_dv));              // DeltaNet inputs
   need = std::max<int64_t>(need, (int64_t)2 * vt * gs * hd + 2 * C * hd + vt * gs * C + 6 * vt * gs);  // items
   need = std::max<int64_t>(need, (int64_t)3 * vt * 129);                                  // combine staging
@@ -1186,6 +1185,15 @@ int mk_get_position(mk_ctx* ctx, int32_t* pos) {
     ctx->pos_host = ctl.pos;
     ctx->pos_exact = true;
   }
+  return MK_OK;
+}
+
+int mk_set_position(mk_ctx* ctx, int32_t pos) {
+  if (!ctx) return fail_global(MK_E_INVALID, "ctx is NULL");
+  if (pos < 0 || pos > ctx->cfg.max_ctx) return fail(ctx, MK_E_INVALID, "position outside [0, max_ctx]");
+  if (mk_launch_set_ctl(ctx->base.ctl, pos, 0, 0, ctx->stream)) return fail(ctx, MK_E_HIP, "set position launch failed");
+  ctx->pos_host = pos;
+  ctx->pos_exact = true;
   return MK_OK;
 }
 

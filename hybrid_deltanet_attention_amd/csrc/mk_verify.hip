@@ -524,46 +524,59 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
         }
       }
       wg_bar();
-      if (streamer()) {
+      {
+        // weighted values: thread (d, tg) keeps column d of the chunk's values in registers and
+        // produces the (position, head) rows tg, tg + NG, ...; each output still adds its 16 products
+        // in slot order, then merges with the item's running values
         const LS float* rin = rml + (k & 1) * 2 * nt * gs;   // running (max, sum) before this chunk
         LS float* rout = rml + ((k + 1) & 1) * 2 * nt * gs;  // ... and after it
-        for (int o = tid(); o < (nt - tmin) * gs * hd; o += NCT) {
-          const int tt = o / (gs * hd), r = o - tt * gs * hd;
-          const int i = r / hd, d = r - i * hd;
-          const int t = tmin + tt;
-          const int ti = t * gs + i;
-          const int nj = min(pos + t + 1, j0 + C) - j0;
-          float a = 0.f;
+        const int NG = MK_NT / hd, nrows = (nt - tmin) * gs;
+        const int d = tid() % hd, tg = tid() / hd;
+        if (tg < NG) {
+          float vcol[ATT_C];
 #pragma unroll
-          for (int jj = 0; jj < ATT_C; ++jj) {
-            const float pv = pb[ti * C + jj];
-            const float vv = jj < nj ? vc[jj * hd + d] : 0.f;
-            a = fmaf(pv, vv, a);
-          }
-          // position t's chunks of this item: c0 .. its last visible chunk
-          const bool first = c == c0;
-          const bool last = c + 1 == min(c1, (pos + t) / C + 1);
-          float M = ml[2 * ti], S = ml[2 * ti + 1];
-          if (!first) {
-            const float Mr = rin[2 * ti], Sr = rin[2 * ti + 1];
-            const float Mn = fmaxf(Mr, M);
-            const float f = expf(Mr - Mn), f1 = expf(M - Mn);
-            a = fmaf(racc[ti * hd + d], f, a * f1);
-            S = fmaf(Sr, f, S * f1);
-            M = Mn;
-          }
-          if (last) {
-            MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2) + i * (hd + 2);
-            ll_put(part + 2 + d, cx.epoch, a);
-            if (d == 0) {
-              ll_put(part, cx.epoch, M);
-              ll_put(part + 1, cx.epoch, S);
+          for (int jj = 0; jj < ATT_C; ++jj) vcol[jj] = vc[jj * hd + d];
+          for (int rr = tg; rr < nrows; rr += NG) {
+            const int tt = rr / gs, i = rr - tt * gs;
+            const int t = tmin + tt;
+            const int ti = t * gs + i;
+            const int nj = min(pos + t + 1, j0 + C) - j0;
+            f32x4 pw[ATT_C / 4];
+#pragma unroll
+            for (int q = 0; q < ATT_C / 4; ++q) pw[q] = *(const LS f32x4*)(pb + ti * C + 4 * q);
+            float a = 0.f;
+#pragma unroll
+            for (int q = 0; q < ATT_C / 4; ++q) {
+              a = fmaf(pw[q].x, 4 * q + 0 < nj ? vcol[4 * q + 0] : 0.f, a);
+              a = fmaf(pw[q].y, 4 * q + 1 < nj ? vcol[4 * q + 1] : 0.f, a);
+              a = fmaf(pw[q].z, 4 * q + 2 < nj ? vcol[4 * q + 2] : 0.f, a);
+              a = fmaf(pw[q].w, 4 * q + 3 < nj ? vcol[4 * q + 3] : 0.f, a);
             }
-          } else {
-            racc[ti * hd + d] = a;
-            if (d == 0) {
-              rout[2 * ti] = M;
-              rout[2 * ti + 1] = S;
+            // position t's chunks of this item: c0 .. its last visible chunk
+            const bool first = c == c0;
+            const bool last = c + 1 == min(c1, (pos + t) / C + 1);
+            float M = ml[2 * ti], S = ml[2 * ti + 1];
+            if (!first) {
+              const float Mr = rin[2 * ti], Sr = rin[2 * ti + 1];
+              const float Mn = fmaxf(Mr, M);
+              const float f = expf(Mr - Mn), f1 = expf(M - Mn);
+              a = fmaf(racc[ti * hd + d], f, a * f1);
+              S = fmaf(Sr, f, S * f1);
+              M = Mn;
+            }
+            if (last) {
+              MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2) + i * (hd + 2);
+              ll_put(part + 2 + d, cx.epoch, a);
+              if (d == 0) {
+                ll_put(part, cx.epoch, M);
+                ll_put(part + 1, cx.epoch, S);
+              }
+            } else {
+              racc[ti * hd + d] = a;
+              if (d == 0) {
+                rout[2 * ti] = M;
+                rout[2 * ti + 1] = S;
+              }
             }
           }
         }
@@ -969,10 +982,11 @@ constexpr int Q4V_CTR = 1;  // the GEMV unit counter sits after the abort flag
 // words of packed activations for n columns (n a multiple of 32)
 __device__ __forceinline__ int q4v_pw(int n) { return (n >> 5) * Q4_XW; }
 
-// segments per column group: the unpacked floats of the group's last position after the packed
-// words of the others, (nt - 1) * pw(cols) + cols <= cap
+// segments per column group: every position's columns of the group side by side, nt * cols <= cap
+// (each position's columns are packed in place, so position t's packed words start at t * cols),
+// and no more columns than one q4_pack call takes
 __device__ __forceinline__ int q4v_group_segs(int cap, int nt) {
-  return max(1, cap / ((nt - 1) * q4v_pw(Q4_COLS) + Q4_COLS));
+  return max(1, min(cap / (nt * Q4_COLS), 8 * MK_NT * Q4_PACK_IT / Q4_COLS));
 }
 
 // rows of one chunk: the segment partials of all nt positions fit MK_RED_CAP (whole 4-row blocks)
@@ -1056,8 +1070,8 @@ __device__ __forceinline__ void q4v_partials(const GemvQ4& g, int sg0, int Sg, c
   wait_vm<0>();  // the ring's last loads read zeros; wait for them before the registers are reused
 }
 
-// W . x_t over a workgroup's rows for nt positions.  pack(c0, n, P, pstride) fills the packed
-// activations of columns [c0, c0 + n) of every position (position t at P + t * pstride words), ends
+// W . x_t over a workgroup's rows for nt positions.  pack(c0, n, P) fills the packed activations of
+// columns [c0, c0 + n) of every position (position t's at P + t * n words), ends
 // with a barrier and returns false when a wait gave up (the same in every thread); epi(row, t, v, 0)
 // or, PAIRS, epi(pair, t, v_even, v_odd) runs on the streaming threads once a row chunk's groups are
 // done.  Returns false when a pack failed.
@@ -1076,8 +1090,8 @@ __device__ __forceinline__ bool gemv_q4_v(const GemvQ4& G, int nt, LS float* P, 
     for (int gi = 0; gi < ngroups; ++gi) {
       const int sg0 = gi * gs, Sg = min(gs, S - sg0);
       const int c0 = sg0 * Q4_COLS, n = min(K, (sg0 + Sg) * Q4_COLS) - c0;
-      const int pstride = q4v_pw(n);
-      if ((ngroups > 1 || r0 == 0) && !pack(c0, n, P, pstride)) return false;  // one group: packed once
+      const int pstride = n;  // position t's packed words start at t * n
+      if ((ngroups > 1 || r0 == 0) && !pack(c0, n, P)) return false;  // one group: packed once
       if (g.R > 0) q4v_partials(g, sg0, Sg, (const LS u32*)P, pstride, nt, red, ctr);
       wg_bar();
       if (tid() == 0) *ctr = 0;  // the next grab comes after at least one more barrier
@@ -1115,30 +1129,42 @@ __device__ __forceinline__ void q4_embed_cols(const MK_G uint16_t* E, int D, int
   }
 }
 
-// Position t's residual columns [c0, c0 + n) -> dst: the embedding row of token tok (first layer,
-// src == nullptr) or records src[t][D].  Every thread calls it; ends with a barrier.
-__device__ __forceinline__ bool q4v_residual(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D, int tok,
-                                            const MK_G mk_u64* src, int t, int c0, int n, LS float* dst) {
+// Columns [c0, c0 + n) of every position's vector -> dst + t * n: records src[t][stride] (one gather
+// for all positions), or, for the first layer's residual (src == nullptr), the embedding rows of the
+// tokens.  Every thread calls it; ends with a barrier; false when a wait gave up.
+__device__ __forceinline__ bool q4v_gather(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D,
+                                          const LS int* toks, const MK_G mk_u64* src, int stride, int nt, int c0,
+                                          int n, LS float* dst) {
   bool ok = true;
-  if (src) ok = gather_vec_all<false, PBV>(cx, src + (size_t)t * D + c0, n, dst);
-  else q4_embed_cols(E, D, tok, c0, n, dst);
+  if (src) {
+    ok = gather_map_all(cx, nt * n, [=](int f) {
+      const int t = f / n;
+      return src + (size_t)t * stride + c0 + (f - t * n);
+    }, [=](int f, float v) { dst[f] = v; });
+  } else {
+    for (int t = 0; t < nt; ++t) q4_embed_cols(E, D, toks[t], c0, n, dst + t * n);
+  }
   return !wg_bar_or(s, !ok);
 }
 
-// RMSNorm scales of nt residuals (rs[t] = 1 / sqrt(mean x_t^2 + eps), the sum of squares formed
-// exactly as the 4-bit decode kernel's rmsnorm_gg forms it) and this workgroup's residual rows
-// [d0, d1) of each position -> xr[t * rstride ..].  tmp: D floats of LDS.
+// RMSNorm scales of nt residuals, rs[t] = 1 / sqrt(mean x_t^2 + eps), and this workgroup's residual
+// rows [d0, d1) of each position -> xr[t * rstride ..].  The residuals come in chunks of whole
+// 1024-value strides of the 4-bit decode kernel's rmsnorm_gg (all positions per gather); wave t
+// carries position t's running per-lane sum through the chunks in exactly that kernel's order, so the
+// scale is bit-identical.
 __device__ __forceinline__ bool q4v_norm_scales(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D,
                                                 const LS int* toks, const MK_G mk_u64* src, int nt, float eps,
-                                                LS float* tmp, LS float* rs, LS float* xr, int rstride, int d0,
-                                                int d1) {
+                                                LS float* P, int pcap, LS float* rs, LS float* xr, int rstride,
+                                                int d0, int d1) {
   const int D4 = D >> 2;
-  for (int t = 0; t < nt; ++t) {
-    if (!q4v_residual(cx, s, E, D, toks[t], src, t, 0, D, tmp)) return false;
-    if (wave() == 0) {
-      const LS f32x4* x4 = (const LS f32x4*)tmp;
-      float sq = 0.f;
-      for (int c0 = lane(); c0 < D4; c0 += 256) {
+  const int ch = max(1024, (pcap / nt) / 1024 * 1024);
+  float sq = 0.f;
+  for (int a = 0; a < D; a += ch) {
+    const int n = min(ch, D - a);
+    if (!q4v_gather(cx, s, E, D, toks, src, D, nt, a, n, P)) return false;
+    if (wave() < nt) {
+      const LS f32x4* x4 = (const LS f32x4*)(P + wave() * n) - (a >> 2);  // indexed by the residual's f32x4
+      for (int c0 = (a >> 2) + lane(); c0 < min((a + n) >> 2, D4); c0 += 256) {
         f32x4 v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -1153,46 +1179,47 @@ __device__ __forceinline__ bool q4v_norm_scales(const Ctx& cx, const Lds& s, con
           sq = fmaf(v[k].w, v[k].w, sq);
         }
       }
-      sq = wave_sum(sq);
-      if (lane() == 0) rs[t] = 1.0f / sqrtf(sq / (float)D + eps);
     }
-    for (int r = tid(); r < d1 - d0; r += MK_NT) xr[t * rstride + r] = tmp[d0 + r];
+    const int nr = d1 - d0;
+    for (int i = tid(); i < nt * nr; i += MK_NT) {
+      const int t = i / nr, r = i - t * nr, col = d0 + r;
+      if (col >= a && col < a + n) xr[t * rstride + r] = P[t * n + col - a];
+    }
     wg_bar();
   }
+  if (wave() < nt) {
+    sq = wave_sum(sq);
+    if (lane() == 0) rs[wave()] = 1.0f / sqrtf(sq / (float)D + eps);
+  }
+  wg_bar();
   return true;
 }
 
-// Packed normalised activations of columns [c0, c0 + n) for every position: x * rs[t] * g, as
-// rmsnorm_gg scales, then q4_pack.
+// Packed normalised activations of columns [c0, c0 + n) for every position (position t at P + t * n):
+// x * rs[t] * g, as rmsnorm_gg scales, then q4_pack.
 __device__ __forceinline__ bool q4v_pack_norm(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D,
                                               const LS int* toks, const MK_G mk_u64* src, int nt,
-                                              const MK_G uint16_t* g, const LS float* rs, int c0, int n, LS float* P,
-                                              int pstride) {
-  for (int t = 0; t < nt; ++t) {
-    LS float* pt = P + t * pstride;
-    if (!q4v_residual(cx, s, E, D, toks[t], src, t, c0, n, pt)) return false;
+                                              const MK_G uint16_t* g, const LS float* rs, int c0, int n, LS float* P) {
+  if (!q4v_gather(cx, s, E, D, toks, src, D, nt, c0, n, P)) return false;
+  const int n4 = n >> 2;
+  for (int i = tid(); i < nt * n4; i += MK_NT) {
+    const int t = i / n4, c = i - t * n4;
     const float r = rs[t];
-    for (int i = tid(); i < (n >> 2); i += MK_NT) {
-      const f32x4 v = ((LS f32x4*)pt)[i];
-      const u32x2 gg = *(const MK_G u32x2*)(g + c0 + 4 * i);
-      ((LS f32x4*)pt)[i] = f32x4{v.x * r * __uint_as_float(gg.x << 16), v.y * r * __uint_as_float(gg.x & 0xffff0000u),
-                                 v.z * r * __uint_as_float(gg.y << 16), v.w * r * __uint_as_float(gg.y & 0xffff0000u)};
-    }
-    wg_bar();
-    q4_pack(pt, n);
+    const f32x4 v = ((LS f32x4*)P)[i];
+    const u32x2 gg = *(const MK_G u32x2*)(g + c0 + 4 * c);
+    ((LS f32x4*)P)[i] = f32x4{v.x * r * __uint_as_float(gg.x << 16), v.y * r * __uint_as_float(gg.x & 0xffff0000u),
+                              v.z * r * __uint_as_float(gg.y << 16), v.w * r * __uint_as_float(gg.y & 0xffff0000u)};
   }
+  wg_bar();
+  for (int t = 0; t < nt; ++t) q4_pack(P + t * n, n);
   return true;
 }
 
-// Packed record vectors: columns [c0, c0 + n) of src[t][stride] for every position.
+// Packed record vectors: columns [c0, c0 + n) of src[t][stride] for every position (at P + t * n).
 __device__ __forceinline__ bool q4v_pack_records(const Ctx& cx, const Lds& s, const MK_G mk_u64* src, int stride,
-                                                 int nt, int c0, int n, LS float* P, int pstride) {
-  for (int t = 0; t < nt; ++t) {
-    LS float* pt = P + t * pstride;
-    const bool ok = gather_vec_all<false, PBV>(cx, src + (size_t)t * stride + c0, n, pt);
-    if (wg_bar_or(s, !ok)) return false;
-    q4_pack(pt, n);
-  }
+                                                 int nt, int c0, int n, LS float* P) {
+  if (!q4v_gather(cx, s, nullptr, 0, nullptr, src, stride, nt, c0, n, P)) return false;
+  for (int t = 0; t < nt; ++t) q4_pack(P + t * n, n);
   return true;
 }
 
@@ -1270,10 +1297,11 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
   const MK_G mk_u64* xsrc = nullptr;  // the residual's records (null: the embedding rows)
   for (int l = 0; l < p.n_layers; ++l) {
     const MkLayerDev L = layer_desc(s.desc, l);
-    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, rs, s.x, rstride, d0, d1)) return;
+    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1))
+      return;
     tr.mark();
-    auto pack_in = [&](int c0, int n, LS float* P, int ps) {
-      return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12, rs, c0, n, P, ps);
+    auto pack_in = [&](int c0, int n, LS float* P) {
+      return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12, rs, c0, n, P);
     };
     int P0;
     GemvQ4 gin;
@@ -1307,7 +1335,7 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
       gout.init(L.w_out, d0 >> 2, d1 - d0, K);
       if (!gemv_q4_v<false>(
               gout, nt, s.vec, pcap, s.att, ctr,
-              [&](int c0, int n, LS float* P, int ps) { return q4v_pack_records(cx, s, L.ll_o, K, nt, c0, n, P, ps); },
+              [&](int c0, int n, LS float* P) { return q4v_pack_records(cx, s, L.ll_o, K, nt, c0, n, P); },
               [&](int r, int t, float v, float) {
                 ll_put(L.ll_x1 + (size_t)t * D + d0 + r, cx.epoch, s.x[t * rstride + r] + v);
               }))
@@ -1315,14 +1343,15 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
     }
     tr.mark();
     xsrc = L.ll_x1;
-    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, rs, s.x, rstride, d0, d1)) return;
+    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1))
+      return;
     {
       GemvQ4 ggu;
       ggu.init(L.w_gu, j0 >> 1, 2 * (j1 - j0), D);
       if (!gemv_q4_v<true>(
               ggu, nt, s.vec, pcap, s.att, ctr,
-              [&](int c0, int n, LS float* P, int ps) {
-                return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12 + D, rs, c0, n, P, ps);
+              [&](int c0, int n, LS float* P) {
+                return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12 + D, rs, c0, n, P);
               },
               [&](int j, int t, float gv, float uv) {
                 ll_put(L.ll_h + (size_t)t * F + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
@@ -1335,7 +1364,7 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
       gdn.init(L.w_down, d0 >> 2, d1 - d0, F);
       if (!gemv_q4_v<false>(
               gdn, nt, s.vec, pcap, s.att, ctr,
-              [&](int c0, int n, LS float* P, int ps) { return q4v_pack_records(cx, s, L.ll_h, F, nt, c0, n, P, ps); },
+              [&](int c0, int n, LS float* P) { return q4v_pack_records(cx, s, L.ll_h, F, nt, c0, n, P); },
               [&](int r, int t, float v, float) {
                 ll_put(L.ll_x2 + (size_t)t * D + d0 + r, cx.epoch, s.x[t * rstride + r] + v);
               }))
@@ -1346,7 +1375,8 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
   }
 
   // final norm + tied LM head + per-position argmax (lowest index among equal maxima)
-  if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, rs, s.x, rstride, d0, d1)) return;
+  if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1))
+    return;
   {
     LS float* amv = s.att + MK_RED_CAP;  // running argmax per (position, streaming thread)
     LS int* ami = (LS int*)(amv + nt * NCT);
@@ -1362,8 +1392,8 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
     gl.init(p.embed, B0, max(0, min(4 * B1, p.vocab) - 4 * B0), D);
     const bool hok = gemv_q4_v<false>(
         gl, nt, s.vec, pcap, s.att, ctr,
-        [&](int c0, int n, LS float* P, int ps) {
-          return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, p.g_final, rs, c0, n, P, ps);
+        [&](int c0, int n, LS float* P) {
+          return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, p.g_final, rs, c0, n, P);
         },
         [&](int r, int t, float v, float) {
                        const int idx = v0 + r;

@@ -197,6 +197,11 @@ size_t mk_state_bytes(const mk_ctx* ctx, int32_t layer);
 int mk_read_state(mk_ctx* ctx, int32_t layer, void* dst);
 int mk_write_state(mk_ctx* ctx, int32_t layer, const void* src);
 
+/* Set the sequence position to pos (0 <= pos <= max_ctx): the other half of a state hand-off, after
+ * mk_write_state has restored every layer's DeltaNet state and KV entries [0, pos) of a sequence.
+ * Enqueued on the stream; errors: MK_E_INVALID. */
+int mk_set_position(mk_ctx* ctx, int32_t pos);
+
 /* Number of workgroups of the persistent grid (default: one per compute unit).  Results are
  * bitwise identical for every grid size; smaller grids exist for that check and for tuning.
  * Errors: MK_E_INVALID (n < 1 or more than the device's compute units). */

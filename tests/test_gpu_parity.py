@@ -149,3 +149,32 @@ def test_determinism_repeat():
     b = run_teacher_forced(m, prompt, fed)
     assert np.array_equal(a[0], b[0])
     assert all(np.array_equal(x, y) for x, y in zip(a[2], b[2]))
+
+
+def test_state_handoff_write_state_and_set_position():
+    """a sequence's states read from one context and written to a fresh one with the position set
+    there continues bit for bit like the original (mk_read_state / mk_write_state / mk_set_position)"""
+    torch = __import__("gpu_util").torch_cuda()
+    cfg = synth.get_config("tiny")
+    W = synth.make_weights(cfg, 40)
+    prompt = synth.make_prompt(cfg.vocab, 23, 40)
+    a = new_model(cfg, W)
+    b = new_model(cfg, W)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a.mk_prefill(torch.tensor(prompt, device="cuda"), len(prompt), tok)
+    a.mk_sync()
+    for l in range(cfg.n_layers):
+        b.mk_write_state(l, a.mk_read_state(l))
+    b.mk_set_position(len(prompt))
+    ta, tb = tok.clone(), tok.clone()
+    la = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    lb = torch.empty_like(la)
+    for _ in range(6):
+        a.mk_decode_step(ta, ta, la)
+        b.mk_decode_step(tb, tb, lb)
+        a.mk_sync()
+        b.mk_sync()
+        assert torch.equal(la, lb) and int(ta.item()) == int(tb.item())
+    assert a.mk_get_position() == b.mk_get_position() == len(prompt) + 6
+    a.close()
+    b.close()
