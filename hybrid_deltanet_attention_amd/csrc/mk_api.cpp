@@ -378,7 +378,6 @@ std::string lds_layout_verify_q4(const mk_config& c, int grid, MkDecodeParams& p
     o += (int)((n + 3) / 4 * 4);
     return at;
   };
-  p.lds_desc = take(c.n_layers * (int)(sizeof(MkLayerDev) / 4));
   p.lds_gain = 0;
   p.lds_rope = take(vt * hd);
   p.lds_x = take((int64_t)vt * rst);
@@ -393,11 +392,22 @@ std::string lds_layout_verify_q4(const mk_config& c, int grid, MkDecodeParams& p
   p.lds_vec = take(vec);
   p.vec_floats = vec;
   p.lds_floats = o;
+  // layer descriptors are read from memory; the rollback's copy of the table sits at the tail of the
+  // vector region, after the argmax records it gathers there
+  const int ndesc = (c.n_layers * (int)(sizeof(MkLayerDev) / 4) + 3) / 4 * 4;
+  p.lds_desc = p.lds_vec + vec - ndesc;
+  if ((int64_t)2 * vt * grid + ndesc > vec)
+    return "4-bit verify: the layer descriptors and argmax records do not fit the vector LDS";
   int64_t need = (int64_t)vt * 2048;                                                      // one column group
   need = std::max<int64_t>(need, (int64_t)vt * (2 * c.dn_dk + 2 + c.dn_dv));              // DeltaNet inputs
   need = std::max<int64_t>(need, (int64_t)2 * vt * gs * hd + 2 * C * hd + vt * gs * C + 6 * vt * gs);  // items
   need = std::max<int64_t>(need, (int64_t)3 * vt * 129);                                  // combine staging
   need = std::max<int64_t>(need, (int64_t)2 * vt * grid);                                 // argmax records
+  // a workgroup's FFN hidden slice (whole 32-column blocks) is staged in the LM head's argmax cells
+  const int64_t hw = 32 * (((int64_t)c.ffn / 32 + grid - 1) / grid);
+  if (vt * hw > 2 * vt * MK_NCT)
+    return "4-bit verify stages " + std::to_string(hw) + " FFN hidden columns per workgroup at this grid; at most " +
+           std::to_string(2 * MK_NCT) + " fit";
   if (vec < need)
     return "4-bit verify needs " + std::to_string(need * 4) + " B of vector LDS; " + std::to_string((int64_t)vec * 4) +
            " B are left";

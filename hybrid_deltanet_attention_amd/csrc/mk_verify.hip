@@ -1080,7 +1080,8 @@ __device__ __forceinline__ bool gemv_q4_v(const GemvQ4& G, int nt, LS float* P, 
                                           Pack pack, Epi epi) {
   const int S = uni(G.S), K = uni(G.K);
   nt = uni(nt);
-  const int gs = min(S, q4v_group_segs(pcap, nt));
+  // one group when every position's columns fit (then they are packed once for all row chunks)
+  const int gs = nt * K <= pcap && K <= 8 * MK_NT * Q4_PACK_IT ? S : min(S, q4v_group_segs(pcap, nt));
   const int ngroups = (S + gs - 1) / gs;
   const int rc = q4v_rows(S, nt);
   for (int r0 = 0; r0 == 0 || r0 < G.R; r0 += rc) {
@@ -1148,16 +1149,18 @@ __device__ __forceinline__ bool q4v_gather(const Ctx& cx, const Lds& s, const MK
 }
 
 // RMSNorm scales of nt residuals, rs[t] = 1 / sqrt(mean x_t^2 + eps), and this workgroup's residual
-// rows [d0, d1) of each position -> xr[t * rstride ..].  The residuals come in chunks of whole
+// rows [d0, d1) of each position -> xr[t * rstride ..].  whole: the residuals came in one gather and
+// are left at P + t * D.  The residuals come in chunks of whole
 // 1024-value strides of the 4-bit decode kernel's rmsnorm_gg (all positions per gather); wave t
 // carries position t's running per-lane sum through the chunks in exactly that kernel's order, so the
 // scale is bit-identical.
 __device__ __forceinline__ bool q4v_norm_scales(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D,
                                                 const LS int* toks, const MK_G mk_u64* src, int nt, float eps,
                                                 LS float* P, int pcap, LS float* rs, LS float* xr, int rstride,
-                                                int d0, int d1) {
+                                                int d0, int d1, bool& whole) {
   const int D4 = D >> 2;
   const int ch = max(1024, (pcap / nt) / 1024 * 1024);
+  whole = ch >= D;  // one gather: every position's residual is left at P + t * D
   float sq = 0.f;
   for (int a = 0; a < D; a += ch) {
     const int n = min(ch, D - a);
@@ -1196,11 +1199,13 @@ __device__ __forceinline__ bool q4v_norm_scales(const Ctx& cx, const Lds& s, con
 }
 
 // Packed normalised activations of columns [c0, c0 + n) for every position (position t at P + t * n):
-// x * rs[t] * g, as rmsnorm_gg scales, then q4_pack.
+// x * rs[t] * g, as rmsnorm_gg scales, then q4_pack.  resident: the norm left every whole residual
+// in P, so all columns need no second gather.
 __device__ __forceinline__ bool q4v_pack_norm(const Ctx& cx, const Lds& s, const MK_G uint16_t* E, int D,
                                               const LS int* toks, const MK_G mk_u64* src, int nt,
-                                              const MK_G uint16_t* g, const LS float* rs, int c0, int n, LS float* P) {
-  if (!q4v_gather(cx, s, E, D, toks, src, D, nt, c0, n, P)) return false;
+                                              const MK_G uint16_t* g, const LS float* rs, int c0, int n, LS float* P,
+                                              bool resident) {
+  if (!(resident && c0 == 0 && n == D) && !q4v_gather(cx, s, E, D, toks, src, D, nt, c0, n, P)) return false;
   const int n4 = n >> 2;
   for (int i = tid(); i < nt * n4; i += MK_NT) {
     const int t = i / n4, c = i - t * n4;
@@ -1213,6 +1218,22 @@ __device__ __forceinline__ bool q4v_pack_norm(const Ctx& cx, const Lds& s, const
   wg_bar();
   for (int t = 0; t < nt; ++t) q4_pack(P + t * n, n);
   return true;
+}
+
+// Packed activations of columns [c0, c0 + n) (n a multiple of 32) for every position from records
+// that already hold packed words -- position t's at src + t * stride, block b's Q4_XW words at
+// b * Q4_XW -- to P + t * n.  Every thread calls it; ends with a barrier.
+__device__ __forceinline__ bool q4v_gather_packed(const Ctx& cx, const Lds& s, const MK_G mk_u64* src, int stride,
+                                                  int nt, int c0, int n, LS float* P) {
+  const int pw = (n >> 5) * Q4_XW, w0 = (c0 >> 5) * Q4_XW;
+  const bool ok = gather_map_all(cx, nt * pw, [=](int f) {
+    const int t = f / pw;
+    return src + (size_t)t * stride + w0 + (f - t * pw);
+  }, [=](int f, float v) {
+    const int t = f / pw;
+    P[t * n + (f - t * pw)] = v;
+  });
+  return !wg_bar_or(s, !ok);
 }
 
 // Packed record vectors: columns [c0, c0 + n) of src[t][stride] for every position (at P + t * n).
@@ -1267,9 +1288,6 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
             0};
   tr.mark();
   {
-    const int nw = p.n_layers * (int)(sizeof(MkLayerDev) / 4);
-    const MK_G u32* dsrc = (const MK_G u32*)p.layers;
-    for (int i = tid(); i < nw; i += MK_NT) ((LS u32*)s.desc)[i] = dsrc[i];
     if (tid() < nt) toks[tid()] = p.vtok[tid()];
     const int half = p.hd / 2;
     for (int i = tid(); i < nt * half; i += MK_NT) {
@@ -1287,7 +1305,9 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
   // the 4-bit decode kernel's row slices: residual-sized projections and FFN pairs in whole 4-row
   // blocks, in-projection and LM-head rows by 4-row blocks
   const int d0 = 4 * split(D >> 2, NW, w), d1 = min(D, 4 * split(D >> 2, NW, w + 1));
-  const int j0 = 2 * split(F >> 1, NW, w), j1 = 2 * split(F >> 1, NW, w + 1);
+  // FFN hidden columns by whole 32-column blocks, so that each workgroup packs its own slice of the
+  // down projection's input once (the 4-bit decode kernel packs the same blocks from the same values)
+  const int j0 = 32 * split(F >> 5, NW, w), j1 = 32 * split(F >> 5, NW, w + 1);
   auto in_slice = [&](const MkLayerDev& Lx, GemvQ4& g, int& P0) {
     const int nbi = (Lx.rows_in + 3) >> 2;
     const int B0 = split(nbi, NW, w), B1 = split(nbi, NW, w + 1);
@@ -1295,13 +1315,15 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
     g.init(Lx.w_in, B0, max(0, min(4 * B1, Lx.rows_in) - 4 * B0), D);
   };
   const MK_G mk_u64* xsrc = nullptr;  // the residual's records (null: the embedding rows)
+  bool whole = false;                 // the last norm left every whole residual in s.vec
   for (int l = 0; l < p.n_layers; ++l) {
-    const MkLayerDev L = layer_desc(s.desc, l);
-    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1))
+    const MkLayerDev L = p.layers[l];  // read-only descriptors (uniform loads)
+    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1,
+                         whole))
       return;
     tr.mark();
     auto pack_in = [&](int c0, int n, LS float* P) {
-      return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12, rs, c0, n, P);
+      return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12, rs, c0, n, P, whole);
     };
     int P0;
     GemvQ4 gin;
@@ -1343,20 +1365,32 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
     }
     tr.mark();
     xsrc = L.ll_x1;
-    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1))
+    if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1,
+                         whole))
       return;
     {
       GemvQ4 ggu;
       ggu.init(L.w_gu, j0 >> 1, 2 * (j1 - j0), D);
+      // this workgroup's FFN hidden values [t][hw] in the LM head's argmax cells (not live here)
+      LS float* hb = s.att + MK_RED_CAP;
+      const int hw = j1 - j0;
       if (!gemv_q4_v<true>(
               ggu, nt, s.vec, pcap, s.att, ctr,
               [&](int c0, int n, LS float* P) {
-                return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12 + D, rs, c0, n, P);
+                return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, L.g12 + D, rs, c0, n, P, whole);
               },
-              [&](int j, int t, float gv, float uv) {
-                ll_put(L.ll_h + (size_t)t * F + j0 + j, cx.epoch, gv / (1.0f + expf(-gv)) * uv);
-              }))
+              [&](int j, int t, float gv, float uv) { hb[t * hw + j] = gv / (1.0f + expf(-gv)) * uv; }))
         return;
+      // pack the slice (blocks are packed independently, so position t's blocks follow t - 1's) and
+      // publish the packed words: position t's at ll_h + t * F, block b's at b * Q4_XW
+      if (hw > 0) {
+        q4_pack(hb, nt * hw);
+        const int pw = (hw >> 5) * Q4_XW;
+        for (int i = tid(); i < nt * pw; i += MK_NT) {
+          const int t = i / pw, r = i - t * pw;
+          ll_put(L.ll_h + (size_t)t * F + (j0 >> 5) * Q4_XW + r, cx.epoch, hb[t * pw + r]);
+        }
+      }
     }
     tr.mark();
     {
@@ -1364,7 +1398,7 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
       gdn.init(L.w_down, d0 >> 2, d1 - d0, F);
       if (!gemv_q4_v<false>(
               gdn, nt, s.vec, pcap, s.att, ctr,
-              [&](int c0, int n, LS float* P) { return q4v_pack_records(cx, s, L.ll_h, F, nt, c0, n, P); },
+              [&](int c0, int n, LS float* P) { return q4v_gather_packed(cx, s, L.ll_h, F, nt, c0, n, P); },
               [&](int r, int t, float v, float) {
                 ll_put(L.ll_x2 + (size_t)t * D + d0 + r, cx.epoch, s.x[t * rstride + r] + v);
               }))
@@ -1375,7 +1409,7 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
   }
 
   // final norm + tied LM head + per-position argmax (lowest index among equal maxima)
-  if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1))
+  if (!q4v_norm_scales(cx, s, p.embed, D, toks, xsrc, nt, p.rms_eps, s.vec, pcap, rs, s.x, rstride, d0, d1, whole))
     return;
   {
     LS float* amv = s.att + MK_RED_CAP;  // running argmax per (position, streaming thread)
@@ -1393,7 +1427,7 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
     const bool hok = gemv_q4_v<false>(
         gl, nt, s.vec, pcap, s.att, ctr,
         [&](int c0, int n, LS float* P) {
-          return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, p.g_final, rs, c0, n, P);
+          return q4v_pack_norm(cx, s, p.embed, D, toks, xsrc, nt, p.g_final, rs, c0, n, P, whole);
         },
         [&](int r, int t, float v, float) {
                        const int idx = v0 + r;
@@ -1432,6 +1466,14 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
       }
     }
   }
+  // the rollback walks every layer's descriptor: the table goes to the tail of the vector region,
+  // which is free from here on
+  {
+    const int nw = p.n_layers * (int)(sizeof(MkLayerDev) / 4);
+    const MK_G u32* dsrc = (const MK_G u32*)p.layers;
+    for (int i = tid(); i < nw; i += MK_NT) ((LS u32*)s.desc)[i] = dsrc[i];
+  }
+  wg_bar();
   verify_accept_rollback(p, cx, s, toks, NW, w, pos, nt, tr);
 }
 
