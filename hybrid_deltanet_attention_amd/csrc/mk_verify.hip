@@ -397,15 +397,116 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
   LS float* kc = qv + nt * gs * hd;    // [C][hd]
   LS float* vc = kc + C * hd;          // [C][hd]
   LS float* pb = vc + C * hd;          // [nt][gs][C] probabilities (unnormalised)
-  LS float* ml = pb + nt * gs * C;     // [nt][gs][2] this chunk's max and sum
-  LS float* racc = ml + 2 * nt * gs;   // [nt][gs][hd] running acc of the item
+  LS float* mf = pb + nt * gs * C;     // [nt][gs][2] this chunk's merge factors (running acc, chunk acc)
+  LS float* racc = mf + 2 * nt * gs;   // [nt][gs][hd] running acc of the item
   LS float* rml = racc + nt * gs * hd; // [2 (chunk parity)][nt][gs][2] running max and sum
   const MK_G mk_u64* llq = L.ll_in;
   const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   const MK_G mk_u64* llv = llk + nkv * hd;
   const size_t tstride = (size_t)p.max_items * gs * (hd + 2);  // partial records per position
+  const int h4 = hd >> 2;
+  // Keys and values of the positions already in the cache, loaded by the streaming threads one chunk
+  // ahead into registers (raw cache words; up to ATT_C * 64 four-value groups per chunk)
+  constexpr int KVR = (ATT_C * 64 + MK_NCT - 1) / MK_NCT;
+  u32x4 rk[KVR], rv[KVR];
+  float rks[KVR], rvs[KVR];
+  int pf_n = 0;  // four-value groups held for the chunk to come (per workgroup)
+  auto kv_fetch = [&](int itn, int cn) {
+    pf_n = 0;
+    if (itn >= items) return;
+    const int g = itn - (itn / nkv) * nkv, j0 = cn * C;
+    pf_n = max(0, min(pos, min(Lmax, j0 + C)) - j0) * h4;
+    if (!streamer()) return;
+#pragma unroll
+    for (int e = 0; e < KVR; ++e) {
+      const int x = tid() + e * NCT;
+      if (x < pf_n) {
+        const int jj = x / h4, d = (x - jj * h4) * 4;
+        const size_t gi = ((size_t)g * p.max_ctx + j0 + jj) * hd + d;
+        if (p.kvt == MK_KV_F32) {
+          rk[e] = *(const MK_G u32x4*)(L.Kc + gi);
+          rv[e] = *(const MK_G u32x4*)(L.Vc + gi);
+        } else if (p.kvt == MK_KV_F16) {
+          const u32x2 a = *(const MK_G u32x2*)((const MK_G _Float16*)L.Kc + gi);
+          const u32x2 b = *(const MK_G u32x2*)((const MK_G _Float16*)L.Vc + gi);
+          rk[e] = u32x4{a.x, a.y, 0u, 0u};
+          rv[e] = u32x4{b.x, b.y, 0u, 0u};
+        } else {
+          rk[e].x = *(const MK_G u32*)((const MK_G signed char*)L.Kc + gi);
+          rv[e].x = *(const MK_G u32*)((const MK_G signed char*)L.Vc + gi);
+          rks[e] = L.Ks[gi / MK_KV_Q8_BLOCK];
+          rvs[e] = L.Vs[gi / MK_KV_Q8_BLOCK];
+        }
+      }
+    }
+  };
+  // the held groups -> kc / vc rows in FP32 (the decode kernel's expansion of the same rows)
+  auto kv_stash = [&]() {
+    if (!streamer()) return;
+#pragma unroll
+    for (int e = 0; e < KVR; ++e) {
+      const int x = tid() + e * NCT;
+      if (x < pf_n) {
+        const int jj = x / h4, d = (x - jj * h4) * 4;
+        f32x4 kk, vv;
+        if (p.kvt == MK_KV_F32) {
+          kk = f32x4{__uint_as_float(rk[e].x), __uint_as_float(rk[e].y), __uint_as_float(rk[e].z),
+                     __uint_as_float(rk[e].w)};
+          vv = f32x4{__uint_as_float(rv[e].x), __uint_as_float(rv[e].y), __uint_as_float(rv[e].z),
+                     __uint_as_float(rv[e].w)};
+        } else if (p.kvt == MK_KV_F16) {
+          kk = f32x4{half_bits_f32(rk[e].x & 0xffffu), half_bits_f32(rk[e].x >> 16), half_bits_f32(rk[e].y & 0xffffu),
+                     half_bits_f32(rk[e].y >> 16)};
+          vv = f32x4{half_bits_f32(rv[e].x & 0xffffu), half_bits_f32(rv[e].x >> 16), half_bits_f32(rv[e].y & 0xffffu),
+                     half_bits_f32(rv[e].y >> 16)};
+        } else {
+          const float ks = rks[e], vs = rvs[e];
+          kk = f32x4{i8_f32(rk[e].x, 0) * ks, i8_f32(rk[e].x, 1) * ks, i8_f32(rk[e].x, 2) * ks, i8_f32(rk[e].x, 3) * ks};
+          vv = f32x4{i8_f32(rv[e].x, 0) * vs, i8_f32(rv[e].x, 1) * vs, i8_f32(rv[e].x, 2) * vs, i8_f32(rv[e].x, 3) * vs};
+        }
+        *(LS f32x4*)(kc + jj * hd + d) = kk;
+        *(LS f32x4*)(vc + jj * hd + d) = vv;
+      }
+    }
+  };
+  // q0 . k and q1 . k over the chunk slot's key row (loaded once for both), each in the decode
+  // kernel's order: four-value groups starting at group jj mod (hd / 4), wrapping around
+  auto qk2 = [&](const LS float* kr, const LS float* qr0, const LS float* qr1, int jj, float& a0, float& a1) {
+    const int n4 = hd >> 2;
+    const int start = jj % n4;
+    a0 = 0.f;
+    a1 = 0.f;
+    for (int d0 = 0; d0 < n4; d0 += 8) {
+      f32x4 kk[8], q0[8], q1[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        int dd = d0 + x + start;
+        dd = (dd >= n4 ? dd - n4 : dd) * 4;
+        kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        q0[x] = kk[x];
+        q1[x] = kk[x];
+        if (d0 + x < n4) {
+          kk[x] = *(const LS f32x4*)(kr + dd);
+          q0[x] = *(const LS f32x4*)(qr0 + dd);
+          q1[x] = *(const LS f32x4*)(qr1 + dd);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        a0 = fmaf(kk[x].x, q0[x].x, a0);
+        a1 = fmaf(kk[x].x, q1[x].x, a1);
+        a0 = fmaf(kk[x].y, q0[x].y, a0);
+        a1 = fmaf(kk[x].y, q1[x].y, a1);
+        a0 = fmaf(kk[x].z, q0[x].z, a0);
+        a1 = fmaf(kk[x].z, q1[x].z, a1);
+        a0 = fmaf(kk[x].w, q0[x].w, a0);
+        a1 = fmaf(kk[x].w, q1[x].w, a1);
+      }
+    }
+  };
   int gq = -1;  // KV head whose queries are in qv
   int k = 0;    // chunk sequence number in this workgroup (running-value parity)
+  if (w < items) kv_fetch(w, (w / nkv) * cpi);
   for (int it = w; it < items; it += NW) {
     const int blk = it / nkv, g = it - blk * nkv;
     const int c0 = blk * cpi, c1 = min(nch, c0 + cpi);
@@ -415,121 +516,112 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
       const int jend = min(Lmax, j0 + C);
       const int jnew = max(j0, pos);
       const int nnew = max(0, jend - jnew);
+      kv_stash();
       const int nqr = g != gq ? nt * gs * hd : 0;  // queries: once per KV head
       gq = g;
       const int nkvr = nnew * hd;
-      const bool ok = gather_map_all(cx, nqr + 2 * nkvr, [=](int f) {
-        if (f < nqr) {
-          const int tt = f / (gs * hd), r = f - tt * gs * hd;
-          return llq + (size_t)tt * rows_in + g * gs * hd + r;
-        }
-        f -= nqr;
-        const int sel = f >= nkvr ? 1 : 0;
-        f -= sel * nkvr;
-        const int jj = f / hd, d = f - jj * hd;
-        return (sel ? llv : llk) + (size_t)(jnew + jj - pos) * rows_in + g * hd + d;
-      }, [=](int f, float v) {
-        if (f < nqr) {
-          qv[f] = v;
-        } else {
+      bool ok = true;
+      if (nqr + 2 * nkvr > 0) {
+        ok = gather_map_all(cx, nqr + 2 * nkvr, [=](int f) {
+          if (f < nqr) {
+            const int tt = f / (gs * hd), r = f - tt * gs * hd;
+            return llq + (size_t)tt * rows_in + g * gs * hd + r;
+          }
           f -= nqr;
           const int sel = f >= nkvr ? 1 : 0;
           f -= sel * nkvr;
           const int jj = f / hd, d = f - jj * hd;
-          (sel ? vc : kc)[(jnew - j0 + jj) * hd + d] = v;
-        }
-      });
-      if (streamer()) {
-        const int nold = min(pos, jend) - j0;  // cached positions of the chunk (may be <= 0)
-        const int h4 = hd >> 2;
-        for (int x = tid(); x < nold * h4; x += NCT) {
-          const int jj = x / h4, d = (x - jj * h4) * 4;
-          const size_t gi = ((size_t)g * p.max_ctx + j0 + jj) * hd + d;
-          f32x4 kk, vv;
-          if (p.kvt == MK_KV_F32) {
-            kk = *(const MK_G f32x4*)(L.Kc + gi);
-            vv = *(const MK_G f32x4*)(L.Vc + gi);
-          } else if (p.kvt == MK_KV_F16) {
-            // the decode kernel's expansion of the same rows (mk_device.h, kv_expand)
-            const u32x2 a = *(const MK_G u32x2*)((const MK_G _Float16*)L.Kc + gi);
-            const u32x2 b = *(const MK_G u32x2*)((const MK_G _Float16*)L.Vc + gi);
-            kk = f32x4{half_bits_f32(a.x & 0xffffu), half_bits_f32(a.x >> 16), half_bits_f32(a.y & 0xffffu),
-                       half_bits_f32(a.y >> 16)};
-            vv = f32x4{half_bits_f32(b.x & 0xffffu), half_bits_f32(b.x >> 16), half_bits_f32(b.y & 0xffffu),
-                       half_bits_f32(b.y >> 16)};
+          return (sel ? llv : llk) + (size_t)(jnew + jj - pos) * rows_in + g * hd + d;
+        }, [=](int f, float v) {
+          if (f < nqr) {
+            qv[f] = v;
           } else {
-            const u32 a = *(const MK_G u32*)((const MK_G signed char*)L.Kc + gi);
-            const u32 b = *(const MK_G u32*)((const MK_G signed char*)L.Vc + gi);
-            const float ks = L.Ks[gi / MK_KV_Q8_BLOCK], vs = L.Vs[gi / MK_KV_Q8_BLOCK];
-            kk = f32x4{i8_f32(a, 0) * ks, i8_f32(a, 1) * ks, i8_f32(a, 2) * ks, i8_f32(a, 3) * ks};
-            vv = f32x4{i8_f32(b, 0) * vs, i8_f32(b, 1) * vs, i8_f32(b, 2) * vs, i8_f32(b, 3) * vs};
+            f -= nqr;
+            const int sel = f >= nkvr ? 1 : 0;
+            f -= sel * nkvr;
+            const int jj = f / hd, d = f - jj * hd;
+            (sel ? vc : kc)[(jnew - j0 + jj) * hd + d] = v;
           }
-          *(LS f32x4*)(kc + jj * hd + d) = kk;
-          *(LS f32x4*)(vc + jj * hd + d) = vv;
-        }
+        });
       }
+      // the next chunk's cached rows load while this one is processed (after the gather, whose
+      // final wait would otherwise drain them)
+      if (c + 1 < c1) kv_fetch(it, c + 1);
+      else kv_fetch(it + NW, ((it + NW) / nkv) * cpi);
       if (wg_bar_or(s, !ok)) return false;
       // this launch's positions in the chunk take the cache's values and are appended (barriers inside)
       if (p.kvt != MK_KV_F32 && nnew > 0)
         kv_round_append(p, L, kc + (jnew - j0) * hd, vc + (jnew - j0) * hd, nnew, pb, g, jnew);
-      // scores, softmax numerators, row max and sum: one thread per (position, head, slot), whole
-      // 16-lane rows
+      // scores, softmax numerators, row max and sum: one thread per (position, head, slot) of the
+      // first half of the rows and the row of the same slot one half further on (so the key row is
+      // loaded once for both), whole 16-lane rows.  The slot-0 thread of each row also forms the
+      // row's merge with the item's running values (the decode kernel's formula) -> merge factors,
+      // and the running or published (max, sum).
+      const LS float* rin = rml + (k & 1) * 2 * nt * gs;   // running (max, sum) before this chunk
+      LS float* rout = rml + ((k + 1) & 1) * 2 * nt * gs;  // ... and after it
+      const bool first = c == c0;
       const int nrow = (nt - tmin) * gs * C;
-      for (int b0 = 0; b0 < nrow; b0 += MK_NT) {
-        const int f = b0 + tid();
-        if (f < nrow) {
-          const int tt = f / (gs * C), r = f - tt * gs * C;
-          const int i = r / C, jj = r - i * C;
-          const int t = tmin + tt;
+      const int nh = ((nrow / C + 1) / 2) * C;  // rows of the first half (whole 16-lane rows)
+      for (int b0 = 0; b0 < nh; b0 += MK_NT) {
+        int fr[2];
+        fr[0] = b0 + tid();
+        fr[1] = fr[0] + nh;
+        float a[2] = {0.f, 0.f};
+        int tt[2], ii[2], jq[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int f = min(fr[u], nrow - 1);
+          tt[u] = f / (gs * C);
+          const int r = f - tt[u] * gs * C;
+          ii[u] = r / C;
+          jq[u] = r - ii[u] * C;
+        }
+        if (fr[0] < nh)
+          qk2(kc + jq[0] * hd, qv + ((tmin + tt[0]) * gs + ii[0]) * hd, qv + ((tmin + tt[1]) * gs + ii[1]) * hd, jq[0],
+              a[0], a[1]);
+        for (int u = 0; u < 2; ++u) {
+          const int t = tmin + tt[u], i = ii[u], jj = jq[u];
           const int nj = min(pos + t + 1, j0 + C) - j0;
-          const bool valid = jj < nj;
-          float scv = -INFINITY;
-          if (valid) {
-            const LS float* kr = kc + jj * hd;
-            const LS float* qr = qv + (t * gs + i) * hd;
-            const int n4 = hd >> 2;
-            const int start = jj % n4;
-            float a = 0.f;
-            for (int d0 = 0; d0 < n4; d0 += 8) {
-              f32x4 kk[8], qq[8];
-#pragma unroll
-              for (int x = 0; x < 8; ++x) {
-                int dd = d0 + x + start;
-                dd = (dd >= n4 ? dd - n4 : dd) * 4;
-                kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-                qq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (d0 + x < n4) {
-                  kk[x] = *(const LS f32x4*)(kr + dd);
-                  qq[x] = *(const LS f32x4*)(qr + dd);
-                }
-              }
-#pragma unroll
-              for (int x = 0; x < 8; ++x) {
-                a = fmaf(kk[x].x, qq[x].x, a);
-                a = fmaf(kk[x].y, qq[x].y, a);
-                a = fmaf(kk[x].z, qq[x].z, a);
-                a = fmaf(kk[x].w, qq[x].w, a);
-              }
-            }
-            scv = a * scale;
-          }
+          const bool valid = fr[0] < nh && fr[u] < nrow && jj < nj;
+          const float scv = valid ? a[u] * scale : -INFINITY;
           const float m = row_max16(scv);
           const float e = valid ? expf(scv - m) : 0.f;
           const float l = row_sum16(e);
-          pb[(t * gs + i) * C + jj] = e;
-          if (jj == 0) {
-            ml[2 * (t * gs + i)] = m;
-            ml[2 * (t * gs + i) + 1] = l;
+          if (fr[0] < nh && fr[u] < nrow) {
+            const int ti = t * gs + i;
+            pb[ti * C + jj] = e;
+            if (jj == 0) {
+              // position t's chunks of this item: c0 .. its last visible chunk
+              const bool last = c + 1 == min(c1, (pos + t) / C + 1);
+              float M = m, S = l, fr0 = 0.f, fr1 = 1.f;
+              if (!first) {
+                const float Mr = rin[2 * ti], Sr = rin[2 * ti + 1];
+                const float Mn = fmaxf(Mr, M);
+                const float f = expf(Mr - Mn), f1 = expf(M - Mn);
+                S = fmaf(Sr, f, S * f1);
+                M = Mn;
+                fr0 = f;
+                fr1 = f1;
+              }
+              mf[2 * ti] = fr0;
+              mf[2 * ti + 1] = fr1;
+              if (last) {
+                MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2) + i * (hd + 2);
+                ll_put(part, cx.epoch, M);
+                ll_put(part + 1, cx.epoch, S);
+              } else {
+                rout[2 * ti] = M;
+                rout[2 * ti + 1] = S;
+              }
+            }
           }
         }
       }
       wg_bar();
       {
         // weighted values: thread (d, tg) keeps column d of the chunk's values in registers and
-        // produces the (position, head) rows tg, tg + NG, ...; each output still adds its 16 products
-        // in slot order, then merges with the item's running values
-        const LS float* rin = rml + (k & 1) * 2 * nt * gs;   // running (max, sum) before this chunk
-        LS float* rout = rml + ((k + 1) & 1) * 2 * nt * gs;  // ... and after it
+        // produces the (position, head) rows tg, tg + NG, ...; each output adds its 16 products in
+        // slot order, then merges with the item's running acc by the row's factors
         const int NG = MK_NT / hd, nrows = (nt - tmin) * gs;
         const int d = tid() % hd, tg = tid() / hd;
         if (tg < NG) {
@@ -544,39 +636,31 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
             f32x4 pw[ATT_C / 4];
 #pragma unroll
             for (int q = 0; q < ATT_C / 4; ++q) pw[q] = *(const LS f32x4*)(pb + ti * C + 4 * q);
-            float a = 0.f;
+            float acc = 0.f;
+            if (nj >= ATT_C) {
 #pragma unroll
-            for (int q = 0; q < ATT_C / 4; ++q) {
-              a = fmaf(pw[q].x, 4 * q + 0 < nj ? vcol[4 * q + 0] : 0.f, a);
-              a = fmaf(pw[q].y, 4 * q + 1 < nj ? vcol[4 * q + 1] : 0.f, a);
-              a = fmaf(pw[q].z, 4 * q + 2 < nj ? vcol[4 * q + 2] : 0.f, a);
-              a = fmaf(pw[q].w, 4 * q + 3 < nj ? vcol[4 * q + 3] : 0.f, a);
-            }
-            // position t's chunks of this item: c0 .. its last visible chunk
-            const bool first = c == c0;
-            const bool last = c + 1 == min(c1, (pos + t) / C + 1);
-            float M = ml[2 * ti], S = ml[2 * ti + 1];
-            if (!first) {
-              const float Mr = rin[2 * ti], Sr = rin[2 * ti + 1];
-              const float Mn = fmaxf(Mr, M);
-              const float f = expf(Mr - Mn), f1 = expf(M - Mn);
-              a = fmaf(racc[ti * hd + d], f, a * f1);
-              S = fmaf(Sr, f, S * f1);
-              M = Mn;
-            }
-            if (last) {
-              MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2) + i * (hd + 2);
-              ll_put(part + 2 + d, cx.epoch, a);
-              if (d == 0) {
-                ll_put(part, cx.epoch, M);
-                ll_put(part + 1, cx.epoch, S);
+              for (int q = 0; q < ATT_C / 4; ++q) {
+                acc = fmaf(pw[q].x, vcol[4 * q + 0], acc);
+                acc = fmaf(pw[q].y, vcol[4 * q + 1], acc);
+                acc = fmaf(pw[q].z, vcol[4 * q + 2], acc);
+                acc = fmaf(pw[q].w, vcol[4 * q + 3], acc);
               }
             } else {
-              racc[ti * hd + d] = a;
-              if (d == 0) {
-                rout[2 * ti] = M;
-                rout[2 * ti + 1] = S;
+#pragma unroll
+              for (int q = 0; q < ATT_C / 4; ++q) {
+                acc = fmaf(pw[q].x, 4 * q + 0 < nj ? vcol[4 * q + 0] : 0.f, acc);
+                acc = fmaf(pw[q].y, 4 * q + 1 < nj ? vcol[4 * q + 1] : 0.f, acc);
+                acc = fmaf(pw[q].z, 4 * q + 2 < nj ? vcol[4 * q + 2] : 0.f, acc);
+                acc = fmaf(pw[q].w, 4 * q + 3 < nj ? vcol[4 * q + 3] : 0.f, acc);
               }
+            }
+            if (!first) acc = fmaf(racc[ti * hd + d], mf[2 * ti], acc * mf[2 * ti + 1]);
+            const bool last = c + 1 == min(c1, (pos + t) / C + 1);
+            if (last) {
+              MK_G mk_u64* part = L.ll_part + (size_t)t * tstride + (size_t)it * gs * (hd + 2) + i * (hd + 2);
+              ll_put(part + 2 + d, cx.epoch, acc);
+            } else {
+              racc[ti * hd + d] = acc;
             }
           }
         }
