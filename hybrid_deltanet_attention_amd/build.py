@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmk.so")
-SOURCES = ["mk_api.cpp", "mk_decode.hip", "mk_decode_q4.hip", "mk_prefill.hip", "mk_verify.hip", "mk_noalloc.hip"]
+SOURCES = ["mk_api.cpp", "mk_decode.hip", "mk_decode_q4.hip", "mk_prefill.hip", "mk_prefill_q4.hip", "mk_verify.hip",
+           "mk_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -132,8 +132,9 @@ struct Layout {
   size_t vdescs, v_am, v_acc;
   int64_t snap_stride;  // floats between the snapshots of consecutive positions
   // prefill scratch: a chunk of up to pf_T tokens
-  int pf_T, pf_lda, pf_ldy;
+  int pf_T, pf_lda, pf_ldy, pf_ldh;
   size_t pf_x, pf_ahi, pf_alo, pf_hhi, pf_hlo, pf_y, pf_qk, pf_ab, pf_q, pf_part, pf_ch, pf_sk;
+  size_t pf_wq;   // 4-bit weights: one matrix expanded to rows [W_hi | W_lo] of BF16
   size_t pf_kvf;  // compact KV caches: a chunk's rotated keys and values in FP32, [2][nkv][T][hd]
 };
 
@@ -232,20 +233,29 @@ Layout make_layout(const mk_config& c) {
   }
   L.ndescs = take(sizeof(MkLayerDev) * c.n_layers);
   L.scratch = take(4096);
-  // prefill scratch (4-bit models run their prompts through the decode kernel and need none)
-  if (!q4) {
+  // prefill scratch.  With 4-bit weights every GEMM runs over 2K columns ([A_hi | A_hi] and
+  // [A_lo | 0] against [W_hi | W_lo]), so the activation rows are twice as wide, and one matrix at a
+  // time is expanded into pf_wq.
+  {
     const int64_t T = std::min(c.max_ctx, 1024);
     const int64_t kmax = std::max(std::max(D, (int64_t)c.ffn), std::max(H * c.dn_dv, (int64_t)c.n_q_heads * c.head_dim));
     const int64_t ndn = 2 * H * c.dn_dk + H * c.dn_dv + 2 * H;
     const int64_t natt = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+    const int64_t wide = q4 ? 2 : 1;
     L.pf_T = (int)T;
-    L.pf_lda = (int)((kmax + 7) / 8 * 8);
+    L.pf_lda = (int)((wide * kmax + 7) / 8 * 8);
+    L.pf_ldh = (int)(wide * c.ffn);
     L.pf_ldy = (int)((std::max(ndn, natt) + 3) / 4 * 4);  // rows 16-byte aligned
     L.pf_x = take((size_t)T * D * 4);
     L.pf_ahi = take((size_t)T * L.pf_lda * 2);
     L.pf_alo = take((size_t)T * L.pf_lda * 2);
-    L.pf_hhi = take((size_t)T * c.ffn * 2);
-    L.pf_hlo = take((size_t)T * c.ffn * 2);
+    L.pf_hhi = take((size_t)T * L.pf_ldh * 2);
+    L.pf_hlo = take((size_t)T * L.pf_ldh * 2);
+    if (q4) {
+      int64_t wmax = std::max(2 * (int64_t)c.ffn * D, D * (int64_t)c.ffn);
+      for (const LayerOff& lo : L.layers) wmax = std::max(wmax, std::max(lo.rows_in * D, D * lo.k_out));
+      L.pf_wq = take((size_t)wmax * 2 * 2);
+    }
     L.pf_y = take((size_t)T * L.pf_ldy * 4);
     L.pf_qk = take((size_t)T * H * 2 * c.dn_dk * 4);
     L.pf_ab = take((size_t)T * H * 2 * 4);
@@ -1045,9 +1055,12 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   const mk_config& c = ctx->cfg;
   const int gs = c.n_q_heads / c.n_kv_heads;
   const int kvt = ctx->base.kvt;
-  if (16 % gs != 0 || ctx->base.wq4 || (kvt != MK_KV_F32 && c.head_dim != 64 && c.head_dim != 128)) {
-    // 4-bit weights, or shapes the prefill attention tiling does not cover (compact KV caches are
-    // read by the matrix-core attention only): token by token through the decode kernel
+  const bool q4 = ctx->base.wq4;
+  // the matrix-core attention (head size 64 or 128) takes any head grouping and cache type; the
+  // VALU one needs groups dividing 16 and an FP32 cache
+  const bool mfma_att = c.head_dim == 64 || c.head_dim == 128;
+  if (!mfma_att && (16 % gs != 0 || kvt != MK_KV_F32)) {
+    // shapes the prefill attention does not cover: token by token through the decode kernel
     int32_t* scratch_tok = (int32_t*)(ctx->ws + ctx->lay.scratch) + 8;
     for (int32_t i = 0; i < n; ++i) {
       const bool last = (i == n - 1);
@@ -1070,28 +1083,44 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
   float* QK = (float*)(ws + L.pf_qk);
   float* AB = (float*)(ws + L.pf_ab);
   float* Q = (float*)(ws + L.pf_q);
-  const int lda = L.pf_lda, ldy = L.pf_ldy;
+  const int lda = L.pf_lda, ldy = L.pf_ldy, ldh = L.pf_ldh;
   float* PK = (float*)(ws + L.pf_sk);
   const size_t PKN = PF_SPLITK_FLOATS;
   MkCtl* ctl = (MkCtl*)(ws + L.ctl);
   const float* rcos = (const float*)(ws + L.rope_cos);
   const float* rsin = (const float*)(ws + L.rope_sin);
   const uint16_t* embed = (const uint16_t*)(ws + L.embed);
+  uint16_t* Wq = q4 ? (uint16_t*)(ws + L.pf_wq) : nullptr;
+  // a GEMM's weights and inner size: BF16 weights as stored, or a 4-bit matrix expanded to
+  // [W_hi | W_lo] with its activations (hi, lo, leading dimension ld) widened to match
   int rc = 0;
+  int T = 0;  // tokens of the current chunk
+  auto operand = [&](uint16_t* hi, uint16_t* lo, int ld, const uint16_t* w, int N, int K, int& KK) -> const uint16_t* {
+    if (!q4) {
+      KK = K;
+      return w;
+    }
+    rc |= mk_pf_widen(hi, lo, ld, T, K, st);
+    rc |= mk_pf_q4_expand(w, N, K, Wq, st);
+    KK = 2 * K;
+    return Wq;
+  };
+  // the 4-bit path leaves the last prompt token to a decode launch, which forms its logits
+  const int32_t ngemm = q4 ? n - 1 : n;
   int p0 = ctx->pos_host;
-  int T = 0;
-  for (int c0 = 0; c0 < n && !rc; c0 += T) {
-    T = std::min(L.pf_T, n - c0);
-    rc |= mk_pf_embed(d_tokens + c0, T, embed, D, c.vocab, X, ctl, st);
+  for (int c0 = 0; c0 < ngemm && !rc; c0 += T) {
+    T = std::min(L.pf_T, ngemm - c0);
+    if (q4) rc |= mk_pf_embed_q4(d_tokens + c0, T, embed, D, c.vocab, X, ctl, st);
+    else rc |= mk_pf_embed(d_tokens + c0, T, embed, D, c.vocab, X, ctl, st);
     rc |= mk_pf_rms_split(X, T, D, (const uint16_t*)(ws + L.layers[0].g12), c.rms_eps, Ahi, Alo, lda, st);
     for (int l = 0; l < c.n_layers && !rc; ++l) {
       const LayerOff& lo = L.layers[l];
       const uint16_t* g12 = (const uint16_t*)(ws + lo.g12);
-      const uint16_t* w_in = (const uint16_t*)(ws + lo.w_in);
-      const uint16_t* w_out = (const uint16_t*)(ws + lo.w_out);
       // the next layer's input norm rides on this layer's last residual add
       const uint16_t* g_next = l + 1 < c.n_layers ? (const uint16_t*)(ws + L.layers[l + 1].g12) : nullptr;
-      rc |= mk_pf_gemm(0, Ahi, Alo, lda, T, D, w_in, (int)lo.rows_in, Y, ldy, nullptr, nullptr, 0, PK, PKN, st);
+      int K;
+      const uint16_t* W = operand(Ahi, Alo, lda, (const uint16_t*)(ws + lo.w_in), (int)lo.rows_in, D, K);
+      rc |= mk_pf_gemm(0, Ahi, Alo, lda, T, K, W, (int)lo.rows_in, Y, ldy, nullptr, nullptr, 0, PK, PKN, st);
       if (is_attention(c, l)) {
         float* Kc = (float*)(ws + lo.Kc);
         float* Vc = (float*)(ws + lo.Vc);
@@ -1112,21 +1141,27 @@ int mk_prefill(mk_ctx* ctx, const int32_t* d_tokens, int32_t n, int32_t* d_next,
         rc |= mk_pf_dn_scan((float*)(ws + lo.S), QK, AB, Y, ldy, T, H, dk, dv, c.l2_eps, Ahi, Alo, lda,
                             (float*)(ws + L.pf_ch), st);
       }
-      rc |= mk_pf_gemm_res(Ahi, Alo, lda, T, (int)lo.k_out, w_out, D, X, D, PK, PKN, g12 + D, c.rms_eps, Ahi, Alo,
-                           lda, st);
-      rc |= mk_pf_gemm(2, Ahi, Alo, lda, T, D, (const uint16_t*)(ws + lo.w_gu), 2 * F, nullptr, 0, Hhi, Hlo, F, PK, PKN,
-                       st);
-      rc |= mk_pf_gemm_res(Hhi, Hlo, F, T, F, (const uint16_t*)(ws + lo.w_down), D, X, D, PK, PKN, g_next, c.rms_eps,
-                           Ahi, Alo, lda, st);
+      W = operand(Ahi, Alo, lda, (const uint16_t*)(ws + lo.w_out), D, (int)lo.k_out, K);
+      rc |= mk_pf_gemm_res(Ahi, Alo, lda, T, K, W, D, X, D, PK, PKN, g12 + D, c.rms_eps, Ahi, Alo, lda, st);
+      W = operand(Ahi, Alo, lda, (const uint16_t*)(ws + lo.w_gu), 2 * F, D, K);
+      rc |= mk_pf_gemm(2, Ahi, Alo, lda, T, K, W, 2 * F, nullptr, 0, Hhi, Hlo, ldh, PK, PKN, st);
+      W = operand(Hhi, Hlo, ldh, (const uint16_t*)(ws + lo.w_down), D, F, K);
+      rc |= mk_pf_gemm_res(Hhi, Hlo, ldh, T, K, W, D, X, D, PK, PKN, g_next, c.rms_eps, Ahi, Alo, lda, st);
     }
     p0 += T;
   }
-  if (!rc) {
-    float* part = (float*)(ws + L.pf_part);
-    rc |= mk_pf_lmhead(X + (size_t)(T - 1) * D, D, (const uint16_t*)(ws + L.g_final), c.rms_eps, embed, c.vocab,
-                       d_logits, part, PF_LM_WG, st);
-    rc |= mk_pf_finish(part, PF_LM_WG, d_next, ctl, p0, st);
+  if (rc) return fail(ctx, MK_E_HIP, "prefill launch failed");
+  if (q4) {
+    // the last token: one 4-bit decode launch at position p0 (LM head and greedy choice included)
+    if (ngemm > 0 && mk_launch_set_ctl(ctl, p0, 0, 0, st)) return fail(ctx, MK_E_HIP, "prefill launch failed");
+    ctx->pos_host = p0;
+    ctx->pos_exact = true;
+    return mk_decode_step(ctx, d_tokens + n - 1, d_next, d_logits);
   }
+  float* part = (float*)(ws + L.pf_part);
+  rc |= mk_pf_lmhead(X + (size_t)(T - 1) * D, D, (const uint16_t*)(ws + L.g_final), c.rms_eps, embed, c.vocab,
+                     d_logits, part, PF_LM_WG, st);
+  rc |= mk_pf_finish(part, PF_LM_WG, d_next, ctl, p0, st);
   if (rc) return fail(ctx, MK_E_HIP, "prefill launch failed");
   ctx->pos_host = p0;
   return MK_OK;

@@ -172,6 +172,11 @@ int mk_pf_attention(const float* Q, const void* Kc, const void* Vc, int kvt, con
 int mk_pf_lmhead(const float* x, int D, const uint16_t* g, float eps, const uint16_t* E, int vocab, float* logits,
                  float* part, int nwg, void* stream);
 int mk_pf_finish(const float* part, int nwg, int32_t* next, MkCtl* ctl, int32_t pos, void* stream);
+// 4-bit prefill (mk_prefill_q4.hip): a tiled 4-bit matrix -> rows [W_hi | W_lo] of 2K BF16 values;
+// 4-bit embedding rows -> FP32; activations -> [A_hi | A_hi], [A_lo | 0]
+int mk_pf_q4_expand(const void* T, int N, int K, uint16_t* Wd, void* stream);
+int mk_pf_embed_q4(const int32_t* tok, int T, const void* E, int D, int vocab, float* X, MkCtl* ctl, void* stream);
+int mk_pf_widen(uint16_t* Ahi, uint16_t* Alo, int ld, int T, int K, void* stream);
 #ifdef __cplusplus
 }
 #endif

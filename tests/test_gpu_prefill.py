@@ -4,8 +4,11 @@ Prefill leaves the DeltaNet state and the KV cache exactly where token-by-token 
 returns the last position's logits and greedy token.  Cases: a prompt alone (state and cache
 checked right after prefill), a prompt longer than one prefill chunk (1024 tokens), a prefill that
 continues a context built by an earlier prefill and decode steps, a head grouping the prefill
-attention tiling does not cover (handled token by token), and DeltaNet key widths that do not fill
-the chunk kernels' tiles or exceed them.  Bars as in test_gpu_parity.
+attention tiling does not cover (handled token by token), three query heads per KV head on the
+matrix-core attention (a partly filled head group), DeltaNet key widths that do not fill the chunk
+kernels' tiles or exceed them, and 4-bit (Q4G32) weights: every GEMM over 2K columns against the
+weights expanded to BF16 high and low parts, the last prompt token through one 4-bit decode launch.
+Bars as in test_gpu_parity.
 """
 import numpy as np
 import pytest
@@ -142,4 +145,43 @@ def test_prefill_key_widths(heads, dk, dv):
     assert e <= LOGIT_TOL
     assert nxt == int(np.argmax(lg))
     _check_state(m, cfg, fwd, 100)
+    m.close()
+
+
+def test_prefill_mfma_attention_partial_head_group():
+    # 6 query heads over 2 KV heads at head size 64: the matrix-core attention's group of four query
+    # heads is partly filled (three heads live)
+    cfg = synth.get_config("tiny", n_q_heads=6, n_kv_heads=2, head_dim=64)
+    W = synth.make_weights(cfg, 6)
+    prompt = synth.make_prompt(cfg.vocab, 150, 6)
+    fwd = Oracle(cfg, W).forward(prompt, logits="last")
+    m = new_model(cfg, W)
+    lg, nxt = _prefill(m, prompt)
+    e = rel_l2(lg, fwd["logits"])
+    print(f"[6q/2kv hd64 prefill 150] logits rel-L2 {e:.2e}", flush=True)
+    assert e <= LOGIT_TOL
+    assert nxt == int(np.argmax(lg))
+    _check_state(m, cfg, fwd, 150)
+    m.close()
+
+
+MK_Q4G32 = 5
+
+
+@pytest.mark.parametrize("n,max_ctx", [(16, None), (200, None), (1100, 1200)])
+def test_prefill_q4_state_and_logits(n, max_ctx):
+    # 4-bit weights: 16 tokens (one partial DeltaNet chunk), 200 (several chunks), 1100 (two prefill
+    # chunks of up to 1024 tokens before the last token's decode launch)
+    cfg = synth.get_config("tiny") if max_ctx is None else synth.get_config("tiny", max_ctx=max_ctx)
+    W = synth.make_q4_weights(cfg, 11)
+    prompt = synth.make_prompt(cfg.vocab, n, 11)
+    fwd = Oracle(cfg, W).forward(prompt, logits="last")
+    m = new_model(cfg, W, weight_dtype=MK_Q4G32)
+    lg, nxt = _prefill(m, prompt)
+    e = rel_l2(lg, fwd["logits"])
+    print(f"[tiny 4-bit prefill {n}] logits rel-L2 {e:.2e}", flush=True)
+    assert e <= LOGIT_TOL
+    assert nxt == int(np.argmax(lg))
+    assert m.mk_get_position() == n
+    _check_state(m, cfg, fwd, n)
     m.close()

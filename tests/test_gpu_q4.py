@@ -2,8 +2,8 @@
 
 The oracle decodes the same bytes exactly (float64) and runs the same model, so the bars are the
 BF16 path's: logits relative L2 <= 1e-2 at every step, top-1 agreement >= 99 %, mean KL <= 1e-3
-nats, DeltaNet state and KV cache relative L2 <= 1e-3.  The prompt runs one decode launch per
-token (4-bit models have no prefill kernels).
+nats, DeltaNet state and KV cache relative L2 <= 1e-3.  The prompt runs through the prefill GEMMs
+(weights expanded to BF16 high and low parts) and its last token through one decode launch.
 
 Sizes: the tiny hybrid; ragged widths (columns that do not fill a 2048-column unit, odd head
 counts); a 4-layer slice at the 27B-scale width (hidden 5120: 2.5 units per row; FFN 17408:
