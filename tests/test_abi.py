@@ -166,7 +166,10 @@ def test_q4_config_and_tensor_checks(lib):
             b.mk_workspace_bytes(b.mk_config_from(synth.get_config("tiny", **bad), weight_dtype=b.MK_Q4G32))
     # speculative verify with 4-bit weights: the verify records and DeltaNet snapshots add workspace
     assert b.mk_workspace_bytes(b.mk_config_from(cfg, max_verify_k=1, weight_dtype=b.MK_Q4G32)) > q4
-    # 27B-scale: 14.08 GB of 4-bit weights (0.625 B per weight) plus state, cache and records
+    # 27B-scale: 14.08 GB of 4-bit weights (0.625 B per weight) plus state, cache and records, and the
+    # prefill's scratch: the largest matrix expanded to BF16 high and low parts (2 x 17,408 rows of
+    # 2 x 5,120 values, 0.71 GB) and activation rows twice as wide as the BF16 path's
     c27 = synth.get_config("hybrid_27b", max_ctx=2048)
     n = b.mk_workspace_bytes(b.mk_config_from(c27, weight_dtype=b.MK_Q4G32))
-    assert 14.0e9 < n < 14.6e9
+    wq = 2 * 17408 * (2 * 5120) * 2
+    assert 14.0e9 + wq < n < 14.6e9 + wq + 0.5e9
