@@ -27,6 +27,8 @@ EXPORTS = ["mk_workspace_bytes", "mk_create", "mk_load_weights", "mk_check_tenso
            "mk_decode_step", "mk_decode_step_noalloc", "mk_verify_k", "mk_reset", "mk_sync", "mk_get_position", "mk_set_position",
            "mk_state_bytes", "mk_read_state", "mk_write_state", "mk_set_grid", "mk_get_grid",
            "mk_set_trace", "mk_last_error", "mk_destroy"]
+# every symbol include/mk_test.h declares (single phases for unit parity tests; not product surface)
+TEST_EXPORTS = ["mk_test_gemv", "mk_test_q4_tile", "mk_test_gemv_q4", "mk_test_deltanet", "mk_test_argmax"]
 
 
 class MkError(RuntimeError):
@@ -85,6 +87,11 @@ def load_library():
         "mk_set_trace": (ctypes.c_int, [P, P, SZ]),
         "mk_last_error": (ctypes.c_char_p, [P]),
         "mk_destroy": (None, [P]),
+        "mk_test_gemv": (ctypes.c_int, [P, I32, I32, P, P, P]),
+        "mk_test_q4_tile": (ctypes.c_int, [P, I32, I32, P, P]),
+        "mk_test_gemv_q4": (ctypes.c_int, [P, I32, I32, P, P, P]),
+        "mk_test_deltanet": (ctypes.c_int, [P, I32, I32, I32, ctypes.c_float, P, P, P]),
+        "mk_test_argmax": (ctypes.c_int, [P, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -287,3 +294,30 @@ def _ptr(t):
     if t is None:
         return None
     return ctypes.c_void_p(t.data_ptr())
+
+
+# ---- test-only single phases (include/mk_test.h): device tensors in, device tensors out; the
+# current torch stream.  Argument marshalling only.
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def mk_test_gemv(d_W, R: int, K: int, d_x, d_y):
+    _check(load_library().mk_test_gemv(_ptr(d_W), R, K, _ptr(d_x), _ptr(d_y), _stream()))
+
+
+def mk_test_q4_tile(d_src, R: int, K: int, d_tiles):
+    _check(load_library().mk_test_q4_tile(_ptr(d_src), R, K, _ptr(d_tiles), _stream()))
+
+
+def mk_test_gemv_q4(d_tiles, R: int, K: int, d_x, d_y):
+    _check(load_library().mk_test_gemv_q4(_ptr(d_tiles), R, K, _ptr(d_x), _ptr(d_y), _stream()))
+
+
+def mk_test_deltanet(d_in, H: int, dk: int, dv: int, l2eps: float, d_S, d_o):
+    _check(load_library().mk_test_deltanet(_ptr(d_in), H, dk, dv, l2eps, _ptr(d_S), _ptr(d_o), _stream()))
+
+
+def mk_test_argmax(d_v, n: int, d_idx):
+    _check(load_library().mk_test_argmax(_ptr(d_v), n, _ptr(d_idx), _stream()))

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmk.so")
 SOURCES = ["mk_api.cpp", "mk_decode.hip", "mk_decode_q4.hip", "mk_prefill.hip", "mk_prefill_q4.hip", "mk_verify.hip",
-           "mk_noalloc.hip"]
+           "mk_noalloc.hip", "mk_test.hip"]
 ARCH = "gfx950"
 
 

@@ -835,6 +835,54 @@ __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf
 __device__ __forceinline__ float softplusf_(float z) { return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z))); }
 
 // ------------------------------------------------------------------------ DeltaNet
+// Per-head scalars of the gated delta rule from the head's raw q, k and gate logits ab = (a, b):
+// 1 / ||q|| and 1 / ||k|| (each with eps), alpha = exp(-softplus(a)), beta = sigmoid(b).  Called by a
+// whole wave (the sums are wave reductions); every wave forms them identically.
+struct DnHead {
+  float sq, sk, alpha, beta;
+};
+__device__ __forceinline__ DnHead dn_head(const LS float* q, const LS float* k, const LS float* ab, int dk,
+                                          float l2eps) {
+  float qq = 0.f, kk = 0.f;
+  for (int e = lane(); e < dk; e += 64) {
+    qq = fmaf(q[e], q[e], qq);
+    kk = fmaf(k[e], k[e], kk);
+  }
+  qq = wave_sum(qq);
+  kk = wave_sum(kk);
+  DnHead h;
+  h.sq = 1.0f / sqrtf(qq + l2eps);
+  h.sk = 1.0f / sqrtf(kk + l2eps);
+  h.alpha = expf(-softplusf_(ab[0]));
+  h.beta = sigmoidf_(ab[1]);
+  return h;
+}
+// One state row through the gated delta rule, by a whole wave.  sr[t] is this lane's S[row][lane +
+// 64 t]; the updated row S' = alpha S + beta (v - alpha S.k^) k^ is stored to Srow, and the row's
+// output S'.q^ (read after the update) is returned in every lane.
+__device__ __forceinline__ float dn_row(const float (&sr)[4], const LS float* q, const LS float* k, const DnHead& h,
+                                        float v, MK_G float* Srow, int dk) {
+  float kd = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int e = lane() + 64 * t;
+    if (e < dk) kd = fmaf(sr[t], k[e] * h.sk, kd);
+  }
+  kd = wave_sum(kd);
+  const float u = h.beta * (v - h.alpha * kd);
+  float od = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int e = lane() + 64 * t;
+    if (e < dk) {
+      const float nv2 = fmaf(u, k[e] * h.sk, h.alpha * sr[t]);
+      Srow[e] = nv2;
+      od = fmaf(nv2, q[e] * h.sq, od);
+    }
+  }
+  return wave_sum(od);
+}
+
 // state rows [s0, s1) -> stage slots: dk/4 lanes per row, 64/(dk/4) rows per slot.  Returns copies
 // issued by this wave.
 __device__ __forceinline__ int state_stage(const MkDecodeParams& p, const MkLayerDev& L, int s0, int s1,
@@ -884,17 +932,7 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
     if (wg_bar_or(s, !ok)) return false;
     tr.mark();
     if (streamer()) {
-      float qq = 0.f, kk = 0.f;
-      for (int e = lane(); e < dk; e += 64) {
-        qq = fmaf(q[e], q[e], qq);
-        kk = fmaf(k[e], k[e], kk);
-      }
-      qq = wave_sum(qq);
-      kk = wave_sum(kk);
-      const float sq = 1.0f / sqrtf(qq + p.l2_eps);
-      const float sk = 1.0f / sqrtf(kk + p.l2_eps);
-      const float alpha = expf(-softplusf_(ab[0]));
-      const float beta = sigmoidf_(ab[1]);
+      const DnHead hs = dn_head(q, k, ab, dk, p.l2_eps);
       // rows of head h, local index li = row - s0, owned by streaming wave li % NCW
       const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
       // Two copies of the row loop: when every row of this head is staged the loop issues no global
@@ -922,25 +960,7 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
               sr[t] = e < dk ? (staged ? srow[e] : L.S[(size_t)row * dk + e]) : 0.f;
             }
           }
-          float kd = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int e = lane() + 64 * t;
-            if (e < dk) kd = fmaf(sr[t], k[e] * sk, kd);
-          }
-          kd = wave_sum(kd);
-          const float u = beta * (vr[row - h * dv - i0] - alpha * kd);
-          float od = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int e = lane() + 64 * t;
-            if (e < dk) {
-              const float nv2 = fmaf(u, k[e] * sk, alpha * sr[t]);
-              L.S[(size_t)row * dk + e] = nv2;
-              od = fmaf(nv2, q[e] * sq, od);
-            }
-          }
-          od = wave_sum(od);
+          const float od = dn_row(sr, q, k, hs, vr[row - h * dv - i0], L.S + (size_t)row * dk, dk);
           if (lane() == 0) ll_put(L.ll_o + row, cx.epoch, od);
         }
       };

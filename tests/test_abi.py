@@ -15,6 +15,7 @@ from hybrid_deltanet_attention_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mk.h")
+TEST_HEADER = os.path.join(ROOT, "include", "mk_test.h")
 
 
 @pytest.fixture(scope="module")
@@ -25,8 +26,8 @@ def lib():
     return B.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     return sorted(set(re.findall(r"\b(mk_[a-z0-9_]+)\s*\(", text)))
@@ -40,12 +41,30 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), n
 
 
+def test_exports_every_test_only_function(lib):
+    # the single-phase entry points for unit parity tests, declared apart from the product surface
+    names = declared_functions(TEST_HEADER)
+    assert sorted(names) == sorted(B.TEST_EXPORTS)
+    assert not set(names) & set(declared_functions())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_test_only_functions_reject_bad_arguments(lib):
+    # argument checks answer MK_E_INVALID (-1) before anything is launched (no device needed)
+    assert lib.mk_test_gemv(None, 4, 8, None, None, None) == -1
+    assert lib.mk_test_gemv_q4(None, 4, 32, None, None, None) == -1
+    assert lib.mk_test_q4_tile(None, 4, 33, None, None) == -1
+    assert lib.mk_test_deltanet(None, 1, 512, 8, 1e-6, None, None, None) == -1
+    assert lib.mk_test_argmax(None, 9000, None, None) == -1
+
+
 def test_exported_symbols_are_plain_c(lib):
     # C linkage: the dynamic symbol table holds the plain names
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True, text=True).stdout
     syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
-    for n in declared_functions():
+    for n in declared_functions() + declared_functions(TEST_HEADER):
         assert n in syms, n
 
 
