@@ -405,10 +405,14 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
   const MK_G mk_u64* llv = llk + nkv * hd;
   const size_t tstride = (size_t)p.max_items * gs * (hd + 2);  // partial records per position
   const int h4 = hd >> 2;
-  // Keys and values of the positions already in the cache, loaded by the streaming threads one chunk
-  // ahead into registers (raw cache words; up to ATT_C * 64 four-value groups per chunk)
-  constexpr int KVR = (ATT_C * 64 + MK_NCT - 1) / MK_NCT;
+  // Keys and values of the positions already in the cache, loaded by every thread one chunk ahead into
+  // registers (raw cache words; up to ATT_C * 64 four-value groups per chunk)
+  constexpr int KVR = (ATT_C * 64 + MK_NT - 1) / MK_NT;
+  // (each cache type loads into registers of its own width, so that no load's destination has to be
+  // assembled into a wider vector -- which would make the wave wait for the load right away)
   u32x4 rk[KVR], rv[KVR];
+  u32x2 rk2[KVR], rv2[KVR];
+  u32 rk1[KVR], rv1[KVR];
   float rks[KVR], rvs[KVR];
   int pf_n = 0;  // four-value groups held for the chunk to come (per workgroup)
   auto kv_fetch = [&](int itn, int cn) {
@@ -416,10 +420,9 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
     if (itn >= items) return;
     const int g = itn - (itn / nkv) * nkv, j0 = cn * C;
     pf_n = max(0, min(pos, min(Lmax, j0 + C)) - j0) * h4;
-    if (!streamer()) return;
 #pragma unroll
     for (int e = 0; e < KVR; ++e) {
-      const int x = tid() + e * NCT;
+      const int x = tid() + e * MK_NT;
       if (x < pf_n) {
         const int jj = x / h4, d = (x - jj * h4) * 4;
         const size_t gi = ((size_t)g * p.max_ctx + j0 + jj) * hd + d;
@@ -427,13 +430,11 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
           rk[e] = *(const MK_G u32x4*)(L.Kc + gi);
           rv[e] = *(const MK_G u32x4*)(L.Vc + gi);
         } else if (p.kvt == MK_KV_F16) {
-          const u32x2 a = *(const MK_G u32x2*)((const MK_G _Float16*)L.Kc + gi);
-          const u32x2 b = *(const MK_G u32x2*)((const MK_G _Float16*)L.Vc + gi);
-          rk[e] = u32x4{a.x, a.y, 0u, 0u};
-          rv[e] = u32x4{b.x, b.y, 0u, 0u};
+          rk2[e] = *(const MK_G u32x2*)((const MK_G _Float16*)L.Kc + gi);
+          rv2[e] = *(const MK_G u32x2*)((const MK_G _Float16*)L.Vc + gi);
         } else {
-          rk[e].x = *(const MK_G u32*)((const MK_G signed char*)L.Kc + gi);
-          rv[e].x = *(const MK_G u32*)((const MK_G signed char*)L.Vc + gi);
+          rk1[e] = *(const MK_G u32*)((const MK_G signed char*)L.Kc + gi);
+          rv1[e] = *(const MK_G u32*)((const MK_G signed char*)L.Vc + gi);
           rks[e] = L.Ks[gi / MK_KV_Q8_BLOCK];
           rvs[e] = L.Vs[gi / MK_KV_Q8_BLOCK];
         }
@@ -442,10 +443,9 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
   };
   // the held groups -> kc / vc rows in FP32 (the decode kernel's expansion of the same rows)
   auto kv_stash = [&]() {
-    if (!streamer()) return;
 #pragma unroll
     for (int e = 0; e < KVR; ++e) {
-      const int x = tid() + e * NCT;
+      const int x = tid() + e * MK_NT;
       if (x < pf_n) {
         const int jj = x / h4, d = (x - jj * h4) * 4;
         f32x4 kk, vv;
@@ -455,14 +455,14 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
           vv = f32x4{__uint_as_float(rv[e].x), __uint_as_float(rv[e].y), __uint_as_float(rv[e].z),
                      __uint_as_float(rv[e].w)};
         } else if (p.kvt == MK_KV_F16) {
-          kk = f32x4{half_bits_f32(rk[e].x & 0xffffu), half_bits_f32(rk[e].x >> 16), half_bits_f32(rk[e].y & 0xffffu),
-                     half_bits_f32(rk[e].y >> 16)};
-          vv = f32x4{half_bits_f32(rv[e].x & 0xffffu), half_bits_f32(rv[e].x >> 16), half_bits_f32(rv[e].y & 0xffffu),
-                     half_bits_f32(rv[e].y >> 16)};
+          kk = f32x4{half_bits_f32(rk2[e].x & 0xffffu), half_bits_f32(rk2[e].x >> 16), half_bits_f32(rk2[e].y & 0xffffu),
+                     half_bits_f32(rk2[e].y >> 16)};
+          vv = f32x4{half_bits_f32(rv2[e].x & 0xffffu), half_bits_f32(rv2[e].x >> 16), half_bits_f32(rv2[e].y & 0xffffu),
+                     half_bits_f32(rv2[e].y >> 16)};
         } else {
           const float ks = rks[e], vs = rvs[e];
-          kk = f32x4{i8_f32(rk[e].x, 0) * ks, i8_f32(rk[e].x, 1) * ks, i8_f32(rk[e].x, 2) * ks, i8_f32(rk[e].x, 3) * ks};
-          vv = f32x4{i8_f32(rv[e].x, 0) * vs, i8_f32(rv[e].x, 1) * vs, i8_f32(rv[e].x, 2) * vs, i8_f32(rv[e].x, 3) * vs};
+          kk = f32x4{i8_f32(rk1[e], 0) * ks, i8_f32(rk1[e], 1) * ks, i8_f32(rk1[e], 2) * ks, i8_f32(rk1[e], 3) * ks};
+          vv = f32x4{i8_f32(rv1[e], 0) * vs, i8_f32(rv1[e], 1) * vs, i8_f32(rv1[e], 2) * vs, i8_f32(rv1[e], 3) * vs};
         }
         *(LS f32x4*)(kc + jj * hd + d) = kk;
         *(LS f32x4*)(vc + jj * hd + d) = vv;
