@@ -135,9 +135,11 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
       gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
       state_stage(p, L, s0, s1, s.stB, sslots);
       gemv_stage(gout, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS);
-      if (!dn_state(p, L, cx, s, s0, s1, sslots, 0, tr)) return;
-      // gate/up units -> stage A once the critical state update is out
-      cntA = gemv_stage(ggu, s.stA, A_UNITS);
+      // the polling waves update the state rows while the streaming waves issue the gate/up
+      // units -> stage A (free since the in-projection)
+      cntA = 0;
+      if (!dn_state<true>(p, L, cx, s, s0, s1, sslots, 0, tr, [&] { cntA = gemv_stage(ggu, s.stA, A_UNITS); }))
+        return;
       tr.mark();
       // mixer output -> out-projection rows + residual -> records
       {

@@ -136,7 +136,7 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
       const int rps = 64 / (p.dk >> 2);
       const int sslots = min((s1 - s0 + rps - 1) / rps, Q4_STAGE_B);
       state_stage(p, L, s0, s1, s.stB, sslots);
-      if (!dn_state(p, L, cx, s, s0, s1, sslots, 0, tr)) return;
+      if (!dn_state<false>(p, L, cx, s, s0, s1, sslots, 0, tr, [] {})) return;
       tr.mark();
     } else {
       K = p.nq * p.hd;

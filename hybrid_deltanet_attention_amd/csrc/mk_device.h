@@ -900,9 +900,14 @@ __device__ __forceinline__ int state_stage(const MkDecodeParams& p, const MkLaye
 }
 
 // gated delta rule on rows [s0, s1) of S; o = S q read after the update -> records.  Rows of
-// staged slots come from LDS, the rest straight from HBM.  Streaming waves own the rows.
+// staged slots come from LDS, the rest straight from HBM.  With POLL_ROWS the polling waves own the
+// rows and the streaming waves call side() once, after the first head's inputs have arrived, so
+// the copies it issues enter the compute unit's queue while the rows are computed rather than
+// ahead of the next gather's polls; otherwise the streaming waves own the rows and side is not
+// called.
+template <bool POLL_ROWS, typename Side>
 __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
-                                         int s0, int s1, int st_slots, int wait_after, Tracer& tr) {
+                                         int s0, int s1, int st_slots, int wait_after, Tracer& tr, Side side) {
   const int H = p.H, dk = p.dk, dv = p.dv;
   const int lpr = dk >> 2, rps = 64 / lpr;
   LS float* q = s.att;
@@ -912,7 +917,11 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
   const LS float* st = (const LS float*)s.stB;
   const MK_G mk_u64* in = L.ll_in;
   const int off_k = H * dk, off_v = 2 * H * dk, off_a = 2 * H * dk + H * dv, off_b = off_a + H;
-  bool first = true;
+  bool first = true, side_done = false;
+  // row waves: rw = 0 .. NRW - 1
+  constexpr int NRW = POLL_ROWS ? MK_NWAVE - NCW : NCW;
+  const bool row_wave = POLL_ROWS ? !streamer() : streamer();
+  const int rw = POLL_ROWS ? wave() - NCW : wave();
   const int h0 = s0 < s1 ? s0 / dv : 0, h1 = s0 < s1 ? (s1 - 1) / dv : -1;
   for (int h = h0; h <= h1; ++h) {
     const int i0 = max(s0, h * dv) - h * dv, i1 = min(s1, (h + 1) * dv) - h * dv;
@@ -931,16 +940,20 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
     tr.mark();
     if (wg_bar_or(s, !ok)) return false;
     tr.mark();
-    if (streamer()) {
+    if (POLL_ROWS && !side_done) {
+      if (streamer()) side();
+      side_done = true;
+    }
+    if (row_wave) {
       const DnHead hs = dn_head(q, k, ab, dk, p.l2_eps);
-      // rows of head h, local index li = row - s0, owned by streaming wave li % NCW
+      // rows of head h, local index li = row - s0, owned by row wave li % NRW
       const int lo = h * dv + i0 - s0, hi = h * dv + i1 - s0;
       // Two copies of the row loop: when every row of this head is staged the loop issues no global
       // load, so the compiler has no reason to wait on the vector-memory counter inside it -- a
       // wait there would also wait for the previous row's state stores and record store.
       auto rows = [&](auto staged_tag) {
         constexpr bool STAGED = decltype(staged_tag)::value;
-        for (int li = lo + ((wave() - lo % NCW) + NCW) % NCW; li < hi; li += NCW) {
+        for (int li = lo + ((rw - lo % NRW) + NRW) % NRW; li < hi; li += NRW) {
           const int row = s0 + li;
           const int sl = li / rps;
           const LS float* srow = st + sl * 256 + (li % rps) * dk;
@@ -971,6 +984,7 @@ __device__ __forceinline__ bool dn_state(const MkDecodeParams& p, const MkLayerD
     wg_bar();  // s.att is reused by the next head
   }
   if (first && streamer()) wait_vm_n(wait_after);
+  if (POLL_ROWS && !side_done && streamer()) side();
   return true;
 }
 
