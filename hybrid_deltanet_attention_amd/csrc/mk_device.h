@@ -1344,12 +1344,13 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
       tr.mark();
       wg_bar();
       tr.mark();
-      if (streamer()) {
+      {
+        // P.V by all eight waves, one (query head, dimension) output per thread and pass
         const bool first = c == c0, last = c + 1 == c1;
         const LS float* rin = rml + (k & 1) * 2 * gs;       // running (max, sum) before this chunk
         LS float* rout = rml + ((k + 1) & 1) * 2 * gs;      // ... and after it
         MK_G mk_u64* part = L.ll_part + (size_t)it * gs * (hd + 2);
-        for (int o = tid(); o < gs * hd; o += NCT) {
+        for (int o = tid(); o < gs * hd; o += MK_NT) {
           const int i = o / hd, d = o - i * hd;
           float pv[ATT_C], vv[ATT_C];
           const LS float* va[ATT_C];
