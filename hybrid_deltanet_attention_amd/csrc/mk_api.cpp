@@ -277,7 +277,8 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   const int gs = c.n_q_heads / c.n_kv_heads;
   const int hd = c.head_dim, C = MK_ATT_CHUNK;
   // gathered mixer output / FFN hidden, argmax records
-  const int vec = std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid));
+  // (also the attention items' partial scores: at most MK_NT floats)
+  const int vec = std::max(std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid)), MK_NT);
   // gathered DeltaNet inputs (one head), attention item inputs, combine staging, GEMV unit partials
   int att = 2 * c.dn_dk + 2 + c.dn_dv;
   att = std::max(att, 2 * gs * hd + 2 * hd + gs * C + 6 * gs);  // attention items, running merge included
@@ -312,7 +313,8 @@ void lds_layout_q4(const mk_config& c, int grid, MkDecodeParams& p) {
   const int D = c.hidden;
   const int gs = c.n_q_heads / c.n_kv_heads;
   const int hd = c.head_dim, C = MK_ATT_CHUNK;
-  const int vec = std::max(std::max(std::max(c.ffn, D), c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid));
+  const int vec = std::max(std::max(std::max(std::max(c.ffn, D), c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid)),
+                           MK_NT);  // (also the attention items' partial scores)
   int att = 2 * c.dn_dk + 2 + c.dn_dv;
   att = std::max(att, 2 * gs * hd + 2 * hd + gs * C + 6 * gs);
   att = std::max(att, 2048);  // Q4_RED_CAP

@@ -185,6 +185,19 @@ __device__ __forceinline__ void stage_f4x8(const LS float* const (&a)[8], f32x4 
       : "memory");
 }
 
+// four float4 at independent addresses
+__device__ __forceinline__ void stage_f4x4(const LS float* const (&a)[4], f32x4 (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(lds_addr(a[0])), "v"(lds_addr(a[1])), "v"(lds_addr(a[2])), "v"(lds_addr(a[3]))
+      : "memory");
+}
+
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_add(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
@@ -1207,6 +1220,179 @@ __device__ __forceinline__ int kv_nbuf(int hd, int kvt, int a_slots) {
 // chunk nb - 1 into the last, unused buffer), then waits until only the copies of the chunks after
 // k may remain (chunk 0 waits for all of them).  Queries are gathered once per KV head; the keys and
 // values of position pos only by the chunk that holds it.
+// ---- attention scores in key-dimension parts
+// A (query, key) score is a dot product over hd dimensions, taken as hd/4 groups of four.  The
+// groups are cut into np = att_parts(gs, hd) equal parts of gpp = hd/4/np groups, each summed by its
+// own thread: part `part` is one fused multiply-add chain over groups part*gpp .. part*gpp + gpp - 1,
+// starting at group jj mod gpp of the part and wrapping around (jj is the key's slot in its 16-position
+// chunk, so the slots of a row start on different banks), four FMAs per group.  The np part sums are
+// added in a fixed pairwise tree (att_part_sum).  np is the largest power of two that divides hd/4
+// with np * gs * 16 <= MK_NT, so one position's scores of a chunk take at most one pass of the
+// workgroup -- unless a verify launch's rows (MK_VERIFY_MAXT positions) already outnumber the
+// workgroup's threads: then the parts would only add instructions to a loop that is bound by its
+// issue (measured at the 27B-scale shape), and the score is one chain (np = 1).  The decode and
+// verify kernels both score through these helpers, so their scores agree bit for bit.
+__host__ __device__ inline int att_parts(int gs, int hd) {
+  const int rows = gs * ATT_C, n4 = hd >> 2;
+  int np = 1;
+  if (MK_VERIFY_MAXT * rows > MK_NT) return np;
+  while (2 * np * rows <= MK_NT && n4 % (2 * np) == 0) np *= 2;
+  return np;
+}
+// one part of q . k, W groups per step (the loads of a step are in flight together; steps past the
+// part's end add zero products); KSTAGE: the key row lies in an LDS-DMA stage region (read through
+// asm, see g_stage)
+template <bool KSTAGE, int W>
+__device__ __forceinline__ float qk_part_w(const LS float* kr, const LS float* qr, int jj, int part, int gpp) {
+  const int g0 = part * gpp, start = jj % gpp;
+  float a = 0.f;
+  for (int x0 = 0; x0 < gpp; x0 += W) {
+    f32x4 kk[W], qq[W];
+    const LS float* ka[W];
+#pragma unroll
+    for (int x = 0; x < W; ++x) {
+      int gg = x0 + x + start;
+      gg = gg >= gpp ? gg - gpp : gg;
+      const bool in = x0 + x < gpp;
+      const int dd = (g0 + gg) * 4;
+      ka[x] = kr + (in ? dd : 0);
+      qq[x] = in ? *(const LS f32x4*)(qr + dd) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (KSTAGE) {
+      if constexpr (W == 8) stage_f4x8(ka, kk);
+      else stage_f4x4(ka, kk);
+    } else {
+#pragma unroll
+      for (int x = 0; x < W; ++x) kk[x] = *(const LS f32x4*)ka[x];
+    }
+#pragma unroll
+    for (int x = 0; x < W; ++x) {
+      if (x0 + x >= gpp) kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+      a = fmaf(kk[x].x, qq[x].x, a);
+      a = fmaf(kk[x].y, qq[x].y, a);
+      a = fmaf(kk[x].z, qq[x].z, a);
+      a = fmaf(kk[x].w, qq[x].w, a);
+    }
+  }
+  return a;
+}
+// steps of four groups (eight would hold 64 more registers in the 4-bit decode kernel, which has none
+// to spare)
+template <bool KSTAGE>
+__device__ __forceinline__ float qk_part(const LS float* kr, const LS float* qr, int jj, int part, int gpp) {
+  return qk_part_w<KSTAGE, 4>(kr, qr, jj, part, gpp);
+}
+// the same part for two query rows against one key row (loaded once)
+template <int W>
+__device__ __forceinline__ void qk_part2_w(const LS float* kr, const LS float* qr0, const LS float* qr1, int jj,
+                                           int part, int gpp, float& a0, float& a1) {
+  const int g0 = part * gpp, start = jj % gpp;
+  a0 = 0.f;
+  a1 = 0.f;
+  for (int x0 = 0; x0 < gpp; x0 += W) {
+    f32x4 kk[W], q0[W], q1[W];
+#pragma unroll
+    for (int x = 0; x < W; ++x) {
+      int gg = x0 + x + start;
+      gg = gg >= gpp ? gg - gpp : gg;
+      const int dd = (g0 + gg) * 4;
+      kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+      q0[x] = kk[x];
+      q1[x] = kk[x];
+      if (x0 + x < gpp) {
+        kk[x] = *(const LS f32x4*)(kr + dd);
+        q0[x] = *(const LS f32x4*)(qr0 + dd);
+        q1[x] = *(const LS f32x4*)(qr1 + dd);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < W; ++x) {
+      a0 = fmaf(kk[x].x, q0[x].x, a0);
+      a1 = fmaf(kk[x].x, q1[x].x, a1);
+      a0 = fmaf(kk[x].y, q0[x].y, a0);
+      a1 = fmaf(kk[x].y, q1[x].y, a1);
+      a0 = fmaf(kk[x].z, q0[x].z, a0);
+      a1 = fmaf(kk[x].z, q1[x].z, a1);
+      a0 = fmaf(kk[x].w, q0[x].w, a0);
+      a1 = fmaf(kk[x].w, q1[x].w, a1);
+    }
+  }
+}
+// Steps of eight groups where the part is a whole number of them (the same products in the same
+// order as four-group steps), else of four (so the padding products of a part, if any, are qk_part's)
+__device__ __forceinline__ void qk_part2(const LS float* kr, const LS float* qr0, const LS float* qr1, int jj, int part,
+                                         int gpp, float& a0, float& a1) {
+  if (gpp % 8 == 0) qk_part2_w<8>(kr, qr0, qr1, jj, part, gpp, a0, a1);
+  else qk_part2_w<4>(kr, qr0, qr1, jj, part, gpp, a0, a1);
+}
+// parts part and part + 1 of q0 . k and q1 . k at once (four chains; a step's loads of both parts are
+// in flight together): a = {part: q0, q1; part + 1: q0, q1}, each chain in qk_part's order
+__device__ __forceinline__ void qk_parts2x2(const LS float* kr, const LS float* qr0, const LS float* qr1, int jj,
+                                            int part, int gpp, float (&a)[4]) {
+  const int start = jj % gpp;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) a[c] = 0.f;
+  for (int x0 = 0; x0 < gpp; x0 += 4) {
+    f32x4 kk[2][4], q0[2][4], q1[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int g0 = (part + hf) * gpp;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        int gg = x0 + x + start;
+        gg = gg >= gpp ? gg - gpp : gg;
+        const int dd = (g0 + gg) * 4;
+        kk[hf][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        q0[hf][x] = kk[hf][x];
+        q1[hf][x] = kk[hf][x];
+        if (x0 + x < gpp) {
+          kk[hf][x] = *(const LS f32x4*)(kr + dd);
+          q0[hf][x] = *(const LS f32x4*)(qr0 + dd);
+          q1[hf][x] = *(const LS f32x4*)(qr1 + dd);
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float& b0 = a[2 * hf];
+        float& b1 = a[2 * hf + 1];
+        b0 = fmaf(kk[hf][x].x, q0[hf][x].x, b0);
+        b1 = fmaf(kk[hf][x].x, q1[hf][x].x, b1);
+        b0 = fmaf(kk[hf][x].y, q0[hf][x].y, b0);
+        b1 = fmaf(kk[hf][x].y, q1[hf][x].y, b1);
+        b0 = fmaf(kk[hf][x].z, q0[hf][x].z, b0);
+        b1 = fmaf(kk[hf][x].z, q1[hf][x].z, b1);
+        b0 = fmaf(kk[hf][x].w, q0[hf][x].w, b0);
+        b1 = fmaf(kk[hf][x].w, q1[hf][x].w, b1);
+      }
+  }
+}
+template <int NP>
+__device__ __forceinline__ float part_tree(const LS float* p, int stride) {
+  float v[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) v[i] = p[i * stride];
+#pragma unroll
+  for (int w = 1; w < NP; w *= 2)
+#pragma unroll
+    for (int i = 0; i + w < NP; i += 2 * w) v[i] += v[i + w];
+  return v[0];
+}
+// p[0] + p[stride] + ... + p[(np - 1) stride] in the pairwise tree: (0 + 1), (2 + 3), ..., then
+// (01 + 23), ..., up to the two halves
+__device__ __forceinline__ float att_part_sum(const LS float* p, int stride, int np) {
+  switch (np) {
+    case 1: return p[0];
+    case 2: return part_tree<2>(p, stride);
+    case 4: return part_tree<4>(p, stride);
+    case 8: return part_tree<8>(p, stride);
+    case 16: return part_tree<16>(p, stride);
+    default: return part_tree<32>(p, stride);
+  }
+}
+
 __device__ __forceinline__ int att_items_count(const MkDecodeParams& p, int pos) {
   const int nch = (pos + ATT_C) / ATT_C;
   return ((nch + p.att_cpi - 1) / p.att_cpi) * p.nkv;
@@ -1245,6 +1431,8 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
   LS float* ml = pb + gs * ATT_C;      // [gs][2] this chunk's max and sum
   LS float* racc = ml + 2 * gs;        // [gs][hd] running acc of the item
   LS float* rml = racc + gs * hd;      // [2 (chunk parity)][gs][2] running max and sum
+  const int np = att_parts(gs, hd), gpp = (hd >> 2) / np;
+  LS float* sp = s.vec;                // [np][gs][16] partial scores
   const MK_G mk_u64* llq = L.ll_in;
   const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   const MK_G mk_u64* llv = llk + nkv * hd;
@@ -1294,44 +1482,26 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
         else wg_bar();
       }
       tr.mark();
-      // scores, softmax numerators, row max and sum (whole rows of 16 lanes take part in the DPP)
+      // scores: the key-dimension parts of every (query head, slot) dot product by their own
+      // threads, into the vector region (free while the items run), then added in the fixed tree
+      {
+        const int rows = gs * ATT_C;
+        for (int task = tid(); task < np * rows; task += MK_NT) {
+          const int part = task / rows, r = task - part * rows;
+          const int i = r >> 4, jj = r & 15;
+          if (jj < nj) {
+            const LS float* kr = j0 + jj == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
+            sp[task] = qk_part<true>(kr, qv + i * hd, jj, part, gpp);
+          }
+        }
+      }
+      wg_bar();
+      // softmax numerators, row max and sum (whole rows of 16 lanes take part in the DPP)
       const int t = tid();
       if (t < gs * ATT_C) {
         const int i = t >> 4, jj = t & 15;
         const bool valid = jj < nj;
-        float sc = -INFINITY;
-        if (valid) {
-          const int j = j0 + jj;
-          const LS float* kr = j == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
-          const LS float* qr = qv + i * hd;
-          const int n4 = hd >> 2;
-          const int start = jj % n4;  // staggered start: the 16 positions of a row read different banks
-          float a = 0.f;
-          for (int d0 = 0; d0 < n4; d0 += 8) {
-            f32x4 kk[8], qq[8];
-            const LS float* ka[8];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              int dd = d0 + x + start;
-              dd = (dd >= n4 ? dd - n4 : dd) * 4;
-              ka[x] = kr + (d0 + x < n4 ? dd : 0);
-              qq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-              if (d0 + x < n4) qq[x] = *(const LS f32x4*)(qr + dd);
-            }
-            stage_f4x8(ka, kk);
-#pragma unroll
-            for (int x = 0; x < 8; ++x)
-              if (d0 + x >= n4) kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              a = fmaf(kk[x].x, qq[x].x, a);
-              a = fmaf(kk[x].y, qq[x].y, a);
-              a = fmaf(kk[x].z, qq[x].z, a);
-              a = fmaf(kk[x].w, qq[x].w, a);
-            }
-          }
-          sc = a * scale;
-        }
+        const float sc = valid ? att_part_sum(sp + t, gs * ATT_C, np) * scale : -INFINITY;
         const float m = row_max16(sc);
         const float e = valid ? expf(sc - m) : 0.f;
         const float l = row_sum16(e);

@@ -386,6 +386,11 @@ __device__ __forceinline__ void att_qkv_v(const MkDecodeParams& p, const MkLayer
 // head the chunk's (max, sum, acc) are formed exactly as a decode chunk forms them and merged into
 // the position's running values for the item in chunk order, with the decode kernel's formula; a
 // position publishes its (max, sum, acc[hd]) at its last chunk of the item.
+// TWO_PARTS: the score parts go two at a time (qk_parts2x2; more loads in flight, more registers),
+// else one at a time (qk_part2); the products and sums are the same either way.  ONE_PART: the
+// instance for shapes whose scores are one part (att_parts == 1) with hd / 4 a multiple of 8 (so
+// eight-group steps are qk_part2's own), without the code for the other cases.
+template <bool TWO_PARTS, bool ONE_PART = false>
 __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                             LS float* sc, int NW, int w, int pos, int nt) {
   const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, C = ATT_C, rows_in = L.rows_in, cpi = p.att_cpi;
@@ -400,6 +405,11 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
   LS float* mf = pb + nt * gs * C;     // [nt][gs][2] this chunk's merge factors (running acc, chunk acc)
   LS float* racc = mf + 2 * nt * gs;   // [nt][gs][hd] running acc of the item
   LS float* rml = racc + nt * gs * hd; // [2 (chunk parity)][nt][gs][2] running max and sum
+  const int np = ONE_PART ? 1 : att_parts(gs, hd), gpp = (hd >> 2) / np;
+  // partial scores [np][2 nh] in the GEMV partials region, each written and read by one thread (at
+  // most MK_VERIFY_MAXT * MK_NT + MK_NT floats: np * gs * 16 <= MK_NT)
+  LS float* sp = s.att;
+  static_assert(MK_VERIFY_MAXT * MK_NT + MK_NT <= MK_RED_CAP, "partial scores exceed the GEMV partials region");
   const MK_G mk_u64* llq = L.ll_in;
   const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
   const MK_G mk_u64* llv = llk + nkv * hd;
@@ -469,41 +479,6 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
       }
     }
   };
-  // q0 . k and q1 . k over the chunk slot's key row (loaded once for both), each in the decode
-  // kernel's order: four-value groups starting at group jj mod (hd / 4), wrapping around
-  auto qk2 = [&](const LS float* kr, const LS float* qr0, const LS float* qr1, int jj, float& a0, float& a1) {
-    const int n4 = hd >> 2;
-    const int start = jj % n4;
-    a0 = 0.f;
-    a1 = 0.f;
-    for (int d0 = 0; d0 < n4; d0 += 8) {
-      f32x4 kk[8], q0[8], q1[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        int dd = d0 + x + start;
-        dd = (dd >= n4 ? dd - n4 : dd) * 4;
-        kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-        q0[x] = kk[x];
-        q1[x] = kk[x];
-        if (d0 + x < n4) {
-          kk[x] = *(const LS f32x4*)(kr + dd);
-          q0[x] = *(const LS f32x4*)(qr0 + dd);
-          q1[x] = *(const LS f32x4*)(qr1 + dd);
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        a0 = fmaf(kk[x].x, q0[x].x, a0);
-        a1 = fmaf(kk[x].x, q1[x].x, a1);
-        a0 = fmaf(kk[x].y, q0[x].y, a0);
-        a1 = fmaf(kk[x].y, q1[x].y, a1);
-        a0 = fmaf(kk[x].z, q0[x].z, a0);
-        a1 = fmaf(kk[x].z, q1[x].z, a1);
-        a0 = fmaf(kk[x].w, q0[x].w, a0);
-        a1 = fmaf(kk[x].w, q1[x].w, a1);
-      }
-    }
-  };
   int gq = -1;  // KV head whose queries are in qv
   int k = 0;    // chunk sequence number in this workgroup (running-value parity)
   if (w < items) kv_fetch(w, (w / nkv) * cpi);
@@ -562,6 +537,18 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
       const bool first = c == c0;
       const int nrow = (nt - tmin) * gs * C;
       const int nh = ((nrow / C + 1) / 2) * C;  // rows of the first half (whole 16-lane rows)
+      // row f (< nrow) = (position tmin + f / (gs C), head, slot)
+      auto row_of = [&](int f, int& tt, int& ii, int& jq) {
+        f = min(f, nrow - 1);
+        tt = f / (gs * C);
+        const int r = f - tt * gs * C;
+        ii = r / C;
+        jq = r - ii * C;
+      };
+      // scores, softmax numerators, row max and sum: one thread per row f of the first half and the
+      // row f + nh of the same slot (one key row serves both), whole 16-lane rows.  A thread forms the
+      // decode kernel's key-dimension parts of its two dot products one after another (qk_part2),
+      // keeps them in the GEMV partials region and adds them in the decode kernel's tree
       for (int b0 = 0; b0 < nh; b0 += MK_NT) {
         int fr[2];
         fr[0] = b0 + tid();
@@ -569,16 +556,35 @@ __device__ __forceinline__ bool att_items_v(const MkDecodeParams& p, const MkLay
         float a[2] = {0.f, 0.f};
         int tt[2], ii[2], jq[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int f = min(fr[u], nrow - 1);
-          tt[u] = f / (gs * C);
-          const int r = f - tt[u] * gs * C;
-          ii[u] = r / C;
-          jq[u] = r - ii[u] * C;
+        for (int u = 0; u < 2; ++u) row_of(fr[u], tt[u], ii[u], jq[u]);
+        if (fr[0] < nh) {
+          const int sst = 2 * nh;
+          const LS float* kr = kc + jq[0] * hd;
+          const LS float* qr0 = qv + ((tmin + tt[0]) * gs + ii[0]) * hd;
+          const LS float* qr1 = qv + ((tmin + tt[1]) * gs + ii[1]) * hd;
+          if (ONE_PART) {
+            qk_part2_w<8>(kr, qr0, qr1, jq[0], 0, gpp, a[0], a[1]);  // gpp = hd / 4, a multiple of 8 here
+            sp[fr[0]] = a[0];
+            sp[fr[1]] = a[1];
+          } else if (np == 1 || !TWO_PARTS) {
+            for (int part = 0; part < np; ++part) {
+              qk_part2(kr, qr0, qr1, jq[0], part, gpp, a[0], a[1]);
+              sp[part * sst + fr[0]] = a[0];
+              sp[part * sst + fr[1]] = a[1];
+            }
+          } else {
+            for (int part = 0; part + 1 < np; part += 2) {  // np is a power of two
+              float ap[4];
+              qk_parts2x2(kr, qr0, qr1, jq[0], part, gpp, ap);
+              sp[part * sst + fr[0]] = ap[0];
+              sp[part * sst + fr[1]] = ap[1];
+              sp[(part + 1) * sst + fr[0]] = ap[2];
+              sp[(part + 1) * sst + fr[1]] = ap[3];
+            }
+          }
+          a[0] = att_part_sum(sp + fr[0], sst, np);
+          a[1] = att_part_sum(sp + fr[1], sst, np);
         }
-        if (fr[0] < nh)
-          qk2(kc + jq[0] * hd, qv + ((tmin + tt[0]) * gs + ii[0]) * hd, qv + ((tmin + tt[1]) * gs + ii[1]) * hd, jq[0],
-              a[0], a[1]);
         for (int u = 0; u < 2; ++u) {
           const int t = tmin + tt[u], i = ii[u], jj = jq[u];
           const int nj = min(pos + t + 1, j0 + C) - j0;
@@ -940,7 +946,7 @@ __device__ __forceinline__ void verify_body(const MkDecodeParams& p0) {
       tr.mark();
       gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
       gemv_v_pre(gout, nt, pre);
-      if (!att_items_v(p, L, cx, s, s.vec, NW, w, pos, nt)) return;
+      if (!att_items_v<!KV_COMPACT>(p, L, cx, s, s.vec, NW, w, pos, nt)) return;
       const int o0 = split(K, NW, w), o1 = split(K, NW, w + 1);
       if (!att_combine_v(p, L, cx, s, s.vec, vcap, o0, o1, pos, nt)) return;
     }
@@ -1328,6 +1334,7 @@ __device__ __forceinline__ bool q4v_pack_records(const Ctx& cx, const Lds& s, co
   return true;
 }
 
+template <bool ONE_PART>
 __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
   extern __shared__ float lds_raw[];
   LS float* lds = (LS float*)lds_raw;
@@ -1430,7 +1437,7 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
           }))
         return;
       tr.mark();
-      if (!att_items_v(p, L, cx, s, s.vec, NW, w, pos, nt)) return;
+      if (!att_items_v<true, ONE_PART>(p, L, cx, s, s.vec, NW, w, pos, nt)) return;
       const int o0 = split(K, NW, w), o1 = split(K, NW, w + 1);
       if (!att_combine_v(p, L, cx, s, s.vec, pcap, o0, o1, pos, nt)) return;
     }
@@ -1586,17 +1593,25 @@ VerifyKernel pick_verify(const MkDecodeParams& p) {
 }
 }  // namespace
 
-// 4-bit weights (any KV cache type)
-__global__ void __launch_bounds__(MK_NT, 1) mk_verify_q4_kernel(MkDecodeParams p) { verify_q4_body(p); }
+// 4-bit weights (any KV cache type); the second instance serves shapes whose attention scores are one
+// part (the 27B-scale shape among them) without the code for several
+__global__ void __launch_bounds__(MK_NT, 1) mk_verify_q4_kernel(MkDecodeParams p) { verify_q4_body<false>(p); }
+__global__ void __launch_bounds__(MK_NT, 1) mk_verify_q4_kernel_1p(MkDecodeParams p) { verify_q4_body<true>(p); }
+
+namespace {
+VerifyKernel pick_verify_q4(const MkDecodeParams& p) {
+  return att_parts(p.nq / p.nkv, p.hd) == 1 && (p.hd / 4) % 8 == 0 ? mk_verify_q4_kernel_1p : mk_verify_q4_kernel;
+}
+}  // namespace
 
 extern "C" int mk_launch_verify_q4(const MkDecodeParams* p, int n_wg, void* stream) {
-  hipLaunchKernelGGL(mk_verify_q4_kernel, dim3(n_wg), dim3(MK_NT), (size_t)p->lds_floats * 4, (hipStream_t)stream, *p);
+  hipLaunchKernelGGL(pick_verify_q4(*p), dim3(n_wg), dim3(MK_NT), (size_t)p->lds_floats * 4, (hipStream_t)stream, *p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 extern "C" int mk_verify_q4_max_blocks_per_cu(const MkDecodeParams* p, int lds_bytes) {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mk_verify_q4_kernel, MK_NT, lds_bytes) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pick_verify_q4(*p), MK_NT, lds_bytes) != hipSuccess) return 0;
   return nb;
 }
 
