@@ -5,8 +5,9 @@
 //
 // Grid: one 512-lane workgroup per compute unit (regular launch; one workgroup fits per CU and the
 // grid is no larger than the CU count, so all workgroups are resident together).  Inside a
-// workgroup, waves 0..3 stream (every global copy and store), waves 4..7 poll exchange records,
-// and all eight compute out of LDS.
+// workgroup, waves 0..3 stream (every weight, state and KV copy), waves 4..7 poll exchange
+// records, and all eight compute out of LDS (the polling waves also update the DeltaNet state rows
+// and store their rows and records, and every wave forms a share of the attention P.V).
 //
 // Exchanges between phases use no barrier, fence or counter.  A phase publishes its outputs as
 // 8-byte records (FP32 value, launch epoch) with device-coherent stores; the next phase polls
