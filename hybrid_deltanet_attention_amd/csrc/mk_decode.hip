@@ -31,11 +31,11 @@ namespace {
 // compile-time constant, so divisions and trip counts fold) and once generically (sizes read from
 // the parameters); the host picks the instance that matches the model.
 // ------------------------------------------------------------------------------------------
-template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, bool KV_COMPACT>
+template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, int KVT>
 __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
   MkDecodeParams p = p0;
-  // instances for an FP32 KV cache compile without the compact-row code
-  if (!KV_COMPACT) p.kvt = MK_KV_F32;
+  // each instance serves one KV cache type and compiles only that type's row code
+  p.kvt = KVT;
   if (D_) p.D = D_;
   if (FFN_) p.ffn = FFN_;
   if (H_) p.H = H_;
@@ -301,22 +301,28 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
 
 // generic shape
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel(MkDecodeParams p) {
-  decode_body<0, 0, 0, 0, 0, 0, 0, 0, false>(p);
+  decode_body<0, 0, 0, 0, 0, 0, 0, 0, MK_KV_F32>(p);
 }
 // hidden 1024, FFN 3584, 16 DeltaNet heads of 128, 8 Q / 2 KV heads of 128 (the 0.8B-shaped hybrid)
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h1024(MkDecodeParams p) {
-  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128, false>(p);
+  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128, MK_KV_F32>(p);
 }
 // hidden 256, FFN 768, 4 DeltaNet heads of 64, 4 Q / 2 KV heads of 64 (the tiny hybrid)
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h256(MkDecodeParams p) {
-  decode_body<256, 768, 4, 64, 64, 4, 2, 64, false>(p);
+  decode_body<256, 768, 4, 64, 64, 4, 2, 64, MK_KV_F32>(p);
 }
-// binary16 or int8 KV cache: generic shape, and the 0.8B-shaped hybrid
-__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_kvc(MkDecodeParams p) {
-  decode_body<0, 0, 0, 0, 0, 0, 0, 0, true>(p);
+// binary16 and int8 KV caches: generic shape, and the 0.8B-shaped hybrid
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_f16(MkDecodeParams p) {
+  decode_body<0, 0, 0, 0, 0, 0, 0, 0, MK_KV_F16>(p);
 }
-__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h1024_kvc(MkDecodeParams p) {
-  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128, true>(p);
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_q8(MkDecodeParams p) {
+  decode_body<0, 0, 0, 0, 0, 0, 0, 0, MK_KV_Q8>(p);
+}
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h1024_f16(MkDecodeParams p) {
+  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128, MK_KV_F16>(p);
+}
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_kernel_h1024_q8(MkDecodeParams p) {
+  decode_body<1024, 3584, 16, 128, 128, 8, 2, 128, MK_KV_Q8>(p);
 }
 
 namespace {
@@ -328,7 +334,8 @@ bool shape_is(const MkDecodeParams& p) {
 typedef void (*DecodeKernel)(MkDecodeParams);
 DecodeKernel pick_kernel(const MkDecodeParams& p) {
   const bool h1024 = shape_is<1024, 3584, 16, 128, 128, 8, 2, 128>(p);
-  if (p.kvt != MK_KV_F32) return h1024 ? mk_decode_kernel_h1024_kvc : mk_decode_kernel_kvc;
+  if (p.kvt == MK_KV_F16) return h1024 ? mk_decode_kernel_h1024_f16 : mk_decode_kernel_f16;
+  if (p.kvt == MK_KV_Q8) return h1024 ? mk_decode_kernel_h1024_q8 : mk_decode_kernel_q8;
   if (h1024) return mk_decode_kernel_h1024;
   if (shape_is<256, 768, 4, 64, 64, 4, 2, 64>(p)) return mk_decode_kernel_h256;
   return mk_decode_kernel;

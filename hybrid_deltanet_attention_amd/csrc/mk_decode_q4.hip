@@ -24,10 +24,11 @@ constexpr int Q4_STAGE_A = 32;  // KV chunk buffers (1 KB slots)
 constexpr int Q4_STAGE_B = 16;  // DeltaNet state rows
 __shared__ __attribute__((aligned(1024))) u32x4 g_stage_q4[(Q4_STAGE_A + Q4_STAGE_B) * SLOT];
 
-template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, bool KV_COMPACT>
+template <int D_, int FFN_, int H_, int DK_, int DV_, int NQ_, int NKV_, int HD_, int KVT>
 __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
   MkDecodeParams p = p0;
-  if (!KV_COMPACT) p.kvt = MK_KV_F32;
+  // each instance serves one KV cache type and compiles only that type's row code
+  p.kvt = KVT;
   if (D_) p.D = D_;
   if (FFN_) p.ffn = FFN_;
   if (H_) p.H = H_;
@@ -287,18 +288,24 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
 
 // generic shape
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel(MkDecodeParams p) {
-  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0, false>(p);
+  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0, MK_KV_F32>(p);
 }
 // hidden 5120, FFN 17408, 32 DeltaNet heads of 128, 24 Q / 4 KV heads of 128 (the 27B-scale hybrid)
 __global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_h5120(MkDecodeParams p) {
-  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128, false>(p);
+  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128, MK_KV_F32>(p);
 }
-// binary16 or int8 KV cache
-__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_kvc(MkDecodeParams p) {
-  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0, true>(p);
+// binary16 and int8 KV caches
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_f16(MkDecodeParams p) {
+  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0, MK_KV_F16>(p);
 }
-__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_h5120_kvc(MkDecodeParams p) {
-  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128, true>(p);
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_q8(MkDecodeParams p) {
+  decode_q4_body<0, 0, 0, 0, 0, 0, 0, 0, MK_KV_Q8>(p);
+}
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_h5120_f16(MkDecodeParams p) {
+  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128, MK_KV_F16>(p);
+}
+__global__ void __launch_bounds__(MK_NT, 1) mk_decode_q4_kernel_h5120_q8(MkDecodeParams p) {
+  decode_q4_body<5120, 17408, 32, 128, 128, 24, 4, 128, MK_KV_Q8>(p);
 }
 
 namespace {
@@ -306,7 +313,8 @@ typedef void (*DecodeKernel)(MkDecodeParams);
 DecodeKernel pick_q4_kernel(const MkDecodeParams& p) {
   const bool h5120 = p.D == 5120 && p.ffn == 17408 && p.H == 32 && p.dk == 128 && p.dv == 128 && p.nq == 24 &&
                      p.nkv == 4 && p.hd == 128;
-  if (p.kvt != MK_KV_F32) return h5120 ? mk_decode_q4_kernel_h5120_kvc : mk_decode_q4_kernel_kvc;
+  if (p.kvt == MK_KV_F16) return h5120 ? mk_decode_q4_kernel_h5120_f16 : mk_decode_q4_kernel_f16;
+  if (p.kvt == MK_KV_Q8) return h5120 ? mk_decode_q4_kernel_h5120_q8 : mk_decode_q4_kernel_q8;
   return h5120 ? mk_decode_q4_kernel_h5120 : mk_decode_q4_kernel;
 }
 }  // namespace

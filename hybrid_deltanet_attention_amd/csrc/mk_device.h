@@ -1069,29 +1069,64 @@ __device__ __forceinline__ float half_bits_f32(u32 h) {
 __device__ __forceinline__ float f16_round(float x) { return (float)(_Float16)x; }
 __device__ __forceinline__ float i8_f32(u32 w, int b) { return (float)(int)(signed char)(w >> (8 * b)); }
 
-// The compact rows of a staged chunk (positions j0 .. j0 + nold - 1) -> FP32 rows laid out as a FP32
-// chunk buffer (what kv_stage copies for an FP32 cache), four values per thread at a time.
-__device__ __forceinline__ void kv_expand(int hd, int kvt, const LS u32x4* cmp, LS u32x4* f32, int nold) {
-  const int rb = kv_rowbytes(hd, kvt), ppsc = 1024 / rb, ksc = kv_slots(hd, kvt);
-  const int pps32 = 1024 / (4 * hd), ks32 = kv_slots(hd, MK_KV_F32);
-  const int n4 = hd >> 2, fpp = hd / MK_KV_Q8_BLOCK;
-  const LS char* cb = (const LS char*)cmp;
-  const LS float* scl = (const LS float*)(cmp + 2 * ksc * SLOT);
-  for (int x = tid(); x < 2 * nold * n4; x += MK_NT) {
-    const int v = x >= nold * n4 ? 1 : 0;
-    const int r = x - v * nold * n4, jj = r / n4, d = (r - jj * n4) * 4;
-    const LS char* src = cb + (v * ksc + jj / ppsc) * 1024 + (jj % ppsc) * rb;
-    f32x4 o;
-    if (kvt == MK_KV_F16) {
-      const u32x2 h = stage_b64(src + 2 * d);
-      o = f32x4{half_bits_f32(h.x & 0xffffu), half_bits_f32(h.x >> 16), half_bits_f32(h.y & 0xffffu),
-                half_bits_f32(h.y >> 16)};
-    } else {
-      const u32 c = stage_b32(src + d);
-      const float sc = __uint_as_float(stage_b32(scl + v * 128 + jj * fpp + d / MK_KV_Q8_BLOCK));
-      o = f32x4{i8_f32(c, 0) * sc, i8_f32(c, 1) * sc, i8_f32(c, 2) * sc, i8_f32(c, 3) * sc};
+// Compact rows of a staged chunk are read where they are used and converted to FP32 in registers:
+// binary16 values exactly, int8 codes times their block's FP32 scale (one multiplication), the same
+// values the verify kernels form.  Staged layout of a chunk (kv_stage): K rows in slots [0, ksc), V rows
+// in [ksc, 2 ksc), ppsc = 1024 / rowbytes rows per slot; int8 rows also carry a slot of scales, K at
+// byte 0 and V at byte 512, hd / 32 floats per position.
+struct KvCompact {
+  const LS char* base;
+  int rb, ppsc, ksc, fpp;
+  __device__ __forceinline__ const LS char* row(int v, int jj) const {
+    return base + (v * ksc + jj / ppsc) * 1024 + (jj % ppsc) * rb;
+  }
+  __device__ __forceinline__ const LS float* scales(int v, int jj) const {
+    return (const LS float*)(base + 2 * ksc * 1024) + v * 128 + jj * fpp;
+  }
+};
+__device__ __forceinline__ KvCompact kv_compact(int hd, int kvt, const LS u32x4* buf) {
+  KvCompact c;
+  c.base = (const LS char*)buf;
+  c.rb = kv_rowbytes(hd, kvt);
+  c.ppsc = 1024 / c.rb;
+  c.ksc = kv_slots(hd, kvt);
+  c.fpp = hd / MK_KV_Q8_BLOCK;
+  return c;
+}
+// four groups of four values (elements 4 g[x] .. 4 g[x] + 3) of one compact row (scale row sr for
+// int8), converted, with one wait for all the reads
+template <int KVT>
+__device__ __forceinline__ void kv_groups4(const LS char* r, const LS float* sr, const int (&g)[4], f32x4 (&o)[4]) {
+  if (KVT == MK_KV_F16) {
+    u32x2 h[4];
+    asm volatile(
+        "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+        : "v"(lds_addr(r + 8 * g[0])), "v"(lds_addr(r + 8 * g[1])), "v"(lds_addr(r + 8 * g[2])),
+          "v"(lds_addr(r + 8 * g[3]))
+        : "memory");
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      o[x] = f32x4{half_bits_f32(h[x].x & 0xffffu), half_bits_f32(h[x].x >> 16), half_bits_f32(h[x].y & 0xffffu),
+                   half_bits_f32(h[x].y >> 16)};
+  } else {
+    u32 c[4], f[4];
+    asm volatile(
+        "ds_read_b32 %0, %8\n\tds_read_b32 %1, %9\n\tds_read_b32 %2, %10\n\tds_read_b32 %3, %11\n\t"
+        "ds_read_b32 %4, %12\n\tds_read_b32 %5, %13\n\tds_read_b32 %6, %14\n\tds_read_b32 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+        : "v"(lds_addr(r + 4 * g[0])), "v"(lds_addr(r + 4 * g[1])), "v"(lds_addr(r + 4 * g[2])),
+          "v"(lds_addr(r + 4 * g[3])), "v"(lds_addr(sr + (4 * g[0]) / MK_KV_Q8_BLOCK)),
+          "v"(lds_addr(sr + (4 * g[1]) / MK_KV_Q8_BLOCK)), "v"(lds_addr(sr + (4 * g[2]) / MK_KV_Q8_BLOCK)),
+          "v"(lds_addr(sr + (4 * g[3]) / MK_KV_Q8_BLOCK))
+        : "memory");
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float sc = __uint_as_float(f[x]);
+      o[x] = f32x4{i8_f32(c[x], 0) * sc, i8_f32(c[x], 1) * sc, i8_f32(c[x], 2) * sc, i8_f32(c[x], 3) * sc};
     }
-    stage_write_f4((LS float*)f32 + (v * ks32 + jj / pps32) * 256 + (jj % pps32) * hd + d, o);
   }
 }
 
@@ -1200,11 +1235,9 @@ __device__ __forceinline__ void att_qkv(const MkDecodeParams& p, const MkLayerDe
 __device__ __forceinline__ int kv_buf_slots(int hd, int kvt = MK_KV_F32) {
   return (2 * kv_slots(hd, kvt) + (kvt == MK_KV_Q8 ? 1 : 0) + 3) & ~3;
 }
-// chunk buffers in stage A (up to 3: the copies of the next two chunks run while one is used); with
-// compact rows the FP32 buffer they are expanded into takes the space after them
+// chunk buffers in stage A (up to 3: the copies of the next two chunks run while one is used)
 __device__ __forceinline__ int kv_nbuf(int hd, int kvt, int a_slots) {
-  const int room = kvt == MK_KV_F32 ? a_slots : a_slots - kv_buf_slots(hd);
-  return max(1, min(3, room / kv_buf_slots(hd, kvt)));
+  return max(1, min(3, a_slots / kv_buf_slots(hd, kvt)));
 }
 
 // Split-K attention over positions 0..pos.  A work item is (block of p.att_cpi 16-position chunks,
@@ -1281,6 +1314,66 @@ __device__ __forceinline__ float qk_part_w(const LS float* kr, const LS float* q
 template <bool KSTAGE>
 __device__ __forceinline__ float qk_part(const LS float* kr, const LS float* qr, int jj, int part, int gpp) {
   return qk_part_w<KSTAGE, 4>(kr, qr, jj, part, gpp);
+}
+// qk_part for a compact key row (binary16, or int8 codes with the scale row sr): the four values of
+// a group converted as kv_groups4 converts them, in qk_part's order and steps
+// element d of four compact rows r[0..3] (scale rows sr for int8), converted as kv_groups4 converts
+template <int KVT>
+__device__ __forceinline__ void kv_col4(const LS char* const (&r)[4], const LS float* const (&sr)[4], int d,
+                                        float (&o)[4]) {
+  if (KVT == MK_KV_F16) {
+    u32 h[4];
+    asm volatile(
+        "ds_read_u16 %0, %4\n\tds_read_u16 %1, %5\n\tds_read_u16 %2, %6\n\tds_read_u16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+        : "v"(lds_addr(r[0] + 2 * d)), "v"(lds_addr(r[1] + 2 * d)), "v"(lds_addr(r[2] + 2 * d)),
+          "v"(lds_addr(r[3] + 2 * d))
+        : "memory");
+#pragma unroll
+    for (int x = 0; x < 4; ++x) o[x] = half_bits_f32(h[x]);
+  } else {
+    u32 c[4], f[4];
+    const int b = d / MK_KV_Q8_BLOCK;
+    asm volatile(
+        "ds_read_i8 %0, %8\n\tds_read_i8 %1, %9\n\tds_read_i8 %2, %10\n\tds_read_i8 %3, %11\n\t"
+        "ds_read_b32 %4, %12\n\tds_read_b32 %5, %13\n\tds_read_b32 %6, %14\n\tds_read_b32 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+        : "v"(lds_addr(r[0] + d)), "v"(lds_addr(r[1] + d)), "v"(lds_addr(r[2] + d)), "v"(lds_addr(r[3] + d)),
+          "v"(lds_addr(sr[0] + b)), "v"(lds_addr(sr[1] + b)), "v"(lds_addr(sr[2] + b)), "v"(lds_addr(sr[3] + b))
+        : "memory");
+#pragma unroll
+    for (int x = 0; x < 4; ++x) o[x] = (float)(int)c[x] * __uint_as_float(f[x]);
+  }
+}
+template <int KVT>
+__device__ __forceinline__ float qk_part_c(const LS char* kr, const LS float* sr, const LS float* qr, int jj, int part,
+                                           int gpp) {
+  const int g0 = part * gpp, start = jj % gpp;
+  float a = 0.f;
+  for (int x0 = 0; x0 < gpp; x0 += 4) {
+    f32x4 kk[4], qq[4];
+    int gi[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      int gg = x0 + x + start;
+      gg = gg >= gpp ? gg - gpp : gg;
+      const bool in = x0 + x < gpp;
+      gi[x] = g0 + (in ? gg : 0);
+      qq[x] = in ? *(const LS f32x4*)(qr + 4 * gi[x]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    kv_groups4<KVT>(kr, sr, gi, kk);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      if (x0 + x >= gpp) kk[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+      a = fmaf(kk[x].x, qq[x].x, a);
+      a = fmaf(kk[x].y, qq[x].y, a);
+      a = fmaf(kk[x].z, qq[x].z, a);
+      a = fmaf(kk[x].w, qq[x].w, a);
+    }
+  }
+  return a;
 }
 // the same part for two query rows against one key row (loaded once)
 template <int W>
@@ -1421,8 +1514,6 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
   const int kvt = p.kvt;
   const int nb = kv_nbuf(hd, kvt, s.a_slots);
   const int kvb = kv_buf_slots(hd, kvt);
-  // compact rows are expanded into the FP32 buffer after the chunk buffers
-  LS u32x4* const f32buf = s.stA + nb * kvb * SLOT;
   int cnt0 = 0, cnt1 = 0, cnt2 = 0;  // copies this wave issued for the chunk in buffers 0, 1, 2
   LS float* qv = s.att;                // [gs][hd]
   LS float* kpos = qv + gs * hd;       // [hd]
@@ -1445,7 +1536,8 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
     for (int c = c0; c < c1; ++c, ++k) {
       const int j0 = c * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
       const bool has_pos = j0 + nj == Lpos;
-      const LS float* stf = (const LS float*)(kvt == MK_KV_F32 ? s.stA + (k % nb) * kvb * SLOT : f32buf);
+      const LS float* stf = (const LS float*)(s.stA + (k % nb) * kvb * SLOT);  // FP32 rows
+      const KvCompact kc = kv_compact(hd, kvt, s.stA + (k % nb) * kvb * SLOT);  // compact rows
       int pending = 0;  // copies issued after this chunk's that may stay outstanding
       if (k > 0 || nb > 1) {
         const int kn = k + nb - 1, bn = kn % nb;
@@ -1476,11 +1568,7 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
       }
       tr.mark();
       if (wg_bar_or(s, !ok)) return false;
-      if (kvt != MK_KV_F32) {
-        kv_expand(hd, kvt, s.stA + (k % nb) * kvb * SLOT, f32buf, nj - (has_pos ? 1 : 0));
-        if (has_pos) kv_round_append(p, L, kpos, vpos, 1, pb, g, pos);  // barriers inside
-        else wg_bar();
-      }
+      if (kvt != MK_KV_F32 && has_pos) kv_round_append(p, L, kpos, vpos, 1, pb, g, pos);  // barriers inside
       tr.mark();
       // scores: the key-dimension parts of every (query head, slot) dot product by their own
       // threads, into the vector region (free while the items run), then added in the fixed tree
@@ -1490,8 +1578,14 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
           const int part = task / rows, r = task - part * rows;
           const int i = r >> 4, jj = r & 15;
           if (jj < nj) {
-            const LS float* kr = j0 + jj == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
-            sp[task] = qk_part<true>(kr, qv + i * hd, jj, part, gpp);
+            if (kvt == MK_KV_F32 || j0 + jj == pos) {
+              const LS float* kr = j0 + jj == pos ? kpos : stf + (jj / pps) * 256 + (jj % pps) * hd;
+              sp[task] = qk_part<true>(kr, qv + i * hd, jj, part, gpp);
+            } else if (kvt == MK_KV_F16) {
+              sp[task] = qk_part_c<MK_KV_F16>(kc.row(0, jj), nullptr, qv + i * hd, jj, part, gpp);
+            } else {
+              sp[task] = qk_part_c<MK_KV_Q8>(kc.row(0, jj), kc.scales(0, jj), qv + i * hd, jj, part, gpp);
+            }
           }
         }
       }
@@ -1532,7 +1626,19 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
 #pragma unroll
           for (int q4 = 0; q4 < ATT_C; q4 += 4) {
             float t4[4];
-            stage_f32x4(va[q4], va[q4 + 1], va[q4 + 2], va[q4 + 3], t4);
+            if (kvt == MK_KV_F32) {
+              stage_f32x4(va[q4], va[q4 + 1], va[q4 + 2], va[q4 + 3], t4);
+            } else {
+              // column d of four compact V rows (the slot of position pos, not staged, takes vpos)
+              const LS char* vr[4] = {kc.row(1, q4), kc.row(1, q4 + 1), kc.row(1, q4 + 2), kc.row(1, q4 + 3)};
+              const LS float* vs[4] = {kc.scales(1, q4), kc.scales(1, q4 + 1), kc.scales(1, q4 + 2),
+                                       kc.scales(1, q4 + 3)};
+              if (kvt == MK_KV_F16) kv_col4<MK_KV_F16>(vr, vs, d, t4);
+              else kv_col4<MK_KV_Q8>(vr, vs, d, t4);
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                if (j0 + q4 + x == pos) t4[x] = vpos[d];
+            }
 #pragma unroll
             for (int x = 0; x < 4; ++x) vv[q4 + x] = q4 + x < nj ? t4[x] : 0.f;
           }
