@@ -7,8 +7,9 @@
 // differs is sized for wide models whose weights dominate every phase:
 //  * every GEMV streams its 4-bit units through registers on all eight waves (mk_q4.h); weights
 //    are not staged in LDS.  Before each exchange the streaming waves take and load their first
-//    units of the GEMV that follows it (the polling waves keep their queues for the polls), so
-//    HBM keeps streaming while the records travel;
+//    units of the GEMV that follows it, so HBM keeps streaming while the records travel; every
+//    wave then polls the exchange records (the streaming waves' polls queue behind their primed
+//    loads, which the GEMV needs first anyway);
 //  * the LDS keeps the residual, one vector region (normalised activations, gathered mixer output
 //    or FFN hidden -- never live together), the unit partials and two layer descriptors (the next
 //    one is fetched by the polling waves during a gather); RMSNorm gains are read from global
@@ -20,6 +21,14 @@
 
 namespace {
 
+// Poll loads in flight per thread in the gathers, which every wave takes part in: a streaming
+// wave's polls queue behind the units it primed for the next GEMV, whose data is needed right
+// after the gather anyway, and the gathers of wide vectors then take one round of polls (or, for
+// the FFN hidden vector of a 27B-scale model, two instead of five).  Measured on the 27B-scale
+// shape: 4,755 us per token with the polling waves alone, 4,530 with every wave, 4,515 with 12
+// polls in flight for the FFN hidden gather (16: 4,556).
+constexpr int Q4_PB = 8;
+constexpr int Q4_PB_FFN = 12;
 constexpr int Q4_STAGE_A = 32;  // KV chunk buffers (1 KB slots)
 constexpr int Q4_STAGE_B = 16;  // DeltaNet state rows
 __shared__ __attribute__((aligned(1024))) u32x4 g_stage_q4[(Q4_STAGE_A + Q4_STAGE_B) * SLOT];
@@ -117,9 +126,12 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
     in_slice(layer_desc(s.desc, 0), g, P0);
     if (streamer()) gemv_q4_prime(g, c0, q);
   }
+  // input-norm gains of the layer about to start: loaded ahead of the gather that precedes the norm
+  Q4Gains<D_ ? (D_ / 4 + NPT - 1) / NPT : Q4_GAIN_IT> gin_g;
+  gains_gg_issue(layer_desc(s.desc, 0).g12, D, gin_g);
   for (int l = 0; l < p.n_layers; ++l) {
     const MkLayerDev L = layer_desc(s.desc, l & 1);
-    rmsnorm_gg(s.x, L.g12, s.vec, D, p.rms_eps, tr);
+    rmsnorm_gg(s.x, gin_g, s.vec, D, p.rms_eps, tr);
     q4_pack(s.vec, D);
     tr.mark();
     int P0;
@@ -160,7 +172,7 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
     gout.init(L.w_out, d0 >> 2, d1 - d0, K);
     if (streamer()) gemv_q4_prime(gout, c1, q);
     {
-      const bool ok = gather_vec(cx, L.ll_o, K, s.vec);
+      const bool ok = gather_vec_all<false, Q4_PB>(cx, L.ll_o, K, s.vec);
       if (wg_bar_or(s, !ok)) return;
       q4_pack(s.vec, K);
     }
@@ -178,7 +190,7 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
       const bool fetch = !streamer() && di < NDW && l + 1 < p.n_layers;
       u32 dw = 0u;
       if (fetch) dw = ((const MK_G u32*)(p.layers + l + 1))[di];
-      const bool ok = gather_vec(cx, L.ll_x1, D, s.x);
+      const bool ok = gather_vec_all<false, Q4_PB>(cx, L.ll_x1, D, s.x);
       if (fetch) ((LS u32*)(s.desc + ((l + 1) & 1)))[di] = dw;
       if (wg_bar_or(s, !ok)) return;
     }
@@ -193,7 +205,7 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
     gdn.init(L.w_down, d0 >> 2, d1 - d0, p.ffn);
     if (streamer()) gemv_q4_prime(gdn, c1, q);
     {
-      const bool ok = gather_vec(cx, L.ll_h, p.ffn, s.vec);
+      const bool ok = gather_vec_all<false, Q4_PB_FFN>(cx, L.ll_h, p.ffn, s.vec);
       if (wg_bar_or(s, !ok)) return;
       q4_pack(s.vec, p.ffn);
     }
@@ -201,16 +213,22 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
     gemv_q4<false, false>(gdn, (const LS u32*)s.vec, s.att, c1, q, streamer(), tr,
                           [&](int r, float v, float) { ll_put(L.ll_x2 + d0 + r, cx.epoch, s.x[d0 + r] + v); });
     tr.mark();
-    // the next layer's in-projection units (or the LM head's) while the residual travels
+    // the next layer's input-norm gains (polling threads) and in-projection units (or the LM
+    // head's; streaming threads) while the residual travels
     {
       GemvQ4 g;
       int i0;
-      if (l + 1 < p.n_layers) in_slice(layer_desc(s.desc, (l + 1) & 1), g, i0);
-      else head_slice(g, i0);
+      if (l + 1 < p.n_layers) {
+        const MkLayerDev Ln = layer_desc(s.desc, (l + 1) & 1);
+        gains_gg_issue(Ln.g12, D, gin_g);
+        in_slice(Ln, g, i0);
+      } else {
+        head_slice(g, i0);
+      }
       if (streamer()) gemv_q4_prime(g, c0, q);
     }
     {
-      const bool ok = gather_vec(cx, L.ll_x2, D, s.x);
+      const bool ok = gather_vec_all<false, Q4_PB>(cx, L.ll_x2, D, s.x);
       if (wg_bar_or(s, !ok)) return;
     }
     tr.mark();

@@ -269,19 +269,31 @@ __device__ __forceinline__ void q4_embed_row(const MK_G uint16_t* E, int D, int 
 // from global memory (issued before the sum) and write xf, so the streaming waves, whose queues
 // may hold the next GEMV's primed loads, issue no load here.  D <= 4 * NPT * Q4_GAIN_IT.
 constexpr int Q4_GAIN_IT = 8;
-__device__ __forceinline__ void rmsnorm_gg(const LS float* x, const MK_G uint16_t* g, LS float* xf, int D, float eps,
+// gains held by the polling threads, IT pieces of 4 each (D <= 4 * NPT * IT)
+template <int IT = Q4_GAIN_IT>
+struct Q4Gains {
+  u32x2 gg[IT];
+};
+// the polling threads' loads of the gains g[0..D) (a caller may issue them early, before a gather)
+template <int IT>
+__device__ __forceinline__ void gains_gg_issue(const MK_G uint16_t* g, int D, Q4Gains<IT>& gn) {
+  const int D4 = uni(D) >> 2;
+  const int pl = tid() - NCT;
+  if (!streamer()) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int c = pl + k * NPT;
+      gn.gg[k] = c < D4 ? *(const MK_G u32x2*)(g + 4 * c) : u32x2{0u, 0u};
+    }
+  }
+}
+template <int IT>
+__device__ __forceinline__ void rmsnorm_gg(const LS float* x, const Q4Gains<IT>& gn, LS float* xf, int D, float eps,
                                            Tracer& tr) {
   D = uni(D);
   const int D4 = D >> 2;
   const int pl = tid() - NCT;
-  u32x2 gg[Q4_GAIN_IT];
-  if (!streamer()) {
-#pragma unroll
-    for (int k = 0; k < Q4_GAIN_IT; ++k) {
-      const int c = pl + k * NPT;
-      gg[k] = c < D4 ? *(const MK_G u32x2*)(g + 4 * c) : u32x2{0u, 0u};
-    }
-  }
+  const u32x2(&gg)[IT] = gn.gg;
   const LS f32x4* x4 = (const LS f32x4*)x;
   float s = 0.f;
   for (int c0 = lane(); c0 < D4; c0 += 256) {
@@ -304,7 +316,7 @@ __device__ __forceinline__ void rmsnorm_gg(const LS float* x, const MK_G uint16_
   tr.mark();
   if (!streamer()) {
 #pragma unroll
-    for (int k = 0; k < Q4_GAIN_IT; ++k) {
+    for (int k = 0; k < IT; ++k) {
       const int c = pl + k * NPT;
       if (c < D4) {
         const f32x4 v = x4[c];
@@ -316,6 +328,12 @@ __device__ __forceinline__ void rmsnorm_gg(const LS float* x, const MK_G uint16_
   }
   tr.mark();
   wg_bar();
+}
+__device__ __forceinline__ void rmsnorm_gg(const LS float* x, const MK_G uint16_t* g, LS float* xf, int D, float eps,
+                                           Tracer& tr) {
+  Q4Gains<> gn;
+  gains_gg_issue(g, D, gn);
+  rmsnorm_gg(x, gn, xf, D, eps, tr);
 }
 
 // FP32 v[0..n) (n a multiple of 32) -> in place, the GEMV's packed activations: block g of 32
