@@ -8,8 +8,9 @@
 //  * every GEMV streams its 4-bit units through registers on all eight waves (mk_q4.h); weights
 //    are not staged in LDS.  Before each exchange the streaming waves take and load their first
 //    units of the GEMV that follows it, so HBM keeps streaming while the records travel; every
-//    wave then polls the exchange records (the streaming waves' polls queue behind their primed
-//    loads, which the GEMV needs first anyway);
+//    wave then polls the residual and FFN-hidden records (the streaming waves' polls queue behind
+//    their primed loads, which the GEMV needs first anyway); the mixer output, one round of polls
+//    for the polling waves alone, stays with them;
 //  * the LDS keeps the residual, one vector region (normalised activations, gathered mixer output
 //    or FFN hidden -- never live together), the unit partials and two layer descriptors (the next
 //    one is fetched by the polling waves during a gather); RMSNorm gains are read from global
@@ -21,12 +22,13 @@
 
 namespace {
 
-// Poll loads in flight per thread in the gathers, which every wave takes part in: a streaming
-// wave's polls queue behind the units it primed for the next GEMV, whose data is needed right
-// after the gather anyway, and the gathers of wide vectors then take one round of polls (or, for
-// the FFN hidden vector of a 27B-scale model, two instead of five).  Measured on the 27B-scale
-// shape: 4,755 us per token with the polling waves alone, 4,530 with every wave, 4,515 with 12
-// polls in flight for the FFN hidden gather (16: 4,556).
+// Poll loads in flight per thread in the residual and FFN-hidden gathers, which every wave takes
+// part in: a streaming wave's polls queue behind the units it primed for the next GEMV, whose data
+// is needed right after the gather anyway, and the gathers of wide vectors then take one round of
+// polls (or, for the FFN hidden vector of a 27B-scale model, two instead of five).  Measured on the
+// 27B-scale shape: 4,755 us per token with the polling waves alone, 4,530 with every wave in all
+// four gathers, 4,515 with 12 polls in flight for the FFN hidden gather (16: 4,556), 4,430 with
+// the mixer-output gather (4,096 records: one round either way) back on the polling waves.
 constexpr int Q4_PB = 8;
 constexpr int Q4_PB_FFN = 12;
 constexpr int Q4_STAGE_A = 32;  // KV chunk buffers (1 KB slots)
@@ -172,7 +174,7 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
     gout.init(L.w_out, d0 >> 2, d1 - d0, K);
     if (streamer()) gemv_q4_prime(gout, c1, q);
     {
-      const bool ok = gather_vec_all<false, Q4_PB>(cx, L.ll_o, K, s.vec);
+      const bool ok = gather_vec(cx, L.ll_o, K, s.vec);
       if (wg_bar_or(s, !ok)) return;
       q4_pack(s.vec, K);
     }
