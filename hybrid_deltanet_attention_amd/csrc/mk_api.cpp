@@ -277,11 +277,14 @@ void lds_layout(const mk_config& c, int grid, MkDecodeParams& p) {
   const int gs = c.n_q_heads / c.n_kv_heads;
   const int hd = c.head_dim, C = MK_ATT_CHUNK;
   // gathered mixer output / FFN hidden, argmax records
-  // (also the attention items' partial scores: at most MK_NT floats)
-  const int vec = std::max(std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid)), MK_NT);
+  // (also the attention items' partial scores: a pass of MK_ATT_PASS chunks takes at most
+  // MK_ATT_PASS * MK_NT floats)
+  const int vec = std::max(std::max(std::max(c.ffn, c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid)),
+                           MK_ATT_PASS * MK_NT);
   // gathered DeltaNet inputs (one head), attention item inputs, combine staging, GEMV unit partials
   int att = 2 * c.dn_dk + 2 + c.dn_dv;
-  att = std::max(att, 2 * gs * hd + 2 * hd + gs * C + 6 * gs);  // attention items, running merge included
+  // attention items (a pass of up to MK_ATT_PASS chunks), running merge included
+  att = std::max(att, 2 * gs * hd + 2 * hd + MK_ATT_PASS * (gs * C + 2 * gs) + 4 * gs);
   att = std::max(att, MK_RED_CAP);
   att = std::max(att, 3 * 129);  // combine staging of one output: at most 128 items per KV head (+1)
   int o = 0;

@@ -24,6 +24,8 @@
 
 #include "mk_device.h"
 
+constexpr int ATT_PASS = MK_ATT_PASS;
+
 namespace {
 
 // ------------------------------------------------------------------------------------------
@@ -156,16 +158,20 @@ __device__ __forceinline__ void decode_body(const MkDecodeParams& p0) {
       K = p.nq * p.hd;
       att_qkv(p, L, cx, s, gin, P0, pos, tr);
       tr.mark();
-      // K/V rows of the first two work items -> stage A (free until the gate/up units), the
-      // out-projection units -> stage B
+      // K/V rows of the first chunks of the work items -> stage A (free until the gate/up units),
+      // the out-projection units -> stage B.  Compact caches whose chunk buffers fit 2 ATT_PASS
+      // times in stage A take their chunks ATT_PASS at a time (att_items_multi).
       const int boff = 0;
-      for (int kc = 0; kc + 1 < kv_nbuf(p.hd, p.kvt, s.a_slots) || kc == 0; ++kc) {
+      const bool multi = KVT != MK_KV_F32 && 2 * ATT_PASS * kv_buf_slots(p.hd, p.kvt) <= s.a_slots;
+      const int first = multi ? ATT_PASS : max(1, kv_nbuf(p.hd, p.kvt, s.a_slots) - 1);
+      for (int kc = 0; kc < first; ++kc) {
         const int cn = att_chunk_at(p, NW, w, pos, kc);
         if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd, p.kvt) * SLOT);
       }
       gout.init(L.w_out + (size_t)d0 * K, d1 - d0, K);
       gemv_stage(gout, s.stB + boff * SLOT, (MK_STAGE_B_SLOTS - boff) / USLOTS);
-      if (!att_items(p, L, cx, s, NW, w, pos, 0, tr)) return;
+      if (multi ? !att_items_multi<ATT_PASS>(p, L, cx, s, NW, w, pos, 0, tr) : !att_items(p, L, cx, s, NW, w, pos, 0, tr))
+        return;
       cntA = gemv_stage(ggu, s.stA, A_UNITS);
       tr.mark();
       const int o0 = split(K, NW, w), o1 = split(K, NW, w + 1);

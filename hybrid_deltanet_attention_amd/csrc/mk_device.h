@@ -1676,6 +1676,204 @@ __device__ __forceinline__ bool att_items(const MkDecodeParams& p, const MkLayer
   return true;
 }
 
+// Copies kv_stage issues for chunk-level index it in this wave (the same count, nothing issued).
+__device__ __forceinline__ int kv_stage_count(const MkDecodeParams& p, int it, int pos) {
+  if (!streamer()) return 0;
+  const int kvt = p.kvt;
+  const int rb = kv_rowbytes(p.hd, kvt), lpp = rb >> 4, pps = 64 / lpp, ks = kv_slots(p.hd, kvt);
+  const int c = it / p.nkv;
+  const int j0 = c * ATT_C, jend = min(pos, j0 + ATT_C);
+  int cnt = 0;
+  for (int q = wave(); q < 2 * ks; q += NCW) {
+    const int sl = q >= ks ? q - ks : q;
+    if (j0 + sl * pps < jend) ++cnt;
+  }
+  if (kvt == MK_KV_Q8 && wave() == (2 * ks) % NCW && j0 < jend) ++cnt;
+  return cnt;
+}
+
+// ---- multi-chunk passes (compact KV caches)
+// The items, chunks and per-output arithmetic of att_items, with up to B consecutive chunks of an
+// item per pass: the chunks of the next pass are copied while this one is used (2 B chunk buffers
+// in stage A, chunk k of the workgroup's sequence in buffer k % 2B), and each step -- scores,
+// softmax rows, P.V -- covers the pass's chunks in one sweep.  The thread that owns an output takes
+// the pass's chunk merges in chunk order in registers, with the formulas of att_items, so the
+// results are bitwise those of att_items (and of the verify kernels).  A pass has four workgroup
+// barriers where B single chunks have 4 B: at long contexts the barriers and LDS round trips of
+// each chunk, not its bytes, set the time of a chunk.  The caller has issued the copies of
+// sequence numbers 0 .. B - 1; a workgroup without items waits until at most wait_first of its
+// copies are outstanding.
+template <int B>
+__device__ __forceinline__ bool att_items_multi(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx,
+                                                const Lds& s, int NW, int w, int pos, int wait_first, Tracer& tr) {
+  constexpr int NBUF = 2 * B;
+  const int hd = p.hd, nkv = p.nkv, gs = p.nq / p.nkv, cpi = p.att_cpi;
+  const int Lpos = pos + 1;
+  const int nch = (Lpos + ATT_C - 1) / ATT_C;
+  const int items = att_items_count(p, pos);
+  const float scale = 1.0f / sqrtf((float)hd);
+  const int kvt = p.kvt;
+  const int kvb = kv_buf_slots(hd, kvt);
+  const int rows = gs * ATT_C;
+  LS float* qv = s.att;                 // [gs][hd]
+  LS float* kpos = qv + gs * hd;        // [hd]
+  LS float* vpos = kpos + hd;           // [hd]
+  LS float* pb = vpos + hd;             // [B][gs][16] probabilities (unnormalised)
+  LS float* ml = pb + B * rows;         // [B][gs][2] each chunk's max and sum
+  LS float* racc = ml + 2 * B * gs;     // [gs][hd] running acc of the item
+  LS float* rml = racc + gs * hd;       // [2 (pass parity)][gs][2] running max and sum
+  const int np = att_parts(gs, hd), gpp = (hd >> 2) / np;
+  LS float* sp = s.vec;                 // [B][np][gs][16] partial scores
+  const MK_G mk_u64* llq = L.ll_in;
+  const MK_G mk_u64* llk = L.ll_in + p.nq * hd;
+  const MK_G mk_u64* llv = llk + nkv * hd;
+  int gq = -1;      // KV head whose queries are in qv
+  int k = 0;        // sequence number of the pass's first chunk
+  int issued = B;   // sequence numbers whose copies have been issued
+  int par = 0;      // pass parity of the running (max, sum)
+  for (int it = w; it < items; it += NW) {
+    const int blk = it / nkv, g = it - blk * nkv;
+    const int c0 = blk * cpi, c1 = min(nch, c0 + cpi);
+    for (int cp = c0, nP = 0; cp < c1; cp += nP, k += nP, par ^= 1) {
+      nP = min(B, c1 - cp);  // chunks of this pass: cp .. cp + nP - 1 (sequence numbers k ..)
+      // the next B chunks of the sequence -> their buffers (last used two passes ago); then wait
+      // until only copies of chunks after this pass may remain
+      int pending = 0;
+      for (; issued < k + nP + B; ++issued) {
+        const int cn = att_chunk_at(p, NW, w, pos, issued);
+        if (cn < 0) break;
+        kv_stage(p, L, cn, pos, s.stA + (issued % NBUF) * kvb * SLOT);
+      }
+      for (int q = k + nP; q < issued; ++q) pending += kv_stage_count(p, att_chunk_at(p, NW, w, pos, q), pos);
+      const bool has_pos = cp + nP == nch;  // the last chunk of the pass holds position pos
+      const bool need_q = g != gq;
+      gq = g;
+      const int qoff = need_q ? 0 : gs * hd;  // records skipped
+      const int n = gs * hd + (has_pos ? 2 * hd : 0) - qoff;
+      const bool ok = gather_map(cx, n, [=](int f) {
+        f += qoff;
+        if (f < gs * hd) return llq + g * gs * hd + f;
+        if (f < gs * hd + hd) return llk + g * hd + (f - gs * hd);
+        return llv + g * hd + (f - gs * hd - hd);
+      }, [=](int f, float v) { s.att[f + qoff] = v; });
+      tr.mark();
+      // (the copies of the pass's chunks, and everything this wave issued before them, such as
+      // the caller's out-projection units, are older than the `pending` most recent ones)
+      if (streamer()) wait_vm_n(pending);
+      tr.mark();
+      if (wg_bar_or(s, !ok)) return false;
+      if (has_pos) kv_round_append(p, L, kpos, vpos, 1, pb, g, pos);  // barriers inside
+      tr.mark();
+      // scores of every chunk of the pass, in key-dimension parts
+      for (int task = tid(); task < nP * np * rows; task += MK_NT) {
+        const int b = task / (np * rows), pr = task - b * (np * rows);
+        const int part = pr / rows, r = pr - part * rows;
+        const int i = r >> 4, jj = r & 15;
+        const int j0 = (cp + b) * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
+        if (jj < nj) {
+          const KvCompact kc = kv_compact(hd, kvt, s.stA + ((k + b) % NBUF) * kvb * SLOT);
+          if (j0 + jj == pos) {
+            sp[task] = qk_part<true>(kpos, qv + i * hd, jj, part, gpp);
+          } else if (kvt == MK_KV_F16) {
+            sp[task] = qk_part_c<MK_KV_F16>(kc.row(0, jj), nullptr, qv + i * hd, jj, part, gpp);
+          } else {
+            sp[task] = qk_part_c<MK_KV_Q8>(kc.row(0, jj), kc.scales(0, jj), qv + i * hd, jj, part, gpp);
+          }
+        }
+      }
+      wg_bar();
+      // softmax numerators, row max and sum of every chunk (whole rows of 16 lanes in the DPP)
+      for (int t = tid(); t < nP * rows; t += MK_NT) {
+        const int b = t / rows, r = t - b * rows;
+        const int i = r >> 4, jj = r & 15;
+        const int j0 = (cp + b) * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
+        const bool valid = jj < nj;
+        const float sc = valid ? att_part_sum(sp + b * np * rows + r, rows, np) * scale : -INFINITY;
+        const float m = row_max16(sc);
+        const float e = valid ? expf(sc - m) : 0.f;
+        const float l = row_sum16(e);
+        pb[b * rows + i * ATT_C + jj] = e;
+        if (jj == 0) {
+          ml[2 * (b * gs + i)] = m;
+          ml[2 * (b * gs + i) + 1] = l;
+        }
+      }
+      tr.mark();
+      wg_bar();
+      tr.mark();
+      {
+        // P.V of each chunk and the running merge in chunk order, one (query head, dimension)
+        // output per thread and pass
+        const bool last_pass = cp + nP == c1;
+        const LS float* rin = rml + par * 2 * gs;        // running (max, sum) before this pass
+        LS float* rout = rml + (par ^ 1) * 2 * gs;       // ... and after it
+        MK_G mk_u64* part = L.ll_part + (size_t)it * gs * (hd + 2);
+        for (int o = tid(); o < gs * hd; o += MK_NT) {
+          const int i = o / hd, d = o - i * hd;
+          float A = 0.f, M = 0.f, S = 0.f;
+          if (cp > c0) {
+            A = racc[o];
+            M = rin[2 * i];
+            S = rin[2 * i + 1];
+          }
+          for (int b = 0; b < nP; ++b) {
+            const int c = cp + b, j0 = c * ATT_C, nj = min(Lpos, j0 + ATT_C) - j0;
+            const KvCompact kc = kv_compact(hd, kvt, s.stA + ((k + b) % NBUF) * kvb * SLOT);
+            float pv[ATT_C], vv[ATT_C];
+#pragma unroll
+            for (int jj = 0; jj < ATT_C; ++jj) pv[jj] = pb[b * rows + i * ATT_C + jj];  // zero beyond nj
+#pragma unroll
+            for (int q4 = 0; q4 < ATT_C; q4 += 4) {
+              float t4[4];
+              // column d of four compact V rows (the slot of position pos, not staged, takes vpos)
+              const LS char* vr[4] = {kc.row(1, q4), kc.row(1, q4 + 1), kc.row(1, q4 + 2), kc.row(1, q4 + 3)};
+              const LS float* vs[4] = {kc.scales(1, q4), kc.scales(1, q4 + 1), kc.scales(1, q4 + 2),
+                                       kc.scales(1, q4 + 3)};
+              if (kvt == MK_KV_F16) kv_col4<MK_KV_F16>(vr, vs, d, t4);
+              else kv_col4<MK_KV_Q8>(vr, vs, d, t4);
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                if (j0 + q4 + x == pos) t4[x] = vpos[d];
+                vv[q4 + x] = q4 + x < nj ? t4[x] : 0.f;
+              }
+            }
+            float a = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < ATT_C; ++jj) a = fmaf(pv[jj], vv[jj], a);
+            float Mc = ml[2 * (b * gs + i)], Sc = ml[2 * (b * gs + i) + 1];
+            if (c > c0) {
+              const float Mn = fmaxf(M, Mc);
+              const float f = expf(M - Mn), f1 = expf(Mc - Mn);
+              a = fmaf(A, f, a * f1);
+              Sc = fmaf(S, f, Sc * f1);
+              Mc = Mn;
+            }
+            A = a;
+            M = Mc;
+            S = Sc;
+          }
+          if (last_pass) {
+            ll_put(part + i * (hd + 2) + 2 + d, cx.epoch, A);
+            if (d == 0) {
+              ll_put(part + i * (hd + 2), cx.epoch, M);
+              ll_put(part + i * (hd + 2) + 1, cx.epoch, S);
+            }
+          } else {
+            racc[o] = A;
+            if (d == 0) {
+              rout[2 * i] = M;
+              rout[2 * i + 1] = S;
+            }
+          }
+        }
+      }
+      wg_bar();  // LDS and the KV buffers are reused by the next pass
+    }
+  }
+  if (w >= items && streamer()) wait_vm_n(wait_first);
+  return true;
+}
+
 // log-sum-exp merge (in item order) of the item partials for o[o0..o1) -> records
 __device__ __forceinline__ bool att_combine(const MkDecodeParams& p, const MkLayerDev& L, const Ctx& cx, const Lds& s,
                                             int o0, int o1, int pos) {

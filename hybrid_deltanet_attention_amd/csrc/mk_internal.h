@@ -24,6 +24,8 @@ typedef unsigned long long mk_u64;
 #define MK_NCT (MK_NCW * 64)
 // Positions per split-K attention work item (one 16-lane DPP row per query head).
 #define MK_ATT_CHUNK 16
+// chunks per attention pass of the decode kernel for compact KV caches
+#define MK_ATT_PASS 3
 // 8-byte trace words per workgroup (pairs of wall clock, core clock).
 #define MK_TRACE_EVENTS 1024
 // Polls of an exchange word before a wait gives up and reports MK_E_DEVICE_TIMEOUT.
