@@ -438,6 +438,22 @@ def q4_27b_verify_leg(W, ctx: int, n_launch: int, k: int = 5) -> dict:
     snaps = k * b["state"] // 2
     bytes_pass = b["total"]
     gbs = bytes_pass / (us * 1e-6) / 1e9
+    # plain decode launches at the same context (one position each)
+    for _ in range(2):
+        m.mk_decode_step(nxt, nxt)
+    m.mk_sync()
+    n_dec = 16
+    evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dec)]
+    torch.cuda.synchronize()
+    for i in range(n_dec):
+        evd[i][0].record(m.stream)
+        m.mk_decode_step(nxt, nxt)
+        evd[i][1].record(m.stream)
+    m.mk_sync()
+    torch.cuda.synchronize()
+    us_dec = float(np.mean([x.elapsed_time(y) for x, y in evd])) * 1e3
+    p_dec = m.mk_get_position() - n_dec // 2
+    bytes_dec = algorithmic_bytes(cfg, p_dec, 0.625, kv="f16")["total"]
     m.close()
     return {"workload": f"hybrid_27b 4-bit verify, pending token + {k} random drafts at position {ctx} "
                         f"(32,768-position binary16 KV cache, context from a {ctx}-token 4-bit prefill)",
@@ -446,7 +462,10 @@ def q4_27b_verify_leg(W, ctx: int, n_launch: int, k: int = 5) -> dict:
             "tok_per_s_measured": round(float((a + 1).sum()) / (n_launch * us * 1e-6), 1),
             "tok_per_s_all_accepted": round((k + 1) / (us * 1e-6), 1), "launches": n_launch,
             "bytes_per_pass": int(bytes_pass), "snapshot_bytes": int(snaps), "achieved_GBs": round(gbs, 1),
-            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "decode_at_context": {"position": int(p_dec), "us_per_launch": round(us_dec, 1),
+                                  "tok_per_s": round(1e6 / us_dec, 1), "bytes_per_launch": int(bytes_dec),
+                                  "frac": round(bytes_dec / (us_dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
 def q4_27b_leg(ctx: int, n_steps: int, verify_ctx: int = 30000) -> dict:

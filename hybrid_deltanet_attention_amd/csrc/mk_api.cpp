@@ -317,9 +317,9 @@ void lds_layout_q4(const mk_config& c, int grid, MkDecodeParams& p) {
   const int gs = c.n_q_heads / c.n_kv_heads;
   const int hd = c.head_dim, C = MK_ATT_CHUNK;
   const int vec = std::max(std::max(std::max(std::max(c.ffn, D), c.dn_heads * c.dn_dv), std::max(c.n_q_heads * hd, 2 * grid)),
-                           MK_NT);  // (also the attention items' partial scores)
+                           2 * MK_NT);  // (also the attention items' partial scores: passes of two chunks)
   int att = 2 * c.dn_dk + 2 + c.dn_dv;
-  att = std::max(att, 2 * gs * hd + 2 * hd + gs * C + 6 * gs);
+  att = std::max(att, 2 * gs * hd + 2 * hd + 2 * (gs * C + 2 * gs) + 4 * gs);
   att = std::max(att, 2048);  // Q4_RED_CAP
   att = std::max(att, 3 * 129);
   int o = 0;

@@ -158,12 +158,17 @@ __device__ __forceinline__ void decode_q4_body(const MkDecodeParams& p0) {
       att_qkv_run(p, L, cx, s, P0, pos,
                   [&](auto epi) { gemv_q4<true, false>(gin, s.xn, s.att, c0, q, streamer(), tr, epi); });
       tr.mark();
-      // K/V rows of the first work items -> stage A
-      for (int kc = 0; kc + 1 < kv_nbuf(p.hd, p.kvt, s.a_slots) || kc == 0; ++kc) {
+      // K/V rows of the first chunks of the work items -> stage A.  In the shape-specialised
+      // instances, compact caches whose chunk buffers fit four times in the stage take their chunks
+      // two at a time (att_items_multi; the generic instance would spill registers with both walks).
+      const bool multi = D_ != 0 && KVT != MK_KV_F32 && 4 * kv_buf_slots(p.hd, p.kvt) <= s.a_slots;
+      const int first = multi ? 2 : max(1, kv_nbuf(p.hd, p.kvt, s.a_slots) - 1);
+      for (int kc = 0; kc < first; ++kc) {
         const int cn = att_chunk_at(p, NW, w, pos, kc);
         if (cn >= 0) kv_stage(p, L, cn, pos, s.stA + kc * kv_buf_slots(p.hd, p.kvt) * SLOT);
       }
-      if (!att_items(p, L, cx, s, NW, w, pos, 0, tr)) return;
+      if (multi ? !att_items_multi<2>(p, L, cx, s, NW, w, pos, 0, tr) : !att_items(p, L, cx, s, NW, w, pos, 0, tr))
+        return;
       tr.mark();
       const int o0 = split(K, NW, w), o1 = split(K, NW, w + 1);
       if (!att_combine(p, L, cx, s, o0, o1, pos)) return;

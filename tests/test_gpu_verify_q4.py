@@ -66,9 +66,12 @@ def _oracle_from_gpu(cfg, W, m, T, kv="f32", cache_bytes=None):
     return o
 
 
-def _verify_vs_oracle(cfg, W, prompt, seed, kv_dtype=MK_F32, kv="f32", cache_bytes=None, grid=None):
+def _verify_vs_oracle(cfg, W, prompt, seed, kv_dtype=MK_F32, kv="f32", cache_bytes=None, grid=None,
+                      decode_steps=0):
     """GPU prompt (decode launches), state handed to the oracle; greedy, planted and random drafts
-    scored by one verify launch each (from the same handed-off state) and by Oracle.verify"""
+    scored by one verify launch each (from the same handed-off state) and by Oracle.verify; then,
+    with decode_steps, that many teacher-forced decode launches from the same state against the
+    oracle's steps (logits relative L2 <= 1e-2, the fused argmax of the launch's own logits)"""
     torch = torch_cuda()
     mv = _verify_model(cfg, W, 5, grid, kv_dtype, MK_Q4G32)
     nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -114,6 +117,24 @@ def _verify_vs_oracle(cfg, W, prompt, seed, kv_dtype=MK_F32, kv="f32", cache_byt
                 e = rel_l2(st, o.S[l])
                 assert e <= 1e-3, f"{label}: layer {l} state rel-L2 {e:.2e}"
         assert mv.mk_get_position() == P
+    if decode_steps:
+        o.restore(start)
+        assert gpu_prompt() == pend
+        d_tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+        d_next = torch.zeros(1, dtype=torch.int32, device="cuda")
+        d_lg = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+        t = pend
+        for i in range(decode_steps):
+            d_tok.fill_(t)
+            mv.mk_decode_step(d_tok, d_next, d_lg)
+            mv.mk_sync()
+            g = d_lg.cpu().numpy()
+            ref = o.step(t)
+            e = rel_l2(g, ref)
+            print(f"[q4 decode {cfg.name} T={T} step {i}] logits rel-L2 {e:.2e}", flush=True)
+            assert e <= 1e-2, f"decode step {i}: logits rel-L2 {e:.2e}"
+            assert int(d_next.item()) == int(np.argmax(g))
+            t = o.argmax(ref)
     mv.close()
 
 
@@ -128,4 +149,6 @@ def test_q4_27b_width_slice_30k_context_against_oracle_verify():
     cfg = synth.get_config("hybrid_27b", n_layers=4, max_ctx=32768)
     W = synth.make_q4_weights(cfg, 0)
     prompt = [int(t) for t in synth.make_prompt(cfg.vocab, 30000, 13)]
-    _verify_vs_oracle(cfg, W, prompt, 13, kv_dtype=MK_F16, kv="f16", cache_bytes=1 << 36)
+    # the decode steps run the shape-specialised 4-bit kernel, whose attention takes the binary16
+    # chunks two at a time
+    _verify_vs_oracle(cfg, W, prompt, 13, kv_dtype=MK_F16, kv="f16", cache_bytes=1 << 36, decode_steps=3)
