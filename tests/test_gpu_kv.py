@@ -46,6 +46,19 @@ def test_tiny_multi_chunk_items_odd_grid(kv):
 
 
 @pytest.mark.parametrize("kv", KVS, ids=IDS)
+def test_tiny_many_items_per_workgroup(kv):
+    # an 8,192-position cache (items of 4 chunks) on a grid of 8 after a 1,500-token prompt: each
+    # workgroup walks about 6 items, 24 chunks, in passes of three and one chunk, and its six chunk
+    # buffers wrap around several times.  Decode against the oracle, then the verify launch (which
+    # takes the chunks one at a time) against decode launches, bit for bit.
+    cfg = synth.get_config("tiny", max_ctx=8192)
+    W = synth.make_weights(cfg, 36)
+    prompt = synth.make_prompt(cfg.vocab, 1500, 36)
+    _check_run(cfg, W, prompt, 8, grid=8, kv_dtype=kv)
+    assert _check_against_decode(cfg, W, prompt, lambda c: c, 5, grid=8, label="many items", kv_dtype=kv) == 5
+
+
+@pytest.mark.parametrize("kv", KVS, ids=IDS)
 def test_head_dim_96_prompt_through_decode(kv):
     # head_dim 96: rows that do not fill the 1 KB staging slots evenly; the prompt runs through the
     # decode kernel (the matrix-core prefill attention takes head sizes 64 and 128)
