@@ -1744,7 +1744,13 @@ __device__ __forceinline__ bool att_items_multi(const MkDecodeParams& p, const M
         if (cn < 0) break;
         kv_stage(p, L, cn, pos, s.stA + (issued % NBUF) * kvb * SLOT);
       }
-      for (int q = k + nP; q < issued; ++q) pending += kv_stage_count(p, att_chunk_at(p, NW, w, pos, q), pos);
+      // (sequence numbers past the workgroup's last chunk were never issued: the caller's first B
+      // may run past it)
+      for (int q = k + nP; q < issued; ++q) {
+        const int cn = att_chunk_at(p, NW, w, pos, q);
+        if (cn < 0) break;
+        pending += kv_stage_count(p, cn, pos);
+      }
       const bool has_pos = cp + nP == nch;  // the last chunk of the pass holds position pos
       const bool need_q = g != gq;
       gq = g;
