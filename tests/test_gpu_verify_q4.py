@@ -21,7 +21,7 @@ from test_gpu_verify import _check_against_decode, _verify_model, _dev
 
 pytestmark = pytest.mark.gpu
 
-MK_Q4G32, MK_F32, MK_F16 = 5, 2, 3
+MK_Q4G32, MK_F32, MK_F16, MK_Q8 = 5, 2, 3, 6
 
 
 @pytest.mark.parametrize("seed", [0, 1])
@@ -152,3 +152,14 @@ def test_q4_27b_width_slice_30k_context_against_oracle_verify():
     # the decode steps run the shape-specialised 4-bit kernel, whose attention takes the binary16
     # chunks two at a time
     _verify_vs_oracle(cfg, W, prompt, 13, kv_dtype=MK_F16, kv="f16", cache_bytes=1 << 36, decode_steps=3)
+
+
+@pytest.mark.timeout(900)
+def test_q4_27b_width_slice_int8_cache_against_oracle():
+    # an int8 cache at 27B width: an 8,192-position cache (attention items of 4 chunks, which the
+    # shape-specialised 4-bit decode kernel takes two at a time) after a 2,000-token prompt; verify
+    # and decode against the oracle from the handed-off context
+    cfg = synth.get_config("hybrid_27b", n_layers=4, max_ctx=8192)
+    W = synth.make_q4_weights(cfg, 2)
+    prompt = [int(t) for t in synth.make_prompt(cfg.vocab, 2000, 14)]
+    _verify_vs_oracle(cfg, W, prompt, 14, kv_dtype=MK_Q8, kv="q8", cache_bytes=1 << 36, decode_steps=3)
