@@ -1165,13 +1165,16 @@ __device__ __forceinline__ void q4v_partials(const GemvQ4& g, int sg0, int Sg, c
 // with a barrier and returns false when a wait gave up (the same in every thread); epi(row, t, v, 0)
 // or, PAIRS, epi(pair, t, v_even, v_odd) runs on the streaming threads once a row chunk's groups are
 // done.  Returns false when a pack failed.
-template <bool PAIRS, typename Pack, typename Epi>
+// PACKED: pack() gathers words that are already packed, position t's at P + t (n / 32) Q4_XW, so a
+// column group takes 0.625 of the LDS of FP32 values and groups are that much wider.
+template <bool PAIRS, bool PACKED = false, typename Pack, typename Epi>
 __device__ __forceinline__ bool gemv_q4_v(const GemvQ4& G, int nt, LS float* P, int pcap, LS float* red, LS int* ctr,
                                           Pack pack, Epi epi) {
   const int S = uni(G.S), K = uni(G.K);
   nt = uni(nt);
   // one group when every position's columns fit (then they are packed once for all row chunks)
-  const int gs = nt * K <= pcap && K <= 8 * MK_NT * Q4_PACK_IT ? S : min(S, q4v_group_segs(pcap, nt));
+  const int gs = PACKED ? (nt * (K >> 5) * Q4_XW <= pcap ? S : min(S, max(1, pcap / (nt * (Q4_COLS >> 5) * Q4_XW))))
+                        : (nt * K <= pcap && K <= 8 * MK_NT * Q4_PACK_IT ? S : min(S, q4v_group_segs(pcap, nt)));
   const int ngroups = (S + gs - 1) / gs;
   const int rc = q4v_rows(S, nt);
   for (int r0 = 0; r0 == 0 || r0 < G.R; r0 += rc) {
@@ -1181,7 +1184,7 @@ __device__ __forceinline__ bool gemv_q4_v(const GemvQ4& G, int nt, LS float* P, 
     for (int gi = 0; gi < ngroups; ++gi) {
       const int sg0 = gi * gs, Sg = min(gs, S - sg0);
       const int c0 = sg0 * Q4_COLS, n = min(K, (sg0 + Sg) * Q4_COLS) - c0;
-      const int pstride = n;  // position t's packed words start at t * n
+      const int pstride = PACKED ? (n >> 5) * Q4_XW : n;  // position t's packed words start at t * pstride
       if ((ngroups > 1 || r0 == 0) && !pack(c0, n, P)) return false;  // one group: packed once
       if (g.R > 0) q4v_partials(g, sg0, Sg, (const LS u32*)P, pstride, nt, red, ctr);
       wg_bar();
@@ -1312,17 +1315,15 @@ __device__ __forceinline__ bool q4v_pack_norm(const Ctx& cx, const Lds& s, const
 
 // Packed activations of columns [c0, c0 + n) (n a multiple of 32) for every position from records
 // that already hold packed words -- position t's at src + t * stride, block b's Q4_XW words at
-// b * Q4_XW -- to P + t * n.  Every thread calls it; ends with a barrier.
+// b * Q4_XW -- to P + t * pw, pw = (n / 32) Q4_XW (the packed stride of gemv_q4_v<.., true>).  Every
+// thread calls it; ends with a barrier.
 __device__ __forceinline__ bool q4v_gather_packed(const Ctx& cx, const Lds& s, const MK_G mk_u64* src, int stride,
                                                   int nt, int c0, int n, LS float* P) {
   const int pw = (n >> 5) * Q4_XW, w0 = (c0 >> 5) * Q4_XW;
   const bool ok = gather_map_all(cx, nt * pw, [=](int f) {
     const int t = f / pw;
     return src + (size_t)t * stride + w0 + (f - t * pw);
-  }, [=](int f, float v) {
-    const int t = f / pw;
-    P[t * n + (f - t * pw)] = v;
-  });
+  }, [=](int f, float v) { P[f] = v; });
   return !wg_bar_or(s, !ok);
 }
 
@@ -1487,7 +1488,7 @@ __device__ __forceinline__ void verify_q4_body(const MkDecodeParams& p) {
     {
       GemvQ4 gdn;
       gdn.init(L.w_down, d0 >> 2, d1 - d0, F);
-      if (!gemv_q4_v<false>(
+      if (!gemv_q4_v<false, true>(
               gdn, nt, s.vec, pcap, s.att, ctr,
               [&](int c0, int n, LS float* P) { return q4v_gather_packed(cx, s, L.ll_h, F, nt, c0, n, P); },
               [&](int r, int t, float v, float) {
